@@ -1,0 +1,178 @@
+"""CPU oracle for cone-beam DRR ray casting -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and its
+Python binding) never imports, links or calls it, and this package never
+imports the product: the two share only the seeded input arrays from
+``workloads``.
+
+The arithmetic lives in ``drr_oracle.c`` (plain C, scalar fp64, OpenMP over
+rays); this module only builds it with gcc, loads it with ctypes and converts
+arrays.  Inputs the HIP side receives in fp32 (spacing, K, poses) are widened
+exactly to fp64 here; the volume stays fp32 and is widened per read.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(HERE, "drr_oracle.c")
+LIBRARY = os.path.join(HERE, "libdrr_oracle.so")
+
+BEER_LAMBERT = 0
+LINE_INTEGRAL = 1
+
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the oracle with gcc: -O2, OpenMP, no fast-math, no FMA contraction."""
+    cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-Wall", "-Wextra", "-o", LIBRARY + ".tmp", SOURCE, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIBRARY + ".tmp", LIBRARY)
+    return LIBRARY
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+        build()
+    lib = ctypes.CDLL(LIBRARY)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.oracle_forward.argtypes = [P, I, I, I, P, P, P, I, I, I, I, I, P, P, I]
+    lib.oracle_forward.restype = I
+    lib.oracle_adjoint.argtypes = [P, I, I, I, P, P, P, I, I, I, I, I, P, P, I, ctypes.c_longlong]
+    lib.oracle_adjoint.restype = I
+    lib.oracle_ray.argtypes = [P, P, P, I, I, P]
+    lib.oracle_ray.restype = I
+    lib.oracle_forward_spheres.argtypes = [P, I, P, P, P, I, I, I, I, I, P, I]
+    lib.oracle_forward_spheres.restype = I
+    lib.oracle_exact_line_integral.argtypes = [P, I, I, I, P, P, P, I, I, I, P, I]
+    lib.oracle_exact_line_integral.restype = I
+    lib.oracle_max_threads.restype = I
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float32).astype(np.float64))
+
+
+def _threads(n: Optional[int]) -> int:
+    return int(n) if n else (os.cpu_count() or 1)
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def forward(volume: np.ndarray, spacing, K, poses, det_h: int, det_w: int, n_samples: int,
+            mode: int, n_threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Forward DRR.  Returns (image, line_integral), both float64 (V, H, W)."""
+    lib = _load()
+    vol = np.ascontiguousarray(volume, dtype=np.float32)
+    nz, ny, nx = vol.shape
+    sp, Kd, Pd = _f64(spacing), _f64(K), _f64(poses).reshape(-1, 12)
+    V = Pd.shape[0]
+    out = np.zeros((V, det_h, det_w), dtype=np.float64)
+    s = np.zeros((V, det_h, det_w), dtype=np.float64)
+    rc = lib.oracle_forward(_ptr(vol), nz, ny, nx, _ptr(sp), _ptr(Kd), _ptr(Pd), V, det_h, det_w,
+                            n_samples, mode, _ptr(out), _ptr(s), _threads(n_threads))
+    if rc != 0:
+        raise ValueError("oracle_forward: invalid arguments")
+    return out, s
+
+
+def adjoint(volume: Optional[np.ndarray], shape, spacing, K, poses, det_h: int, det_w: int,
+            n_samples: int, mode: int, grad_out: np.ndarray, n_threads: Optional[int] = None,
+            max_buffer_bytes: int = 4 << 30) -> Tuple[np.ndarray, int]:
+    """Volume gradient for upstream dL/dI = grad_out.  ``volume`` is required for
+    Beer-Lambert (it fixes exp(-s)) and ignored for the line integral.
+    Returns (grad float64 (nz, ny, nx), threads used)."""
+    lib = _load()
+    nz, ny, nx = (int(x) for x in shape)
+    vol = None if volume is None else np.ascontiguousarray(volume, dtype=np.float32)
+    sp, Kd, Pd = _f64(spacing), _f64(K), _f64(poses).reshape(-1, 12)
+    V = Pd.shape[0]
+    g = np.ascontiguousarray(grad_out, dtype=np.float64).reshape(V, det_h, det_w)
+    grad = np.zeros((nz, ny, nx), dtype=np.float64)
+    rc = lib.oracle_adjoint(None if vol is None else _ptr(vol), nz, ny, nx, _ptr(sp), _ptr(Kd),
+                            _ptr(Pd), V, det_h, det_w, n_samples, mode, _ptr(g), _ptr(grad),
+                            _threads(n_threads), int(max_buffer_bytes))
+    if rc < 1:
+        raise ValueError("oracle_adjoint: invalid arguments or out of memory")
+    return grad, int(rc)
+
+
+def ray(K, pose, extent, r: int, c: int):
+    """(hit, C, d, t0, t1) of the ray through pixel (r, c)."""
+    lib = _load()
+    out = np.zeros(8, dtype=np.float64)
+    hit = lib.oracle_ray(_ptr(_f64(K)), _ptr(_f64(pose).reshape(12)),
+                         _ptr(np.ascontiguousarray(extent, dtype=np.float64)), r, c, _ptr(out))
+    if hit < 0:
+        raise ValueError("singular K")
+    return bool(hit), out[0:3].copy(), out[3:6].copy(), float(out[6]), float(out[7])
+
+
+def forward_spheres(spheres, extent, K, poses, det_h: int, det_w: int, n_samples: int,
+                    mode: int, n_threads: Optional[int] = None) -> np.ndarray:
+    """Forward through an analytic density: a sum of uniform balls given as rows
+    (cx, cy, cz, radius, mu); the box ``extent`` (centred at 0) still clips."""
+    lib = _load()
+    sph = np.ascontiguousarray(np.asarray(spheres, dtype=np.float64).reshape(-1, 5))
+    Kd, Pd = _f64(K), _f64(poses).reshape(-1, 12)
+    V = Pd.shape[0]
+    out = np.zeros((V, det_h, det_w), dtype=np.float64)
+    rc = lib.oracle_forward_spheres(_ptr(sph), sph.shape[0],
+                                    _ptr(np.ascontiguousarray(extent, dtype=np.float64)),
+                                    _ptr(Kd), _ptr(Pd), V, det_h, det_w, n_samples, mode,
+                                    _ptr(out), _threads(n_threads))
+    if rc != 0:
+        raise ValueError("oracle_forward_spheres: invalid arguments")
+    return out
+
+
+def exact_line_integral(volume: np.ndarray, spacing, K, poses, det_h: int, det_w: int,
+                        n_threads: Optional[int] = None) -> np.ndarray:
+    """Exact integral of the clamped trilinear field along each clipped ray."""
+    lib = _load()
+    vol = np.ascontiguousarray(volume, dtype=np.float32)
+    nz, ny, nx = vol.shape
+    sp, Kd, Pd = _f64(spacing), _f64(K), _f64(poses).reshape(-1, 12)
+    V = Pd.shape[0]
+    s = np.zeros((V, det_h, det_w), dtype=np.float64)
+    rc = lib.oracle_exact_line_integral(_ptr(vol), nz, ny, nx, _ptr(sp), _ptr(Kd), _ptr(Pd), V,
+                                        det_h, det_w, _ptr(s), _threads(n_threads))
+    if rc != 0:
+        raise ValueError("oracle_exact_line_integral: invalid arguments")
+    return s
+
+
+def forward_workload(w, n_threads: Optional[int] = None, use_bf16: bool = False):
+    """Convenience: forward of a ``workloads.Workload``."""
+    vol = w.volume_bf16_as_f32() if use_bf16 else w.volume
+    return forward(vol, w.spacing, w.K, w.poses, w.det_h, w.det_w, w.n_samples, w.mode, n_threads)
+
+
+def adjoint_workload(w, grad_out=None, n_threads: Optional[int] = None,
+                     max_buffer_bytes: int = 4 << 30):
+    """Convenience: volume gradient of a ``workloads.Workload``."""
+    g = w.grad_out if grad_out is None else grad_out
+    return adjoint(w.volume, w.volume.shape, w.spacing, w.K, w.poses, w.det_h, w.det_w,
+                   w.n_samples, w.mode, g, n_threads, max_buffer_bytes)

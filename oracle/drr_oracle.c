@@ -1,0 +1,514 @@
+/*
+ * drr_oracle.c -- CPU oracle for differentiable cone-beam DRR ray casting.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the package smoke check and
+ * the benchmark's CPU-baseline leg may load this library.  It shares no source,
+ * header, table or helper with the HIP library: it reads the same seeded input
+ * arrays and nothing else.
+ *
+ * Plain, slow and meant to be checked by eye: scalar double arithmetic, no SIMD,
+ * no fast-math, no FMA contraction, OpenMP only across rays.  Every function
+ * names the passage of the source pages it follows:
+ *
+ *   [nanodrr]   "nanodrr" project page, introduction: projective geometry uses
+ *               the Hartley-Zisserman pinhole camera (P = K [R | t]).
+ *   [fd-init]   flashdrr.rendering API, VolumeRaycaster.__init__: ray_samples
+ *               samples per ray; use_beer_lambert returns 1 - exp(-int mu dz).
+ *   [fd-fov]    flashdrr.rendering API, VolumeRaycaster.set_fov: per-pixel ray
+ *               directions are built in the image plane and normalised.
+ *   [fd-class]  flashdrr.rendering API, VolumeRaycaster class text: samples
+ *               along each ray are trilinear (grid_sample) gathers of the volume;
+ *               rendering is differentiable with respect to the volume.
+ *   [diffct-qs] diffct 2.1.0, Quickstart: project() gives line integrals,
+ *               backproject() the matched adjoint A^T, and for
+ *               0.5 ||A x - y||^2 the gradient is A^T (A x - y).
+ *   [tt-adj]    torchtomo, "Discrete Adjoint and Learned Primal-Dual": the
+ *               adjoint satisfies <A x, y> = <x, A^T y>.
+ *
+ * Readings taken where the pages are silent (each is restated at the code that
+ * implements it):
+ *   - world units are mm, mu is 1/mm, ray directions are unit vectors so the
+ *     ray parameter t is a distance in mm;
+ *   - the volume vol[k][j][i] (x fastest) fills the axis-aligned box
+ *     [-E/2, E/2] with E = (nx sx, ny sy, nz sz); voxel (i,j,k) is centred at
+ *     ((i+1/2) sx - Ex/2, (j+1/2) sy - Ey/2, (k+1/2) sz - Ez/2);
+ *   - pixel (r, c) is the homogeneous image point (c + 1/2, r + 1/2, 1);
+ *   - each ray is clipped to the box (slab test), t0 = max(t_entry, 0),
+ *     t1 = t_exit, and it misses when t1 <= t0 (output 0, no gradient);
+ *   - the N samples sit at the midpoints t0 + (k + 1/2) dz, dz = (t1 - t0) / N;
+ *   - trilinear interpolation at the continuous index q = (p + E/2) / s - 1/2
+ *     with both corner indices of every axis clamped to [0, n-1];
+ *   - the Beer-Lambert output is evaluated as -expm1(-s), equal to 1 - exp(-s).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_BEER_LAMBERT 0
+#define ORACLE_LINE_INTEGRAL 1
+
+/* ------------------------------------------------------------------ geometry */
+
+/* Camera centre of a world-to-camera pose [R | t] ([nanodrr]): x_cam = R x + t,
+ * so the centre (x_cam = 0) is C = -R^T t.  pose is 3x4 row-major. */
+static void camera_centre(const double *pose, double C[3])
+{
+    for (int a = 0; a < 3; ++a) {
+        C[a] = -(pose[0 * 4 + a] * pose[0 * 4 + 3] +
+                 pose[1 * 4 + a] * pose[1 * 4 + 3] +
+                 pose[2 * 4 + a] * pose[2 * 4 + 3]);
+    }
+}
+
+static double det3(const double m[9])
+{
+    return m[0] * (m[4] * m[8] - m[5] * m[7])
+         - m[1] * (m[3] * m[8] - m[5] * m[6])
+         + m[2] * (m[3] * m[7] - m[4] * m[6]);
+}
+
+/* Solve K x = b by Cramer's rule (K row-major).  Returns 0 if K is singular. */
+static int solve3(const double K[9], const double b[3], double x[3])
+{
+    double D = det3(K);
+    if (D == 0.0) return 0;
+    for (int col = 0; col < 3; ++col) {
+        double M[9];
+        memcpy(M, K, sizeof(M));
+        for (int row = 0; row < 3; ++row) M[row * 3 + col] = b[row];
+        x[col] = det3(M) / D;
+    }
+    return 1;
+}
+
+/* Unit world direction of the ray through pixel (r, c) ([nanodrr], [fd-fov]):
+ * back-project the homogeneous pixel centre m = (c + 1/2, r + 1/2, 1) through
+ * K^-1 into camera coordinates, rotate to world with R^T, normalise. */
+static int pixel_direction(const double K[9], const double *pose, int r, int c, double d[3])
+{
+    double m[3] = { c + 0.5, r + 0.5, 1.0 };
+    double dc[3];
+    if (!solve3(K, m, dc)) return 0;
+    for (int a = 0; a < 3; ++a)
+        d[a] = pose[0 * 4 + a] * dc[0] + pose[1 * 4 + a] * dc[1] + pose[2 * 4 + a] * dc[2];
+    double len = sqrt(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
+    if (!(len > 0.0)) return 0;
+    for (int a = 0; a < 3; ++a) d[a] /= len;
+    return 1;
+}
+
+/* Slab test of the ray C + t d against the box [-E/2, E/2].  An axis with
+ * d_a == 0 constrains nothing if C_a lies inside the slab and misses otherwise.
+ * Returns 1 and the clipped range [t0, t1] (t0 = max(t_entry, 0)) on a hit. */
+static int clip_to_box(const double C[3], const double d[3], const double E[3],
+                       double *t0, double *t1)
+{
+    double t_entry = -INFINITY, t_exit = INFINITY;
+    for (int a = 0; a < 3; ++a) {
+        double lo = -0.5 * E[a], hi = 0.5 * E[a];
+        if (d[a] == 0.0) {
+            if (C[a] < lo || C[a] > hi) return 0;
+            continue;
+        }
+        double ta = (lo - C[a]) / d[a];
+        double tb = (hi - C[a]) / d[a];
+        double tmin = ta < tb ? ta : tb;
+        double tmax = ta < tb ? tb : ta;
+        if (tmin > t_entry) t_entry = tmin;
+        if (tmax < t_exit) t_exit = tmax;
+    }
+    double start = t_entry > 0.0 ? t_entry : 0.0;
+    if (!(t_exit > start)) return 0;
+    *t0 = start;
+    *t1 = t_exit;
+    return 1;
+}
+
+typedef struct {
+    double C[3], d[3];
+    double t0, t1;
+    int hit;
+} oracle_ray_t;
+
+/* Steps 1-2 of the forward: ray generation and clipping for pixel (r, c). */
+static void make_ray(const double K[9], const double *pose, const double E[3],
+                     int r, int c, oracle_ray_t *ray)
+{
+    camera_centre(pose, ray->C);
+    ray->hit = 0;
+    ray->t0 = 0.0;
+    ray->t1 = 0.0;
+    ray->d[0] = ray->d[1] = ray->d[2] = 0.0;
+    if (!pixel_direction(K, pose, r, c, ray->d)) return;
+    ray->hit = clip_to_box(ray->C, ray->d, E, &ray->t0, &ray->t1);
+}
+
+/* ------------------------------------------------------------------ volume */
+
+typedef struct {
+    const float *vol;  /* vol[(k * ny + j) * nx + i] */
+    long n[3];         /* nx, ny, nz */
+    double s[3];       /* voxel spacing sx, sy, sz (mm) */
+    double E[3];       /* box extent n_a * s_a (mm) */
+} oracle_volume_t;
+
+static void volume_init(oracle_volume_t *V, const float *vol, int nz, int ny, int nx,
+                        const double *spacing)
+{
+    V->vol = vol;
+    V->n[0] = nx;
+    V->n[1] = ny;
+    V->n[2] = nz;
+    for (int a = 0; a < 3; ++a) {
+        V->s[a] = spacing[a];
+        V->E[a] = (double)V->n[a] * spacing[a];
+    }
+}
+
+/* Continuous voxel index of a world point: voxel centres sit at integers. */
+static void world_to_index(const oracle_volume_t *V, const double p[3], double q[3])
+{
+    for (int a = 0; a < 3; ++a) q[a] = (p[a] + 0.5 * V->E[a]) / V->s[a] - 0.5;
+}
+
+static long clamp_index(long i, long n)
+{
+    if (i < 0) return 0;
+    if (i > n - 1) return n - 1;
+    return i;
+}
+
+/* The eight trilinear corners of q ([fd-class] grid_sample, trilinear): corner
+ * c (bit 0 = x, bit 1 = y, bit 2 = z) has linear offset off[c] and weight w[c];
+ * corner indices are clamped to the volume (clamp to edge), so near a face two
+ * corners may share one voxel and their weights then add up. */
+static void trilinear_corners(const oracle_volume_t *V, const double q[3], long off[8], double w[8])
+{
+    long lo[3], hi[3];
+    double f[3];
+    for (int a = 0; a < 3; ++a) {
+        double fl = floor(q[a]);
+        f[a] = q[a] - fl;
+        lo[a] = clamp_index((long)fl, V->n[a]);
+        hi[a] = clamp_index((long)fl + 1, V->n[a]);
+    }
+    for (int c = 0; c < 8; ++c) {
+        long i = (c & 1) ? hi[0] : lo[0];
+        long j = (c & 2) ? hi[1] : lo[1];
+        long k = (c & 4) ? hi[2] : lo[2];
+        double wx = (c & 1) ? f[0] : 1.0 - f[0];
+        double wy = (c & 2) ? f[1] : 1.0 - f[1];
+        double wz = (c & 4) ? f[2] : 1.0 - f[2];
+        off[c] = (k * V->n[1] + j) * V->n[0] + i;
+        w[c] = wx * wy * wz;
+    }
+}
+
+static double trilinear(const oracle_volume_t *V, const double q[3])
+{
+    long off[8];
+    double w[8];
+    trilinear_corners(V, q, off, w);
+    double val = 0.0;
+    for (int c = 0; c < 8; ++c) val += w[c] * (double)V->vol[off[c]];
+    return val;
+}
+
+/* Sample k of N on a clipped ray, as a continuous voxel index: midpoint rule,
+ * t_k = t0 + (k + 1/2) dz with dz = (t1 - t0) / N. */
+static void sample_index(const oracle_volume_t *V, const oracle_ray_t *ray, double dz, int k,
+                         double q[3])
+{
+    double t = ray->t0 + ((double)k + 0.5) * dz;
+    double p[3];
+    for (int a = 0; a < 3; ++a) p[a] = ray->C[a] + t * ray->d[a];
+    world_to_index(V, p, q);
+}
+
+/* s = sum_k mu(t_k) dz over the N samples of one ray ([fd-init] ray_samples,
+ * Beer-Lambert integrand mu dz).  A ray that misses the box integrates to 0. */
+static double ray_line_integral(const oracle_volume_t *V, const oracle_ray_t *ray, int N)
+{
+    if (!ray->hit) return 0.0;
+    double dz = (ray->t1 - ray->t0) / (double)N;
+    double acc = 0.0;
+    for (int k = 0; k < N; ++k) {
+        double q[3];
+        sample_index(V, ray, dz, k, q);
+        acc += trilinear(V, q);
+    }
+    return acc * dz;
+}
+
+/* Output stage: Beer-Lambert image 1 - exp(-s) ([fd-init] use_beer_lambert,
+ * evaluated as -expm1(-s)) or the raw line integral ([diffct-qs] project). */
+static double output_value(double s, int mode)
+{
+    return mode == ORACLE_BEER_LAMBERT ? -expm1(-s) : s;
+}
+
+static int check_common(int nz, int ny, int nx, const double *spacing, int n_views, int H,
+                        int W, int n_samples, int mode)
+{
+    if (nz < 1 || ny < 1 || nx < 1) return -1;
+    if (n_views < 0 || H < 0 || W < 0) return -1;
+    if (n_samples < 1) return -1;
+    if (mode != ORACLE_BEER_LAMBERT && mode != ORACLE_LINE_INTEGRAL) return -1;
+    for (int a = 0; a < 3; ++a)
+        if (!(spacing[a] > 0.0)) return -1;
+    return 0;
+}
+
+static void set_threads(int n_threads)
+{
+#ifdef _OPENMP
+    if (n_threads > 0) omp_set_num_threads(n_threads);
+#else
+    (void)n_threads;
+#endif
+}
+
+/* ------------------------------------------------------------------ exports */
+
+/* Forward DRR for every pixel of every view.  out[(v*H + r)*W + c] receives the
+ * Beer-Lambert image or the line integral; line_integral (nullable) receives s.
+ * Returns 0, or -1 on invalid arguments. */
+int oracle_forward(const float *vol, int nz, int ny, int nx, const double *spacing,
+                   const double *K, const double *poses, int n_views, int H, int W,
+                   int n_samples, int mode, double *out, double *line_integral, int n_threads)
+{
+    if (check_common(nz, ny, nx, spacing, n_views, H, W, n_samples, mode)) return -1;
+    oracle_volume_t V;
+    volume_init(&V, vol, nz, ny, nx, spacing);
+    long n_rays = (long)n_views * H * W;
+    set_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 64)
+    for (long ray_id = 0; ray_id < n_rays; ++ray_id) {
+        int v = (int)(ray_id / ((long)H * W));
+        int r = (int)((ray_id / W) % H);
+        int c = (int)(ray_id % W);
+        oracle_ray_t ray;
+        make_ray(K, poses + 12L * v, V.E, r, c, &ray);
+        double s = ray_line_integral(&V, &ray, n_samples);
+        out[ray_id] = output_value(s, mode);
+        if (line_integral) line_integral[ray_id] = s;
+    }
+    return 0;
+}
+
+/* Adjoint / volume gradient ([diffct-qs] backproject and x.grad; [fd-class]
+ * differentiable with respect to the volume).  For upstream g = dL/dI:
+ *   y_p = g_p exp(-s_p)   (Beer-Lambert, dI/ds = exp(-s))
+ *   y_p = g_p             (line integral)
+ * and for every sample and trilinear corner grad[corner] += y_p dz w_corner.
+ * The weights depend on geometry only, so for the line integral this is exactly
+ * A^T.  vol is needed only for Beer-Lambert (to evaluate s) and may be NULL for
+ * the line integral.  grad (nz*ny*nx doubles) is overwritten.  Threads get
+ * private gradient buffers while (threads - 1) buffers fit in max_buffer_bytes;
+ * otherwise the scatter runs on one thread.  Returns the thread count used, or
+ * -1 on invalid arguments. */
+int oracle_adjoint(const float *vol, int nz, int ny, int nx, const double *spacing,
+                   const double *K, const double *poses, int n_views, int H, int W,
+                   int n_samples, int mode, const double *g, double *grad, int n_threads,
+                   long long max_buffer_bytes)
+{
+    if (check_common(nz, ny, nx, spacing, n_views, H, W, n_samples, mode)) return -1;
+    if (mode == ORACLE_BEER_LAMBERT && vol == NULL) return -1;
+    oracle_volume_t V;
+    volume_init(&V, vol, nz, ny, nx, spacing);
+    long n_vox = (long)nx * ny * nz;
+    long n_rays = (long)n_views * H * W;
+    memset(grad, 0, sizeof(double) * (size_t)n_vox);
+
+    int T = n_threads > 0 ? n_threads : 1;
+#ifndef _OPENMP
+    T = 1;
+#endif
+    while (T > 1 && (long long)(T - 1) * n_vox * (long long)sizeof(double) > max_buffer_bytes) --T;
+    double **bufs = (double **)calloc((size_t)T, sizeof(double *));
+    if (!bufs) return -1;
+    bufs[0] = grad;
+    for (int i = 1; i < T; ++i) {
+        bufs[i] = (double *)calloc((size_t)n_vox, sizeof(double));
+        if (!bufs[i]) {
+            for (int j = 1; j < i; ++j) free(bufs[j]);
+            free(bufs);
+            return -1;
+        }
+    }
+    set_threads(T);
+#pragma omp parallel for schedule(dynamic, 64) num_threads(T)
+    for (long ray_id = 0; ray_id < n_rays; ++ray_id) {
+#ifdef _OPENMP
+        double *acc = bufs[omp_get_thread_num()];
+#else
+        double *acc = bufs[0];
+#endif
+        int v = (int)(ray_id / ((long)H * W));
+        int r = (int)((ray_id / W) % H);
+        int c = (int)(ray_id % W);
+        oracle_ray_t ray;
+        make_ray(K, poses + 12L * v, V.E, r, c, &ray);
+        if (!ray.hit) continue;
+        double y = g[ray_id];
+        if (mode == ORACLE_BEER_LAMBERT) y *= exp(-ray_line_integral(&V, &ray, n_samples));
+        double dz = (ray.t1 - ray.t0) / (double)n_samples;
+        for (int k = 0; k < n_samples; ++k) {
+            double q[3];
+            long off[8];
+            double w[8];
+            sample_index(&V, &ray, dz, k, q);
+            trilinear_corners(&V, q, off, w);
+            for (int cn = 0; cn < 8; ++cn) acc[off[cn]] += y * dz * w[cn];
+        }
+    }
+    for (int i = 1; i < T; ++i) {
+        for (long x = 0; x < n_vox; ++x) grad[x] += bufs[i][x];
+        free(bufs[i]);
+    }
+    free(bufs);
+    return T;
+}
+
+/* Geometry of one ray, for pins: out = (C[3], d[3], t0, t1).  Returns 1 on a
+ * hit, 0 on a miss (t0 = t1 = 0), -1 if K is singular. */
+int oracle_ray(const double *K, const double *pose, const double *extent, int r, int c,
+               double *out)
+{
+    oracle_ray_t ray;
+    double d[3];
+    if (!pixel_direction(K, pose, r, c, d)) return -1;
+    make_ray(K, pose, extent, r, c, &ray);
+    for (int a = 0; a < 3; ++a) {
+        out[a] = ray.C[a];
+        out[3 + a] = ray.d[a];
+    }
+    out[6] = ray.t0;
+    out[7] = ray.t1;
+    return ray.hit;
+}
+
+/* The same forward with an analytic density in place of the trilinear volume:
+ * a sum of uniform balls, spheres[5 m .. 5 m + 4] = (cx, cy, cz, radius, mu).
+ * The box (extent, centred at the origin) still clips the rays.  Used to pin
+ * the geometry against the chord of a ball, 2 mu sqrt(r^2 - d^2). */
+int oracle_forward_spheres(const double *spheres, int n_spheres, const double *extent,
+                           const double *K, const double *poses, int n_views, int H, int W,
+                           int n_samples, int mode, double *out, int n_threads)
+{
+    if (n_views < 0 || H < 0 || W < 0 || n_samples < 1) return -1;
+    long n_rays = (long)n_views * H * W;
+    set_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 64)
+    for (long ray_id = 0; ray_id < n_rays; ++ray_id) {
+        int v = (int)(ray_id / ((long)H * W));
+        int r = (int)((ray_id / W) % H);
+        int c = (int)(ray_id % W);
+        oracle_ray_t ray;
+        make_ray(K, poses + 12L * v, extent, r, c, &ray);
+        double s = 0.0;
+        if (ray.hit) {
+            double dz = (ray.t1 - ray.t0) / (double)n_samples;
+            double acc = 0.0;
+            for (int k = 0; k < n_samples; ++k) {
+                double t = ray.t0 + ((double)k + 0.5) * dz;
+                double p[3];
+                for (int a = 0; a < 3; ++a) p[a] = ray.C[a] + t * ray.d[a];
+                for (int b = 0; b < n_spheres; ++b) {
+                    const double *sp = spheres + 5L * b;
+                    double r2 = 0.0;
+                    for (int a = 0; a < 3; ++a) r2 += (p[a] - sp[a]) * (p[a] - sp[a]);
+                    if (r2 <= sp[3] * sp[3]) acc += sp[4];
+                }
+            }
+            s = acc * dz;
+        }
+        out[ray_id] = output_value(s, mode);
+    }
+    return 0;
+}
+
+static int cmp_double(const void *a, const void *b)
+{
+    double x = *(const double *)a, y = *(const double *)b;
+    return (x > y) - (x < y);
+}
+
+/* The N -> infinity limit of the sampled line integral: the exact integral of
+ * the clamped trilinear field over [t0, t1].  The ray is cut wherever a
+ * continuous index q_a(t) crosses an integer in [0, n_a - 1]; on each piece
+ * every axis is either inside one cell (weight affine in t) or clamped
+ * (constant), so the field is a cubic polynomial in t and 2-point
+ * Gauss-Legendre integrates it exactly. */
+int oracle_exact_line_integral(const float *vol, int nz, int ny, int nx, const double *spacing,
+                               const double *K, const double *poses, int n_views, int H, int W,
+                               double *s_out, int n_threads)
+{
+    if (check_common(nz, ny, nx, spacing, n_views, H, W, 1, ORACLE_LINE_INTEGRAL)) return -1;
+    oracle_volume_t V;
+    volume_init(&V, vol, nz, ny, nx, spacing);
+    long n_rays = (long)n_views * H * W;
+    long max_breaks = (long)nx + ny + nz + 2;
+    const double gl = 0.5 / sqrt(3.0);
+    set_threads(n_threads);
+#pragma omp parallel
+    {
+        double *tb = (double *)malloc(sizeof(double) * (size_t)max_breaks);
+#pragma omp for schedule(dynamic, 16)
+        for (long ray_id = 0; ray_id < n_rays; ++ray_id) {
+            int v = (int)(ray_id / ((long)H * W));
+            int r = (int)((ray_id / W) % H);
+            int c = (int)(ray_id % W);
+            oracle_ray_t ray;
+            make_ray(K, poses + 12L * v, V.E, r, c, &ray);
+            if (!ray.hit || !tb) {
+                s_out[ray_id] = 0.0;
+                continue;
+            }
+            long nb = 0;
+            tb[nb++] = ray.t0;
+            for (int a = 0; a < 3; ++a) {
+                if (ray.d[a] == 0.0) continue;
+                for (long m = 0; m < V.n[a]; ++m) {
+                    /* q_a(t) = m  <=>  C_a + t d_a = (m + 1/2) s_a - E_a / 2 */
+                    double t = (((double)m + 0.5) * V.s[a] - 0.5 * V.E[a] - ray.C[a]) / ray.d[a];
+                    if (t > ray.t0 && t < ray.t1) tb[nb++] = t;
+                }
+            }
+            tb[nb++] = ray.t1;
+            qsort(tb, (size_t)nb, sizeof(double), cmp_double);
+            double s = 0.0;
+            for (long b = 0; b + 1 < nb; ++b) {
+                double len = tb[b + 1] - tb[b];
+                if (!(len > 0.0)) continue;
+                double mid = 0.5 * (tb[b] + tb[b + 1]);
+                double nodes[2] = { mid - gl * len, mid + gl * len };
+                for (int e = 0; e < 2; ++e) {
+                    double p[3], q[3];
+                    for (int a = 0; a < 3; ++a) p[a] = ray.C[a] + nodes[e] * ray.d[a];
+                    world_to_index(&V, p, q);
+                    s += 0.5 * len * trilinear(&V, q);
+                }
+            }
+            s_out[ray_id] = s;
+        }
+        free(tb);
+    }
+    return 0;
+}
+
+/* Build information for the Python loader. */
+int oracle_abi_version(void) { return 1; }
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
