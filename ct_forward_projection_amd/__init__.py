@@ -1,0 +1,215 @@
+"""Differentiable cone-beam DRR ray casting on AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libdrr.so`` (``include/drr.h``): it
+only marshals arguments -- torch tensors provide device memory and the current
+HIP stream -- and every step of the path runs in the library's HIP kernels.
+There is no CPU or PyTorch fallback: if the library is not built, or a tensor
+is not on a GPU, the call raises.
+
+Functions carry the C names (``drr_forward``, ``drr_backward_volume``,
+``drr_workspace_bytes``); ``render`` wraps them as a ``torch.autograd.Function``
+(flashdrr ``VolumeRaycaster`` style: gradients flow to the volume) and
+``project`` / ``backproject`` give diffct's A and A^T (line-integral mode).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from .build import LIBRARY
+
+F32, BF16 = 0, 1
+BEER_LAMBERT, LINE_INTEGRAL = 0, 1
+STATUS = {0: "DRR_OK", 1: "DRR_ERR_INVALID_ARGUMENT", 2: "DRR_ERR_UNSUPPORTED",
+          3: "DRR_ERR_WORKSPACE_TOO_SMALL", 4: "DRR_ERR_HIP"}
+
+_lib = None
+
+
+class DRRError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """Load the in-tree libdrr.so (built by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(f"{LIBRARY} is not built; run `python -c 'import __graft_entry__ as "
+                               "g; g.build()'` (hipcc, gfx950)")
+        lib = ctypes.CDLL(LIBRARY)
+        P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        lib.drr_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, I]
+        lib.drr_workspace_bytes.restype = Z
+        lib.drr_forward.argtypes = [P, I, I, I, I, P, P, P, I, I, I, I, I, P, P, P, Z, P]
+        lib.drr_forward.restype = I
+        lib.drr_backward_volume.argtypes = [I, I, I, P, P, P, I, I, I, I, I, P, P, P, P, Z, P]
+        lib.drr_backward_volume.restype = I
+        lib.drr_status_string.argtypes = [I]
+        lib.drr_status_string.restype = ctypes.c_char_p
+        lib.drr_last_error.restype = ctypes.c_char_p
+        lib.drr_abi_version.restype = I
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise DRRError(status, library().drr_last_error().decode())
+
+
+def _host_floats(x, n: int):
+    vals = torch.as_tensor(x, dtype=torch.float32).detach().cpu().reshape(-1)
+    if vals.numel() != n:
+        raise ValueError(f"expected {n} values, got {vals.numel()}")
+    return (ctypes.c_float * n)(*[float(v) for v in vals])
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _device_tensor(t: torch.Tensor, name: str, dtype=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _volume_dtype(volume: torch.Tensor) -> int:
+    if volume.dtype == torch.float32:
+        return F32
+    if volume.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"volume must be float32 or bfloat16, got {volume.dtype}")
+
+
+def drr_workspace_bytes(nz: int, ny: int, nx: int, dtype: int, n_views: int, det_h: int,
+                        det_w: int, n_samples: int, for_backward: int) -> int:
+    return int(library().drr_workspace_bytes(nz, ny, nx, dtype, n_views, det_h, det_w,
+                                             n_samples, for_backward))
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def drr_forward(volume: torch.Tensor, spacing: Sequence[float], K, poses: torch.Tensor,
+                det_h: int, det_w: int, n_samples: int, mode: int = BEER_LAMBERT,
+                out: Optional[torch.Tensor] = None, line_integral=True,
+                workspace: Optional[torch.Tensor] = None,
+                stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Forward DRR of ``volume`` (nz, ny, nx) for ``poses`` (V, 3, 4) world-to-camera.
+    Returns (image (V, det_h, det_w) fp32, line integrals or None)."""
+    volume = _device_tensor(volume, "volume")
+    dtype = _volume_dtype(volume)
+    poses = _device_tensor(poses, "poses", torch.float32)
+    if volume.dim() != 3 or poses.dim() != 3 or tuple(poses.shape[1:]) != (3, 4):
+        raise ValueError("volume must be (nz, ny, nx) and poses (V, 3, 4)")
+    nz, ny, nx = (int(s) for s in volume.shape)
+    V = int(poses.shape[0])
+    dev = volume.device
+    if out is None:
+        out = torch.empty((V, det_h, det_w), dtype=torch.float32, device=dev)
+    out = _device_tensor(out, "out", torch.float32)
+    if out.numel() != V * det_h * det_w:
+        raise ValueError("out has the wrong size")
+    if line_integral is True:
+        line_integral = torch.empty_like(out)
+    elif line_integral is False:
+        line_integral = None
+    if line_integral is not None:
+        line_integral = _device_tensor(line_integral, "line_integral", torch.float32)
+        if line_integral.numel() != out.numel():
+            raise ValueError("line_integral has the wrong size")
+    need = drr_workspace_bytes(nz, ny, nx, dtype, V, det_h, det_w, n_samples, 0)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().drr_forward(
+        _ptr(volume), dtype, nz, ny, nx, _host_floats(spacing, 3), _host_floats(K, 9),
+        _ptr(poses), V, det_h, det_w, n_samples, mode, _ptr(out), _ptr(line_integral),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, line_integral
+
+
+def drr_backward_volume(shape: Sequence[int], spacing: Sequence[float], K, poses: torch.Tensor,
+                        det_h: int, det_w: int, n_samples: int, mode: int,
+                        grad_out: torch.Tensor, line_integral: Optional[torch.Tensor],
+                        grad_volume: Optional[torch.Tensor] = None,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Volume gradient for upstream ``grad_out`` (V, det_h, det_w); ``line_integral``
+    (the forward's s) is required for Beer-Lambert.  Returns (nz, ny, nx) fp32."""
+    nz, ny, nx = (int(s) for s in shape)
+    poses = _device_tensor(poses, "poses", torch.float32)
+    grad_out = _device_tensor(grad_out, "grad_out", torch.float32)
+    V = int(poses.shape[0])
+    if grad_out.numel() != V * det_h * det_w:
+        raise ValueError("grad_out has the wrong size")
+    if line_integral is not None:
+        line_integral = _device_tensor(line_integral, "line_integral", torch.float32)
+    dev = grad_out.device
+    if grad_volume is None:
+        grad_volume = torch.empty((nz, ny, nx), dtype=torch.float32, device=dev)
+    grad_volume = _device_tensor(grad_volume, "grad_volume", torch.float32)
+    if grad_volume.numel() != nz * ny * nx:
+        raise ValueError("grad_volume has the wrong size")
+    need = drr_workspace_bytes(nz, ny, nx, F32, V, det_h, det_w, n_samples, 1)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().drr_backward_volume(
+        nz, ny, nx, _host_floats(spacing, 3), _host_floats(K, 9), _ptr(poses), V, det_h, det_w,
+        n_samples, mode, _ptr(grad_out), _ptr(line_integral), _ptr(grad_volume),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return grad_volume
+
+
+class _Render(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, volume, spacing, K, poses, det_h, det_w, n_samples, mode):
+        img, s = drr_forward(volume.detach(), spacing, K, poses, det_h, det_w, n_samples, mode)
+        ctx.save_for_backward(poses, s)
+        ctx.geom = (tuple(volume.shape), spacing, K, det_h, det_w, n_samples, mode, volume.dtype)
+        return img
+
+    @staticmethod
+    def backward(ctx, grad_img):
+        poses, s = ctx.saved_tensors
+        shape, spacing, K, det_h, det_w, n_samples, mode, vdtype = ctx.geom
+        g = drr_backward_volume(shape, spacing, K, poses, det_h, det_w, n_samples, mode,
+                                grad_img.contiguous().float(), s)
+        return g.to(vdtype), None, None, None, None, None, None, None
+
+
+def render(volume: torch.Tensor, spacing, K, poses: torch.Tensor, det_h: int, det_w: int,
+           n_samples: int, mode: int = BEER_LAMBERT) -> torch.Tensor:
+    """Differentiable DRR: image (V, det_h, det_w); gradients flow to ``volume``."""
+    return _Render.apply(volume, spacing, K, poses, det_h, det_w, n_samples, mode)
+
+
+def project(volume, spacing, K, poses, det_h, det_w, n_samples) -> torch.Tensor:
+    """A x: raw line integrals (diffct ``project``)."""
+    return drr_forward(volume, spacing, K, poses, det_h, det_w, n_samples, LINE_INTEGRAL,
+                       line_integral=False)[0]
+
+
+def backproject(y, shape, spacing, K, poses, det_h, det_w, n_samples) -> torch.Tensor:
+    """A^T y: the matched adjoint of ``project`` (diffct ``backproject``)."""
+    return drr_backward_volume(shape, spacing, K, poses, det_h, det_w, n_samples, LINE_INTEGRAL,
+                               y.contiguous(), None)

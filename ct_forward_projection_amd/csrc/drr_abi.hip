@@ -1,0 +1,185 @@
+// drr_abi.hip -- the extern "C" boundary of libdrr (declared in include/drr.h):
+// host-side validation, conversion of the arguments to the kernels' form and
+// launches on the caller's stream.  Nothing here allocates device memory or
+// synchronises.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/drr.h"
+#include "drr_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok()
+{
+    g_last_error[0] = '\0';
+    return DRR_OK;
+}
+
+constexpr long long kMaxDim = 16384;
+constexpr long long kMaxElems = (1LL << 31) - 1;
+constexpr long long kMaxVolumeBytes = (1LL << 32) - 1;  // 32-bit buffer offsets
+constexpr int kMaxSamples = 1 << 24;
+
+// Shared validation of the geometry arguments; fills `a` on success.
+int check_geometry(int nz, int ny, int nx, int elem_bytes, const float* spacing, const float* K,
+                   const float* poses, int n_views, int det_h, int det_w, int n_samples,
+                   int mode, drr::LaunchArgs& a)
+{
+    if (nz < 1 || ny < 1 || nx < 1)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "volume dims must be >= 1 (got %d x %d x %d)", nz,
+                    ny, nx);
+    if (nz > kMaxDim || ny > kMaxDim || nx > kMaxDim ||
+        (long long)nz * ny * nx > kMaxElems ||
+        (long long)nz * ny * nx * elem_bytes > kMaxVolumeBytes)
+        return fail(DRR_ERR_UNSUPPORTED, "volume %d x %d x %d exceeds the supported size", nz, ny,
+                    nx);
+    if (n_views < 0 || det_h < 0 || det_w < 0)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "n_views, det_h, det_w must be >= 0");
+    if ((long long)n_views * det_h * det_w > kMaxElems)
+        return fail(DRR_ERR_UNSUPPORTED, "more than 2^31 - 1 rays");
+    if (n_samples < 1)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "n_samples must be >= 1 (got %d)", n_samples);
+    if (n_samples > kMaxSamples)
+        return fail(DRR_ERR_UNSUPPORTED, "n_samples above 2^24");
+    if (mode != DRR_BEER_LAMBERT && mode != DRR_LINE_INTEGRAL)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown mode %d", mode);
+    if (!spacing) return fail(DRR_ERR_INVALID_ARGUMENT, "spacing is NULL");
+    if (!K) return fail(DRR_ERR_INVALID_ARGUMENT, "K is NULL");
+    for (int i = 0; i < 3; ++i)
+        if (!(spacing[i] > 0.0f) || !isfinite(spacing[i]))
+            return fail(DRR_ERR_INVALID_ARGUMENT, "spacing[%d] must be finite and > 0", i);
+    double k[9];
+    for (int i = 0; i < 9; ++i) {
+        if (!isfinite(K[i])) return fail(DRR_ERR_INVALID_ARGUMENT, "K[%d] is not finite", i);
+        k[i] = K[i];
+    }
+    const double det = k[0] * (k[4] * k[8] - k[5] * k[7]) - k[1] * (k[3] * k[8] - k[5] * k[6]) +
+                       k[2] * (k[3] * k[7] - k[4] * k[6]);
+    if (det == 0.0) return fail(DRR_ERR_INVALID_ARGUMENT, "K is singular");
+    const long long n_rays = (long long)n_views * det_h * det_w;
+    if (n_rays > 0 && !poses) return fail(DRR_ERR_INVALID_ARGUMENT, "poses is NULL");
+
+    const int n[3] = {nx, ny, nz};
+    for (int i = 0; i < 3; ++i) {
+        a.V.n[i] = n[i];
+        a.V.inv_s[i] = 1.0 / (double)spacing[i];
+        a.V.half_e[i] = 0.5 * (double)n[i] * (double)spacing[i];
+        a.V.q_off[i] = 0.5 * (double)(n[i] - 1);
+    }
+    a.V.row_bytes = (uint32_t)nx * (uint32_t)elem_bytes;
+    a.V.slice_bytes = (uint32_t)nx * (uint32_t)ny * (uint32_t)elem_bytes;
+    a.V.total_bytes = (uint32_t)((long long)nz * ny * nx * elem_bytes);
+    for (int i = 0; i < 9; ++i) a.K.k[i] = K[i];
+    a.poses = poses;
+    a.n_views = n_views;
+    a.H = det_h;
+    a.W = det_w;
+    a.N = n_samples;
+    a.mode = mode;
+    return DRR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int drr_abi_version(void) { return DRR_ABI_VERSION; }
+
+const char* drr_last_error(void) { return g_last_error; }
+
+const char* drr_status_string(int status)
+{
+    switch (status) {
+    case DRR_OK: return "ok";
+    case DRR_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case DRR_ERR_UNSUPPORTED: return "unsupported size or option";
+    case DRR_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DRR_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+    }
+}
+
+size_t drr_workspace_bytes(int nz, int ny, int nx, int dtype, int n_views, int det_h,
+                           int det_w, int n_samples, int for_backward)
+{
+    (void)nz; (void)ny; (void)nx; (void)dtype; (void)n_views; (void)det_h; (void)det_w;
+    (void)n_samples; (void)for_backward;
+    return 0;
+}
+
+int drr_forward(const void* volume, int dtype, int nz, int ny, int nx, const float* spacing,
+                const float* K, const float* poses, int n_views, int det_h, int det_w,
+                int n_samples, int mode, float* out, float* line_integral, void* workspace,
+                size_t workspace_bytes, void* stream)
+{
+    if (dtype != DRR_F32 && dtype != DRR_BF16)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    drr::LaunchArgs a;
+    int st = check_geometry(nz, ny, nx, dtype == DRR_F32 ? 4 : 2, spacing, K, poses, n_views,
+                            det_h, det_w, n_samples, mode, a);
+    if (st != DRR_OK) return st;
+    if (!volume) return fail(DRR_ERR_INVALID_ARGUMENT, "volume is NULL");
+    const long long n_rays = (long long)n_views * det_h * det_w;
+    if (n_rays > 0 && !out) return fail(DRR_ERR_INVALID_ARGUMENT, "out is NULL");
+    const size_t need =
+        drr_workspace_bytes(nz, ny, nx, dtype, n_views, det_h, det_w, n_samples, 0);
+    if (workspace_bytes < need)
+        return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
+                    workspace_bytes, need);
+    if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
+        return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+    if (n_rays == 0) return ok();
+    hipError_t e = drr::launch_forward(a, volume, dtype, out, line_integral,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DRR_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int drr_backward_volume(int nz, int ny, int nx, const float* spacing, const float* K,
+                        const float* poses, int n_views, int det_h, int det_w, int n_samples,
+                        int mode, const float* grad_out, const float* line_integral,
+                        float* grad_volume, void* workspace, size_t workspace_bytes,
+                        void* stream)
+{
+    drr::LaunchArgs a;
+    int st = check_geometry(nz, ny, nx, 4, spacing, K, poses, n_views, det_h, det_w, n_samples,
+                            mode, a);
+    if (st != DRR_OK) return st;
+    if (!grad_volume) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_volume is NULL");
+    const long long n_rays = (long long)n_views * det_h * det_w;
+    if (n_rays > 0 && !grad_out) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+    if (n_rays > 0 && mode == DRR_BEER_LAMBERT && !line_integral)
+        return fail(DRR_ERR_INVALID_ARGUMENT,
+                    "line_integral is required for the Beer-Lambert backward");
+    const size_t need =
+        drr_workspace_bytes(nz, ny, nx, DRR_F32, n_views, det_h, det_w, n_samples, 1);
+    if (workspace_bytes < need)
+        return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
+                    workspace_bytes, need);
+    if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
+        return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+    hipError_t e = drr::launch_backward(a, grad_out, line_integral, grad_volume,
+                                        static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DRR_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

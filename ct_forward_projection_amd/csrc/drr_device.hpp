@@ -1,0 +1,197 @@
+// drr_device.hpp -- device-side building blocks of the cone-beam DRR path for
+// gfx950: per-view camera setup, per-ray generation and box clipping, exact
+// fixed-point sample stepping, and the clamped trilinear cell of a sample.
+// Shared by the forward march and the backward scatter so both see
+// bit-identical sample positions.
+//
+// Method (source pages): nanodrr introduction (Hartley-Zisserman pinhole
+// camera, P = K [R | t]); flashdrr.rendering VolumeRaycaster.set_fov
+// (normalised per-pixel directions), __init__ (ray_samples, Beer-Lambert) and
+// class text (trilinear grid_sample gathers, differentiable in the volume).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace drr {
+
+constexpr int kTile = 16;          // a workgroup renders a 16 x 16 pixel tile
+constexpr int kWaveTile = 8;       // each wave64 renders an 8 x 8 sub-tile
+constexpr int kBlock = kTile * kTile;
+constexpr int kNumXcd = 8;         // MI355X: 8 XCDs, each with its own L2
+
+// Raw-buffer descriptor word 3 for the gfx9 family (untyped dword access).
+constexpr int kBufferWord3 = 0x00020000;
+
+struct Intrinsics {
+    float k[9];                    // row-major 3x3 K
+};
+
+// Volume description.  Sample positions are continuous voxel indices q
+// (voxel centres at integers, q = (p + E/2) / s - 1/2) kept in 32.32 fixed
+// point: the high word is floor(q), the low word the trilinear weight of the
+// upper corner in units of 2^-32.  Stepping along a ray is an exact 64-bit
+// integer add, so the only position error is the rounding of the start and of
+// the step to 2^-33 voxel (about 6e-8 voxel after 512 steps) -- far below the
+// 1e-5 voxel an fp32 position carries at |q| ~ 128, which would move a
+// low-signal ray's integral at a sharp air/tissue edge by more than 1e-5.
+struct VolumeDesc {
+    int n[3];                      // nx, ny, nz
+    double inv_s[3];               // 1 / spacing
+    double half_e[3];              // box half extent n s / 2 (mm)
+    double q_off[3];               // E / (2 s) - 1/2 = (n - 1) / 2
+    uint32_t row_bytes;            // nx * element size
+    uint32_t slice_bytes;          // nx * ny * element size
+    uint32_t total_bytes;          // whole volume (buffer range)
+};
+
+// Per-view camera, fp64: world direction of image point (u, v, 1) is
+// M (u, v, 1) with M = R^T K^-1; camera centre C = -R^T t.
+struct ViewGeom {
+    double M[9];
+    double C[3];
+};
+
+// One clipped ray: sample k sits at q = q0 + k dq (32.32 fixed point), the
+// midpoint rule t_k = t0 + (k + 1/2) dz.
+struct MarchRay {
+    int64_t q0[3];
+    int64_t dq[3];
+    float dz;                      // (t1 - t0) / N in mm
+};
+
+__device__ inline void view_setup(const float* __restrict__ pose, const Intrinsics& K,
+                                  ViewGeom& G)
+{
+    double k[9];
+#pragma unroll
+    for (int i = 0; i < 9; ++i) k[i] = (double)K.k[i];
+    // K^-1 = adj(K) / det(K)
+    const double a00 = k[4] * k[8] - k[5] * k[7];
+    const double a01 = k[2] * k[7] - k[1] * k[8];
+    const double a02 = k[1] * k[5] - k[2] * k[4];
+    const double a10 = k[5] * k[6] - k[3] * k[8];
+    const double a11 = k[0] * k[8] - k[2] * k[6];
+    const double a12 = k[2] * k[3] - k[0] * k[5];
+    const double a20 = k[3] * k[7] - k[4] * k[6];
+    const double a21 = k[1] * k[6] - k[0] * k[7];
+    const double a22 = k[0] * k[4] - k[1] * k[3];
+    const double inv_det = 1.0 / (k[0] * a00 + k[1] * a10 + k[2] * a20);
+    const double Ki[9] = {a00 * inv_det, a01 * inv_det, a02 * inv_det,
+                          a10 * inv_det, a11 * inv_det, a12 * inv_det,
+                          a20 * inv_det, a21 * inv_det, a22 * inv_det};
+    double R[9], t[3];
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+#pragma unroll
+        for (int c = 0; c < 3; ++c) R[r * 3 + c] = (double)pose[r * 4 + c];
+        t[r] = (double)pose[r * 4 + 3];
+    }
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+#pragma unroll
+        for (int b = 0; b < 3; ++b)
+            G.M[a * 3 + b] = R[0 * 3 + a] * Ki[0 * 3 + b] + R[1 * 3 + a] * Ki[1 * 3 + b] +
+                             R[2 * 3 + a] * Ki[2 * 3 + b];
+        G.C[a] = -(R[0 * 3 + a] * t[0] + R[1 * 3 + a] * t[1] + R[2 * 3 + a] * t[2]);
+    }
+}
+
+__device__ inline int64_t to_fixed(double x) { return __double2ll_rn(x * 4294967296.0); }
+
+// Ray through pixel (r, c), clipped to the volume box by the slab method in
+// fp64.  Returns false when the ray misses (t1 <= t0 with t0 = max(t_entry, 0)).
+__device__ inline bool ray_setup(const ViewGeom& G, const VolumeDesc& V, int r, int c, int N,
+                                 MarchRay& R)
+{
+    const double u = (double)c + 0.5, v = (double)r + 0.5;
+    double d[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) d[a] = G.M[a * 3 + 0] * u + G.M[a * 3 + 1] * v + G.M[a * 3 + 2];
+    const double inv_len = 1.0 / sqrt(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
+    double t_entry = -__builtin_inf(), t_exit = __builtin_inf();
+    bool inside = true;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        d[a] *= inv_len;
+        const double lo = -V.half_e[a], hi = V.half_e[a];
+        if (d[a] == 0.0) {
+            inside = inside && !(G.C[a] < lo || G.C[a] > hi);
+        } else {
+            const double ta = (lo - G.C[a]) / d[a];
+            const double tb = (hi - G.C[a]) / d[a];
+            t_entry = fmax(t_entry, fmin(ta, tb));
+            t_exit = fmin(t_exit, fmax(ta, tb));
+        }
+    }
+    const double t0 = fmax(t_entry, 0.0);
+    if (!inside || !(t_exit > t0)) return false;
+    const double dz = (t_exit - t0) / (double)N;
+    const double ts = t0 + 0.5 * dz;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        R.q0[a] = to_fixed((G.C[a] + ts * d[a]) * V.inv_s[a] + V.q_off[a]);
+        R.dq[a] = to_fixed(dz * d[a] * V.inv_s[a]);
+    }
+    R.dz = (float)dz;
+    return true;
+}
+
+__device__ inline int fixed_floor(int64_t q) { return (int)(q >> 32); }
+
+__device__ inline float fixed_frac(int64_t q)
+{
+    return (float)(uint32_t)q * 2.3283064365386963e-10f;  // 2^-32
+}
+
+__device__ inline int clampi(int i, int lo, int hi) { return min(max(i, lo), hi); }
+
+// Clamped trilinear cell of a sample: both corner indices per axis clamped to
+// [0, n-1] (clamp to edge) and the weights of the upper corners.
+struct Cell {
+    int x0, x1, y0, y1, z0, z1;
+    float fx, fy, fz;
+};
+
+__device__ inline void cell_of(const VolumeDesc& V, int64_t qx, int64_t qy, int64_t qz, Cell& C)
+{
+    const int ix = fixed_floor(qx), iy = fixed_floor(qy), iz = fixed_floor(qz);
+    C.fx = fixed_frac(qx);
+    C.fy = fixed_frac(qy);
+    C.fz = fixed_frac(qz);
+    C.x0 = clampi(ix, 0, V.n[0] - 1);
+    C.x1 = clampi(ix + 1, 0, V.n[0] - 1);
+    C.y0 = clampi(iy, 0, V.n[1] - 1);
+    C.y1 = clampi(iy + 1, 0, V.n[1] - 1);
+    C.z0 = clampi(iz, 0, V.n[2] - 1);
+    C.z1 = clampi(iz + 1, 0, V.n[2] - 1);
+}
+
+// Map a hardware workgroup id to a logical tile so that the workgroups one XCD
+// receives (ids x, x + 8, x + 16, ...) own one contiguous run of tiles: every
+// XCD's L2 then serves a compact part of the detector, and so of the volume.
+__device__ inline int xcd_contiguous_tile(int bid, int nblocks)
+{
+    const int xcd = bid % kNumXcd, idx = bid / kNumXcd;
+    const int per = nblocks / kNumXcd, rem = nblocks % kNumXcd;
+    return xcd * per + min(xcd, rem) + idx;
+}
+
+// Pixel owned by this thread: 16 x 16 tiles, four 8 x 8 wave sub-tiles.
+struct PixelCoord {
+    int view, r, c;
+};
+
+__device__ inline PixelCoord tile_pixel(int tile, int tiles_x, int tiles_per_view)
+{
+    PixelCoord p;
+    p.view = tile / tiles_per_view;
+    const int t = tile - p.view * tiles_per_view;
+    const int ty = t / tiles_x, tx = t - ty * tiles_x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    p.r = ty * kTile + (wave >> 1) * kWaveTile + (lane >> 3);
+    p.c = tx * kTile + (wave & 1) * kWaveTile + (lane & 7);
+    return p;
+}
+
+}  // namespace drr

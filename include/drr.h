@@ -1,0 +1,133 @@
+/*
+ * drr.h -- C ABI of libdrr: differentiable cone-beam DRR ray casting on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (source pages):
+ *   - nanodrr project page, introduction: rays come from a Hartley-Zisserman
+ *     pinhole camera, intrinsics K and a world-to-camera pose [R | t].
+ *   - flashdrr.rendering API, VolumeRaycaster.__init__ and set_fov: ray_samples
+ *     samples per ray along normalised per-pixel directions; with
+ *     use_beer_lambert the image is 1 - exp(-integral of mu dz).
+ *   - flashdrr.rendering API, VolumeRaycaster class text: samples are
+ *     trilinear gathers of the volume; rendering is differentiable with
+ *     respect to the volume.
+ *   - diffct 2.1.0, Quickstart: project() returns raw line integrals and
+ *     backproject() applies the matched adjoint A^T.
+ *   - torchtomo, "Fast CUDA Kernels": kernels are launched on the caller's
+ *     current stream.
+ *
+ * Conventions (readings where the pages are silent):
+ *   - units: mm for geometry, 1/mm for mu; ray directions are unit vectors;
+ *   - the volume vol[k][j][i] (x fastest, shape nz x ny x nx) fills the box
+ *     [-E/2, E/2], E = (nx sx, ny sy, nz sz), centred at the world origin;
+ *   - pixel (r, c) of a det_h x det_w detector is the image point
+ *     (c + 1/2, r + 1/2, 1); its world ray is C + t d with
+ *     d = normalize(R^T K^-1 (c + 1/2, r + 1/2, 1)) and C = -R^T t;
+ *   - each ray is clipped to the box: t0 = max(t_entry, 0), t1 = t_exit; a ray
+ *     with t1 <= t0 misses and produces exactly 0 and no gradient;
+ *   - n_samples midpoint samples t_k = t0 + (k + 1/2) dz, dz = (t1 - t0) / N,
+ *     each a trilinear interpolation with corner indices clamped to the
+ *     volume (clamp to edge);
+ *   - s = dz * sum_k mu(t_k); Beer-Lambert output 1 - exp(-s) (computed as
+ *     -expm1(-s)), line-integral output s.
+ *
+ * Ownership and errors:
+ *   - every buffer is owned by the caller; the library never allocates,
+ *     frees or synchronises device memory, and keeps no state between calls;
+ *   - calls are asynchronous: work is enqueued on `stream` (a hipStream_t;
+ *     NULL = the default stream) and the call returns without waiting;
+ *   - arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns a non-zero drr_status and enqueues nothing;
+ *   - a failed kernel launch returns DRR_ERR_HIP; faults inside a kernel
+ *     surface at the caller's next synchronisation;
+ *   - drr_last_error() gives a thread-local description of the last failure;
+ *   - no C++ exception crosses this interface; calls are reentrant.
+ */
+#ifndef DRR_H
+#define DRR_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DRR_ABI_VERSION 1
+
+/* Volume element types.  bf16 volumes are read as bf16 and widened exactly
+ * to fp32; every sum is accumulated in fp32. */
+typedef enum { DRR_F32 = 0, DRR_BF16 = 1 } drr_dtype;
+
+/* Output modes: Beer-Lambert image 1 - exp(-s) (flashdrr use_beer_lambert) or
+ * the raw line integral s (diffct project). */
+typedef enum { DRR_BEER_LAMBERT = 0, DRR_LINE_INTEGRAL = 1 } drr_mode;
+
+typedef enum {
+    DRR_OK = 0,
+    DRR_ERR_INVALID_ARGUMENT = 1,     /* null pointer, bad size, bad enum ... */
+    DRR_ERR_UNSUPPORTED = 2,          /* valid but beyond the documented limits */
+    DRR_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < drr_workspace_bytes(...) */
+    DRR_ERR_HIP = 4                   /* a HIP runtime call or launch failed */
+} drr_status;
+
+/* Limits: 1 <= nx, ny, nz <= 16384 with nx*ny*nz < 2^31 voxels and the
+ * volume (and, for the backward, the fp32 gradient) smaller than 4 GiB;
+ * 0 <= n_views, det_h, det_w and n_views*det_h*det_w < 2^31 rays;
+ * 1 <= n_samples <= 2^24. */
+
+/* Bytes of device workspace drr_forward (for_backward = 0) or
+ * drr_backward_volume (for_backward = 1) needs for these sizes; 0 means no
+ * workspace is needed (a NULL workspace is then accepted).  Returns 0 as well
+ * for invalid sizes (the call itself then reports the error). */
+size_t drr_workspace_bytes(int nz, int ny, int nx, int dtype, int n_views, int det_h,
+                           int det_w, int n_samples, int for_backward);
+
+/* Forward DRR (flashdrr VolumeRaycaster.forward / diffct project).
+ *   volume        device, nz*ny*nx elements of `dtype`, C-contiguous, x fastest
+ *   spacing       host, 3 floats: sx, sy, sz (mm), each > 0
+ *   K             host, 9 floats, row-major 3x3 intrinsics (invertible)
+ *   poses         device, n_views x 12 floats: row-major 3x4 world-to-camera [R | t]
+ *   det_h, det_w  detector rows and columns
+ *   n_samples     samples per ray (N)
+ *   mode          DRR_BEER_LAMBERT or DRR_LINE_INTEGRAL
+ *   out           device, n_views*det_h*det_w floats, [view][row][col]
+ *   line_integral device or NULL: receives s in the same layout (the
+ *                 Beer-Lambert backward needs it)
+ *   workspace     device, workspace_bytes >= drr_workspace_bytes(..., 0), 256-byte aligned
+ * n_views, det_h or det_w equal to 0 is a valid empty call. */
+int drr_forward(const void *volume, int dtype, int nz, int ny, int nx, const float *spacing,
+                const float *K, const float *poses, int n_views, int det_h, int det_w,
+                int n_samples, int mode, float *out, float *line_integral, void *workspace,
+                size_t workspace_bytes, void *stream);
+
+/* Volume gradient of the forward (flashdrr autograd backward / diffct
+ * backproject): for upstream dL/dI = grad_out,
+ *   y_p = grad_out_p * exp(-s_p)  (Beer-Lambert; s from the forward's line_integral)
+ *   y_p = grad_out_p              (line integral; this is exactly A^T grad_out)
+ * and every sample adds y_p * dz * w_corner to each of its 8 trilinear corners.
+ *   grad_out      device, n_views*det_h*det_w floats
+ *   line_integral device, same layout; required for Beer-Lambert, ignored (may be
+ *                 NULL) for the line integral
+ *   grad_volume   device, nz*ny*nx floats, OVERWRITTEN (zeroed, then accumulated)
+ * The volume itself is not needed.  Accumulation uses fp32 atomics, so the
+ * result may differ between runs in the last bits. */
+int drr_backward_volume(int nz, int ny, int nx, const float *spacing, const float *K,
+                        const float *poses, int n_views, int det_h, int det_w, int n_samples,
+                        int mode, const float *grad_out, const float *line_integral,
+                        float *grad_volume, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
+/* Static description of a drr_status value. */
+const char *drr_status_string(int status);
+
+/* Thread-local description of the last failing call on this thread ("" if none). */
+const char *drr_last_error(void);
+
+/* DRR_ABI_VERSION of the loaded library. */
+int drr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DRR_H */

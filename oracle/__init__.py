@@ -60,6 +60,8 @@ def _load():
     lib.oracle_forward_spheres.restype = I
     lib.oracle_exact_line_integral.argtypes = [P, I, I, I, P, P, P, I, I, I, P, I]
     lib.oracle_exact_line_integral.restype = I
+    lib.oracle_chords.argtypes = [P, P, P, I, I, I, P, I]
+    lib.oracle_chords.restype = I
     lib.oracle_max_threads.restype = I
     _lib = lib
     return lib
@@ -128,6 +130,26 @@ def ray(K, pose, extent, r: int, c: int):
     if hit < 0:
         raise ValueError("singular K")
     return bool(hit), out[0:3].copy(), out[3:6].copy(), float(out[6]), float(out[7])
+
+
+def chords(extent, K, poses, det_h: int, det_w: int, n_threads: Optional[int] = None):
+    """Clipped chord length t1 - t0 of every ray, 0 where the ray misses the box."""
+    lib = _load()
+    Kd, Pd = _f64(K), _f64(poses).reshape(-1, 12)
+    V = Pd.shape[0]
+    out = np.zeros((V, det_h, det_w), dtype=np.float64)
+    rc = lib.oracle_chords(_ptr(np.ascontiguousarray(extent, dtype=np.float64)), _ptr(Kd),
+                           _ptr(Pd), V, det_h, det_w, _ptr(out), _threads(n_threads))
+    if rc != 0:
+        raise ValueError("oracle_chords: invalid arguments")
+    return out
+
+
+def chords_workload(w, n_threads: Optional[int] = None):
+    sp = np.asarray(w.spacing, dtype=np.float32).astype(np.float64)
+    nz, ny, nx = w.volume.shape
+    extent = np.array([nx * sp[0], ny * sp[1], nz * sp[2]])
+    return chords(extent, w.K, w.poses, w.det_h, w.det_w, n_threads)
 
 
 def forward_spheres(spheres, extent, K, poses, det_h: int, det_w: int, n_samples: int,

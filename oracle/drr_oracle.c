@@ -392,6 +392,26 @@ int oracle_ray(const double *K, const double *pose, const double *extent, int r,
     return ray.hit;
 }
 
+/* Clipped chord length t1 - t0 of every ray (0 for a miss): which rays the
+ * forward integrates at all.  Pinned by the constant-box chords. */
+int oracle_chords(const double *extent, const double *K, const double *poses, int n_views,
+                  int H, int W, double *chord, int n_threads)
+{
+    if (n_views < 0 || H < 0 || W < 0) return -1;
+    long n_rays = (long)n_views * H * W;
+    set_threads(n_threads);
+#pragma omp parallel for schedule(dynamic, 256)
+    for (long ray_id = 0; ray_id < n_rays; ++ray_id) {
+        int v = (int)(ray_id / ((long)H * W));
+        int r = (int)((ray_id / W) % H);
+        int c = (int)(ray_id % W);
+        oracle_ray_t ray;
+        make_ray(K, poses + 12L * v, extent, r, c, &ray);
+        chord[ray_id] = ray.hit ? ray.t1 - ray.t0 : 0.0;
+    }
+    return 0;
+}
+
 /* The same forward with an analytic density in place of the trilinear volume:
  * a sum of uniform balls, spheres[5 m .. 5 m + 4] = (cx, cy, cz, radius, mu).
  * The box (extent, centred at the origin) still clips the rays.  Used to pin

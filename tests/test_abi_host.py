@@ -1,0 +1,118 @@
+"""The C-ABI library loads, exports every symbol include/drr.h declares, and
+rejects invalid calls on the host before anything touches a GPU.  Runs without
+a GPU: every call here returns from host validation."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ct_forward_projection_amd as drr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "drr.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(drr_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = drr.library()
+    names = declared_functions()
+    assert {"drr_forward", "drr_backward_volume", "drr_workspace_bytes", "drr_status_string",
+            "drr_last_error", "drr_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.drr_abi_version() == 1
+
+
+def test_status_strings():
+    lib = drr.library()
+    for code, text in [(0, b"ok"), (1, b"invalid argument"), (3, b"workspace too small"),
+                       (4, b"HIP runtime error"), (99, b"unknown status")]:
+        assert lib.drr_status_string(code) == text
+
+
+def _f(*v):
+    return (ctypes.c_float * len(v))(*v)
+
+
+SP = _f(1.0, 1.0, 1.0)
+K = _f(500.0, 0.0, 32.0, 0.0, 500.0, 32.0, 0.0, 0.0, 1.0)
+DUMMY = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def fwd(**kw):
+    args = dict(volume=DUMMY, dtype=0, nz=8, ny=8, nx=8, spacing=SP, K=K, poses=DUMMY,
+                n_views=1, det_h=4, det_w=4, n_samples=8, mode=0, out=DUMMY, s=None,
+                ws=None, ws_bytes=0, stream=None)
+    args.update(kw)
+    lib = drr.library()
+    return lib.drr_forward(args["volume"], args["dtype"], args["nz"], args["ny"], args["nx"],
+                           args["spacing"], args["K"], args["poses"], args["n_views"],
+                           args["det_h"], args["det_w"], args["n_samples"], args["mode"],
+                           args["out"], args["s"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+def bwd(**kw):
+    args = dict(nz=8, ny=8, nx=8, spacing=SP, K=K, poses=DUMMY, n_views=1, det_h=4, det_w=4,
+                n_samples=8, mode=0, g=DUMMY, s=DUMMY, grad=DUMMY, ws=None, ws_bytes=0,
+                stream=None)
+    args.update(kw)
+    lib = drr.library()
+    return lib.drr_backward_volume(args["nz"], args["ny"], args["nx"], args["spacing"], args["K"],
+                                   args["poses"], args["n_views"], args["det_h"], args["det_w"],
+                                   args["n_samples"], args["mode"], args["g"], args["s"],
+                                   args["grad"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nz=0), 1), (dict(ny=-3), 1), (dict(nx=20000), 2),
+    (dict(nz=2048, ny=2048, nx=1024), 2),
+    (dict(n_views=-1), 1), (dict(det_h=-1), 1),
+    (dict(n_samples=0), 1), (dict(n_samples=(1 << 24) + 1), 2),
+    (dict(mode=2), 1), (dict(dtype=3), 1),
+    (dict(volume=None), 1), (dict(poses=None), 1), (dict(out=None), 1),
+    (dict(spacing=None), 1), (dict(K=None), 1),
+    (dict(spacing=_f(1.0, 0.0, 1.0)), 1), (dict(spacing=_f(1.0, -2.0, 1.0)), 1),
+    (dict(spacing=_f(1.0, float("nan"), 1.0)), 1),
+    (dict(K=_f(1, 2, 3, 2, 4, 6, 0, 0, 1)), 1),            # singular
+    (dict(K=_f(500, 0, 32, 0, float("inf"), 32, 0, 0, 1)), 1),
+    (dict(n_views=65536, det_h=256, det_w=256), 2),          # > 2^31 rays
+])
+def test_forward_rejects_invalid_arguments(kw, status):
+    assert fwd(**kw) == status
+    assert drr.library().drr_last_error() != b""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nz=0), 1), (dict(n_samples=0), 1), (dict(mode=-1), 1),
+    (dict(grad=None), 1), (dict(g=None), 1), (dict(s=None), 1),  # BL needs line integrals
+    (dict(poses=None), 1), (dict(spacing=_f(0.0, 1.0, 1.0)), 1),
+])
+def test_backward_rejects_invalid_arguments(kw, status):
+    assert bwd(**kw) == status
+
+
+def test_empty_forward_is_a_valid_no_op():
+    # nothing to render: returns OK without touching the device
+    assert fwd(n_views=0, poses=None, out=None) == 0
+    assert fwd(det_h=0) == 0
+    assert drr.library().drr_last_error() == b""
+
+
+def test_workspace_query_is_consistent():
+    for args in [(64, 64, 64, 0, 1, 64, 64, 128, 0), (256, 256, 256, 1, 16, 200, 200, 256, 0),
+                 (128, 128, 128, 0, 360, 256, 384, 256, 1)]:
+        n = drr.drr_workspace_bytes(*args)
+        assert n >= 0 and n % 256 == 0
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        drr.drr_forward(torch.zeros(4, 4, 4), [1, 1, 1], torch.eye(3), torch.zeros(1, 3, 4),
+                        4, 4, 8)

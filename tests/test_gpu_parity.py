@@ -1,0 +1,303 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle, on the
+same seeded inputs.
+
+Bars (floating point; the oracle is fp64):
+  * forward, fp32 volume:   max |g - o| / max(|o|, 1e-3 max|o|) <= 1e-5
+  * forward, bf16 volume:   <= 1e-2 against the oracle on the fp32 volume and
+                            <= 1e-5 against the oracle on the bf16-rounded volume
+                            (fp32 accumulation, no bf16 arithmetic)
+  * volume gradient:        max |g - o| / max |o| <= 1e-4 (normwise)
+  * misses:                 exactly 0 wherever the oracle's ray misses the box
+The full-size workloads run in the launch configuration the benchmark times;
+where the oracle cannot afford a whole workload it checks a subset of views,
+and properties (the adjoint identity) cover the rest at full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import ct_forward_projection_amd as drr
+import oracle
+import workloads as W
+from helpers import forward_rel_err, l2_err, normwise_err, say
+
+pytestmark = pytest.mark.gpu
+
+FWD_F32 = 1e-5
+FWD_BF16 = 1e-2
+GRAD = 1e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def gpu_forward(w, dev, bf16=False, stream=None):
+    if bf16:
+        vol = torch.from_numpy(w.volume_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        vol = torch.from_numpy(w.volume).to(dev)
+    poses = torch.from_numpy(w.poses).to(dev)
+    img, s = drr.drr_forward(vol, w.spacing, w.K, poses, w.det_h, w.det_w, w.n_samples, w.mode,
+                             stream=stream)
+    torch.cuda.synchronize()
+    return img, s
+
+
+def gpu_backward(w, dev, s, g):
+    poses = torch.from_numpy(w.poses).to(dev)
+    grad = drr.drr_backward_volume(w.volume.shape, w.spacing, w.K, poses, w.det_h, w.det_w,
+                                   w.n_samples, w.mode, torch.from_numpy(g).to(dev), s)
+    torch.cuda.synchronize()
+    return grad.cpu().double().numpy()
+
+
+def check_forward(img_gpu, ref, bar, what, chord=None):
+    """Floored max relative error within ``bar``; rays the oracle finds missing
+    the box (chord 0) must be exactly 0 on the GPU as well."""
+    g = img_gpu.cpu().double().numpy() if torch.is_tensor(img_gpu) else img_gpu
+    err = forward_rel_err(g, ref)
+    say(f"{what}: forward max rel err {err:.3e} (bar {bar:g}), "
+        f"normwise {normwise_err(g, ref):.3e}")
+    assert err <= bar
+    if chord is not None:
+        miss = chord == 0.0
+        assert np.all(g[miss] == 0.0), f"{what}: misses must be exactly 0"
+        say(f"{what}: {int(miss.sum())} misses, all exactly 0")
+    return err
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def test_tiny_workload_forward(dev):
+    w = W.make_workload(1)
+    say("case: tiny 64^3 forward BL")
+    img, s = gpu_forward(w, dev)
+    ref, ref_s = oracle.forward_workload(w)
+    check_forward(img, ref, FWD_F32, "tiny", oracle.chords_workload(w))
+    check_forward(s, ref_s, FWD_F32, "tiny s")
+
+
+def test_tiny_workload_backward(dev):
+    w = W.make_workload(1)
+    say("case: tiny 64^3 backward BL")
+    g = np.random.default_rng(1).uniform(-1, 1, size=(1, 64, 64)).astype(np.float32)
+    _, s = gpu_forward(w, dev)
+    grad = gpu_backward(w, dev, s, g)
+    ref, _ = oracle.adjoint_workload(w, grad_out=g)
+    err = normwise_err(grad, ref)
+    say(f"tiny: gradient normwise err {err:.3e}, l2 {l2_err(grad, ref):.3e}")
+    assert err <= GRAD
+
+
+@pytest.fixture(scope="module")
+def batch_workload():
+    return W.make_workload(2, with_bf16=True)
+
+
+def test_nanodrr_batch_forward_fp32(dev, batch_workload):
+    w = batch_workload
+    say("case: batch 256^3 x 16 views 200x200 fp32")
+    img, s = gpu_forward(w, dev)
+    ref, _ = oracle.forward_workload(w)
+    check_forward(img, ref, FWD_F32, "batch fp32", oracle.chords_workload(w))
+
+
+def test_nanodrr_batch_forward_bf16(dev, batch_workload):
+    w = batch_workload
+    say("case: batch 256^3 x 16 views 200x200 bf16")
+    img, _ = gpu_forward(w, dev, bf16=True)
+    ref32, _ = oracle.forward_workload(w)
+    ref16, _ = oracle.forward_workload(w, use_bf16=True)
+    check_forward(img, ref32, FWD_BF16, "batch bf16 vs fp32 oracle")
+    check_forward(img, ref16, FWD_F32, "batch bf16 vs bf16-rounded oracle")
+
+
+def test_train_step_forward_and_backward(dev):
+    w = W.make_workload(3)
+    say("case: train step 256^3 1024x1024 512 samples fwd+bwd")
+    img, s = gpu_forward(w, dev)
+    ref, ref_s = oracle.forward_workload(w)
+    check_forward(img, ref, FWD_F32, "train fwd", oracle.chords_workload(w))
+    grad = gpu_backward(w, dev, s, w.grad_out)
+    ref_g, _ = oracle.adjoint_workload(w)
+    err = normwise_err(grad, ref_g)
+    say(f"train: gradient normwise err {err:.3e}, l2 {l2_err(grad, ref_g):.3e}")
+    assert err <= GRAD
+
+
+def test_hires_forward(dev):
+    w = W.make_workload(4)
+    say("case: hires 256^3 2048x2048 256 samples fwd")
+    img, _ = gpu_forward(w, dev)
+    ref, _ = oracle.forward_workload(w)
+    check_forward(img, ref, FWD_F32, "hires", oracle.chords_workload(w))
+
+
+@pytest.fixture(scope="module")
+def helix():
+    return W.make_workload(5)
+
+
+SAMPLED_VIEWS = np.arange(0, 360, 15)
+
+
+def test_cbct_helix_forward_sampled_views(dev, helix):
+    """All 360 views render in one launch; 24 of them are checked view by view."""
+    w = helix
+    say("case: helix 128^3 360 views 256x384 RAW fwd")
+    img, _ = gpu_forward(w, dev)
+    sub = w.subset_views(SAMPLED_VIEWS)
+    ref, _ = oracle.forward_workload(sub)
+    check_forward(img[torch.from_numpy(SAMPLED_VIEWS).to(dev)], ref, FWD_F32, "helix views",
+                  oracle.chords_workload(sub))
+
+
+def test_cbct_helix_backward(dev, helix):
+    """The gradient of the sampled views against the oracle, and the adjoint
+    identity <A x, y> = <x, A^T y> at the full 360-view size on the GPU."""
+    w = helix
+    say("case: helix backward (24 sampled views)")
+    sub = w.subset_views(SAMPLED_VIEWS)
+    _, s = gpu_forward(sub, dev)
+    grad = gpu_backward(sub, dev, s, sub.grad_out)
+    ref, _ = oracle.adjoint_workload(sub)
+    err = normwise_err(grad, ref)
+    say(f"helix sampled: gradient normwise err {err:.3e}")
+    assert err <= GRAD
+
+    say("case: helix full-size adjoint identity")
+    x = torch.from_numpy(w.volume).to(dev)
+    poses = torch.from_numpy(w.poses).to(dev)
+    y = torch.from_numpy(w.grad_out).to(dev)
+    ax = drr.project(x, w.spacing, w.K, poses, w.det_h, w.det_w, w.n_samples)
+    aty = drr.backproject(y, w.volume.shape, w.spacing, w.K, poses, w.det_h, w.det_w,
+                          w.n_samples)
+    lhs = float((ax.double() * y.double()).sum())
+    rhs = float((x.double() * aty.double()).sum())
+    say(f"helix: <Ax,y> = {lhs:.9e}, <x,A^T y> = {rhs:.9e}, rel {abs(lhs - rhs) / abs(lhs):.2e}")
+    assert abs(lhs - rhs) <= 1e-5 * abs(lhs)
+
+
+# ------------------------------------------------------------------ ragged and edge cases
+
+@pytest.mark.parametrize("seed,mode,shape,det,n", [
+    (1, W.BEER_LAMBERT, (7, 9, 11), (13, 17), 37),
+    (2, W.LINE_INTEGRAL, (16, 5, 33), (40, 23), 64),
+    (3, W.BEER_LAMBERT, (1, 12, 12), (17, 33), 5),
+    (4, W.LINE_INTEGRAL, (20, 20, 1), (9, 50), 1),
+    (5, W.BEER_LAMBERT, (31, 29, 27), (65, 47), 203),
+])
+def test_random_ragged_workloads(dev, seed, mode, shape, det, n):
+    """Tiles with ragged tails, anisotropic voxels, degenerate (1-voxel-thick)
+    volumes, N = 1 and N not a multiple of the unroll."""
+    w = W.make_random_small(seed, shape=shape, n_views=3, det=det, n_samples=n, mode=mode)
+    say(f"case: random seed={seed} mode={mode} shape={shape} det={det} N={n}")
+    img, s = gpu_forward(w, dev)
+    ref, ref_s = oracle.forward_workload(w)
+    check_forward(img, ref, FWD_F32, f"random {seed}", oracle.chords_workload(w))
+    grad = gpu_backward(w, dev, s, w.grad_out)
+    ref_g, _ = oracle.adjoint_workload(w)
+    err = normwise_err(grad, ref_g)
+    say(f"random {seed}: gradient normwise err {err:.3e}")
+    assert err <= GRAD
+
+
+def test_all_rays_miss(dev):
+    w = W.make_random_small(11, n_views=2)
+    w.poses = np.stack([W.pose_from_rotation_and_centre(np.diag([1.0, -1.0, -1.0]),
+                                                        [0.0, 0.0, -200.0])] * 2)
+    say("case: all rays miss")
+    img, s = gpu_forward(w, dev)
+    assert torch.count_nonzero(img).item() == 0 and torch.count_nonzero(s).item() == 0
+    grad = gpu_backward(w, dev, s, w.grad_out)
+    assert not grad.any()
+
+
+def test_source_inside_the_volume(dev):
+    w = W.make_random_small(12, shape=(20, 20, 20), n_views=2, det=(21, 21), n_samples=50,
+                            distance=3.0)
+    say("case: sources inside the volume")
+    img, s = gpu_forward(w, dev)
+    ref, _ = oracle.forward_workload(w)
+    check_forward(img, ref, FWD_F32, "inside")
+    grad = gpu_backward(w, dev, s, w.grad_out)
+    ref_g, _ = oracle.adjoint_workload(w)
+    assert normwise_err(grad, ref_g) <= GRAD
+
+
+def test_empty_inputs(dev):
+    say("case: empty inputs")
+    vol = torch.rand(8, 8, 8, device=dev)
+    poses = torch.zeros(0, 3, 4, device=dev)
+    img, s = drr.drr_forward(vol, [1, 1, 1], W.intrinsics(10, 2, 2), poses, 4, 4, 8)
+    assert img.shape == (0, 4, 4)
+    # the backward overwrites: with no rays the gradient is all zeros
+    grad = torch.full((8, 8, 8), 7.0, device=dev)
+    drr.drr_backward_volume((8, 8, 8), [1, 1, 1], W.intrinsics(10, 2, 2), poses, 4, 4, 8,
+                            drr.LINE_INTEGRAL, torch.zeros(0, 4, 4, device=dev), None,
+                            grad_volume=grad)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(grad).item() == 0
+
+
+def test_many_samples(dev):
+    w = W.make_random_small(13, shape=(10, 12, 14), n_views=1, det=(8, 8), n_samples=5000)
+    say("case: N = 5000")
+    img, s = gpu_forward(w, dev)
+    ref, _ = oracle.forward_workload(w)
+    check_forward(img, ref, FWD_F32, "N=5000")
+
+
+def test_forward_is_deterministic(dev):
+    w = W.make_workload(1)
+    a, _ = gpu_forward(w, dev)
+    b, _ = gpu_forward(w, dev)
+    assert torch.equal(a, b)
+
+
+def test_backward_is_stable_run_to_run(dev):
+    w = W.make_random_small(14, shape=(24, 24, 24), n_views=4, det=(48, 48), n_samples=96)
+    _, s = gpu_forward(w, dev)
+    g1 = gpu_backward(w, dev, s, w.grad_out)
+    g2 = gpu_backward(w, dev, s, w.grad_out)
+    assert normwise_err(g1, g2) <= 1e-6
+
+
+def test_autograd_render_matches_abi(dev):
+    w = W.make_random_small(15, shape=(12, 14, 16), n_views=2, det=(20, 24), n_samples=40)
+    say("case: autograd")
+    vol = torch.from_numpy(w.volume).to(dev).requires_grad_(True)
+    poses = torch.from_numpy(w.poses).to(dev)
+    img = drr.render(vol, w.spacing, w.K, poses, w.det_h, w.det_w, w.n_samples, w.mode)
+    g = torch.from_numpy(w.grad_out).to(dev)
+    (img * g).sum().backward()
+    ref_g, _ = oracle.adjoint_workload(w)
+    assert normwise_err(vol.grad.cpu().numpy(), ref_g) <= GRAD
+
+
+def test_least_squares_gradient_is_At_residual(dev):
+    """diffct Quickstart: for 0.5 ||A x - y||^2, x.grad = A^T (A x - y)."""
+    w = W.make_random_small(16, shape=(10, 11, 12), n_views=3, det=(15, 16), n_samples=30,
+                            mode=W.LINE_INTEGRAL)
+    x = torch.from_numpy(w.volume).to(dev).requires_grad_(True)
+    poses = torch.from_numpy(w.poses).to(dev)
+    y = torch.from_numpy(w.grad_out).to(dev)
+    ax = drr.render(x, w.spacing, w.K, poses, w.det_h, w.det_w, w.n_samples, drr.LINE_INTEGRAL)
+    (0.5 * (ax - y).square().sum()).backward()
+    r = (ax.detach().cpu().double().numpy() - w.grad_out)
+    ref, _ = oracle.adjoint(None, w.volume.shape, w.spacing, w.K, w.poses, w.det_h, w.det_w,
+                            w.n_samples, W.LINE_INTEGRAL, r)
+    assert normwise_err(x.grad.cpu().numpy(), ref) <= GRAD
+
+
+def test_runs_on_a_non_default_stream(dev):
+    w = W.make_workload(1)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        img, _ = gpu_forward(w, dev, stream=st)
+    ref, _ = oracle.forward_workload(w)
+    check_forward(img, ref, FWD_F32, "side stream")

@@ -118,6 +118,13 @@ def test_constant_box_equals_mu_times_chord_for_every_N(seed):
                     assert s[v, r, c] == pytest.approx(mu_c * L, rel=1e-11, abs=1e-11 * ext)
                     assert img[v, r, c] == pytest.approx(-math.expm1(-mu_c * L), rel=1e-11,
                                                          abs=1e-13)
+        ch = oracle.chords(E, K, poses, H, Wd)
+        for v in range(3):
+            C = centre(poses[v])
+            for r in range(H):
+                for c in range(Wd):
+                    L = chord_by_faces(C, direction(K, poses[v], r, c), E)
+                    assert ch[v, r, c] == pytest.approx(L, rel=1e-11, abs=1e-11 * ext)
     assert hits > 100  # the geometry really exercises the box
 
 
