@@ -1,0 +1,303 @@
+#!/usr/bin/env python3
+"""Throughput of the cone-beam DRR hot path on one MI355X.
+
+A step is one FlashDRR-style train step on the 1024x1024 workload (256^3 fp32
+phantom, one view, 512 samples per ray, Beer-Lambert): the forward DRR
+(ray setup, box clip, march, epilogue) followed by the volume backward (fill,
+scatter) -- every stage of the path, on inputs already resident in HBM.
+
+Printed (one JSON line on stdout):
+  value        rays x samples per second of the step (nominal: every pixel's
+               ray counts N samples), in Gsamples/s
+  fps          views per second of the step
+  roofline     the dominant kernel against the 8 TB/s HBM peak, on
+               algorithmic bytes (8 corners x element bytes per sample on rays
+               that hit the volume, plus per-ray reads/writes), with its
+               duration measured by HIP events on the launch stream
+  cpu_baseline the CPU oracle on the same step, timed on the host cores
+  workloads    the other workloads (200x200 16-view batch in fp32 and bf16,
+               2048^2 eval, 360-view helix, 64^3 tiny) as context lines
+
+Options: --gpus N (only 1 is supported: this build runs on one GPU),
+--steps K, --warmup W, --no-cpu, --no-workloads, and --pmc-pass
+{forward,backward,copy} which runs a short fixed launch sequence for
+rocprofv3 counter collection.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "DRR FPS and Gsamples/s (rays x samples) at 200^2 and 1024^2; % HBM roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_revision() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "ct_forward_projection_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+class Resident:
+    """A workload's arrays on the device plus preallocated outputs."""
+
+    def __init__(self, w, dev, bf16=False):
+        import torch
+        self.w = w
+        if bf16:
+            self.vol = torch.from_numpy(w.volume_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
+        else:
+            self.vol = torch.from_numpy(w.volume).to(dev)
+        self.poses = torch.from_numpy(w.poses).to(dev)
+        self.out = torch.empty((w.n_views, w.det_h, w.det_w), device=dev)
+        self.s = torch.empty_like(self.out)
+        self.g = None if w.grad_out is None else torch.from_numpy(w.grad_out).to(dev)
+        self.grad = torch.empty(w.volume.shape, device=dev) if w.grad_out is not None else None
+        self.elem_bytes = 2 if bf16 else 4
+
+    def forward(self):
+        import ct_forward_projection_amd as drr
+        w = self.w
+        drr.drr_forward(self.vol, w.spacing, w.K, self.poses, w.det_h, w.det_w, w.n_samples,
+                        w.mode, out=self.out, line_integral=self.s)
+
+    def backward(self):
+        import ct_forward_projection_amd as drr
+        w = self.w
+        drr.drr_backward_volume(w.volume.shape, w.spacing, w.K, self.poses, w.det_h, w.det_w,
+                                w.n_samples, w.mode, self.g, self.s, grad_volume=self.grad)
+
+    def hit_rays(self) -> int:
+        """Rays that intersect the volume box, counted by the library itself: the
+        line integral of a volume of ones is the chord, > 0 exactly on hits."""
+        import torch
+
+        import ct_forward_projection_amd as drr
+        w = self.w
+        ones = torch.ones(w.volume.shape, device=self.out.device)
+        chord = drr.project(ones, w.spacing, w.K, self.poses, w.det_h, w.det_w, 1)
+        return int((chord > 0).sum().item())
+
+
+def time_events(fns, reps):
+    """Per-function GPU time (ms, mean over reps) from events recorded on the
+    current stream -- the stream the library launches on."""
+    import torch
+    st = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for r in range(reps):
+        ev[r][0].record(st)
+        for i, f in enumerate(fns):
+            f()
+            ev[r][i + 1].record(st)
+    torch.cuda.synchronize()
+    return [float(np.mean([ev[r][i].elapsed_time(ev[r][i + 1]) for r in range(reps)]))
+            for i in range(len(fns))]
+
+
+def forward_bytes(res, hits):
+    w = res.w
+    return hits * w.n_samples * 8 * res.elem_bytes + w.n_rays * 8
+
+
+def backward_bytes(res, hits):
+    w = res.w
+    return hits * w.n_samples * 8 * 4 + w.n_rays * 8
+
+
+def roofline(name, alg_bytes, ms, traffic=None):
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_revision") != kernel_revision():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w):
+    """The CPU oracle on the same train step (forward + volume gradient)."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+    t0 = time.perf_counter()
+    oracle.forward_workload(w, n_threads=threads)
+    _, used = oracle.adjoint_workload(w, n_threads=threads, max_buffer_bytes=8 << 30)
+    dt = time.perf_counter() - t0
+    return {"value": round(w.nominal_samples / dt / 1e9, 4), "unit": "Gsamples/s",
+            "cores": int(min(threads, used) if used else threads), "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"the whole step: {w.name} forward + volume gradient, fp64, "
+                      f"{threads} threads forward / {used} threads scatter"}
+
+
+def workload_lines(dev, reps):
+    import workloads as W
+    lines = {}
+    for i, bf16 in [(1, False), (2, False), (2, True), (4, False), (5, False)]:
+        w = W.make_workload(i, with_bf16=bf16)
+        res = Resident(w, dev, bf16=bf16)
+        hits = res.hit_rays()
+        fns = [res.forward] + ([res.backward] if w.grad_out is not None else [])
+        for f in fns:
+            f()
+        t = time_events(fns, reps)
+        fwd_ms = t[0]
+        line = {"views": w.n_views, "detector": [w.det_h, w.det_w], "n_samples": w.n_samples,
+                "dtype": "bf16" if bf16 else "f32",
+                "forward_ms": round(fwd_ms, 4),
+                "forward_fps": round(w.n_views / fwd_ms * 1e3, 1),
+                "forward_gsamples_s": round(w.nominal_samples / fwd_ms / 1e6, 1),
+                "forward_effective_gsamples_s": round(hits * w.n_samples / fwd_ms / 1e6, 1),
+                "forward_hbm_frac": round(forward_bytes(res, hits) / (fwd_ms * 1e-3) / 1e9
+                                          / HBM_PEAK_GBS, 4),
+                "hit_rays": hits}
+        if len(t) > 1:
+            line["backward_ms"] = round(t[1], 4)
+            line["backward_gsamples_s"] = round(w.nominal_samples / t[1] / 1e6, 1)
+            line["backward_hbm_frac"] = round(backward_bytes(res, hits) / (t[1] * 1e-3) / 1e9
+                                              / HBM_PEAK_GBS, 4)
+        lines[w.name + ("-bf16" if bf16 else "")] = line
+        log(f"workload {w.name}{' bf16' if bf16 else ''}: {line}")
+        del res
+    return lines
+
+
+def pmc_pass(kind: str, dev):
+    """A short fixed launch sequence for rocprofv3 counter runs: 3 launches of
+    the chosen kernel on the train-step workload, or a plain 1 GiB copy (the
+    calibration kernel for the byte counters)."""
+    import torch
+
+    import workloads as W
+    if kind == "copy":
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("pmc copy: 3 x 1 GiB")
+        return
+    res = Resident(W.make_workload(3), dev)
+    res.forward()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        res.forward() if kind == "forward" else res.backward()
+    torch.cuda.synchronize()
+    log(f"pmc pass: 3 x {kind}")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true")
+    ap.add_argument("--pmc-pass", choices=["forward", "backward", "copy"])
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 "
+              "(the multi-GPU sharding design is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import ct_forward_projection_amd as drr
+    import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    drr.library()   # fail loudly if the HIP library is not built
+    dev = torch.device("cuda:0")
+    if args.pmc_pass:
+        pmc_pass(args.pmc_pass, dev)
+        return
+
+    w = W.make_workload(3)
+    res = Resident(w, dev)
+    hits = res.hit_rays()
+    log(f"bench: {w.name} on {torch.cuda.get_device_name(0)}; {hits} of {w.n_rays} rays hit")
+
+    def step():
+        res.forward()
+        res.backward()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / max(args.steps, 1) * 1e3
+
+    # per-kernel GPU time of the same step, HIP events on the launch stream
+    fwd_ms, bwd_ms = time_events([res.forward, res.backward], max(args.steps, 1))
+    rf = roofline("drr_march_kernel", forward_bytes(res, hits), fwd_ms,
+                  measured_traffic("drr_march_kernel"))
+    rb = roofline("drr_scatter_kernel (with gradient fill)", backward_bytes(res, hits), bwd_ms,
+                  measured_traffic("drr_scatter_kernel"))
+    dominant, other = (rb, rf) if bwd_ms >= fwd_ms else (rf, rb)
+
+    out = {
+        "metric": METRIC,
+        "value": round(w.nominal_samples / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "Gsamples/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "volume": list(w.volume.shape), "voxel_mm": 1.0,
+                   "views": w.n_views, "detector": [w.det_h, w.det_w], "n_samples": w.n_samples,
+                   "output": "beer-lambert", "pass": "forward+volume-backward",
+                   "parallelism": "single-gpu"},
+        "fps": round(w.n_views / (ms_per_step * 1e-3), 2),
+        "kernels_ms": {"forward": round(fwd_ms, 4), "backward": round(bwd_ms, 4)},
+        "effective_gsamples_s": round(hits * w.n_samples / (ms_per_step * 1e-3) / 1e9, 2),
+        "roofline": dominant,
+        "roofline_other": other,
+        "kernel_revision": kernel_revision(),
+        "context": "pages' figures, other hardware: FlashDRR Triton train step 15.4 ms at "
+                   "1024^2/512 (RTX 5070 Ti); nanodrr 12,600 FPS fused / 17,820 FPS bf16+compile "
+                   "at 200^2 (RTX 6000 Ada); FlashDRR 9.16 ms at 2048^2/256 (RTX 5070 Ti)",
+    }
+    if not args.no_workloads:
+        out["workloads"] = workload_lines(dev, reps=10)
+    if not args.no_cpu:
+        log("cpu baseline: oracle on the same step ...")
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,7 +7,8 @@
 //                       diffct Quickstart project.)
 //   drr_scatter_kernel  backward: the same samples scatter y dz w_corner into the
 //                       fp32 volume gradient, y = g exp(-s) (Beer-Lambert) or g
-//                       (line integral), pre-reduced in an LDS window.
+//                       (line integral), pre-reduced in fixed point in an LDS
+//                       window.
 //                       (flashdrr VolumeRaycaster: differentiable in the volume;
 //                       diffct Quickstart backproject = A^T.)
 //   drr_fill_kernel     zeroes the gradient before the scatter (a kernel rather
@@ -237,7 +238,7 @@ __device__ inline void scatter_sample_global(float* __restrict__ grad, uint32_t 
     unsafeAtomicAdd(grad + r11 + x1, w[7]);
 }
 
-// LDS window of the backward: 8192 fp32 (32 KB), five workgroups per CU.
+// LDS window of the backward: 8192 int32 (32 KB), five workgroups per CU.
 constexpr int kWinCap = 8192;
 
 // Workgroup-wide min of six ints (maxima are passed negated).
@@ -262,26 +263,105 @@ __device__ inline void block_min6(int v[6], int* red, int* out)
     __syncthreads();
 }
 
-// Backward scatter with LDS pre-reduction.  The 256 rays of a 16 x 16 tile walk
-// their samples in chunks; for each chunk the tile's corner bounding box (the
-// rays are straight, so a chunk's end samples bound it) is reduced across the
-// workgroup, and if the box fits the window every sample adds its 8 weights
-// into LDS; the window is then flushed with one global atomic per touched
-// voxel.  Coherent neighbouring rays hit the same voxels many times, so this
-// replaces most same-address global atomics with LDS atomics.  A chunk whose
-// box does not fit even at one sample falls back to global atomics.
+// Workgroup-wide sums of two floats.
+__device__ inline void block_sum2(float& a, float& b, float* red)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        a += __shfl_xor(a, off, 64);
+        b += __shfl_xor(b, off, 64);
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) {
+        red[2 * wave] = a;
+        red[2 * wave + 1] = b;
+    }
+    __syncthreads();
+    a = 0.0f;
+    b = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kBlock / 64; ++w) {
+        a += red[2 * w];
+        b += red[2 * w + 1];
+    }
+    __syncthreads();
+}
+
+// Pixel owned by a thread of the backward: the 16 x 16 tile is split into four
+// interleaved 8 x 8 lattices (stride 2), one per wave, so the 64 lanes of a
+// wave sit two pixels apart and hit fewer common voxels in one LDS atomic
+// instruction (same-address lanes serialise).
+__device__ inline PixelCoord tile_pixel_interleaved(int tile, int tiles_x, int tiles_per_view)
+{
+    PixelCoord p;
+    p.view = tile / tiles_per_view;
+    const int t = tile - p.view * tiles_per_view;
+    const int ty = t / tiles_x, tx = t - ty * tiles_x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    p.r = ty * kTile + 2 * (lane >> 3) + (wave >> 1);
+    p.c = tx * kTile + 2 * (lane & 7) + (wave & 1);
+    return p;
+}
+
+// Add the eight (scaled) weights of one cell to the LDS window.
+__device__ inline void window_add(int* win, const Cell& C, const int lo[3], int wy, int wz,
+                                  const float w[8])
+{
+    const int x0 = C.x0 - lo[0], x1 = C.x1 - lo[0];
+    const int y0 = (C.y0 - lo[1]) * wy, y1 = (C.y1 - lo[1]) * wy;
+    const int z0 = (C.z0 - lo[2]) * wz, z1 = (C.z1 - lo[2]) * wz;
+    atomicAdd(&win[z0 + y0 + x0], __float2int_rn(w[0]));
+    atomicAdd(&win[z0 + y0 + x1], __float2int_rn(w[1]));
+    atomicAdd(&win[z0 + y1 + x0], __float2int_rn(w[2]));
+    atomicAdd(&win[z0 + y1 + x1], __float2int_rn(w[3]));
+    atomicAdd(&win[z1 + y0 + x0], __float2int_rn(w[4]));
+    atomicAdd(&win[z1 + y0 + x1], __float2int_rn(w[5]));
+    atomicAdd(&win[z1 + y1 + x0], __float2int_rn(w[6]));
+    atomicAdd(&win[z1 + y1 + x1], __float2int_rn(w[7]));
+}
+
+__device__ inline bool same_cell(const Cell& a, const Cell& b)
+{
+    return a.x0 == b.x0 && a.x1 == b.x1 && a.y0 == b.y0 && a.y1 == b.y1 && a.z0 == b.z0 &&
+           a.z1 == b.z1;
+}
+
+// Backward scatter with LDS pre-reduction in fixed point.
+//
+// The 256 rays of a 16 x 16 tile walk their samples in chunks.  For each chunk
+// the tile's corner bounding box (rays are straight, so a chunk's end samples
+// bound it) is reduced across the workgroup; if it fits the window, every
+// lane adds its samples' weights into the LDS window -- consecutive samples in
+// the same cell are summed in registers first -- and the window is flushed
+// with one global float atomic per touched voxel.  Coherent neighbouring rays
+// hit the same voxels many times, so most same-address global atomics become
+// LDS adds.
+//
+// The LDS adds are integer atomics on fixed-point weights: gfx950's LDS float
+// atomic add is an order of magnitude slower than its integer add, and integer
+// sums are exact, so the window total does not depend on the order of the
+// adds.  The scale 2^e is chosen per tile so that no window entry overflows:
+// one sample puts at most |y dz| on any voxel and a ray has at most
+// c = min(N, floor(2 / |dq|_inf) + 1) samples inside a voxel's 2 x 2 x 2
+// support, so an entry never exceeds B = sum over the tile's rays of
+// |y dz| c, and 2^e B <= 2^30.  (|y dz| c is about |y| times the ray's
+// length inside that support, so B stays small even for short chords.)  Each
+// rounding adds at most 1/2 and an entry receives at most Cs = sum of c
+// roundings, which must stay below 2^31 as well.  A tile whose weights are not
+// finite or whose Cs is too large, or a chunk whose box does not fit the window
+// even for one sample, uses global float atomics directly.
 template <int MODE>
 __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
     VolumeDesc V, Intrinsics K, const float* __restrict__ poses, int H, int W, int N,
     int tiles_x, int tiles_per_view, const float* __restrict__ grad_out,
     const float* __restrict__ s_in, float* __restrict__ grad)
 {
-    __shared__ float win[kWinCap];
+    __shared__ int win[kWinCap];
     __shared__ int red[(kBlock / 64) * 6];
     __shared__ int box[6];
 
     const int tile = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
-    const PixelCoord px = tile_pixel(tile, tiles_x, tiles_per_view);
+    const PixelCoord px = tile_pixel_interleaved(tile, tiles_x, tiles_per_view);
     bool active = px.r < H && px.c < W;
     MarchRay R;
     float yd = 0.0f;
@@ -299,6 +379,26 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
     }
     // element strides of the gradient volume
     const uint32_t sy = (uint32_t)V.n[0], sz = (uint32_t)V.n[0] * (uint32_t)V.n[1];
+
+    // fixed-point scale of this tile
+    float B = 0.0f, Cs = 0.0f;
+    if (active) {
+        const double dq_inf = fmax(fmax(fabs((double)R.dq[0]), fabs((double)R.dq[1])),
+                                   fabs((double)R.dq[2])) * 2.3283064365386963e-10;
+        const double c = fmin((double)N, floor(2.0 / dq_inf) + 1.0);
+        B = (float)(fabs((double)yd) * c);
+        Cs = (float)c;
+    }
+    block_sum2(B, Cs, reinterpret_cast<float*>(red));
+    if (Cs == 0.0f) return;                        // no ray of this tile contributes
+    const bool fixed_ok = isfinite(B) && B > 0.0f && Cs <= 1073741824.0f;
+    float scale = 0.0f, inv_scale = 0.0f;
+    if (fixed_ok) {
+        const int e = clampi((int)floor(log2(1073741824.0 / (double)B)), -126, 126);
+        scale = ldexpf(1.0f, e);
+        inv_scale = ldexpf(1.0f, -e);
+    }
+    const float ys = yd * scale;
 
     int S = N;
     int k0 = 0;
@@ -326,51 +426,52 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 ext[a] = max(-box[3 + a] - box[a] + 1, 1);
                 vol *= ext[a];
             }
-            if (box[0] == INT_MAX) vol = 0;            // no active ray in this tile
-            if (vol <= kWinCap || S == 1) break;
+            if (!fixed_ok || vol <= kWinCap || S == 1) break;
             S = max(1, S >> 1);
         }
-        if (vol == 0) break;
-        if (vol <= kWinCap) {
+        if (fixed_ok && vol <= kWinCap) {
             const int n_win = (int)vol;
-            for (int i = threadIdx.x; i < n_win; i += kBlock) win[i] = 0.0f;
+            for (int i = threadIdx.x; i < n_win; i += kBlock) win[i] = 0;
             __syncthreads();
             if (active) {
                 const int wy = ext[0], wz = ext[0] * ext[1];
                 int64_t qx = R.q0[0] + (int64_t)k0 * R.dq[0];
                 int64_t qy = R.q0[1] + (int64_t)k0 * R.dq[1];
                 int64_t qz = R.q0[2] + (int64_t)k0 * R.dq[2];
-                for (int k = k0; k < k0 + S; ++k) {
+                Cell P;
+                float acc[8];
+                cell_of(V, qx, qy, qz, P);
+                corner_weights(P, ys, acc);
+                qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
+                for (int k = k0 + 1; k < k0 + S; ++k) {
                     Cell C;
                     cell_of(V, qx, qy, qz, C);
                     qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
                     float w[8];
-                    corner_weights(C, yd, w);
-                    // window offsets of the corners
-                    const int x0 = C.x0 - lo[0], x1 = C.x1 - lo[0];
-                    const int y0 = (C.y0 - lo[1]) * wy, y1 = (C.y1 - lo[1]) * wy;
-                    const int z0 = (C.z0 - lo[2]) * wz, z1 = (C.z1 - lo[2]) * wz;
-                    atomicAdd(&win[z0 + y0 + x0], w[0]);
-                    atomicAdd(&win[z0 + y0 + x1], w[1]);
-                    atomicAdd(&win[z0 + y1 + x0], w[2]);
-                    atomicAdd(&win[z0 + y1 + x1], w[3]);
-                    atomicAdd(&win[z1 + y0 + x0], w[4]);
-                    atomicAdd(&win[z1 + y0 + x1], w[5]);
-                    atomicAdd(&win[z1 + y1 + x0], w[6]);
-                    atomicAdd(&win[z1 + y1 + x1], w[7]);
+                    corner_weights(C, ys, w);
+                    if (same_cell(C, P)) {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) acc[i] += w[i];
+                    } else {
+                        window_add(win, P, lo, wy, wz, acc);
+                        P = C;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) acc[i] = w[i];
+                    }
                 }
+                window_add(win, P, lo, wy, wz, acc);
             }
             __syncthreads();
             for (int i = threadIdx.x; i < n_win; i += kBlock) {
-                const float val = win[i];
-                if (val != 0.0f) {
+                const int val = win[i];
+                if (val != 0) {
                     const int ix = i % ext[0];
                     const int rest = i / ext[0];
                     const int iy = rest % ext[1];
                     const int iz = rest / ext[1];
                     unsafeAtomicAdd(grad + (uint32_t)(lo[2] + iz) * sz +
                                         (uint32_t)(lo[1] + iy) * sy + (uint32_t)(lo[0] + ix),
-                                    val);
+                                    (float)val * inv_scale);
                 }
             }
             __syncthreads();
