@@ -214,6 +214,129 @@ def pmc_pass(kind: str, dev):
     log(f"pmc pass: 3 x {kind}")
 
 
+# ---------------------------------------------------------------- profile summaries
+
+PROFILE_COMMANDS = {
+    "trace": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/trace -o trace "
+             "--output-format csv -- python3 bench.py --steps 20 --warmup 5 --no-cpu "
+             "--no-workloads",
+    "pmc": "rocprofv3 --pmc {counters} -d gpurun_out/prof/{kind}_{tag} -o pmc "
+           "--output-format csv -- python3 bench.py --pmc-pass {kind}",
+}
+PMC_SETS = {
+    "fetch": ["FETCH_SIZE"],
+    "write": ["WRITE_SIZE", "TCC_HIT_sum", "TCC_MISS_sum"],
+    "sq": ["SQ_WAVES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD",
+           "SQ_INSTS_LDS", "SQ_ACTIVE_INST_VALU", "SQ_WAIT_INST_ANY", "GRBM_GUI_ACTIVE"],
+    "ta": ["TA_TA_BUSY_sum", "TA_BUSY_avr", "TD_TD_BUSY_sum", "SQ_LDS_BANK_CONFLICT",
+           "SQ_LDS_ADDR_CONFLICT"],
+}
+KERNEL_KEYS = {"forward": "drr_march_kernel", "backward": "drr_scatter_kernel",
+               "copy": "copy"}
+
+
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _find(root, suffix):
+    hits = []
+    for d, _, files in os.walk(root):
+        hits += [os.path.join(d, f) for f in files if f.endswith(suffix)]
+    return sorted(hits)
+
+
+def profile_summary(root: str):
+    """Summarise rocprofv3 outputs under ``root`` (the layout PROFILE_COMMANDS
+    writes) into profiles/*.md and profiles/pmc_traffic.json."""
+    prof_dir = os.path.join(ROOT, "profiles")
+    os.makedirs(prof_dir, exist_ok=True)
+    rev = kernel_revision()
+    # kernel trace statistics
+    stats = _find(os.path.join(root, "trace"), "kernel_stats.csv")
+    if stats:
+        rows = _csv_rows(stats[0])
+        lines = ["# Kernel trace: train step on the 1024x1024 workload", "",
+                 f"Command: `{PROFILE_COMMANDS['trace']}`", "",
+                 f"Kernel sources revision: `{rev}`", "",
+                 "| kernel | calls | average (us) | min (us) | max (us) | share |",
+                 "|---|---|---|---|---|---|"]
+        for r in rows:
+            name = r.get("Name", r.get("KernelName", "?"))
+            if len(name) > 90:
+                name = name[:87] + "..."
+            lines.append(f"| `{name}` | {r.get('Calls')} | {float(r.get('AverageNs', 0)) / 1e3:.2f} "
+                         f"| {float(r.get('MinNs', 0)) / 1e3:.2f} | {float(r.get('MaxNs', 0)) / 1e3:.2f} "
+                         f"| {float(r.get('Percentage', 0)):.1f}% |")
+        path = os.path.join(prof_dir, "kernel_trace_train_step_1024.md")
+        with open(path, "w") as f:
+            f.write("\n".join(lines) + "\n")
+        log("wrote", path)
+    # counters
+    values = {}
+    for kind in ("forward", "backward", "copy"):
+        for tag in PMC_SETS:
+            for path in _find(os.path.join(root, f"{kind}_{tag}"), "counter_collection.csv"):
+                per = {}
+                for r in _csv_rows(path):
+                    if KERNEL_KEYS[kind] not in r.get("Kernel_Name", ""):
+                        continue
+                    key = (r["Counter_Name"], r["Dispatch_Id"])
+                    per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+                for (cname, _), v in per.items():
+                    values.setdefault(kind, {}).setdefault(cname, []).append(v)
+    if not values:
+        return
+    med = {k: {c: float(np.median(v)) for c, v in d.items()} for k, d in values.items()}
+    copy_bytes = float(1 << 30)
+    fetch_factor = write_factor = None
+    if "copy" in med:
+        if med["copy"].get("FETCH_SIZE"):
+            fetch_factor = copy_bytes / (med["copy"]["FETCH_SIZE"] * 1024.0)
+        if med["copy"].get("WRITE_SIZE"):
+            write_factor = copy_bytes / (med["copy"]["WRITE_SIZE"] * 1024.0)
+    traffic = {"kernel_revision": rev, "fetch_calibration": fetch_factor,
+               "write_calibration": write_factor, "kernels": {}}
+    lines = ["# Hardware counters per dispatch (median), train-step workload 1024x1024", "",
+             "Commands (one counter set per run):", ""]
+    for tag, counters in PMC_SETS.items():
+        lines.append("- `" + PROFILE_COMMANDS["pmc"].format(counters=" ".join(counters),
+                                                            kind="<forward|backward|copy>",
+                                                            tag=tag) + "`")
+    lines += ["", f"Kernel sources revision: `{rev}`", "",
+              "Calibration: a plain 1 GiB device copy (`bench.py --pmc-pass copy`) reads "
+              f"FETCH_SIZE x {fetch_factor} and WRITE_SIZE x {write_factor} of its known size "
+              "(factors applied below).", ""]
+    for kind, name in (("forward", "drr_march_kernel"), ("backward", "drr_scatter_kernel")):
+        if kind not in med:
+            continue
+        m = med[kind]
+        lines += [f"## {name}", "", "| counter | value |", "|---|---|"]
+        for c in sorted(m):
+            lines.append(f"| {c} | {m[c]:.6g} |")
+        fb = m.get("FETCH_SIZE", 0.0) * 1024.0 * (fetch_factor or 1.0)
+        wb = m.get("WRITE_SIZE", 0.0) * 1024.0 * (write_factor or 1.0)
+        hit = m.get("TCC_HIT_sum"), m.get("TCC_MISS_sum")
+        if all(h is not None for h in hit) and sum(hit) > 0:
+            lines.append(f"| L2 hit rate | {hit[0] / (hit[0] + hit[1]):.4f} |")
+        if m.get("SQ_ACTIVE_INST_VALU") and m.get("SQ_BUSY_CYCLES"):
+            lines.append(f"| VALU active / SQ busy cycles | "
+                         f"{m['SQ_ACTIVE_INST_VALU'] / m['SQ_BUSY_CYCLES']:.4f} |")
+        lines += ["", f"HBM-side traffic per launch (calibrated): read {fb / 1e6:.1f} MB, "
+                      f"write {wb / 1e6:.1f} MB, total {(fb + wb) / 1e6:.1f} MB", ""]
+        if fb or wb:
+            traffic["kernels"][name] = {"hbm_bytes_per_launch": fb + wb, "read_bytes": fb,
+                                        "write_bytes": wb}
+    path = os.path.join(prof_dir, "counters_train_step_1024.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(prof_dir, "pmc_traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    log("wrote", path)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,7 +345,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-workloads", action="store_true")
     ap.add_argument("--pmc-pass", choices=["forward", "backward", "copy"])
+    ap.add_argument("--profile-summary", metavar="DIR",
+                    help="summarise rocprofv3 outputs under DIR into profiles/ (CPU only)")
     args = ap.parse_args()
+    if args.profile_summary:
+        profile_summary(args.profile_summary)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 "
