@@ -141,60 +141,103 @@ __device__ inline float interpolate(const SampleAddr& A, const CornerVals& c)
 // consumed, so each wave has 4 x 4 loads outstanding.
 constexpr int kInflight = 4;
 
-template <typename T, bool PAIR, int MODE>
+// Pixel of a thread when SPLIT adjacent lanes share one ray (small launches):
+// a workgroup covers a (256 / SPLIT)-ray square patch, ray-major.
+template <int SPLIT>
+__device__ inline PixelCoord split_pixel(int tile, int tiles_x, int tiles_per_view)
+{
+    constexpr int side = SPLIT == 4 ? 8 : (SPLIT == 16 ? 4 : 2);
+    static_assert(side * side * SPLIT == kBlock, "SPLIT must be 4, 16 or 64");
+    PixelCoord p;
+    p.view = tile / tiles_per_view;
+    const int t = tile - p.view * tiles_per_view;
+    const int ty = t / tiles_x, tx = t - ty * tiles_x;
+    const int ray = threadIdx.x / SPLIT;
+    p.r = ty * side + ray / side;
+    p.c = tx * side + ray % side;
+    return p;
+}
+
+template <int SPLIT>
+constexpr int march_tile_side() { return SPLIT == 1 ? kTile : (SPLIT == 4 ? 8 : (SPLIT == 16 ? 4 : 2)); }
+
+// Forward DRR.  SPLIT = 1: one ray per lane (16 x 16 tiles of four 8 x 8 wave
+// sub-tiles).  SPLIT > 1 (launches with few rays): SPLIT adjacent lanes share
+// a ray, lane j taking samples j, j + SPLIT, ... (neighbouring lanes still
+// gather neighbouring voxels), and their partial sums meet in a cross-lane
+// reduction, so a 64 x 64 detector still fills the chip.
+template <typename T, bool PAIR, int MODE, int SPLIT>
 __global__ __launch_bounds__(kBlock) void drr_march_kernel(
     const T* __restrict__ vol, VolumeDesc V, Intrinsics K, const float* __restrict__ poses,
     int H, int W, int N, int tiles_x, int tiles_per_view, float* __restrict__ out,
     float* __restrict__ s_out)
 {
     const int tile = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
-    const PixelCoord px = tile_pixel(tile, tiles_x, tiles_per_view);
+    PixelCoord px;
+    int j = 0;
+    if constexpr (SPLIT == 1) {
+        px = tile_pixel(tile, tiles_x, tiles_per_view);
+    } else {
+        px = split_pixel<SPLIT>(tile, tiles_x, tiles_per_view);
+        j = (int)threadIdx.x % SPLIT;
+    }
+    // every lane of a ray sees the same pixel, so a ray's lanes leave together
     if (px.r >= H || px.c >= W) return;
 
     ViewGeom G;
     view_setup(poses + 12 * px.view, K, G);
     MarchRay R;
     float s = 0.0f;
-    if (ray_setup(G, V, px.r, px.c, N, R)) {
+    const bool hit = ray_setup(G, V, px.r, px.c, N, R);
+    if (hit) {
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc((void*)vol, 0, (int)V.total_bytes, kBufferWord3);
-        int64_t qx = R.q0[0], qy = R.q0[1], qz = R.q0[2];
-        const int64_t dqx = R.dq[0], dqy = R.dq[1], dqz = R.dq[2];
+        int64_t qx = R.q0[0] + (int64_t)j * R.dq[0];
+        int64_t qy = R.q0[1] + (int64_t)j * R.dq[1];
+        int64_t qz = R.q0[2] + (int64_t)j * R.dq[2];
+        const int64_t dqx = (int64_t)SPLIT * R.dq[0], dqy = (int64_t)SPLIT * R.dq[1];
+        const int64_t dqz = (int64_t)SPLIT * R.dq[2];
+        const int n_mine = j < N ? (N - j + SPLIT - 1) / SPLIT : 0;
         // independent partial sums, one per in-flight sample: a shorter fp32
         // summation chain as well
         float acc[kInflight];
 #pragma unroll
-        for (int j = 0; j < kInflight; ++j) acc[j] = 0.0f;
+        for (int i = 0; i < kInflight; ++i) acc[i] = 0.0f;
         int k = 0;
-        for (; k + kInflight <= N; k += kInflight) {
+        for (; k + kInflight <= n_mine; k += kInflight) {
             SampleAddr A[kInflight];
             CornerVals c[kInflight];
 #pragma unroll
-            for (int j = 0; j < kInflight; ++j) {
-                A[j] = sample_addr<T, PAIR>(V, qx, qy, qz);
+            for (int i = 0; i < kInflight; ++i) {
+                A[i] = sample_addr<T, PAIR>(V, qx, qy, qz);
                 qx += dqx; qy += dqy; qz += dqz;
             }
 #pragma unroll
-            for (int j = 0; j < kInflight; ++j) gather<T, PAIR>(rs, A[j], c[j]);
+            for (int i = 0; i < kInflight; ++i) gather<T, PAIR>(rs, A[i], c[i]);
             // keep every gather of the group ahead of the first use: otherwise
             // the scheduler sinks each sample's loads to just before their use
             // and a wave never has more than one sample's loads in flight
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < kInflight; ++j) acc[j] += interpolate(A[j], c[j]);
+            for (int i = 0; i < kInflight; ++i) acc[i] += interpolate(A[i], c[i]);
         }
-        for (; k < N; ++k) {
+        for (; k < n_mine; ++k) {
             const SampleAddr A = sample_addr<T, PAIR>(V, qx, qy, qz);
             qx += dqx; qy += dqy; qz += dqz;
             CornerVals c;
             gather<T, PAIR>(rs, A, c);
             acc[0] += interpolate(A, c);
         }
-        float sum = 0.0f;
 #pragma unroll
-        for (int j = 0; j < kInflight; ++j) sum += acc[j];
-        s = R.dz * sum;
+        for (int i = 0; i < kInflight; ++i) s += acc[i];
     }
+    if constexpr (SPLIT > 1) {
+        // all SPLIT lanes of this ray are here (hit or miss alike)
+#pragma unroll
+        for (int off = SPLIT / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
+        if (j != 0) return;
+    }
+    if (hit) s *= R.dz;
     const size_t o = ((size_t)px.view * H + px.r) * W + px.c;
     out[o] = (MODE == kBeerLambert) ? -expm1f(-s) : s;
     if (s_out) s_out[o] = s;
@@ -500,46 +543,68 @@ __global__ __launch_bounds__(256) void drr_fill_kernel(float* __restrict__ p, si
 
 // ----------------------------------------------------------------- launchers
 
-static void tile_grid(int n_views, int H, int W, int& tiles_x, int& tiles_per_view, int& n_tiles)
+static void tile_grid(int n_views, int H, int W, int side, int& tiles_x, int& tiles_per_view,
+                      int& n_tiles)
 {
-    tiles_x = (W + kTile - 1) / kTile;
-    const int tiles_y = (H + kTile - 1) / kTile;
+    tiles_x = (W + side - 1) / side;
+    const int tiles_y = (H + side - 1) / side;
     tiles_per_view = tiles_x * tiles_y;
     n_tiles = tiles_per_view * n_views;
 }
 
-template <typename T, bool PAIR>
-static void launch_march(const LaunchArgs& a, const T* v, float* out, float* s_out, int tiles_x,
-                         int tiles_per_view, dim3 grid, hipStream_t stream)
+template <typename T, bool PAIR, int SPLIT>
+static void launch_march(const LaunchArgs& a, const T* v, float* out, float* s_out,
+                         hipStream_t stream)
 {
+    int tiles_x, tiles_per_view, n_tiles;
+    tile_grid(a.n_views, a.H, a.W, march_tile_side<SPLIT>(), tiles_x, tiles_per_view, n_tiles);
+    const dim3 grid(n_tiles), block(kBlock);
     if (a.mode == kBeerLambert)
-        hipLaunchKernelGGL((drr_march_kernel<T, PAIR, kBeerLambert>), grid, dim3(kBlock), 0,
+        hipLaunchKernelGGL((drr_march_kernel<T, PAIR, kBeerLambert, SPLIT>), grid, block, 0,
                            stream, v, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view,
                            out, s_out);
     else
-        hipLaunchKernelGGL((drr_march_kernel<T, PAIR, kLineIntegral>), grid, dim3(kBlock), 0,
+        hipLaunchKernelGGL((drr_march_kernel<T, PAIR, kLineIntegral, SPLIT>), grid, block, 0,
                            stream, v, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view,
                            out, s_out);
+}
+
+// Lanes per ray: one, unless the launch has too few rays to give every SIMD of
+// the chip a wave (65536 lanes).
+static int march_split(long long n_rays, int N)
+{
+    const long long target = 65536;
+    if (n_rays >= target || N < 8) return 1;
+    if (n_rays * 4 >= target || N < 32) return 4;
+    if (n_rays * 16 >= target || N < 128) return 16;
+    return 64;
+}
+
+template <typename T, bool PAIR>
+static void launch_march_split(const LaunchArgs& a, const T* v, float* out, float* s_out,
+                               hipStream_t stream)
+{
+    switch (march_split((long long)a.n_views * a.H * a.W, a.N)) {
+    case 1: launch_march<T, PAIR, 1>(a, v, out, s_out, stream); break;
+    case 4: launch_march<T, PAIR, 4>(a, v, out, s_out, stream); break;
+    case 16: launch_march<T, PAIR, 16>(a, v, out, s_out, stream); break;
+    default: launch_march<T, PAIR, 64>(a, v, out, s_out, stream); break;
+    }
 }
 
 hipError_t launch_forward(const LaunchArgs& a, const void* vol, int dtype, float* out,
                           float* s_out, hipStream_t stream)
 {
-    int tiles_x, tiles_per_view, n_tiles;
-    tile_grid(a.n_views, a.H, a.W, tiles_x, tiles_per_view, n_tiles);
-    if (n_tiles == 0) return hipSuccess;
-    const dim3 grid(n_tiles);
+    if ((long long)a.n_views * a.H * a.W == 0) return hipSuccess;
     const bool pair = a.V.n[0] >= 2;
     if (dtype == 0) {
         const float* v = static_cast<const float*>(vol);
-        if (pair) launch_march<float, true>(a, v, out, s_out, tiles_x, tiles_per_view, grid, stream);
-        else launch_march<float, false>(a, v, out, s_out, tiles_x, tiles_per_view, grid, stream);
+        if (pair) launch_march_split<float, true>(a, v, out, s_out, stream);
+        else launch_march_split<float, false>(a, v, out, s_out, stream);
     } else {
         const uint16_t* v = static_cast<const uint16_t*>(vol);
-        if (pair)
-            launch_march<uint16_t, true>(a, v, out, s_out, tiles_x, tiles_per_view, grid, stream);
-        else
-            launch_march<uint16_t, false>(a, v, out, s_out, tiles_x, tiles_per_view, grid, stream);
+        if (pair) launch_march_split<uint16_t, true>(a, v, out, s_out, stream);
+        else launch_march_split<uint16_t, false>(a, v, out, s_out, stream);
     }
     return hipGetLastError();
 }
@@ -554,7 +619,7 @@ hipError_t launch_backward(const LaunchArgs& a, const float* grad_out, const flo
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     int tiles_x, tiles_per_view, n_tiles;
-    tile_grid(a.n_views, a.H, a.W, tiles_x, tiles_per_view, n_tiles);
+    tile_grid(a.n_views, a.H, a.W, kTile, tiles_x, tiles_per_view, n_tiles);
     if (n_tiles == 0) return hipSuccess;
     const dim3 grid(n_tiles), block(kBlock);
     if (a.mode == kBeerLambert)

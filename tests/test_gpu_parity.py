@@ -301,3 +301,39 @@ def test_runs_on_a_non_default_stream(dev):
         img, _ = gpu_forward(w, dev, stream=st)
     ref, _ = oracle.forward_workload(w)
     check_forward(img, ref, FWD_F32, "side stream")
+
+
+def test_graph_capture_replays_match_eager(dev):
+    """Forward and backward captured in a HIP graph (torch.cuda.graph on the
+    current stream) replay to the eager results, several times, with eager work
+    and synchronisations in between; the gradient zeroing is a kernel, so no
+    memset node is recorded."""
+    w = W.make_random_small(21, shape=(20, 18, 22), n_views=2, det=(33, 29), n_samples=60)
+    vol = torch.from_numpy(w.volume).to(dev)
+    poses = torch.from_numpy(w.poses).to(dev)
+    g = torch.from_numpy(w.grad_out).to(dev)
+    out = torch.empty((2, 33, 29), device=dev)
+    s = torch.empty_like(out)
+    grad = torch.empty(w.volume.shape, device=dev)
+
+    def step():
+        drr.drr_forward(vol, w.spacing, w.K, poses, 33, 29, 60, w.mode, out=out, line_integral=s)
+        drr.drr_backward_volume(w.volume.shape, w.spacing, w.K, poses, 33, 29, 60, w.mode, g, s,
+                                grad_volume=grad)
+
+    step()
+    torch.cuda.synchronize()
+    ref_img, ref_grad = out.clone(), grad.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for i in range(4):
+        out.fill_(-1.0)
+        grad.fill_(123.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_img), f"replay {i}: image"
+        assert normwise_err(grad.cpu().numpy(), ref_grad.cpu().numpy()) <= 1e-6, f"replay {i}"
+        step()   # eager work between replays
+        torch.cuda.synchronize()
