@@ -72,12 +72,17 @@ class Resident:
         self.g = None if w.grad_out is None else torch.from_numpy(w.grad_out).to(dev)
         self.grad = torch.empty(w.volume.shape, device=dev) if w.grad_out is not None else None
         self.elem_bytes = 2 if bf16 else 4
+        import ct_forward_projection_amd as drr
+        nz, ny, nx = w.volume.shape
+        need = drr.drr_workspace_bytes(nz, ny, nx, drr.BF16 if bf16 else drr.F32, w.n_views,
+                                       w.det_h, w.det_w, w.n_samples, 0)
+        self.workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
 
     def forward(self):
         import ct_forward_projection_amd as drr
         w = self.w
         drr.drr_forward(self.vol, w.spacing, w.K, self.poses, w.det_h, w.det_w, w.n_samples,
-                        w.mode, out=self.out, line_integral=self.s)
+                        w.mode, out=self.out, line_integral=self.s, workspace=self.workspace)
 
     def backward(self):
         import ct_forward_projection_amd as drr

@@ -82,6 +82,7 @@ int check_geometry(int nz, int ny, int nx, int elem_bytes, const float* spacing,
         a.V.half_e[i] = 0.5 * (double)n[i] * (double)spacing[i];
         a.V.q_off[i] = 0.5 * (double)(n[i] - 1);
     }
+    a.V.cell_row_bytes = a.V.cell_slice_bytes = a.V.cell_total_bytes = 0;
     a.V.row_bytes = (uint32_t)nx * (uint32_t)elem_bytes;
     a.V.slice_bytes = (uint32_t)nx * (uint32_t)ny * (uint32_t)elem_bytes;
     a.V.total_bytes = (uint32_t)((long long)nz * ny * nx * elem_bytes);
@@ -118,9 +119,12 @@ const char* drr_status_string(int status)
 size_t drr_workspace_bytes(int nz, int ny, int nx, int dtype, int n_views, int det_h,
                            int det_w, int n_samples, int for_backward)
 {
-    (void)nz; (void)ny; (void)nx; (void)dtype; (void)n_views; (void)det_h; (void)det_w;
-    (void)n_samples; (void)for_backward;
-    return 0;
+    if (for_backward || nz < 1 || ny < 1 || nx < 1 || n_views < 0 || det_h < 0 || det_w < 0 ||
+        n_samples < 1 || (dtype != DRR_F32 && dtype != DRR_BF16))
+        return 0;
+    return drr::plan_forward(nz, ny, nx, dtype == DRR_F32 ? 4 : 2,
+                             (long long)n_views * det_h * det_w, n_samples)
+        .workspace_bytes;
 }
 
 int drr_forward(const void* volume, int dtype, int nz, int ny, int nx, const float* spacing,
@@ -137,16 +141,21 @@ int drr_forward(const void* volume, int dtype, int nz, int ny, int nx, const flo
     if (!volume) return fail(DRR_ERR_INVALID_ARGUMENT, "volume is NULL");
     const long long n_rays = (long long)n_views * det_h * det_w;
     if (n_rays > 0 && !out) return fail(DRR_ERR_INVALID_ARGUMENT, "out is NULL");
-    const size_t need =
-        drr_workspace_bytes(nz, ny, nx, dtype, n_views, det_h, det_w, n_samples, 0);
-    if (workspace_bytes < need)
+    const int eb = dtype == DRR_F32 ? 4 : 2;
+    const drr::ForwardPlan plan = drr::plan_forward(nz, ny, nx, eb, n_rays, n_samples);
+    if (workspace_bytes < plan.workspace_bytes)
         return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
-                    workspace_bytes, need);
-    if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
+                    workspace_bytes, plan.workspace_bytes);
+    if (plan.workspace_bytes > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
         return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
     if (n_rays == 0) return ok();
-    hipError_t e = drr::launch_forward(a, volume, dtype, out, line_integral,
-                                       static_cast<hipStream_t>(stream));
+    if (plan.cells) {
+        a.V.cell_row_bytes = (uint32_t)(nx + 1) * 8u * (uint32_t)eb;
+        a.V.cell_slice_bytes = (uint32_t)(ny + 1) * a.V.cell_row_bytes;
+        a.V.cell_total_bytes = (uint32_t)((long long)(nz + 1) * a.V.cell_slice_bytes);
+    }
+    hipError_t e = drr::launch_forward(a, volume, dtype, plan.cells, workspace, out,
+                                       line_integral, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(DRR_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -43,6 +43,12 @@ struct VolumeDesc {
     uint32_t row_bytes;            // nx * element size
     uint32_t slice_bytes;          // nx * ny * element size
     uint32_t total_bytes;          // whole volume (buffer range)
+    // corner-cell copy (when the forward uses one): (nx+1) x (ny+1) x (nz+1)
+    // cells of 8 elements, cell (i, j, k) holding the clamped corners of the
+    // trilinear cell whose low corner is voxel (i-1, j-1, k-1)
+    uint32_t cell_row_bytes;
+    uint32_t cell_slice_bytes;
+    uint32_t cell_total_bytes;
 };
 
 // Per-view camera, fp64: world direction of image point (u, v, 1) is

@@ -14,11 +14,14 @@
 //   drr_fill_kernel     zeroes the gradient before the scatter (a kernel rather
 //                       than a memset so that the sequence is graph-capturable).
 //
+//   drr_cells_kernel    optional relayout: the corner-cell copy of the volume the
+//                       march reads when samples reuse cells enough.
+//
 // The march is gather-bound, not a contraction, so there is no MFMA here: the
 // design levers are the number of vector-memory instructions per sample (x-pair
-// loads: one 2-element load per trilinear row, 4 per sample instead of 8),
-// cheap full-rate integer position stepping, and wave-coherent 8 x 8 pixel
-// tiles so neighbouring lanes gather from the same cache lines.
+// loads: 4 per sample instead of 8; corner cells: 1 or 2), cheap full-rate
+// integer position stepping, and wave-coherent 8 x 8 pixel tiles so
+// neighbouring lanes gather from the same cache lines.
 #include <limits.h>
 
 #include "drr_device.hpp"
@@ -67,20 +70,23 @@ __device__ inline float load_one<uint16_t>(__amdgpu_buffer_rsrc_t rs, uint32_t o
                            << 16);
 }
 
-// Where the eight trilinear corners of one sample live: the byte offset of the
-// (y0, z0) row start plus the row deltas, and the three weights.  With PAIR
-// (nx >= 2) each of the four (y, z) rows is read as one x-pair starting at
-// xp = clamp(ix, 0, nx - 2); at the clamped x edges the pair still holds the
-// right voxel and the weight is pinned to 0 (ix < 0) or 1 (ix > nx - 2), which
-// is exactly clamp to edge.  Without PAIR (nx == 1) the x corners are read one
-// by one.
+// How the march reads the eight trilinear corners of a sample.
+//   Pair   (nx >= 2): each of the four (y, z) rows is one x-pair load starting
+//          at xp = clamp(ix, 0, nx - 2); at the clamped x edges the pair still
+//          holds the right voxel and the weight is pinned to 0 (ix < 0) or 1
+//          (ix > nx - 2), which is exactly clamp to edge.  4 loads per sample.
+//   Single (nx == 1): the x corners are read one by one.  8 loads per sample.
+//   Cell   (corner-cell copy): the 8 clamped corners are one 16-byte (bf16) or
+//          two 16-byte (fp32) loads at cell (ix + 1, iy + 1, iz + 1); no clamp.
+enum class Layout { Single, Pair, Cell };
+
 struct SampleAddr {
-    uint32_t o, dy, dz;            // bytes: row (y0, z0) + x offset, row steps
-    uint32_t x1;                   // !PAIR: byte offset of the x1 corner minus x0
+    uint32_t o, dy, dz;            // bytes: first row (+ x offset), row steps
+    uint32_t x1;                   // Single: byte offset of the x1 corner minus x0
     float fx, fy, fz;
 };
 
-template <typename T, bool PAIR>
+template <typename T, Layout L>
 __device__ inline SampleAddr sample_addr(const VolumeDesc& V, int64_t qx, int64_t qy, int64_t qz)
 {
     SampleAddr A;
@@ -88,12 +94,20 @@ __device__ inline SampleAddr sample_addr(const VolumeDesc& V, int64_t qx, int64_
     A.fx = fixed_frac(qx);
     A.fy = fixed_frac(qy);
     A.fz = fixed_frac(qz);
+    if constexpr (L == Layout::Cell) {
+        // a sample inside the box has -1 <= floor(q) <= n - 1; anything else
+        // would fall outside the buffer range and read zeros, never fault
+        A.o = (uint32_t)(iz + 1) * V.cell_slice_bytes +
+              __umul24((uint32_t)(iy + 1), V.cell_row_bytes) + (uint32_t)(ix + 1) * (8 * sizeof(T));
+        A.dy = A.dz = A.x1 = 0;
+        return A;
+    }
     const int y0 = clampi(iy, 0, V.n[1] - 1), y1 = clampi(iy + 1, 0, V.n[1] - 1);
     const int z0 = clampi(iz, 0, V.n[2] - 1), z1 = clampi(iz + 1, 0, V.n[2] - 1);
     const uint32_t r00 = (uint32_t)z0 * V.slice_bytes + __umul24((uint32_t)y0, V.row_bytes);
     A.dy = y1 > y0 ? V.row_bytes : 0u;
     A.dz = z1 > z0 ? V.slice_bytes : 0u;
-    if constexpr (PAIR) {
+    if constexpr (L == Layout::Pair) {
         const int xp = clampi(ix, 0, V.n[0] - 2);
         A.fx = __builtin_amdgcn_fmed3f(A.fx + (float)(ix - xp), 0.0f, 1.0f);
         A.o = r00 + (uint32_t)xp * (uint32_t)sizeof(T);
@@ -111,13 +125,43 @@ struct CornerVals {
     float v[8];
 };
 
-template <typename T, bool PAIR>
+template <typename T>
+__device__ inline void load_cell(__amdgpu_buffer_rsrc_t rs, uint32_t off, CornerVals& c);
+
+template <>
+__device__ inline void load_cell<float>(__amdgpu_buffer_rsrc_t rs, uint32_t off, CornerVals& c)
+{
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+    const auto b = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 16), 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        c.v[i] = __uint_as_float(a[i]);
+        c.v[4 + i] = __uint_as_float(b[i]);
+    }
+}
+
+template <>
+__device__ inline void load_cell<uint16_t>(__amdgpu_buffer_rsrc_t rs, uint32_t off, CornerVals& c)
+{
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        c.v[2 * i] = bf16_lo(a[i]);
+        c.v[2 * i + 1] = bf16_hi(a[i]);
+    }
+}
+
+template <typename T, Layout L>
 __device__ inline void gather(__amdgpu_buffer_rsrc_t rs, const SampleAddr& A, CornerVals& c)
 {
+    if constexpr (L == Layout::Cell) {
+        load_cell<T>(rs, A.o, c);
+        return;
+    }
     const uint32_t rows[4] = {A.o, A.o + A.dy, A.o + A.dz, A.o + A.dz + A.dy};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        if constexpr (PAIR) {
+        if constexpr (L == Layout::Pair) {
             load_pair<T>(rs, rows[r], c.v[2 * r], c.v[2 * r + 1]);
         } else {
             c.v[2 * r] = load_one<T>(rs, rows[r]);
@@ -137,8 +181,35 @@ __device__ inline float interpolate(const SampleAddr& A, const CornerVals& c)
     return fmaf(A.fz, c1 - c0, c0);
 }
 
+// Corner-cell relayout: cell (i, j, k), 0 <= i <= nx etc., holds the eight
+// clamped corners (x0, x1) x (y0, y1) x (z0, z1) of the trilinear cell whose
+// low corner is voxel (i-1, j-1, k-1), in the CornerVals order.  One thread
+// per cell; consecutive threads write consecutive cells.
+template <typename T>
+__global__ __launch_bounds__(256) void drr_cells_kernel(const T* __restrict__ vol, int nx, int ny,
+                                                        int nz, T* __restrict__ cells)
+{
+    const int cx = nx + 1, cy = ny + 1;
+    const long long n = (long long)cx * cy * (nz + 1);
+    const size_t sy = (size_t)nx, sz = (size_t)nx * ny;
+    for (long long id = (long long)blockIdx.x * blockDim.x + threadIdx.x; id < n;
+         id += (long long)gridDim.x * blockDim.x) {
+        const int i = (int)(id % cx);
+        const long long rest = id / cx;
+        const int j = (int)(rest % cy), k = (int)(rest / cy);
+        const size_t x0 = (size_t)clampi(i - 1, 0, nx - 1), x1 = (size_t)clampi(i, 0, nx - 1);
+        const size_t y0 = (size_t)clampi(j - 1, 0, ny - 1) * sy, y1 = (size_t)clampi(j, 0, ny - 1) * sy;
+        const size_t z0 = (size_t)clampi(k - 1, 0, nz - 1) * sz, z1 = (size_t)clampi(k, 0, nz - 1) * sz;
+        const T v[8] = {vol[z0 + y0 + x0], vol[z0 + y0 + x1], vol[z0 + y1 + x0], vol[z0 + y1 + x1],
+                        vol[z1 + y0 + x0], vol[z1 + y0 + x1], vol[z1 + y1 + x0], vol[z1 + y1 + x1]};
+        T* o = cells + (size_t)id * 8;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) o[c] = v[c];
+    }
+}
+
 // Samples a lane keeps in flight: their gathers are all issued before any is
-// consumed, so each wave has 4 x 4 loads outstanding.
+// consumed, so each wave has 4 samples' loads outstanding.
 constexpr int kInflight = 4;
 
 // Pixel of a thread when SPLIT adjacent lanes share one ray (small launches):
@@ -165,12 +236,13 @@ constexpr int march_tile_side() { return SPLIT == 1 ? kTile : (SPLIT == 4 ? 8 : 
 // sub-tiles).  SPLIT > 1 (launches with few rays): SPLIT adjacent lanes share
 // a ray, lane j taking samples j, j + SPLIT, ... (neighbouring lanes still
 // gather neighbouring voxels), and their partial sums meet in a cross-lane
-// reduction, so a 64 x 64 detector still fills the chip.
-template <typename T, bool PAIR, int MODE, int SPLIT>
+// reduction, so a 64 x 64 detector still fills the chip.  `src` is the volume
+// (Pair, Single) or its corner-cell copy (Cell); `src_bytes` its size.
+template <typename T, Layout L, int MODE, int SPLIT>
 __global__ __launch_bounds__(kBlock) void drr_march_kernel(
-    const T* __restrict__ vol, VolumeDesc V, Intrinsics K, const float* __restrict__ poses,
-    int H, int W, int N, int tiles_x, int tiles_per_view, float* __restrict__ out,
-    float* __restrict__ s_out)
+    const T* __restrict__ src, uint32_t src_bytes, VolumeDesc V, Intrinsics K,
+    const float* __restrict__ poses, int H, int W, int N, int tiles_x, int tiles_per_view,
+    float* __restrict__ out, float* __restrict__ s_out)
 {
     const int tile = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
     PixelCoord px;
@@ -191,7 +263,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
     const bool hit = ray_setup(G, V, px.r, px.c, N, R);
     if (hit) {
         const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)vol, 0, (int)V.total_bytes, kBufferWord3);
+            __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, (int)src_bytes, kBufferWord3);
         int64_t qx = R.q0[0] + (int64_t)j * R.dq[0];
         int64_t qy = R.q0[1] + (int64_t)j * R.dq[1];
         int64_t qz = R.q0[2] + (int64_t)j * R.dq[2];
@@ -209,11 +281,11 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
             CornerVals c[kInflight];
 #pragma unroll
             for (int i = 0; i < kInflight; ++i) {
-                A[i] = sample_addr<T, PAIR>(V, qx, qy, qz);
+                A[i] = sample_addr<T, L>(V, qx, qy, qz);
                 qx += dqx; qy += dqy; qz += dqz;
             }
 #pragma unroll
-            for (int i = 0; i < kInflight; ++i) gather<T, PAIR>(rs, A[i], c[i]);
+            for (int i = 0; i < kInflight; ++i) gather<T, L>(rs, A[i], c[i]);
             // keep every gather of the group ahead of the first use: otherwise
             // the scheduler sinks each sample's loads to just before their use
             // and a wave never has more than one sample's loads in flight
@@ -222,10 +294,10 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
             for (int i = 0; i < kInflight; ++i) acc[i] += interpolate(A[i], c[i]);
         }
         for (; k < n_mine; ++k) {
-            const SampleAddr A = sample_addr<T, PAIR>(V, qx, qy, qz);
+            const SampleAddr A = sample_addr<T, L>(V, qx, qy, qz);
             qx += dqx; qy += dqy; qz += dqz;
             CornerVals c;
-            gather<T, PAIR>(rs, A, c);
+            gather<T, L>(rs, A, c);
             acc[0] += interpolate(A, c);
         }
 #pragma unroll
@@ -552,21 +624,21 @@ static void tile_grid(int n_views, int H, int W, int side, int& tiles_x, int& ti
     n_tiles = tiles_per_view * n_views;
 }
 
-template <typename T, bool PAIR, int SPLIT>
-static void launch_march(const LaunchArgs& a, const T* v, float* out, float* s_out,
-                         hipStream_t stream)
+template <typename T, Layout L, int SPLIT>
+static void launch_march(const LaunchArgs& a, const T* src, uint32_t src_bytes, float* out,
+                         float* s_out, hipStream_t stream)
 {
     int tiles_x, tiles_per_view, n_tiles;
     tile_grid(a.n_views, a.H, a.W, march_tile_side<SPLIT>(), tiles_x, tiles_per_view, n_tiles);
     const dim3 grid(n_tiles), block(kBlock);
     if (a.mode == kBeerLambert)
-        hipLaunchKernelGGL((drr_march_kernel<T, PAIR, kBeerLambert, SPLIT>), grid, block, 0,
-                           stream, v, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view,
-                           out, s_out);
+        hipLaunchKernelGGL((drr_march_kernel<T, L, kBeerLambert, SPLIT>), grid, block, 0, stream,
+                           src, src_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                           tiles_per_view, out, s_out);
     else
-        hipLaunchKernelGGL((drr_march_kernel<T, PAIR, kLineIntegral, SPLIT>), grid, block, 0,
-                           stream, v, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view,
-                           out, s_out);
+        hipLaunchKernelGGL((drr_march_kernel<T, L, kLineIntegral, SPLIT>), grid, block, 0, stream,
+                           src, src_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                           tiles_per_view, out, s_out);
 }
 
 // Lanes per ray: one, unless the launch has too few rays to give every SIMD of
@@ -580,33 +652,47 @@ static int march_split(long long n_rays, int N)
     return 64;
 }
 
-template <typename T, bool PAIR>
-static void launch_march_split(const LaunchArgs& a, const T* v, float* out, float* s_out,
-                               hipStream_t stream)
+template <typename T, Layout L>
+static void launch_march_split(const LaunchArgs& a, const T* src, uint32_t src_bytes, float* out,
+                               float* s_out, hipStream_t stream)
 {
     switch (march_split((long long)a.n_views * a.H * a.W, a.N)) {
-    case 1: launch_march<T, PAIR, 1>(a, v, out, s_out, stream); break;
-    case 4: launch_march<T, PAIR, 4>(a, v, out, s_out, stream); break;
-    case 16: launch_march<T, PAIR, 16>(a, v, out, s_out, stream); break;
-    default: launch_march<T, PAIR, 64>(a, v, out, s_out, stream); break;
+    case 1: launch_march<T, L, 1>(a, src, src_bytes, out, s_out, stream); break;
+    case 4: launch_march<T, L, 4>(a, src, src_bytes, out, s_out, stream); break;
+    case 16: launch_march<T, L, 16>(a, src, src_bytes, out, s_out, stream); break;
+    default: launch_march<T, L, 64>(a, src, src_bytes, out, s_out, stream); break;
     }
 }
 
-hipError_t launch_forward(const LaunchArgs& a, const void* vol, int dtype, float* out,
-                          float* s_out, hipStream_t stream)
+template <typename T>
+static hipError_t forward_typed(const LaunchArgs& a, const T* vol, bool cells, T* cell_buf,
+                               float* out, float* s_out, hipStream_t stream)
 {
-    if ((long long)a.n_views * a.H * a.W == 0) return hipSuccess;
-    const bool pair = a.V.n[0] >= 2;
-    if (dtype == 0) {
-        const float* v = static_cast<const float*>(vol);
-        if (pair) launch_march_split<float, true>(a, v, out, s_out, stream);
-        else launch_march_split<float, false>(a, v, out, s_out, stream);
+    if (cells) {
+        const long long n_cells = (long long)(a.V.n[0] + 1) * (a.V.n[1] + 1) * (a.V.n[2] + 1);
+        const int blocks = (int)((n_cells + 255) / 256 < 16384 ? (n_cells + 255) / 256 : 16384);
+        hipLaunchKernelGGL((drr_cells_kernel<T>), dim3(blocks), dim3(256), 0, stream, vol,
+                           a.V.n[0], a.V.n[1], a.V.n[2], cell_buf);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        launch_march_split<T, Layout::Cell>(a, cell_buf, a.V.cell_total_bytes, out, s_out, stream);
+    } else if (a.V.n[0] >= 2) {
+        launch_march_split<T, Layout::Pair>(a, vol, a.V.total_bytes, out, s_out, stream);
     } else {
-        const uint16_t* v = static_cast<const uint16_t*>(vol);
-        if (pair) launch_march_split<uint16_t, true>(a, v, out, s_out, stream);
-        else launch_march_split<uint16_t, false>(a, v, out, s_out, stream);
+        launch_march_split<T, Layout::Single>(a, vol, a.V.total_bytes, out, s_out, stream);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_forward(const LaunchArgs& a, const void* vol, int dtype, bool cells,
+                          void* workspace, float* out, float* s_out, hipStream_t stream)
+{
+    if ((long long)a.n_views * a.H * a.W == 0) return hipSuccess;
+    if (dtype == 0)
+        return forward_typed<float>(a, static_cast<const float*>(vol), cells,
+                                    static_cast<float*>(workspace), out, s_out, stream);
+    return forward_typed<uint16_t>(a, static_cast<const uint16_t*>(vol), cells,
+                                   static_cast<uint16_t*>(workspace), out, s_out, stream);
 }
 
 hipError_t launch_backward(const LaunchArgs& a, const float* grad_out, const float* s_in,

@@ -116,3 +116,16 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError):
         drr.drr_forward(torch.zeros(4, 4, 4), [1, 1, 1], torch.eye(3), torch.zeros(1, 3, 4),
                         4, 4, 8)
+
+
+def test_workspace_too_small_is_rejected_on_the_host():
+    # a dense-ray launch plans the corner-cell relayout, which needs a workspace
+    need = drr.drr_workspace_bytes(8, 8, 8, 0, 1, 256, 256, 64, 0)
+    assert need >= 9 * 9 * 9 * 32
+    assert fwd(det_h=256, det_w=256, n_samples=64, ws=None, ws_bytes=0) == 3
+    assert b"workspace" in drr.library().drr_last_error()
+    # misaligned workspace
+    assert fwd(det_h=256, det_w=256, n_samples=64, ws=ctypes.c_void_p(0x1004),
+               ws_bytes=need) == 1
+    # the backward needs none
+    assert drr.drr_workspace_bytes(8, 8, 8, 0, 1, 256, 256, 64, 1) == 0
