@@ -404,9 +404,12 @@ __device__ inline void block_sum2(float& a, float& b, float* red)
 
 // Pixel owned by a thread of the backward: the 16 x 16 tile is split into four
 // interleaved 8 x 8 lattices (stride 2), one per wave, so the 64 lanes of a
-// wave sit two pixels apart and hit fewer common voxels in one LDS atomic
-// instruction (same-address lanes serialise).
-__device__ inline PixelCoord tile_pixel_interleaved(int tile, int tiles_x, int tiles_per_view)
+// wave sit two pixels apart and rarely target the same voxel in one LDS atomic
+// instruction (same-address lanes serialise).  Measured on the 1024^2 step:
+// 2.97 ms with 8 x 8 contiguous wave tiles, 1.56 ms interleaved.  (Wider
+// lattices -- 32 x 32 tiles, four rays per thread -- cost registers and window
+// room and were slower.)
+__device__ inline PixelCoord scatter_pixel(int tile, int tiles_x, int tiles_per_view)
 {
     PixelCoord p;
     p.view = tile / tiles_per_view;
@@ -423,8 +426,9 @@ __device__ inline void window_add(int* win, const Cell& C, const int lo[3], int 
                                   const float w[8])
 {
     const int x0 = C.x0 - lo[0], x1 = C.x1 - lo[0];
-    const int y0 = (C.y0 - lo[1]) * wy, y1 = (C.y1 - lo[1]) * wy;
-    const int z0 = (C.z0 - lo[2]) * wz, z1 = (C.z1 - lo[2]) * wz;
+    // window extents are below 2^13, so 24-bit multiplies are exact (full rate)
+    const int y0 = __mul24(C.y0 - lo[1], wy), y1 = __mul24(C.y1 - lo[1], wy);
+    const int z0 = __mul24(C.z0 - lo[2], wz), z1 = __mul24(C.z1 - lo[2], wz);
     atomicAdd(&win[z0 + y0 + x0], __float2int_rn(w[0]));
     atomicAdd(&win[z0 + y0 + x1], __float2int_rn(w[1]));
     atomicAdd(&win[z0 + y1 + x0], __float2int_rn(w[2]));
@@ -443,14 +447,13 @@ __device__ inline bool same_cell(const Cell& a, const Cell& b)
 
 // Backward scatter with LDS pre-reduction in fixed point.
 //
-// The 256 rays of a 16 x 16 tile walk their samples in chunks.  For each chunk
-// the tile's corner bounding box (rays are straight, so a chunk's end samples
-// bound it) is reduced across the workgroup; if it fits the window, every
-// lane adds its samples' weights into the LDS window -- consecutive samples in
-// the same cell are summed in registers first -- and the window is flushed
-// with one global float atomic per touched voxel.  Coherent neighbouring rays
-// hit the same voxels many times, so most same-address global atomics become
-// LDS adds.
+// The rays of a tile walk their samples in chunks.  For each chunk the tile's
+// corner bounding box (rays are straight, so a chunk's end samples bound it) is
+// reduced across the workgroup; if it fits the window, every ray adds its
+// samples' weights into the LDS window -- consecutive samples in the same cell
+// are summed in registers first -- and the window is flushed with one global
+// float atomic per touched voxel.  Coherent neighbouring rays hit the same
+// voxels many times, so most same-address global atomics become LDS adds.
 //
 // The LDS adds are integer atomics on fixed-point weights: gfx950's LDS float
 // atomic add is an order of magnitude slower than its integer add, and integer
@@ -476,7 +479,7 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
     __shared__ int box[6];
 
     const int tile = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
-    const PixelCoord px = tile_pixel_interleaved(tile, tiles_x, tiles_per_view);
+    const PixelCoord px = scatter_pixel(tile, tiles_x, tiles_per_view);
     bool active = px.r < H && px.c < W;
     MarchRay R;
     float yd = 0.0f;

@@ -337,3 +337,43 @@ def test_graph_capture_replays_match_eager(dev):
         assert normwise_err(grad.cpu().numpy(), ref_grad.cpu().numpy()) <= 1e-6, f"replay {i}"
         step()   # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_backward_window_fallback_for_diverging_rays(dev):
+    """A source inside the volume with a ~150 degree field of view: a tile's rays
+    spread over the whole 48^3 volume, so even a one-sample chunk overflows the
+    LDS window and the scatter takes its global-atomic path."""
+    rng = np.random.default_rng(31)
+    vol = rng.uniform(0.0, 1.0, size=(48, 48, 48)).astype(np.float32)
+    K = W.intrinsics(4.0, 8.0, 8.0)
+    poses = W.random_poses(2, 2.0, 30.0, 1.0, seed=32)
+    w = W.Workload("inside-wide-fov", vol, np.ones(3, np.float32), K, poses, 16, 16, 96,
+                   W.LINE_INTEGRAL,
+                   grad_out=rng.uniform(-1, 1, size=(2, 16, 16)).astype(np.float32))
+    say("case: diverging rays, window fallback")
+    img, s = gpu_forward(w, dev)
+    ref, _ = oracle.forward_workload(w)
+    check_forward(img, ref, FWD_F32, "wide fov", oracle.chords_workload(w))
+    grad = gpu_backward(w, dev, s, w.grad_out)
+    ref_g, _ = oracle.adjoint_workload(w)
+    err = normwise_err(grad, ref_g)
+    say(f"wide fov: gradient normwise err {err:.3e}")
+    assert err <= GRAD
+
+
+def test_non_finite_upstream_gradient_propagates(dev):
+    """A NaN upstream gradient cannot go through fixed point: its tile falls back
+    to float atomics, and exactly the voxels the oracle marks NaN (every corner
+    of every sample of that ray) are NaN on the GPU; the rest still matches."""
+    w = W.make_random_small(33, shape=(12, 14, 16), n_views=1, det=(20, 24), n_samples=40,
+                            mode=W.LINE_INTEGRAL)
+    g = w.grad_out.copy()
+    g[0, 7, 11] = np.nan
+    say("case: NaN upstream gradient")
+    _, s = gpu_forward(w, dev)
+    grad = gpu_backward(w, dev, s, g)
+    ref, _ = oracle.adjoint_workload(w, grad_out=g)
+    assert np.isnan(ref).any()
+    assert np.array_equal(np.isnan(grad), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert normwise_err(grad[ok], ref[ok]) <= GRAD
