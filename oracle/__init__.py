@@ -62,6 +62,8 @@ def _load():
     lib.oracle_exact_line_integral.restype = I
     lib.oracle_chords.argtypes = [P, P, P, I, I, I, P, I]
     lib.oracle_chords.restype = I
+    lib.oracle_pose_gradient.argtypes = [P, I, I, I, P, P, P, I, I, I, I, I, P, P, I]
+    lib.oracle_pose_gradient.restype = I
     lib.oracle_max_threads.restype = I
     _lib = lib
     return lib
@@ -72,7 +74,12 @@ def _ptr(a: np.ndarray):
 
 
 def _f64(a) -> np.ndarray:
-    return np.ascontiguousarray(np.asarray(a, dtype=np.float32).astype(np.float64))
+    """fp32 inputs (what the HIP side receives) widen exactly; fp64 arrays pass
+    through unchanged (finite-difference pins perturb below fp32 resolution)."""
+    a = np.asarray(a)
+    if a.dtype == np.float64:
+        return np.ascontiguousarray(a)
+    return np.ascontiguousarray(a.astype(np.float32).astype(np.float64))
 
 
 def _threads(n: Optional[int]) -> int:
@@ -184,6 +191,23 @@ def exact_line_integral(volume: np.ndarray, spacing, K, poses, det_h: int, det_w
     if rc != 0:
         raise ValueError("oracle_exact_line_integral: invalid arguments")
     return s
+
+
+def pose_gradient(volume: np.ndarray, spacing, K, poses, det_h: int, det_w: int, n_samples: int,
+                  mode: int, grad_out: np.ndarray, n_threads: Optional[int] = None) -> np.ndarray:
+    """dL/dP for L = sum g I, per view: float64 (V, 3, 4) over the [R | t] entries."""
+    lib = _load()
+    vol = np.ascontiguousarray(volume, dtype=np.float32)
+    nz, ny, nx = vol.shape
+    sp, Kd, Pd = _f64(spacing), _f64(K), _f64(poses).reshape(-1, 12)
+    V = Pd.shape[0]
+    g = np.ascontiguousarray(grad_out, dtype=np.float64).reshape(V, det_h, det_w)
+    out = np.zeros((V, 12), dtype=np.float64)
+    rc = lib.oracle_pose_gradient(_ptr(vol), nz, ny, nx, _ptr(sp), _ptr(Kd), _ptr(Pd), V, det_h,
+                                  det_w, n_samples, mode, _ptr(g), _ptr(out), _threads(n_threads))
+    if rc != 0:
+        raise ValueError("oracle_pose_gradient: invalid arguments")
+    return out.reshape(V, 3, 4)
 
 
 def forward_workload(w, n_threads: Optional[int] = None, use_bf16: bool = False):

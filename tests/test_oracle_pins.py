@@ -579,3 +579,81 @@ def test_gradient_matches_central_finite_differences(mode):
         dn[idx] -= hm
         fd = (loss(up) - loss(dn)) / (hp + hm)
         assert fd == pytest.approx(grad[idx], rel=1e-5, abs=1e-9)
+
+
+# ----------------------------------------------------------------- pose gradient
+
+def _pose_problem(seed, mode):
+    rng = np.random.default_rng(seed)
+    shape = (9, 10, 11)
+    spacing = np.array([1.0, 1.1, 0.9], dtype=np.float32)
+    vol = rng.uniform(0.0, 0.3, size=shape).astype(np.float32)
+    K = W.intrinsics(14.0, 3.1, 2.6)
+    poses = W.random_poses(2, 25.0, 40.0, 1.0, seed=seed + 1).astype(np.float64)
+    g = rng.normal(size=(2, 6, 7))
+    return vol, spacing, K, poses, g
+
+
+@pytest.mark.parametrize("mode", [BL, RAW])
+@pytest.mark.parametrize("seed", [40, 41])
+def test_pose_gradient_matches_central_differences(mode, seed):
+    """dL/dP of L = sum g I(P) against central differences of the oracle forward
+    in fp64 (h = 1e-7 moves samples ~1e-6 voxel, so no sample crosses a voxel
+    plane and the difference quotient sees one smooth piece)."""
+    vol, spacing, K, poses, g = _pose_problem(seed, mode)
+    N = 23
+    grad = oracle.pose_gradient(vol, spacing, K, poses, 6, 7, N, mode, g)
+    h = 1e-7
+    fd = np.zeros_like(grad)
+    for v in range(2):
+        for r in range(3):
+            for c in range(4):
+                up, dn = poses.copy(), poses.copy()
+                up[v, r, c] += h
+                dn[v, r, c] -= h
+                Lp = float((g * oracle.forward(vol, spacing, K, up, 6, 7, N, mode)[0]).sum())
+                Lm = float((g * oracle.forward(vol, spacing, K, dn, 6, 7, N, mode)[0]).sum())
+                fd[v, r, c] = (Lp - Lm) / (2 * h)
+    scale = np.abs(fd).max()
+    assert scale > 1e-3
+    assert np.abs(grad - fd).max() <= 1e-6 * scale, (grad, fd)
+
+
+def test_pose_gradient_of_constant_box_is_the_chord_derivative():
+    """For a constant mu_c volume I = 1 - exp(-mu_c L(P)): the pose gradient is
+    g exp(-mu_c L) mu_c dL/dP with the chord L from face intersections and its
+    derivative by central differences of that independent chord (no voxels)."""
+    mu_c = float(np.float32(0.05))
+    shape = (8, 10, 12)
+    vol = np.full(shape, mu_c, dtype=np.float32)
+    spacing = np.ones(3, dtype=np.float32)
+    E = np.array([12.0, 10.0, 8.0])
+    K = W.intrinsics(12.0, 2.5, 2.5)
+    poses = W.random_poses(1, 30.0, 35.0, 1.0, seed=50).astype(np.float64)
+    rng = np.random.default_rng(51)
+    g = rng.normal(size=(1, 5, 5))
+    grad = oracle.pose_gradient(vol, spacing, K, poses, 5, 5, 17, BL, g)
+
+    def chords(P):
+        Rm, t = P[:, :3], P[:, 3]
+        C = -Rm.T @ t
+        out = np.zeros((5, 5))
+        for r in range(5):
+            for c in range(5):
+                u = np.linalg.solve(K.astype(np.float64), [c + 0.5, r + 0.5, 1.0])
+                d = Rm.T @ u
+                out[r, c] = chord_by_faces(C, d / np.linalg.norm(d), E)
+        return out
+
+    L0 = chords(poses[0])
+    ref = np.zeros((3, 4))
+    h = 1e-6
+    for r in range(3):
+        for c in range(4):
+            up, dn = poses[0].copy(), poses[0].copy()
+            up[r, c] += h
+            dn[r, c] -= h
+            dL = (chords(up) - chords(dn)) / (2 * h)
+            ref[r, c] = float((g[0] * np.exp(-mu_c * L0) * mu_c * dL).sum())
+    assert (L0 > 0).sum() > 10
+    assert np.abs(grad[0] - ref).max() <= 1e-6 * np.abs(ref).max()
