@@ -15,8 +15,10 @@ Printed (one JSON line on stdout):
                that hit the volume, plus per-ray reads/writes), with its
                duration measured by HIP events on the launch stream
   cpu_baseline the CPU oracle on the same step, timed on the host cores
-  workloads    the other workloads (200x200 16-view batch in fp32 and bf16,
-               2048^2 eval, 360-view helix, 64^3 tiny) as context lines, each
+  workloads    every workload (200x200 16-view batch in fp32 and bf16, the
+               1024^2 step's kernels, 2048^2 eval, 360-view helix, 64^3 tiny)
+               as context lines, with the pose gradient (registration) on the
+               batch and the 1024^2 camera, each
                kernel timed per launch from a replayed HIP graph of
                back-to-back launches (GPU time, no host launch latency)
 
@@ -77,6 +79,7 @@ class Resident:
         need = drr.drr_workspace_bytes(nz, ny, nx, drr.BF16 if bf16 else drr.F32, w.n_views,
                                        w.det_h, w.det_w, w.n_samples, 0)
         self.workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        self.pose_ws = None
 
     def forward(self):
         import ct_forward_projection_amd as drr
@@ -89,6 +92,21 @@ class Resident:
         w = self.w
         drr.drr_backward_volume(w.volume.shape, w.spacing, w.K, self.poses, w.det_h, w.det_w,
                                 w.n_samples, w.mode, self.g, self.s, grad_volume=self.grad)
+
+    def pose_backward(self):
+        import ct_forward_projection_amd as drr
+        w = self.w
+        if self.pose_ws is None:
+            import torch
+            nz, ny, nx = w.volume.shape
+            need = drr.drr_workspace_bytes(nz, ny, nx, drr.BF16 if self.elem_bytes == 2 else drr.F32,
+                                           w.n_views, w.det_h, w.det_w, w.n_samples, 2)
+            self.pose_ws = torch.empty(need, dtype=torch.uint8, device=self.out.device)
+            self.pose_g = torch.ones_like(self.out) if self.g is None else self.g
+            self.grad_poses = torch.empty((w.n_views, 3, 4), device=self.out.device)
+        drr.drr_backward_pose(self.vol, w.spacing, w.K, self.poses, w.det_h, w.det_w, w.n_samples,
+                              w.mode, self.pose_g, grad_poses=self.grad_poses,
+                              workspace=self.pose_ws)
 
     def hit_rays(self) -> int:
         """Rays that intersect the volume box, counted by the library itself: the
@@ -201,11 +219,15 @@ def cpu_baseline(w):
 def workload_lines(dev, reps):
     import workloads as W
     lines = {}
-    for i, bf16 in [(1, False), (2, False), (2, True), (4, False), (5, False)]:
+    for i, bf16 in [(1, False), (2, False), (2, True), (3, False), (4, False), (5, False)]:
         w = W.make_workload(i, with_bf16=bf16)
         res = Resident(w, dev, bf16=bf16)
         hits = res.hit_rays()
         fns = [res.forward] + ([res.backward] if w.grad_out is not None else [])
+        with_pose = i in (2, 3)
+        if with_pose:
+            res.pose_backward()
+            fns.append(res.pose_backward)
         t = time_graph(fns)
         fwd_ms = t[0]
         line = {"views": w.n_views, "detector": [w.det_h, w.det_w], "n_samples": w.n_samples,
@@ -217,6 +239,11 @@ def workload_lines(dev, reps):
                 "forward_hbm_frac": round(forward_bytes(res, hits) / (fwd_ms * 1e-3) / 1e9
                                           / HBM_PEAK_GBS, 4),
                 "hit_rays": hits}
+        if with_pose:
+            pose_ms = t.pop()
+            line["pose_backward_ms"] = round(pose_ms, 4)
+            line["pose_backward_gsamples_s"] = round(w.nominal_samples / pose_ms / 1e6, 1)
+            line["registration_step_fps"] = round(w.n_views / (fwd_ms + pose_ms) * 1e3, 1)
         if len(t) > 1:
             line["backward_ms"] = round(t[1], 4)
             line["backward_gsamples_s"] = round(w.nominal_samples / t[1] / 1e6, 1)

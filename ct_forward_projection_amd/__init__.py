@@ -7,8 +7,9 @@ There is no CPU or PyTorch fallback: if the library is not built, or a tensor
 is not on a GPU, the call raises.
 
 Functions carry the C names (``drr_forward``, ``drr_backward_volume``,
-``drr_workspace_bytes``); ``render`` wraps them as a ``torch.autograd.Function``
-(flashdrr ``VolumeRaycaster`` style: gradients flow to the volume) and
+``drr_backward_pose``, ``drr_workspace_bytes``); ``render`` wraps them as a
+``torch.autograd.Function`` (flashdrr ``VolumeRaycaster`` style: gradients flow
+to the volume and to the view poses) and
 ``project`` / ``backproject`` give diffct's A and A^T (line-integral mode).
 """
 from __future__ import annotations
@@ -50,6 +51,8 @@ def library() -> ctypes.CDLL:
         lib.drr_forward.restype = I
         lib.drr_backward_volume.argtypes = [I, I, I, P, P, P, I, I, I, I, I, P, P, P, P, Z, P]
         lib.drr_backward_volume.restype = I
+        lib.drr_backward_pose.argtypes = [P, I, I, I, I, P, P, P, I, I, I, I, I, P, P, P, Z, P]
+        lib.drr_backward_pose.restype = I
         lib.drr_status_string.argtypes = [I]
         lib.drr_status_string.restype = ctypes.c_char_p
         lib.drr_last_error.restype = ctypes.c_char_p
@@ -180,26 +183,61 @@ def drr_backward_volume(shape: Sequence[int], spacing: Sequence[float], K, poses
     return grad_volume
 
 
+def drr_backward_pose(volume: torch.Tensor, spacing: Sequence[float], K, poses: torch.Tensor,
+                      det_h: int, det_w: int, n_samples: int, mode: int, grad_out: torch.Tensor,
+                      grad_poses: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """dL/dP for L = sum(grad_out * I): (V, 3, 4) fp32 over each view's [R | t]."""
+    volume = _device_tensor(volume, "volume")
+    dtype = _volume_dtype(volume)
+    poses = _device_tensor(poses, "poses", torch.float32)
+    grad_out = _device_tensor(grad_out, "grad_out", torch.float32)
+    nz, ny, nx = (int(s) for s in volume.shape)
+    V = int(poses.shape[0])
+    if grad_out.numel() != V * det_h * det_w:
+        raise ValueError("grad_out has the wrong size")
+    if grad_poses is None:
+        grad_poses = torch.empty((V, 3, 4), dtype=torch.float32, device=volume.device)
+    grad_poses = _device_tensor(grad_poses, "grad_poses", torch.float32)
+    need = drr_workspace_bytes(nz, ny, nx, dtype, V, det_h, det_w, n_samples, 2)
+    if workspace is None:
+        workspace = _workspace(need, volume.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().drr_backward_pose(
+        _ptr(volume), dtype, nz, ny, nx, _host_floats(spacing, 3), _host_floats(K, 9),
+        _ptr(poses), V, det_h, det_w, n_samples, mode, _ptr(grad_out), _ptr(grad_poses),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return grad_poses
+
+
 class _Render(torch.autograd.Function):
     @staticmethod
     def forward(ctx, volume, spacing, K, poses, det_h, det_w, n_samples, mode):
-        img, s = drr_forward(volume.detach(), spacing, K, poses, det_h, det_w, n_samples, mode)
-        ctx.save_for_backward(poses, s)
-        ctx.geom = (tuple(volume.shape), spacing, K, det_h, det_w, n_samples, mode, volume.dtype)
+        img, s = drr_forward(volume.detach(), spacing, K, poses.detach(), det_h, det_w,
+                             n_samples, mode)
+        ctx.save_for_backward(volume.detach(), poses.detach(), s)
+        ctx.geom = (spacing, K, det_h, det_w, n_samples, mode)
         return img
 
     @staticmethod
     def backward(ctx, grad_img):
-        poses, s = ctx.saved_tensors
-        shape, spacing, K, det_h, det_w, n_samples, mode, vdtype = ctx.geom
-        g = drr_backward_volume(shape, spacing, K, poses, det_h, det_w, n_samples, mode,
-                                grad_img.contiguous().float(), s)
-        return g.to(vdtype), None, None, None, None, None, None, None
+        volume, poses, s = ctx.saved_tensors
+        spacing, K, det_h, det_w, n_samples, mode = ctx.geom
+        g_img = grad_img.contiguous().float()
+        g_vol = g_pose = None
+        if ctx.needs_input_grad[0]:
+            g_vol = drr_backward_volume(tuple(volume.shape), spacing, K, poses, det_h, det_w,
+                                        n_samples, mode, g_img, s).to(volume.dtype)
+        if ctx.needs_input_grad[3]:
+            g_pose = drr_backward_pose(volume, spacing, K, poses, det_h, det_w, n_samples, mode,
+                                       g_img)
+        return g_vol, None, None, g_pose, None, None, None, None
 
 
 def render(volume: torch.Tensor, spacing, K, poses: torch.Tensor, det_h: int, det_w: int,
            n_samples: int, mode: int = BEER_LAMBERT) -> torch.Tensor:
-    """Differentiable DRR: image (V, det_h, det_w); gradients flow to ``volume``."""
+    """Differentiable DRR: image (V, det_h, det_w); gradients flow to ``volume``
+    and to ``poses`` (each view's [R | t] entries)."""
     return _Render.apply(volume, spacing, K, poses, det_h, det_w, n_samples, mode)
 
 

@@ -119,12 +119,15 @@ const char* drr_status_string(int status)
 size_t drr_workspace_bytes(int nz, int ny, int nx, int dtype, int n_views, int det_h,
                            int det_w, int n_samples, int for_backward)
 {
-    if (for_backward || nz < 1 || ny < 1 || nx < 1 || n_views < 0 || det_h < 0 || det_w < 0 ||
+    if (nz < 1 || ny < 1 || nx < 1 || n_views < 0 || det_h < 0 || det_w < 0 ||
         n_samples < 1 || (dtype != DRR_F32 && dtype != DRR_BF16))
         return 0;
-    return drr::plan_forward(nz, ny, nx, dtype == DRR_F32 ? 4 : 2,
-                             (long long)n_views * det_h * det_w, n_samples)
-        .workspace_bytes;
+    if (for_backward == DRR_WORKSPACE_VOLUME_BACKWARD) return 0;
+    const size_t cells = drr::plan_forward(nz, ny, nx, dtype == DRR_F32 ? 4 : 2,
+                                           (long long)n_views * det_h * det_w, n_samples)
+                             .workspace_bytes;
+    if (for_backward == DRR_WORKSPACE_POSE_BACKWARD) return drr::pose_acc_bytes(n_views) + cells;
+    return for_backward == DRR_WORKSPACE_FORWARD ? cells : 0;
 }
 
 int drr_forward(const void* volume, int dtype, int nz, int ny, int nx, const float* spacing,
@@ -188,6 +191,45 @@ int drr_backward_volume(int nz, int ny, int nx, const float* spacing, const floa
                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(DRR_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int drr_backward_pose(const void* volume, int dtype, int nz, int ny, int nx, const float* spacing,
+                      const float* K, const float* poses, int n_views, int det_h, int det_w,
+                      int n_samples, int mode, const float* grad_out, float* grad_poses,
+                      void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (dtype != DRR_F32 && dtype != DRR_BF16)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    drr::LaunchArgs a;
+    const int eb = dtype == DRR_F32 ? 4 : 2;
+    int st = check_geometry(nz, ny, nx, eb, spacing, K, poses, n_views, det_h, det_w, n_samples,
+                            mode, a);
+    if (st != DRR_OK) return st;
+    if (!volume) return fail(DRR_ERR_INVALID_ARGUMENT, "volume is NULL");
+    const long long n_rays = (long long)n_views * det_h * det_w;
+    if (n_rays > 0 && !grad_out) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+    if (n_views > 0 && !grad_poses) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_poses is NULL");
+    const drr::ForwardPlan plan = drr::plan_forward(nz, ny, nx, eb, n_rays, n_samples);
+    const size_t acc_bytes = drr::pose_acc_bytes(n_views);
+    const size_t need = acc_bytes + plan.workspace_bytes;
+    if (n_views == 0) return ok();
+    if (workspace_bytes < need)
+        return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
+                    workspace_bytes, need);
+    if (!workspace || ((uintptr_t)workspace & 255u))
+        return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+    if (plan.cells) {
+        a.V.cell_row_bytes = (uint32_t)(nx + 1) * 8u * (uint32_t)eb;
+        a.V.cell_slice_bytes = (uint32_t)(ny + 1) * a.V.cell_row_bytes;
+        a.V.cell_total_bytes = (uint32_t)((long long)(nz + 1) * a.V.cell_slice_bytes);
+    }
+    char* ws = static_cast<char*>(workspace);
+    hipError_t e = drr::launch_backward_pose(a, volume, dtype, plan.cells, ws + acc_bytes,
+                                             reinterpret_cast<double*>(ws), grad_out, grad_poses,
+                                             static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DRR_ERR_HIP, "pose backward launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

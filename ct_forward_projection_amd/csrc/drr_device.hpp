@@ -66,13 +66,12 @@ struct MarchRay {
     float dz;                      // (t1 - t0) / N in mm
 };
 
-__device__ inline void view_setup(const float* __restrict__ pose, const Intrinsics& K,
-                                  ViewGeom& G)
+// K^-1 = adj(K) / det(K), fp64.
+__device__ inline void intrinsics_inverse(const Intrinsics& K, double Ki[9])
 {
     double k[9];
 #pragma unroll
     for (int i = 0; i < 9; ++i) k[i] = (double)K.k[i];
-    // K^-1 = adj(K) / det(K)
     const double a00 = k[4] * k[8] - k[5] * k[7];
     const double a01 = k[2] * k[7] - k[1] * k[8];
     const double a02 = k[1] * k[5] - k[2] * k[4];
@@ -83,9 +82,16 @@ __device__ inline void view_setup(const float* __restrict__ pose, const Intrinsi
     const double a21 = k[1] * k[6] - k[0] * k[7];
     const double a22 = k[0] * k[4] - k[1] * k[3];
     const double inv_det = 1.0 / (k[0] * a00 + k[1] * a10 + k[2] * a20);
-    const double Ki[9] = {a00 * inv_det, a01 * inv_det, a02 * inv_det,
-                          a10 * inv_det, a11 * inv_det, a12 * inv_det,
-                          a20 * inv_det, a21 * inv_det, a22 * inv_det};
+    Ki[0] = a00 * inv_det; Ki[1] = a01 * inv_det; Ki[2] = a02 * inv_det;
+    Ki[3] = a10 * inv_det; Ki[4] = a11 * inv_det; Ki[5] = a12 * inv_det;
+    Ki[6] = a20 * inv_det; Ki[7] = a21 * inv_det; Ki[8] = a22 * inv_det;
+}
+
+__device__ inline void view_setup(const float* __restrict__ pose, const Intrinsics& K,
+                                  ViewGeom& G)
+{
+    double Ki[9];
+    intrinsics_inverse(K, Ki);
     double R[9], t[3];
 #pragma unroll
     for (int r = 0; r < 3; ++r) {

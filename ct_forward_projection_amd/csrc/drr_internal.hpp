@@ -49,4 +49,12 @@ hipError_t launch_forward(const LaunchArgs& a, const void* vol, int dtype, bool 
 hipError_t launch_backward(const LaunchArgs& a, const float* grad_out, const float* s_in,
                            float* grad, hipStream_t stream);
 
+// Pose gradient: the march of the forward (same volume plan) with gradient
+// accumulators; `acc` holds 12 doubles per view.
+inline size_t pose_acc_bytes(int n_views) { return ((size_t)n_views * 12 * 8 + 255) & ~(size_t)255; }
+
+hipError_t launch_backward_pose(const LaunchArgs& a, const void* vol, int dtype, bool cells,
+                                void* cell_buf, double* acc, const float* grad_out,
+                                float* grad_poses, hipStream_t stream);
+
 }  // namespace drr

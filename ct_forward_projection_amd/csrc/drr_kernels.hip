@@ -26,160 +26,9 @@
 
 #include "drr_device.hpp"
 #include "drr_internal.hpp"
+#include "drr_sample.hpp"
 
 namespace drr {
-
-__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Two x-neighbours (x, x+1) of one volume row starting at byte offset `off`.
-template <typename T>
-__device__ inline void load_pair(__amdgpu_buffer_rsrc_t rs, uint32_t off, float& a, float& b);
-
-template <>
-__device__ inline void load_pair<float>(__amdgpu_buffer_rsrc_t rs, uint32_t off, float& a,
-                                        float& b)
-{
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 0);
-    a = __uint_as_float((uint32_t)v[0]);
-    b = __uint_as_float((uint32_t)v[1]);
-}
-
-template <>
-__device__ inline void load_pair<uint16_t>(__amdgpu_buffer_rsrc_t rs, uint32_t off, float& a,
-                                           float& b)
-{
-    const uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 0);
-    a = bf16_lo(v);
-    b = bf16_hi(v);
-}
-
-template <typename T>
-__device__ inline float load_one(__amdgpu_buffer_rsrc_t rs, uint32_t off);
-
-template <>
-__device__ inline float load_one<float>(__amdgpu_buffer_rsrc_t rs, uint32_t off)
-{
-    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, 0));
-}
-
-template <>
-__device__ inline float load_one<uint16_t>(__amdgpu_buffer_rsrc_t rs, uint32_t off)
-{
-    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)off, 0, 0)
-                           << 16);
-}
-
-// How the march reads the eight trilinear corners of a sample.
-//   Pair   (nx >= 2): each of the four (y, z) rows is one x-pair load starting
-//          at xp = clamp(ix, 0, nx - 2); at the clamped x edges the pair still
-//          holds the right voxel and the weight is pinned to 0 (ix < 0) or 1
-//          (ix > nx - 2), which is exactly clamp to edge.  4 loads per sample.
-//   Single (nx == 1): the x corners are read one by one.  8 loads per sample.
-//   Cell   (corner-cell copy): the 8 clamped corners are one 16-byte (bf16) or
-//          two 16-byte (fp32) loads at cell (ix + 1, iy + 1, iz + 1); no clamp.
-enum class Layout { Single, Pair, Cell };
-
-struct SampleAddr {
-    uint32_t o, dy, dz;            // bytes: first row (+ x offset), row steps
-    uint32_t x1;                   // Single: byte offset of the x1 corner minus x0
-    float fx, fy, fz;
-};
-
-template <typename T, Layout L>
-__device__ inline SampleAddr sample_addr(const VolumeDesc& V, int64_t qx, int64_t qy, int64_t qz)
-{
-    SampleAddr A;
-    const int ix = fixed_floor(qx), iy = fixed_floor(qy), iz = fixed_floor(qz);
-    A.fx = fixed_frac(qx);
-    A.fy = fixed_frac(qy);
-    A.fz = fixed_frac(qz);
-    if constexpr (L == Layout::Cell) {
-        // a sample inside the box has -1 <= floor(q) <= n - 1; anything else
-        // would fall outside the buffer range and read zeros, never fault
-        A.o = (uint32_t)(iz + 1) * V.cell_slice_bytes +
-              __umul24((uint32_t)(iy + 1), V.cell_row_bytes) + (uint32_t)(ix + 1) * (8 * sizeof(T));
-        A.dy = A.dz = A.x1 = 0;
-        return A;
-    }
-    const int y0 = clampi(iy, 0, V.n[1] - 1), y1 = clampi(iy + 1, 0, V.n[1] - 1);
-    const int z0 = clampi(iz, 0, V.n[2] - 1), z1 = clampi(iz + 1, 0, V.n[2] - 1);
-    const uint32_t r00 = (uint32_t)z0 * V.slice_bytes + __umul24((uint32_t)y0, V.row_bytes);
-    A.dy = y1 > y0 ? V.row_bytes : 0u;
-    A.dz = z1 > z0 ? V.slice_bytes : 0u;
-    if constexpr (L == Layout::Pair) {
-        const int xp = clampi(ix, 0, V.n[0] - 2);
-        A.fx = __builtin_amdgcn_fmed3f(A.fx + (float)(ix - xp), 0.0f, 1.0f);
-        A.o = r00 + (uint32_t)xp * (uint32_t)sizeof(T);
-        A.x1 = 0;
-    } else {
-        const int x0 = clampi(ix, 0, V.n[0] - 1), x1 = clampi(ix + 1, 0, V.n[0] - 1);
-        A.o = r00 + (uint32_t)x0 * (uint32_t)sizeof(T);
-        A.x1 = (uint32_t)(x1 - x0) * (uint32_t)sizeof(T);
-    }
-    return A;
-}
-
-// The eight corner values (x0, x1) of rows (y0,z0) (y1,z0) (y0,z1) (y1,z1).
-struct CornerVals {
-    float v[8];
-};
-
-template <typename T>
-__device__ inline void load_cell(__amdgpu_buffer_rsrc_t rs, uint32_t off, CornerVals& c);
-
-template <>
-__device__ inline void load_cell<float>(__amdgpu_buffer_rsrc_t rs, uint32_t off, CornerVals& c)
-{
-    const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
-    const auto b = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(off + 16), 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        c.v[i] = __uint_as_float(a[i]);
-        c.v[4 + i] = __uint_as_float(b[i]);
-    }
-}
-
-template <>
-__device__ inline void load_cell<uint16_t>(__amdgpu_buffer_rsrc_t rs, uint32_t off, CornerVals& c)
-{
-    const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        c.v[2 * i] = bf16_lo(a[i]);
-        c.v[2 * i + 1] = bf16_hi(a[i]);
-    }
-}
-
-template <typename T, Layout L>
-__device__ inline void gather(__amdgpu_buffer_rsrc_t rs, const SampleAddr& A, CornerVals& c)
-{
-    if constexpr (L == Layout::Cell) {
-        load_cell<T>(rs, A.o, c);
-        return;
-    }
-    const uint32_t rows[4] = {A.o, A.o + A.dy, A.o + A.dz, A.o + A.dz + A.dy};
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        if constexpr (L == Layout::Pair) {
-            load_pair<T>(rs, rows[r], c.v[2 * r], c.v[2 * r + 1]);
-        } else {
-            c.v[2 * r] = load_one<T>(rs, rows[r]);
-            c.v[2 * r + 1] = load_one<T>(rs, rows[r] + A.x1);
-        }
-    }
-}
-
-__device__ inline float interpolate(const SampleAddr& A, const CornerVals& c)
-{
-    const float c00 = fmaf(A.fx, c.v[1] - c.v[0], c.v[0]);
-    const float c10 = fmaf(A.fx, c.v[3] - c.v[2], c.v[2]);
-    const float c01 = fmaf(A.fx, c.v[5] - c.v[4], c.v[4]);
-    const float c11 = fmaf(A.fx, c.v[7] - c.v[6], c.v[6]);
-    const float c0 = fmaf(A.fy, c10 - c00, c00);
-    const float c1 = fmaf(A.fy, c11 - c01, c01);
-    return fmaf(A.fz, c1 - c0, c0);
-}
 
 // Corner-cell relayout: cell (i, j, k), 0 <= i <= nx etc., holds the eight
 // clamped corners (x0, x1) x (y0, y1) x (z0, z1) of the trilinear cell whose
@@ -667,16 +516,28 @@ static void launch_march_split(const LaunchArgs& a, const T* src, uint32_t src_b
     }
 }
 
+hipError_t launch_cells(const VolumeDesc& V, const void* vol, int dtype, void* cells,
+                        hipStream_t stream)
+{
+    const long long n_cells = (long long)(V.n[0] + 1) * (V.n[1] + 1) * (V.n[2] + 1);
+    const int blocks = (int)((n_cells + 255) / 256 < 16384 ? (n_cells + 255) / 256 : 16384);
+    if (dtype == 0)
+        hipLaunchKernelGGL((drr_cells_kernel<float>), dim3(blocks), dim3(256), 0, stream,
+                           static_cast<const float*>(vol), V.n[0], V.n[1], V.n[2],
+                           static_cast<float*>(cells));
+    else
+        hipLaunchKernelGGL((drr_cells_kernel<uint16_t>), dim3(blocks), dim3(256), 0, stream,
+                           static_cast<const uint16_t*>(vol), V.n[0], V.n[1], V.n[2],
+                           static_cast<uint16_t*>(cells));
+    return hipGetLastError();
+}
+
 template <typename T>
 static hipError_t forward_typed(const LaunchArgs& a, const T* vol, bool cells, T* cell_buf,
                                float* out, float* s_out, hipStream_t stream)
 {
     if (cells) {
-        const long long n_cells = (long long)(a.V.n[0] + 1) * (a.V.n[1] + 1) * (a.V.n[2] + 1);
-        const int blocks = (int)((n_cells + 255) / 256 < 16384 ? (n_cells + 255) / 256 : 16384);
-        hipLaunchKernelGGL((drr_cells_kernel<T>), dim3(blocks), dim3(256), 0, stream, vol,
-                           a.V.n[0], a.V.n[1], a.V.n[2], cell_buf);
-        const hipError_t e = hipGetLastError();
+        const hipError_t e = launch_cells(a.V, vol, sizeof(T) == 4 ? 0 : 1, cell_buf, stream);
         if (e != hipSuccess) return e;
         launch_march_split<T, Layout::Cell>(a, cell_buf, a.V.cell_total_bytes, out, s_out, stream);
     } else if (a.V.n[0] >= 2) {

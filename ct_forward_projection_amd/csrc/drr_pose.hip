@@ -1,0 +1,327 @@
+// drr_pose.hip -- gradient of the DRR with respect to each view's pose.
+//
+// flashdrr.rendering API, VolumeRaycaster class text: rendering is
+// differentiable with respect to the input volume and the view matrices
+// (flashdrr README, Features: gradients flow through both the volume and the
+// camera parameters).  For L = sum_p g_p I_p the kernels return dL/dP_v for
+// every view's 3x4 world-to-camera [R | t], the twelve entries treated as
+// independent (a caller chains them through its own rotation parameters).
+//
+// Per ray (C = -R^T t, unnormalised direction w = R^T u with u = K^-1 m,
+// d = w / |w|, clipped range [t0, t1], dz = (t1 - t0) / N, samples
+// p_k = C + (t0 + (k + 1/2) dz) d):
+//   ds = ddz S0 + dz sum_k grad mu(p_k) . dp_k,   S0 = sum_k mu(p_k),
+// which with G0 = sum_k grad mu_k and G1 = sum_k b_k grad mu_k,
+// b_k = (k + 1/2) / N, collapses to
+//   ds = A . dC + Bv . dd + beta0 dt0 + beta1 dt1,
+//   A = dz G0,  Bv = dz (t0 G0 + (t1 - t0) G1),
+//   beta0 = -S0 / N + dz (G0 - G1) . d,  beta1 = S0 / N + dz G1 . d.
+// The range ends move with the planes that bound them: t = (plane - C_a) / d_a
+// gives dt = -(dC_a + t dd_a) / d_a (and dt0 = 0 when the range starts at the
+// source), so ds = Ac . dC + Bd . dd; with dd = (I - d d^T) dw / |w| this is
+// ds = Ac . dC + Bw . dw, Bw = (I - d d^T) Bd / |w|.  Finally dC/dR_ij =
+// -t_i e_j, dw/dR_ij = u_i e_j, dC/dt_i = -R_i. (row i), so with y = g dI/ds
+// summed over a view's rays, P = sum y Ac and Q_ij = sum y u_i Bw_j:
+//   dL/dR_ij = -t_i P_j + Q_ij,   dL/dt_i = -sum_a R_ia P_a.
+// The march interpolates in fp32 and accumulates S0, G0 and sum_k k grad mu_k
+// per ray in fp64; the chain rule runs in fp64 and the view sums in fp64
+// atomics.
+#include <limits.h>
+
+#include "drr_device.hpp"
+#include "drr_internal.hpp"
+#include "drr_sample.hpp"
+
+namespace drr {
+
+// Ray geometry of the pose gradient: the same slab clip as ray_setup, the axes
+// of the planes that bound the range, and the sample positions in fp64.
+struct RayFrame {
+    double C[3], d[3], u[3];
+    double q0[3], dq[3];     // continuous index of sample 0 and the step, fp64
+    double len, t0, t1;
+    int a_in;      // entry plane axis, -1 when the range starts at the source
+    int a_out;     // exit plane axis
+};
+
+__device__ inline bool ray_frame(const ViewGeom& G, const double Ki[9], const VolumeDesc& V,
+                                 int r, int c, int N, RayFrame& F)
+{
+    const double m0 = (double)c + 0.5, m1 = (double)r + 0.5;
+    double w[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        F.u[a] = Ki[a * 3 + 0] * m0 + Ki[a * 3 + 1] * m1 + Ki[a * 3 + 2];
+        w[a] = G.M[a * 3 + 0] * m0 + G.M[a * 3 + 1] * m1 + G.M[a * 3 + 2];
+        F.C[a] = G.C[a];
+    }
+    F.len = sqrt(w[0] * w[0] + w[1] * w[1] + w[2] * w[2]);
+    const double inv_len = 1.0 / F.len;
+    double t_entry = -__builtin_inf(), t_exit = __builtin_inf();
+    int a_in = -1, a_out = -1;
+    bool inside = true;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        F.d[a] = w[a] * inv_len;
+        const double lo = -V.half_e[a], hi = V.half_e[a];
+        if (F.d[a] == 0.0) {
+            inside = inside && !(G.C[a] < lo || G.C[a] > hi);
+        } else {
+            const double ta = (lo - G.C[a]) / F.d[a];
+            const double tb = (hi - G.C[a]) / F.d[a];
+            const double tmin = fmin(ta, tb), tmax = fmax(ta, tb);
+            if (tmin > t_entry) { t_entry = tmin; a_in = a; }
+            if (tmax < t_exit) { t_exit = tmax; a_out = a; }
+        }
+    }
+    F.t0 = fmax(t_entry, 0.0);
+    F.t1 = t_exit;
+    if (!inside || !(F.t1 > F.t0)) return false;
+    if (!(t_entry > 0.0)) a_in = -1;
+    F.a_in = a_in;
+    F.a_out = a_out;
+    const double dz = (F.t1 - F.t0) / (double)N;
+    const double ts = F.t0 + 0.5 * dz;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        F.q0[a] = (G.C[a] + ts * F.d[a]) * V.inv_s[a] + V.q_off[a];
+        F.dq[a] = dz * F.d[a] * V.inv_s[a];
+    }
+    return true;
+}
+
+// Sample k's position, evaluated directly in fp64 and rounded once to 32.32
+// fixed point.  The gradient of trilinear mu jumps where a sample crosses a
+// cell face, so positions here must not drift: stepping by a rounded fixed
+// increment, as the value-only kernels do, would let the error grow with k.
+__device__ inline int64_t sample_fixed(const RayFrame& F, int a, int k)
+{
+    return to_fixed(fma((double)k, F.dq[a], F.q0[a]));
+}
+
+// Workgroup sum of twelve doubles, returned to threads 0..11 (one each).
+__device__ inline double block_sum12(const double v_in[12], double* red)
+{
+    double v[12];
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+        v[i] = v_in[i];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) v[i] += __shfl_xor(v[i], off, 64);
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < 12; ++i) red[wave * 12 + i] = v[i];
+    }
+    __syncthreads();
+    double t = 0.0;
+    if (threadIdx.x < 12)
+        for (int w = 0; w < kBlock / 64; ++w) t += red[w * 12 + threadIdx.x];
+    return t;
+}
+
+template <typename T, Layout L, int MODE>
+__global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
+    const T* __restrict__ src, uint32_t src_bytes, VolumeDesc V, Intrinsics K,
+    const float* __restrict__ poses, int H, int W, int N, int tiles_x, int tiles_per_view,
+    const float* __restrict__ grad_out, double* __restrict__ acc)
+{
+    __shared__ double red[(kBlock / 64) * 12];
+    const int tile = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
+    const PixelCoord px = tile_pixel(tile, tiles_x, tiles_per_view);
+    double contrib[12];
+#pragma unroll
+    for (int i = 0; i < 12; ++i) contrib[i] = 0.0;
+
+    const float g = (px.r < H && px.c < W) ? grad_out[((size_t)px.view * H + px.r) * W + px.c]
+                                           : 0.0f;
+    RayFrame F;
+    bool hit = false;
+    if (g != 0.0f) {
+        ViewGeom G;
+        view_setup(poses + 12 * px.view, K, G);
+        double Ki[9];
+        intrinsics_inverse(K, Ki);
+        hit = ray_frame(G, Ki, V, px.r, px.c, N, F);
+    }
+    if (hit) {
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, (int)src_bytes, kBufferWord3);
+        // fp64 accumulators: sum grad mu . d telescopes to about mu(exit) - mu(entry),
+        // a small difference of large edge terms that fp32 sums would round away
+        double s0 = 0.0, g0[3] = {0.0, 0.0, 0.0}, h1[3] = {0.0, 0.0, 0.0};
+        constexpr int kGroup = 4;
+        int k = 0;
+        for (; k + kGroup <= N; k += kGroup) {
+            SampleAddr A[kGroup];
+            CornerVals c[kGroup];
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i)
+                A[i] = sample_addr<T, L>(V, sample_fixed(F, 0, k + i), sample_fixed(F, 1, k + i),
+                                         sample_fixed(F, 2, k + i));
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) gather<T, L>(rs, A[i], c[i]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) {
+                float gq[3];
+                s0 += (double)interpolate_grad(A[i], c[i], gq);
+                const double kd = (double)(k + i);
+#pragma unroll
+                for (int a = 0; a < 3; ++a) {
+                    g0[a] += (double)gq[a];
+                    h1[a] = fma(kd, (double)gq[a], h1[a]);
+                }
+            }
+        }
+        for (; k < N; ++k) {
+            const SampleAddr A = sample_addr<T, L>(V, sample_fixed(F, 0, k), sample_fixed(F, 1, k),
+                                                   sample_fixed(F, 2, k));
+            CornerVals c;
+            gather<T, L>(rs, A, c);
+            float gq[3];
+            s0 += (double)interpolate_grad(A, c, gq);
+#pragma unroll
+            for (int a = 0; a < 3; ++a) {
+                g0[a] += (double)gq[a];
+                h1[a] = fma((double)k, (double)gq[a], h1[a]);
+            }
+        }
+        // chain rule, fp64
+        const double Nd = (double)N, dz = (F.t1 - F.t0) / Nd;
+        const double S0 = s0;
+        double G0[3], G1[3];
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            G0[a] = g0[a] * V.inv_s[a];                               // per mm
+            G1[a] = (h1[a] + 0.5 * g0[a]) / Nd * V.inv_s[a];
+        }
+        const double s = dz * S0;
+        const double y = (double)g * (MODE == kBeerLambert ? exp(-s) : 1.0);
+        double G0d = 0.0, G1d = 0.0;
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            G0d += G0[a] * F.d[a];
+            G1d += G1[a] * F.d[a];
+        }
+        const double beta0 = -S0 / Nd + dz * (G0d - G1d);
+        const double beta1 = S0 / Nd + dz * G1d;
+        double Ac[3], Bd[3];
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            Ac[a] = dz * G0[a];
+            Bd[a] = dz * (F.t0 * G0[a] + (F.t1 - F.t0) * G1[a]);
+        }
+        if (F.a_in >= 0) {
+            Ac[F.a_in] -= beta0 / F.d[F.a_in];
+            Bd[F.a_in] -= beta0 * F.t0 / F.d[F.a_in];
+        }
+        Ac[F.a_out] -= beta1 / F.d[F.a_out];
+        Bd[F.a_out] -= beta1 * F.t1 / F.d[F.a_out];
+        const double dBd = Bd[0] * F.d[0] + Bd[1] * F.d[1] + Bd[2] * F.d[2];
+        double Bw[3];
+#pragma unroll
+        for (int a = 0; a < 3; ++a) Bw[a] = (Bd[a] - F.d[a] * dBd) / F.len;
+#pragma unroll
+        for (int a = 0; a < 3; ++a) contrib[a] = y * Ac[a];
+#pragma unroll
+        for (int i = 0; i < 3; ++i)
+#pragma unroll
+            for (int j = 0; j < 3; ++j) contrib[3 + i * 3 + j] = y * F.u[i] * Bw[j];
+    }
+    const double t = block_sum12(contrib, red);
+    if (threadIdx.x < 12 && t != 0.0) unsafeAtomicAdd(acc + 12 * px.view + threadIdx.x, t);
+}
+
+// dL/dR_ij = -t_i P_j + Q_ij, dL/dt_i = -sum_a R_ia P_a, written as 3x4 rows.
+__global__ __launch_bounds__(64) void drr_pose_finalize_kernel(const double* __restrict__ acc,
+                                                                const float* __restrict__ poses,
+                                                                int n_views,
+                                                                float* __restrict__ grad_poses)
+{
+    const int id = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (id >= n_views * 12) return;
+    const int v = id / 12, e = id % 12, r = e / 4, c = e % 4;
+    const double* P = acc + 12 * v;
+    const double* Q = P + 3;
+    const float* pose = poses + 12 * v;
+    double val;
+    if (c < 3) {
+        val = -(double)pose[r * 4 + 3] * P[c] + Q[r * 3 + c];
+    } else {
+        val = -((double)pose[r * 4 + 0] * P[0] + (double)pose[r * 4 + 1] * P[1] +
+                (double)pose[r * 4 + 2] * P[2]);
+    }
+    grad_poses[id] = (float)val;
+}
+
+__global__ __launch_bounds__(256) void drr_zero_f64_kernel(double* __restrict__ p, int n)
+{
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n) p[i] = 0.0;
+}
+
+// Corner-cell relayout (shared with the forward).
+hipError_t launch_cells(const VolumeDesc& V, const void* vol, int dtype, void* cells,
+                        hipStream_t stream);
+
+template <typename T, Layout L>
+static void launch_pose(const LaunchArgs& a, const T* src, uint32_t src_bytes,
+                        const float* grad_out, double* acc, hipStream_t stream)
+{
+    const int tiles_x = (a.W + kTile - 1) / kTile, tiles_y = (a.H + kTile - 1) / kTile;
+    const int tiles_per_view = tiles_x * tiles_y;
+    const dim3 grid(tiles_per_view * a.n_views), block(kBlock);
+    if (a.mode == kBeerLambert)
+        hipLaunchKernelGGL((drr_pose_grad_kernel<T, L, kBeerLambert>), grid, block, 0, stream, src,
+                           src_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view,
+                           grad_out, acc);
+    else
+        hipLaunchKernelGGL((drr_pose_grad_kernel<T, L, kLineIntegral>), grid, block, 0, stream,
+                           src, src_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                           tiles_per_view, grad_out, acc);
+}
+
+template <typename T>
+static void pose_typed(const LaunchArgs& a, const T* vol, bool cells, T* cell_buf,
+                       const float* grad_out, double* acc, hipStream_t stream)
+{
+    if (cells)
+        launch_pose<T, Layout::Cell>(a, cell_buf, a.V.cell_total_bytes, grad_out, acc, stream);
+    else if (a.V.n[0] >= 2)
+        launch_pose<T, Layout::Pair>(a, vol, a.V.total_bytes, grad_out, acc, stream);
+    else
+        launch_pose<T, Layout::Single>(a, vol, a.V.total_bytes, grad_out, acc, stream);
+}
+
+hipError_t launch_backward_pose(const LaunchArgs& a, const void* vol, int dtype, bool cells,
+                                void* cell_buf, double* acc, const float* grad_out,
+                                float* grad_poses, hipStream_t stream)
+{
+    if (a.n_views == 0) return hipSuccess;
+    const int n_acc = 12 * a.n_views;
+    hipLaunchKernelGGL(drr_zero_f64_kernel, dim3((n_acc + 255) / 256), dim3(256), 0, stream, acc,
+                       n_acc);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if ((long long)a.H * a.W > 0) {
+        if (cells) {
+            e = launch_cells(a.V, vol, dtype, cell_buf, stream);
+            if (e != hipSuccess) return e;
+        }
+        if (dtype == 0)
+            pose_typed<float>(a, static_cast<const float*>(vol), cells,
+                              static_cast<float*>(cell_buf), grad_out, acc, stream);
+        else
+            pose_typed<uint16_t>(a, static_cast<const uint16_t*>(vol), cells,
+                                 static_cast<uint16_t*>(cell_buf), grad_out, acc, stream);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(drr_pose_finalize_kernel, dim3((n_acc + 63) / 64), dim3(64), 0, stream, acc,
+                       a.poses, a.n_views, grad_poses);
+    return hipGetLastError();
+}
+
+}  // namespace drr

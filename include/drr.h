@@ -75,10 +75,17 @@ typedef enum {
  * 0 <= n_views, det_h, det_w and n_views*det_h*det_w < 2^31 rays;
  * 1 <= n_samples <= 2^24. */
 
-/* Bytes of device workspace drr_forward (for_backward = 0) or
- * drr_backward_volume (for_backward = 1) needs for these sizes; 0 means no
- * workspace is needed (a NULL workspace is then accepted).  Returns 0 as well
- * for invalid sizes (the call itself then reports the error). */
+/* Which call a workspace query is for. */
+#define DRR_WORKSPACE_FORWARD 0
+#define DRR_WORKSPACE_VOLUME_BACKWARD 1
+#define DRR_WORKSPACE_POSE_BACKWARD 2
+
+/* Bytes of device workspace drr_forward (for_backward = 0), drr_backward_volume
+ * (1) or drr_backward_pose (2) needs for these sizes; 0 means no workspace is
+ * needed (a NULL workspace is then accepted).  Returns 0 as well for invalid
+ * sizes (the call itself then reports the error).  The forward and the pose
+ * backward use the workspace for a corner-cell copy of the volume (8 clamped
+ * trilinear corners per cell) when rays reuse cells enough for it to pay. */
 size_t drr_workspace_bytes(int nz, int ny, int nx, int dtype, int n_views, int det_h,
                            int det_w, int n_samples, int for_backward);
 
@@ -116,6 +123,27 @@ int drr_backward_volume(int nz, int ny, int nx, const float *spacing, const floa
                         int mode, const float *grad_out, const float *line_integral,
                         float *grad_volume, void *workspace, size_t workspace_bytes,
                         void *stream);
+
+/* Pose gradient of the forward (flashdrr API, VolumeRaycaster class text:
+ * rendering is differentiable with respect to the view matrices; flashdrr
+ * README, Features: gradients through the camera parameters).  For
+ * L = sum_p grad_out_p I_p it writes dL/dP_v for every view's 3x4
+ * world-to-camera [R | t], the twelve entries treated as independent (chain
+ * them through any rotation parameterisation on the caller's side).  The
+ * derivative includes the motion of the clipped range's end points (the box
+ * planes that bound it) and of the sample spacing dz; the trilinear field is
+ * differentiated within each cell (one-sided on cell faces).
+ *   volume, dtype, spacing, K, poses, det_h, det_w, n_samples, mode: as drr_forward
+ *   grad_out      device, n_views*det_h*det_w floats (dL/dI)
+ *   grad_poses    device, n_views x 12 floats, row-major 3x4, OVERWRITTEN
+ *   workspace     device, >= drr_workspace_bytes(..., DRR_WORKSPACE_POSE_BACKWARD),
+ *                 256-byte aligned (it is never empty for n_views > 0)
+ * View sums use fp64 atomics, so the result may differ between runs in the
+ * last bits. */
+int drr_backward_pose(const void *volume, int dtype, int nz, int ny, int nx, const float *spacing,
+                      const float *K, const float *poses, int n_views, int det_h, int det_w,
+                      int n_samples, int mode, const float *grad_out, float *grad_poses,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static description of a drr_status value. */
 const char *drr_status_string(int status);

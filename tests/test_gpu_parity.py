@@ -377,3 +377,80 @@ def test_non_finite_upstream_gradient_propagates(dev):
     assert np.array_equal(np.isnan(grad), np.isnan(ref))
     ok = ~np.isnan(ref)
     assert normwise_err(grad[ok], ref[ok]) <= GRAD
+
+
+# ------------------------------------------------------------------ pose gradient
+
+def gpu_pose_grad(w, dev, g, bf16=False):
+    if bf16:
+        vol = torch.from_numpy(w.volume_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        vol = torch.from_numpy(w.volume).to(dev)
+    poses = torch.from_numpy(w.poses).to(dev)
+    out = drr.drr_backward_pose(vol, w.spacing, w.K, poses, w.det_h, w.det_w, w.n_samples,
+                                w.mode, torch.from_numpy(np.ascontiguousarray(g)).to(dev))
+    torch.cuda.synchronize()
+    return out.cpu().double().numpy()
+
+
+def check_pose(gpu, ref, what):
+    """Per view, max |g - o| / max |o| over the twelve entries."""
+    worst = 0.0
+    for v in range(ref.shape[0]):
+        worst = max(worst, normwise_err(gpu[v], ref[v]))
+    say(f"{what}: pose gradient normwise err {worst:.3e}")
+    assert worst <= GRAD
+    return worst
+
+
+@pytest.mark.parametrize("seed,mode,shape,det,n", [
+    (61, W.BEER_LAMBERT, (9, 10, 11), (13, 17), 37),
+    (62, W.LINE_INTEGRAL, (16, 5, 33), (40, 23), 64),
+    (63, W.BEER_LAMBERT, (20, 20, 1), (9, 50), 9),
+    (64, W.LINE_INTEGRAL, (31, 29, 27), (65, 47), 203),
+])
+def test_pose_gradient_random(dev, seed, mode, shape, det, n):
+    w = W.make_random_small(seed, shape=shape, n_views=3, det=det, n_samples=n, mode=mode)
+    say(f"case: pose gradient seed={seed} mode={mode} shape={shape} det={det} N={n}")
+    ref = oracle.pose_gradient(w.volume, w.spacing, w.K, w.poses, w.det_h, w.det_w,
+                               w.n_samples, w.mode, w.grad_out)
+    check_pose(gpu_pose_grad(w, dev, w.grad_out), ref, f"random {seed}")
+
+
+def test_pose_gradient_batch_workload(dev, batch_workload):
+    """The 16-view 200x200 batch (x-pair reads in fp32, corner cells in bf16)."""
+    w = batch_workload
+    g = np.random.default_rng(71).uniform(-1, 1, size=(16, 200, 200)).astype(np.float32)
+    say("case: pose gradient, 16-view batch")
+    ref = oracle.pose_gradient(w.volume, w.spacing, w.K, w.poses, 200, 200, 256, w.mode, g)
+    check_pose(gpu_pose_grad(w, dev, g), ref, "batch fp32")
+    ref16 = oracle.pose_gradient(w.volume_bf16_as_f32(), w.spacing, w.K, w.poses, 200, 200, 256,
+                                 w.mode, g)
+    check_pose(gpu_pose_grad(w, dev, g, bf16=True), ref16, "batch bf16")
+
+
+def test_pose_gradient_train_workload_row_band(dev):
+    """The 1024^2 train-step camera restricted to a 96-row band through the
+    volume's centre (same rays; cy moved so the band is the whole detector)."""
+    w = W.make_workload(3)
+    K = w.K.copy()
+    K[1, 2] -= 464.0                  # rows 464..559 of the full detector
+    band = W.Workload("train-band", w.volume, w.spacing, K, w.poses, 96, 1024, 512, w.mode,
+                      grad_out=np.ascontiguousarray(w.grad_out[:, 464:560, :]))
+    say("case: pose gradient, 1024-wide band of the train-step camera")
+    ref = oracle.pose_gradient(band.volume, band.spacing, band.K, band.poses, 96, 1024, 512,
+                               band.mode, band.grad_out)
+    check_pose(gpu_pose_grad(band, dev, band.grad_out), ref, "train band")
+
+
+def test_pose_gradient_through_autograd(dev):
+    w = W.make_random_small(65, shape=(12, 14, 16), n_views=2, det=(20, 24), n_samples=40)
+    vol = torch.from_numpy(w.volume).to(dev).requires_grad_(True)
+    poses = torch.from_numpy(w.poses).to(dev).requires_grad_(True)
+    img = drr.render(vol, w.spacing, w.K, poses, w.det_h, w.det_w, w.n_samples, w.mode)
+    (img * torch.from_numpy(w.grad_out).to(dev)).sum().backward()
+    ref = oracle.pose_gradient(w.volume, w.spacing, w.K, w.poses, w.det_h, w.det_w,
+                               w.n_samples, w.mode, w.grad_out)
+    check_pose(poses.grad.cpu().double().numpy(), ref, "autograd")
+    ref_v, _ = oracle.adjoint_workload(w)
+    assert normwise_err(vol.grad.cpu().numpy(), ref_v) <= GRAD
