@@ -186,9 +186,10 @@ def roofline(name, alg_bytes, ms, traffic=None):
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; otherwise None."""
+def measured_traffic(kernels):
+    """HBM bytes per launch of a pass (the sum over its kernels) from the
+    committed rocprofv3 counter summary, if it was taken on the current kernel
+    sources and covers every kernel; otherwise None."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     try:
         with open(path) as f:
@@ -197,8 +198,13 @@ def measured_traffic(kernel: str):
         return None
     if d.get("kernel_revision") != kernel_revision():
         return None
-    k = d.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("hbm_bytes_per_launch")
+    total = 0.0
+    for name in kernels:
+        k = d.get("kernels", {}).get(name)
+        if k is None or k.get("hbm_bytes_per_launch") is None:
+            return None
+        total += k["hbm_bytes_per_launch"]
+    return round(total)
 
 
 def cpu_baseline(w):
@@ -257,8 +263,9 @@ def workload_lines(dev, reps):
 
 def pmc_pass(kind: str, dev):
     """A short fixed launch sequence for rocprofv3 counter runs: 3 launches of
-    the chosen kernel on the train-step workload, or a plain 1 GiB copy (the
-    calibration kernel for the byte counters)."""
+    the chosen pass (forward, volume backward or pose backward) on the
+    train-step workload, or a plain 1 GiB copy (the calibration kernel for the
+    byte counters)."""
     import torch
 
     import workloads as W
@@ -273,8 +280,9 @@ def pmc_pass(kind: str, dev):
     res = Resident(W.make_workload(3), dev)
     res.forward()
     torch.cuda.synchronize()
+    run = {"forward": res.forward, "backward": res.backward, "pose": res.pose_backward}[kind]
     for _ in range(3):
-        res.forward() if kind == "forward" else res.backward()
+        run()
     torch.cuda.synchronize()
     log(f"pmc pass: 3 x {kind}")
 
@@ -296,8 +304,12 @@ PMC_SETS = {
     "ta": ["TA_TA_BUSY_sum", "TA_BUSY_avr", "TD_TD_BUSY_sum", "SQ_LDS_BANK_CONFLICT",
            "SQ_LDS_ADDR_CONFLICT"],
 }
-KERNEL_KEYS = {"forward": "drr_march_kernel", "backward": "drr_scatter_kernel",
-               "copy": "copy"}
+# kernels whose counters each pass reports (matched as substrings of the name)
+KERNEL_KEYS = {"forward": ["drr_cells_kernel", "drr_march_kernel"],
+               "backward": ["drr_fill_kernel", "drr_scatter_kernel"],
+               "pose": ["drr_cells_kernel", "drr_pose_grad_kernel"],
+               "copy": ["copy"]}
+PMC_KINDS = ("forward", "backward", "pose", "copy")
 
 
 def _csv_rows(path):
@@ -340,66 +352,75 @@ def profile_summary(root: str):
             f.write("\n".join(lines) + "\n")
         log("wrote", path)
     # counters
-    values = {}
-    for kind in ("forward", "backward", "copy"):
+    values = {}   # (pass, kernel) -> counter -> per-dispatch values
+    for kind in PMC_KINDS:
         for tag in PMC_SETS:
             for path in _find(os.path.join(root, f"{kind}_{tag}"), "counter_collection.csv"):
                 per = {}
                 for r in _csv_rows(path):
-                    if KERNEL_KEYS[kind] not in r.get("Kernel_Name", ""):
+                    name = r.get("Kernel_Name", "")
+                    key = next((k for k in KERNEL_KEYS[kind] if k in name), None)
+                    if key is None:
                         continue
-                    key = (r["Counter_Name"], r["Dispatch_Id"])
-                    per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
-                for (cname, _), v in per.items():
-                    values.setdefault(kind, {}).setdefault(cname, []).append(v)
+                    per_key = (key, r["Counter_Name"], r["Dispatch_Id"])
+                    per[per_key] = per.get(per_key, 0.0) + float(r["Counter_Value"])
+                for (key, cname, _), v in per.items():
+                    values.setdefault((kind, key), {}).setdefault(cname, []).append(v)
     if not values:
         return
     med = {k: {c: float(np.median(v)) for c, v in d.items()} for k, d in values.items()}
     copy_bytes = float(1 << 30)
     fetch_factor = write_factor = None
-    if "copy" in med:
-        if med["copy"].get("FETCH_SIZE"):
-            fetch_factor = copy_bytes / (med["copy"]["FETCH_SIZE"] * 1024.0)
-        if med["copy"].get("WRITE_SIZE"):
-            write_factor = copy_bytes / (med["copy"]["WRITE_SIZE"] * 1024.0)
+    cm = med.get(("copy", "copy"), {})
+    if cm.get("FETCH_SIZE"):
+        fetch_factor = copy_bytes / (cm["FETCH_SIZE"] * 1024.0)
+    if cm.get("WRITE_SIZE"):
+        write_factor = copy_bytes / (cm["WRITE_SIZE"] * 1024.0)
     traffic = {"kernel_revision": rev, "fetch_calibration": fetch_factor,
                "write_calibration": write_factor, "kernels": {}}
     lines = ["# Hardware counters per dispatch (median), train-step workload 1024x1024", "",
              "Commands (one counter set per run):", ""]
     for tag, counters in PMC_SETS.items():
         lines.append("- `" + PROFILE_COMMANDS["pmc"].format(counters=" ".join(counters),
-                                                            kind="<forward|backward|copy>",
+                                                            kind="<forward|backward|pose|copy>",
                                                             tag=tag) + "`")
     lines += ["", f"Kernel sources revision: `{rev}`", "",
               "Calibration: a plain 1 GiB device copy (`bench.py --pmc-pass copy`) reads "
               f"FETCH_SIZE x {fetch_factor} and WRITE_SIZE x {write_factor} of its known size "
               "(factors applied below).", ""]
-    for kind, name in (("forward", "drr_march_kernel"), ("backward", "drr_scatter_kernel")):
-        if kind not in med:
-            continue
-        m = med[kind]
-        lines += [f"## {name}", "", "| counter | value |", "|---|---|"]
-        for c in sorted(m):
-            lines.append(f"| {c} | {m[c]:.6g} |")
-        fb = m.get("FETCH_SIZE", 0.0) * 1024.0 * (fetch_factor or 1.0)
-        wb = m.get("WRITE_SIZE", 0.0) * 1024.0 * (write_factor or 1.0)
-        hit = m.get("TCC_HIT_sum"), m.get("TCC_MISS_sum")
-        if all(h is not None for h in hit) and sum(hit) > 0:
-            lines.append(f"| L2 hit rate | {hit[0] / (hit[0] + hit[1]):.4f} |")
-        if m.get("SQ_ACTIVE_INST_VALU") and m.get("SQ_BUSY_CYCLES"):
-            lines.append(f"| VALU active / SQ busy cycles | "
-                         f"{m['SQ_ACTIVE_INST_VALU'] / m['SQ_BUSY_CYCLES']:.4f} |")
-        lines += ["", f"HBM-side traffic per launch (calibrated): read {fb / 1e6:.1f} MB, "
-                      f"write {wb / 1e6:.1f} MB, total {(fb + wb) / 1e6:.1f} MB", ""]
-        if fb or wb:
-            traffic["kernels"][name] = {"hbm_bytes_per_launch": fb + wb, "read_bytes": fb,
-                                        "write_bytes": wb}
+    for kind in ("forward", "backward", "pose"):
+        for name in KERNEL_KEYS[kind]:
+            if (kind, name) not in med or (kind == "pose" and name == "drr_cells_kernel"):
+                continue
+            _counter_table(lines, traffic, name, f"{kind} pass", med[(kind, name)],
+                           fetch_factor, write_factor)
     path = os.path.join(prof_dir, "counters_train_step_1024.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(os.path.join(prof_dir, "pmc_traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
     log("wrote", path)
+
+
+def _counter_table(lines, traffic, name, where, m, fetch_factor, write_factor):
+    """One kernel's median counters as a markdown table, plus its calibrated
+    HBM bytes per launch into ``traffic``."""
+    lines += [f"## {name} ({where})", "", "| counter | value |", "|---|---|"]
+    for c in sorted(m):
+        lines.append(f"| {c} | {m[c]:.6g} |")
+    fb = m.get("FETCH_SIZE", 0.0) * 1024.0 * (fetch_factor or 1.0)
+    wb = m.get("WRITE_SIZE", 0.0) * 1024.0 * (write_factor or 1.0)
+    hit = m.get("TCC_HIT_sum"), m.get("TCC_MISS_sum")
+    if all(h is not None for h in hit) and sum(hit) > 0:
+        lines.append(f"| L2 hit rate | {hit[0] / (hit[0] + hit[1]):.4f} |")
+    if m.get("SQ_ACTIVE_INST_VALU") and m.get("SQ_BUSY_CYCLES"):
+        lines.append(f"| VALU active / SQ busy cycles | "
+                     f"{m['SQ_ACTIVE_INST_VALU'] / m['SQ_BUSY_CYCLES']:.4f} |")
+    lines += ["", f"HBM-side traffic per launch (calibrated): read {fb / 1e6:.1f} MB, "
+                  f"write {wb / 1e6:.1f} MB, total {(fb + wb) / 1e6:.1f} MB", ""]
+    if fb or wb:
+        traffic["kernels"][name] = {"hbm_bytes_per_launch": fb + wb, "read_bytes": fb,
+                                    "write_bytes": wb}
 
 
 def main():
@@ -409,7 +430,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-workloads", action="store_true")
-    ap.add_argument("--pmc-pass", choices=["forward", "backward", "copy"])
+    ap.add_argument("--pmc-pass", choices=list(PMC_KINDS))
     ap.add_argument("--profile-summary", metavar="DIR",
                     help="summarise rocprofv3 outputs under DIR into profiles/ (CPU only)")
     args = ap.parse_args()
@@ -456,10 +477,12 @@ def main():
 
     # per-kernel GPU time of the same step, HIP events on the launch stream
     fwd_ms, bwd_ms = time_events([res.forward, res.backward], max(args.steps, 1))
-    rf = roofline("drr_march_kernel", forward_bytes(res, hits), fwd_ms,
-                  measured_traffic("drr_march_kernel"))
+    # each pass is one ABI call: the forward launches the corner-cell relayout
+    # and the march, the backward the gradient fill and the scatter
+    rf = roofline("drr_march_kernel (with corner-cell relayout)", forward_bytes(res, hits), fwd_ms,
+                  measured_traffic(["drr_cells_kernel", "drr_march_kernel"]))
     rb = roofline("drr_scatter_kernel (with gradient fill)", backward_bytes(res, hits), bwd_ms,
-                  measured_traffic("drr_scatter_kernel"))
+                  measured_traffic(["drr_fill_kernel", "drr_scatter_kernel"]))
     dominant, other = (rb, rf) if bwd_ms >= fwd_ms else (rf, rb)
 
     out = {
