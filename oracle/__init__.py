@@ -64,6 +64,11 @@ def _load():
     lib.oracle_chords.restype = I
     lib.oracle_pose_gradient.argtypes = [P, I, I, I, P, P, P, I, I, I, I, I, P, P, I]
     lib.oracle_pose_gradient.restype = I
+    lib.oracle_siddon_forward.argtypes = [P, I, I, I, P, P, P, I, I, I, I, P, P, I]
+    lib.oracle_siddon_forward.restype = I
+    lib.oracle_siddon_adjoint.argtypes = [P, I, I, I, P, P, P, I, I, I, I, P, P, I,
+                                          ctypes.c_longlong]
+    lib.oracle_siddon_adjoint.restype = I
     lib.oracle_max_threads.restype = I
     _lib = lib
     return lib
@@ -208,6 +213,58 @@ def pose_gradient(volume: np.ndarray, spacing, K, poses, det_h: int, det_w: int,
     if rc != 0:
         raise ValueError("oracle_pose_gradient: invalid arguments")
     return out.reshape(V, 3, 4)
+
+
+def siddon_forward(volume: np.ndarray, spacing, K, poses, det_h: int, det_w: int, mode: int,
+                   n_threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Forward DRR in the cell-constant (Siddon) model: s = sum_v mu_v l_v.
+    Returns (image, line_integral), both float64 (V, H, W)."""
+    lib = _load()
+    vol = np.ascontiguousarray(volume, dtype=np.float32)
+    nz, ny, nx = vol.shape
+    sp, Kd, Pd = _f64(spacing), _f64(K), _f64(poses).reshape(-1, 12)
+    V = Pd.shape[0]
+    out = np.zeros((V, det_h, det_w), dtype=np.float64)
+    s = np.zeros((V, det_h, det_w), dtype=np.float64)
+    rc = lib.oracle_siddon_forward(_ptr(vol), nz, ny, nx, _ptr(sp), _ptr(Kd), _ptr(Pd), V,
+                                   det_h, det_w, mode, _ptr(out), _ptr(s), _threads(n_threads))
+    if rc != 0:
+        raise ValueError("oracle_siddon_forward: invalid arguments or out of memory")
+    return out, s
+
+
+def siddon_adjoint(volume: Optional[np.ndarray], shape, spacing, K, poses, det_h: int,
+                   det_w: int, mode: int, grad_out: np.ndarray, n_threads: Optional[int] = None,
+                   max_buffer_bytes: int = 4 << 30) -> Tuple[np.ndarray, int]:
+    """Matched adjoint of ``siddon_forward`` (volume gradient for dL/dI =
+    grad_out).  Returns (grad float64 (nz, ny, nx), threads used)."""
+    lib = _load()
+    nz, ny, nx = (int(x) for x in shape)
+    vol = None if volume is None else np.ascontiguousarray(volume, dtype=np.float32)
+    sp, Kd, Pd = _f64(spacing), _f64(K), _f64(poses).reshape(-1, 12)
+    V = Pd.shape[0]
+    g = np.ascontiguousarray(grad_out, dtype=np.float64).reshape(V, det_h, det_w)
+    grad = np.zeros((nz, ny, nx), dtype=np.float64)
+    rc = lib.oracle_siddon_adjoint(None if vol is None else _ptr(vol), nz, ny, nx, _ptr(sp),
+                                   _ptr(Kd), _ptr(Pd), V, det_h, det_w, mode, _ptr(g),
+                                   _ptr(grad), _threads(n_threads), int(max_buffer_bytes))
+    if rc < 1:
+        raise ValueError("oracle_siddon_adjoint: invalid arguments or out of memory")
+    return grad, int(rc)
+
+
+def siddon_forward_workload(w, n_threads: Optional[int] = None, use_bf16: bool = False):
+    """Convenience: cell-constant forward of a ``workloads.Workload``."""
+    vol = w.volume_bf16_as_f32() if use_bf16 else w.volume
+    return siddon_forward(vol, w.spacing, w.K, w.poses, w.det_h, w.det_w, w.mode, n_threads)
+
+
+def siddon_adjoint_workload(w, grad_out=None, n_threads: Optional[int] = None,
+                            max_buffer_bytes: int = 4 << 30):
+    """Convenience: cell-constant volume gradient of a ``workloads.Workload``."""
+    g = w.grad_out if grad_out is None else grad_out
+    return siddon_adjoint(w.volume, w.volume.shape, w.spacing, w.K, w.poses, w.det_h, w.det_w,
+                          w.mode, g, n_threads, max_buffer_bytes)
 
 
 def forward_workload(w, n_threads: Optional[int] = None, use_bf16: bool = False):
