@@ -108,6 +108,18 @@ class Resident:
                               w.mode, self.pose_g, grad_poses=self.grad_poses,
                               workspace=self.pose_ws)
 
+    def siddon_forward(self):
+        import ct_forward_projection_amd as drr
+        w = self.w
+        drr.drr_forward_siddon(self.vol, w.spacing, w.K, self.poses, w.det_h, w.det_w, w.mode,
+                               out=self.out, line_integral=self.s)
+
+    def siddon_backward(self):
+        import ct_forward_projection_amd as drr
+        w = self.w
+        drr.drr_backward_volume_siddon(w.volume.shape, w.spacing, w.K, self.poses, w.det_h,
+                                       w.det_w, w.mode, self.g, self.s, grad_volume=self.grad)
+
     def hit_rays(self) -> int:
         """Rays that intersect the volume box, counted by the library itself: the
         line integral of a volume of ones is the chord, > 0 exactly on hits."""
@@ -168,6 +180,42 @@ def time_graph(fns, min_ms=40.0):
         out.append(float(np.median(ts)))
         del g
     return out
+
+
+def siddon_pieces(w) -> int:
+    """Ray-voxel pieces of a workload (the cell-constant model's unit of work):
+    a ray crossing the box from entry point p0 to exit point p1 visits
+    1 + sum_a |floor index of p1 - floor index of p0| voxels.  Host-side
+    geometry for the measurement only, vectorised over the rays of a view."""
+    nz, ny, nx = w.volume.shape
+    n = np.array([nx, ny, nz])
+    s = np.asarray(w.spacing, dtype=np.float64)
+    half = 0.5 * n * s
+    K = np.asarray(w.K, dtype=np.float64)
+    Ki = np.linalg.inv(K)
+    cc, rr = np.meshgrid(np.arange(w.det_w) + 0.5, np.arange(w.det_h) + 0.5)
+    m = np.stack([cc.ravel(), rr.ravel(), np.ones(cc.size)])
+    total = 0
+    for P in np.asarray(w.poses, dtype=np.float64):
+        R, t = P[:, :3], P[:, 3]
+        C = -R.T @ t
+        d = R.T @ (Ki @ m)
+        d /= np.linalg.norm(d, axis=0)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            ta = (-half[:, None] - C[:, None]) / d
+            tb = (half[:, None] - C[:, None]) / d
+        inside = (np.abs(C) <= half)[:, None] | (d != 0)
+        ta = np.where(d == 0, -np.inf, ta)
+        tb = np.where(d == 0, np.inf, tb)
+        t0 = np.maximum(np.max(np.minimum(ta, tb), axis=0), 0.0)
+        t1 = np.min(np.maximum(ta, tb), axis=0)
+        hit = (t1 > t0) & inside.all(axis=0)
+        p0 = C[:, None] + t0 * d
+        p1 = C[:, None] + t1 * d
+        i0 = np.clip(np.floor((p0 + half[:, None]) / s[:, None]), 0, n[:, None] - 1)
+        i1 = np.clip(np.floor((p1 + half[:, None]) / s[:, None]), 0, n[:, None] - 1)
+        total += int(np.sum(np.where(hit, 1 + np.abs(i1 - i0).sum(axis=0), 0)))
+    return total
 
 
 def forward_bytes(res, hits):
@@ -255,6 +303,23 @@ def workload_lines(dev, reps):
             line["backward_gsamples_s"] = round(w.nominal_samples / t[1] / 1e6, 1)
             line["backward_hbm_frac"] = round(backward_bytes(res, hits) / (t[1] * 1e-3) / 1e9
                                               / HBM_PEAK_GBS, 4)
+        if i in (2, 3, 5):
+            # cell-constant (Siddon) pair on the same inputs: algorithmic bytes are
+            # one element read (forward) or one fp32 update (backward) per
+            # ray-voxel piece, plus 8 B per ray
+            pieces = siddon_pieces(w)
+            sfns = [res.siddon_forward] + ([res.siddon_backward] if res.g is not None else [])
+            ts = time_graph(sfns)
+            line["siddon_pieces"] = pieces
+            line["siddon_forward_ms"] = round(ts[0], 4)
+            line["siddon_forward_fps"] = round(w.n_views / ts[0] * 1e3, 1)
+            line["siddon_forward_gpieces_s"] = round(pieces / ts[0] / 1e6, 1)
+            line["siddon_forward_hbm_frac"] = round(
+                (pieces * res.elem_bytes + w.n_rays * 8) / (ts[0] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            if len(ts) > 1:
+                line["siddon_backward_ms"] = round(ts[1], 4)
+                line["siddon_backward_hbm_frac"] = round(
+                    (pieces * 4 + w.n_rays * 8) / (ts[1] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
         lines[w.name + ("-bf16" if bf16 else "")] = line
         log(f"workload {w.name}{' bf16' if bf16 else ''}: {line}")
         del res

@@ -7,10 +7,12 @@ There is no CPU or PyTorch fallback: if the library is not built, or a tensor
 is not on a GPU, the call raises.
 
 Functions carry the C names (``drr_forward``, ``drr_backward_volume``,
-``drr_backward_pose``, ``drr_workspace_bytes``); ``render`` wraps them as a
+``drr_backward_pose``, ``drr_forward_siddon``, ``drr_backward_volume_siddon``,
+``drr_workspace_bytes``); ``render`` wraps the trilinear model as a
 ``torch.autograd.Function`` (flashdrr ``VolumeRaycaster`` style: gradients flow
-to the volume and to the view poses) and
-``project`` / ``backproject`` give diffct's A and A^T (line-integral mode).
+to the volume and to the view poses), ``render_siddon`` the cell-constant model,
+and ``project`` / ``backproject`` (``project_siddon`` / ``backproject_siddon``)
+give diffct's A and A^T in line-integral mode.
 """
 from __future__ import annotations
 
@@ -53,6 +55,10 @@ def library() -> ctypes.CDLL:
         lib.drr_backward_volume.restype = I
         lib.drr_backward_pose.argtypes = [P, I, I, I, I, P, P, P, I, I, I, I, I, P, P, P, Z, P]
         lib.drr_backward_pose.restype = I
+        lib.drr_forward_siddon.argtypes = [P, I, I, I, I, P, P, P, I, I, I, I, P, P, P]
+        lib.drr_forward_siddon.restype = I
+        lib.drr_backward_volume_siddon.argtypes = [I, I, I, P, P, P, I, I, I, I, P, P, P, P]
+        lib.drr_backward_volume_siddon.restype = I
         lib.drr_status_string.argtypes = [I]
         lib.drr_status_string.restype = ctypes.c_char_p
         lib.drr_last_error.restype = ctypes.c_char_p
@@ -210,6 +216,63 @@ def drr_backward_pose(volume: torch.Tensor, spacing: Sequence[float], K, poses: 
     return grad_poses
 
 
+def drr_forward_siddon(volume: torch.Tensor, spacing: Sequence[float], K, poses: torch.Tensor,
+                       det_h: int, det_w: int, mode: int = BEER_LAMBERT,
+                       out: Optional[torch.Tensor] = None, line_integral=True,
+                       stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Forward DRR in the cell-constant (Siddon) model: s = sum_v mu_v l_v.
+    Returns (image (V, det_h, det_w) fp32, line integrals or None)."""
+    volume = _device_tensor(volume, "volume")
+    dtype = _volume_dtype(volume)
+    poses = _device_tensor(poses, "poses", torch.float32)
+    if volume.dim() != 3 or poses.dim() != 3 or tuple(poses.shape[1:]) != (3, 4):
+        raise ValueError("volume must be (nz, ny, nx) and poses (V, 3, 4)")
+    nz, ny, nx = (int(s) for s in volume.shape)
+    V = int(poses.shape[0])
+    if out is None:
+        out = torch.empty((V, det_h, det_w), dtype=torch.float32, device=volume.device)
+    out = _device_tensor(out, "out", torch.float32)
+    if out.numel() != V * det_h * det_w:
+        raise ValueError("out has the wrong size")
+    if line_integral is True:
+        line_integral = torch.empty_like(out)
+    elif line_integral is False:
+        line_integral = None
+    if line_integral is not None:
+        line_integral = _device_tensor(line_integral, "line_integral", torch.float32)
+        if line_integral.numel() != out.numel():
+            raise ValueError("line_integral has the wrong size")
+    _check(library().drr_forward_siddon(
+        _ptr(volume), dtype, nz, ny, nx, _host_floats(spacing, 3), _host_floats(K, 9),
+        _ptr(poses), V, det_h, det_w, mode, _ptr(out), _ptr(line_integral), _stream(stream)))
+    return out, line_integral
+
+
+def drr_backward_volume_siddon(shape: Sequence[int], spacing: Sequence[float], K,
+                               poses: torch.Tensor, det_h: int, det_w: int, mode: int,
+                               grad_out: torch.Tensor, line_integral: Optional[torch.Tensor],
+                               grad_volume: Optional[torch.Tensor] = None,
+                               stream=None) -> torch.Tensor:
+    """Matched adjoint of ``drr_forward_siddon`` (its volume gradient)."""
+    nz, ny, nx = (int(s) for s in shape)
+    poses = _device_tensor(poses, "poses", torch.float32)
+    grad_out = _device_tensor(grad_out, "grad_out", torch.float32)
+    V = int(poses.shape[0])
+    if grad_out.numel() != V * det_h * det_w:
+        raise ValueError("grad_out has the wrong size")
+    if line_integral is not None:
+        line_integral = _device_tensor(line_integral, "line_integral", torch.float32)
+    if grad_volume is None:
+        grad_volume = torch.empty((nz, ny, nx), dtype=torch.float32, device=grad_out.device)
+    grad_volume = _device_tensor(grad_volume, "grad_volume", torch.float32)
+    if grad_volume.numel() != nz * ny * nx:
+        raise ValueError("grad_volume has the wrong size")
+    _check(library().drr_backward_volume_siddon(
+        nz, ny, nx, _host_floats(spacing, 3), _host_floats(K, 9), _ptr(poses), V, det_h, det_w,
+        mode, _ptr(grad_out), _ptr(line_integral), _ptr(grad_volume), _stream(stream)))
+    return grad_volume
+
+
 class _Render(torch.autograd.Function):
     @staticmethod
     def forward(ctx, volume, spacing, K, poses, det_h, det_w, n_samples, mode):
@@ -239,6 +302,45 @@ def render(volume: torch.Tensor, spacing, K, poses: torch.Tensor, det_h: int, de
     """Differentiable DRR: image (V, det_h, det_w); gradients flow to ``volume``
     and to ``poses`` (each view's [R | t] entries)."""
     return _Render.apply(volume, spacing, K, poses, det_h, det_w, n_samples, mode)
+
+
+class _RenderSiddon(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, volume, spacing, K, poses, det_h, det_w, mode):
+        img, s = drr_forward_siddon(volume.detach(), spacing, K, poses.detach(), det_h, det_w,
+                                    mode)
+        ctx.save_for_backward(poses.detach(), s)
+        ctx.geom = (tuple(volume.shape), volume.dtype, spacing, K, det_h, det_w, mode)
+        return img
+
+    @staticmethod
+    def backward(ctx, grad_img):
+        poses, s = ctx.saved_tensors
+        shape, dtype, spacing, K, det_h, det_w, mode = ctx.geom
+        g_vol = None
+        if ctx.needs_input_grad[0]:
+            g_vol = drr_backward_volume_siddon(shape, spacing, K, poses, det_h, det_w, mode,
+                                               grad_img.contiguous().float(), s).to(dtype)
+        return g_vol, None, None, None, None, None, None
+
+
+def render_siddon(volume: torch.Tensor, spacing, K, poses: torch.Tensor, det_h: int, det_w: int,
+                  mode: int = BEER_LAMBERT) -> torch.Tensor:
+    """Differentiable cell-constant DRR: image (V, det_h, det_w); the gradient
+    flows to ``volume`` (the poses are treated as constants here)."""
+    return _RenderSiddon.apply(volume, spacing, K, poses, det_h, det_w, mode)
+
+
+def project_siddon(volume, spacing, K, poses, det_h, det_w) -> torch.Tensor:
+    """A x in the cell-constant model (diffct ``project``)."""
+    return drr_forward_siddon(volume, spacing, K, poses, det_h, det_w, LINE_INTEGRAL,
+                              line_integral=False)[0]
+
+
+def backproject_siddon(y, shape, spacing, K, poses, det_h, det_w) -> torch.Tensor:
+    """A^T y, the matched adjoint of ``project_siddon`` (diffct ``backproject``)."""
+    return drr_backward_volume_siddon(shape, spacing, K, poses, det_h, det_w, LINE_INTEGRAL,
+                                      y.contiguous(), None)
 
 
 def project(volume, spacing, K, poses, det_h, det_w, n_samples) -> torch.Tensor:

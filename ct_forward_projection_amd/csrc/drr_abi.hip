@@ -78,6 +78,7 @@ int check_geometry(int nz, int ny, int nx, int elem_bytes, const float* spacing,
     const int n[3] = {nx, ny, nz};
     for (int i = 0; i < 3; ++i) {
         a.V.n[i] = n[i];
+        a.V.s[i] = (double)spacing[i];
         a.V.inv_s[i] = 1.0 / (double)spacing[i];
         a.V.half_e[i] = 0.5 * (double)n[i] * (double)spacing[i];
         a.V.q_off[i] = 0.5 * (double)(n[i] - 1);
@@ -230,6 +231,49 @@ int drr_backward_pose(const void* volume, int dtype, int nz, int ny, int nx, con
                                              static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(DRR_ERR_HIP, "pose backward launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int drr_forward_siddon(const void* volume, int dtype, int nz, int ny, int nx,
+                       const float* spacing, const float* K, const float* poses, int n_views,
+                       int det_h, int det_w, int mode, float* out, float* line_integral,
+                       void* stream)
+{
+    if (dtype != DRR_F32 && dtype != DRR_BF16)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    drr::LaunchArgs a;
+    int st = check_geometry(nz, ny, nx, dtype == DRR_F32 ? 4 : 2, spacing, K, poses, n_views,
+                            det_h, det_w, 1, mode, a);
+    if (st != DRR_OK) return st;
+    if (!volume) return fail(DRR_ERR_INVALID_ARGUMENT, "volume is NULL");
+    const long long n_rays = (long long)n_views * det_h * det_w;
+    if (n_rays > 0 && !out) return fail(DRR_ERR_INVALID_ARGUMENT, "out is NULL");
+    if (n_rays == 0) return ok();
+    hipError_t e = drr::launch_siddon_forward(a, volume, dtype, out, line_integral,
+                                              static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DRR_ERR_HIP, "Siddon forward launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int drr_backward_volume_siddon(int nz, int ny, int nx, const float* spacing, const float* K,
+                               const float* poses, int n_views, int det_h, int det_w, int mode,
+                               const float* grad_out, const float* line_integral,
+                               float* grad_volume, void* stream)
+{
+    drr::LaunchArgs a;
+    int st = check_geometry(nz, ny, nx, 4, spacing, K, poses, n_views, det_h, det_w, 1, mode, a);
+    if (st != DRR_OK) return st;
+    if (!grad_volume) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_volume is NULL");
+    const long long n_rays = (long long)n_views * det_h * det_w;
+    if (n_rays > 0 && !grad_out) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+    if (n_rays > 0 && mode == DRR_BEER_LAMBERT && !line_integral)
+        return fail(DRR_ERR_INVALID_ARGUMENT,
+                    "line_integral is required for the Beer-Lambert backward");
+    hipError_t e = drr::launch_siddon_backward(a, grad_out, line_integral, grad_volume,
+                                               static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DRR_ERR_HIP, "Siddon backward launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

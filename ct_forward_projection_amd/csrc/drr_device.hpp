@@ -37,6 +37,7 @@ struct Intrinsics {
 // low-signal ray's integral at a sharp air/tissue edge by more than 1e-5.
 struct VolumeDesc {
     int n[3];                      // nx, ny, nz
+    double s[3];                   // spacing (mm)
     double inv_s[3];               // 1 / spacing
     double half_e[3];              // box half extent n s / 2 (mm)
     double q_off[3];               // E / (2 s) - 1/2 = (n - 1) / 2

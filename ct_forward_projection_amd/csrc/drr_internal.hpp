@@ -48,6 +48,14 @@ hipError_t launch_forward(const LaunchArgs& a, const void* vol, int dtype, bool 
                           void* workspace, float* out, float* s_out, hipStream_t stream);
 hipError_t launch_backward(const LaunchArgs& a, const float* grad_out, const float* s_in,
                            float* grad, hipStream_t stream);
+// zero n floats with a kernel (graph-capturable, unlike a memset node)
+hipError_t launch_fill(float* p, size_t n, hipStream_t stream);
+
+// Cell-constant (Siddon) pair: no workspace.
+hipError_t launch_siddon_forward(const LaunchArgs& a, const void* vol, int dtype, float* out,
+                                 float* s_out, hipStream_t stream);
+hipError_t launch_siddon_backward(const LaunchArgs& a, const float* grad_out, const float* s_in,
+                                  float* grad, hipStream_t stream);
 
 // Pose gradient: the march of the forward (same volume plan) with gradient
 // accumulators; `acc` holds 12 doubles per view.

@@ -27,6 +27,7 @@
 #include "drr_device.hpp"
 #include "drr_internal.hpp"
 #include "drr_sample.hpp"
+#include "drr_window.hpp"
 
 namespace drr {
 
@@ -200,74 +201,6 @@ __device__ inline void scatter_sample_global(float* __restrict__ grad, uint32_t 
     unsafeAtomicAdd(grad + r10 + x1, w[5]);
     unsafeAtomicAdd(grad + r11 + x0, w[6]);
     unsafeAtomicAdd(grad + r11 + x1, w[7]);
-}
-
-// LDS window of the backward: 8192 int32 (32 KB), five workgroups per CU.
-constexpr int kWinCap = 8192;
-
-// Workgroup-wide min of six ints (maxima are passed negated).
-__device__ inline void block_min6(int v[6], int* red, int* out)
-{
-#pragma unroll
-    for (int i = 0; i < 6; ++i) {
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v[i] = min(v[i], __shfl_xor(v[i], off, 64));
-    }
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (lane == 0) {
-#pragma unroll
-        for (int i = 0; i < 6; ++i) red[wave * 6 + i] = v[i];
-    }
-    __syncthreads();
-    if (threadIdx.x < 6) {
-        int m = red[threadIdx.x];
-        for (int w = 1; w < kBlock / 64; ++w) m = min(m, red[w * 6 + threadIdx.x]);
-        out[threadIdx.x] = m;
-    }
-    __syncthreads();
-}
-
-// Workgroup-wide sums of two floats.
-__device__ inline void block_sum2(float& a, float& b, float* red)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        a += __shfl_xor(a, off, 64);
-        b += __shfl_xor(b, off, 64);
-    }
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (lane == 0) {
-        red[2 * wave] = a;
-        red[2 * wave + 1] = b;
-    }
-    __syncthreads();
-    a = 0.0f;
-    b = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kBlock / 64; ++w) {
-        a += red[2 * w];
-        b += red[2 * w + 1];
-    }
-    __syncthreads();
-}
-
-// Pixel owned by a thread of the backward: the 16 x 16 tile is split into four
-// interleaved 8 x 8 lattices (stride 2), one per wave, so the 64 lanes of a
-// wave sit two pixels apart and rarely target the same voxel in one LDS atomic
-// instruction (same-address lanes serialise).  Measured on the 1024^2 step:
-// 2.97 ms with 8 x 8 contiguous wave tiles, 1.56 ms interleaved.  (Wider
-// lattices -- 32 x 32 tiles, four rays per thread -- cost registers and window
-// room and were slower.)
-__device__ inline PixelCoord scatter_pixel(int tile, int tiles_x, int tiles_per_view)
-{
-    PixelCoord p;
-    p.view = tile / tiles_per_view;
-    const int t = tile - p.view * tiles_per_view;
-    const int ty = t / tiles_x, tx = t - ty * tiles_x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    p.r = ty * kTile + 2 * (lane >> 3) + (wave >> 1);
-    p.c = tx * kTile + 2 * (lane & 7) + (wave & 1);
-    return p;
 }
 
 // Add the eight (scaled) weights of one cell to the LDS window.
@@ -559,14 +492,18 @@ hipError_t launch_forward(const LaunchArgs& a, const void* vol, int dtype, bool 
                                    static_cast<uint16_t*>(workspace), out, s_out, stream);
 }
 
+hipError_t launch_fill(float* p, size_t n, hipStream_t stream)
+{
+    if (n == 0) return hipSuccess;
+    const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+    hipLaunchKernelGGL(drr_fill_kernel, dim3(blocks), dim3(256), 0, stream, p, n, 0.0f);
+    return hipGetLastError();
+}
+
 hipError_t launch_backward(const LaunchArgs& a, const float* grad_out, const float* s_in,
                            float* grad, hipStream_t stream)
 {
-    const size_t n_vox = (size_t)a.V.n[0] * a.V.n[1] * a.V.n[2];
-    const int fill_blocks = (int)((n_vox + 255) / 256 < 4096 ? (n_vox + 255) / 256 : 4096);
-    hipLaunchKernelGGL(drr_fill_kernel, dim3(fill_blocks), dim3(256), 0, stream, grad, n_vox,
-                       0.0f);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_fill(grad, (size_t)a.V.n[0] * a.V.n[1] * a.V.n[2], stream);
     if (e != hipSuccess) return e;
     int tiles_x, tiles_per_view, n_tiles;
     tile_grid(a.n_views, a.H, a.W, kTile, tiles_x, tiles_per_view, n_tiles);

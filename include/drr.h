@@ -145,6 +145,36 @@ int drr_backward_pose(const void *volume, int dtype, int nz, int ny, int nx, con
                       int n_samples, int mode, const float *grad_out, float *grad_poses,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* Forward DRR in the cell-constant (Siddon) model (diffct 2.1.0, "Why
+ * diffct": project() and backproject() are an exact adjoint pair for the
+ * cell-constant Siddon model).  Each voxel is a constant box
+ * [i sx - Ex/2, (i + 1) sx - Ex/2] x ... and the line integral of a ray is
+ *   s = sum over voxels v of mu_v l_v,  l_v = length of the clipped ray in v,
+ * with the same cameras, box clip, outputs and layouts as drr_forward (no
+ * sample count: the lengths are exact).  A ray that lies exactly in a voxel
+ * plane is given the voxel on the side of increasing index.
+ *   volume, dtype, spacing, K, poses, det_h, det_w, mode, out, line_integral:
+ *                 as drr_forward
+ * No workspace is needed.  n_views, det_h or det_w equal to 0 is a valid empty
+ * call. */
+int drr_forward_siddon(const void *volume, int dtype, int nz, int ny, int nx,
+                       const float *spacing, const float *K, const float *poses, int n_views,
+                       int det_h, int det_w, int mode, float *out, float *line_integral,
+                       void *stream);
+
+/* Volume gradient of drr_forward_siddon, its matched adjoint: every voxel
+ * receives sum over rays of y_p l_v with y_p = grad_out_p * exp(-s_p)
+ * (Beer-Lambert; s from drr_forward_siddon's line_integral) or grad_out_p
+ * (line integral; this is A^T grad_out for the same A as the forward).
+ *   grad_out, line_integral, grad_volume: as drr_backward_volume (grad_volume
+ *                 is OVERWRITTEN)
+ * The volume itself is not needed.  Accumulation uses fp32 atomics, so the
+ * result may differ between runs in the last bits. */
+int drr_backward_volume_siddon(int nz, int ny, int nx, const float *spacing, const float *K,
+                               const float *poses, int n_views, int det_h, int det_w, int mode,
+                               const float *grad_out, const float *line_integral,
+                               float *grad_volume, void *stream);
+
 /* Static description of a drr_status value. */
 const char *drr_status_string(int status);
 

@@ -32,3 +32,18 @@ def l2_err(gpu, ref):
 
 def say(*a):
     print(*a, flush=True)
+
+
+def check_forward(img_gpu, ref, bar, what, chord=None):
+    """Floored max relative error within ``bar``; rays the oracle finds missing
+    the box (chord 0) must be exactly 0 on the GPU as well."""
+    g = img_gpu.cpu().double().numpy() if hasattr(img_gpu, "cpu") else np.asarray(img_gpu)
+    err = forward_rel_err(g, ref)
+    say(f"{what}: forward max rel err {err:.3e} (bar {bar:g}), "
+        f"normwise {normwise_err(g, ref):.3e}")
+    assert err <= bar
+    if chord is not None:
+        miss = chord == 0.0
+        assert np.all(g[miss] == 0.0), f"{what}: misses must be exactly 0"
+        say(f"{what}: {int(miss.sum())} misses, all exactly 0")
+    return err

@@ -129,3 +129,49 @@ def test_workspace_too_small_is_rejected_on_the_host():
                ws_bytes=need) == 1
     # the backward needs none
     assert drr.drr_workspace_bytes(8, 8, 8, 0, 1, 256, 256, 64, 1) == 0
+
+
+def fwd_siddon(**kw):
+    args = dict(volume=DUMMY, dtype=0, nz=8, ny=8, nx=8, spacing=SP, K=K, poses=DUMMY,
+                n_views=1, det_h=4, det_w=4, mode=0, out=DUMMY, s=None, stream=None)
+    args.update(kw)
+    return drr.library().drr_forward_siddon(
+        args["volume"], args["dtype"], args["nz"], args["ny"], args["nx"], args["spacing"],
+        args["K"], args["poses"], args["n_views"], args["det_h"], args["det_w"], args["mode"],
+        args["out"], args["s"], args["stream"])
+
+
+def bwd_siddon(**kw):
+    args = dict(nz=8, ny=8, nx=8, spacing=SP, K=K, poses=DUMMY, n_views=1, det_h=4, det_w=4,
+                mode=0, g=DUMMY, s=DUMMY, grad=DUMMY, stream=None)
+    args.update(kw)
+    return drr.library().drr_backward_volume_siddon(
+        args["nz"], args["ny"], args["nx"], args["spacing"], args["K"], args["poses"],
+        args["n_views"], args["det_h"], args["det_w"], args["mode"], args["g"], args["s"],
+        args["grad"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nz=0), 1), (dict(nx=20000), 2), (dict(n_views=-1), 1), (dict(mode=2), 1),
+    (dict(dtype=3), 1), (dict(volume=None), 1), (dict(poses=None), 1), (dict(out=None), 1),
+    (dict(spacing=_f(1.0, 0.0, 1.0)), 1), (dict(K=_f(1, 2, 3, 2, 4, 6, 0, 0, 1)), 1),
+    (dict(n_views=65536, det_h=256, det_w=256), 2),
+])
+def test_siddon_forward_rejects_invalid_arguments(kw, status):
+    assert fwd_siddon(**kw) == status
+    assert drr.library().drr_last_error() != b""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nz=0), 1), (dict(mode=-1), 1), (dict(grad=None), 1), (dict(g=None), 1),
+    (dict(s=None), 1), (dict(poses=None), 1), (dict(K=None), 1),
+])
+def test_siddon_backward_rejects_invalid_arguments(kw, status):
+    assert bwd_siddon(**kw) == status
+    assert drr.library().drr_last_error() != b""
+
+
+def test_siddon_empty_calls_are_valid_no_ops():
+    assert fwd_siddon(n_views=0, poses=None, out=None) == 0
+    assert fwd_siddon(det_w=0) == 0
+    assert drr.library().drr_last_error() == b""

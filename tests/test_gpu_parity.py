@@ -19,7 +19,7 @@ import torch
 import ct_forward_projection_amd as drr
 import oracle
 import workloads as W
-from helpers import forward_rel_err, l2_err, normwise_err, say
+from helpers import check_forward, l2_err, normwise_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -53,21 +53,6 @@ def gpu_backward(w, dev, s, g):
                                    w.n_samples, w.mode, torch.from_numpy(g).to(dev), s)
     torch.cuda.synchronize()
     return grad.cpu().double().numpy()
-
-
-def check_forward(img_gpu, ref, bar, what, chord=None):
-    """Floored max relative error within ``bar``; rays the oracle finds missing
-    the box (chord 0) must be exactly 0 on the GPU as well."""
-    g = img_gpu.cpu().double().numpy() if torch.is_tensor(img_gpu) else img_gpu
-    err = forward_rel_err(g, ref)
-    say(f"{what}: forward max rel err {err:.3e} (bar {bar:g}), "
-        f"normwise {normwise_err(g, ref):.3e}")
-    assert err <= bar
-    if chord is not None:
-        miss = chord == 0.0
-        assert np.all(g[miss] == 0.0), f"{what}: misses must be exactly 0"
-        say(f"{what}: {int(miss.sum())} misses, all exactly 0")
-    return err
 
 
 # ------------------------------------------------------------------ the five workloads
