@@ -26,6 +26,9 @@ LIBRARY = os.path.join(HERE, "libdrr_oracle.so")
 
 BEER_LAMBERT = 0
 LINE_INTEGRAL = 1
+ALPHA_COMPOSITE = 2
+CLIP_BOX = 0
+CLIP_NEAR_FAR = 1
 
 _lib = None
 
@@ -69,6 +72,15 @@ def _load():
     lib.oracle_siddon_adjoint.argtypes = [P, I, I, I, P, P, P, I, I, I, I, P, P, I,
                                           ctypes.c_longlong]
     lib.oracle_siddon_adjoint.restype = I
+    D = ctypes.c_double
+    lib.oracle_render.argtypes = [P, I, I, I, I, I, P, P, P, I, I, I, I, I, D, I, D, P, P, I, P,
+                                  P, I]
+    lib.oracle_render.restype = I
+    lib.oracle_render_adjoint.argtypes = [P, I, I, I, I, I, P, P, P, I, I, I, I, I, D, I, D, P,
+                                          P, I, P, P, I, ctypes.c_longlong]
+    lib.oracle_render_adjoint.restype = I
+    lib.oracle_view_range.argtypes = [P, P, D, P]
+    lib.oracle_view_range.restype = None
     lib.oracle_max_threads.restype = I
     _lib = lib
     return lib
@@ -279,3 +291,72 @@ def adjoint_workload(w, grad_out=None, n_threads: Optional[int] = None,
     g = w.grad_out if grad_out is None else grad_out
     return adjoint(w.volume, w.volume.shape, w.spacing, w.K, w.poses, w.det_h, w.det_w,
                    w.n_samples, w.mode, g, n_threads, max_buffer_bytes)
+
+
+def _render_args(volume, poses, transfer):
+    vol = np.ascontiguousarray(volume, dtype=np.float32)
+    if vol.ndim == 3:
+        vol = vol[None, None]
+    if vol.ndim != 5:
+        raise ValueError("volume must be (nz, ny, nx) or (B, C, nz, ny, nx)")
+    Pd = _f64(poses).reshape(-1, 12)
+    if transfer is None:
+        return vol, Pd, None, None, 0
+    xp = np.ascontiguousarray(np.asarray(transfer[0], dtype=np.float64).reshape(vol.shape[1], -1))
+    yp = np.ascontiguousarray(np.asarray(transfer[1], dtype=np.float64).reshape(xp.shape))
+    return vol, Pd, xp, yp, xp.shape[1]
+
+
+def render(volume: np.ndarray, spacing, K, poses, det_h: int, det_w: int, n_samples: int,
+           mode: int, density_factor: float = 1.0, clip: int = CLIP_BOX, margin: float = 30.0,
+           transfer=None, n_threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """flashdrr-style render of ``volume`` (B, C, nz, ny, nx) (or (nz, ny, nx)):
+    view v of ``poses`` (V = B * views_per_vol) renders volume v // views_per_vol.
+    ``transfer`` = (xp, yp), each (C, K): a per-channel piecewise-linear map
+    applied to the voxels first.  Returns (image, optical depth), float64
+    (V, C, H, W)."""
+    lib = _load()
+    vol, Pd, xp, yp, nk = _render_args(volume, poses, transfer)
+    B, C, nz, ny, nx = vol.shape
+    V = Pd.shape[0]
+    out = np.zeros((V, C, det_h, det_w), dtype=np.float64)
+    tau = np.zeros_like(out)
+    rc = lib.oracle_render(_ptr(vol), B, C, nz, ny, nx, _ptr(_f64(spacing)), _ptr(_f64(K)),
+                           _ptr(Pd), V, det_h, det_w, n_samples, mode, float(density_factor),
+                           clip, float(margin), None if xp is None else _ptr(xp),
+                           None if yp is None else _ptr(yp), nk, _ptr(out), _ptr(tau),
+                           _threads(n_threads))
+    if rc != 0:
+        raise ValueError("oracle_render: invalid arguments or out of memory")
+    return out, tau
+
+
+def render_adjoint(volume: np.ndarray, spacing, K, poses, det_h: int, det_w: int,
+                   n_samples: int, mode: int, grad_out: np.ndarray, density_factor: float = 1.0,
+                   clip: int = CLIP_BOX, margin: float = 30.0, transfer=None,
+                   n_threads: Optional[int] = None, max_buffer_bytes: int = 4 << 30) -> np.ndarray:
+    """Gradient of sum(grad_out * render(volume)) with respect to ``volume``:
+    float64 of the volume's shape (B, C, nz, ny, nx) (or (nz, ny, nx))."""
+    lib = _load()
+    vol, Pd, xp, yp, nk = _render_args(volume, poses, transfer)
+    B, C, nz, ny, nx = vol.shape
+    V = Pd.shape[0]
+    g = np.ascontiguousarray(grad_out, dtype=np.float64).reshape(V, C, det_h, det_w)
+    grad = np.zeros(vol.shape, dtype=np.float64)
+    rc = lib.oracle_render_adjoint(_ptr(vol), B, C, nz, ny, nx, _ptr(_f64(spacing)),
+                                   _ptr(_f64(K)), _ptr(Pd), V, det_h, det_w, n_samples, mode,
+                                   float(density_factor), clip, float(margin),
+                                   None if xp is None else _ptr(xp),
+                                   None if yp is None else _ptr(yp), nk, _ptr(g), _ptr(grad),
+                                   _threads(n_threads), int(max_buffer_bytes))
+    if rc < 1:
+        raise ValueError("oracle_render_adjoint: invalid arguments or out of memory")
+    return grad.reshape(np.shape(volume))
+
+
+def view_range(extent, pose, margin: float):
+    """(near, far) of the near/far clipping mode for one view."""
+    out = np.zeros(2, dtype=np.float64)
+    _load().oracle_view_range(_ptr(np.ascontiguousarray(extent, dtype=np.float64)),
+                              _ptr(_f64(pose).reshape(12)), float(margin), _ptr(out))
+    return float(out[0]), float(out[1])

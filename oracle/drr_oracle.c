@@ -852,6 +852,430 @@ int oracle_siddon_adjoint(const float *vol, int nz, int ny, int nx, const double
     return failed ? -1 : T;
 }
 
+/* ------------------------------------------------- render: the flashdrr front end */
+
+/* The VolumeRaycaster options of the flashdrr pages on top of the same rays:
+ *   [fd-fwd]    flashdrr.rendering API, VolumeRaycaster.forward: vol is
+ *               (B, C, D, H, W); N = B * views_per_vol view matrices, view v
+ *               rendering volume v / views_per_vol; output (N, C, H, W).
+ *   [fd-init]   __init__: density_factor multiplies the volume intensities
+ *               before integration; use_beer_lambert = False selects
+ *               front-to-back alpha compositing (the "over" operator).
+ *   [fd-clip]   compute_clipping_distances: one near / far distance per view,
+ *               from the camera to the closest / farthest volume point, widened
+ *               by a margin (30 mm by default).
+ *   [fd-tf]     Transfer functions, piecewise_linear_channelwise: a per-channel
+ *               piecewise-linear map over sorted knots (xp, yp) that extends
+ *               its first and last segments, applied to the volume before ray
+ *               casting.
+ * Readings (the pages give no formulas for these):
+ *   - the density factor f scales mu: the optical depth of a ray is
+ *     tau = f dz sum_k mu_k; Beer-Lambert gives 1 - exp(-tau), the line
+ *     integral gives tau;
+ *   - alpha compositing treats each sample as a slab of thickness dz that
+ *     emits its own value mu_k and absorbs with density f mu_k:
+ *     alpha_k = 1 - exp(-f mu_k dz), T_k = prod_{j<k} (1 - alpha_j), and the
+ *     front-to-back over operator accumulates I = sum_k T_k alpha_k mu_k;
+ *   - the transfer function acts on voxels (mu_v = tf_c(x_v)), then the
+ *     volume of mu is sampled trilinearly as everywhere else;
+ *   - the near/far mode uses the box's closest point and farthest corner
+ *     (near not below 0), samples the midpoints of [near, far] on every ray of
+ *     the view, and reads 0 outside the volume (grid_sample's zero padding:
+ *     a trilinear corner outside [0, n-1] holds 0); with far <= near a ray
+ *     renders 0. */
+
+#define ORACLE_ALPHA_COMPOSITE 2
+#define ORACLE_CLIP_BOX 0
+#define ORACLE_CLIP_NEAR_FAR 1
+
+/* [fd-tf] the piecewise-linear map of one channel.  Segment i spans
+ * [xp[i], xp[i+1]); below xp[1] segment 0 applies and from xp[K-2] on segment
+ * K-2, which extends both end segments.  *slope receives the segment's slope
+ * (one-sided at a knot: the segment on the right). */
+static double transfer(const double *xp, const double *yp, int K, double x, double *slope)
+{
+    int i = 0;
+    while (i < K - 2 && x >= xp[i + 1]) ++i;
+    double m = (yp[i + 1] - yp[i]) / (xp[i + 1] - xp[i]);
+    if (slope) *slope = m;
+    return yp[i] + m * (x - xp[i]);
+}
+
+/* [fd-clip] near / far distances of a camera centre C from the box
+ * [-E/2, E/2]: the closest point of the box (0 inside it) and the farthest
+ * corner, then the margin. */
+static void near_far(const double C[3], const double E[3], double margin, double *t_near,
+                     double *t_far)
+{
+    double dn2 = 0.0, df2 = 0.0;
+    for (int a = 0; a < 3; ++a) {
+        double h = 0.5 * E[a];
+        double dn = 0.0;
+        if (C[a] < -h) dn = -h - C[a];
+        if (C[a] > h) dn = C[a] - h;
+        double df = fabs(C[a]) + h;
+        dn2 += dn * dn;
+        df2 += df * df;
+    }
+    double tn = sqrt(dn2) - margin;
+    *t_near = tn > 0.0 ? tn : 0.0;
+    *t_far = sqrt(df2) + margin;
+}
+
+/* The eight trilinear corners of q in a volume of n voxels: clamp to edge
+ * (zero_pad = 0) as in the forward above, or zero padding (zero_pad = 1), where
+ * a corner outside [0, n-1] holds 0 and its weight is dropped. */
+static void render_corners(const long n[3], const double q[3], int zero_pad, long off[8],
+                           double w[8])
+{
+    long lo[3];
+    double f[3];
+    for (int a = 0; a < 3; ++a) {
+        double fl = floor(q[a]);
+        f[a] = q[a] - fl;
+        lo[a] = (long)fl;
+    }
+    for (int c = 0; c < 8; ++c) {
+        long idx[3];
+        double wt = 1.0;
+        int outside = 0;
+        for (int a = 0; a < 3; ++a) {
+            int up = (c >> a) & 1;
+            long i = lo[a] + up;
+            wt *= up ? f[a] : 1.0 - f[a];
+            if (i < 0 || i > n[a] - 1) outside = 1;
+            idx[a] = clamp_index(i, n[a]);
+        }
+        off[c] = (idx[2] * n[1] + idx[1]) * n[0] + idx[0];
+        w[c] = (zero_pad && outside) ? 0.0 : wt;
+    }
+}
+
+typedef struct {
+    long n[3];
+    double s[3], E[3];
+    int n_samples, mode, clip, zero_pad;
+    double f, margin;
+} render_params_t;
+
+/* Sample range of one ray: [t0, t1] of the box clip, or the view's near/far.
+ * Returns 0 when the ray renders nothing. */
+static int render_range(const render_params_t *P, const oracle_ray_t *ray, double *t0,
+                        double *t1)
+{
+    if (P->clip == ORACLE_CLIP_BOX) {
+        *t0 = ray->t0;
+        *t1 = ray->t1;
+        return ray->hit;
+    }
+    near_far(ray->C, P->E, P->margin, t0, t1);
+    return *t1 > *t0;
+}
+
+/* Sample values mu_k (k = 0..N-1) of one ray at t0 + (k + 1/2) dz, and, when
+ * off/w are given, their corners and weights (8 per sample). */
+static void render_samples(const render_params_t *P, const double *mu, const oracle_ray_t *ray,
+                           double t0, double dz, double *vals, long *off, double *w)
+{
+    for (int k = 0; k < P->n_samples; ++k) {
+        double t = t0 + ((double)k + 0.5) * dz;
+        double q[3];
+        for (int a = 0; a < 3; ++a)
+            q[a] = (ray->C[a] + t * ray->d[a] + 0.5 * P->E[a]) / P->s[a] - 0.5;
+        long o[8];
+        double wt[8];
+        render_corners(P->n, q, P->zero_pad, o, wt);
+        double v = 0.0;
+        for (int c = 0; c < 8; ++c) v += wt[c] * mu[o[c]];
+        vals[k] = v;
+        if (off) {
+            memcpy(off + 8L * k, o, sizeof(o));
+            memcpy(w + 8L * k, wt, sizeof(wt));
+        }
+    }
+}
+
+/* Output of one ray from its samples; *tau receives the optical depth. */
+static double render_output(const render_params_t *P, const double *vals, double dz,
+                            double *tau)
+{
+    double sum = 0.0;
+    for (int k = 0; k < P->n_samples; ++k) sum += vals[k];
+    *tau = P->f * dz * sum;
+    if (P->mode == ORACLE_BEER_LAMBERT) return -expm1(-*tau);
+    if (P->mode == ORACLE_LINE_INTEGRAL) return *tau;
+    /* front-to-back over operator */
+    double I = 0.0, T = 1.0;
+    for (int k = 0; k < P->n_samples; ++k) {
+        double a = P->f * vals[k] * dz;
+        double alpha = -expm1(-a);
+        I += T * alpha * vals[k];
+        T *= exp(-a);
+    }
+    return I;
+}
+
+/* mu volumes of all B * C channels in fp64: the input widened, or the
+ * channel's transfer function applied voxel by voxel ([fd-tf]); slopes
+ * (nullable) receives the transfer function's slope per voxel. */
+static double *render_mu(const float *vol, long n_chvol, int C, long n_vox, const double *tf_xp,
+                         const double *tf_yp, int tf_knots, double *slopes)
+{
+    double *mu = (double *)malloc(sizeof(double) * (size_t)(n_chvol * n_vox));
+    if (!mu) return NULL;
+    for (long cv = 0; cv < n_chvol; ++cv) {
+        int ch = (int)(cv % C);
+        for (long x = 0; x < n_vox; ++x) {
+            long i = cv * n_vox + x;
+            if (tf_xp) {
+                double m;
+                mu[i] = transfer(tf_xp + (long)ch * tf_knots, tf_yp + (long)ch * tf_knots,
+                                 tf_knots, (double)vol[i], &m);
+                if (slopes) slopes[i] = m;
+            } else {
+                mu[i] = (double)vol[i];
+                if (slopes) slopes[i] = 1.0;
+            }
+        }
+    }
+    return mu;
+}
+
+static int render_check(int B, int C, int nz, int ny, int nx, const double *spacing,
+                        int n_views, int H, int W, int n_samples, int mode, double f, int clip,
+                        double margin, const double *tf_xp, const double *tf_yp, int tf_knots)
+{
+    if (B < 1 || C < 1 || nz < 1 || ny < 1 || nx < 1 || n_views < 0 || H < 0 || W < 0) return -1;
+    if (n_views % B) return -1;
+    if (n_samples < 1) return -1;
+    if (mode != ORACLE_BEER_LAMBERT && mode != ORACLE_LINE_INTEGRAL &&
+        mode != ORACLE_ALPHA_COMPOSITE)
+        return -1;
+    if (clip != ORACLE_CLIP_BOX && clip != ORACLE_CLIP_NEAR_FAR) return -1;
+    if (!isfinite(f) || !isfinite(margin)) return -1;
+    for (int a = 0; a < 3; ++a)
+        if (!(spacing[a] > 0.0)) return -1;
+    if (tf_xp || tf_yp) {
+        if (!tf_xp || !tf_yp || tf_knots < 2) return -1;
+        for (int c = 0; c < C; ++c)
+            for (int k = 0; k + 1 < tf_knots; ++k)
+                if (!(tf_xp[c * tf_knots + k + 1] > tf_xp[c * tf_knots + k])) return -1;
+    }
+    return 0;
+}
+
+static void render_init(render_params_t *P, int nz, int ny, int nx, const double *spacing,
+                        int n_samples, int mode, double f, int clip, double margin)
+{
+    P->n[0] = nx;
+    P->n[1] = ny;
+    P->n[2] = nz;
+    for (int a = 0; a < 3; ++a) {
+        P->s[a] = spacing[a];
+        P->E[a] = (double)P->n[a] * spacing[a];
+    }
+    P->n_samples = n_samples;
+    P->mode = mode;
+    P->f = f;
+    P->clip = clip;
+    P->zero_pad = clip == ORACLE_CLIP_NEAR_FAR;
+    P->margin = margin;
+}
+
+/* Render B volumes of C channels ([fd-fwd]): vol is (B, C, nz, ny, nx) fp32,
+ * poses n_views x 12 with n_views a multiple of B, out and tau (nullable) are
+ * (n_views, C, H, W).  tf_xp / tf_yp (C x tf_knots, nullable) give a transfer
+ * function per channel.  Returns 0, or -1 on invalid arguments or no memory. */
+int oracle_render(const float *vol, int B, int C, int nz, int ny, int nx, const double *spacing,
+                  const double *K, const double *poses, int n_views, int H, int W, int n_samples,
+                  int mode, double f, int clip, double margin, const double *tf_xp,
+                  const double *tf_yp, int tf_knots, double *out, double *tau, int n_threads)
+{
+    if (render_check(B, C, nz, ny, nx, spacing, n_views, H, W, n_samples, mode, f, clip, margin,
+                     tf_xp, tf_yp, tf_knots))
+        return -1;
+    render_params_t P;
+    render_init(&P, nz, ny, nx, spacing, n_samples, mode, f, clip, margin);
+    long n_vox = (long)nx * ny * nz;
+    double *mu = render_mu(vol, (long)B * C, C, n_vox, tf_xp, tf_yp, tf_knots, NULL);
+    if (!mu) return -1;
+    int views_per_vol = n_views / B;
+    long n_out = (long)n_views * C * H * W;
+    int failed = 0;
+    set_threads(n_threads);
+#pragma omp parallel
+    {
+        double *vals = (double *)malloc(sizeof(double) * (size_t)n_samples);
+        if (!vals) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 64)
+        for (long id = 0; id < n_out; ++id) {
+            if (!vals) continue;
+            int v = (int)(id / ((long)C * H * W));
+            int ch = (int)((id / ((long)H * W)) % C);
+            int r = (int)((id / W) % H);
+            int c = (int)(id % W);
+            const double *m = mu + ((long)(v / views_per_vol) * C + ch) * n_vox;
+            oracle_ray_t ray;
+            make_ray(K, poses + 12L * v, P.E, r, c, &ray);
+            double t0, t1, t = 0.0, I = 0.0;
+            if (render_range(&P, &ray, &t0, &t1)) {
+                double dz = (t1 - t0) / (double)n_samples;
+                render_samples(&P, m, &ray, t0, dz, vals, NULL, NULL);
+                I = render_output(&P, vals, dz, &t);
+            }
+            out[id] = I;
+            if (tau) tau[id] = t;
+        }
+        free(vals);
+    }
+    free(mu);
+    return failed ? -1 : 0;
+}
+
+/* Volume gradient of oracle_render for upstream g = dL/dI (n_views, C, H, W),
+ * with respect to the input volume x (B, C, nz, ny, nx):
+ *   dL/dmu_v = sum over rays and samples of c_k w_corner, with
+ *     Beer-Lambert      c_k = g f dz exp(-tau)
+ *     line integral     c_k = g f dz
+ *     alpha compositing c_k = g (T_k (alpha_k + f dz (1 - alpha_k) mu_k)
+ *                                - f dz sum_{j>k} T_j alpha_j mu_j)
+ *   (the last: d/dmu_k of sum_j T_j alpha_j mu_j, where mu_k enters its own
+ *   alpha and emission and the transmittance of every later sample);
+ *   dL/dx_v = dL/dmu_v tf'(x_v) (1 without a transfer function).
+ * grad (B * C * nz * ny * nx doubles) is overwritten.  Threads get private
+ * gradient buffers while (threads - 1) buffers fit in max_buffer_bytes.
+ * Returns the thread count used, or -1. */
+int oracle_render_adjoint(const float *vol, int B, int C, int nz, int ny, int nx,
+                          const double *spacing, const double *K, const double *poses,
+                          int n_views, int H, int W, int n_samples, int mode, double f, int clip,
+                          double margin, const double *tf_xp, const double *tf_yp, int tf_knots,
+                          const double *g, double *grad, int n_threads,
+                          long long max_buffer_bytes)
+{
+    if (render_check(B, C, nz, ny, nx, spacing, n_views, H, W, n_samples, mode, f, clip, margin,
+                     tf_xp, tf_yp, tf_knots))
+        return -1;
+    render_params_t P;
+    render_init(&P, nz, ny, nx, spacing, n_samples, mode, f, clip, margin);
+    long n_vox = (long)nx * ny * nz;
+    long n_all = (long)B * C * n_vox;
+    double *slopes = (double *)malloc(sizeof(double) * (size_t)n_all);
+    double *mu = slopes ? render_mu(vol, (long)B * C, C, n_vox, tf_xp, tf_yp, tf_knots, slopes)
+                        : NULL;
+    if (!mu) {
+        free(slopes);
+        return -1;
+    }
+    memset(grad, 0, sizeof(double) * (size_t)n_all);
+    int T = n_threads > 0 ? n_threads : 1;
+#ifndef _OPENMP
+    T = 1;
+#endif
+    while (T > 1 && (long long)(T - 1) * n_all * (long long)sizeof(double) > max_buffer_bytes) --T;
+    double **bufs = (double **)calloc((size_t)T, sizeof(double *));
+    int failed = bufs == NULL;
+    if (bufs) {
+        bufs[0] = grad;
+        for (int i = 1; i < T; ++i) {
+            bufs[i] = (double *)calloc((size_t)n_all, sizeof(double));
+            if (!bufs[i]) failed = 1;
+        }
+    }
+    int views_per_vol = B > 0 ? n_views / B : 1;
+    long n_out = (long)n_views * C * H * W;
+    if (!failed) {
+        set_threads(T);
+#pragma omp parallel num_threads(T)
+        {
+#ifdef _OPENMP
+            double *acc = bufs[omp_get_thread_num()];
+#else
+            double *acc = bufs[0];
+#endif
+            double *vals = (double *)malloc(sizeof(double) * (size_t)n_samples);
+            double *coef = (double *)malloc(sizeof(double) * (size_t)n_samples);
+            long *off = (long *)malloc(sizeof(long) * 8 * (size_t)n_samples);
+            double *w = (double *)malloc(sizeof(double) * 8 * (size_t)n_samples);
+            int ok = vals && coef && off && w;
+            if (!ok) {
+#pragma omp atomic write
+                failed = 1;
+            }
+#pragma omp for schedule(dynamic, 64)
+            for (long id = 0; id < n_out; ++id) {
+                if (!ok) continue;
+                int v = (int)(id / ((long)C * H * W));
+                int ch = (int)((id / ((long)H * W)) % C);
+                int r = (int)((id / W) % H);
+                int c = (int)(id % W);
+                long base = ((long)(v / views_per_vol) * C + ch) * n_vox;
+                oracle_ray_t ray;
+                make_ray(K, poses + 12L * v, P.E, r, c, &ray);
+                double t0, t1, tau;
+                if (!render_range(&P, &ray, &t0, &t1)) continue;
+                double dz = (t1 - t0) / (double)n_samples;
+                render_samples(&P, mu + base, &ray, t0, dz, vals, off, w);
+                render_output(&P, vals, dz, &tau);
+                if (P.mode == ORACLE_BEER_LAMBERT) {
+                    for (int k = 0; k < n_samples; ++k) coef[k] = g[id] * f * dz * exp(-tau);
+                } else if (P.mode == ORACLE_LINE_INTEGRAL) {
+                    for (int k = 0; k < n_samples; ++k) coef[k] = g[id] * f * dz;
+                } else {
+                    /* transmittance in front of each sample, then the later
+                     * samples' emission summed back to front */
+                    double Tk = 1.0;
+                    for (int k = 0; k < n_samples; ++k) {
+                        double a = f * vals[k] * dz;
+                        coef[k] = Tk;          /* T_k for now */
+                        Tk *= exp(-a);
+                    }
+                    double later = 0.0;
+                    for (int k = n_samples - 1; k >= 0; --k) {
+                        double a = f * vals[k] * dz;
+                        double alpha = -expm1(-a);
+                        double Tf = coef[k];
+                        coef[k] = g[id] * (Tf * (alpha + f * dz * (1.0 - alpha) * vals[k]) -
+                                           f * dz * later);
+                        later += Tf * alpha * vals[k];
+                    }
+                }
+                for (int k = 0; k < n_samples; ++k)
+                    for (int cn = 0; cn < 8; ++cn)
+                        acc[base + off[8L * k + cn]] += coef[k] * w[8L * k + cn];
+            }
+            free(vals);
+            free(coef);
+            free(off);
+            free(w);
+        }
+    }
+    if (bufs) {
+        for (int i = 1; i < T; ++i) {
+            if (bufs[i] && !failed)
+                for (long x = 0; x < n_all; ++x) grad[x] += bufs[i][x];
+            free(bufs[i]);
+        }
+        free(bufs);
+    }
+    if (!failed)
+        for (long x = 0; x < n_all; ++x) grad[x] *= slopes[x];
+    free(mu);
+    free(slopes);
+    return failed ? -1 : T;
+}
+
+/* Near / far range of the near/far mode for one view, for pins: out = (near,
+ * far).  extent = (Ex, Ey, Ez). */
+void oracle_view_range(const double *extent, const double *pose, double margin, double *out)
+{
+    double C[3];
+    camera_centre(pose, C);
+    near_far(C, extent, margin, &out[0], &out[1]);
+}
+
 /* Build information for the Python loader. */
 int oracle_abi_version(void) { return 1; }
 
