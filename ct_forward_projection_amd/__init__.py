@@ -8,7 +8,10 @@ is not on a GPU, the call raises.
 
 Functions carry the C names (``drr_forward``, ``drr_backward_volume``,
 ``drr_backward_pose``, ``drr_forward_siddon``, ``drr_backward_volume_siddon``,
-``drr_workspace_bytes``); ``render`` wraps the trilinear model as a
+``drr_render``, ``drr_render_backward_volume``, ``drr_workspace_bytes``,
+``drr_render_workspace_bytes``); ``raycast`` wraps the flashdrr front end
+(volume and channel batches, density factor, alpha compositing, transfer
+function, near/far clipping) with autograd to the volume; ``render`` wraps the trilinear model as a
 ``torch.autograd.Function`` (flashdrr ``VolumeRaycaster`` style: gradients flow
 to the volume and to the view poses), ``render_siddon`` the cell-constant model,
 and ``project`` / ``backproject`` (``project_siddon`` / ``backproject_siddon``)
@@ -25,7 +28,8 @@ import torch
 from .build import LIBRARY
 
 F32, BF16 = 0, 1
-BEER_LAMBERT, LINE_INTEGRAL = 0, 1
+BEER_LAMBERT, LINE_INTEGRAL, ALPHA_COMPOSITE = 0, 1, 2
+CLIP_BOX, CLIP_NEAR_FAR = 0, 1
 STATUS = {0: "DRR_OK", 1: "DRR_ERR_INVALID_ARGUMENT", 2: "DRR_ERR_UNSUPPORTED",
           3: "DRR_ERR_WORKSPACE_TOO_SMALL", 4: "DRR_ERR_HIP"}
 
@@ -59,6 +63,15 @@ def library() -> ctypes.CDLL:
         lib.drr_forward_siddon.restype = I
         lib.drr_backward_volume_siddon.argtypes = [I, I, I, P, P, P, I, I, I, I, P, P, P, P]
         lib.drr_backward_volume_siddon.restype = I
+        F = ctypes.c_float
+        lib.drr_render_workspace_bytes.argtypes = [I] * 14
+        lib.drr_render_workspace_bytes.restype = Z
+        lib.drr_render.argtypes = [P, I, I, I, I, I, I, P, P, P, I, I, I, I, I, F, I, F, P, P, I,
+                                   P, P, P, Z, P]
+        lib.drr_render.restype = I
+        lib.drr_render_backward_volume.argtypes = [P, I, I, I, I, I, I, P, P, P, I, I, I, I, I, F,
+                                                   I, F, P, P, I, P, P, P, P, P, Z, P]
+        lib.drr_render_backward_volume.restype = I
         lib.drr_status_string.argtypes = [I]
         lib.drr_status_string.restype = ctypes.c_char_p
         lib.drr_last_error.restype = ctypes.c_char_p
@@ -353,3 +366,167 @@ def backproject(y, shape, spacing, K, poses, det_h, det_w, n_samples) -> torch.T
     """A^T y: the matched adjoint of ``project`` (diffct ``backproject``)."""
     return drr_backward_volume(shape, spacing, K, poses, det_h, det_w, n_samples, LINE_INTEGRAL,
                                y.contiguous(), None)
+
+
+# ---------------------------------------------------------------- flashdrr front end
+
+def _transfer(transfer, C: int):
+    """(xp, yp), each (C, K) -> two host float arrays and K (or Nones and 0)."""
+    if transfer is None:
+        return None, None, 0
+    xp = torch.as_tensor(transfer[0], dtype=torch.float32).detach().cpu().reshape(C, -1)
+    yp = torch.as_tensor(transfer[1], dtype=torch.float32).detach().cpu().reshape(C, -1)
+    if xp.shape != yp.shape:
+        raise ValueError("transfer xp and yp must have the same shape (C, K)")
+    k = int(xp.shape[1])
+    return _host_floats(xp, C * k), _host_floats(yp, C * k), k
+
+
+def _batched_volume(volume: torch.Tensor):
+    if volume.dim() == 3:
+        return 1, 1, tuple(int(x) for x in volume.shape)
+    if volume.dim() == 5:
+        B, C, nz, ny, nx = (int(x) for x in volume.shape)
+        return B, C, (nz, ny, nx)
+    raise ValueError("volume must be (nz, ny, nx) or (B, C, nz, ny, nx)")
+
+
+def drr_render_workspace_bytes(n_volumes: int, n_channels: int, nz: int, ny: int, nx: int,
+                               dtype: int, n_views: int, det_h: int, det_w: int, n_samples: int,
+                               mode: int, clip: int, tf_knots: int, for_backward: int) -> int:
+    return int(library().drr_render_workspace_bytes(n_volumes, n_channels, nz, ny, nx, dtype,
+                                                    n_views, det_h, det_w, n_samples, mode, clip,
+                                                    tf_knots, for_backward))
+
+
+def drr_render(volume: torch.Tensor, spacing, K, poses: torch.Tensor, det_h: int, det_w: int,
+               n_samples: int, mode: int = BEER_LAMBERT, density_factor: float = 1.0,
+               clip: int = CLIP_BOX, margin: float = 30.0, transfer=None,
+               out: Optional[torch.Tensor] = None, aux=True,
+               workspace: Optional[torch.Tensor] = None,
+               stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Render ``volume`` (B, C, nz, ny, nx) (or (nz, ny, nx)) for ``poses``
+    (V, 3, 4), V a multiple of B (view v renders volume v // (V // B)).
+    Returns (image (V, C, det_h, det_w) fp32, optical depth or None)."""
+    volume = _device_tensor(volume, "volume")
+    dtype = _volume_dtype(volume)
+    poses = _device_tensor(poses, "poses", torch.float32)
+    if poses.dim() != 3 or tuple(poses.shape[1:]) != (3, 4):
+        raise ValueError("poses must be (V, 3, 4)")
+    B, C, (nz, ny, nx) = _batched_volume(volume)
+    V = int(poses.shape[0])
+    xp, yp, nk = _transfer(transfer, C)
+    dev = volume.device
+    if out is None:
+        out = torch.empty((V, C, det_h, det_w), dtype=torch.float32, device=dev)
+    out = _device_tensor(out, "out", torch.float32)
+    if out.numel() != V * C * det_h * det_w:
+        raise ValueError("out has the wrong size")
+    if aux is True:
+        aux = torch.empty_like(out)
+    elif aux is False:
+        aux = None
+    if aux is not None:
+        aux = _device_tensor(aux, "aux", torch.float32)
+        if aux.numel() != out.numel():
+            raise ValueError("aux has the wrong size")
+    need = drr_render_workspace_bytes(B, C, nz, ny, nx, dtype, V, det_h, det_w, n_samples, mode,
+                                      clip, nk, 0)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().drr_render(
+        _ptr(volume), dtype, B, C, nz, ny, nx, _host_floats(spacing, 3), _host_floats(K, 9),
+        _ptr(poses), V, det_h, det_w, n_samples, mode, float(density_factor), clip, float(margin),
+        xp, yp, nk, _ptr(out), _ptr(aux), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, aux
+
+
+def drr_render_backward_volume(volume: Optional[torch.Tensor], shape, dtype: int, spacing, K,
+                               poses: torch.Tensor, det_h: int, det_w: int, n_samples: int,
+                               mode: int, grad_out: torch.Tensor,
+                               out: Optional[torch.Tensor], aux: Optional[torch.Tensor],
+                               density_factor: float = 1.0, clip: int = CLIP_BOX,
+                               margin: float = 30.0, transfer=None,
+                               grad_volume: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None,
+                               stream=None) -> torch.Tensor:
+    """Gradient of sum(grad_out * image) with respect to the input volume of
+    ``drr_render``; ``shape`` is the volume's (B, C, nz, ny, nx) or (nz, ny, nx).
+    ``volume`` is needed for alpha compositing and with a transfer function,
+    ``out`` for alpha compositing, ``aux`` for Beer-Lambert.  Returns fp32 of
+    ``shape``."""
+    shape = tuple(int(x) for x in shape)
+    if len(shape) == 3:
+        B, C, (nz, ny, nx) = 1, 1, shape
+    elif len(shape) == 5:
+        B, C, nz, ny, nx = shape
+    else:
+        raise ValueError("shape must be (nz, ny, nx) or (B, C, nz, ny, nx)")
+    if volume is not None:
+        volume = _device_tensor(volume, "volume")
+        dtype = _volume_dtype(volume)
+    poses = _device_tensor(poses, "poses", torch.float32)
+    grad_out = _device_tensor(grad_out, "grad_out", torch.float32)
+    V = int(poses.shape[0])
+    if grad_out.numel() != V * C * det_h * det_w:
+        raise ValueError("grad_out has the wrong size")
+    if out is not None:
+        out = _device_tensor(out, "out", torch.float32)
+    if aux is not None:
+        aux = _device_tensor(aux, "aux", torch.float32)
+    xp, yp, nk = _transfer(transfer, C)
+    dev = grad_out.device
+    if grad_volume is None:
+        grad_volume = torch.empty(shape, dtype=torch.float32, device=dev)
+    grad_volume = _device_tensor(grad_volume, "grad_volume", torch.float32)
+    if grad_volume.numel() != B * C * nz * ny * nx:
+        raise ValueError("grad_volume has the wrong size")
+    need = drr_render_workspace_bytes(B, C, nz, ny, nx, dtype, V, det_h, det_w, n_samples, mode,
+                                      clip, nk, 1)
+    if workspace is None:
+        workspace = _workspace(need, dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().drr_render_backward_volume(
+        _ptr(volume), dtype, B, C, nz, ny, nx, _host_floats(spacing, 3), _host_floats(K, 9),
+        _ptr(poses), V, det_h, det_w, n_samples, mode, float(density_factor), clip, float(margin),
+        xp, yp, nk, _ptr(grad_out), _ptr(out), _ptr(aux), _ptr(grad_volume), _ptr(workspace),
+        ws_bytes, _stream(stream)))
+    return grad_volume
+
+
+class _Raycast(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, volume, spacing, K, poses, det_h, det_w, n_samples, mode, density_factor,
+                clip, margin, transfer):
+        img, tau = drr_render(volume.detach(), spacing, K, poses.detach(), det_h, det_w,
+                              n_samples, mode, density_factor, clip, margin, transfer)
+        ctx.save_for_backward(volume.detach(), poses.detach(), img, tau)
+        ctx.args = (spacing, K, det_h, det_w, n_samples, mode, density_factor, clip, margin,
+                    transfer)
+        return img
+
+    @staticmethod
+    def backward(ctx, grad_img):
+        volume, poses, img, tau = ctx.saved_tensors
+        spacing, K, det_h, det_w, n_samples, mode, f, clip, margin, transfer = ctx.args
+        g_vol = None
+        if ctx.needs_input_grad[0]:
+            g_vol = drr_render_backward_volume(
+                volume, tuple(volume.shape), _volume_dtype(volume), spacing, K, poses, det_h,
+                det_w, n_samples, mode, grad_img.contiguous().float(), img, tau, f, clip, margin,
+                transfer).to(volume.dtype)
+        return (g_vol,) + (None,) * 11
+
+
+def raycast(volume: torch.Tensor, spacing, K, poses: torch.Tensor, det_h: int, det_w: int,
+            n_samples: int, mode: int = BEER_LAMBERT, density_factor: float = 1.0,
+            clip: int = CLIP_BOX, margin: float = 30.0, transfer=None) -> torch.Tensor:
+    """Differentiable flashdrr-style render: ``volume`` (B, C, nz, ny, nx) and
+    ``poses`` (V, 3, 4) with V a multiple of B -- or one pose, used for every
+    volume -- give images (V, C, det_h, det_w); the gradient flows to the
+    volume (the poses are constants here)."""
+    if volume.dim() == 5 and poses.shape[0] == 1 and volume.shape[0] > 1:
+        poses = poses.expand(volume.shape[0], 3, 4).contiguous()
+    return _Raycast.apply(volume, spacing, K, poses, det_h, det_w, n_samples, mode,
+                          density_factor, clip, margin, transfer)

@@ -39,7 +39,7 @@ constexpr int kMaxSamples = 1 << 24;
 // Shared validation of the geometry arguments; fills `a` on success.
 int check_geometry(int nz, int ny, int nx, int elem_bytes, const float* spacing, const float* K,
                    const float* poses, int n_views, int det_h, int det_w, int n_samples,
-                   int mode, drr::LaunchArgs& a)
+                   int mode, drr::LaunchArgs& a, int max_mode = DRR_LINE_INTEGRAL)
 {
     if (nz < 1 || ny < 1 || nx < 1)
         return fail(DRR_ERR_INVALID_ARGUMENT, "volume dims must be >= 1 (got %d x %d x %d)", nz,
@@ -57,8 +57,8 @@ int check_geometry(int nz, int ny, int nx, int elem_bytes, const float* spacing,
         return fail(DRR_ERR_INVALID_ARGUMENT, "n_samples must be >= 1 (got %d)", n_samples);
     if (n_samples > kMaxSamples)
         return fail(DRR_ERR_UNSUPPORTED, "n_samples above 2^24");
-    if (mode != DRR_BEER_LAMBERT && mode != DRR_LINE_INTEGRAL)
-        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown mode %d", mode);
+    if (mode < DRR_BEER_LAMBERT || mode > max_mode)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown or unsupported mode %d", mode);
     if (!spacing) return fail(DRR_ERR_INVALID_ARGUMENT, "spacing is NULL");
     if (!K) return fail(DRR_ERR_INVALID_ARGUMENT, "K is NULL");
     for (int i = 0; i < 3; ++i)
@@ -94,6 +94,79 @@ int check_geometry(int nz, int ny, int nx, int elem_bytes, const float* spacing,
     a.W = det_w;
     a.N = n_samples;
     a.mode = mode;
+    a.n_volumes = 1;
+    a.C = 1;
+    a.f = 1.0f;
+    a.clip = drr::kClipBox;
+    a.margin = 0.0f;
+    a.has_tf = false;
+    a.tf.knots = 0;
+    return DRR_OK;
+}
+
+// Corner-cell byte geometry of the volume for cells of elem_bytes elements.
+void set_cells(drr::VolumeDesc& V, int nz, int ny, int nx, int elem_bytes)
+{
+    V.cell_row_bytes = (uint32_t)(nx + 1) * 8u * (uint32_t)elem_bytes;
+    V.cell_slice_bytes = (uint32_t)(ny + 1) * V.cell_row_bytes;
+    V.cell_total_bytes = (uint32_t)((long long)(nz + 1) * V.cell_slice_bytes);
+}
+
+// Validation of the front-end options of drr_render / drr_render_backward_volume;
+// fills the batch, factor, clip and transfer fields of `a`.
+int check_render(int n_volumes, int n_channels, int n_views, float density_factor, int clip,
+                 float margin, const float* tf_xp, const float* tf_yp, int tf_knots,
+                 drr::LaunchArgs& a)
+{
+    if (n_volumes < 1 || n_channels < 1)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "n_volumes and n_channels must be >= 1");
+    if ((long long)n_volumes * n_channels > 65535)
+        return fail(DRR_ERR_UNSUPPORTED, "more than 65535 channel-volumes");
+    if (n_views % n_volumes != 0)
+        return fail(DRR_ERR_INVALID_ARGUMENT,
+                    "n_views (%d) must be a multiple of n_volumes (%d)", n_views, n_volumes);
+    if ((long long)n_views * n_channels * a.H * a.W > kMaxElems)
+        return fail(DRR_ERR_UNSUPPORTED, "more than 2^31 - 1 outputs");
+    if (!isfinite(density_factor))
+        return fail(DRR_ERR_INVALID_ARGUMENT, "density_factor must be finite");
+    if (clip != DRR_CLIP_BOX && clip != DRR_CLIP_NEAR_FAR)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown clip mode %d", clip);
+    if (!isfinite(margin)) return fail(DRR_ERR_INVALID_ARGUMENT, "margin must be finite");
+    if ((tf_xp == nullptr) != (tf_yp == nullptr))
+        return fail(DRR_ERR_INVALID_ARGUMENT, "tf_xp and tf_yp must both be given or both NULL");
+    a.n_volumes = n_volumes;
+    a.C = n_channels;
+    a.f = density_factor;
+    a.clip = clip;
+    a.margin = margin;
+    a.has_tf = tf_xp != nullptr;
+    a.tf.knots = 0;
+    if (a.has_tf) {
+        if (tf_knots < 2)
+            return fail(DRR_ERR_INVALID_ARGUMENT, "tf_knots must be >= 2 (got %d)", tf_knots);
+        if ((long long)tf_knots * n_channels > drr::kMaxTransferEntries)
+            return fail(DRR_ERR_UNSUPPORTED, "n_channels * tf_knots above %d",
+                        drr::kMaxTransferEntries);
+        a.tf.knots = tf_knots;
+        for (int c = 0; c < n_channels; ++c) {
+            for (int k = 0; k < tf_knots; ++k) {
+                const int i = c * tf_knots + k;
+                if (!isfinite(tf_xp[i]) || !isfinite(tf_yp[i]))
+                    return fail(DRR_ERR_INVALID_ARGUMENT, "transfer knot %d is not finite", i);
+                if (k > 0 && !(tf_xp[i] > tf_xp[i - 1]))
+                    return fail(DRR_ERR_INVALID_ARGUMENT,
+                                "tf_xp of channel %d must be strictly increasing", c);
+                a.tf.xp[i] = tf_xp[i];
+                a.tf.yp[i] = tf_yp[i];
+            }
+            for (int k = 0; k + 1 < tf_knots; ++k) {
+                const int i = c * tf_knots + k;
+                a.tf.m[i] = (float)(((double)tf_yp[i + 1] - (double)tf_yp[i]) /
+                                    ((double)tf_xp[i + 1] - (double)tf_xp[i]));
+            }
+            a.tf.m[c * tf_knots + tf_knots - 1] = 0.0f;
+        }
+    }
     return DRR_OK;
 }
 
@@ -146,20 +219,17 @@ int drr_forward(const void* volume, int dtype, int nz, int ny, int nx, const flo
     const long long n_rays = (long long)n_views * det_h * det_w;
     if (n_rays > 0 && !out) return fail(DRR_ERR_INVALID_ARGUMENT, "out is NULL");
     const int eb = dtype == DRR_F32 ? 4 : 2;
-    const drr::ForwardPlan plan = drr::plan_forward(nz, ny, nx, eb, n_rays, n_samples);
+    const drr::RenderPlan plan = drr::plan_render(1, 1, nz, ny, nx, eb, n_views, det_h, det_w,
+                                                  n_samples, drr::kClipBox, false);
     if (workspace_bytes < plan.workspace_bytes)
         return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
                     workspace_bytes, plan.workspace_bytes);
     if (plan.workspace_bytes > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
         return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
     if (n_rays == 0) return ok();
-    if (plan.cells) {
-        a.V.cell_row_bytes = (uint32_t)(nx + 1) * 8u * (uint32_t)eb;
-        a.V.cell_slice_bytes = (uint32_t)(ny + 1) * a.V.cell_row_bytes;
-        a.V.cell_total_bytes = (uint32_t)((long long)(nz + 1) * a.V.cell_slice_bytes);
-    }
-    hipError_t e = drr::launch_forward(a, volume, dtype, plan.cells, workspace, out,
-                                       line_integral, static_cast<hipStream_t>(stream));
+    if (plan.cells) set_cells(a.V, nz, ny, nx, plan.read_elem);
+    hipError_t e = drr::launch_forward(a, plan, volume, dtype, workspace, out, line_integral,
+                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(DRR_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -188,10 +258,107 @@ int drr_backward_volume(int nz, int ny, int nx, const float* spacing, const floa
                     workspace_bytes, need);
     if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
         return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
-    hipError_t e = drr::launch_backward(a, grad_out, line_integral, grad_volume,
-                                        static_cast<hipStream_t>(stream));
+    hipError_t e = drr::launch_backward(a, nullptr, DRR_F32, grad_out, nullptr, line_integral,
+                                        grad_volume, nullptr, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(DRR_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+size_t drr_render_workspace_bytes(int n_volumes, int n_channels, int nz, int ny, int nx,
+                                  int dtype, int n_views, int det_h, int det_w, int n_samples,
+                                  int mode, int clip, int tf_knots, int for_backward)
+{
+    if (n_volumes < 1 || n_channels < 1 || nz < 1 || ny < 1 || nx < 1 || n_views < 0 ||
+        det_h < 0 || det_w < 0 || n_samples < 1 || (dtype != DRR_F32 && dtype != DRR_BF16) ||
+        n_views % n_volumes != 0 || (clip != DRR_CLIP_BOX && clip != DRR_CLIP_NEAR_FAR))
+        return 0;
+    const bool has_tf = tf_knots > 0;
+    if (for_backward == DRR_WORKSPACE_VOLUME_BACKWARD)
+        return drr::render_backward_workspace(n_volumes, n_channels, nz, ny, nx, mode, has_tf);
+    if (for_backward != DRR_WORKSPACE_FORWARD) return 0;
+    return drr::plan_render(n_volumes, n_channels, nz, ny, nx, dtype == DRR_F32 ? 4 : 2, n_views,
+                            det_h, det_w, n_samples, clip, has_tf)
+        .workspace_bytes;
+}
+
+int drr_render(const void* volume, int dtype, int n_volumes, int n_channels, int nz, int ny,
+               int nx, const float* spacing, const float* K, const float* poses, int n_views,
+               int det_h, int det_w, int n_samples, int mode, float density_factor, int clip,
+               float margin, const float* tf_xp, const float* tf_yp, int tf_knots, float* out,
+               float* aux, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (dtype != DRR_F32 && dtype != DRR_BF16)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    const int eb = dtype == DRR_F32 ? 4 : 2;
+    drr::LaunchArgs a;
+    int st = check_geometry(nz, ny, nx, eb, spacing, K, poses, n_views, det_h, det_w, n_samples,
+                            mode, a, DRR_ALPHA_COMPOSITE);
+    if (st != DRR_OK) return st;
+    st = check_render(n_volumes, n_channels, n_views, density_factor, clip, margin, tf_xp, tf_yp,
+                      tf_knots, a);
+    if (st != DRR_OK) return st;
+    if (!volume) return fail(DRR_ERR_INVALID_ARGUMENT, "volume is NULL");
+    const long long n_out = (long long)n_views * n_channels * det_h * det_w;
+    if (n_out > 0 && !out) return fail(DRR_ERR_INVALID_ARGUMENT, "out is NULL");
+    const drr::RenderPlan plan = drr::plan_render(n_volumes, n_channels, nz, ny, nx, eb, n_views,
+                                                  det_h, det_w, n_samples, clip, a.has_tf);
+    if (!plan.fits)
+        return fail(DRR_ERR_UNSUPPORTED, "one channel-volume of the march's copy exceeds 4 GiB");
+    if (workspace_bytes < plan.workspace_bytes)
+        return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
+                    workspace_bytes, plan.workspace_bytes);
+    if (plan.workspace_bytes > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
+        return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+    if (n_out == 0) return ok();
+    if (plan.cells) set_cells(a.V, nz, ny, nx, plan.read_elem);
+    hipError_t e = drr::launch_forward(a, plan, volume, dtype, workspace, out, aux,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DRR_ERR_HIP, "render launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int drr_render_backward_volume(const void* volume, int dtype, int n_volumes, int n_channels,
+                               int nz, int ny, int nx, const float* spacing, const float* K,
+                               const float* poses, int n_views, int det_h, int det_w,
+                               int n_samples, int mode, float density_factor, int clip,
+                               float margin, const float* tf_xp, const float* tf_yp,
+                               int tf_knots, const float* grad_out, const float* out,
+                               const float* aux, float* grad_volume, void* workspace,
+                               size_t workspace_bytes, void* stream)
+{
+    if (dtype != DRR_F32 && dtype != DRR_BF16)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    drr::LaunchArgs a;
+    int st = check_geometry(nz, ny, nx, 4, spacing, K, poses, n_views, det_h, det_w, n_samples,
+                            mode, a, DRR_ALPHA_COMPOSITE);
+    if (st != DRR_OK) return st;
+    st = check_render(n_volumes, n_channels, n_views, density_factor, clip, margin, tf_xp, tf_yp,
+                      tf_knots, a);
+    if (st != DRR_OK) return st;
+    if (!grad_volume) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_volume is NULL");
+    const long long n_out = (long long)n_views * n_channels * det_h * det_w;
+    if (n_out > 0 && !grad_out) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+    if (n_out > 0 && mode == DRR_BEER_LAMBERT && !aux)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "aux (optical depth) is required for Beer-Lambert");
+    if (n_out > 0 && mode == DRR_ALPHA_COMPOSITE && !out)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "out (the forward image) is required for alpha "
+                                              "compositing");
+    if ((mode == DRR_ALPHA_COMPOSITE || a.has_tf) && !volume)
+        return fail(DRR_ERR_INVALID_ARGUMENT,
+                    "volume is required for alpha compositing and for a transfer function");
+    const size_t need =
+        drr::render_backward_workspace(n_volumes, n_channels, nz, ny, nx, mode, a.has_tf);
+    if (workspace_bytes < need)
+        return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
+                    workspace_bytes, need);
+    if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
+        return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+    hipError_t e = drr::launch_backward(a, volume, dtype, grad_out, out, aux, grad_volume,
+                                        workspace, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DRR_ERR_HIP, "render backward launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 
@@ -220,11 +387,7 @@ int drr_backward_pose(const void* volume, int dtype, int nz, int ny, int nx, con
                     workspace_bytes, need);
     if (!workspace || ((uintptr_t)workspace & 255u))
         return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
-    if (plan.cells) {
-        a.V.cell_row_bytes = (uint32_t)(nx + 1) * 8u * (uint32_t)eb;
-        a.V.cell_slice_bytes = (uint32_t)(ny + 1) * a.V.cell_row_bytes;
-        a.V.cell_total_bytes = (uint32_t)((long long)(nz + 1) * a.V.cell_slice_bytes);
-    }
+    if (plan.cells) set_cells(a.V, nz, ny, nx, eb);
     char* ws = static_cast<char*>(workspace);
     hipError_t e = drr::launch_backward_pose(a, volume, dtype, plan.cells, ws + acc_bytes,
                                              reinterpret_cast<double*>(ws), grad_out, grad_poses,

@@ -52,6 +52,21 @@ struct VolumeDesc {
     uint32_t cell_total_bytes;
 };
 
+// Several volumes and channels in one call (flashdrr API,
+// VolumeRaycaster.forward: (B, C, D, H, W) volumes, N = B * views_per_vol
+// views, view v rendering volume v / views_per_vol, output (N, C, H, W)).  A
+// launch covers every (view, channel) pair; channel-volume (b, c) sits at
+// element offset (b * C + c) * (one volume) of its array.  The density factor
+// scales mu (optical depth f dz sum mu); margin widens the near/far range.
+struct Batch {
+    uint64_t src_stride;           // bytes from one channel-volume to the next (read side)
+    uint32_t grad_stride;          // fp32 elements per gradient channel-volume
+    int C;                         // channels
+    int vpv;                       // views per volume
+    float f;                       // density factor
+    float margin;                  // near/far margin (mm)
+};
+
 // Per-view camera, fp64: world direction of image point (u, v, 1) is
 // M (u, v, 1) with M = R^T K^-1; camera centre C = -R^T t.
 struct ViewGeom {
@@ -112,21 +127,42 @@ __device__ inline void view_setup(const float* __restrict__ pose, const Intrinsi
 
 __device__ inline int64_t to_fixed(double x) { return __double2ll_rn(x * 4294967296.0); }
 
+// Unit world direction of the ray through pixel (r, c), fp64.
+__device__ inline void ray_direction(const ViewGeom& G, int r, int c, double d[3])
+{
+    const double u = (double)c + 0.5, v = (double)r + 0.5;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) d[a] = G.M[a * 3 + 0] * u + G.M[a * 3 + 1] * v + G.M[a * 3 + 2];
+    const double inv_len = 1.0 / sqrt(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
+#pragma unroll
+    for (int a = 0; a < 3; ++a) d[a] *= inv_len;
+}
+
+// The N midpoint samples of [t0, t1] on the ray C + t d, in fixed point.
+__device__ inline void march_from_range(const ViewGeom& G, const VolumeDesc& V, const double d[3],
+                                        double t0, double t1, int N, MarchRay& R)
+{
+    const double dz = (t1 - t0) / (double)N;
+    const double ts = t0 + 0.5 * dz;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        R.q0[a] = to_fixed((G.C[a] + ts * d[a]) * V.inv_s[a] + V.q_off[a]);
+        R.dq[a] = to_fixed(dz * d[a] * V.inv_s[a]);
+    }
+    R.dz = (float)dz;
+}
+
 // Ray through pixel (r, c), clipped to the volume box by the slab method in
 // fp64.  Returns false when the ray misses (t1 <= t0 with t0 = max(t_entry, 0)).
 __device__ inline bool ray_setup(const ViewGeom& G, const VolumeDesc& V, int r, int c, int N,
                                  MarchRay& R)
 {
-    const double u = (double)c + 0.5, v = (double)r + 0.5;
     double d[3];
-#pragma unroll
-    for (int a = 0; a < 3; ++a) d[a] = G.M[a * 3 + 0] * u + G.M[a * 3 + 1] * v + G.M[a * 3 + 2];
-    const double inv_len = 1.0 / sqrt(d[0] * d[0] + d[1] * d[1] + d[2] * d[2]);
+    ray_direction(G, r, c, d);
     double t_entry = -__builtin_inf(), t_exit = __builtin_inf();
     bool inside = true;
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
-        d[a] *= inv_len;
         const double lo = -V.half_e[a], hi = V.half_e[a];
         if (d[a] == 0.0) {
             inside = inside && !(G.C[a] < lo || G.C[a] > hi);
@@ -139,14 +175,41 @@ __device__ inline bool ray_setup(const ViewGeom& G, const VolumeDesc& V, int r, 
     }
     const double t0 = fmax(t_entry, 0.0);
     if (!inside || !(t_exit > t0)) return false;
-    const double dz = (t_exit - t0) / (double)N;
-    const double ts = t0 + 0.5 * dz;
+    march_from_range(G, V, d, t0, t_exit, N, R);
+    return true;
+}
+
+// Per-view clipping range of the near/far mode (flashdrr API,
+// compute_clipping_distances: one near and one far distance per view, from the
+// camera to the closest and to the farthest point of the volume, widened by a
+// margin): the closest point of the box (distance 0 inside it) and its
+// farthest corner; near is not allowed below 0.
+__device__ inline void view_near_far(const ViewGeom& G, const VolumeDesc& V, float margin,
+                                     double& t_near, double& t_far)
+{
+    double dn2 = 0.0, df2 = 0.0;
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
-        R.q0[a] = to_fixed((G.C[a] + ts * d[a]) * V.inv_s[a] + V.q_off[a]);
-        R.dq[a] = to_fixed(dz * d[a] * V.inv_s[a]);
+        const double h = V.half_e[a], c = G.C[a];
+        const double dn = c < -h ? -h - c : (c > h ? c - h : 0.0);
+        const double df = fabs(c) + h;
+        dn2 += dn * dn;
+        df2 += df * df;
     }
-    R.dz = (float)dz;
+    t_near = fmax(sqrt(dn2) - (double)margin, 0.0);
+    t_far = sqrt(df2) + (double)margin;
+}
+
+// Ray through pixel (r, c) sampled over the view's [t_near, t_far] (near/far
+// mode: every ray of the view shares the range; samples outside the volume
+// read zero padding).  Returns false when the range is empty.
+__device__ inline bool ray_setup_range(const ViewGeom& G, const VolumeDesc& V, int r, int c, int N,
+                                       double t_near, double t_far, MarchRay& R)
+{
+    if (!(t_far > t_near)) return false;
+    double d[3];
+    ray_direction(G, r, c, d);
+    march_from_range(G, V, d, t_near, t_far, N, R);
     return true;
 }
 

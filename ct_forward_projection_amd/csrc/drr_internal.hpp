@@ -9,6 +9,21 @@ namespace drr {
 
 constexpr int kBeerLambert = 0;
 constexpr int kLineIntegral = 1;
+constexpr int kAlpha = 2;          // front-to-back alpha compositing
+constexpr int kClipBox = 0;        // per-ray box clip
+constexpr int kClipNearFar = 1;    // per-view near/far range, zero padding
+
+// Per-channel piecewise-linear transfer function (flashdrr API, Transfer
+// functions, piecewise_linear_channelwise): channel c's knots are entries
+// [c * knots, (c + 1) * knots); m holds each segment's slope.  The map is
+// applied to voxels before sampling.
+constexpr int kMaxTransferEntries = 128;
+struct TransferFn {
+    int knots;
+    float xp[kMaxTransferEntries];
+    float yp[kMaxTransferEntries];
+    float m[kMaxTransferEntries];
+};
 
 // Validated call arguments, already converted to the kernels' form.
 struct LaunchArgs {
@@ -16,6 +31,14 @@ struct LaunchArgs {
     Intrinsics K;
     const float* poses;   // device, n_views x 12
     int n_views, H, W, N, mode;
+    // front end: n_volumes volumes of C channels, density factor, clip mode,
+    // transfer function (single volume, factor 1, box clip, none by default)
+    int n_volumes, C;
+    float f;
+    int clip;
+    float margin;
+    bool has_tf;
+    TransferFn tf;
 };
 
 // How the forward reads the volume.  The corner-cell copy (8 elements per
@@ -44,10 +67,70 @@ inline ForwardPlan plan_forward(int nz, int ny, int nx, int elem_bytes, long lon
     return p;
 }
 
-hipError_t launch_forward(const LaunchArgs& a, const void* vol, int dtype, bool cells,
+// How a render call reads its volumes: the march reads either the caller's
+// volumes, a corner-cell copy (the reuse rule above; always in the near/far
+// mode, whose cells carry the zero padding), or -- with a transfer function
+// and no cells -- an fp32 copy of the mapped volumes.  One channel-volume of
+// what the march reads is per_volume_bytes (256-byte multiple in the
+// workspace); workspace_bytes covers all n_volumes * C of them.
+struct RenderPlan {
+    bool cells;
+    bool mapped;             // the march reads fp32 mu made by the transfer function
+    int read_elem;           // element bytes the march reads
+    size_t per_volume_bytes;
+    size_t workspace_bytes;
+    bool fits;               // every channel-volume fits 32-bit byte offsets
+};
+
+inline RenderPlan plan_render(int n_volumes, int C, int nz, int ny, int nx, int elem_bytes,
+                              int n_views, int H, int W, int N, int clip, bool has_tf)
+{
+    RenderPlan p{};
+    p.mapped = has_tf;
+    p.read_elem = has_tf ? 4 : elem_bytes;
+    const double n_cells = (double)(nx + 1) * (double)(ny + 1) * (double)(nz + 1);
+    const double cell_bytes = n_cells * 8.0 * p.read_elem;
+    const double lin_bytes = (double)nx * (double)ny * (double)nz * p.read_elem;
+    const long long rays_per_volume =
+        n_volumes > 0 ? (long long)(n_views / n_volumes) * H * W : 0;
+    const double samples_per_cell = (double)rays_per_volume * (double)N / n_cells;
+    const double min_reuse = p.read_elem == 4 ? 16.0 : 4.0;
+    const bool cells_fit = cell_bytes < 4294967040.0;
+    p.cells = clip == kClipNearFar ||
+              (rays_per_volume > 0 && samples_per_cell >= min_reuse && cells_fit);
+    p.fits = p.cells ? cells_fit : lin_bytes < 4294967040.0;
+    const double nv = (double)n_volumes * (double)C;
+    if (p.cells) {
+        p.per_volume_bytes = ((size_t)cell_bytes + 255) & ~(size_t)255;
+        p.workspace_bytes = (size_t)(nv * (double)p.per_volume_bytes);
+    } else if (p.mapped) {
+        p.per_volume_bytes = ((size_t)lin_bytes + 255) & ~(size_t)255;
+        p.workspace_bytes = (size_t)(nv * (double)p.per_volume_bytes);
+    } else {
+        p.per_volume_bytes = (size_t)lin_bytes;
+        p.workspace_bytes = 0;
+    }
+    return p;
+}
+
+// Workspace of the volume backward: the alpha-compositing backward gathers the
+// mapped volumes, so with a transfer function it needs their fp32 copy.
+inline size_t render_backward_workspace(int n_volumes, int C, int nz, int ny, int nx, int mode,
+                                        bool has_tf)
+{
+    if (mode != kAlpha || !has_tf) return 0;
+    const size_t per = ((size_t)nx * ny * nz * 4 + 255) & ~(size_t)255;
+    return per * (size_t)n_volumes * (size_t)C;
+}
+
+hipError_t launch_forward(const LaunchArgs& a, const RenderPlan& plan, const void* vol, int dtype,
                           void* workspace, float* out, float* s_out, hipStream_t stream);
-hipError_t launch_backward(const LaunchArgs& a, const float* grad_out, const float* s_in,
-                           float* grad, hipStream_t stream);
+// The volume backward of a render call.  `vol` is read for alpha compositing
+// and for the transfer function's slope; `out_in` (the forward's image) for
+// alpha compositing; `s_in` (optical depth) for Beer-Lambert.
+hipError_t launch_backward(const LaunchArgs& a, const void* vol, int dtype, const float* grad_out,
+                           const float* out_in, const float* s_in, float* grad, void* workspace,
+                           hipStream_t stream);
 // zero n floats with a kernel (graph-capturable, unlike a memset node)
 hipError_t launch_fill(float* p, size_t n, hipStream_t stream);
 

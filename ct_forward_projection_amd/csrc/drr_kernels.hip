@@ -15,7 +15,20 @@
 //                       than a memset so that the sequence is graph-capturable).
 //
 //   drr_cells_kernel    optional relayout: the corner-cell copy of the volume the
-//                       march reads when samples reuse cells enough.
+//                       march reads when samples reuse cells enough (always in
+//                       the near/far mode, where the cells carry zero padding);
+//                       with a transfer function it writes mapped fp32 cells.
+//   drr_transfer_kernel the transfer function applied to every voxel (fp32 copy)
+//                       when a mapped volume is marched without cells.
+//   drr_slope_kernel    the backward's last step with a transfer function:
+//                       dL/dx = dL/dmu tf'(x) per voxel.
+//   drr_alpha_scatter_kernel  backward of alpha compositing: gathers each
+//                       sample again and scatters its own weight with global
+//                       atomics.
+//
+// Every kernel covers several volumes and channels per launch (flashdrr API,
+// VolumeRaycaster.forward: (B, C, D, H, W) volumes, N = B * views_per_vol views,
+// output (N, C, H, W)): a launch walks (view, channel) pairs.
 //
 // The march is gather-bound, not a contraction, so there is no MFMA here: the
 // design levers are the number of vector-memory instructions per sample (x-pair
@@ -31,14 +44,43 @@
 
 namespace drr {
 
-// Corner-cell relayout: cell (i, j, k), 0 <= i <= nx etc., holds the eight
-// clamped corners (x0, x1) x (y0, y1) x (z0, z1) of the trilinear cell whose
-// low corner is voxel (i-1, j-1, k-1), in the CornerVals order.  One thread
-// per cell; consecutive threads write consecutive cells.
-template <typename T>
-__global__ __launch_bounds__(256) void drr_cells_kernel(const T* __restrict__ vol, int nx, int ny,
-                                                        int nz, T* __restrict__ cells)
+// Value of one voxel as fp32 (bf16 widens exactly).
+__device__ inline float widen(float x) { return x; }
+__device__ inline float widen(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// The transfer function of channel ch at x (segment search over uniform knots,
+// so every knot is a scalar operand); slope receives the segment's slope.
+__device__ inline float transfer_eval(const TransferFn& T, int ch, float x, float& slope)
 {
+    const int b = ch * T.knots;
+    float x0 = T.xp[b], y0 = T.yp[b], m = T.m[b];
+    for (int i = 1; i < T.knots - 1; ++i) {
+        const bool up = x >= T.xp[b + i];
+        x0 = up ? T.xp[b + i] : x0;
+        y0 = up ? T.yp[b + i] : y0;
+        m = up ? T.m[b + i] : m;
+    }
+    slope = m;
+    return fmaf(m, x - x0, y0);
+}
+
+// Corner-cell relayout: cell (i, j, k), 0 <= i <= nx etc., holds the eight
+// corners (x0, x1) x (y0, y1) x (z0, z1) of the trilinear cell whose low corner
+// is voxel (i-1, j-1, k-1), in the CornerVals order: clamped to the volume
+// (ZP = false) or 0 outside it (ZP, the near/far mode's zero padding).  With TF
+// the corners are mapped by channel c's transfer function and written as fp32.
+// One thread per cell, consecutive threads on consecutive cells;
+// blockIdx.y = channel-volume (b * C + c).
+template <typename Tin, typename Tout, bool ZP, bool TF>
+__global__ __launch_bounds__(256) void drr_cells_kernel(const Tin* __restrict__ vol, int nx, int ny,
+                                                        int nz, size_t in_stride,
+                                                        Tout* __restrict__ cells,
+                                                        size_t out_stride, int C, TransferFn tf)
+{
+    static_assert(TF || sizeof(Tin) == sizeof(Tout), "no transfer: cells keep the dtype");
+    const int cv = (int)blockIdx.y, ch = cv % C;
+    vol += (size_t)cv * in_stride;
+    cells += (size_t)cv * out_stride;
     const int cx = nx + 1, cy = ny + 1;
     const long long n = (long long)cx * cy * (nz + 1);
     const size_t sy = (size_t)nx, sz = (size_t)nx * ny;
@@ -50,11 +92,66 @@ __global__ __launch_bounds__(256) void drr_cells_kernel(const T* __restrict__ vo
         const size_t x0 = (size_t)clampi(i - 1, 0, nx - 1), x1 = (size_t)clampi(i, 0, nx - 1);
         const size_t y0 = (size_t)clampi(j - 1, 0, ny - 1) * sy, y1 = (size_t)clampi(j, 0, ny - 1) * sy;
         const size_t z0 = (size_t)clampi(k - 1, 0, nz - 1) * sz, z1 = (size_t)clampi(k, 0, nz - 1) * sz;
-        const T v[8] = {vol[z0 + y0 + x0], vol[z0 + y0 + x1], vol[z0 + y1 + x0], vol[z0 + y1 + x1],
-                        vol[z1 + y0 + x0], vol[z1 + y0 + x1], vol[z1 + y1 + x0], vol[z1 + y1 + x1]};
-        T* o = cells + (size_t)id * 8;
+        const Tin v[8] = {vol[z0 + y0 + x0], vol[z0 + y0 + x1], vol[z0 + y1 + x0], vol[z0 + y1 + x1],
+                          vol[z1 + y0 + x0], vol[z1 + y0 + x1], vol[z1 + y1 + x0], vol[z1 + y1 + x1]};
+        Tout o[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] = v[c];
+        for (int c = 0; c < 8; ++c) {
+            if constexpr (TF) {
+                float m;
+                o[c] = transfer_eval(tf, ch, widen(v[c]), m);
+            } else {
+                o[c] = v[c];
+            }
+        }
+        if constexpr (ZP) {
+            // corner c of cell (i, j, k) is voxel (i - 1 + (c & 1), j - 1 + ..., ...)
+            const bool xl = i >= 1, xh = i <= nx - 1, yl = j >= 1, yh = j <= ny - 1;
+            const bool zl = k >= 1, zh = k <= nz - 1;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const bool in = ((c & 1) ? xh : xl) && ((c & 2) ? yh : yl) && ((c & 4) ? zh : zl);
+                if (!in) o[c] = Tout(0);
+            }
+        }
+        Tout* dst = cells + (size_t)id * 8;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dst[c] = o[c];
+    }
+}
+
+// mu = tf(x) for every voxel of every channel-volume (blockIdx.y), fp32 out.
+template <typename Tin>
+__global__ __launch_bounds__(256) void drr_transfer_kernel(const Tin* __restrict__ vol,
+                                                           size_t n_vox, size_t in_stride,
+                                                           float* __restrict__ mu,
+                                                           size_t out_stride, int C,
+                                                           TransferFn tf)
+{
+    const int cv = (int)blockIdx.y, ch = cv % C;
+    vol += (size_t)cv * in_stride;
+    mu += (size_t)cv * out_stride;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vox;
+         i += (size_t)gridDim.x * blockDim.x) {
+        float m;
+        mu[i] = transfer_eval(tf, ch, widen(vol[i]), m);
+    }
+}
+
+// grad = grad * tf'(x) for every voxel of every channel-volume (blockIdx.y).
+template <typename Tin>
+__global__ __launch_bounds__(256) void drr_slope_kernel(const Tin* __restrict__ vol, size_t n_vox,
+                                                        size_t in_stride, float* __restrict__ grad,
+                                                        int C, TransferFn tf)
+{
+    const int cv = (int)blockIdx.y, ch = cv % C;
+    vol += (size_t)cv * in_stride;
+    grad += (size_t)cv * n_vox;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_vox;
+         i += (size_t)gridDim.x * blockDim.x) {
+        float m;
+        transfer_eval(tf, ch, widen(vol[i]), m);
+        grad[i] *= m;
     }
 }
 
@@ -82,18 +179,39 @@ __device__ inline PixelCoord split_pixel(int tile, int tiles_x, int tiles_per_vi
 template <int SPLIT>
 constexpr int march_tile_side() { return SPLIT == 1 ? kTile : (SPLIT == 4 ? 8 : (SPLIT == 16 ? 4 : 2)); }
 
+// One sample of front-to-back alpha compositing (flashdrr API,
+// VolumeRaycaster.__init__: use_beer_lambert = False): the sample is a slab of
+// thickness dz emitting v with opacity alpha = 1 - exp(-f v dz) behind the
+// transmittance T = exp(-tau) of the samples in front of it.  tau and I run in
+// fp64 so that neither drifts over long rays.
+__device__ inline void composite(float v, float fdz, double& tau, double& I)
+{
+    const float a = fdz * v;
+    const float T = expf(-(float)tau);
+    const float alpha = -expm1f(-a);
+    I += (double)(T * alpha * v);
+    tau += (double)a;
+}
+
 // Forward DRR.  SPLIT = 1: one ray per lane (16 x 16 tiles of four 8 x 8 wave
 // sub-tiles).  SPLIT > 1 (launches with few rays): SPLIT adjacent lanes share
 // a ray, lane j taking samples j, j + SPLIT, ... (neighbouring lanes still
 // gather neighbouring voxels), and their partial sums meet in a cross-lane
 // reduction, so a 64 x 64 detector still fills the chip.  `src` is the volume
-// (Pair, Single) or its corner-cell copy (Cell); `src_bytes` its size.
-template <typename T, Layout L, int MODE, int SPLIT>
+// (Pair, Single) or its corner-cell copy (Cell); `src_bytes` the size of one
+// channel-volume of it, b.src_stride the distance between them.  The tiles of
+// a launch run over (view, channel) pairs.  MODE = kAlpha composites (one lane
+// per ray: the over operator is sequential); CLIP = kClipNearFar samples the
+// view's near/far range through zero-padded cells.
+template <typename T, Layout L, int MODE, int SPLIT, int CLIP>
 __global__ __launch_bounds__(kBlock) void drr_march_kernel(
     const T* __restrict__ src, uint32_t src_bytes, VolumeDesc V, Intrinsics K,
     const float* __restrict__ poses, int H, int W, int N, int tiles_x, int tiles_per_view,
-    float* __restrict__ out, float* __restrict__ s_out)
+    Batch b, float* __restrict__ out, float* __restrict__ s_out)
 {
+    constexpr bool ZP = CLIP == kClipNearFar;
+    static_assert(!ZP || L == Layout::Cell, "the near/far mode reads zero-padded cells");
+    static_assert(MODE != kAlpha || SPLIT == 1, "compositing runs one lane per ray");
     const int tile = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
     PixelCoord px;
     int j = 0;
@@ -106,20 +224,33 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
     // every lane of a ray sees the same pixel, so a ray's lanes leave together
     if (px.r >= H || px.c >= W) return;
 
+    // px.view counts (view, channel) pairs
+    const int view = px.view / b.C, ch = px.view - view * b.C;
+    const int cvol = (view / b.vpv) * b.C + ch;
     ViewGeom G;
-    view_setup(poses + 12 * px.view, K, G);
+    view_setup(poses + 12 * view, K, G);
     MarchRay R;
+    bool hit;
+    if constexpr (CLIP == kClipBox) {
+        hit = ray_setup(G, V, px.r, px.c, N, R);
+    } else {
+        double t_near, t_far;
+        view_near_far(G, V, b.margin, t_near, t_far);
+        hit = ray_setup_range(G, V, px.r, px.c, N, t_near, t_far, R);
+    }
     float s = 0.0f;
-    const bool hit = ray_setup(G, V, px.r, px.c, N, R);
+    double tau_c = 0.0, I_c = 0.0;   // compositing
     if (hit) {
+        const char* base = reinterpret_cast<const char*>(src) + (uint64_t)cvol * b.src_stride;
         const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, (int)src_bytes, kBufferWord3);
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)src_bytes, kBufferWord3);
         int64_t qx = R.q0[0] + (int64_t)j * R.dq[0];
         int64_t qy = R.q0[1] + (int64_t)j * R.dq[1];
         int64_t qz = R.q0[2] + (int64_t)j * R.dq[2];
         const int64_t dqx = (int64_t)SPLIT * R.dq[0], dqy = (int64_t)SPLIT * R.dq[1];
         const int64_t dqz = (int64_t)SPLIT * R.dq[2];
         const int n_mine = j < N ? (N - j + SPLIT - 1) / SPLIT : 0;
+        const float fdz = b.f * R.dz;
         // independent partial sums, one per in-flight sample: a shorter fp32
         // summation chain as well
         float acc[kInflight];
@@ -131,7 +262,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
             CornerVals c[kInflight];
 #pragma unroll
             for (int i = 0; i < kInflight; ++i) {
-                A[i] = sample_addr<T, L>(V, qx, qy, qz);
+                A[i] = sample_addr<T, L, ZP>(V, qx, qy, qz);
                 qx += dqx; qy += dqy; qz += dqz;
             }
 #pragma unroll
@@ -141,14 +272,20 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
             // and a wave never has more than one sample's loads in flight
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < kInflight; ++i) acc[i] += interpolate(A[i], c[i]);
+            for (int i = 0; i < kInflight; ++i) {
+                const float v = ZP ? interpolate_exact(A[i], c[i]) : interpolate(A[i], c[i]);
+                if constexpr (MODE == kAlpha) composite(v, fdz, tau_c, I_c);
+                else acc[i] += v;
+            }
         }
         for (; k < n_mine; ++k) {
-            const SampleAddr A = sample_addr<T, L>(V, qx, qy, qz);
+            const SampleAddr A = sample_addr<T, L, ZP>(V, qx, qy, qz);
             qx += dqx; qy += dqy; qz += dqz;
             CornerVals c;
             gather<T, L>(rs, A, c);
-            acc[0] += interpolate(A, c);
+            const float v = ZP ? interpolate_exact(A, c) : interpolate(A, c);
+            if constexpr (MODE == kAlpha) composite(v, fdz, tau_c, I_c);
+            else acc[0] += v;
         }
 #pragma unroll
         for (int i = 0; i < kInflight; ++i) s += acc[i];
@@ -159,20 +296,51 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
         for (int off = SPLIT / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
         if (j != 0) return;
     }
-    if (hit) s *= R.dz;
+    float res, tau;
+    if constexpr (MODE == kAlpha) {
+        res = (float)I_c;
+        tau = (float)tau_c;
+    } else {
+        if (hit) s *= R.dz;
+        tau = b.f * s;                     // optical depth f dz sum mu
+        res = (MODE == kBeerLambert) ? -expm1f(-tau) : tau;
+    }
     const size_t o = ((size_t)px.view * H + px.r) * W + px.c;
-    out[o] = (MODE == kBeerLambert) ? -expm1f(-s) : s;
-    if (s_out) s_out[o] = s;
+    out[o] = res;
+    if (s_out) s_out[o] = tau;
+}
+
+// Zero padding (near/far mode): 1 for a corner index inside [0, n - 1], 0
+// outside, per axis and end: m = (x0, x1, y0, y1, z0, z1).  Used with the
+// clamped Cell, whose indices then only serve as in-range addresses.
+__device__ inline void pad_mask(const VolumeDesc& V, int64_t qx, int64_t qy, int64_t qz,
+                                float m[6])
+{
+    const int i[3] = {fixed_floor(qx), fixed_floor(qy), fixed_floor(qz)};
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        m[2 * a] = (uint32_t)i[a] < (uint32_t)V.n[a] ? 1.0f : 0.0f;
+        m[2 * a + 1] = (uint32_t)(i[a] + 1) < (uint32_t)V.n[a] ? 1.0f : 0.0f;
+    }
 }
 
 // Trilinear weights of one sample, scaled by yd = y dz: w[c] for corner c
-// (bit 0 = x1, bit 1 = y1, bit 2 = z1).
-__device__ inline void corner_weights(const Cell& C, float yd, float w[8])
+// (bit 0 = x1, bit 1 = y1, bit 2 = z1); with ZP the pad mask drops corners
+// outside the volume.
+template <bool ZP = false>
+__device__ inline void corner_weights(const Cell& C, float yd, float w[8],
+                                      const float* m = nullptr)
 {
-    const float wz1 = yd * C.fz, wz0 = yd * (1.0f - C.fz);
-    const float w11 = wz1 * C.fy, w10 = wz1 * (1.0f - C.fy);
-    const float w01 = wz0 * C.fy, w00 = wz0 * (1.0f - C.fy);
-    const float fx1 = C.fx, fx0 = 1.0f - C.fx;
+    float wz1 = yd * C.fz, wz0 = yd * (1.0f - C.fz);
+    float fy1 = C.fy, fy0 = 1.0f - C.fy;
+    float fx1 = C.fx, fx0 = 1.0f - C.fx;
+    if constexpr (ZP) {
+        fx0 *= m[0]; fx1 *= m[1];
+        fy0 *= m[2]; fy1 *= m[3];
+        wz0 *= m[4]; wz1 *= m[5];
+    }
+    const float w11 = wz1 * fy1, w10 = wz1 * fy0;
+    const float w01 = wz0 * fy1, w00 = wz0 * fy0;
     w[0] = w00 * fx0;
     w[1] = w00 * fx1;
     w[2] = w01 * fx0;
@@ -183,11 +351,12 @@ __device__ inline void corner_weights(const Cell& C, float yd, float w[8])
     w[7] = w11 * fx1;
 }
 
+template <bool ZP = false>
 __device__ inline void scatter_sample_global(float* __restrict__ grad, uint32_t sy, uint32_t sz,
-                                             const Cell& C, float yd)
+                                             const Cell& C, float yd, const float* m = nullptr)
 {
     float w[8];
-    corner_weights(C, yd, w);
+    corner_weights<ZP>(C, yd, w, m);
     const uint32_t r00 = (uint32_t)C.z0 * sz + (uint32_t)C.y0 * sy;
     const uint32_t r01 = (uint32_t)C.z0 * sz + (uint32_t)C.y1 * sy;
     const uint32_t r10 = (uint32_t)C.z1 * sz + (uint32_t)C.y0 * sy;
@@ -250,28 +419,44 @@ __device__ inline bool same_cell(const Cell& a, const Cell& b)
 // roundings, which must stay below 2^31 as well.  A tile whose weights are not
 // finite or whose Cs is too large, or a chunk whose box does not fit the window
 // even for one sample, uses global float atomics directly.
-template <int MODE>
+//
+// The tiles of a launch run over (view, channel) pairs; a pair's rays scatter
+// into the gradient of its channel-volume, with y scaled by the density factor
+// (y = g f exp(-tau) or g f).  CLIP = kClipNearFar samples the view's
+// near/far range and drops corners outside the volume (zero padding); all
+// rays of a workgroup belong to one view, so they share the range.
+template <int MODE, int CLIP>
 __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
     VolumeDesc V, Intrinsics K, const float* __restrict__ poses, int H, int W, int N,
-    int tiles_x, int tiles_per_view, const float* __restrict__ grad_out,
+    int tiles_x, int tiles_per_view, Batch bt, const float* __restrict__ grad_out,
     const float* __restrict__ s_in, float* __restrict__ grad)
 {
+    constexpr bool ZP = CLIP == kClipNearFar;
     __shared__ int win[kWinCap];
     __shared__ int red[(kBlock / 64) * 6];
     __shared__ int box[6];
 
     const int tile = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
     const PixelCoord px = scatter_pixel(tile, tiles_x, tiles_per_view);
+    // px.view counts (view, channel) pairs; a tile lies in one pair
+    const int view = px.view / bt.C, ch = px.view - view * bt.C;
+    grad += (size_t)((view / bt.vpv) * bt.C + ch) * bt.grad_stride;
     bool active = px.r < H && px.c < W;
     MarchRay R;
     float yd = 0.0f;
     if (active) {
         ViewGeom G;
-        view_setup(poses + 12 * px.view, K, G);
-        active = ray_setup(G, V, px.r, px.c, N, R);
+        view_setup(poses + 12 * view, K, G);
+        if constexpr (CLIP == kClipBox) {
+            active = ray_setup(G, V, px.r, px.c, N, R);
+        } else {
+            double t_near, t_far;
+            view_near_far(G, V, bt.margin, t_near, t_far);
+            active = ray_setup_range(G, V, px.r, px.c, N, t_near, t_far, R);
+        }
         if (active) {
             const size_t o = ((size_t)px.view * H + px.r) * W + px.c;
-            float y = grad_out[o];
+            float y = grad_out[o] * bt.f;
             if (MODE == kBeerLambert) y *= expf(-s_in[o]);
             yd = y * R.dz;
             active = yd != 0.0f;
@@ -339,16 +524,18 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 int64_t qy = R.q0[1] + (int64_t)k0 * R.dq[1];
                 int64_t qz = R.q0[2] + (int64_t)k0 * R.dq[2];
                 Cell P;
-                float acc[8];
+                float acc[8], m[6];
                 cell_of(V, qx, qy, qz, P);
-                corner_weights(P, ys, acc);
+                if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
+                corner_weights<ZP>(P, ys, acc, m);
                 qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
                 for (int k = k0 + 1; k < k0 + S; ++k) {
                     Cell C;
                     cell_of(V, qx, qy, qz, C);
+                    if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
                     qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
                     float w[8];
-                    corner_weights(C, ys, w);
+                    corner_weights<ZP>(C, ys, w, m);
                     if (same_cell(C, P)) {
 #pragma unroll
                         for (int i = 0; i < 8; ++i) acc[i] += w[i];
@@ -381,14 +568,92 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
             int64_t qz = R.q0[2] + (int64_t)k0 * R.dq[2];
             for (int k = k0; k < k0 + S; ++k) {
                 Cell C;
+                float m[6];
                 cell_of(V, qx, qy, qz, C);
+                if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
                 qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
-                scatter_sample_global(grad, sy, sz, C, yd);
+                scatter_sample_global<ZP>(grad, sy, sz, C, yd, m);
             }
         }
         k0 += S;
         // a chunk that left room in the window: try a longer one next
         if (vol * 2 <= kWinCap) S *= 2;
+    }
+}
+
+// Backward of alpha compositing.  For I = sum_k T_k alpha_k v_k with
+// alpha_k = 1 - exp(-f v_k dz) and T_k = exp(-f dz sum_{j<k} v_j), sample k's
+// own weight is
+//   dI/dv_k = T_k (alpha_k + f dz (1 - alpha_k) v_k) - f dz sum_{j>k} T_j alpha_j v_j
+// (its emission and opacity, and the transmittance it takes from every later
+// sample); the later-sample sum is the forward's I minus the running sum up to
+// k (fp64).  Each sample gathers its eight corners from the linear volume (of
+// the caller, or the fp32 mapped copy), clamped or zero-padded, and scatters
+// g dI/dv_k w_corner with global float atomics.  One lane per ray.
+template <typename T, int CLIP>
+__global__ __launch_bounds__(kBlock) void drr_alpha_scatter_kernel(
+    const T* __restrict__ vol, uint32_t vol_bytes, VolumeDesc V, Intrinsics K,
+    const float* __restrict__ poses, int H, int W, int N, int tiles_x, int tiles_per_view,
+    Batch bt, const float* __restrict__ grad_out, const float* __restrict__ out_in,
+    float* __restrict__ grad)
+{
+    constexpr bool ZP = CLIP == kClipNearFar;
+    const int tile = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
+    const PixelCoord px = scatter_pixel(tile, tiles_x, tiles_per_view);
+    if (px.r >= H || px.c >= W) return;
+    const int view = px.view / bt.C, ch = px.view - view * bt.C;
+    const int cvol = (view / bt.vpv) * bt.C + ch;
+    ViewGeom G;
+    view_setup(poses + 12 * view, K, G);
+    MarchRay R;
+    bool hit;
+    if constexpr (CLIP == kClipBox) {
+        hit = ray_setup(G, V, px.r, px.c, N, R);
+    } else {
+        double t_near, t_far;
+        view_near_far(G, V, bt.margin, t_near, t_far);
+        hit = ray_setup_range(G, V, px.r, px.c, N, t_near, t_far, R);
+    }
+    if (!hit) return;
+    const size_t o = ((size_t)px.view * H + px.r) * W + px.c;
+    const float g = grad_out[o];
+    if (g == 0.0f) return;
+    const double I_total = (double)out_in[o];
+    grad += (size_t)cvol * bt.grad_stride;
+    const char* base = reinterpret_cast<const char*>(vol) + (uint64_t)cvol * bt.src_stride;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)vol_bytes, kBufferWord3);
+    const uint32_t sy = (uint32_t)V.n[0], sz = (uint32_t)V.n[0] * (uint32_t)V.n[1];
+    const float fdz = bt.f * R.dz;
+    int64_t qx = R.q0[0], qy = R.q0[1], qz = R.q0[2];
+    double tau = 0.0, run = 0.0;
+    for (int k = 0; k < N; ++k) {
+        Cell C;
+        float m[6];
+        cell_of(V, qx, qy, qz, C);
+        if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
+        qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
+        float w[8];
+        corner_weights<ZP>(C, 1.0f, w, m);
+        const uint32_t r00 = (uint32_t)C.z0 * sz + (uint32_t)C.y0 * sy;
+        const uint32_t r01 = (uint32_t)C.z0 * sz + (uint32_t)C.y1 * sy;
+        const uint32_t r10 = (uint32_t)C.z1 * sz + (uint32_t)C.y0 * sy;
+        const uint32_t r11 = (uint32_t)C.z1 * sz + (uint32_t)C.y1 * sy;
+        const uint32_t idx[8] = {r00 + C.x0, r00 + C.x1, r01 + C.x0, r01 + C.x1,
+                                 r10 + C.x0, r10 + C.x1, r11 + C.x0, r11 + C.x1};
+        float v = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v = fmaf(w[c], load_one<T>(rs, idx[c] * (uint32_t)sizeof(T)), v);
+        const float a = fdz * v;
+        const float Tk = expf(-(float)tau);
+        const float alpha = -expm1f(-a);
+        const float e = Tk * alpha * v;
+        run += (double)e;
+        const float later = (float)(I_total - run);
+        const float coef = g * (Tk * (alpha + fdz * (1.0f - alpha) * v) - fdz * later);
+        tau += (double)a;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) unsafeAtomicAdd(grad + idx[c], coef * w[c]);
     }
 }
 
@@ -400,30 +665,37 @@ __global__ __launch_bounds__(256) void drr_fill_kernel(float* __restrict__ p, si
 
 // ----------------------------------------------------------------- launchers
 
-static void tile_grid(int n_views, int H, int W, int side, int& tiles_x, int& tiles_per_view,
+static void tile_grid(int n_pairs, int H, int W, int side, int& tiles_x, int& tiles_per_view,
                       int& n_tiles)
 {
     tiles_x = (W + side - 1) / side;
     const int tiles_y = (H + side - 1) / side;
     tiles_per_view = tiles_x * tiles_y;
-    n_tiles = tiles_per_view * n_views;
+    n_tiles = tiles_per_view * n_pairs;
 }
 
-template <typename T, Layout L, int SPLIT>
-static void launch_march(const LaunchArgs& a, const T* src, uint32_t src_bytes, float* out,
-                         float* s_out, hipStream_t stream)
+static Batch make_batch(const LaunchArgs& a, const RenderPlan* plan, size_t in_volume_bytes)
+{
+    Batch b;
+    b.src_stride = plan ? (uint64_t)plan->per_volume_bytes : (uint64_t)in_volume_bytes;
+    b.grad_stride = (uint32_t)((size_t)a.V.n[0] * a.V.n[1] * a.V.n[2]);
+    b.C = a.C;
+    b.vpv = a.n_views / a.n_volumes;
+    b.f = a.f;
+    b.margin = a.margin;
+    return b;
+}
+
+template <typename T, Layout L, int MODE, int SPLIT, int CLIP>
+static void launch_march(const LaunchArgs& a, const T* src, uint32_t src_bytes, const Batch& b,
+                         float* out, float* s_out, hipStream_t stream)
 {
     int tiles_x, tiles_per_view, n_tiles;
-    tile_grid(a.n_views, a.H, a.W, march_tile_side<SPLIT>(), tiles_x, tiles_per_view, n_tiles);
-    const dim3 grid(n_tiles), block(kBlock);
-    if (a.mode == kBeerLambert)
-        hipLaunchKernelGGL((drr_march_kernel<T, L, kBeerLambert, SPLIT>), grid, block, 0, stream,
-                           src, src_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
-                           tiles_per_view, out, s_out);
-    else
-        hipLaunchKernelGGL((drr_march_kernel<T, L, kLineIntegral, SPLIT>), grid, block, 0, stream,
-                           src, src_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
-                           tiles_per_view, out, s_out);
+    tile_grid(a.n_views * a.C, a.H, a.W, march_tile_side<SPLIT>(), tiles_x, tiles_per_view,
+              n_tiles);
+    hipLaunchKernelGGL((drr_march_kernel<T, L, MODE, SPLIT, CLIP>), dim3(n_tiles), dim3(kBlock), 0,
+                       stream, src, src_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                       tiles_per_view, b, out, s_out);
 }
 
 // Lanes per ray: one, unless the launch has too few rays to give every SIMD of
@@ -437,59 +709,156 @@ static int march_split(long long n_rays, int N)
     return 64;
 }
 
-template <typename T, Layout L>
-static void launch_march_split(const LaunchArgs& a, const T* src, uint32_t src_bytes, float* out,
-                               float* s_out, hipStream_t stream)
+template <typename T, Layout L, int MODE, int CLIP>
+static void launch_march_split(const LaunchArgs& a, const T* src, uint32_t src_bytes,
+                               const Batch& b, float* out, float* s_out, hipStream_t stream)
 {
-    switch (march_split((long long)a.n_views * a.H * a.W, a.N)) {
-    case 1: launch_march<T, L, 1>(a, src, src_bytes, out, s_out, stream); break;
-    case 4: launch_march<T, L, 4>(a, src, src_bytes, out, s_out, stream); break;
-    case 16: launch_march<T, L, 16>(a, src, src_bytes, out, s_out, stream); break;
-    default: launch_march<T, L, 64>(a, src, src_bytes, out, s_out, stream); break;
+    if constexpr (MODE == kAlpha) {
+        launch_march<T, L, MODE, 1, CLIP>(a, src, src_bytes, b, out, s_out, stream);
+    } else {
+        switch (march_split((long long)a.n_views * a.C * a.H * a.W, a.N)) {
+        case 1: launch_march<T, L, MODE, 1, CLIP>(a, src, src_bytes, b, out, s_out, stream); break;
+        case 4: launch_march<T, L, MODE, 4, CLIP>(a, src, src_bytes, b, out, s_out, stream); break;
+        case 16: launch_march<T, L, MODE, 16, CLIP>(a, src, src_bytes, b, out, s_out, stream); break;
+        default: launch_march<T, L, MODE, 64, CLIP>(a, src, src_bytes, b, out, s_out, stream); break;
+        }
     }
 }
 
+template <typename T, Layout L, int CLIP>
+static void launch_march_mode(const LaunchArgs& a, const T* src, uint32_t src_bytes,
+                              const Batch& b, float* out, float* s_out, hipStream_t stream)
+{
+    if (a.mode == kBeerLambert)
+        launch_march_split<T, L, kBeerLambert, CLIP>(a, src, src_bytes, b, out, s_out, stream);
+    else if (a.mode == kLineIntegral)
+        launch_march_split<T, L, kLineIntegral, CLIP>(a, src, src_bytes, b, out, s_out, stream);
+    else
+        launch_march_split<T, L, kAlpha, CLIP>(a, src, src_bytes, b, out, s_out, stream);
+}
+
+static int grid_blocks(long long n, int cap)
+{
+    const long long b = (n + 255) / 256;
+    return (int)(b < cap ? (b > 0 ? b : 1) : cap);
+}
+
+// Corner cells of all n_volumes * C channel-volumes into `cells` (stride
+// per_volume_bytes), zero-padded in the near/far mode, mapped by the transfer
+// function when there is one (then fp32).
+template <typename Tin>
+static hipError_t launch_cells_typed(const LaunchArgs& a, const RenderPlan& p, const Tin* vol,
+                                     void* cells, hipStream_t stream)
+{
+    const long long n_cells = (long long)(a.V.n[0] + 1) * (a.V.n[1] + 1) * (a.V.n[2] + 1);
+    const dim3 grid(grid_blocks(n_cells, 16384), a.n_volumes * a.C);
+    const size_t in_stride = (size_t)a.V.n[0] * a.V.n[1] * a.V.n[2];
+    const bool zp = a.clip == kClipNearFar;
+    if (p.mapped) {
+        const size_t out_stride = p.per_volume_bytes / sizeof(float);
+        float* c = static_cast<float*>(cells);
+        if (zp)
+            hipLaunchKernelGGL((drr_cells_kernel<Tin, float, true, true>), grid, dim3(256), 0,
+                               stream, vol, a.V.n[0], a.V.n[1], a.V.n[2], in_stride, c,
+                               out_stride, a.C, a.tf);
+        else
+            hipLaunchKernelGGL((drr_cells_kernel<Tin, float, false, true>), grid, dim3(256), 0,
+                               stream, vol, a.V.n[0], a.V.n[1], a.V.n[2], in_stride, c,
+                               out_stride, a.C, a.tf);
+    } else {
+        const size_t out_stride = p.per_volume_bytes / sizeof(Tin);
+        Tin* c = static_cast<Tin*>(cells);
+        if (zp)
+            hipLaunchKernelGGL((drr_cells_kernel<Tin, Tin, true, false>), grid, dim3(256), 0,
+                               stream, vol, a.V.n[0], a.V.n[1], a.V.n[2], in_stride, c,
+                               out_stride, a.C, a.tf);
+        else
+            hipLaunchKernelGGL((drr_cells_kernel<Tin, Tin, false, false>), grid, dim3(256), 0,
+                               stream, vol, a.V.n[0], a.V.n[1], a.V.n[2], in_stride, c,
+                               out_stride, a.C, a.tf);
+    }
+    return hipGetLastError();
+}
+
+// The plain corner-cell copy of one volume (the pose gradient's march).
 hipError_t launch_cells(const VolumeDesc& V, const void* vol, int dtype, void* cells,
                         hipStream_t stream)
 {
-    const long long n_cells = (long long)(V.n[0] + 1) * (V.n[1] + 1) * (V.n[2] + 1);
-    const int blocks = (int)((n_cells + 255) / 256 < 16384 ? (n_cells + 255) / 256 : 16384);
+    LaunchArgs a{};
+    a.V = V;
+    a.n_volumes = a.C = 1;
+    a.clip = kClipBox;
+    RenderPlan p{};
+    p.cells = true;
+    p.read_elem = dtype == 0 ? 4 : 2;
+    p.per_volume_bytes = (size_t)V.cell_total_bytes;
     if (dtype == 0)
-        hipLaunchKernelGGL((drr_cells_kernel<float>), dim3(blocks), dim3(256), 0, stream,
-                           static_cast<const float*>(vol), V.n[0], V.n[1], V.n[2],
-                           static_cast<float*>(cells));
-    else
-        hipLaunchKernelGGL((drr_cells_kernel<uint16_t>), dim3(blocks), dim3(256), 0, stream,
-                           static_cast<const uint16_t*>(vol), V.n[0], V.n[1], V.n[2],
-                           static_cast<uint16_t*>(cells));
+        return launch_cells_typed<float>(a, p, static_cast<const float*>(vol), cells, stream);
+    return launch_cells_typed<uint16_t>(a, p, static_cast<const uint16_t*>(vol), cells, stream);
+}
+
+template <typename Tin>
+static hipError_t launch_transfer_typed(const LaunchArgs& a, const RenderPlan& p, const Tin* vol,
+                                        float* mu, hipStream_t stream)
+{
+    const size_t n_vox = (size_t)a.V.n[0] * a.V.n[1] * a.V.n[2];
+    const dim3 grid(grid_blocks((long long)n_vox, 4096), a.n_volumes * a.C);
+    hipLaunchKernelGGL((drr_transfer_kernel<Tin>), grid, dim3(256), 0, stream, vol, n_vox, n_vox,
+                       mu, p.per_volume_bytes / sizeof(float), a.C, a.tf);
     return hipGetLastError();
 }
 
-template <typename T>
-static hipError_t forward_typed(const LaunchArgs& a, const T* vol, bool cells, T* cell_buf,
-                               float* out, float* s_out, hipStream_t stream)
+template <typename Tin>
+static hipError_t forward_typed(const LaunchArgs& a, const RenderPlan& p, const Tin* vol,
+                                void* workspace, float* out, float* s_out, hipStream_t stream)
 {
-    if (cells) {
-        const hipError_t e = launch_cells(a.V, vol, sizeof(T) == 4 ? 0 : 1, cell_buf, stream);
+    const Batch b = make_batch(a, &p, 0);
+    const uint32_t bytes = p.cells ? a.V.cell_total_bytes : (uint32_t)((size_t)a.V.n[0] * a.V.n[1] *
+                                                                      a.V.n[2] * p.read_elem);
+    if (p.cells) {
+        hipError_t e = launch_cells_typed<Tin>(a, p, vol, workspace, stream);
         if (e != hipSuccess) return e;
-        launch_march_split<T, Layout::Cell>(a, cell_buf, a.V.cell_total_bytes, out, s_out, stream);
+        if (p.mapped) {
+            const float* c = static_cast<const float*>(workspace);
+            if (a.clip == kClipNearFar)
+                launch_march_mode<float, Layout::Cell, kClipNearFar>(a, c, bytes, b, out, s_out, stream);
+            else
+                launch_march_mode<float, Layout::Cell, kClipBox>(a, c, bytes, b, out, s_out, stream);
+        } else {
+            const Tin* c = static_cast<const Tin*>(workspace);
+            if (a.clip == kClipNearFar)
+                launch_march_mode<Tin, Layout::Cell, kClipNearFar>(a, c, bytes, b, out, s_out, stream);
+            else
+                launch_march_mode<Tin, Layout::Cell, kClipBox>(a, c, bytes, b, out, s_out, stream);
+        }
+        return hipGetLastError();
+    }
+    // linear reads: the caller's volume, or its mapped fp32 copy
+    if (p.mapped) {
+        float* mu = static_cast<float*>(workspace);
+        hipError_t e = launch_transfer_typed<Tin>(a, p, vol, mu, stream);
+        if (e != hipSuccess) return e;
+        if (a.V.n[0] >= 2)
+            launch_march_mode<float, Layout::Pair, kClipBox>(a, mu, bytes, b, out, s_out, stream);
+        else
+            launch_march_mode<float, Layout::Single, kClipBox>(a, mu, bytes, b, out, s_out, stream);
     } else if (a.V.n[0] >= 2) {
-        launch_march_split<T, Layout::Pair>(a, vol, a.V.total_bytes, out, s_out, stream);
+        launch_march_mode<Tin, Layout::Pair, kClipBox>(a, vol, bytes, b, out, s_out, stream);
     } else {
-        launch_march_split<T, Layout::Single>(a, vol, a.V.total_bytes, out, s_out, stream);
+        launch_march_mode<Tin, Layout::Single, kClipBox>(a, vol, bytes, b, out, s_out, stream);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_forward(const LaunchArgs& a, const void* vol, int dtype, bool cells,
+hipError_t launch_forward(const LaunchArgs& a, const RenderPlan& plan, const void* vol, int dtype,
                           void* workspace, float* out, float* s_out, hipStream_t stream)
 {
-    if ((long long)a.n_views * a.H * a.W == 0) return hipSuccess;
+    if ((long long)a.n_views * a.C * a.H * a.W == 0) return hipSuccess;
     if (dtype == 0)
-        return forward_typed<float>(a, static_cast<const float*>(vol), cells,
-                                    static_cast<float*>(workspace), out, s_out, stream);
-    return forward_typed<uint16_t>(a, static_cast<const uint16_t*>(vol), cells,
-                                   static_cast<uint16_t*>(workspace), out, s_out, stream);
+        return forward_typed<float>(a, plan, static_cast<const float*>(vol), workspace, out, s_out,
+                                    stream);
+    return forward_typed<uint16_t>(a, plan, static_cast<const uint16_t*>(vol), workspace, out,
+                                   s_out, stream);
 }
 
 hipError_t launch_fill(float* p, size_t n, hipStream_t stream)
@@ -500,22 +869,83 @@ hipError_t launch_fill(float* p, size_t n, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t launch_backward(const LaunchArgs& a, const float* grad_out, const float* s_in,
-                           float* grad, hipStream_t stream)
+template <typename T>
+static void launch_alpha_scatter(const LaunchArgs& a, const T* vol, uint32_t vol_bytes,
+                                 const Batch& b, const float* grad_out, const float* out_in,
+                                 float* grad, int tiles_x, int tiles_per_view, int n_tiles,
+                                 hipStream_t stream)
 {
-    hipError_t e = launch_fill(grad, (size_t)a.V.n[0] * a.V.n[1] * a.V.n[2], stream);
+    if (a.clip == kClipNearFar)
+        hipLaunchKernelGGL((drr_alpha_scatter_kernel<T, kClipNearFar>), dim3(n_tiles), dim3(kBlock),
+                           0, stream, vol, vol_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                           tiles_per_view, b, grad_out, out_in, grad);
+    else
+        hipLaunchKernelGGL((drr_alpha_scatter_kernel<T, kClipBox>), dim3(n_tiles), dim3(kBlock), 0,
+                           stream, vol, vol_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                           tiles_per_view, b, grad_out, out_in, grad);
+}
+
+template <typename Tin>
+static hipError_t backward_typed(const LaunchArgs& a, const Tin* vol, const float* grad_out,
+                                 const float* out_in, const float* s_in, float* grad,
+                                 void* workspace, hipStream_t stream)
+{
+    const size_t n_vox = (size_t)a.V.n[0] * a.V.n[1] * a.V.n[2];
+    hipError_t e = launch_fill(grad, n_vox * (size_t)a.n_volumes * a.C, stream);
     if (e != hipSuccess) return e;
     int tiles_x, tiles_per_view, n_tiles;
-    tile_grid(a.n_views, a.H, a.W, kTile, tiles_x, tiles_per_view, n_tiles);
+    tile_grid(a.n_views * a.C, a.H, a.W, kTile, tiles_x, tiles_per_view, n_tiles);
     if (n_tiles == 0) return hipSuccess;
     const dim3 grid(n_tiles), block(kBlock);
-    if (a.mode == kBeerLambert)
-        hipLaunchKernelGGL((drr_scatter_kernel<kBeerLambert>), grid, block, 0, stream, a.V, a.K,
-                           a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view, grad_out, s_in, grad);
-    else
-        hipLaunchKernelGGL((drr_scatter_kernel<kLineIntegral>), grid, block, 0, stream, a.V, a.K,
-                           a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view, grad_out, s_in, grad);
+    if (a.mode == kAlpha) {
+        if (a.has_tf) {
+            // gather the mapped volumes: their fp32 copy in the workspace
+            RenderPlan p{};
+            p.mapped = true;
+            p.per_volume_bytes = (n_vox * 4 + 255) & ~(size_t)255;
+            float* mu = static_cast<float*>(workspace);
+            e = launch_transfer_typed<Tin>(a, p, vol, mu, stream);
+            if (e != hipSuccess) return e;
+            Batch b = make_batch(a, &p, 0);
+            launch_alpha_scatter<float>(a, mu, (uint32_t)(n_vox * 4), b, grad_out, out_in, grad,
+                                        tiles_x, tiles_per_view, n_tiles, stream);
+        } else {
+            const Batch b = make_batch(a, nullptr, n_vox * sizeof(Tin));
+            launch_alpha_scatter<Tin>(a, vol, (uint32_t)(n_vox * sizeof(Tin)), b, grad_out, out_in,
+                                      grad, tiles_x, tiles_per_view, n_tiles, stream);
+        }
+    } else {
+        const Batch b = make_batch(a, nullptr, 0);
+#define DRR_SCATTER(MODE, CLIP)                                                                 \
+    hipLaunchKernelGGL((drr_scatter_kernel<MODE, CLIP>), grid, block, 0, stream, a.V, a.K,      \
+                       a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view, b, grad_out, s_in, grad)
+        if (a.mode == kBeerLambert) {
+            if (a.clip == kClipNearFar) DRR_SCATTER(kBeerLambert, kClipNearFar);
+            else DRR_SCATTER(kBeerLambert, kClipBox);
+        } else {
+            if (a.clip == kClipNearFar) DRR_SCATTER(kLineIntegral, kClipNearFar);
+            else DRR_SCATTER(kLineIntegral, kClipBox);
+        }
+#undef DRR_SCATTER
+    }
+    e = hipGetLastError();
+    if (e != hipSuccess || !a.has_tf) return e;
+    // dL/dx = dL/dmu tf'(x)
+    const dim3 sgrid(grid_blocks((long long)n_vox, 4096), a.n_volumes * a.C);
+    hipLaunchKernelGGL((drr_slope_kernel<Tin>), sgrid, dim3(256), 0, stream, vol, n_vox, n_vox,
+                       grad, a.C, a.tf);
     return hipGetLastError();
+}
+
+hipError_t launch_backward(const LaunchArgs& a, const void* vol, int dtype, const float* grad_out,
+                           const float* out_in, const float* s_in, float* grad, void* workspace,
+                           hipStream_t stream)
+{
+    if (dtype == 0)
+        return backward_typed<float>(a, static_cast<const float*>(vol), grad_out, out_in, s_in,
+                                     grad, workspace, stream);
+    return backward_typed<uint16_t>(a, static_cast<const uint16_t*>(vol), grad_out, out_in, s_in,
+                                    grad, workspace, stream);
 }
 
 }  // namespace drr

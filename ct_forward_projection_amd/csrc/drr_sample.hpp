@@ -68,9 +68,28 @@ struct SampleAddr {
     float fx, fy, fz;
     float gxs;                     // Pair: 0 where the x weight was pinned at a clamped
                                    // edge (the field is flat in x there), else 1
+    float ex, ey, ez;              // zero padding: 1 - fx, 1 - fy, 1 - fz, exact
 };
 
-template <typename T, Layout L>
+// 1 - f for the fraction f of a 32.32 fixed-point position, taken from the
+// integer so that it keeps full relative precision when f is close to 1.  With
+// zero padding a voxel next to the volume's edge is weighed against a zero
+// voxel by 1 - f alone, and 1 - (f rounded to fp32) would carry up to 3e-8
+// absolute error into values that can be 1e-3 of the image's maximum.
+__device__ inline float fixed_comp(int64_t q)
+{
+    const uint32_t fr = (uint32_t)q;
+    return fr ? (float)(0u - fr) * 2.3283064365386963e-10f : 1.0f;
+}
+
+// Byte offset past the end of any corner-cell copy (those stay below
+// 0xffffff00 bytes): buffer loads there return zeros.
+constexpr uint32_t kOutOfRange = 0xffffff00u;
+
+// ZP (zero padding, Cell layout only): a sample whose cell lies outside the
+// corner-cell grid reads 0; the cells themselves hold 0 for corners outside the
+// volume.
+template <typename T, Layout L, bool ZP = false>
 __device__ inline SampleAddr sample_addr(const VolumeDesc& V, int64_t qx, int64_t qy, int64_t qz)
 {
     SampleAddr A;
@@ -84,8 +103,19 @@ __device__ inline SampleAddr sample_addr(const VolumeDesc& V, int64_t qx, int64_
         // would fall outside the buffer range and read zeros, never fault
         A.o = (uint32_t)(iz + 1) * V.cell_slice_bytes +
               __umul24((uint32_t)(iy + 1), V.cell_row_bytes) + (uint32_t)(ix + 1) * (8 * sizeof(T));
+        if constexpr (ZP) {
+            A.ex = fixed_comp(qx);
+            A.ey = fixed_comp(qy);
+            A.ez = fixed_comp(qz);
+            const bool in = (uint32_t)(ix + 1) <= (uint32_t)V.n[0] &&
+                            (uint32_t)(iy + 1) <= (uint32_t)V.n[1] &&
+                            (uint32_t)(iz + 1) <= (uint32_t)V.n[2];
+            if (!in) A.o = kOutOfRange;
+        }
         A.dy = A.dz = A.x1 = 0;
         return A;
+    } else {
+        static_assert(!ZP, "zero padding reads the corner-cell copy");
     }
     const int y0 = clampi(iy, 0, V.n[1] - 1), y1 = clampi(iy + 1, 0, V.n[1] - 1);
     const int z0 = clampi(iz, 0, V.n[2] - 1), z1 = clampi(iz + 1, 0, V.n[2] - 1);
@@ -167,6 +197,18 @@ __device__ inline float interpolate(const SampleAddr& A, const CornerVals& c)
     return fmaf(A.fz, c1 - c0, c0);
 }
 
+// The same trilinear value as weighted sums with the exact complements (zero
+// padding): every corner's weight keeps full relative precision.
+__device__ inline float interpolate_exact(const SampleAddr& A, const CornerVals& c)
+{
+    const float c00 = fmaf(A.fx, c.v[1], A.ex * c.v[0]);
+    const float c10 = fmaf(A.fx, c.v[3], A.ex * c.v[2]);
+    const float c01 = fmaf(A.fx, c.v[5], A.ex * c.v[4]);
+    const float c11 = fmaf(A.fx, c.v[7], A.ex * c.v[6]);
+    const float c0 = fmaf(A.fy, c10, A.ey * c00);
+    const float c1 = fmaf(A.fy, c11, A.ey * c01);
+    return fmaf(A.fz, c1, A.ez * c0);
+}
 
 // Trilinear value and its gradient with respect to the continuous index q
 // (per voxel); with clamped corners the differences along a clamped axis vanish.

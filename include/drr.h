@@ -58,9 +58,15 @@ extern "C" {
  * to fp32; every sum is accumulated in fp32. */
 typedef enum { DRR_F32 = 0, DRR_BF16 = 1 } drr_dtype;
 
-/* Output modes: Beer-Lambert image 1 - exp(-s) (flashdrr use_beer_lambert) or
- * the raw line integral s (diffct project). */
-typedef enum { DRR_BEER_LAMBERT = 0, DRR_LINE_INTEGRAL = 1 } drr_mode;
+/* Output modes: Beer-Lambert image 1 - exp(-s) (flashdrr use_beer_lambert),
+ * the raw line integral s (diffct project), or -- drr_render only --
+ * front-to-back alpha compositing (flashdrr use_beer_lambert = False, the
+ * "over" operator; see drr_render). */
+typedef enum { DRR_BEER_LAMBERT = 0, DRR_LINE_INTEGRAL = 1, DRR_ALPHA_COMPOSITE = 2 } drr_mode;
+
+/* Sample range of a ray (drr_render only): the per-ray box clip of every other
+ * call, or flashdrr's per-view near/far range (see drr_render). */
+typedef enum { DRR_CLIP_BOX = 0, DRR_CLIP_NEAR_FAR = 1 } drr_clip;
 
 typedef enum {
     DRR_OK = 0,
@@ -174,6 +180,103 @@ int drr_backward_volume_siddon(int nz, int ny, int nx, const float *spacing, con
                                const float *poses, int n_views, int det_h, int det_w, int mode,
                                const float *grad_out, const float *line_integral,
                                float *grad_volume, void *stream);
+
+/* ------------------------------------------------------------------------
+ * The flashdrr front end: drr_render and its volume gradient.
+ *
+ * flashdrr.rendering API, VolumeRaycaster.forward: vol is (B, C, D, H, W)
+ * in voxel space, view matrices number N = B * views_per_vol (view v renders
+ * volume v / views_per_vol), output (N, C, H, W).  VolumeRaycaster.__init__:
+ * density_factor scales the volume before integration; use_beer_lambert =
+ * False selects front-to-back alpha compositing.  compute_clipping_distances:
+ * one near and one far distance per view from the camera to the closest and
+ * farthest volume point, widened by a margin.  Transfer functions,
+ * piecewise_linear_channelwise: a per-channel piecewise-linear map over sorted
+ * knots that extends its end segments, applied to the volume before ray
+ * casting.
+ *
+ * Readings (the pages give no formulas):
+ *   - mu = tf_c(x) voxel by voxel when a transfer function is given (else
+ *     mu = x), then sampled trilinearly as in drr_forward;
+ *   - optical depth tau = f dz sum_k mu(t_k) with f = density_factor;
+ *     Beer-Lambert 1 - exp(-tau); line integral tau;
+ *   - alpha compositing: sample k is a slab of thickness dz that emits mu_k
+ *     with opacity alpha_k = 1 - exp(-f mu_k dz) behind the transmittance
+ *     T_k = prod_{j<k} (1 - alpha_j); I = sum_k T_k alpha_k mu_k;
+ *   - DRR_CLIP_NEAR_FAR: near = max(distance from the camera centre to the
+ *     closest point of the box - margin, 0), far = distance to the farthest
+ *     box corner + margin; every ray of the view samples the midpoints of
+ *     [near, far] (far <= near renders 0) and reads 0 outside the volume
+ *     (zero padding: a trilinear corner outside [0, n-1] holds 0);
+ *   - transfer segment i spans [xp_i, xp_{i+1}); below xp_1 the first and from
+ *     xp_{K-2} on the last segment applies; at a knot the slope is the right
+ *     segment's. */
+
+/* Workspace bytes of drr_render (for_backward = DRR_WORKSPACE_FORWARD) or
+ * drr_render_backward_volume (DRR_WORKSPACE_VOLUME_BACKWARD) for these
+ * sizes; tf_knots = 0 means no transfer function.  0 for invalid sizes or when
+ * none is needed.  The forward uses it for a corner-cell copy of every
+ * channel-volume (when rays reuse cells enough, and always in the near/far
+ * mode), or for the mapped fp32 volumes; the compositing backward with a
+ * transfer function for the mapped fp32 volumes. */
+size_t drr_render_workspace_bytes(int n_volumes, int n_channels, int nz, int ny, int nx,
+                                  int dtype, int n_views, int det_h, int det_w, int n_samples,
+                                  int mode, int clip, int tf_knots, int for_backward);
+
+/* Render n_volumes volumes of n_channels channels.
+ *   volume        device, n_volumes x n_channels x nz x ny x nx elements of
+ *                 dtype, C-contiguous (each channel-volume x fastest)
+ *   spacing, K    host, as drr_forward
+ *   poses         device, n_views x 12 fp32 world-to-camera [R | t];
+ *                 n_views must be a multiple of n_volumes
+ *   n_samples     samples per ray
+ *   mode          DRR_BEER_LAMBERT, DRR_LINE_INTEGRAL or DRR_ALPHA_COMPOSITE
+ *   density_factor  f (finite)
+ *   clip, margin  DRR_CLIP_BOX (margin ignored) or DRR_CLIP_NEAR_FAR with the
+ *                 margin in mm (finite; negative narrows the range)
+ *   tf_xp, tf_yp  host or both NULL: n_channels x tf_knots floats, each
+ *                 channel's knots strictly increasing; 2 <= tf_knots and
+ *                 n_channels * tf_knots <= 128
+ *   out           device, n_views x n_channels x det_h x det_w floats
+ *   aux           device or NULL: the optical depth tau in the same layout
+ *                 (the Beer-Lambert backward needs it)
+ *   workspace     device, >= drr_render_workspace_bytes(..., DRR_WORKSPACE_FORWARD),
+ *                 256-byte aligned
+ * Limits as drr_forward per channel-volume; n_volumes * n_channels <= 65535.
+ * drr_forward(...) equals drr_render with one volume, one channel, f = 1, the
+ * box clip and no transfer function. */
+int drr_render(const void *volume, int dtype, int n_volumes, int n_channels, int nz, int ny,
+               int nx, const float *spacing, const float *K, const float *poses, int n_views,
+               int det_h, int det_w, int n_samples, int mode, float density_factor, int clip,
+               float margin, const float *tf_xp, const float *tf_yp, int tf_knots, float *out,
+               float *aux, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Gradient of L = sum grad_out * out with respect to the input volume x of
+ * drr_render (same arguments).  Per sample k of a ray, dL/dmu at its trilinear
+ * corners receives grad_out * c_k * w_corner with
+ *   Beer-Lambert       c_k = f dz exp(-tau)
+ *   line integral      c_k = f dz
+ *   alpha compositing  c_k = T_k (alpha_k + f dz (1 - alpha_k) mu_k)
+ *                            - f dz sum_{j>k} T_j alpha_j mu_j
+ * and with a transfer function dL/dx = dL/dmu tf'(x) per voxel.
+ *   volume        device; required for alpha compositing and with a transfer
+ *                 function, else may be NULL
+ *   grad_out      device, n_views x n_channels x det_h x det_w floats
+ *   out           device, the forward's image; required for alpha compositing
+ *   aux           device, the forward's optical depth; required for Beer-Lambert
+ *   grad_volume   device, n_volumes x n_channels x nz x ny x nx floats, OVERWRITTEN
+ *   workspace     device, >= drr_render_workspace_bytes(..., DRR_WORKSPACE_VOLUME_BACKWARD),
+ *                 256-byte aligned
+ * Accumulation uses fp32 atomics, so the result may differ between runs in
+ * the last bits. */
+int drr_render_backward_volume(const void *volume, int dtype, int n_volumes, int n_channels,
+                               int nz, int ny, int nx, const float *spacing, const float *K,
+                               const float *poses, int n_views, int det_h, int det_w,
+                               int n_samples, int mode, float density_factor, int clip,
+                               float margin, const float *tf_xp, const float *tf_yp,
+                               int tf_knots, const float *grad_out, const float *out,
+                               const float *aux, float *grad_volume, void *workspace,
+                               size_t workspace_bytes, void *stream);
 
 /* Static description of a drr_status value. */
 const char *drr_status_string(int status);

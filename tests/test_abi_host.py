@@ -175,3 +175,82 @@ def test_siddon_empty_calls_are_valid_no_ops():
     assert fwd_siddon(n_views=0, poses=None, out=None) == 0
     assert fwd_siddon(det_w=0) == 0
     assert drr.library().drr_last_error() == b""
+
+
+# ----------------------------------------------------------------- drr_render
+
+def render_call(**kw):
+    args = dict(volume=DUMMY, dtype=0, B=1, C=1, nz=8, ny=8, nx=8, spacing=SP, K=K, poses=DUMMY,
+                n_views=2, det_h=4, det_w=4, n_samples=8, mode=0, f=1.0, clip=0, margin=30.0,
+                xp=None, yp=None, knots=0, out=DUMMY, aux=None, ws=None, ws_bytes=0, stream=None)
+    args.update(kw)
+    a = args
+    return drr.library().drr_render(a["volume"], a["dtype"], a["B"], a["C"], a["nz"], a["ny"],
+                                    a["nx"], a["spacing"], a["K"], a["poses"], a["n_views"],
+                                    a["det_h"], a["det_w"], a["n_samples"], a["mode"], a["f"],
+                                    a["clip"], a["margin"], a["xp"], a["yp"], a["knots"],
+                                    a["out"], a["aux"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def render_bwd_call(**kw):
+    args = dict(volume=DUMMY, dtype=0, B=1, C=1, nz=8, ny=8, nx=8, spacing=SP, K=K, poses=DUMMY,
+                n_views=2, det_h=4, det_w=4, n_samples=8, mode=1, f=1.0, clip=0, margin=30.0,
+                xp=None, yp=None, knots=0, g=DUMMY, out=DUMMY, aux=DUMMY, grad=DUMMY, ws=None,
+                ws_bytes=0, stream=None)
+    args.update(kw)
+    a = args
+    return drr.library().drr_render_backward_volume(
+        a["volume"], a["dtype"], a["B"], a["C"], a["nz"], a["ny"], a["nx"], a["spacing"], a["K"],
+        a["poses"], a["n_views"], a["det_h"], a["det_w"], a["n_samples"], a["mode"], a["f"],
+        a["clip"], a["margin"], a["xp"], a["yp"], a["knots"], a["g"], a["out"], a["aux"],
+        a["grad"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 1), (dict(C=0), 1), (dict(B=3), 1), (dict(mode=3), 1), (dict(clip=2), 1),
+    (dict(f=float("nan")), 1), (dict(margin=float("inf")), 1), (dict(dtype=2), 1),
+    (dict(volume=None), 1), (dict(out=None), 1), (dict(poses=None), 1),
+    (dict(xp=_f(0.0, 1.0), yp=None, knots=2), 1),
+    (dict(xp=_f(0.0, 0.0), yp=_f(0.0, 1.0), knots=2), 1),
+    (dict(xp=_f(0.0), yp=_f(0.0), knots=1), 1),
+    (dict(xp=_f(0.0, float("nan")), yp=_f(0.0, 1.0), knots=2), 1),
+    (dict(C=65, xp=_f(*range(130)), yp=_f(*range(130)), knots=2), 2),
+    (dict(B=300, C=300, n_views=300), 2),
+    (dict(clip=1), 3),                      # the near/far mode always needs its cells
+])
+def test_render_rejects_invalid_arguments(kw, status):
+    assert render_call(**kw) == status
+    assert drr.library().drr_last_error() != b""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mode=0, aux=None), 1),            # Beer-Lambert needs the optical depth
+    (dict(mode=2, out=None), 1),            # compositing needs the forward image
+    (dict(mode=2, volume=None), 1),         # ... and the volume
+    (dict(volume=None, xp=_f(0.0, 1.0), yp=_f(0.0, 2.0), knots=2), 1),
+    (dict(grad=None), 1), (dict(g=None), 1), (dict(B=2, n_views=3), 1),
+    (dict(mode=2, xp=_f(0.0, 1.0), yp=_f(0.0, 2.0), knots=2), 3),   # mapped fp32 copy
+])
+def test_render_backward_rejects_invalid_arguments(kw, status):
+    assert render_bwd_call(**kw) == status
+
+
+def test_render_empty_call_and_workspace_queries():
+    assert render_call(n_views=0) == 0
+    assert render_call(det_h=0, out=None) == 0
+    lib = drr.library()
+    q = lib.drr_render_workspace_bytes
+    # near/far: zero-padded corner cells of every channel-volume, 256-byte multiples
+    cells = ((9 * 9 * 9 * 8 * 4 + 255) // 256) * 256
+    assert q(2, 3, 8, 8, 8, 0, 4, 4, 4, 8, 0, 1, 0, 0) == 6 * cells
+    # a transfer function without cells: the mapped fp32 volumes
+    assert q(1, 2, 8, 8, 8, 1, 1, 4, 4, 8, 0, 0, 3, 0) == 2 * 2048
+    # compositing backward with a transfer function: mapped fp32 volumes; else none
+    assert q(1, 2, 8, 8, 8, 0, 1, 4, 4, 8, 2, 0, 3, 1) == 2 * 2048
+    assert q(1, 2, 8, 8, 8, 0, 1, 4, 4, 8, 0, 0, 3, 1) == 0
+    assert q(2, 1, 8, 8, 8, 0, 3, 4, 4, 8, 0, 0, 0, 0) == 0     # views not a multiple
+    # the single-volume call's plan is drr_forward's
+    for args in [(64, 64, 64, 0, 1, 1024, 1024, 512), (64, 64, 64, 0, 1, 16, 16, 8)]:
+        nz, ny, nx, dt, V, H, Wd, N = args
+        assert q(1, 1, nz, ny, nx, dt, V, H, Wd, N, 0, 0, 0, 0) == \
+            lib.drr_workspace_bytes(nz, ny, nx, dt, V, H, Wd, N, 0)
