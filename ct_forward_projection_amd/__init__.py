@@ -9,7 +9,10 @@ is not on a GPU, the call raises.
 Functions carry the C names (``drr_forward``, ``drr_backward_volume``,
 ``drr_backward_pose``, ``drr_forward_siddon``, ``drr_backward_volume_siddon``,
 ``drr_render``, ``drr_render_backward_volume``, ``drr_workspace_bytes``,
-``drr_render_workspace_bytes``); ``raycast`` wraps the flashdrr front end
+``drr_render_workspace_bytes``, ``drr_intrinsics_from_fov``,
+``drr_poses_from_view_matrices``, ``drr_view_matrices_backward``);
+``render_view_matrices`` renders from flashdrr's VTK view matrices, ras2ijk and
+fov with gradients to the volume and the view matrices; ``raycast`` wraps the flashdrr front end
 (volume and channel batches, density factor, alpha compositing, transfer
 function, near/far clipping) with autograd to the volume; ``render`` wraps the trilinear model as a
 ``torch.autograd.Function`` (flashdrr ``VolumeRaycaster`` style: gradients flow
@@ -72,6 +75,12 @@ def library() -> ctypes.CDLL:
         lib.drr_render_backward_volume.argtypes = [P, I, I, I, I, I, I, P, P, P, I, I, I, I, I, F,
                                                    I, F, P, P, I, P, P, P, P, P, Z, P]
         lib.drr_render_backward_volume.restype = I
+        lib.drr_intrinsics_from_fov.argtypes = [F, I, I, P]
+        lib.drr_intrinsics_from_fov.restype = I
+        lib.drr_poses_from_view_matrices.argtypes = [P, I, P, I, I, I, P, P, P]
+        lib.drr_poses_from_view_matrices.restype = I
+        lib.drr_view_matrices_backward.argtypes = [P, I, P, I, I, I, P, P, P]
+        lib.drr_view_matrices_backward.restype = I
         lib.drr_status_string.argtypes = [I]
         lib.drr_status_string.restype = ctypes.c_char_p
         lib.drr_last_error.restype = ctypes.c_char_p
@@ -530,3 +539,83 @@ def raycast(volume: torch.Tensor, spacing, K, poses: torch.Tensor, det_h: int, d
         poses = poses.expand(volume.shape[0], 3, 4).contiguous()
     return _Raycast.apply(volume, spacing, K, poses, det_h, det_w, n_samples, mode,
                           density_factor, clip, margin, transfer)
+
+
+# ---------------------------------------------------------------- flashdrr cameras
+
+def drr_intrinsics_from_fov(fov_deg: float, det_h: int, det_w: int) -> torch.Tensor:
+    """HZ intrinsics (3, 3) fp32 (host) for a vertical field of view in degrees."""
+    K = (ctypes.c_float * 9)()
+    _check(library().drr_intrinsics_from_fov(float(fov_deg), det_h, det_w, K))
+    return torch.tensor(list(K), dtype=torch.float32).reshape(3, 3)
+
+
+def drr_poses_from_view_matrices(view_mats: torch.Tensor, ras2ijk, shape,
+                                 poses: Optional[torch.Tensor] = None,
+                                 stream=None) -> Tuple[torch.Tensor, Tuple[float, float, float]]:
+    """VTK camera-to-world view matrices (V, 4, 4) and a ras2ijk affine -> HZ
+    world-to-camera poses (V, 3, 4) in the rendering frame of a volume of
+    ``shape`` (nz, ny, nx), and its voxel sizes (sx, sy, sz)."""
+    view_mats = _device_tensor(view_mats, "view_mats", torch.float32)
+    if view_mats.dim() != 3 or tuple(view_mats.shape[1:]) != (4, 4):
+        raise ValueError("view_mats must be (V, 4, 4)")
+    nz, ny, nx = (int(x) for x in shape)
+    V = int(view_mats.shape[0])
+    if poses is None:
+        poses = torch.empty((V, 3, 4), dtype=torch.float32, device=view_mats.device)
+    poses = _device_tensor(poses, "poses", torch.float32)
+    sp = (ctypes.c_float * 3)()
+    _check(library().drr_poses_from_view_matrices(
+        _ptr(view_mats), V, _host_floats(ras2ijk, 16), nz, ny, nx, _ptr(poses), sp,
+        _stream(stream)))
+    return poses, (sp[0], sp[1], sp[2])
+
+
+def drr_view_matrices_backward(view_mats: torch.Tensor, ras2ijk, shape, grad_poses: torch.Tensor,
+                               grad_view_mats: Optional[torch.Tensor] = None,
+                               stream=None) -> torch.Tensor:
+    """dL/d(view_mats) (V, 4, 4) from dL/d(poses) (V, 3, 4)."""
+    view_mats = _device_tensor(view_mats, "view_mats", torch.float32)
+    grad_poses = _device_tensor(grad_poses, "grad_poses", torch.float32)
+    nz, ny, nx = (int(x) for x in shape)
+    V = int(view_mats.shape[0])
+    if grad_poses.numel() != V * 12:
+        raise ValueError("grad_poses must be (V, 3, 4)")
+    if grad_view_mats is None:
+        grad_view_mats = torch.empty((V, 4, 4), dtype=torch.float32, device=view_mats.device)
+    grad_view_mats = _device_tensor(grad_view_mats, "grad_view_mats", torch.float32)
+    _check(library().drr_view_matrices_backward(
+        _ptr(view_mats), V, _host_floats(ras2ijk, 16), nz, ny, nx, _ptr(grad_poses),
+        _ptr(grad_view_mats), _stream(stream)))
+    return grad_view_mats
+
+
+class _ViewPoses(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, view_mats, ras2ijk, shape):
+        poses, spacing = drr_poses_from_view_matrices(view_mats.detach(), ras2ijk, shape)
+        ctx.save_for_backward(view_mats.detach())
+        ctx.args = (ras2ijk, shape)
+        ctx.spacing = spacing
+        return poses
+
+    @staticmethod
+    def backward(ctx, grad_poses):
+        (view_mats,) = ctx.saved_tensors
+        ras2ijk, shape = ctx.args
+        g = drr_view_matrices_backward(view_mats, ras2ijk, shape, grad_poses.contiguous().float())
+        return g, None, None
+
+
+def render_view_matrices(volume: torch.Tensor, view_mats: torch.Tensor, ras2ijk, fov_deg: float,
+                         det_h: int, det_w: int, n_samples: int,
+                         mode: int = BEER_LAMBERT) -> torch.Tensor:
+    """flashdrr-style render of one volume (nz, ny, nx) in IJK voxel space from
+    VTK camera-to-world ``view_mats`` (V, 4, 4), a ``ras2ijk`` affine and a
+    vertical field of view: images (V, det_h, det_w), differentiable with
+    respect to the volume and the view matrices."""
+    shape = tuple(int(x) for x in volume.shape)
+    _, spacing = drr_poses_from_view_matrices(view_mats.detach(), ras2ijk, shape)
+    poses = _ViewPoses.apply(view_mats, ras2ijk, shape)
+    K = drr_intrinsics_from_fov(fov_deg, det_h, det_w)
+    return render(volume, spacing, K, poses, det_h, det_w, n_samples, mode)

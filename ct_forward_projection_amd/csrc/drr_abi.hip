@@ -170,9 +170,100 @@ int check_render(int n_volumes, int n_channels, int n_views, float density_facto
     return DRR_OK;
 }
 
+// The rendering frame of a ras2ijk affine (row-major 4 x 4): voxel sizes from
+// the row norms of its linear part, which must be a scaled orthonormal matrix.
+int frame_from_ras(const float* ras2ijk, int nz, int ny, int nx, drr::VolumeFrame& F, double s[3])
+{
+    if (!ras2ijk) return fail(DRR_ERR_INVALID_ARGUMENT, "ras2ijk is NULL");
+    for (int i = 0; i < 16; ++i)
+        if (!isfinite(ras2ijk[i]))
+            return fail(DRR_ERR_INVALID_ARGUMENT, "ras2ijk[%d] is not finite", i);
+    if (fabs(ras2ijk[12]) > 1e-6 || fabs(ras2ijk[13]) > 1e-6 || fabs(ras2ijk[14]) > 1e-6 ||
+        fabs(ras2ijk[15] - 1.0) > 1e-6)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "ras2ijk's last row must be (0, 0, 0, 1)");
+    const int n[3] = {nx, ny, nz};
+    for (int a = 0; a < 3; ++a) {
+        double norm = 0.0;
+        for (int k = 0; k < 3; ++k) norm += (double)ras2ijk[a * 4 + k] * ras2ijk[a * 4 + k];
+        norm = sqrt(norm);
+        if (!(norm > 0.0)) return fail(DRR_ERR_INVALID_ARGUMENT, "ras2ijk row %d is zero", a);
+        s[a] = 1.0 / norm;
+        for (int k = 0; k < 3; ++k) F.Q[a * 3 + k] = (double)ras2ijk[a * 4 + k] * s[a];
+        F.o[a] = s[a] * ((double)ras2ijk[a * 4 + 3] - 0.5 * (double)(n[a] - 1));
+    }
+    for (int a = 0; a < 3; ++a)
+        for (int b = 0; b < 3; ++b) {
+            double dot = 0.0;
+            for (int k = 0; k < 3; ++k) dot += F.Q[a * 3 + k] * F.Q[b * 3 + k];
+            if (fabs(dot - (a == b ? 1.0 : 0.0)) > 1e-4)
+                return fail(DRR_ERR_INVALID_ARGUMENT,
+                            "ras2ijk's voxel axes must be orthogonal (a scaled rotation)");
+        }
+    return DRR_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int drr_intrinsics_from_fov(float fov_deg, int det_h, int det_w, float* K)
+{
+    if (!K) return fail(DRR_ERR_INVALID_ARGUMENT, "K is NULL");
+    if (!(fov_deg > 0.0f && fov_deg < 180.0f))
+        return fail(DRR_ERR_INVALID_ARGUMENT, "fov_deg must lie in (0, 180)");
+    if (det_h < 1 || det_w < 1)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "det_h and det_w must be >= 1");
+    const double f = 0.5 * (double)det_h / tan(0.5 * (double)fov_deg * 3.14159265358979323846 / 180.0);
+    const float k[9] = {(float)f, 0.0f, 0.5f * (float)det_w, 0.0f, (float)f, 0.5f * (float)det_h,
+                        0.0f, 0.0f, 1.0f};
+    for (int i = 0; i < 9; ++i) K[i] = k[i];
+    return ok();
+}
+
+int drr_poses_from_view_matrices(const float* view_mats, int n_views, const float* ras2ijk,
+                                 int nz, int ny, int nx, float* poses, float* spacing,
+                                 void* stream)
+{
+    if (n_views < 0) return fail(DRR_ERR_INVALID_ARGUMENT, "n_views must be >= 0");
+    if (nz < 1 || ny < 1 || nx < 1)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "volume dims must be >= 1");
+    if (n_views > 0 && (!view_mats || !poses))
+        return fail(DRR_ERR_INVALID_ARGUMENT, "view_mats and poses must be non-NULL");
+    drr::VolumeFrame F;
+    double s[3];
+    int st = frame_from_ras(ras2ijk, nz, ny, nx, F, s);
+    if (st != DRR_OK) return st;
+    if (spacing)
+        for (int a = 0; a < 3; ++a) spacing[a] = (float)s[a];
+    hipError_t e = drr::launch_vtk_poses(view_mats, n_views, F, poses,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DRR_ERR_HIP, "pose conversion launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int drr_view_matrices_backward(const float* view_mats, int n_views, const float* ras2ijk, int nz,
+                               int ny, int nx, const float* grad_poses, float* grad_view_mats,
+                               void* stream)
+{
+    if (n_views < 0) return fail(DRR_ERR_INVALID_ARGUMENT, "n_views must be >= 0");
+    if (nz < 1 || ny < 1 || nx < 1)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "volume dims must be >= 1");
+    if (n_views > 0 && (!view_mats || !grad_poses || !grad_view_mats))
+        return fail(DRR_ERR_INVALID_ARGUMENT,
+                    "view_mats, grad_poses and grad_view_mats must be non-NULL");
+    drr::VolumeFrame F;
+    double s[3];
+    int st = frame_from_ras(ras2ijk, nz, ny, nx, F, s);
+    if (st != DRR_OK) return st;
+    hipError_t e = drr::launch_vtk_poses_backward(view_mats, n_views, F, grad_poses,
+                                                  grad_view_mats,
+                                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DRR_ERR_HIP, "pose conversion backward launch failed: %s",
+                    hipGetErrorString(e));
+    return ok();
+}
 
 int drr_abi_version(void) { return DRR_ABI_VERSION; }
 

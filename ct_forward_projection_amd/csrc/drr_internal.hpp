@@ -134,6 +134,19 @@ hipError_t launch_backward(const LaunchArgs& a, const void* vol, int dtype, cons
 // zero n floats with a kernel (graph-capturable, unlike a memset node)
 hipError_t launch_fill(float* p, size_t n, hipStream_t stream);
 
+// The rendering frame of a ras2ijk affine: p = Q X + o for a RAS point X
+// (Q orthonormal, o in mm), made on the host from ras2ijk and the volume size.
+struct VolumeFrame {
+    double Q[9];
+    double o[3];
+};
+
+hipError_t launch_vtk_poses(const float* view_mats, int n_views, const VolumeFrame& F,
+                            float* poses, hipStream_t stream);
+hipError_t launch_vtk_poses_backward(const float* view_mats, int n_views, const VolumeFrame& F,
+                                     const float* grad_poses, float* grad_view,
+                                     hipStream_t stream);
+
 // Cell-constant (Siddon) pair: no workspace.
 hipError_t launch_siddon_forward(const LaunchArgs& a, const void* vol, int dtype, float* out,
                                  float* s_out, hipStream_t stream);

@@ -278,6 +278,48 @@ int drr_render_backward_volume(const void *volume, int dtype, int n_volumes, int
                                const float *aux, float *grad_volume, void *workspace,
                                size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Camera conventions of the flashdrr front end (flashdrr.rendering API:
+ * get_vtk_view_mat builds a camera-to-world 4 x 4 whose 3 x 3 block holds the
+ * camera axes [right, up, forward] as columns and whose fourth column is the
+ * camera position, in RAS; VolumeRaycaster.forward takes the volume in IJK
+ * voxel space with a ras2ijk affine; set_fov takes the vertical field of view).
+ *
+ * Readings: ras2ijk maps RAS to the continuous voxel index with voxel centres
+ * at integers, i along x (the fastest axis), j along y, k along z; its linear
+ * part must be a scaled orthonormal matrix (orthogonal voxel axes), whose row
+ * norms are the inverse voxel sizes.  The rendering frame of every other call
+ * (box centred at the origin) is then a rigid image of RAS.  The HZ camera's
+ * image x axis is `right`, its image y axis is -`up` (rows grow downwards),
+ * z is `forward`; the view matrix's 3 x 3 block is taken as orthonormal. */
+
+/* K = [[f, 0, W/2], [0, f, H/2], [0, 0, 1]], f = (H/2) / tan(fov/2), for a
+ * vertical field of view fov_deg in (0, 180) degrees.  Host only: K receives
+ * 9 floats, row-major. */
+int drr_intrinsics_from_fov(float fov_deg, int det_h, int det_w, float *K);
+
+/* World-to-camera HZ poses for the rendering frame of a volume of nz x ny x nx
+ * voxels placed by ras2ijk:
+ *   view_mats  device, n_views x 16 floats, row-major camera-to-world 4 x 4
+ *   ras2ijk    host, 16 floats, row-major 4 x 4 (last row 0 0 0 1)
+ *   poses      device, n_views x 12 floats, OVERWRITTEN ([R | t] for drr_render,
+ *              drr_forward, ...)
+ *   spacing    host or NULL: receives the 3 voxel sizes (sx, sy, sz) in mm
+ * With M the rotation block and c the position of a view matrix, Q X + o the
+ * rendering frame of a RAS point X and D = diag(1, -1, 1):
+ *   R = D M^T Q^T,  t = -R (Q c + o). */
+int drr_poses_from_view_matrices(const float *view_mats, int n_views, const float *ras2ijk,
+                                 int nz, int ny, int nx, float *poses, float *spacing,
+                                 void *stream);
+
+/* Chain rule of drr_poses_from_view_matrices: from grad_poses = dL/d[R | t]
+ * (device, n_views x 12, e.g. from drr_backward_pose) it writes
+ * grad_view_mats = dL/d(view_mats) (device, n_views x 16, OVERWRITTEN; the
+ * bottom row is 0), every entry of the view matrix treated as independent. */
+int drr_view_matrices_backward(const float *view_mats, int n_views, const float *ras2ijk, int nz,
+                               int ny, int nx, const float *grad_poses, float *grad_view_mats,
+                               void *stream);
+
 /* Static description of a drr_status value. */
 const char *drr_status_string(int status);
 

@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import ct_forward_projection_amd as drr
@@ -254,3 +255,37 @@ def test_render_empty_call_and_workspace_queries():
         nz, ny, nx, dt, V, H, Wd, N = args
         assert q(1, 1, nz, ny, nx, dt, V, H, Wd, N, 0, 0, 0, 0) == \
             lib.drr_workspace_bytes(nz, ny, nx, dt, V, H, Wd, N, 0)
+
+
+# ----------------------------------------------------------------- cameras
+
+def test_intrinsics_from_fov_on_the_host():
+    from oracle import camera
+    for fov, H, Wd in [(20.0, 1024, 1024), (35.5, 200, 320)]:
+        K = drr.drr_intrinsics_from_fov(fov, H, Wd).double().numpy()
+        assert np.allclose(K, camera.intrinsics_from_fov(fov, H, Wd), rtol=1e-6)
+    for bad in [(0.0, 10, 10), (180.0, 10, 10), (20.0, 0, 10), (float("nan"), 10, 10)]:
+        with pytest.raises(drr.DRRError):
+            drr.drr_intrinsics_from_fov(*bad)
+
+
+RAS = _f(1.0, 0.0, 0.0, 3.0, 0.0, 0.0, 2.0, 1.0, 0.0, -0.5, 0.0, 2.0, 0.0, 0.0, 0.0, 1.0)
+
+
+@pytest.mark.parametrize("ras,status", [
+    (RAS, 0),
+    (_f(1.0, 0.5, 0.0, 0.0, 0.0, 1.0, 0.0, 0.0, 0.0, 0.0, 1.0, 0.0, 0.0, 0.0, 0.0, 1.0), 1),
+    (_f(1.0, 0.0, 0.0, 0.0, 0.0, 1.0, 0.0, 0.0, 0.0, 0.0, 1.0, 0.0, 0.0, 0.0, 1.0, 1.0), 1),
+    (_f(0.0, 0.0, 0.0, 0.0, 0.0, 1.0, 0.0, 0.0, 0.0, 0.0, 1.0, 0.0, 0.0, 0.0, 0.0, 1.0), 1),
+    (None, 1),
+])
+def test_view_matrix_conversion_validates_ras2ijk(ras, status):
+    """A scaled rotation is accepted (empty call), skewed or projective affines
+    are refused; the voxel sizes come out of the row norms."""
+    lib = drr.library()
+    sp = (ctypes.c_float * 3)()
+    assert lib.drr_poses_from_view_matrices(None, 0, ras, 4, 5, 6, None, sp, None) == status
+    if status == 0:
+        assert list(sp) == pytest.approx([1.0, 0.5, 2.0])
+    assert lib.drr_view_matrices_backward(None, 0, ras, 4, 5, 6, None, None, None) == status
+    assert lib.drr_poses_from_view_matrices(None, 1, RAS, 4, 5, 6, None, None, None) == 1
