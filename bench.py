@@ -15,6 +15,9 @@ Printed (one JSON line on stdout):
                that hit the volume, plus per-ray reads/writes), with its
                duration measured by HIP events on the launch stream
   cpu_baseline the CPU oracle on the same step, timed on the host cores
+  front_end    flashdrr front-end variants (transfer function from HU, near/far
+               clipping, alpha compositing, volume and channel batches),
+               forward and volume backward, graph-timed like the workloads
   workloads    every workload (200x200 16-view batch in fp32 and bf16, the
                1024^2 step's kernels, 2048^2 eval, 360-view helix, 64^3 tiny)
                as context lines, with the pose gradient (registration) on the
@@ -326,6 +329,111 @@ def workload_lines(dev, reps):
     return lines
 
 
+class RenderCase:
+    """A drr_render configuration resident on the device, with preallocated
+    outputs, workspaces and upstream gradient (so a captured graph allocates
+    nothing)."""
+
+    def __init__(self, vol, spacing, K, poses, H, Wd, N, mode, f=1.0, clip=0, margin=30.0,
+                 transfer=None):
+        import torch
+
+        import ct_forward_projection_amd as drr
+        self.args = (spacing, K, poses, H, Wd, N, mode, f, clip, margin, transfer)
+        self.vol = vol
+        B, C, nz, ny, nx = vol.shape
+        V = poses.shape[0]
+        dt = drr.BF16 if vol.dtype == torch.bfloat16 else drr.F32
+        nk = 0 if transfer is None else len(transfer[0][0])
+        dev = vol.device
+        self.out = torch.empty((V, C, H, Wd), device=dev)
+        self.aux = torch.empty_like(self.out)
+        rng = np.random.default_rng(2100 + V)
+        self.g = torch.from_numpy(rng.uniform(-1.0, 1.0, size=tuple(self.out.shape)).astype(
+            np.float32)).to(dev)
+        self.grad = torch.empty(vol.shape, device=dev)
+        wf = drr.drr_render_workspace_bytes(B, C, nz, ny, nx, dt, V, H, Wd, N, mode, clip, nk, 0)
+        wb = drr.drr_render_workspace_bytes(B, C, nz, ny, nx, dt, V, H, Wd, N, mode, clip, nk, 1)
+        self.ws_f = torch.empty(wf, dtype=torch.uint8, device=dev) if wf else None
+        self.ws_b = torch.empty(wb, dtype=torch.uint8, device=dev) if wb else None
+        self.samples = V * C * H * Wd * N
+        self.cells = wf > 0 and wf != B * C * ((nx * ny * nz * 4 + 255) // 256 * 256)
+        self.read_elem = 4 if (transfer is not None or dt == drr.F32) else 2
+
+    def forward(self):
+        import ct_forward_projection_amd as drr
+        sp, K, P, H, Wd, N, mode, f, clip, margin, tf = self.args
+        drr.drr_render(self.vol, sp, K, P, H, Wd, N, mode, f, clip, margin, tf, out=self.out,
+                       aux=self.aux, workspace=self.ws_f)
+
+    def backward(self):
+        import ct_forward_projection_amd as drr
+        sp, K, P, H, Wd, N, mode, f, clip, margin, tf = self.args
+        drr.drr_render_backward_volume(self.vol, tuple(self.vol.shape), 0, sp, K, P, H, Wd, N,
+                                       mode, self.g, self.out, self.aux, f, clip, margin, tf,
+                                       grad_volume=self.grad, workspace=self.ws_b)
+
+
+def frontend_lines(dev):
+    """The flashdrr front end (drr_render) at full size: the 16-view 200^2 batch
+    rendered from the HU phantom through the transfer function (box clip with
+    Beer-Lambert; near/far with a 30 mm margin and alpha compositing; fp32 and
+    bf16 HU), four volumes of two channels, and the 1024^2 camera composited.
+    Nominal samples count every ray's N samples (the near/far range marches
+    its N samples whether or not they fall inside the volume); the HBM
+    fraction prices 8 corner elements per nominal sample of the forward."""
+    import torch
+
+    import ct_forward_projection_amd as drr
+    import workloads as W
+    hu32 = W.hu_phantom().astype(np.float32)
+    bits = W.round_to_bf16_bits(hu32)
+    tf = (np.array([[-1000.0, 0.0, 1500.0]], dtype=np.float32),
+          np.array([[0.0, 0.02, 0.05]], dtype=np.float32))
+    w2, w3 = W.make_workload(2), W.make_workload(3)
+    P2 = torch.from_numpy(w2.poses).to(dev)
+    P3 = torch.from_numpy(w3.poses).to(dev)
+    hu = torch.from_numpy(hu32).to(dev)[None, None]
+    hub = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)[None, None]
+    mu = torch.from_numpy(w2.volume).to(dev)
+    # four volumes of two channels: the mu phantom and a flipped copy, channel 2
+    # a scaled copy; each volume seen by 4 of the 16 batch views
+    mu4 = torch.stack([torch.stack([mu.flip(a % 3), 0.5 * mu.flip(a % 3)]) for a in range(4)])
+    D = drr
+    cases = [
+        ("batch16x200-hu-transfer-box-BL", hu, P2, w2, D.BEER_LAMBERT, 0, tf),
+        ("batch16x200-hu-transfer-nearfar30-alpha", hu, P2, w2, D.ALPHA_COMPOSITE, 1, tf),
+        ("batch16x200-hu-bf16-transfer-nearfar30-alpha", hub, P2, w2, D.ALPHA_COMPOSITE, 1, tf),
+        ("batch16x200-4vol-2ch-BL", mu4.contiguous(), P2, w2, D.BEER_LAMBERT, 0, None),
+        ("train1024-alpha", mu[None, None], P3, w3, D.ALPHA_COMPOSITE, 0, None),
+    ]
+    lines = {}
+    for name, vol, P, w, mode, clip, transfer in cases:
+        c = RenderCase(vol, w.spacing, w.K, P, w.det_h, w.det_w, w.n_samples, mode, 1.0, clip,
+                       30.0, transfer)
+        c.forward()
+        c.backward()
+        torch.cuda.synchronize()
+        f_ms, b_ms = time_graph([c.forward, c.backward])
+        views = P.shape[0] * vol.shape[1]
+        fwd_bytes = c.samples * 8 * c.read_elem + c.out.numel() * 8
+        line = {"views_x_channels": views, "detector": [w.det_h, w.det_w],
+                "n_samples": w.n_samples, "volumes": vol.shape[0], "channels": vol.shape[1],
+                "dtype": "bf16" if vol.dtype == torch.bfloat16 else "f32",
+                "mode": {0: "beer-lambert", 1: "line-integral", 2: "alpha"}[mode],
+                "clip": "near-far-30mm" if clip else "box",
+                "transfer": transfer is not None, "cells": bool(c.cells),
+                "forward_ms": round(f_ms, 4), "forward_fps": round(views / f_ms * 1e3, 1),
+                "forward_gsamples_s": round(c.samples / f_ms / 1e6, 1),
+                "forward_hbm_frac": round(fwd_bytes / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "backward_ms": round(b_ms, 4),
+                "backward_gsamples_s": round(c.samples / b_ms / 1e6, 1)}
+        lines[name] = line
+        log(f"front end {name}: {line}")
+        del c
+    return lines
+
+
 def pmc_pass(kind: str, dev):
     """A short fixed launch sequence for rocprofv3 counter runs: 3 launches of
     the chosen pass (forward, volume backward or pose backward) on the
@@ -574,6 +682,7 @@ def main():
     }
     if not args.no_workloads:
         out["workloads"] = workload_lines(dev, reps=10)
+        out["front_end"] = frontend_lines(dev)
     if not args.no_cpu:
         log("cpu baseline: oracle on the same step ...")
         out["cpu_baseline"] = cpu_baseline(w)
