@@ -22,9 +22,8 @@
 //                       when a mapped volume is marched without cells.
 //   drr_slope_kernel    the backward's last step with a transfer function:
 //                       dL/dx = dL/dmu tf'(x) per voxel.
-//   drr_alpha_scatter_kernel  backward of alpha compositing: gathers each
-//                       sample again and scatters its own weight with global
-//                       atomics.
+//                       The compositing backward runs in the same kernel: each
+//                       sample is gathered again for its own coefficient.
 //
 // Every kernel covers several volumes and channels per launch (flashdrr API,
 // VolumeRaycaster.forward: (B, C, D, H, W) volumes, N = B * views_per_vol views,
@@ -396,6 +395,49 @@ __device__ inline bool same_cell(const Cell& a, const Cell& b)
            a.z1 == b.z1;
 }
 
+// Per-sample coefficient of the compositing backward (MODE = kAlpha).  For
+// I = sum_k T_k alpha_k v_k with alpha_k = 1 - exp(-f v_k dz) and
+// T_k = exp(-f dz sum_{j<k} v_j), sample k's own weight is
+//   dI/dv_k = T_k (alpha_k + f dz (1 - alpha_k) v_k) - f dz sum_{j>k} T_j alpha_j v_j
+// (its emission and opacity, and the transmittance it takes from every later
+// sample); the later-sample sum is the forward's I minus the running emission
+// up to k.  Each call gathers the sample's eight corners again from the linear
+// volume (the caller's, or the fp32 mapped copy; clamped or zero-padded as the
+// cell and mask say) and advances the running state, so samples are visited in
+// order; tau and the running emission are fp64.
+template <typename T, bool ZP>
+struct AlphaCoef {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t sy, sz;               // element strides of the volume
+    float fdz, g;
+    double I, tau, run;
+
+    __device__ float next(const Cell& C, const float* m)
+    {
+        float w[8];
+        corner_weights<ZP>(C, 1.0f, w, m);
+        const uint32_t r00 = (uint32_t)C.z0 * sz + (uint32_t)C.y0 * sy;
+        const uint32_t r01 = (uint32_t)C.z0 * sz + (uint32_t)C.y1 * sy;
+        const uint32_t r10 = (uint32_t)C.z1 * sz + (uint32_t)C.y0 * sy;
+        const uint32_t r11 = (uint32_t)C.z1 * sz + (uint32_t)C.y1 * sy;
+        const uint32_t idx[8] = {r00 + C.x0, r00 + C.x1, r01 + C.x0, r01 + C.x1,
+                                 r10 + C.x0, r10 + C.x1, r11 + C.x0, r11 + C.x1};
+        float val[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) val[c] = load_one<T>(rs, idx[c] * (uint32_t)sizeof(T));
+        float v = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v = fmaf(w[c], val[c], v);
+        const float a = fdz * v;
+        const float Tk = expf(-(float)tau);
+        const float alpha = -expm1f(-a);
+        run += (double)(Tk * alpha * v);
+        const float later = (float)(I - run);
+        tau += (double)a;
+        return g * (Tk * (alpha + fdz * (1.0f - alpha) * v) - fdz * later);
+    }
+};
+
 // Backward scatter with LDS pre-reduction in fixed point.
 //
 // The rays of a tile walk their samples in chunks.  For each chunk the tile's
@@ -410,28 +452,34 @@ __device__ inline bool same_cell(const Cell& a, const Cell& b)
 // atomic add is an order of magnitude slower than its integer add, and integer
 // sums are exact, so the window total does not depend on the order of the
 // adds.  The scale 2^e is chosen per tile so that no window entry overflows:
-// one sample puts at most |y dz| on any voxel and a ray has at most
-// c = min(N, floor(2 / |dq|_inf) + 1) samples inside a voxel's 2 x 2 x 2
+// one sample puts at most |c| on any voxel (c its coefficient: y dz for a
+// whole ray in the Beer-Lambert and line-integral backward, c_k per sample in
+// the compositing one, bounded by a first pass over the ray) and a ray has at
+// most n = min(N, floor(2 / |dq|_inf) + 1) samples inside a voxel's 2 x 2 x 2
 // support, so an entry never exceeds B = sum over the tile's rays of
-// |y dz| c, and 2^e B <= 2^30.  (|y dz| c is about |y| times the ray's
+// max|c| n, and 2^e B <= 2^30.  (|y dz| n is about |y| times the ray's
 // length inside that support, so B stays small even for short chords.)  Each
-// rounding adds at most 1/2 and an entry receives at most Cs = sum of c
-// roundings, which must stay below 2^31 as well.  A tile whose weights are not
-// finite or whose Cs is too large, or a chunk whose box does not fit the window
-// even for one sample, uses global float atomics directly.
+// rounding adds at most 1/2 and an entry receives at most Cs = sum of n
+// roundings, which must stay below 2^31 as well.  A tile whose coefficients
+// are not finite or whose Cs is too large, or a chunk whose box does not fit
+// the window even for one sample, uses global float atomics directly.
 //
 // The tiles of a launch run over (view, channel) pairs; a pair's rays scatter
 // into the gradient of its channel-volume, with y scaled by the density factor
 // (y = g f exp(-tau) or g f).  CLIP = kClipNearFar samples the view's
 // near/far range and drops corners outside the volume (zero padding); all
-// rays of a workgroup belong to one view, so they share the range.
-template <int MODE, int CLIP>
+// rays of a workgroup belong to one view, so they share the range.  MODE =
+// kAlpha reads the volume (`vol`, one channel-volume of `vol_bytes` every
+// bt.src_stride bytes) and the forward image `out_in`.
+template <int MODE, int CLIP, typename T>
 __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
     VolumeDesc V, Intrinsics K, const float* __restrict__ poses, int H, int W, int N,
     int tiles_x, int tiles_per_view, Batch bt, const float* __restrict__ grad_out,
-    const float* __restrict__ s_in, float* __restrict__ grad)
+    const float* __restrict__ s_in, const float* __restrict__ out_in,
+    const T* __restrict__ vol, uint32_t vol_bytes, float* __restrict__ grad)
 {
     constexpr bool ZP = CLIP == kClipNearFar;
+    constexpr bool ALPHA = MODE == kAlpha;
     __shared__ int win[kWinCap];
     __shared__ int red[(kBlock / 64) * 6];
     __shared__ int box[6];
@@ -440,10 +488,14 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
     const PixelCoord px = scatter_pixel(tile, tiles_x, tiles_per_view);
     // px.view counts (view, channel) pairs; a tile lies in one pair
     const int view = px.view / bt.C, ch = px.view - view * bt.C;
-    grad += (size_t)((view / bt.vpv) * bt.C + ch) * bt.grad_stride;
+    const int cvol = (view / bt.vpv) * bt.C + ch;
+    grad += (size_t)cvol * bt.grad_stride;
+    // element strides of the gradient volume
+    const uint32_t sy = (uint32_t)V.n[0], sz = (uint32_t)V.n[0] * (uint32_t)V.n[1];
     bool active = px.r < H && px.c < W;
     MarchRay R;
     float yd = 0.0f;
+    AlphaCoef<T, ZP> coef;
     if (active) {
         ViewGeom G;
         view_setup(poses + 12 * view, K, G);
@@ -456,23 +508,57 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
         }
         if (active) {
             const size_t o = ((size_t)px.view * H + px.r) * W + px.c;
-            float y = grad_out[o] * bt.f;
-            if (MODE == kBeerLambert) y *= expf(-s_in[o]);
-            yd = y * R.dz;
-            active = yd != 0.0f;
+            if constexpr (ALPHA) {
+                const char* base = reinterpret_cast<const char*>(vol) + (uint64_t)cvol * bt.src_stride;
+                coef.rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)vol_bytes,
+                                                            kBufferWord3);
+                coef.sy = sy;
+                coef.sz = sz;
+                coef.fdz = bt.f * R.dz;
+                coef.g = grad_out[o];
+                coef.I = (double)out_in[o];
+                active = coef.g != 0.0f;
+            } else {
+                float y = grad_out[o] * bt.f;
+                if (MODE == kBeerLambert) y *= expf(-s_in[o]);
+                yd = y * R.dz;
+                active = yd != 0.0f;
+            }
         }
     }
-    // element strides of the gradient volume
-    const uint32_t sy = (uint32_t)V.n[0], sz = (uint32_t)V.n[0] * (uint32_t)V.n[1];
 
     // fixed-point scale of this tile
     float B = 0.0f, Cs = 0.0f;
     if (active) {
         const double dq_inf = fmax(fmax(fabs((double)R.dq[0]), fabs((double)R.dq[1])),
                                    fabs((double)R.dq[2])) * 2.3283064365386963e-10;
-        const double c = fmin((double)N, floor(2.0 / dq_inf) + 1.0);
-        B = (float)(fabs((double)yd) * c);
-        Cs = (float)c;
+        const double n = fmin((double)N, floor(2.0 / dq_inf) + 1.0);
+        float cmax = fabsf(yd);
+        if constexpr (ALPHA) {
+            // first pass: the largest coefficient of the ray (NaN if any is not finite)
+            coef.tau = coef.run = 0.0;
+            int64_t qx = R.q0[0], qy = R.q0[1], qz = R.q0[2];
+            bool finite = true;
+            for (int k = 0; k < N; ++k) {
+                Cell C;
+                float m[6];
+                cell_of(V, qx, qy, qz, C);
+                if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
+                qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
+                const float ck = coef.next(C, m);
+                finite = finite && isfinite(ck);
+                cmax = fmaxf(cmax, fabsf(ck));
+            }
+            if (!finite) cmax = __builtin_nanf("");
+            coef.tau = coef.run = 0.0;
+            // a ray whose coefficients are all 0 (through air: emission times
+            // opacity is quadratic in mu) adds nothing
+            active = cmax != 0.0f;
+        }
+        if (active) {
+            B = (float)((double)cmax * n);
+            Cs = (float)n;
+        }
     }
     block_sum2(B, Cs, reinterpret_cast<float*>(red));
     if (Cs == 0.0f) return;                        // no ray of this tile contributes
@@ -490,7 +576,7 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
     while (k0 < N) {
         S = min(S, N - k0);
         int ext[3], lo[3];
-        long long vol;
+        long long vol_cells;
         for (;;) {
             int v[6] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX, INT_MAX, INT_MAX};
             if (active) {
@@ -504,18 +590,18 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 }
             }
             block_min6(v, red, box);
-            vol = 1;
+            vol_cells = 1;
 #pragma unroll
             for (int a = 0; a < 3; ++a) {
                 lo[a] = box[a];
                 ext[a] = max(-box[3 + a] - box[a] + 1, 1);
-                vol *= ext[a];
+                vol_cells *= ext[a];
             }
-            if (!fixed_ok || vol <= kWinCap || S == 1) break;
+            if (!fixed_ok || vol_cells <= kWinCap || S == 1) break;
             S = max(1, S >> 1);
         }
-        if (fixed_ok && vol <= kWinCap) {
-            const int n_win = (int)vol;
+        if (fixed_ok && vol_cells <= kWinCap) {
+            const int n_win = (int)vol_cells;
             for (int i = threadIdx.x; i < n_win; i += kBlock) win[i] = 0;
             __syncthreads();
             if (active) {
@@ -527,7 +613,8 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 float acc[8], m[6];
                 cell_of(V, qx, qy, qz, P);
                 if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
-                corner_weights<ZP>(P, ys, acc, m);
+                if constexpr (ALPHA) corner_weights<ZP>(P, coef.next(P, m) * scale, acc, m);
+                else corner_weights<ZP>(P, ys, acc, m);
                 qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
                 for (int k = k0 + 1; k < k0 + S; ++k) {
                     Cell C;
@@ -535,7 +622,8 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                     if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
                     qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
                     float w[8];
-                    corner_weights<ZP>(C, ys, w, m);
+                    if constexpr (ALPHA) corner_weights<ZP>(C, coef.next(C, m) * scale, w, m);
+                    else corner_weights<ZP>(C, ys, w, m);
                     if (same_cell(C, P)) {
 #pragma unroll
                         for (int i = 0; i < 8; ++i) acc[i] += w[i];
@@ -572,88 +660,13 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 cell_of(V, qx, qy, qz, C);
                 if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
                 qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
-                scatter_sample_global<ZP>(grad, sy, sz, C, yd, m);
+                const float c = ALPHA ? coef.next(C, m) : yd;
+                scatter_sample_global<ZP>(grad, sy, sz, C, c, m);
             }
         }
         k0 += S;
         // a chunk that left room in the window: try a longer one next
-        if (vol * 2 <= kWinCap) S *= 2;
-    }
-}
-
-// Backward of alpha compositing.  For I = sum_k T_k alpha_k v_k with
-// alpha_k = 1 - exp(-f v_k dz) and T_k = exp(-f dz sum_{j<k} v_j), sample k's
-// own weight is
-//   dI/dv_k = T_k (alpha_k + f dz (1 - alpha_k) v_k) - f dz sum_{j>k} T_j alpha_j v_j
-// (its emission and opacity, and the transmittance it takes from every later
-// sample); the later-sample sum is the forward's I minus the running sum up to
-// k (fp64).  Each sample gathers its eight corners from the linear volume (of
-// the caller, or the fp32 mapped copy), clamped or zero-padded, and scatters
-// g dI/dv_k w_corner with global float atomics.  One lane per ray.
-template <typename T, int CLIP>
-__global__ __launch_bounds__(kBlock) void drr_alpha_scatter_kernel(
-    const T* __restrict__ vol, uint32_t vol_bytes, VolumeDesc V, Intrinsics K,
-    const float* __restrict__ poses, int H, int W, int N, int tiles_x, int tiles_per_view,
-    Batch bt, const float* __restrict__ grad_out, const float* __restrict__ out_in,
-    float* __restrict__ grad)
-{
-    constexpr bool ZP = CLIP == kClipNearFar;
-    const int tile = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
-    const PixelCoord px = scatter_pixel(tile, tiles_x, tiles_per_view);
-    if (px.r >= H || px.c >= W) return;
-    const int view = px.view / bt.C, ch = px.view - view * bt.C;
-    const int cvol = (view / bt.vpv) * bt.C + ch;
-    ViewGeom G;
-    view_setup(poses + 12 * view, K, G);
-    MarchRay R;
-    bool hit;
-    if constexpr (CLIP == kClipBox) {
-        hit = ray_setup(G, V, px.r, px.c, N, R);
-    } else {
-        double t_near, t_far;
-        view_near_far(G, V, bt.margin, t_near, t_far);
-        hit = ray_setup_range(G, V, px.r, px.c, N, t_near, t_far, R);
-    }
-    if (!hit) return;
-    const size_t o = ((size_t)px.view * H + px.r) * W + px.c;
-    const float g = grad_out[o];
-    if (g == 0.0f) return;
-    const double I_total = (double)out_in[o];
-    grad += (size_t)cvol * bt.grad_stride;
-    const char* base = reinterpret_cast<const char*>(vol) + (uint64_t)cvol * bt.src_stride;
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)vol_bytes, kBufferWord3);
-    const uint32_t sy = (uint32_t)V.n[0], sz = (uint32_t)V.n[0] * (uint32_t)V.n[1];
-    const float fdz = bt.f * R.dz;
-    int64_t qx = R.q0[0], qy = R.q0[1], qz = R.q0[2];
-    double tau = 0.0, run = 0.0;
-    for (int k = 0; k < N; ++k) {
-        Cell C;
-        float m[6];
-        cell_of(V, qx, qy, qz, C);
-        if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
-        qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
-        float w[8];
-        corner_weights<ZP>(C, 1.0f, w, m);
-        const uint32_t r00 = (uint32_t)C.z0 * sz + (uint32_t)C.y0 * sy;
-        const uint32_t r01 = (uint32_t)C.z0 * sz + (uint32_t)C.y1 * sy;
-        const uint32_t r10 = (uint32_t)C.z1 * sz + (uint32_t)C.y0 * sy;
-        const uint32_t r11 = (uint32_t)C.z1 * sz + (uint32_t)C.y1 * sy;
-        const uint32_t idx[8] = {r00 + C.x0, r00 + C.x1, r01 + C.x0, r01 + C.x1,
-                                 r10 + C.x0, r10 + C.x1, r11 + C.x0, r11 + C.x1};
-        float v = 0.0f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) v = fmaf(w[c], load_one<T>(rs, idx[c] * (uint32_t)sizeof(T)), v);
-        const float a = fdz * v;
-        const float Tk = expf(-(float)tau);
-        const float alpha = -expm1f(-a);
-        const float e = Tk * alpha * v;
-        run += (double)e;
-        const float later = (float)(I_total - run);
-        const float coef = g * (Tk * (alpha + fdz * (1.0f - alpha) * v) - fdz * later);
-        tau += (double)a;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) unsafeAtomicAdd(grad + idx[c], coef * w[c]);
+        if (vol_cells * 2 <= kWinCap) S *= 2;
     }
 }
 
@@ -869,20 +882,20 @@ hipError_t launch_fill(float* p, size_t n, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <typename T>
-static void launch_alpha_scatter(const LaunchArgs& a, const T* vol, uint32_t vol_bytes,
-                                 const Batch& b, const float* grad_out, const float* out_in,
-                                 float* grad, int tiles_x, int tiles_per_view, int n_tiles,
-                                 hipStream_t stream)
+template <int MODE, typename T>
+static void launch_scatter(const LaunchArgs& a, const Batch& b, const float* grad_out,
+                           const float* s_in, const float* out_in, const T* vol,
+                           uint32_t vol_bytes, float* grad, int tiles_x, int tiles_per_view,
+                           int n_tiles, hipStream_t stream)
 {
     if (a.clip == kClipNearFar)
-        hipLaunchKernelGGL((drr_alpha_scatter_kernel<T, kClipNearFar>), dim3(n_tiles), dim3(kBlock),
-                           0, stream, vol, vol_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
-                           tiles_per_view, b, grad_out, out_in, grad);
+        hipLaunchKernelGGL((drr_scatter_kernel<MODE, kClipNearFar, T>), dim3(n_tiles),
+                           dim3(kBlock), 0, stream, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                           tiles_per_view, b, grad_out, s_in, out_in, vol, vol_bytes, grad);
     else
-        hipLaunchKernelGGL((drr_alpha_scatter_kernel<T, kClipBox>), dim3(n_tiles), dim3(kBlock), 0,
-                           stream, vol, vol_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
-                           tiles_per_view, b, grad_out, out_in, grad);
+        hipLaunchKernelGGL((drr_scatter_kernel<MODE, kClipBox, T>), dim3(n_tiles), dim3(kBlock),
+                           0, stream, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view,
+                           b, grad_out, s_in, out_in, vol, vol_bytes, grad);
 }
 
 template <typename Tin>
@@ -896,7 +909,6 @@ static hipError_t backward_typed(const LaunchArgs& a, const Tin* vol, const floa
     int tiles_x, tiles_per_view, n_tiles;
     tile_grid(a.n_views * a.C, a.H, a.W, kTile, tiles_x, tiles_per_view, n_tiles);
     if (n_tiles == 0) return hipSuccess;
-    const dim3 grid(n_tiles), block(kBlock);
     if (a.mode == kAlpha) {
         if (a.has_tf) {
             // gather the mapped volumes: their fp32 copy in the workspace
@@ -906,27 +918,24 @@ static hipError_t backward_typed(const LaunchArgs& a, const Tin* vol, const floa
             float* mu = static_cast<float*>(workspace);
             e = launch_transfer_typed<Tin>(a, p, vol, mu, stream);
             if (e != hipSuccess) return e;
-            Batch b = make_batch(a, &p, 0);
-            launch_alpha_scatter<float>(a, mu, (uint32_t)(n_vox * 4), b, grad_out, out_in, grad,
-                                        tiles_x, tiles_per_view, n_tiles, stream);
+            const Batch b = make_batch(a, &p, 0);
+            launch_scatter<kAlpha, float>(a, b, grad_out, s_in, out_in, mu,
+                                          (uint32_t)(n_vox * 4), grad, tiles_x, tiles_per_view,
+                                          n_tiles, stream);
         } else {
             const Batch b = make_batch(a, nullptr, n_vox * sizeof(Tin));
-            launch_alpha_scatter<Tin>(a, vol, (uint32_t)(n_vox * sizeof(Tin)), b, grad_out, out_in,
-                                      grad, tiles_x, tiles_per_view, n_tiles, stream);
+            launch_scatter<kAlpha, Tin>(a, b, grad_out, s_in, out_in, vol,
+                                        (uint32_t)(n_vox * sizeof(Tin)), grad, tiles_x,
+                                        tiles_per_view, n_tiles, stream);
         }
     } else {
         const Batch b = make_batch(a, nullptr, 0);
-#define DRR_SCATTER(MODE, CLIP)                                                                 \
-    hipLaunchKernelGGL((drr_scatter_kernel<MODE, CLIP>), grid, block, 0, stream, a.V, a.K,      \
-                       a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view, b, grad_out, s_in, grad)
-        if (a.mode == kBeerLambert) {
-            if (a.clip == kClipNearFar) DRR_SCATTER(kBeerLambert, kClipNearFar);
-            else DRR_SCATTER(kBeerLambert, kClipBox);
-        } else {
-            if (a.clip == kClipNearFar) DRR_SCATTER(kLineIntegral, kClipNearFar);
-            else DRR_SCATTER(kLineIntegral, kClipBox);
-        }
-#undef DRR_SCATTER
+        if (a.mode == kBeerLambert)
+            launch_scatter<kBeerLambert, float>(a, b, grad_out, s_in, out_in, nullptr, 0, grad,
+                                                tiles_x, tiles_per_view, n_tiles, stream);
+        else
+            launch_scatter<kLineIntegral, float>(a, b, grad_out, s_in, out_in, nullptr, 0, grad,
+                                                 tiles_x, tiles_per_view, n_tiles, stream);
     }
     e = hipGetLastError();
     if (e != hipSuccess || !a.has_tf) return e;
