@@ -288,8 +288,8 @@ size_t drr_workspace_bytes(int nz, int ny, int nx, int dtype, int n_views, int d
         n_samples < 1 || (dtype != DRR_F32 && dtype != DRR_BF16))
         return 0;
     if (for_backward == DRR_WORKSPACE_VOLUME_BACKWARD) return 0;
-    const size_t cells = drr::plan_forward(nz, ny, nx, dtype == DRR_F32 ? 4 : 2,
-                                           (long long)n_views * det_h * det_w, n_samples)
+    const size_t cells = drr::plan_render(1, 1, nz, ny, nx, dtype == DRR_F32 ? 4 : 2, n_views,
+                                          det_h, det_w, n_samples, drr::kClipBox, false)
                              .workspace_bytes;
     if (for_backward == DRR_WORKSPACE_POSE_BACKWARD) return drr::pose_acc_bytes(n_views) + cells;
     return for_backward == DRR_WORKSPACE_FORWARD ? cells : 0;
@@ -469,7 +469,8 @@ int drr_backward_pose(const void* volume, int dtype, int nz, int ny, int nx, con
     const long long n_rays = (long long)n_views * det_h * det_w;
     if (n_rays > 0 && !grad_out) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_out is NULL");
     if (n_views > 0 && !grad_poses) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_poses is NULL");
-    const drr::ForwardPlan plan = drr::plan_forward(nz, ny, nx, eb, n_rays, n_samples);
+    const drr::RenderPlan plan = drr::plan_render(1, 1, nz, ny, nx, eb, n_views, det_h, det_w,
+                                                  n_samples, drr::kClipBox, false);
     const size_t acc_bytes = drr::pose_acc_bytes(n_views);
     const size_t need = acc_bytes + plan.workspace_bytes;
     if (n_views == 0) return ok();

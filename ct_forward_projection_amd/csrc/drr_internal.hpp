@@ -48,25 +48,7 @@ struct LaunchArgs {
 // samples per cell for fp32 (a 256^3 volume at 1024^2 x 512 samples: 1.48 ms
 // -> 0.89 ms including the relayout; a 16 x 200^2 x 256 batch, ~10 samples per
 // cell, got slower) and about 4 for bf16.  It must also fit 32-bit offsets.
-struct ForwardPlan {
-    bool cells;
-    size_t workspace_bytes;
-};
-
-inline ForwardPlan plan_forward(int nz, int ny, int nx, int elem_bytes, long long n_rays, int N)
-{
-    ForwardPlan p{false, 0};
-    const double n_cells = (double)(nx + 1) * (double)(ny + 1) * (double)(nz + 1);
-    const double cell_bytes = n_cells * 8.0 * elem_bytes;
-    const double samples_per_cell = (double)n_rays * (double)N / n_cells;
-    const double min_reuse = elem_bytes == 4 ? 16.0 : 4.0;
-    if (n_rays > 0 && samples_per_cell >= min_reuse && cell_bytes < 4294967040.0) {
-        p.cells = true;
-        p.workspace_bytes = ((size_t)cell_bytes + 255) & ~(size_t)255;
-    }
-    return p;
-}
-
+//
 // How a render call reads its volumes: the march reads either the caller's
 // volumes, a corner-cell copy (the reuse rule above; always in the near/far
 // mode, whose cells carry the zero padding), or -- with a transfer function
