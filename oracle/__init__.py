@@ -81,6 +81,8 @@ def _load():
     lib.oracle_render_adjoint.restype = I
     lib.oracle_view_range.argtypes = [P, P, D, P]
     lib.oracle_view_range.restype = None
+    lib.oracle_poisson_surrogate.argtypes = [P, P, ctypes.c_long, D, P, P, P]
+    lib.oracle_poisson_surrogate.restype = None
     lib.oracle_max_threads.restype = I
     _lib = lib
     return lib
@@ -360,3 +362,19 @@ def view_range(extent, pose, margin: float):
     _load().oracle_view_range(_ptr(np.ascontiguousarray(extent, dtype=np.float64)),
                               _ptr(_f64(pose).reshape(12)), float(margin), _ptr(out))
     return float(out[0]), float(out[1])
+
+
+def poisson_surrogate(transmission, noise, i0: float, grad_out=None):
+    """flashdrr apply_poisson with the standard-normal draws given: returns the
+    noisy, clamped transmission (float64), and with ``grad_out`` also the
+    gradient with respect to the transmission."""
+    lib = _load()
+    T = _f64(transmission)
+    z = _f64(noise)
+    out = np.zeros(T.shape, dtype=np.float64)
+    g = None if grad_out is None else _f64(grad_out)
+    grad = None if grad_out is None else np.zeros(T.shape, dtype=np.float64)
+    lib.oracle_poisson_surrogate(_ptr(T), _ptr(z), T.size, float(i0), _ptr(out),
+                                 None if g is None else _ptr(g),
+                                 None if grad is None else _ptr(grad))
+    return out if grad is None else (out, grad)

@@ -1276,6 +1276,33 @@ void oracle_view_range(const double *extent, const double *pose, double margin, 
     near_far(C, extent, margin, &out[0], &out[1]);
 }
 
+/* ------------------------------------------------- Gaussian-Poisson surrogate */
+
+/* flashdrr.rendering API, VolumeRaycaster.apply_poisson: Gaussian noise of
+ * standard deviation sqrt(T / i0) added to a transmission map T, clamped to
+ * [0, 1]; a smooth, differentiable surrogate for photon (Poisson) noise.  The
+ * standard-normal draws z are an input.  Readings: a transmission below 0 has
+ * no noise (its standard deviation is taken as 0); the derivative follows
+ * torch.clamp (passed through where min <= value <= max, else 0) and, where
+ * T <= 0, omits the noise term, whose derivative z / (2 sqrt(T i0)) has no
+ * finite value there. */
+void oracle_poisson_surrogate(const double *T, const double *z, long n, double i0, double *out,
+                              const double *g, double *grad)
+{
+    for (long i = 0; i < n; ++i) {
+        double t = T[i];
+        double sd = t > 0.0 ? sqrt(t / i0) : 0.0;
+        double v = t + z[i] * sd;
+        double o = v < 0.0 ? 0.0 : (v > 1.0 ? 1.0 : v);
+        out[i] = o;
+        if (grad) {
+            double pass = (v >= 0.0 && v <= 1.0) ? 1.0 : 0.0;
+            double dv = 1.0 + (t > 0.0 ? z[i] / (2.0 * sqrt(t * i0)) : 0.0);
+            grad[i] = g[i] * pass * dv;
+        }
+    }
+}
+
 /* Build information for the Python loader. */
 int oracle_abi_version(void) { return 1; }
 
