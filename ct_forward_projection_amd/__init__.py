@@ -81,6 +81,11 @@ def library() -> ctypes.CDLL:
         lib.drr_poses_from_view_matrices.restype = I
         lib.drr_view_matrices_backward.argtypes = [P, I, P, I, I, I, P, P, P]
         lib.drr_view_matrices_backward.restype = I
+        L = ctypes.c_longlong
+        lib.drr_poisson_surrogate.argtypes = [P, P, L, F, P, P]
+        lib.drr_poisson_surrogate.restype = I
+        lib.drr_poisson_surrogate_backward.argtypes = [P, P, L, F, P, P, P]
+        lib.drr_poisson_surrogate_backward.restype = I
         lib.drr_status_string.argtypes = [I]
         lib.drr_status_string.restype = ctypes.c_char_p
         lib.drr_last_error.restype = ctypes.c_char_p
@@ -619,3 +624,61 @@ def render_view_matrices(volume: torch.Tensor, view_mats: torch.Tensor, ras2ijk,
     poses = _ViewPoses.apply(view_mats, ras2ijk, shape)
     K = drr_intrinsics_from_fov(fov_deg, det_h, det_w)
     return render(volume, spacing, K, poses, det_h, det_w, n_samples, mode)
+
+
+# ---------------------------------------------------------------- noise surrogate
+
+def drr_poisson_surrogate(transmission: torch.Tensor, noise: torch.Tensor, i0: float,
+                          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """flashdrr apply_poisson with the standard-normal draws ``noise`` given:
+    clamp(T + noise * sqrt(T / i0), 0, 1), same shape as ``transmission``."""
+    T = _device_tensor(transmission, "transmission", torch.float32)
+    z = _device_tensor(noise, "noise", torch.float32)
+    if z.numel() != T.numel():
+        raise ValueError("noise must have as many elements as transmission")
+    if out is None:
+        out = torch.empty_like(T)
+    out = _device_tensor(out, "out", torch.float32)
+    _check(library().drr_poisson_surrogate(_ptr(T), _ptr(z), T.numel(), float(i0), _ptr(out),
+                                           _stream(stream)))
+    return out
+
+
+def drr_poisson_surrogate_backward(transmission: torch.Tensor, noise: torch.Tensor, i0: float,
+                                   grad_out: torch.Tensor,
+                                   grad_transmission: Optional[torch.Tensor] = None,
+                                   stream=None) -> torch.Tensor:
+    T = _device_tensor(transmission, "transmission", torch.float32)
+    z = _device_tensor(noise, "noise", torch.float32)
+    g = _device_tensor(grad_out, "grad_out", torch.float32)
+    if grad_transmission is None:
+        grad_transmission = torch.empty_like(T)
+    grad_transmission = _device_tensor(grad_transmission, "grad_transmission", torch.float32)
+    _check(library().drr_poisson_surrogate_backward(_ptr(T), _ptr(z), T.numel(), float(i0),
+                                                    _ptr(g), _ptr(grad_transmission),
+                                                    _stream(stream)))
+    return grad_transmission
+
+
+class _Poisson(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, transmission, noise, i0):
+        ctx.save_for_backward(transmission.detach(), noise.detach())
+        ctx.i0 = i0
+        return drr_poisson_surrogate(transmission.detach().contiguous(),
+                                     noise.detach().contiguous(), i0)
+
+    @staticmethod
+    def backward(ctx, grad):
+        T, z = ctx.saved_tensors
+        g = drr_poisson_surrogate_backward(T.contiguous(), z.contiguous(), ctx.i0,
+                                           grad.contiguous().float())
+        return g, None, None
+
+
+def poisson_noise(transmission: torch.Tensor, noise: torch.Tensor, i0: Optional[float]):
+    """Differentiable Gaussian-Poisson surrogate; ``i0 = None`` returns the
+    transmission unchanged (flashdrr's default: no noise model)."""
+    if i0 is None:
+        return transmission
+    return _Poisson.apply(transmission, noise, float(i0))

@@ -206,6 +206,39 @@ int frame_from_ras(const float* ras2ijk, int nz, int ny, int nx, drr::VolumeFram
 
 extern "C" {
 
+int drr_poisson_surrogate(const float* transmission, const float* noise, long long n, float i0,
+                          float* out, void* stream)
+{
+    if (n < 0) return fail(DRR_ERR_INVALID_ARGUMENT, "n must be >= 0");
+    if (!(i0 > 0.0f) || !isfinite(i0))
+        return fail(DRR_ERR_INVALID_ARGUMENT, "i0 must be finite and > 0");
+    if (n > 0 && (!transmission || !noise || !out))
+        return fail(DRR_ERR_INVALID_ARGUMENT, "transmission, noise and out must be non-NULL");
+    hipError_t e = drr::launch_poisson(transmission, noise, (size_t)n, i0, out,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DRR_ERR_HIP, "noise launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int drr_poisson_surrogate_backward(const float* transmission, const float* noise, long long n,
+                                   float i0, const float* grad_out, float* grad_transmission,
+                                   void* stream)
+{
+    if (n < 0) return fail(DRR_ERR_INVALID_ARGUMENT, "n must be >= 0");
+    if (!(i0 > 0.0f) || !isfinite(i0))
+        return fail(DRR_ERR_INVALID_ARGUMENT, "i0 must be finite and > 0");
+    if (n > 0 && (!transmission || !noise || !grad_out || !grad_transmission))
+        return fail(DRR_ERR_INVALID_ARGUMENT,
+                    "transmission, noise, grad_out and grad_transmission must be non-NULL");
+    hipError_t e = drr::launch_poisson_backward(transmission, noise, (size_t)n, i0, grad_out,
+                                                grad_transmission,
+                                                static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DRR_ERR_HIP, "noise backward launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 int drr_intrinsics_from_fov(float fov_deg, int det_h, int det_w, float* K)
 {
     if (!K) return fail(DRR_ERR_INVALID_ARGUMENT, "K is NULL");

@@ -129,6 +129,12 @@ hipError_t launch_vtk_poses_backward(const float* view_mats, int n_views, const 
                                      const float* grad_poses, float* grad_view,
                                      hipStream_t stream);
 
+// Gaussian-Poisson surrogate on a transmission map (elementwise).
+hipError_t launch_poisson(const float* T, const float* z, size_t n, float i0, float* out,
+                          hipStream_t stream);
+hipError_t launch_poisson_backward(const float* T, const float* z, size_t n, float i0,
+                                   const float* g, float* grad, hipStream_t stream);
+
 // Cell-constant (Siddon) pair: no workspace.
 hipError_t launch_siddon_forward(const LaunchArgs& a, const void* vol, int dtype, float* out,
                                  float* s_out, hipStream_t stream);

@@ -320,6 +320,26 @@ int drr_view_matrices_backward(const float *view_mats, int n_views, const float 
                                int ny, int nx, const float *grad_poses, float *grad_view_mats,
                                void *stream);
 
+/* Gaussian-Poisson noise surrogate (flashdrr.rendering API,
+ * VolumeRaycaster.apply_poisson): Gaussian noise of standard deviation
+ * sqrt(T / i0) added to a transmission map T, clamped to [0, 1]:
+ *   out = clamp(T + z sqrt(max(T, 0) / i0), 0, 1)
+ * with the standard-normal draws z supplied by the caller (so a run is
+ * reproducible and the same draws serve the backward).
+ *   transmission, noise, out  device, n floats each
+ *   i0            mean photon count at the source, finite and > 0
+ * Readings: a transmission below 0 gets no noise. */
+int drr_poisson_surrogate(const float *transmission, const float *noise, long long n, float i0,
+                          float *out, void *stream);
+
+/* Gradient of the surrogate: grad_transmission = grad_out * d out / dT, with
+ * dT passed through where T + z sqrt(T / i0) lies in [0, 1] (as torch.clamp
+ * does) and 0 elsewhere; d/dT of the noise term is z / (2 sqrt(T i0)) for
+ * T > 0 and is left out for T <= 0.  All device, n floats each. */
+int drr_poisson_surrogate_backward(const float *transmission, const float *noise, long long n,
+                                   float i0, const float *grad_out, float *grad_transmission,
+                                   void *stream);
+
 /* Static description of a drr_status value. */
 const char *drr_status_string(int status);
 

@@ -289,3 +289,14 @@ def test_view_matrix_conversion_validates_ras2ijk(ras, status):
         assert list(sp) == pytest.approx([1.0, 0.5, 2.0])
     assert lib.drr_view_matrices_backward(None, 0, ras, 4, 5, 6, None, None, None) == status
     assert lib.drr_poses_from_view_matrices(None, 1, RAS, 4, 5, 6, None, None, None) == 1
+
+
+def test_poisson_surrogate_validates_on_the_host():
+    lib = drr.library()
+    assert lib.drr_poisson_surrogate(None, None, 0, 100.0, None, None) == 0
+    assert lib.drr_poisson_surrogate(None, None, -1, 100.0, None, None) == 1
+    assert lib.drr_poisson_surrogate(DUMMY, DUMMY, 4, 0.0, DUMMY, None) == 1
+    assert lib.drr_poisson_surrogate(DUMMY, DUMMY, 4, float("inf"), DUMMY, None) == 1
+    assert lib.drr_poisson_surrogate(DUMMY, None, 4, 10.0, DUMMY, None) == 1
+    assert lib.drr_poisson_surrogate_backward(DUMMY, DUMMY, 4, 10.0, None, DUMMY, None) == 1
+    assert lib.drr_poisson_surrogate_backward(None, None, 0, 10.0, None, None, None) == 0
