@@ -359,3 +359,33 @@ def test_invalid_arguments_are_rejected():
                       transfer=(np.array([[0.0, 0.0], [0.0, 1.0]]), np.ones((2, 2))))
     with pytest.raises(ValueError):     # unknown mode
         oracle.render(vol, spacing, K, poses, H, Wd, N, 7)
+
+
+@pytest.mark.parametrize("mode", [BL, RAW])
+@pytest.mark.parametrize("tf", [False, True])
+def test_render_pose_gradient_matches_central_differences(mode, tf):
+    """The batched pose gradient (per view, summed over its channels, density
+    factor and transfer function included) equals central differences of
+    oracle.render with respect to each pose entry (fp64 poses pass through)."""
+    rng, vol, spacing, K, poses, H, Wd, N = _problem(70 + mode + 2 * tf)
+    xp = np.array([[0.0, 0.4, 1.1], [0.1, 0.5, 0.9]], dtype=np.float32)
+    yp = np.array([[0.0, 0.5, 0.6], [0.2, 0.0, 0.7]], dtype=np.float32)
+    transfer = (xp, yp) if tf else None
+    f = 0.8
+    g = rng.normal(size=(poses.shape[0], vol.shape[1], H, Wd))
+    gp = oracle.render_pose_gradient(vol, spacing, K, poses, H, Wd, N, mode, g,
+                                     density_factor=f, transfer=transfer)
+    P = np.asarray(poses, dtype=np.float32).astype(np.float64)
+    h = 1e-6
+    for v in (0, 3):
+        for e in range(12):
+            Pp, Pm = P.copy(), P.copy()
+            Pp[v].reshape(-1)[e] += h
+            Pm[v].reshape(-1)[e] -= h
+            lp = float((oracle.render(vol, spacing, K, Pp, H, Wd, N, mode, density_factor=f,
+                                      transfer=transfer)[0] * g).sum())
+            lm = float((oracle.render(vol, spacing, K, Pm, H, Wd, N, mode, density_factor=f,
+                                      transfer=transfer)[0] * g).sum())
+            fd = (lp - lm) / (2 * h)
+            assert fd == pytest.approx(gp[v].reshape(-1)[e], rel=1e-4,
+                                       abs=1e-5 * np.abs(gp[v]).max())
