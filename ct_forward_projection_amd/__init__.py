@@ -75,6 +75,9 @@ def library() -> ctypes.CDLL:
         lib.drr_render_backward_volume.argtypes = [P, I, I, I, I, I, I, P, P, P, I, I, I, I, I, F,
                                                    I, F, P, P, I, P, P, P, P, P, Z, P]
         lib.drr_render_backward_volume.restype = I
+        lib.drr_render_backward_pose.argtypes = [P, I, I, I, I, I, I, P, P, P, I, I, I, I, I, F, I,
+                                                 F, P, P, I, P, P, P, Z, P]
+        lib.drr_render_backward_pose.restype = I
         lib.drr_intrinsics_from_fov.argtypes = [F, I, I, P]
         lib.drr_intrinsics_from_fov.restype = I
         lib.drr_poses_from_view_matrices.argtypes = [P, I, P, I, I, I, P, P, P]
@@ -509,6 +512,39 @@ def drr_render_backward_volume(volume: Optional[torch.Tensor], shape, dtype: int
     return grad_volume
 
 
+def drr_render_backward_pose(volume: torch.Tensor, spacing, K, poses: torch.Tensor, det_h: int,
+                             det_w: int, n_samples: int, mode: int, grad_out: torch.Tensor,
+                             density_factor: float = 1.0, clip: int = CLIP_BOX,
+                             margin: float = 30.0, transfer=None,
+                             grad_poses: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
+    """dL/dP (V, 3, 4) for L = sum(grad_out * image) of ``drr_render``
+    (Beer-Lambert or line integral, box clip), summed over each view's channels."""
+    volume = _device_tensor(volume, "volume")
+    dtype = _volume_dtype(volume)
+    poses = _device_tensor(poses, "poses", torch.float32)
+    grad_out = _device_tensor(grad_out, "grad_out", torch.float32)
+    B, C, (nz, ny, nx) = _batched_volume(volume)
+    V = int(poses.shape[0])
+    if grad_out.numel() != V * C * det_h * det_w:
+        raise ValueError("grad_out has the wrong size")
+    xp, yp, nk = _transfer(transfer, C)
+    if grad_poses is None:
+        grad_poses = torch.empty((V, 3, 4), dtype=torch.float32, device=volume.device)
+    grad_poses = _device_tensor(grad_poses, "grad_poses", torch.float32)
+    need = drr_render_workspace_bytes(B, C, nz, ny, nx, dtype, V, det_h, det_w, n_samples, mode,
+                                      clip, nk, 2)
+    if workspace is None:
+        workspace = _workspace(need, volume.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(library().drr_render_backward_pose(
+        _ptr(volume), dtype, B, C, nz, ny, nx, _host_floats(spacing, 3), _host_floats(K, 9),
+        _ptr(poses), V, det_h, det_w, n_samples, mode, float(density_factor), clip, float(margin),
+        xp, yp, nk, _ptr(grad_out), _ptr(grad_poses), _ptr(workspace), ws_bytes, _stream(stream)))
+    return grad_poses
+
+
 class _Raycast(torch.autograd.Function):
     @staticmethod
     def forward(ctx, volume, spacing, K, poses, det_h, det_w, n_samples, mode, density_factor,
@@ -524,13 +560,17 @@ class _Raycast(torch.autograd.Function):
     def backward(ctx, grad_img):
         volume, poses, img, tau = ctx.saved_tensors
         spacing, K, det_h, det_w, n_samples, mode, f, clip, margin, transfer = ctx.args
-        g_vol = None
+        g_vol = g_pose = None
+        g_img = grad_img.contiguous().float()
         if ctx.needs_input_grad[0]:
             g_vol = drr_render_backward_volume(
                 volume, tuple(volume.shape), _volume_dtype(volume), spacing, K, poses, det_h,
-                det_w, n_samples, mode, grad_img.contiguous().float(), img, tau, f, clip, margin,
+                det_w, n_samples, mode, g_img, img, tau, f, clip, margin,
                 transfer).to(volume.dtype)
-        return (g_vol,) + (None,) * 11
+        if ctx.needs_input_grad[3]:
+            g_pose = drr_render_backward_pose(volume, spacing, K, poses, det_h, det_w, n_samples,
+                                              mode, g_img, f, clip, margin, transfer)
+        return (g_vol, None, None, g_pose) + (None,) * 8
 
 
 def raycast(volume: torch.Tensor, spacing, K, poses: torch.Tensor, det_h: int, det_w: int,
@@ -538,8 +578,8 @@ def raycast(volume: torch.Tensor, spacing, K, poses: torch.Tensor, det_h: int, d
             clip: int = CLIP_BOX, margin: float = 30.0, transfer=None) -> torch.Tensor:
     """Differentiable flashdrr-style render: ``volume`` (B, C, nz, ny, nx) and
     ``poses`` (V, 3, 4) with V a multiple of B -- or one pose, used for every
-    volume -- give images (V, C, det_h, det_w); the gradient flows to the
-    volume (the poses are constants here)."""
+    volume -- give images (V, C, det_h, det_w); gradients flow to the volume
+    and (Beer-Lambert or line integral with the box clip) to the poses."""
     if volume.dim() == 5 and poses.shape[0] == 1 and volume.shape[0] > 1:
         poses = poses.expand(volume.shape[0], 3, 4).contiguous()
     return _Raycast.apply(volume, spacing, K, poses, det_h, det_w, n_samples, mode,

@@ -400,10 +400,12 @@ size_t drr_render_workspace_bytes(int n_volumes, int n_channels, int nz, int ny,
     const bool has_tf = tf_knots > 0;
     if (for_backward == DRR_WORKSPACE_VOLUME_BACKWARD)
         return drr::render_backward_workspace(n_volumes, n_channels, nz, ny, nx, mode, has_tf);
-    if (for_backward != DRR_WORKSPACE_FORWARD) return 0;
-    return drr::plan_render(n_volumes, n_channels, nz, ny, nx, dtype == DRR_F32 ? 4 : 2, n_views,
-                            det_h, det_w, n_samples, clip, has_tf)
-        .workspace_bytes;
+    const size_t plan = drr::plan_render(n_volumes, n_channels, nz, ny, nx,
+                                         dtype == DRR_F32 ? 4 : 2, n_views, det_h, det_w,
+                                         n_samples, clip, has_tf)
+                            .workspace_bytes;
+    if (for_backward == DRR_WORKSPACE_POSE_BACKWARD) return drr::pose_acc_bytes(n_views) + plan;
+    return for_backward == DRR_WORKSPACE_FORWARD ? plan : 0;
 }
 
 int drr_render(const void* volume, int dtype, int n_volumes, int n_channels, int nz, int ny,
@@ -486,6 +488,50 @@ int drr_render_backward_volume(const void* volume, int dtype, int n_volumes, int
     return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// The pose backward of a validated render call `a` (single-volume calls come
+// here too): Beer-Lambert or line integral, box clip.
+int pose_backward(drr::LaunchArgs& a, const void* volume, int dtype, const float* grad_out,
+                  float* grad_poses, void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (a.mode == DRR_ALPHA_COMPOSITE || a.clip != DRR_CLIP_BOX)
+        return fail(DRR_ERR_UNSUPPORTED,
+                    "pose gradients cover Beer-Lambert and line integral with the box clip");
+    if (!volume) return fail(DRR_ERR_INVALID_ARGUMENT, "volume is NULL");
+    const long long n_out = (long long)a.n_views * a.C * a.H * a.W;
+    if (n_out > 0 && !grad_out) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_out is NULL");
+    if (a.n_views > 0 && !grad_poses) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_poses is NULL");
+    const int eb = dtype == DRR_F32 ? 4 : 2;
+    const drr::RenderPlan plan =
+        drr::plan_render(a.n_volumes, a.C, a.V.n[2], a.V.n[1], a.V.n[0], eb, a.n_views, a.H, a.W,
+                         a.N, drr::kClipBox, a.has_tf);
+    if (!plan.fits)
+        return fail(DRR_ERR_UNSUPPORTED, "one channel-volume of the march's copy exceeds 4 GiB");
+    const size_t acc_bytes = drr::pose_acc_bytes(a.n_views);
+    const size_t need = acc_bytes + plan.workspace_bytes;
+    if (a.n_views == 0) return ok();
+    if (workspace_bytes < need)
+        return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
+                    workspace_bytes, need);
+    if (!workspace || ((uintptr_t)workspace & 255u))
+        return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+    if (plan.cells) set_cells(a.V, a.V.n[2], a.V.n[1], a.V.n[0], plan.read_elem);
+    char* ws = static_cast<char*>(workspace);
+    hipError_t e = drr::launch_backward_pose(a, plan, volume, dtype, ws + acc_bytes,
+                                             reinterpret_cast<double*>(ws), grad_out, grad_poses,
+                                             static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DRR_ERR_HIP, "pose backward launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 int drr_backward_pose(const void* volume, int dtype, int nz, int ny, int nx, const float* spacing,
                       const float* K, const float* poses, int n_views, int det_h, int det_w,
                       int n_samples, int mode, const float* grad_out, float* grad_poses,
@@ -494,32 +540,32 @@ int drr_backward_pose(const void* volume, int dtype, int nz, int ny, int nx, con
     if (dtype != DRR_F32 && dtype != DRR_BF16)
         return fail(DRR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
     drr::LaunchArgs a;
-    const int eb = dtype == DRR_F32 ? 4 : 2;
-    int st = check_geometry(nz, ny, nx, eb, spacing, K, poses, n_views, det_h, det_w, n_samples,
-                            mode, a);
+    int st = check_geometry(nz, ny, nx, dtype == DRR_F32 ? 4 : 2, spacing, K, poses, n_views,
+                            det_h, det_w, n_samples, mode, a);
     if (st != DRR_OK) return st;
-    if (!volume) return fail(DRR_ERR_INVALID_ARGUMENT, "volume is NULL");
-    const long long n_rays = (long long)n_views * det_h * det_w;
-    if (n_rays > 0 && !grad_out) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_out is NULL");
-    if (n_views > 0 && !grad_poses) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_poses is NULL");
-    const drr::RenderPlan plan = drr::plan_render(1, 1, nz, ny, nx, eb, n_views, det_h, det_w,
-                                                  n_samples, drr::kClipBox, false);
-    const size_t acc_bytes = drr::pose_acc_bytes(n_views);
-    const size_t need = acc_bytes + plan.workspace_bytes;
-    if (n_views == 0) return ok();
-    if (workspace_bytes < need)
-        return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
-                    workspace_bytes, need);
-    if (!workspace || ((uintptr_t)workspace & 255u))
-        return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
-    if (plan.cells) set_cells(a.V, nz, ny, nx, eb);
-    char* ws = static_cast<char*>(workspace);
-    hipError_t e = drr::launch_backward_pose(a, volume, dtype, plan.cells, ws + acc_bytes,
-                                             reinterpret_cast<double*>(ws), grad_out, grad_poses,
-                                             static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return fail(DRR_ERR_HIP, "pose backward launch failed: %s", hipGetErrorString(e));
-    return ok();
+    return pose_backward(a, volume, dtype, grad_out, grad_poses, workspace, workspace_bytes,
+                         stream);
+}
+
+int drr_render_backward_pose(const void* volume, int dtype, int n_volumes, int n_channels,
+                             int nz, int ny, int nx, const float* spacing, const float* K,
+                             const float* poses, int n_views, int det_h, int det_w,
+                             int n_samples, int mode, float density_factor, int clip,
+                             float margin, const float* tf_xp, const float* tf_yp, int tf_knots,
+                             const float* grad_out, float* grad_poses, void* workspace,
+                             size_t workspace_bytes, void* stream)
+{
+    if (dtype != DRR_F32 && dtype != DRR_BF16)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    drr::LaunchArgs a;
+    int st = check_geometry(nz, ny, nx, dtype == DRR_F32 ? 4 : 2, spacing, K, poses, n_views,
+                            det_h, det_w, n_samples, mode, a, DRR_ALPHA_COMPOSITE);
+    if (st != DRR_OK) return st;
+    st = check_render(n_volumes, n_channels, n_views, density_factor, clip, margin, tf_xp, tf_yp,
+                      tf_knots, a);
+    if (st != DRR_OK) return st;
+    return pose_backward(a, volume, dtype, grad_out, grad_poses, workspace, workspace_bytes,
+                         stream);
 }
 
 int drr_forward_siddon(const void* volume, int dtype, int nz, int ny, int nx,

@@ -107,6 +107,11 @@ inline size_t render_backward_workspace(int n_volumes, int C, int nz, int ny, in
 
 hipError_t launch_forward(const LaunchArgs& a, const RenderPlan& plan, const void* vol, int dtype,
                           void* workspace, float* out, float* s_out, hipStream_t stream);
+// What the plan's march reads, made in `workspace`: the corner cells (zero-padded
+// and/or mapped as the call asks) or the mapped fp32 volumes; nothing when the
+// march reads the caller's volumes.
+hipError_t launch_read_copy(const LaunchArgs& a, const RenderPlan& plan, const void* vol,
+                            int dtype, void* workspace, hipStream_t stream);
 // The volume backward of a render call.  `vol` is read for alpha compositing
 // and for the transfer function's slope; `out_in` (the forward's image) for
 // alpha compositing; `s_in` (optical depth) for Beer-Lambert.
@@ -141,12 +146,13 @@ hipError_t launch_siddon_forward(const LaunchArgs& a, const void* vol, int dtype
 hipError_t launch_siddon_backward(const LaunchArgs& a, const float* grad_out, const float* s_in,
                                   float* grad, hipStream_t stream);
 
-// Pose gradient: the march of the forward (same volume plan) with gradient
-// accumulators; `acc` holds 12 doubles per view.
+// Pose gradient: the march of the forward (same read plan: the caller's, mapped
+// or corner-cell volumes in `read_buf`) with gradient accumulators; `acc` holds
+// 12 doubles per view.  Beer-Lambert and line integral with the box clip.
 inline size_t pose_acc_bytes(int n_views) { return ((size_t)n_views * 12 * 8 + 255) & ~(size_t)255; }
 
-hipError_t launch_backward_pose(const LaunchArgs& a, const void* vol, int dtype, bool cells,
-                                void* cell_buf, double* acc, const float* grad_out,
+hipError_t launch_backward_pose(const LaunchArgs& a, const RenderPlan& plan, const void* vol,
+                                int dtype, void* read_buf, double* acc, const float* grad_out,
                                 float* grad_poses, hipStream_t stream);
 
 }  // namespace drr

@@ -793,23 +793,6 @@ static hipError_t launch_cells_typed(const LaunchArgs& a, const RenderPlan& p, c
     return hipGetLastError();
 }
 
-// The plain corner-cell copy of one volume (the pose gradient's march).
-hipError_t launch_cells(const VolumeDesc& V, const void* vol, int dtype, void* cells,
-                        hipStream_t stream)
-{
-    LaunchArgs a{};
-    a.V = V;
-    a.n_volumes = a.C = 1;
-    a.clip = kClipBox;
-    RenderPlan p{};
-    p.cells = true;
-    p.read_elem = dtype == 0 ? 4 : 2;
-    p.per_volume_bytes = (size_t)V.cell_total_bytes;
-    if (dtype == 0)
-        return launch_cells_typed<float>(a, p, static_cast<const float*>(vol), cells, stream);
-    return launch_cells_typed<uint16_t>(a, p, static_cast<const uint16_t*>(vol), cells, stream);
-}
-
 template <typename Tin>
 static hipError_t launch_transfer_typed(const LaunchArgs& a, const RenderPlan& p, const Tin* vol,
                                         float* mu, hipStream_t stream)
@@ -819,6 +802,26 @@ static hipError_t launch_transfer_typed(const LaunchArgs& a, const RenderPlan& p
     hipLaunchKernelGGL((drr_transfer_kernel<Tin>), grid, dim3(256), 0, stream, vol, n_vox, n_vox,
                        mu, p.per_volume_bytes / sizeof(float), a.C, a.tf);
     return hipGetLastError();
+}
+
+hipError_t launch_read_copy(const LaunchArgs& a, const RenderPlan& p, const void* vol, int dtype,
+                            void* workspace, hipStream_t stream)
+{
+    if (p.cells) {
+        if (dtype == 0)
+            return launch_cells_typed<float>(a, p, static_cast<const float*>(vol), workspace,
+                                             stream);
+        return launch_cells_typed<uint16_t>(a, p, static_cast<const uint16_t*>(vol), workspace,
+                                            stream);
+    }
+    if (p.mapped) {
+        float* mu = static_cast<float*>(workspace);
+        if (dtype == 0)
+            return launch_transfer_typed<float>(a, p, static_cast<const float*>(vol), mu, stream);
+        return launch_transfer_typed<uint16_t>(a, p, static_cast<const uint16_t*>(vol), mu,
+                                               stream);
+    }
+    return hipSuccess;
 }
 
 template <typename Tin>

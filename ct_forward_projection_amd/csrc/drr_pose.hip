@@ -121,15 +121,21 @@ __device__ inline double block_sum12(const double v_in[12], double* red)
     return t;
 }
 
+// The tiles of a launch run over (view, channel) pairs (a tile lies in one
+// pair); every channel of a view adds to that view's sums, and the density
+// factor enters dI/ds (f exp(-f s) or f).  `src` holds one channel-volume of
+// `src_bytes` every b.src_stride bytes.
 template <typename T, Layout L, int MODE>
 __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
     const T* __restrict__ src, uint32_t src_bytes, VolumeDesc V, Intrinsics K,
     const float* __restrict__ poses, int H, int W, int N, int tiles_x, int tiles_per_view,
-    const float* __restrict__ grad_out, double* __restrict__ acc)
+    Batch b, const float* __restrict__ grad_out, double* __restrict__ acc)
 {
     __shared__ double red[(kBlock / 64) * 12];
     const int tile = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
     const PixelCoord px = tile_pixel(tile, tiles_x, tiles_per_view);
+    const int view = px.view / b.C, ch = px.view - view * b.C;
+    const int cvol = (view / b.vpv) * b.C + ch;
     double contrib[12];
 #pragma unroll
     for (int i = 0; i < 12; ++i) contrib[i] = 0.0;
@@ -140,14 +146,15 @@ __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
     bool hit = false;
     if (g != 0.0f) {
         ViewGeom G;
-        view_setup(poses + 12 * px.view, K, G);
+        view_setup(poses + 12 * view, K, G);
         double Ki[9];
         intrinsics_inverse(K, Ki);
         hit = ray_frame(G, Ki, V, px.r, px.c, N, F);
     }
     if (hit) {
+        const char* base = reinterpret_cast<const char*>(src) + (uint64_t)cvol * b.src_stride;
         const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, (int)src_bytes, kBufferWord3);
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)src_bytes, kBufferWord3);
         // fp64 accumulators: sum grad mu . d telescopes to about mu(exit) - mu(entry),
         // a small difference of large edge terms that fp32 sums would round away
         double s0 = 0.0, g0[3] = {0.0, 0.0, 0.0}, h1[3] = {0.0, 0.0, 0.0};
@@ -197,8 +204,8 @@ __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
             G0[a] = g0[a] * V.inv_s[a];                               // per mm
             G1[a] = (h1[a] + 0.5 * g0[a]) / Nd * V.inv_s[a];
         }
-        const double s = dz * S0;
-        const double y = (double)g * (MODE == kBeerLambert ? exp(-s) : 1.0);
+        const double s = dz * S0, f = (double)b.f;
+        const double y = (double)g * f * (MODE == kBeerLambert ? exp(-f * s) : 1.0);
         double G0d = 0.0, G1d = 0.0;
 #pragma unroll
         for (int a = 0; a < 3; ++a) {
@@ -231,7 +238,7 @@ __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
             for (int j = 0; j < 3; ++j) contrib[3 + i * 3 + j] = y * F.u[i] * Bw[j];
     }
     const double t = block_sum12(contrib, red);
-    if (threadIdx.x < 12 && t != 0.0) unsafeAtomicAdd(acc + 12 * px.view + threadIdx.x, t);
+    if (threadIdx.x < 12 && t != 0.0) unsafeAtomicAdd(acc + 12 * view + threadIdx.x, t);
 }
 
 // dL/dR_ij = -t_i P_j + Q_ij, dL/dt_i = -sum_a R_ia P_a, written as 3x4 rows.
@@ -262,41 +269,41 @@ __global__ __launch_bounds__(256) void drr_zero_f64_kernel(double* __restrict__ 
     if (i < n) p[i] = 0.0;
 }
 
-// Corner-cell relayout (shared with the forward).
-hipError_t launch_cells(const VolumeDesc& V, const void* vol, int dtype, void* cells,
-                        hipStream_t stream);
-
 template <typename T, Layout L>
-static void launch_pose(const LaunchArgs& a, const T* src, uint32_t src_bytes,
+static void launch_pose(const LaunchArgs& a, const T* src, uint32_t src_bytes, const Batch& b,
                         const float* grad_out, double* acc, hipStream_t stream)
 {
     const int tiles_x = (a.W + kTile - 1) / kTile, tiles_y = (a.H + kTile - 1) / kTile;
     const int tiles_per_view = tiles_x * tiles_y;
-    const dim3 grid(tiles_per_view * a.n_views), block(kBlock);
+    const dim3 grid(tiles_per_view * a.n_views * a.C), block(kBlock);
     if (a.mode == kBeerLambert)
         hipLaunchKernelGGL((drr_pose_grad_kernel<T, L, kBeerLambert>), grid, block, 0, stream, src,
                            src_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view,
-                           grad_out, acc);
+                           b, grad_out, acc);
     else
         hipLaunchKernelGGL((drr_pose_grad_kernel<T, L, kLineIntegral>), grid, block, 0, stream,
                            src, src_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
-                           tiles_per_view, grad_out, acc);
+                           tiles_per_view, b, grad_out, acc);
 }
 
+// The march reads T elements in layout L from `src`: the read plan decides.
 template <typename T>
-static void pose_typed(const LaunchArgs& a, const T* vol, bool cells, T* cell_buf,
+static void pose_typed(const LaunchArgs& a, const RenderPlan& p, const T* src, const Batch& b,
                        const float* grad_out, double* acc, hipStream_t stream)
 {
-    if (cells)
-        launch_pose<T, Layout::Cell>(a, cell_buf, a.V.cell_total_bytes, grad_out, acc, stream);
-    else if (a.V.n[0] >= 2)
-        launch_pose<T, Layout::Pair>(a, vol, a.V.total_bytes, grad_out, acc, stream);
+    if (p.cells) {
+        launch_pose<T, Layout::Cell>(a, src, a.V.cell_total_bytes, b, grad_out, acc, stream);
+        return;
+    }
+    const uint32_t bytes = (uint32_t)((size_t)a.V.n[0] * a.V.n[1] * a.V.n[2] * sizeof(T));
+    if (a.V.n[0] >= 2)
+        launch_pose<T, Layout::Pair>(a, src, bytes, b, grad_out, acc, stream);
     else
-        launch_pose<T, Layout::Single>(a, vol, a.V.total_bytes, grad_out, acc, stream);
+        launch_pose<T, Layout::Single>(a, src, bytes, b, grad_out, acc, stream);
 }
 
-hipError_t launch_backward_pose(const LaunchArgs& a, const void* vol, int dtype, bool cells,
-                                void* cell_buf, double* acc, const float* grad_out,
+hipError_t launch_backward_pose(const LaunchArgs& a, const RenderPlan& plan, const void* vol,
+                                int dtype, void* read_buf, double* acc, const float* grad_out,
                                 float* grad_poses, hipStream_t stream)
 {
     if (a.n_views == 0) return hipSuccess;
@@ -306,16 +313,21 @@ hipError_t launch_backward_pose(const LaunchArgs& a, const void* vol, int dtype,
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if ((long long)a.H * a.W > 0) {
-        if (cells) {
-            e = launch_cells(a.V, vol, dtype, cell_buf, stream);
-            if (e != hipSuccess) return e;
-        }
-        if (dtype == 0)
-            pose_typed<float>(a, static_cast<const float*>(vol), cells,
-                              static_cast<float*>(cell_buf), grad_out, acc, stream);
+        e = launch_read_copy(a, plan, vol, dtype, read_buf, stream);
+        if (e != hipSuccess) return e;
+        Batch b;
+        b.src_stride = (uint64_t)plan.per_volume_bytes;
+        b.grad_stride = 0;
+        b.C = a.C;
+        b.vpv = a.n_views / a.n_volumes;
+        b.f = a.f;
+        b.margin = a.margin;
+        const void* src = (plan.cells || plan.mapped) ? read_buf : vol;
+        if (plan.mapped || dtype == 0)
+            pose_typed<float>(a, plan, static_cast<const float*>(src), b, grad_out, acc, stream);
         else
-            pose_typed<uint16_t>(a, static_cast<const uint16_t*>(vol), cells,
-                                 static_cast<uint16_t*>(cell_buf), grad_out, acc, stream);
+            pose_typed<uint16_t>(a, plan, static_cast<const uint16_t*>(src), b, grad_out, acc,
+                                 stream);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -212,9 +212,9 @@ int drr_backward_volume_siddon(int nz, int ny, int nx, const float *spacing, con
  *     xp_{K-2} on the last segment applies; at a knot the slope is the right
  *     segment's. */
 
-/* Workspace bytes of drr_render (for_backward = DRR_WORKSPACE_FORWARD) or
- * drr_render_backward_volume (DRR_WORKSPACE_VOLUME_BACKWARD) for these
- * sizes; tf_knots = 0 means no transfer function.  0 for invalid sizes or when
+/* Workspace bytes of drr_render (for_backward = DRR_WORKSPACE_FORWARD),
+ * drr_render_backward_volume (DRR_WORKSPACE_VOLUME_BACKWARD) or
+ * drr_render_backward_pose (DRR_WORKSPACE_POSE_BACKWARD) for these sizes; tf_knots = 0 means no transfer function.  0 for invalid sizes or when
  * none is needed.  The forward uses it for a corner-cell copy of every
  * channel-volume (when rays reuse cells enough, and always in the near/far
  * mode), or for the mapped fp32 volumes; the compositing backward with a
@@ -277,6 +277,27 @@ int drr_render_backward_volume(const void *volume, int dtype, int n_volumes, int
                                int tf_knots, const float *grad_out, const float *out,
                                const float *aux, float *grad_volume, void *workspace,
                                size_t workspace_bytes, void *stream);
+
+/* Pose gradient of drr_render (flashdrr API, VolumeRaycaster class text:
+ * rendering is differentiable with respect to the view matrices): for
+ * L = sum grad_out * out it writes dL/dP_v for every view's 3x4 [R | t] as
+ * drr_backward_pose does, summed over the view's channels, with the density
+ * factor and the transfer function of the call.  Beer-Lambert and line
+ * integral with DRR_CLIP_BOX (compositing or the near/far range return
+ * DRR_ERR_UNSUPPORTED).
+ *   grad_out      device, n_views x n_channels x det_h x det_w floats
+ *   grad_poses    device, n_views x 12 floats, OVERWRITTEN
+ *   workspace     device, >= drr_render_workspace_bytes(..., DRR_WORKSPACE_POSE_BACKWARD),
+ *                 256-byte aligned (never empty for n_views > 0)
+ * drr_backward_pose is this call for one volume, one channel, f = 1 and no
+ * transfer function. */
+int drr_render_backward_pose(const void *volume, int dtype, int n_volumes, int n_channels,
+                             int nz, int ny, int nx, const float *spacing, const float *K,
+                             const float *poses, int n_views, int det_h, int det_w,
+                             int n_samples, int mode, float density_factor, int clip,
+                             float margin, const float *tf_xp, const float *tf_yp, int tf_knots,
+                             const float *grad_out, float *grad_poses, void *workspace,
+                             size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Camera conventions of the flashdrr front end (flashdrr.rendering API:

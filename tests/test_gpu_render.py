@@ -244,3 +244,50 @@ def test_render_edge_cases(dev):
     ref_g = oracle.render_adjoint(one, spacing, K, poses[:1], H, Wd, 8, RAW, g[:1, :1],
                                   clip=NEAR_FAR, margin=5.0)
     check(img, tau, grad, ref, ref_tau, ref_g, "one voxel near/far")
+
+
+@pytest.mark.parametrize("N", [37, 101])
+@pytest.mark.parametrize("tf", [False, True])
+@pytest.mark.parametrize("mode", [BL, RAW])
+def test_render_pose_gradient(dev, mode, tf, N):
+    """Pose gradients of batched renders (2 volumes x 2 channels, 2 views each,
+    density factor, transfer function) against the oracle, per view normwise
+    over the twelve entries; N = 101 reads (mapped) corner cells."""
+    seed = 400 + 4 * mode + 2 * tf + (N > 50)
+    vol, spacing, K, poses, H, Wd, N, g = problem(seed, N=N, tf=tf)
+    transfer = knots(2) if tf else None
+    f = 30.0 if tf else 0.7
+    say(f"case: render pose gradient mode={mode} tf={tf} N={N}")
+    P = torch.from_numpy(poses).to(dev)
+    gp = drr.drr_render_backward_pose(torch.from_numpy(vol).to(dev), spacing, K, P, H, Wd, N,
+                                      mode, torch.from_numpy(g).to(dev), f, BOX, 0.0, transfer)
+    torch.cuda.synchronize()
+    ref = oracle.render_pose_gradient(vol, spacing, K, poses, H, Wd, N, mode, g,
+                                      density_factor=f, transfer=transfer)
+    got = gp.cpu().double().numpy()
+    errs = [np.abs(got[v] - ref[v]).max() / np.abs(ref[v]).max() for v in range(len(ref))]
+    say(f"render pose gradient m{mode} tf{int(tf)} N{N}: per-view normwise err max {max(errs):.3e}")
+    assert max(errs) <= GRAD
+
+
+def test_raycast_pose_gradient_and_unsupported_modes(dev):
+    """Autograd reaches the poses through raycast (one pose broadcast to two
+    volumes sums both volumes' gradients); compositing and the near/far range
+    refuse pose gradients."""
+    vol, spacing, K, poses, H, Wd, N, g = problem(410, B=2, C=1, vpv=1, N=33)
+    v = torch.from_numpy(vol).to(dev)
+    P = torch.from_numpy(poses[:1]).to(dev).requires_grad_(True)
+    img = drr.raycast(v, spacing, K, P, H, Wd, N, BL, 1.5)
+    (img * torch.from_numpy(g).to(dev)).sum().backward()
+    torch.cuda.synchronize()
+    ref = oracle.render_pose_gradient(vol, spacing, K, np.repeat(poses[:1], 2, axis=0), H, Wd, N,
+                                      BL, g, density_factor=1.5).sum(axis=0)
+    err = np.abs(P.grad.cpu().double().numpy()[0] - ref).max() / np.abs(ref).max()
+    say(f"raycast pose gradient (broadcast pose): normwise err {err:.3e}")
+    assert err <= GRAD
+    gt = torch.from_numpy(g).to(dev)
+    for mode, clip in [(ALPHA, BOX), (BL, NEAR_FAR)]:
+        with pytest.raises(drr.DRRError) as e:
+            drr.drr_render_backward_pose(v, spacing, K, P.detach().expand(2, 3, 4).contiguous(),
+                                         H, Wd, N, mode, gt, 1.0, clip)
+        assert e.value.status == 2
