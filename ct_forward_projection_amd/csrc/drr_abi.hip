@@ -321,11 +321,12 @@ size_t drr_workspace_bytes(int nz, int ny, int nx, int dtype, int n_views, int d
         n_samples < 1 || (dtype != DRR_F32 && dtype != DRR_BF16))
         return 0;
     if (for_backward == DRR_WORKSPACE_VOLUME_BACKWARD) return 0;
-    const size_t cells = drr::plan_render(1, 1, nz, ny, nx, dtype == DRR_F32 ? 4 : 2, n_views,
-                                          det_h, det_w, n_samples, drr::kClipBox, false)
-                             .workspace_bytes;
-    if (for_backward == DRR_WORKSPACE_POSE_BACKWARD) return drr::pose_acc_bytes(n_views) + cells;
-    return for_backward == DRR_WORKSPACE_FORWARD ? cells : 0;
+    const bool fwd = for_backward == DRR_WORKSPACE_FORWARD;
+    const size_t plan = drr::plan_render(1, 1, nz, ny, nx, dtype == DRR_F32 ? 4 : 2, n_views,
+                                         det_h, det_w, n_samples, drr::kClipBox, false, fwd)
+                            .workspace_bytes;
+    if (for_backward == DRR_WORKSPACE_POSE_BACKWARD) return drr::pose_acc_bytes(n_views) + plan;
+    return fwd ? plan : 0;
 }
 
 int drr_forward(const void* volume, int dtype, int nz, int ny, int nx, const float* spacing,
@@ -344,7 +345,7 @@ int drr_forward(const void* volume, int dtype, int nz, int ny, int nx, const flo
     if (n_rays > 0 && !out) return fail(DRR_ERR_INVALID_ARGUMENT, "out is NULL");
     const int eb = dtype == DRR_F32 ? 4 : 2;
     const drr::RenderPlan plan = drr::plan_render(1, 1, nz, ny, nx, eb, n_views, det_h, det_w,
-                                                  n_samples, drr::kClipBox, false);
+                                                  n_samples, drr::kClipBox, false, true);
     if (workspace_bytes < plan.workspace_bytes)
         return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
                     workspace_bytes, plan.workspace_bytes);
@@ -400,12 +401,13 @@ size_t drr_render_workspace_bytes(int n_volumes, int n_channels, int nz, int ny,
     const bool has_tf = tf_knots > 0;
     if (for_backward == DRR_WORKSPACE_VOLUME_BACKWARD)
         return drr::render_backward_workspace(n_volumes, n_channels, nz, ny, nx, mode, has_tf);
+    const bool fwd = for_backward == DRR_WORKSPACE_FORWARD;
     const size_t plan = drr::plan_render(n_volumes, n_channels, nz, ny, nx,
                                          dtype == DRR_F32 ? 4 : 2, n_views, det_h, det_w,
-                                         n_samples, clip, has_tf)
+                                         n_samples, clip, has_tf, fwd)
                             .workspace_bytes;
     if (for_backward == DRR_WORKSPACE_POSE_BACKWARD) return drr::pose_acc_bytes(n_views) + plan;
-    return for_backward == DRR_WORKSPACE_FORWARD ? plan : 0;
+    return fwd ? plan : 0;
 }
 
 int drr_render(const void* volume, int dtype, int n_volumes, int n_channels, int nz, int ny,
@@ -428,7 +430,7 @@ int drr_render(const void* volume, int dtype, int n_volumes, int n_channels, int
     const long long n_out = (long long)n_views * n_channels * det_h * det_w;
     if (n_out > 0 && !out) return fail(DRR_ERR_INVALID_ARGUMENT, "out is NULL");
     const drr::RenderPlan plan = drr::plan_render(n_volumes, n_channels, nz, ny, nx, eb, n_views,
-                                                  det_h, det_w, n_samples, clip, a.has_tf);
+                                                  det_h, det_w, n_samples, clip, a.has_tf, true);
     if (!plan.fits)
         return fail(DRR_ERR_UNSUPPORTED, "one channel-volume of the march's copy exceeds 4 GiB");
     if (workspace_bytes < plan.workspace_bytes)

@@ -309,6 +309,201 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
     if (s_out) s_out[o] = tau;
 }
 
+// LDS-staged forward (box clip).  The rays of a 16 x 16 tile are close and
+// straight, so the voxels a chunk of their samples touch form a small box:
+// the workgroup loads that box once from the caller's volume into LDS -- in
+// unclamped index space, each entry the clamped voxel (clamp to edge), mapped
+// by the transfer function when there is one, widened to fp32 -- and every
+// sample then reads its eight corners from LDS at fixed offsets (+1 in x, +ex
+// in y, +ex ey in z), four ds_read2 per sample instead of two 16-byte global
+// loads.  Chunks are sized like the backward's windows (halved until the box
+// fits, doubled while it has room); a chunk whose box does not fit even for
+// one sample gathers its corners from global memory.  No relayout pass and no
+// workspace.
+constexpr int kStageCap = 8192;              // fp32 entries of the staged box (32 KB)
+
+template <typename T, bool TF>
+__device__ inline float staged_value(__amdgpu_buffer_rsrc_t rs, const VolumeDesc& V, int x,
+                                     int y, int z, const TransferFn& tf, int ch)
+{
+    const uint32_t off = (uint32_t)clampi(z, 0, V.n[2] - 1) * (uint32_t)V.n[1] * (uint32_t)V.n[0] +
+                         (uint32_t)clampi(y, 0, V.n[1] - 1) * (uint32_t)V.n[0] +
+                         (uint32_t)clampi(x, 0, V.n[0] - 1);
+    const float v = load_one<T>(rs, off * (uint32_t)sizeof(T));
+    if constexpr (TF) {
+        float m;
+        return transfer_eval(tf, ch, v, m);
+    } else {
+        return v;
+    }
+}
+
+template <typename T, int MODE, bool TF>
+__global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
+    const T* __restrict__ src, uint32_t src_bytes, VolumeDesc V, Intrinsics K,
+    const float* __restrict__ poses, int H, int W, int N, int tiles_x, int tiles_per_view,
+    Batch b, TransferFn tf, float* __restrict__ out, float* __restrict__ s_out)
+{
+    __shared__ float box[kStageCap];
+    __shared__ int red[(kBlock / 64) * 6];
+    __shared__ int bb[6];
+    const int tile = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
+    const PixelCoord px = tile_pixel(tile, tiles_x, tiles_per_view);
+    const int view = px.view / b.C, ch = px.view - view * b.C;
+    const int cvol = (view / b.vpv) * b.C + ch;
+    const bool mine = px.r < H && px.c < W;
+    MarchRay R;
+    bool hit = false;
+    if (mine) {
+        ViewGeom G;
+        view_setup(poses + 12 * view, K, G);
+        hit = ray_setup(G, V, px.r, px.c, N, R);
+    }
+    const char* base = reinterpret_cast<const char*>(src) + (uint64_t)cvol * b.src_stride;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)src_bytes, kBufferWord3);
+    const float fdz = hit ? b.f * R.dz : 0.0f;
+    float acc[kInflight];
+#pragma unroll
+    for (int i = 0; i < kInflight; ++i) acc[i] = 0.0f;
+    double tau_c = 0.0, I_c = 0.0;
+
+    int S = N;
+    int k0 = 0;
+    while (k0 < N) {
+        S = min(S, N - k0);
+        int ext[3] = {1, 1, 1}, lo[3] = {0, 0, 0};
+        long long vol_cells = 1;
+        for (;;) {
+            // unclamped floor indices of the chunk's end samples, and one past
+            int v[6] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+            if (hit) {
+#pragma unroll
+                for (int a = 0; a < 3; ++a) {
+                    const int fa = fixed_floor(R.q0[a] + (int64_t)k0 * R.dq[a]);
+                    const int fb = fixed_floor(R.q0[a] + (int64_t)(k0 + S - 1) * R.dq[a]);
+                    v[a] = min(fa, fb);
+                    v[3 + a] = -(max(fa, fb) + 1);
+                }
+            }
+            block_min6(v, red, bb);
+            if (bb[0] == INT_MAX) break;             // no ray of this tile hits the box
+            vol_cells = 1;
+#pragma unroll
+            for (int a = 0; a < 3; ++a) {
+                lo[a] = bb[a];
+                ext[a] = max(-bb[3 + a] - bb[a] + 1, 1);
+                vol_cells *= ext[a];
+            }
+            if (vol_cells <= kStageCap || S == 1) break;
+            S = max(1, S >> 1);
+        }
+        if (bb[0] == INT_MAX) break;
+        const int ey = ext[0], ez = ext[0] * ext[1];
+        if (vol_cells <= kStageCap) {
+            const int n_box = (int)vol_cells;
+            for (int i = threadIdx.x; i < n_box; i += kBlock) {
+                const int x = i % ext[0], rest = i / ext[0];
+                box[i] = staged_value<T, TF>(rs, V, lo[0] + x, lo[1] + rest % ext[1],
+                                             lo[2] + rest / ext[1], tf, ch);
+            }
+            __syncthreads();
+            if (hit) {
+                int64_t qx = R.q0[0] + (int64_t)k0 * R.dq[0];
+                int64_t qy = R.q0[1] + (int64_t)k0 * R.dq[1];
+                int64_t qz = R.q0[2] + (int64_t)k0 * R.dq[2];
+                int k = k0;
+                for (; k + kInflight <= k0 + S; k += kInflight) {
+                    SampleAddr A[kInflight];
+                    CornerVals c[kInflight];
+#pragma unroll
+                    for (int i = 0; i < kInflight; ++i) {
+                        A[i].fx = fixed_frac(qx);
+                        A[i].fy = fixed_frac(qy);
+                        A[i].fz = fixed_frac(qz);
+                        A[i].o = (uint32_t)(fixed_floor(qx) - lo[0]) +
+                                 __umul24((uint32_t)(fixed_floor(qy) - lo[1]), (uint32_t)ey) +
+                                 __umul24((uint32_t)(fixed_floor(qz) - lo[2]), (uint32_t)ez);
+                        qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
+                    }
+#pragma unroll
+                    for (int i = 0; i < kInflight; ++i) {
+                        const float* p = box + A[i].o;
+                        c[i].v[0] = p[0];           c[i].v[1] = p[1];
+                        c[i].v[2] = p[ey];          c[i].v[3] = p[ey + 1];
+                        c[i].v[4] = p[ez];          c[i].v[5] = p[ez + 1];
+                        c[i].v[6] = p[ez + ey];     c[i].v[7] = p[ez + ey + 1];
+                    }
+#pragma unroll
+                    for (int i = 0; i < kInflight; ++i) {
+                        const float val = interpolate(A[i], c[i]);
+                        if constexpr (MODE == kAlpha) composite(val, fdz, tau_c, I_c);
+                        else acc[i] += val;
+                    }
+                }
+                for (; k < k0 + S; ++k) {
+                    SampleAddr A;
+                    A.fx = fixed_frac(qx);
+                    A.fy = fixed_frac(qy);
+                    A.fz = fixed_frac(qz);
+                    const float* p = box + (fixed_floor(qx) - lo[0]) +
+                                     __mul24(fixed_floor(qy) - lo[1], ey) +
+                                     __mul24(fixed_floor(qz) - lo[2], ez);
+                    qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
+                    CornerVals c;
+                    c.v[0] = p[0];       c.v[1] = p[1];
+                    c.v[2] = p[ey];      c.v[3] = p[ey + 1];
+                    c.v[4] = p[ez];      c.v[5] = p[ez + 1];
+                    c.v[6] = p[ez + ey]; c.v[7] = p[ez + ey + 1];
+                    const float val = interpolate(A, c);
+                    if constexpr (MODE == kAlpha) composite(val, fdz, tau_c, I_c);
+                    else acc[0] += val;
+                }
+            }
+            __syncthreads();
+        } else if (hit) {
+            // the box does not fit: gather this chunk's corners from global memory
+            int64_t qx = R.q0[0] + (int64_t)k0 * R.dq[0];
+            int64_t qy = R.q0[1] + (int64_t)k0 * R.dq[1];
+            int64_t qz = R.q0[2] + (int64_t)k0 * R.dq[2];
+            for (int k = k0; k < k0 + S; ++k) {
+                const int ix = fixed_floor(qx), iy = fixed_floor(qy), iz = fixed_floor(qz);
+                SampleAddr A;
+                A.fx = fixed_frac(qx);
+                A.fy = fixed_frac(qy);
+                A.fz = fixed_frac(qz);
+                qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
+                CornerVals c;
+#pragma unroll
+                for (int n = 0; n < 8; ++n)
+                    c.v[n] = staged_value<T, TF>(rs, V, ix + (n & 1), iy + ((n >> 1) & 1),
+                                                 iz + (n >> 2), tf, ch);
+                const float val = interpolate(A, c);
+                if constexpr (MODE == kAlpha) composite(val, fdz, tau_c, I_c);
+                else acc[0] += val;
+            }
+        }
+        k0 += S;
+        if (vol_cells * 2 <= kStageCap) S *= 2;
+    }
+    if (!mine) return;
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kInflight; ++i) s += acc[i];
+    float res, tau;
+    if constexpr (MODE == kAlpha) {
+        res = (float)I_c;
+        tau = (float)tau_c;
+    } else {
+        if (hit) s *= R.dz;
+        tau = b.f * s;
+        res = (MODE == kBeerLambert) ? -expm1f(-tau) : tau;
+    }
+    const size_t o = ((size_t)px.view * H + px.r) * W + px.c;
+    out[o] = res;
+    if (s_out) s_out[o] = tau;
+}
+
 // Zero padding (near/far mode): 1 for a corner index inside [0, n - 1], 0
 // outside, per axis and end: m = (x0, x1, y0, y1, z0, z1).  Used with the
 // clamped Cell, whose indices then only serve as in-range addresses.
@@ -824,11 +1019,37 @@ hipError_t launch_read_copy(const LaunchArgs& a, const RenderPlan& p, const void
     return hipSuccess;
 }
 
+template <typename Tin, int MODE>
+static void launch_staged_mode(const LaunchArgs& a, const Tin* vol, const Batch& b, float* out,
+                               float* s_out, hipStream_t stream)
+{
+    int tiles_x, tiles_per_view, n_tiles;
+    tile_grid(a.n_views * a.C, a.H, a.W, kTile, tiles_x, tiles_per_view, n_tiles);
+    const uint32_t bytes = (uint32_t)((size_t)a.V.n[0] * a.V.n[1] * a.V.n[2] * sizeof(Tin));
+    if (a.has_tf)
+        hipLaunchKernelGGL((drr_march_staged_kernel<Tin, MODE, true>), dim3(n_tiles), dim3(kBlock),
+                           0, stream, vol, bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                           tiles_per_view, b, a.tf, out, s_out);
+    else
+        hipLaunchKernelGGL((drr_march_staged_kernel<Tin, MODE, false>), dim3(n_tiles),
+                           dim3(kBlock), 0, stream, vol, bytes, a.V, a.K, a.poses, a.H, a.W, a.N,
+                           tiles_x, tiles_per_view, b, a.tf, out, s_out);
+}
+
 template <typename Tin>
 static hipError_t forward_typed(const LaunchArgs& a, const RenderPlan& p, const Tin* vol,
                                 void* workspace, float* out, float* s_out, hipStream_t stream)
 {
     const Batch b = make_batch(a, &p, 0);
+    if (p.staged) {
+        if (a.mode == kBeerLambert)
+            launch_staged_mode<Tin, kBeerLambert>(a, vol, b, out, s_out, stream);
+        else if (a.mode == kLineIntegral)
+            launch_staged_mode<Tin, kLineIntegral>(a, vol, b, out, s_out, stream);
+        else
+            launch_staged_mode<Tin, kAlpha>(a, vol, b, out, s_out, stream);
+        return hipGetLastError();
+    }
     const uint32_t bytes = p.cells ? a.V.cell_total_bytes : (uint32_t)((size_t)a.V.n[0] * a.V.n[1] *
                                                                       a.V.n[2] * p.read_elem);
     if (p.cells) {

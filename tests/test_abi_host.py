@@ -120,15 +120,17 @@ def test_binding_refuses_host_tensors():
 
 
 def test_workspace_too_small_is_rejected_on_the_host():
-    # a dense-ray launch plans the corner-cell relayout, which needs a workspace
-    need = drr.drr_workspace_bytes(8, 8, 8, 0, 1, 256, 256, 64, 0)
+    # many views that together reuse cells plan the corner-cell relayout, which
+    # needs a workspace
+    need = drr.drr_workspace_bytes(8, 8, 8, 0, 64, 16, 16, 8, 0)
     assert need >= 9 * 9 * 9 * 32
-    assert fwd(det_h=256, det_w=256, n_samples=64, ws=None, ws_bytes=0) == 3
+    assert fwd(n_views=64, det_h=16, det_w=16, n_samples=8, ws=None, ws_bytes=0) == 3
     assert b"workspace" in drr.library().drr_last_error()
     # misaligned workspace
-    assert fwd(det_h=256, det_w=256, n_samples=64, ws=ctypes.c_void_p(0x1004),
+    assert fwd(n_views=64, det_h=16, det_w=16, n_samples=8, ws=ctypes.c_void_p(0x1004),
                ws_bytes=need) == 1
-    # the backward needs none
+    # one dense view stages its boxes in LDS and needs none; neither does the backward
+    assert drr.drr_workspace_bytes(8, 8, 8, 0, 1, 256, 256, 64, 0) == 0
     assert drr.drr_workspace_bytes(8, 8, 8, 0, 1, 256, 256, 64, 1) == 0
 
 
