@@ -402,11 +402,10 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
         const int ey = ext[0], ez = ext[0] * ext[1];
         if (vol_cells <= kStageCap) {
             const int n_box = (int)vol_cells;
-            for (int i = threadIdx.x; i < n_box; i += kBlock) {
-                const int x = i % ext[0], rest = i / ext[0];
-                box[i] = staged_value<T, TF>(rs, V, lo[0] + x, lo[1] + rest % ext[1],
-                                             lo[2] + rest / ext[1], tf, ch);
-            }
+            BoxWalk bw(ext);
+            for (int i = threadIdx.x; i < n_box; i += kBlock, bw.next())
+                box[i] = staged_value<T, TF>(rs, V, lo[0] + bw.x, lo[1] + bw.y, lo[2] + bw.z, tf,
+                                             ch);
             __syncthreads();
             if (hit) {
                 int64_t qx = R.q0[0] + (int64_t)k0 * R.dq[0];
@@ -671,11 +670,11 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
     VolumeDesc V, Intrinsics K, const float* __restrict__ poses, int H, int W, int N,
     int tiles_x, int tiles_per_view, Batch bt, const float* __restrict__ grad_out,
     const float* __restrict__ s_in, const float* __restrict__ out_in,
-    const T* __restrict__ vol, uint32_t vol_bytes, float* __restrict__ grad)
+    const T* __restrict__ vol, uint32_t vol_bytes, float* __restrict__ grad, int win_cap)
 {
     constexpr bool ZP = CLIP == kClipNearFar;
     constexpr bool ALPHA = MODE == kAlpha;
-    __shared__ int win[kWinCap];
+    extern __shared__ int win[];                  // win_cap entries (dynamic LDS)
     __shared__ int red[(kBlock / 64) * 6];
     __shared__ int box[6];
 
@@ -792,10 +791,10 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 ext[a] = max(-box[3 + a] - box[a] + 1, 1);
                 vol_cells *= ext[a];
             }
-            if (!fixed_ok || vol_cells <= kWinCap || S == 1) break;
+            if (!fixed_ok || vol_cells <= win_cap || S == 1) break;
             S = max(1, S >> 1);
         }
-        if (fixed_ok && vol_cells <= kWinCap) {
+        if (fixed_ok && vol_cells <= win_cap) {
             const int n_win = (int)vol_cells;
             for (int i = threadIdx.x; i < n_win; i += kBlock) win[i] = 0;
             __syncthreads();
@@ -832,17 +831,13 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 window_add(win, P, lo, wy, wz, acc);
             }
             __syncthreads();
-            for (int i = threadIdx.x; i < n_win; i += kBlock) {
+            BoxWalk bw(ext);
+            for (int i = threadIdx.x; i < n_win; i += kBlock, bw.next()) {
                 const int val = win[i];
-                if (val != 0) {
-                    const int ix = i % ext[0];
-                    const int rest = i / ext[0];
-                    const int iy = rest % ext[1];
-                    const int iz = rest / ext[1];
-                    unsafeAtomicAdd(grad + (uint32_t)(lo[2] + iz) * sz +
-                                        (uint32_t)(lo[1] + iy) * sy + (uint32_t)(lo[0] + ix),
+                if (val != 0)
+                    unsafeAtomicAdd(grad + (uint32_t)(lo[2] + bw.z) * sz +
+                                        (uint32_t)(lo[1] + bw.y) * sy + (uint32_t)(lo[0] + bw.x),
                                     (float)val * inv_scale);
-                }
             }
             __syncthreads();
         } else if (active) {
@@ -861,7 +856,7 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
         }
         k0 += S;
         // a chunk that left room in the window: try a longer one next
-        if (vol_cells * 2 <= kWinCap) S *= 2;
+        if (vol_cells * 2 <= win_cap) S *= 2;
     }
 }
 
@@ -1112,14 +1107,17 @@ static void launch_scatter(const LaunchArgs& a, const Batch& b, const float* gra
                            uint32_t vol_bytes, float* grad, int tiles_x, int tiles_per_view,
                            int n_tiles, hipStream_t stream)
 {
+    const double cells = (double)(a.V.n[0] + 1) * (a.V.n[1] + 1) * (a.V.n[2] + 1);
+    const int cap = window_cap((double)a.H * a.W * a.N / cells);
+    const size_t lds = (size_t)cap * sizeof(int);
     if (a.clip == kClipNearFar)
         hipLaunchKernelGGL((drr_scatter_kernel<MODE, kClipNearFar, T>), dim3(n_tiles),
-                           dim3(kBlock), 0, stream, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
-                           tiles_per_view, b, grad_out, s_in, out_in, vol, vol_bytes, grad);
+                           dim3(kBlock), lds, stream, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                           tiles_per_view, b, grad_out, s_in, out_in, vol, vol_bytes, grad, cap);
     else
         hipLaunchKernelGGL((drr_scatter_kernel<MODE, kClipBox, T>), dim3(n_tiles), dim3(kBlock),
-                           0, stream, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view,
-                           b, grad_out, s_in, out_in, vol, vol_bytes, grad);
+                           lds, stream, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view,
+                           b, grad_out, s_in, out_in, vol, vol_bytes, grad, cap);
 }
 
 template <typename Tin>

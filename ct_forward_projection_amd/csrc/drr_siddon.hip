@@ -214,9 +214,9 @@ template <int MODE>
 __global__ __launch_bounds__(kBlock) void drr_siddon_scatter_kernel(
     VolumeDesc V, Intrinsics K, const float* __restrict__ poses, int H, int W, int M,
     int tiles_x, int tiles_per_view, const float* __restrict__ grad_out,
-    const float* __restrict__ s_in, float* __restrict__ grad)
+    const float* __restrict__ s_in, float* __restrict__ grad, int win_cap)
 {
-    __shared__ int win[kWinCap];
+    extern __shared__ int win[];                  // win_cap entries (dynamic LDS)
     __shared__ int red[(kBlock / 64) * 6];
     __shared__ int box[6];
 
@@ -286,11 +286,11 @@ __global__ __launch_bounds__(kBlock) void drr_siddon_scatter_kernel(
                 ext[a] = max(-box[3 + a] - box[a] + 1, 1);
                 vol *= ext[a];
             }
-            if (!fixed_ok || vol <= kWinCap || Sc == 1) break;
+            if (!fixed_ok || vol <= win_cap || Sc == 1) break;
             Sc = max(1, Sc >> 1);
         }
         if (box[0] == INT_MAX) break;
-        const bool windowed = fixed_ok && vol <= kWinCap;
+        const bool windowed = fixed_ok && vol <= win_cap;
         const int wy = ext[0], wz = ext[0] * ext[1];
         if (windowed) {
             const int n_win = (int)vol;
@@ -322,23 +322,19 @@ __global__ __launch_bounds__(kBlock) void drr_siddon_scatter_kernel(
         }
         if (windowed) {
             __syncthreads();
-            for (int i = threadIdx.x; i < (int)vol; i += kBlock) {
+            BoxWalk bw(ext);
+            for (int i = threadIdx.x; i < (int)vol; i += kBlock, bw.next()) {
                 const int val = win[i];
-                if (val != 0) {
-                    const int ix = i % ext[0];
-                    const int rest = i / ext[0];
-                    const int iy = rest % ext[1];
-                    const int iz = rest / ext[1];
-                    unsafeAtomicAdd(grad + (uint32_t)(lo[2] + iz) * sz +
-                                        (uint32_t)(lo[1] + iy) * sy + (uint32_t)(lo[0] + ix),
+                if (val != 0)
+                    unsafeAtomicAdd(grad + (uint32_t)(lo[2] + bw.z) * sz +
+                                        (uint32_t)(lo[1] + bw.y) * sy + (uint32_t)(lo[0] + bw.x),
                                     (float)val * inv_scale);
-                }
             }
             __syncthreads();
         }
         k0 += Sc;
         // a chunk that left room in the window: try a longer one next
-        if (vol * 2 <= kWinCap) Sc *= 2;
+        if (vol * 2 <= win_cap) Sc *= 2;
     }
 }
 
@@ -387,14 +383,18 @@ hipError_t launch_siddon_backward(const LaunchArgs& a, const float* grad_out, co
     // chunks of the ray: about one voxel along the longest axis each
     const int M = max(a.V.n[0], max(a.V.n[1], a.V.n[2]));
     const dim3 grid(n_tiles), block(kBlock);
+    // pieces per ray ~ M: the same density measure as the trilinear scatter
+    const double cells = (double)(a.V.n[0] + 1) * (a.V.n[1] + 1) * (a.V.n[2] + 1);
+    const int cap = window_cap((double)a.H * a.W * M / cells);
+    const size_t lds = (size_t)cap * sizeof(int);
     if (a.mode == kBeerLambert)
-        hipLaunchKernelGGL((drr_siddon_scatter_kernel<kBeerLambert>), grid, block, 0, stream, a.V,
-                           a.K, a.poses, a.H, a.W, M, tiles_x, tiles_per_view, grad_out, s_in,
-                           grad);
-    else
-        hipLaunchKernelGGL((drr_siddon_scatter_kernel<kLineIntegral>), grid, block, 0, stream,
+        hipLaunchKernelGGL((drr_siddon_scatter_kernel<kBeerLambert>), grid, block, lds, stream,
                            a.V, a.K, a.poses, a.H, a.W, M, tiles_x, tiles_per_view, grad_out,
-                           s_in, grad);
+                           s_in, grad, cap);
+    else
+        hipLaunchKernelGGL((drr_siddon_scatter_kernel<kLineIntegral>), grid, block, lds, stream,
+                           a.V, a.K, a.poses, a.H, a.W, M, tiles_x, tiles_per_view, grad_out,
+                           s_in, grad, cap);
     return hipGetLastError();
 }
 

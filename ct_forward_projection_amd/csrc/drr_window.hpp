@@ -12,8 +12,54 @@
 
 namespace drr {
 
-// LDS window of the backward: 8192 int32 (32 KB), five workgroups per CU.
-constexpr int kWinCap = 8192;
+// LDS window of the backward scatters, sized per launch (dynamic LDS).  When
+// one view's rays are dense against the voxels a tile's box is thin, chunks
+// are long, and occupancy matters: 6144 int32 (24 KB) lets six workgroups
+// share a CU (the scatter's registers allow six waves per SIMD).  When they
+// are sparse (a voxel or more between neighbouring rays) the box is wide,
+// chunks are short, and a larger window saves chunks: 16000 entries (62.5 KB,
+// two workgroups per CU, under the 64 KB default dynamic-LDS limit).
+// Measured on MI355X (1024^2 step / 360-view helix / 16-view 200^2 batch):
+// 4096 entries 1.15 / 27.9 / - ms, 6144 1.12 / 19.9 / 7.37, 8192
+// 1.19 / 21.4 / 4.96, 12288 1.28 / 23.8 / 3.08, 16384 - / - / 2.81,
+// 24576 2.68 / 56.0 / 4.89.
+constexpr int kWinCapDense = 6144;
+constexpr int kWinCapSparse = 16000;
+
+// Window entries for a launch whose views each put `view_reuse` samples (or
+// ray-voxel pieces) per cell of the volume.
+inline int window_cap(double view_reuse) { return view_reuse >= 4.0 ? kWinCapDense : kWinCapSparse; }
+
+// Position (x, y, z) of entry i = threadIdx.x + n kBlock of a box of
+// ext[0] x ext[1] x ... entries (x fastest), advanced kBlock entries per
+// step with carries instead of divisions.
+struct BoxWalk {
+    int x, y, z;
+    int sx, sy, sz, ex, ey;
+
+    __device__ explicit BoxWalk(const int ext[3])
+    {
+        ex = ext[0];
+        ey = ext[1];
+        const int r = (int)threadIdx.x / ex, q = kBlock / ex;
+        x = (int)threadIdx.x - r * ex;
+        y = r % ey;
+        z = r / ey;
+        sx = kBlock - q * ex;
+        sy = q % ey;
+        sz = q / ey;
+    }
+    __device__ void next()
+    {
+        x += sx;                       // sx < ex: at most one carry
+        int c = x >= ex ? 1 : 0;
+        x -= c * ex;
+        y += sy + c;                   // sy + c <= ey: at most one carry
+        c = y >= ey ? 1 : 0;
+        y -= c * ey;
+        z += sz + c;
+    }
+};
 
 // Workgroup-wide min of six ints (maxima are passed negated).
 __device__ inline void block_min6(int v[6], int* red, int* out)
