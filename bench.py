@@ -478,7 +478,7 @@ PMC_SETS = {
            "SQ_LDS_ADDR_CONFLICT"],
 }
 # kernels whose counters each pass reports (matched as substrings of the name)
-KERNEL_KEYS = {"forward": ["drr_cells_kernel", "drr_march_kernel"],
+KERNEL_KEYS = {"forward": ["drr_march_staged_kernel"],
                "backward": ["drr_fill_kernel", "drr_scatter_kernel"],
                "pose": ["drr_cells_kernel", "drr_pose_grad_kernel"],
                "copy": ["copy"]}
@@ -506,8 +506,14 @@ def profile_summary(root: str):
     rev = kernel_revision()
     # kernel trace statistics
     stats = _find(os.path.join(root, "trace"), "kernel_stats.csv")
+    durations = {}     # kernel key -> average duration (ns) in the trace
     if stats:
         rows = _csv_rows(stats[0])
+        for key in {k for keys in KERNEL_KEYS.values() for k in keys}:
+            hits = [r for r in rows if key in r.get("Name", "")]
+            if hits:
+                best = max(hits, key=lambda r: int(r.get("Calls", 0)))
+                durations[key] = float(best.get("AverageNs", 0))
         lines = ["# Kernel trace: train step on the 1024x1024 workload", "",
                  f"Command: `{PROFILE_COMMANDS['trace']}`", "",
                  f"Kernel sources revision: `{rev}`", "",
@@ -566,7 +572,7 @@ def profile_summary(root: str):
             if (kind, name) not in med or (kind == "pose" and name == "drr_cells_kernel"):
                 continue
             _counter_table(lines, traffic, name, f"{kind} pass", med[(kind, name)],
-                           fetch_factor, write_factor)
+                           fetch_factor, write_factor, durations.get(name))
     path = os.path.join(prof_dir, "counters_train_step_1024.md")
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -575,9 +581,15 @@ def profile_summary(root: str):
     log("wrote", path)
 
 
-def _counter_table(lines, traffic, name, where, m, fetch_factor, write_factor):
+MI355X_CUS, MI355X_SIMDS, MI355X_GHZ = 256, 1024, 2.4
+
+
+def _counter_table(lines, traffic, name, where, m, fetch_factor, write_factor, dur_ns=None):
     """One kernel's median counters as a markdown table, plus its calibrated
-    HBM bytes per launch into ``traffic``."""
+    HBM bytes per launch into ``traffic``.  With the kernel's traced duration,
+    VALU busy = wave instructions x 4 cycles (a wave64 instruction occupies a
+    16-lane SIMD for 4 cycles) over 1024 SIMDs x the duration's cycles, and the
+    LDS bank-conflict share = conflict cycles over 256 CUs x those cycles."""
     lines += [f"## {name} ({where})", "", "| counter | value |", "|---|---|"]
     for c in sorted(m):
         lines.append(f"| {c} | {m[c]:.6g} |")
@@ -586,9 +598,14 @@ def _counter_table(lines, traffic, name, where, m, fetch_factor, write_factor):
     hit = m.get("TCC_HIT_sum"), m.get("TCC_MISS_sum")
     if all(h is not None for h in hit) and sum(hit) > 0:
         lines.append(f"| L2 hit rate | {hit[0] / (hit[0] + hit[1]):.4f} |")
-    if m.get("SQ_ACTIVE_INST_VALU") and m.get("SQ_BUSY_CYCLES"):
-        lines.append(f"| VALU active / SQ busy cycles | "
-                     f"{m['SQ_ACTIVE_INST_VALU'] / m['SQ_BUSY_CYCLES']:.4f} |")
+    if dur_ns:
+        cycles = dur_ns * MI355X_GHZ
+        lines.append(f"| traced duration (us) | {dur_ns / 1e3:.2f} |")
+        if m.get("SQ_INSTS_VALU"):
+            lines.append(f"| VALU busy | {m['SQ_INSTS_VALU'] * 4 / (MI355X_SIMDS * cycles):.3f} |")
+        if m.get("SQ_LDS_BANK_CONFLICT") is not None:
+            lines.append(f"| LDS bank-conflict share | "
+                         f"{m['SQ_LDS_BANK_CONFLICT'] / (MI355X_CUS * cycles):.3f} |")
     lines += ["", f"HBM-side traffic per launch (calibrated): read {fb / 1e6:.1f} MB, "
                   f"write {wb / 1e6:.1f} MB, total {(fb + wb) / 1e6:.1f} MB", ""]
     if fb or wb:
@@ -652,10 +669,11 @@ def main():
     fwd_ms, bwd_ms = time_events([res.forward, res.backward], max(args.steps, 1))
     # each pass is one ABI call: the forward launches the corner-cell relayout
     # and the march, the backward the gradient fill and the scatter
-    rf = roofline("drr_march_kernel (with corner-cell relayout)", forward_bytes(res, hits), fwd_ms,
-                  measured_traffic(["drr_cells_kernel", "drr_march_kernel"]))
+    # the forward of this workload is one launch of the LDS-staged march
+    rf = roofline("drr_march_staged_kernel", forward_bytes(res, hits), fwd_ms,
+                  measured_traffic(KERNEL_KEYS["forward"]))
     rb = roofline("drr_scatter_kernel (with gradient fill)", backward_bytes(res, hits), bwd_ms,
-                  measured_traffic(["drr_fill_kernel", "drr_scatter_kernel"]))
+                  measured_traffic(KERNEL_KEYS["backward"]))
     dominant, other = (rb, rf) if bwd_ms >= fwd_ms else (rf, rb)
 
     out = {
