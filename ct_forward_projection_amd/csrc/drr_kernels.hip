@@ -565,28 +565,35 @@ __device__ inline void scatter_sample_global(float* __restrict__ grad, uint32_t 
     unsafeAtomicAdd(grad + r11 + x1, w[7]);
 }
 
-// Add the eight (scaled) weights of one cell to the LDS window.
-__device__ inline void window_add(int* win, const Cell& C, const int lo[3], int wy, int wz,
-                                  const float w[8])
+// Trilinear weights of one sample scaled by c: w[n] for corner n (bit 0 = x1,
+// bit 1 = y1, bit 2 = z1), the same products as corner_weights without clamps.
+__device__ inline void weights8(float fx, float fy, float fz, float c, float w[8])
 {
-    const int x0 = C.x0 - lo[0], x1 = C.x1 - lo[0];
-    // window extents are below 2^13, so 24-bit multiplies are exact (full rate)
-    const int y0 = __mul24(C.y0 - lo[1], wy), y1 = __mul24(C.y1 - lo[1], wy);
-    const int z0 = __mul24(C.z0 - lo[2], wz), z1 = __mul24(C.z1 - lo[2], wz);
-    atomicAdd(&win[z0 + y0 + x0], __float2int_rn(w[0]));
-    atomicAdd(&win[z0 + y0 + x1], __float2int_rn(w[1]));
-    atomicAdd(&win[z0 + y1 + x0], __float2int_rn(w[2]));
-    atomicAdd(&win[z0 + y1 + x1], __float2int_rn(w[3]));
-    atomicAdd(&win[z1 + y0 + x0], __float2int_rn(w[4]));
-    atomicAdd(&win[z1 + y0 + x1], __float2int_rn(w[5]));
-    atomicAdd(&win[z1 + y1 + x0], __float2int_rn(w[6]));
-    atomicAdd(&win[z1 + y1 + x1], __float2int_rn(w[7]));
+    const float wz1 = c * fz, wz0 = c * (1.0f - fz);
+    const float w11 = wz1 * fy, w10 = wz1 * (1.0f - fy);
+    const float w01 = wz0 * fy, w00 = wz0 * (1.0f - fy);
+    const float fx0 = 1.0f - fx;
+    w[0] = w00 * fx0;
+    w[1] = w00 * fx;
+    w[2] = w01 * fx0;
+    w[3] = w01 * fx;
+    w[4] = w10 * fx0;
+    w[5] = w10 * fx;
+    w[6] = w11 * fx0;
+    w[7] = w11 * fx;
 }
 
-__device__ inline bool same_cell(const Cell& a, const Cell& b)
+// Add eight fixed-point weights at window entry `base` and its corner offsets.
+__device__ inline void window_add_at(int* win, int base, int wy, int wz, const float w[8])
 {
-    return a.x0 == b.x0 && a.x1 == b.x1 && a.y0 == b.y0 && a.y1 == b.y1 && a.z0 == b.z0 &&
-           a.z1 == b.z1;
+    atomicAdd(&win[base], __float2int_rn(w[0]));
+    atomicAdd(&win[base + 1], __float2int_rn(w[1]));
+    atomicAdd(&win[base + wy], __float2int_rn(w[2]));
+    atomicAdd(&win[base + wy + 1], __float2int_rn(w[3]));
+    atomicAdd(&win[base + wz], __float2int_rn(w[4]));
+    atomicAdd(&win[base + wz + 1], __float2int_rn(w[5]));
+    atomicAdd(&win[base + wz + wy], __float2int_rn(w[6]));
+    atomicAdd(&win[base + wz + wy + 1], __float2int_rn(w[7]));
 }
 
 // Per-sample coefficient of the compositing backward (MODE = kAlpha).  For
@@ -778,9 +785,10 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 for (int a = 0; a < 3; ++a) {
                     const int64_t qa = R.q0[a] + (int64_t)k0 * R.dq[a];
                     const int64_t qb = R.q0[a] + (int64_t)(k0 + S - 1) * R.dq[a];
-                    const int fa = fixed_floor(qa), fb = fixed_floor(qb);
-                    v[a] = clampi(min(fa, fb), 0, V.n[a] - 1);
-                    v[3 + a] = -clampi(max(fa, fb) + 1, 0, V.n[a] - 1);
+                    const int fa = clampi(fixed_floor(qa), -1, V.n[a] - 1);
+                    const int fb = clampi(fixed_floor(qb), -1, V.n[a] - 1);
+                    v[a] = min(fa, fb);
+                    v[3 + a] = -(max(fa, fb) + 1);
                 }
             }
             block_min6(v, red, box);
@@ -799,45 +807,67 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
             for (int i = threadIdx.x; i < n_win; i += kBlock) win[i] = 0;
             __syncthreads();
             if (active) {
+                // the window lives in unclamped index space: a sample's floor
+                // (clamped to [-1, n-1]) places its eight corners at fixed
+                // offsets; entries at -1 or n stand for the clamped edge voxel
+                // (clamp to edge) or for nothing (zero padding) and are mapped
+                // when the window is flushed.  Clamping a floor keeps every
+                // corner on the voxel the clamped corners would hit.
                 const int wy = ext[0], wz = ext[0] * ext[1];
                 int64_t qx = R.q0[0] + (int64_t)k0 * R.dq[0];
                 int64_t qy = R.q0[1] + (int64_t)k0 * R.dq[1];
                 int64_t qz = R.q0[2] + (int64_t)k0 * R.dq[2];
-                Cell P;
-                float acc[8], m[6];
-                cell_of(V, qx, qy, qz, P);
-                if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
-                if constexpr (ALPHA) corner_weights<ZP>(P, coef.next(P, m) * scale, acc, m);
-                else corner_weights<ZP>(P, ys, acc, m);
-                qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
-                for (int k = k0 + 1; k < k0 + S; ++k) {
-                    Cell C;
-                    cell_of(V, qx, qy, qz, C);
-                    if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
-                    qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
+                int pbase = -1;
+                float acc[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+                for (int k = k0; k < k0 + S; ++k) {
+                    const int fx = fixed_floor(qx), fy = fixed_floor(qy), fz = fixed_floor(qz);
+                    const int ix = clampi(fx, -1, V.n[0] - 1), iy = clampi(fy, -1, V.n[1] - 1);
+                    const int iz = clampi(fz, -1, V.n[2] - 1);
+                    float c = ys;
+                    if constexpr (ALPHA) {
+                        Cell C;
+                        float m[6];
+                        cell_of(V, qx, qy, qz, C);
+                        if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
+                        c = coef.next(C, m) * scale;
+                    }
+                    if constexpr (ZP) {
+                        // a sample with every corner outside the volume adds nothing
+                        if (fx != ix || fy != iy || fz != iz) c = 0.0f;
+                    }
                     float w[8];
-                    if constexpr (ALPHA) corner_weights<ZP>(C, coef.next(C, m) * scale, w, m);
-                    else corner_weights<ZP>(C, ys, w, m);
-                    if (same_cell(C, P)) {
+                    weights8(fixed_frac(qx), fixed_frac(qy), fixed_frac(qz), c, w);
+                    qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
+                    const int base = (ix - lo[0]) + __mul24(iy - lo[1], wy) + __mul24(iz - lo[2], wz);
+                    if (base == pbase) {
 #pragma unroll
                         for (int i = 0; i < 8; ++i) acc[i] += w[i];
                     } else {
-                        window_add(win, P, lo, wy, wz, acc);
-                        P = C;
+                        if (pbase >= 0) window_add_at(win, pbase, wy, wz, acc);
+                        pbase = base;
 #pragma unroll
                         for (int i = 0; i < 8; ++i) acc[i] = w[i];
                     }
                 }
-                window_add(win, P, lo, wy, wz, acc);
+                if (pbase >= 0) window_add_at(win, pbase, wy, wz, acc);
             }
             __syncthreads();
             BoxWalk bw(ext);
             for (int i = threadIdx.x; i < n_win; i += kBlock, bw.next()) {
                 const int val = win[i];
-                if (val != 0)
-                    unsafeAtomicAdd(grad + (uint32_t)(lo[2] + bw.z) * sz +
-                                        (uint32_t)(lo[1] + bw.y) * sy + (uint32_t)(lo[0] + bw.x),
-                                    (float)val * inv_scale);
+                if (val == 0) continue;
+                int g[3] = {lo[0] + bw.x, lo[1] + bw.y, lo[2] + bw.z};
+                bool inside = true;
+#pragma unroll
+                for (int a = 0; a < 3; ++a) {
+                    inside = inside && g[a] >= 0 && g[a] <= V.n[a] - 1;
+                    g[a] = clampi(g[a], 0, V.n[a] - 1);
+                }
+                if (ZP && !inside) continue;
+                unsafeAtomicAdd(grad + (uint32_t)g[2] * sz + (uint32_t)g[1] * sy + (uint32_t)g[0],
+                                (float)val * inv_scale);
             }
             __syncthreads();
         } else if (active) {
