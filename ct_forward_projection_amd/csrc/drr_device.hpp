@@ -125,6 +125,8 @@ __device__ inline void view_setup(const float* __restrict__ pose, const Intrinsi
     }
 }
 
+constexpr int64_t kFixedOne = int64_t(1) << 32;   // 1.0 in 32.32 fixed point
+
 __device__ inline int64_t to_fixed(double x) { return __double2ll_rn(x * 4294967296.0); }
 
 // Unit world direction of the ray through pixel (r, c), fp64.

@@ -338,6 +338,28 @@ __device__ inline float staged_value(__amdgpu_buffer_rsrc_t rs, const VolumeDesc
     }
 }
 
+// The eight corners of a cell of the staged box at byte address p (row and
+// slice strides sy, sz in bytes): four pairs adjacent in x.
+__device__ inline void box_corners(const char* p, uint32_t sy, uint32_t sz, CornerVals& c)
+{
+    const float* p00 = reinterpret_cast<const float*>(p);
+    const float* p10 = reinterpret_cast<const float*>(p + sy);
+    const float* p01 = reinterpret_cast<const float*>(p + sz);
+    const float* p11 = reinterpret_cast<const float*>(p + sz + sy);
+    c.v[0] = p00[0]; c.v[1] = p00[1];
+    c.v[2] = p10[0]; c.v[3] = p10[1];
+    c.v[4] = p01[0]; c.v[5] = p01[1];
+    c.v[6] = p11[0]; c.v[7] = p11[1];
+}
+
+// Keeps the per-sample position updates a chain of single adds: without it the
+// compiler rebuilds q + i dq for every unrolled sample from precomputed
+// multiples, which costs more 64-bit adds than it saves.
+__device__ inline void serial_step(int64_t& qx, int64_t& qy, int64_t& qz)
+{
+    asm("" : "+v"(qx), "+v"(qy), "+v"(qz));
+}
+
 template <typename T, int MODE, bool TF>
 __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
     const T* __restrict__ src, uint32_t src_bytes, VolumeDesc V, Intrinsics K,
@@ -408,9 +430,13 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
                                              ch);
             __syncthreads();
             if (hit) {
-                int64_t qx = R.q0[0] + (int64_t)k0 * R.dq[0];
-                int64_t qy = R.q0[1] + (int64_t)k0 * R.dq[1];
-                int64_t qz = R.q0[2] + (int64_t)k0 * R.dq[2];
+                // positions relative to the box corner, so that the fixed-point
+                // floor is the box index itself; byte strides of the box
+                int64_t qx = R.q0[0] + (int64_t)k0 * R.dq[0] - (int64_t)lo[0] * kFixedOne;
+                int64_t qy = R.q0[1] + (int64_t)k0 * R.dq[1] - (int64_t)lo[1] * kFixedOne;
+                int64_t qz = R.q0[2] + (int64_t)k0 * R.dq[2] - (int64_t)lo[2] * kFixedOne;
+                const uint32_t sy = 4u * (uint32_t)ey, sz = 4u * (uint32_t)ez;
+                const char* bx = reinterpret_cast<const char*>(box);
                 int k = k0;
                 for (; k + kInflight <= k0 + S; k += kInflight) {
                     SampleAddr A[kInflight];
@@ -420,19 +446,14 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
                         A[i].fx = fixed_frac(qx);
                         A[i].fy = fixed_frac(qy);
                         A[i].fz = fixed_frac(qz);
-                        A[i].o = (uint32_t)(fixed_floor(qx) - lo[0]) +
-                                 __umul24((uint32_t)(fixed_floor(qy) - lo[1]), (uint32_t)ey) +
-                                 __umul24((uint32_t)(fixed_floor(qz) - lo[2]), (uint32_t)ez);
+                        A[i].o = __umul24((uint32_t)fixed_floor(qz), sz) +
+                                 __umul24((uint32_t)fixed_floor(qy), sy) +
+                                 ((uint32_t)fixed_floor(qx) << 2);
                         qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
+                        serial_step(qx, qy, qz);
                     }
 #pragma unroll
-                    for (int i = 0; i < kInflight; ++i) {
-                        const float* p = box + A[i].o;
-                        c[i].v[0] = p[0];           c[i].v[1] = p[1];
-                        c[i].v[2] = p[ey];          c[i].v[3] = p[ey + 1];
-                        c[i].v[4] = p[ez];          c[i].v[5] = p[ez + 1];
-                        c[i].v[6] = p[ez + ey];     c[i].v[7] = p[ez + ey + 1];
-                    }
+                    for (int i = 0; i < kInflight; ++i) box_corners(bx + A[i].o, sy, sz, c[i]);
 #pragma unroll
                     for (int i = 0; i < kInflight; ++i) {
                         const float val = interpolate(A[i], c[i]);
@@ -445,15 +466,12 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
                     A.fx = fixed_frac(qx);
                     A.fy = fixed_frac(qy);
                     A.fz = fixed_frac(qz);
-                    const float* p = box + (fixed_floor(qx) - lo[0]) +
-                                     __mul24(fixed_floor(qy) - lo[1], ey) +
-                                     __mul24(fixed_floor(qz) - lo[2], ez);
+                    A.o = __umul24((uint32_t)fixed_floor(qz), sz) +
+                          __umul24((uint32_t)fixed_floor(qy), sy) +
+                          ((uint32_t)fixed_floor(qx) << 2);
                     qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
                     CornerVals c;
-                    c.v[0] = p[0];       c.v[1] = p[1];
-                    c.v[2] = p[ey];      c.v[3] = p[ey + 1];
-                    c.v[4] = p[ez];      c.v[5] = p[ez + 1];
-                    c.v[6] = p[ez + ey]; c.v[7] = p[ez + ey + 1];
+                    box_corners(bx + A.o, sy, sz, c);
                     const float val = interpolate(A, c);
                     if constexpr (MODE == kAlpha) composite(val, fdz, tau_c, I_c);
                     else acc[0] += val;
