@@ -360,6 +360,14 @@ __device__ inline void serial_step(int64_t& qx, int64_t& qy, int64_t& qz)
     asm("" : "+v"(qx), "+v"(qy), "+v"(qz));
 }
 
+// The same, placed where the sample's fractions have been taken from the
+// positions: the position registers can then be updated in place.
+__device__ inline void serial_step_after(int64_t& qx, int64_t& qy, int64_t& qz, float tx,
+                                         float ty, float tz)
+{
+    asm("" : "+v"(qx), "+v"(qy), "+v"(qz) : "v"(tx), "v"(ty), "v"(tz));
+}
+
 template <typename T, int MODE, bool TF>
 __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
     const T* __restrict__ src, uint32_t src_bytes, VolumeDesc V, Intrinsics K,
@@ -585,20 +593,22 @@ __device__ inline void scatter_sample_global(float* __restrict__ grad, uint32_t 
 
 // Trilinear weights of one sample scaled by c: w[n] for corner n (bit 0 = x1,
 // bit 1 = y1, bit 2 = z1), the same products as corner_weights without clamps.
-__device__ inline void weights8(float fx, float fy, float fz, float c, float w[8])
+// Add c times the eight trilinear weights of fractions (fx, fy, fz) to acc,
+// corner order x fastest: acc[i] += c w_x(i & 1) w_y((i >> 1) & 1) w_z(i >> 2).
+__device__ inline void add_weights8(float fx, float fy, float fz, float c, float acc[8])
 {
     const float wz1 = c * fz, wz0 = c * (1.0f - fz);
     const float w11 = wz1 * fy, w10 = wz1 * (1.0f - fy);
     const float w01 = wz0 * fy, w00 = wz0 * (1.0f - fy);
     const float fx0 = 1.0f - fx;
-    w[0] = w00 * fx0;
-    w[1] = w00 * fx;
-    w[2] = w01 * fx0;
-    w[3] = w01 * fx;
-    w[4] = w10 * fx0;
-    w[5] = w10 * fx;
-    w[6] = w11 * fx0;
-    w[7] = w11 * fx;
+    acc[0] = fmaf(w00, fx0, acc[0]);
+    acc[1] = fmaf(w00, fx, acc[1]);
+    acc[2] = fmaf(w01, fx0, acc[2]);
+    acc[3] = fmaf(w01, fx, acc[3]);
+    acc[4] = fmaf(w10, fx0, acc[4]);
+    acc[5] = fmaf(w10, fx, acc[5]);
+    acc[6] = fmaf(w11, fx0, acc[6]);
+    acc[7] = fmaf(w11, fx, acc[7]);
 }
 
 // Add eight fixed-point weights at window entry `base` and its corner offsets.
@@ -699,6 +709,9 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
 {
     constexpr bool ZP = CLIP == kClipNearFar;
     constexpr bool ALPHA = MODE == kAlpha;
+    // box clip without compositing: sample positions are taken relative to the
+    // window's corner (the compositing coefficient needs absolute cells)
+    constexpr bool REBASE = !ZP && !ALPHA;
     extern __shared__ int win[];                  // win_cap entries (dynamic LDS)
     __shared__ int red[(kBlock / 64) * 6];
     __shared__ int box[6];
@@ -803,8 +816,11 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 for (int a = 0; a < 3; ++a) {
                     const int64_t qa = R.q0[a] + (int64_t)k0 * R.dq[a];
                     const int64_t qb = R.q0[a] + (int64_t)(k0 + S - 1) * R.dq[a];
-                    const int fa = clampi(fixed_floor(qa), -1, V.n[a] - 1);
-                    const int fb = clampi(fixed_floor(qb), -1, V.n[a] - 1);
+                    int fa = fixed_floor(qa), fb = fixed_floor(qb);
+                    if constexpr (!REBASE) {
+                        fa = clampi(fa, -1, V.n[a] - 1);
+                        fb = clampi(fb, -1, V.n[a] - 1);
+                    }
                     v[a] = min(fa, fb);
                     v[3 + a] = -(max(fa, fb) + 1);
                 }
@@ -826,48 +842,60 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
             __syncthreads();
             if (active) {
                 // the window lives in unclamped index space: a sample's floor
-                // (clamped to [-1, n-1]) places its eight corners at fixed
-                // offsets; entries at -1 or n stand for the clamped edge voxel
-                // (clamp to edge) or for nothing (zero padding) and are mapped
-                // when the window is flushed.  Clamping a floor keeps every
-                // corner on the voxel the clamped corners would hit.
+                // places its eight corners at fixed offsets; entries at -1 or n
+                // stand for the clamped edge voxel (clamp to edge) or for
+                // nothing (zero padding) and are mapped when the window is
+                // flushed.  With box clip every sample lies inside the box
+                // [-0.5, n - 0.5], so its floor is in [-1, n - 1] already, and
+                // the window bounds come from the same unclamped floors of the
+                // chunk's end samples (positions are linear in k, so they bound
+                // every sample between); otherwise floors are clamped to
+                // [-1, n - 1], which keeps every corner on the voxel the clamped
+                // corners would hit.
                 const int wy = ext[0], wz = ext[0] * ext[1];
-                int64_t qx = R.q0[0] + (int64_t)k0 * R.dq[0];
-                int64_t qy = R.q0[1] + (int64_t)k0 * R.dq[1];
-                int64_t qz = R.q0[2] + (int64_t)k0 * R.dq[2];
+                const int64_t shift[3] = {REBASE ? (int64_t)lo[0] * kFixedOne : 0,
+                                          REBASE ? (int64_t)lo[1] * kFixedOne : 0,
+                                          REBASE ? (int64_t)lo[2] * kFixedOne : 0};
+                int64_t qx = R.q0[0] + (int64_t)k0 * R.dq[0] - shift[0];
+                int64_t qy = R.q0[1] + (int64_t)k0 * R.dq[1] - shift[1];
+                int64_t qz = R.q0[2] + (int64_t)k0 * R.dq[2] - shift[2];
                 int pbase = -1;
                 float acc[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
                 for (int k = k0; k < k0 + S; ++k) {
                     const int fx = fixed_floor(qx), fy = fixed_floor(qy), fz = fixed_floor(qz);
-                    const int ix = clampi(fx, -1, V.n[0] - 1), iy = clampi(fy, -1, V.n[1] - 1);
-                    const int iz = clampi(fz, -1, V.n[2] - 1);
                     float c = ys;
-                    if constexpr (ALPHA) {
-                        Cell C;
-                        float m[6];
-                        cell_of(V, qx, qy, qz, C);
-                        if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
-                        c = coef.next(C, m) * scale;
-                    }
-                    if constexpr (ZP) {
-                        // a sample with every corner outside the volume adds nothing
-                        if (fx != ix || fy != iy || fz != iz) c = 0.0f;
-                    }
-                    float w[8];
-                    weights8(fixed_frac(qx), fixed_frac(qy), fixed_frac(qz), c, w);
-                    qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
-                    const int base = (ix - lo[0]) + __mul24(iy - lo[1], wy) + __mul24(iz - lo[2], wz);
-                    if (base == pbase) {
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) acc[i] += w[i];
+                    int base;
+                    if constexpr (REBASE) {
+                        base = fx + __mul24(fy, wy) + __mul24(fz, wz);
                     } else {
-                        if (pbase >= 0) window_add_at(win, pbase, wy, wz, acc);
-                        pbase = base;
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) acc[i] = w[i];
+                        const int ix = clampi(fx, -1, V.n[0] - 1), iy = clampi(fy, -1, V.n[1] - 1);
+                        const int iz = clampi(fz, -1, V.n[2] - 1);
+                        if constexpr (ALPHA) {
+                            Cell C;
+                            float m[6];
+                            cell_of(V, qx, qy, qz, C);
+                            if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
+                            c = coef.next(C, m) * scale;
+                        }
+                        if constexpr (ZP) {
+                            // a sample with every corner outside the volume adds nothing
+                            if (fx != ix || fy != iy || fz != iz) c = 0.0f;
+                        }
+                        base = (ix - lo[0]) + __mul24(iy - lo[1], wy) + __mul24(iz - lo[2], wz);
                     }
+                    const float tx = fixed_frac(qx), ty = fixed_frac(qy), tz = fixed_frac(qz);
+                    serial_step_after(qx, qy, qz, tx, ty, tz);
+                    qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
+                    // consecutive samples in one cell are summed in registers;
+                    // a new cell adds the finished sum to the window
+                    const bool same = base == pbase;
+                    if (!same && pbase >= 0) window_add_at(win, pbase, wy, wz, acc);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] = same ? acc[i] : 0.0f;
+                    add_weights8(tx, ty, tz, c, acc);
+                    pbase = base;
                 }
                 if (pbase >= 0) window_add_at(win, pbase, wy, wz, acc);
             }
