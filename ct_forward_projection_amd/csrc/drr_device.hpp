@@ -224,6 +224,14 @@ __device__ inline float fixed_frac(int64_t q)
 
 __device__ inline int clampi(int i, int lo, int hi) { return min(max(i, lo), hi); }
 
+// Keeps per-sample position updates a chain of single adds: without it the
+// compiler rebuilds q + i dq for every unrolled sample from precomputed
+// multiples, which costs more 64-bit adds than it saves.
+__device__ inline void serial_step(int64_t& qx, int64_t& qy, int64_t& qz)
+{
+    asm("" : "+v"(qx), "+v"(qy), "+v"(qz));
+}
+
 // Clamped trilinear cell of a sample: both corner indices per axis clamped to
 // [0, n-1] (clamp to edge) and the weights of the upper corners.
 struct Cell {

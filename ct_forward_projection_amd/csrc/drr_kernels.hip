@@ -352,14 +352,6 @@ __device__ inline void box_corners(const char* p, uint32_t sy, uint32_t sz, Corn
     c.v[6] = p11[0]; c.v[7] = p11[1];
 }
 
-// Keeps the per-sample position updates a chain of single adds: without it the
-// compiler rebuilds q + i dq for every unrolled sample from precomputed
-// multiples, which costs more 64-bit adds than it saves.
-__device__ inline void serial_step(int64_t& qx, int64_t& qy, int64_t& qz)
-{
-    asm("" : "+v"(qx), "+v"(qy), "+v"(qz));
-}
-
 // The same, placed where the sample's fractions have been taken from the
 // positions: the position registers can then be updated in place.
 __device__ inline void serial_step_after(int64_t& qx, int64_t& qy, int64_t& qz, float tx,

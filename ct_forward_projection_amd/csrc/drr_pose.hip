@@ -23,9 +23,10 @@
 // -t_i e_j, dw/dR_ij = u_i e_j, dC/dt_i = -R_i. (row i), so with y = g dI/ds
 // summed over a view's rays, P = sum y Ac and Q_ij = sum y u_i Bw_j:
 //   dL/dR_ij = -t_i P_j + Q_ij,   dL/dt_i = -sum_a R_ia P_a.
-// The march interpolates in fp32 and accumulates S0, G0 and sum_k k grad mu_k
-// per ray in fp64; the chain rule runs in fp64 and the view sums in fp64
-// atomics.
+// The march steps 32.32 fixed-point positions (re-anchored on fp64 every four
+// samples), interpolates in fp32 and accumulates S0, G0 and sum_k k grad mu_k
+// per ray in fp64 (from fp32 sums of four samples); the chain rule runs in fp64
+// and the view sums in fp64 atomics.
 #include <limits.h>
 
 #include "drr_device.hpp"
@@ -90,10 +91,7 @@ __device__ inline bool ray_frame(const ViewGeom& G, const double Ki[9], const Vo
     return true;
 }
 
-// Sample k's position, evaluated directly in fp64 and rounded once to 32.32
-// fixed point.  The gradient of trilinear mu jumps where a sample crosses a
-// cell face, so positions here must not drift: stepping by a rounded fixed
-// increment, as the value-only kernels do, would let the error grow with k.
+// Sample k's position, evaluated in fp64 and rounded once to 32.32 fixed point.
 __device__ inline int64_t sample_fixed(const RayFrame& F, int a, int k)
 {
     return to_fixed(fma((double)k, F.dq[a], F.q0[a]));
@@ -155,31 +153,48 @@ __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
         const char* base = reinterpret_cast<const char*>(src) + (uint64_t)cvol * b.src_stride;
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)src_bytes, kBufferWord3);
-        // fp64 accumulators: sum grad mu . d telescopes to about mu(exit) - mu(entry),
-        // a small difference of large edge terms that fp32 sums would round away
+        // fp64 ray sums: sum grad mu . d telescopes to about mu(exit) - mu(entry),
+        // a small difference of large edge terms that fp32 sums over a whole ray
+        // would round away (a group of four fp32 terms is summed first)
         double s0 = 0.0, g0[3] = {0.0, 0.0, 0.0}, h1[3] = {0.0, 0.0, 0.0};
+        // sample positions in 32.32 fixed point.  The gradient of trilinear mu
+        // jumps where a sample crosses a cell face, so positions must not
+        // drift from their fp64 values: each group of four starts from its
+        // first sample evaluated in fp64 and rounded once, and steps by the
+        // rounded increment from there (at most 3.5 2^-32 voxel off)
+        const int64_t dqx = to_fixed(F.dq[0]), dqy = to_fixed(F.dq[1]), dqz = to_fixed(F.dq[2]);
         constexpr int kGroup = 4;
         int k = 0;
         for (; k + kGroup <= N; k += kGroup) {
             SampleAddr A[kGroup];
             CornerVals c[kGroup];
+            int64_t qx = sample_fixed(F, 0, k), qy = sample_fixed(F, 1, k), qz = sample_fixed(F, 2, k);
 #pragma unroll
-            for (int i = 0; i < kGroup; ++i)
-                A[i] = sample_addr<T, L>(V, sample_fixed(F, 0, k + i), sample_fixed(F, 1, k + i),
-                                         sample_fixed(F, 2, k + i));
+            for (int i = 0; i < kGroup; ++i) {
+                A[i] = sample_addr<T, L>(V, qx, qy, qz);
+                qx += dqx; qy += dqy; qz += dqz;
+                serial_step(qx, qy, qz);
+            }
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) gather<T, L>(rs, A[i], c[i]);
             __builtin_amdgcn_sched_barrier(0);
+            // the group's sums in fp32 (four terms), then into the ray's fp64 sums
+            float ps = 0.0f, pg[3] = {0.0f, 0.0f, 0.0f}, ph[3] = {0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) {
                 float gq[3];
-                s0 += (double)interpolate_grad(A[i], c[i], gq);
-                const double kd = (double)(k + i);
+                ps += interpolate_grad(A[i], c[i], gq);
 #pragma unroll
                 for (int a = 0; a < 3; ++a) {
-                    g0[a] += (double)gq[a];
-                    h1[a] = fma(kd, (double)gq[a], h1[a]);
+                    pg[a] += gq[a];
+                    ph[a] = fmaf((float)i, gq[a], ph[a]);
                 }
+            }
+            s0 += (double)ps;
+#pragma unroll
+            for (int a = 0; a < 3; ++a) {
+                g0[a] += (double)pg[a];
+                h1[a] = fma((double)k, (double)pg[a], h1[a] + (double)ph[a]);
             }
         }
         for (; k < N; ++k) {
