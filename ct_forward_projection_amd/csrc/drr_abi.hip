@@ -104,12 +104,21 @@ int check_geometry(int nz, int ny, int nx, int elem_bytes, const float* spacing,
     return DRR_OK;
 }
 
-// Corner-cell byte geometry of the volume for cells of elem_bytes elements.
-void set_cells(drr::VolumeDesc& V, int nz, int ny, int nx, int elem_bytes)
+// Byte geometry of what the march reads under `plan`: the linear volume (the
+// caller's, or the fp32 mapped copy when a transfer function maps it) and, with
+// the corner-cell copy, its cells, all of plan.read_elem-byte elements.
+void set_read_geometry(drr::VolumeDesc& V, const drr::RenderPlan& plan)
 {
-    V.cell_row_bytes = (uint32_t)(nx + 1) * 8u * (uint32_t)elem_bytes;
-    V.cell_slice_bytes = (uint32_t)(ny + 1) * V.cell_row_bytes;
-    V.cell_total_bytes = (uint32_t)((long long)(nz + 1) * V.cell_slice_bytes);
+    const uint32_t nx = (uint32_t)V.n[0], ny = (uint32_t)V.n[1], nz = (uint32_t)V.n[2];
+    const uint32_t eb = (uint32_t)plan.read_elem;
+    V.row_bytes = nx * eb;
+    V.slice_bytes = nx * ny * eb;
+    V.total_bytes = (uint32_t)((unsigned long long)nz * ny * nx * eb);
+    if (plan.cells) {
+        V.cell_row_bytes = (nx + 1) * 8u * eb;
+        V.cell_slice_bytes = (ny + 1) * V.cell_row_bytes;
+        V.cell_total_bytes = (uint32_t)((unsigned long long)(nz + 1) * V.cell_slice_bytes);
+    }
 }
 
 // Validation of the front-end options of drr_render / drr_render_backward_volume;
@@ -352,7 +361,7 @@ int drr_forward(const void* volume, int dtype, int nz, int ny, int nx, const flo
     if (plan.workspace_bytes > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
         return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
     if (n_rays == 0) return ok();
-    if (plan.cells) set_cells(a.V, nz, ny, nx, plan.read_elem);
+    set_read_geometry(a.V, plan);
     hipError_t e = drr::launch_forward(a, plan, volume, dtype, workspace, out, line_integral,
                                        static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
@@ -439,7 +448,7 @@ int drr_render(const void* volume, int dtype, int n_volumes, int n_channels, int
     if (plan.workspace_bytes > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
         return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
     if (n_out == 0) return ok();
-    if (plan.cells) set_cells(a.V, nz, ny, nx, plan.read_elem);
+    set_read_geometry(a.V, plan);
     hipError_t e = drr::launch_forward(a, plan, volume, dtype, workspace, out, aux,
                                        static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
@@ -520,7 +529,7 @@ int pose_backward(drr::LaunchArgs& a, const void* volume, int dtype, const float
                     workspace_bytes, need);
     if (!workspace || ((uintptr_t)workspace & 255u))
         return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
-    if (plan.cells) set_cells(a.V, a.V.n[2], a.V.n[1], a.V.n[0], plan.read_elem);
+    set_read_geometry(a.V, plan);
     char* ws = static_cast<char*>(workspace);
     hipError_t e = drr::launch_backward_pose(a, plan, volume, dtype, ws + acc_bytes,
                                              reinterpret_cast<double*>(ws), grad_out, grad_poses,

@@ -145,6 +145,38 @@ def test_render_bf16_hu_volume_with_transfer_function(dev):
         assert forward_rel_err(img, ref32) <= FWD_BF16
 
 
+@pytest.mark.parametrize("mode", [BL, RAW, ALPHA])
+def test_render_bf16_transfer_mapped_linear(dev, mode):
+    """bf16 HU volumes with a transfer function and few samples per cell: the
+    march reads the fp32 mapped linear copy (row and slice strides of fp32, not
+    of the bf16 input); forward, volume gradient and pose gradient."""
+    vol, spacing, K, poses, H, Wd, N, g = problem(355 + mode, N=23, tf=True)
+    bits = W.round_to_bf16_bits(vol)
+    vol_r = (bits.astype(np.uint32) << 16).view(np.float32)
+    transfer = knots(2)
+    name = plan_name(vol, H, Wd, N, poses.shape[0], mode, BOX, 3, bf16=True)
+    say(f"case: bf16 HU + transfer, linear mapped copy, mode={mode} plan={name}")
+    assert name == "mapped linear"
+    img, tau, grad = run_gpu(dev, vol, spacing, K, poses, H, Wd, N, mode, 30.0, BOX, 0.0,
+                             transfer, g, bf16_bits=bits)
+    kw = dict(density_factor=30.0, clip=BOX, margin=0.0, transfer=transfer)
+    ref, ref_tau = oracle.render(vol_r, spacing, K, poses, H, Wd, N, mode, **kw)
+    ref_g = oracle.render_adjoint(vol_r, spacing, K, poses, H, Wd, N, mode, g, **kw)
+    check(img, tau, grad, ref, ref_tau, ref_g, f"bf16 mapped linear m{mode}")
+    if mode == ALPHA:
+        return
+    v = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    gp = drr.drr_render_backward_pose(v, spacing, K, torch.from_numpy(poses).to(dev), H, Wd, N,
+                                      mode, torch.from_numpy(g).to(dev), 30.0, BOX, 0.0, transfer)
+    torch.cuda.synchronize()
+    ref_p = oracle.render_pose_gradient(vol_r, spacing, K, poses, H, Wd, N, mode, g,
+                                        density_factor=30.0, transfer=transfer)
+    got = gp.cpu().double().numpy()
+    errs = [np.abs(got[i] - ref_p[i]).max() / np.abs(ref_p[i]).max() for i in range(len(ref_p))]
+    say(f"bf16 mapped linear m{mode}: pose gradient per-view normwise err max {max(errs):.3e}")
+    assert max(errs) <= GRAD
+
+
 def test_render_bf16_density_without_transfer(dev):
     """bf16 densities read directly (cells keep bf16), near/far and box."""
     vol, spacing, K, poses, H, Wd, N, g = problem(352, N=101)
