@@ -105,15 +105,23 @@ int check_geometry(int nz, int ny, int nx, int elem_bytes, const float* spacing,
 }
 
 // Byte geometry of what the march reads under `plan`: the linear volume (the
-// caller's, or the fp32 mapped copy when a transfer function maps it) and, with
-// the corner-cell copy, its cells, all of plan.read_elem-byte elements.
+// caller's, or the fp32 mapped copy when a transfer function maps it) or its
+// z-pair copy and, with the corner-cell copy, its cells, all of
+// plan.read_elem-byte elements.
 void set_read_geometry(drr::VolumeDesc& V, const drr::RenderPlan& plan)
 {
     const uint32_t nx = (uint32_t)V.n[0], ny = (uint32_t)V.n[1], nz = (uint32_t)V.n[2];
     const uint32_t eb = (uint32_t)plan.read_elem;
-    V.row_bytes = nx * eb;
-    V.slice_bytes = nx * ny * eb;
-    V.total_bytes = (uint32_t)((unsigned long long)nz * ny * nx * eb);
+    if (plan.zpair) {
+        // z-pair copy: nz - 1 slices of (x, y) elements of two values each
+        V.row_bytes = nx * 2u * eb;
+        V.slice_bytes = nx * ny * 2u * eb;
+        V.total_bytes = (uint32_t)((unsigned long long)(nz - 1) * V.slice_bytes);
+    } else {
+        V.row_bytes = nx * eb;
+        V.slice_bytes = nx * ny * eb;
+        V.total_bytes = (uint32_t)((unsigned long long)nz * ny * nx * eb);
+    }
     if (plan.cells) {
         V.cell_row_bytes = (nx + 1) * 8u * eb;
         V.cell_slice_bytes = (ny + 1) * V.cell_row_bytes;

@@ -119,6 +119,42 @@ __global__ __launch_bounds__(256) void drr_cells_kernel(const Tin* __restrict__ 
     }
 }
 
+// Z-pair relayout: element (x, y, z) of the copy, 0 <= z <= nz - 2, holds
+// voxels (x, y, z) and (x, y, z + 1) side by side (mapped by channel c's
+// transfer function into fp32 with TF).  One thread per element, consecutive
+// threads on consecutive x: both reads and the paired write are coalesced.
+// blockIdx.y = channel-volume (b * C + c).
+template <typename Tin, typename Tout, bool TF>
+__global__ __launch_bounds__(256) void drr_zpair_kernel(const Tin* __restrict__ vol, int nx,
+                                                        int ny, int nz, size_t in_stride,
+                                                        Tout* __restrict__ pairs,
+                                                        size_t out_stride, int C, TransferFn tf)
+{
+    static_assert(TF || sizeof(Tin) == sizeof(Tout), "no transfer: pairs keep the dtype");
+    const int cv = (int)blockIdx.y, ch = cv % C;
+    vol += (size_t)cv * in_stride;
+    pairs += (size_t)cv * out_stride;
+    const size_t slice = (size_t)nx * ny;
+    const size_t n = slice * (size_t)(nz - 1);
+    for (size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x; id < n;
+         id += (size_t)gridDim.x * blockDim.x) {
+        Tout lo, hi;
+        if constexpr (TF) {
+            float m;
+            lo = transfer_eval(tf, ch, widen(vol[id]), m);
+            hi = transfer_eval(tf, ch, widen(vol[id + slice]), m);
+        } else {
+            lo = vol[id];
+            hi = vol[id + slice];
+        }
+        if constexpr (sizeof(Tout) == 4) {
+            reinterpret_cast<float2*>(pairs)[id] = make_float2(lo, hi);
+        } else {
+            reinterpret_cast<uint32_t*>(pairs)[id] = (uint32_t)lo | ((uint32_t)hi << 16);
+        }
+    }
+}
+
 // mu = tf(x) for every voxel of every channel-volume (blockIdx.y), fp32 out.
 template <typename Tin>
 __global__ __launch_bounds__(256) void drr_transfer_kernel(const Tin* __restrict__ vol,
@@ -1051,6 +1087,26 @@ static hipError_t launch_cells_typed(const LaunchArgs& a, const RenderPlan& p, c
     return hipGetLastError();
 }
 
+// Z-pair copies of all n_volumes * C channel-volumes into `pairs` (stride
+// per_volume_bytes), mapped by the transfer function when there is one (then fp32).
+template <typename Tin>
+static hipError_t launch_zpair_typed(const LaunchArgs& a, const RenderPlan& p, const Tin* vol,
+                                     void* pairs, hipStream_t stream)
+{
+    const long long n = (long long)a.V.n[0] * a.V.n[1] * (a.V.n[2] - 1);
+    const dim3 grid(grid_blocks(n, 16384), a.n_volumes * a.C);
+    const size_t in_stride = (size_t)a.V.n[0] * a.V.n[1] * a.V.n[2];
+    if (p.mapped)
+        hipLaunchKernelGGL((drr_zpair_kernel<Tin, float, true>), grid, dim3(256), 0, stream, vol,
+                           a.V.n[0], a.V.n[1], a.V.n[2], in_stride, static_cast<float*>(pairs),
+                           p.per_volume_bytes / sizeof(float), a.C, a.tf);
+    else
+        hipLaunchKernelGGL((drr_zpair_kernel<Tin, Tin, false>), grid, dim3(256), 0, stream, vol,
+                           a.V.n[0], a.V.n[1], a.V.n[2], in_stride, static_cast<Tin*>(pairs),
+                           p.per_volume_bytes / sizeof(Tin), a.C, a.tf);
+    return hipGetLastError();
+}
+
 template <typename Tin>
 static hipError_t launch_transfer_typed(const LaunchArgs& a, const RenderPlan& p, const Tin* vol,
                                         float* mu, hipStream_t stream)
@@ -1065,6 +1121,13 @@ static hipError_t launch_transfer_typed(const LaunchArgs& a, const RenderPlan& p
 hipError_t launch_read_copy(const LaunchArgs& a, const RenderPlan& p, const void* vol, int dtype,
                             void* workspace, hipStream_t stream)
 {
+    if (p.zpair) {
+        if (dtype == 0)
+            return launch_zpair_typed<float>(a, p, static_cast<const float*>(vol), workspace,
+                                             stream);
+        return launch_zpair_typed<uint16_t>(a, p, static_cast<const uint16_t*>(vol), workspace,
+                                            stream);
+    }
     if (p.cells) {
         if (dtype == 0)
             return launch_cells_typed<float>(a, p, static_cast<const float*>(vol), workspace,
@@ -1113,8 +1176,18 @@ static hipError_t forward_typed(const LaunchArgs& a, const RenderPlan& p, const 
             launch_staged_mode<Tin, kAlpha>(a, vol, b, out, s_out, stream);
         return hipGetLastError();
     }
-    const uint32_t bytes = p.cells ? a.V.cell_total_bytes : (uint32_t)((size_t)a.V.n[0] * a.V.n[1] *
-                                                                      a.V.n[2] * p.read_elem);
+    const uint32_t bytes = p.cells ? a.V.cell_total_bytes : a.V.total_bytes;
+    if (p.zpair) {
+        hipError_t e = launch_zpair_typed<Tin>(a, p, vol, workspace, stream);
+        if (e != hipSuccess) return e;
+        if (p.mapped)
+            launch_march_mode<float, Layout::ZPair, kClipBox>(
+                a, static_cast<const float*>(workspace), bytes, b, out, s_out, stream);
+        else
+            launch_march_mode<Tin, Layout::ZPair, kClipBox>(
+                a, static_cast<const Tin*>(workspace), bytes, b, out, s_out, stream);
+        return hipGetLastError();
+    }
     if (p.cells) {
         hipError_t e = launch_cells_typed<Tin>(a, p, vol, workspace, stream);
         if (e != hipSuccess) return e;

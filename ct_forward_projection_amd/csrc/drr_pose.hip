@@ -310,6 +310,10 @@ static void pose_typed(const LaunchArgs& a, const RenderPlan& p, const T* src, c
         launch_pose<T, Layout::Cell>(a, src, a.V.cell_total_bytes, b, grad_out, acc, stream);
         return;
     }
+    if (p.zpair) {
+        launch_pose<T, Layout::ZPair>(a, src, a.V.total_bytes, b, grad_out, acc, stream);
+        return;
+    }
     const uint32_t bytes = (uint32_t)((size_t)a.V.n[0] * a.V.n[1] * a.V.n[2] * sizeof(T));
     if (a.V.n[0] >= 2)
         launch_pose<T, Layout::Pair>(a, src, bytes, b, grad_out, acc, stream);
@@ -337,7 +341,7 @@ hipError_t launch_backward_pose(const LaunchArgs& a, const RenderPlan& plan, con
         b.vpv = a.n_views / a.n_volumes;
         b.f = a.f;
         b.margin = a.margin;
-        const void* src = (plan.cells || plan.mapped) ? read_buf : vol;
+        const void* src = (plan.cells || plan.zpair || plan.mapped) ? read_buf : vol;
         if (plan.mapped || dtype == 0)
             pose_typed<float>(a, plan, static_cast<const float*>(src), b, grad_out, acc, stream);
         else

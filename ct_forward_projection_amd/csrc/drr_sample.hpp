@@ -60,14 +60,20 @@ __device__ inline float load_one<uint16_t>(__amdgpu_buffer_rsrc_t rs, uint32_t o
 //   Single (nx == 1): the x corners are read one by one.  8 loads per sample.
 //   Cell   (corner-cell copy): the 8 clamped corners are one 16-byte (bf16) or
 //          two 16-byte (fp32) loads at cell (ix + 1, iy + 1, iz + 1); no clamp.
-enum class Layout { Single, Pair, Cell };
+//   ZPair  (z-pair copy, nx >= 2 and nz >= 2): element (x, y, z) of the copy,
+//          0 <= z <= nz - 2, holds the voxels (x, y, z) and (x, y, z + 1), so
+//          the x-neighbours (xp, xp + 1) of one y row are four values in one
+//          16-byte (fp32) or 8-byte (bf16) load: 2 loads per sample.  x and z
+//          are pinned at the clamped edges as in Pair.
+enum class Layout { Single, Pair, Cell, ZPair };
 
 struct SampleAddr {
     uint32_t o, dy, dz;            // bytes: first row (+ x offset), row steps
     uint32_t x1;                   // Single: byte offset of the x1 corner minus x0
     float fx, fy, fz;
-    float gxs;                     // Pair: 0 where the x weight was pinned at a clamped
-                                   // edge (the field is flat in x there), else 1
+    float gxs;                     // Pair, ZPair: 0 where the x weight was pinned at a
+                                   // clamped edge (the field is flat in x there), else 1
+    float gzs;                     // ZPair: the same for z
     float ex, ey, ez;              // zero padding: 1 - fx, 1 - fy, 1 - fz, exact
 };
 
@@ -98,6 +104,22 @@ __device__ inline SampleAddr sample_addr(const VolumeDesc& V, int64_t qx, int64_
     A.fy = fixed_frac(qy);
     A.fz = fixed_frac(qz);
     A.gxs = 1.0f;
+    A.gzs = 1.0f;
+    if constexpr (L == Layout::ZPair) {
+        // row and slice strides of the z-pair copy (V.row_bytes, V.slice_bytes)
+        const int y0 = clampi(iy, 0, V.n[1] - 1), y1 = clampi(iy + 1, 0, V.n[1] - 1);
+        const int xp = clampi(ix, 0, V.n[0] - 2), zp = clampi(iz, 0, V.n[2] - 2);
+        A.fx = __builtin_amdgcn_fmed3f(A.fx + (float)(ix - xp), 0.0f, 1.0f);
+        A.fz = __builtin_amdgcn_fmed3f(A.fz + (float)(iz - zp), 0.0f, 1.0f);
+        A.gxs = ix == xp ? 1.0f : 0.0f;
+        A.gzs = iz == zp ? 1.0f : 0.0f;
+        A.o = (uint32_t)zp * V.slice_bytes + __umul24((uint32_t)y0, V.row_bytes) +
+              (uint32_t)xp * (uint32_t)(2 * sizeof(T));
+        A.dy = y1 > y0 ? V.row_bytes : 0u;
+        A.dz = A.x1 = 0;
+        static_assert(!ZP, "zero padding reads the corner-cell copy");
+        return A;
+    }
     if constexpr (L == Layout::Cell) {
         // a sample inside the box has -1 <= floor(q) <= n - 1; anything else
         // would fall outside the buffer range and read zeros, never fault
@@ -167,11 +189,44 @@ __device__ inline void load_cell<uint16_t>(__amdgpu_buffer_rsrc_t rs, uint32_t o
     }
 }
 
+// One y row of the z-pair copy at byte offset `off`: corners (x0, x1) x (z0, z1)
+// into c.v[base], c.v[base + 1] (z0) and c.v[base + 4], c.v[base + 5] (z1).
+template <typename T>
+__device__ inline void load_zpair_row(__amdgpu_buffer_rsrc_t rs, uint32_t off, CornerVals& c,
+                                      int base);
+
+template <>
+__device__ inline void load_zpair_row<float>(__amdgpu_buffer_rsrc_t rs, uint32_t off,
+                                             CornerVals& c, int base)
+{
+    const auto a = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+    c.v[base] = __uint_as_float(a[0]);
+    c.v[base + 4] = __uint_as_float(a[1]);
+    c.v[base + 1] = __uint_as_float(a[2]);
+    c.v[base + 5] = __uint_as_float(a[3]);
+}
+
+template <>
+__device__ inline void load_zpair_row<uint16_t>(__amdgpu_buffer_rsrc_t rs, uint32_t off,
+                                                CornerVals& c, int base)
+{
+    const auto a = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 0);
+    c.v[base] = bf16_lo((uint32_t)a[0]);
+    c.v[base + 4] = bf16_hi((uint32_t)a[0]);
+    c.v[base + 1] = bf16_lo((uint32_t)a[1]);
+    c.v[base + 5] = bf16_hi((uint32_t)a[1]);
+}
+
 template <typename T, Layout L>
 __device__ inline void gather(__amdgpu_buffer_rsrc_t rs, const SampleAddr& A, CornerVals& c)
 {
     if constexpr (L == Layout::Cell) {
         load_cell<T>(rs, A.o, c);
+        return;
+    }
+    if constexpr (L == Layout::ZPair) {
+        load_zpair_row<T>(rs, A.o, c, 0);
+        load_zpair_row<T>(rs, A.o + A.dy, c, 2);
         return;
     }
     const uint32_t rows[4] = {A.o, A.o + A.dy, A.o + A.dz, A.o + A.dz + A.dy};
@@ -223,8 +278,9 @@ __device__ inline float interpolate_grad(const SampleAddr& A, const CornerVals& 
     const float gx0 = fmaf(A.fy, dx10 - dx00, dx00), gx1 = fmaf(A.fy, dx11 - dx01, dx01);
     g[0] = A.gxs * fmaf(A.fz, gx1 - gx0, gx0);
     g[1] = fmaf(A.fz, dy1 - dy0, dy0);
-    g[2] = c1 - c0;
-    return fmaf(A.fz, g[2], c0);
+    const float dz = c1 - c0;
+    g[2] = A.gzs * dz;
+    return fmaf(A.fz, dz, c0);
 }
 
 }  // namespace drr

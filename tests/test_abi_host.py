@@ -246,8 +246,15 @@ def test_render_empty_call_and_workspace_queries():
     # near/far: zero-padded corner cells of every channel-volume, 256-byte multiples
     cells = ((9 * 9 * 9 * 8 * 4 + 255) // 256) * 256
     assert q(2, 3, 8, 8, 8, 0, 4, 4, 4, 8, 0, 1, 0, 0) == 6 * cells
-    # a transfer function without cells: the mapped fp32 volumes
+    # a transfer function and few samples per cell: the mapped fp32 volumes
     assert q(1, 2, 8, 8, 8, 1, 1, 4, 4, 8, 0, 0, 3, 0) == 2 * 2048
+    # about one sample per cell or more, but under 16: z-pair copies of
+    # (nz - 1) x ny x nx pairs, of the input dtype or mapped fp32
+    assert q(1, 1, 8, 8, 8, 0, 4, 8, 8, 16, 0, 0, 0, 0) == 8 * 8 * 7 * 2 * 4
+    assert q(1, 1, 8, 8, 8, 1, 4, 8, 8, 16, 0, 0, 0, 0) == 8 * 8 * 7 * 2 * 2
+    assert q(2, 1, 8, 8, 8, 1, 8, 8, 8, 16, 0, 0, 3, 0) == 2 * 8 * 8 * 7 * 2 * 4
+    # a volume one voxel deep has no z-pairs: the volume itself
+    assert q(1, 1, 1, 8, 8, 0, 4, 8, 8, 4, 0, 0, 0, 0) == 0
     # compositing backward with a transfer function: mapped fp32 volumes; else none
     assert q(1, 2, 8, 8, 8, 0, 1, 4, 4, 8, 2, 0, 3, 1) == 2 * 2048
     assert q(1, 2, 8, 8, 8, 0, 1, 4, 4, 8, 0, 0, 3, 1) == 0

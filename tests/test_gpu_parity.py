@@ -403,7 +403,7 @@ def test_pose_gradient_random(dev, seed, mode, shape, det, n):
 
 
 def test_pose_gradient_batch_workload(dev, batch_workload):
-    """The 16-view 200x200 batch (x-pair reads in fp32, corner cells in bf16)."""
+    """The 16-view 200x200 batch (z-pair copies in fp32 and bf16)."""
     w = batch_workload
     g = np.random.default_rng(71).uniform(-1, 1, size=(16, 200, 200)).astype(np.float32)
     say("case: pose gradient, 16-view batch")

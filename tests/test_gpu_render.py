@@ -5,8 +5,8 @@ Covers volume and channel batches (N = B * views_per_vol views), the density
 factor, all three outputs (Beer-Lambert, line integral, front-to-back alpha
 compositing), both clip modes (per-ray box; per-view near/far with zero padding)
 and the per-channel transfer function, on every read plan the library picks
-(the caller's volume, its mapped fp32 copy, corner cells, zero-padded or mapped
-cells).  Bars as elsewhere: forward max |g - o| / max(|o|, 1e-3 max|o|) <= 1e-5
+(the caller's volume, its mapped fp32 copy, z-pair copies plain or mapped,
+corner cells, zero-padded or mapped cells, LDS-staged boxes).  Bars as elsewhere: forward max |g - o| / max(|o|, 1e-3 max|o|) <= 1e-5
 for fp32 (1e-2 for bf16 against the fp32 volume, 1e-5 against the bf16-rounded
 one), gradients normwise <= 1e-4.
 """
@@ -80,8 +80,11 @@ def plan_name(vol, H, Wd, N, V, mode, clip, nk, bf16=False):
     elem = 4 if (nk or not bf16) else 2
     cells = B * C * (((nx + 1) * (ny + 1) * (nz + 1) * 8 * elem + 255) // 256 * 256)
     lin = B * C * ((nx * ny * nz * 4 + 255) // 256 * 256)
+    zpair = B * C * ((nx * ny * (nz - 1) * 2 * elem + 255) // 256 * 256)
     if ws == cells:
         return "mapped cells" if nk else "cells"
+    if ws == zpair and nz >= 2:
+        return "mapped z-pairs" if nk else "z-pairs"
     if nk:
         assert ws == lin
         return "mapped linear"
@@ -107,8 +110,9 @@ def check(img, tau, grad, ref, ref_tau, ref_grad, what, bar=FWD_F32):
 @pytest.mark.parametrize("mode", [BL, RAW, ALPHA])
 def test_render_random_batches(dev, mode, clip, tf, N):
     """2 volumes x 2 channels, 2 views each, ragged 13 x 10 x 17 volume and
-    19 x 23 detector, anisotropic voxels; N = 37 reads the volume (or its mapped
-    copy) directly, N = 101 reuses cells enough for the corner-cell copy."""
+    19 x 23 detector, anisotropic voxels; N = 37 reads the z-pair copy (mapped
+    with a transfer function), N = 101 reuses cells enough for the corner-cell
+    copy (the near/far mode always reads zero-padded cells)."""
     seed = 300 + 10 * mode + 4 * clip + 2 * tf + (N > 50)
     vol, spacing, K, poses, H, Wd, N, g = problem(seed, N=N, tf=tf)
     C = vol.shape[1]
@@ -147,10 +151,10 @@ def test_render_bf16_hu_volume_with_transfer_function(dev):
 
 @pytest.mark.parametrize("mode", [BL, RAW, ALPHA])
 def test_render_bf16_transfer_mapped_linear(dev, mode):
-    """bf16 HU volumes with a transfer function and few samples per cell: the
-    march reads the fp32 mapped linear copy (row and slice strides of fp32, not
-    of the bf16 input); forward, volume gradient and pose gradient."""
-    vol, spacing, K, poses, H, Wd, N, g = problem(355 + mode, N=23, tf=True)
+    """bf16 HU volumes with a transfer function and under one sample per cell:
+    the march reads the fp32 mapped linear copy (row and slice strides of fp32,
+    not of the bf16 input); forward, volume gradient and pose gradient."""
+    vol, spacing, K, poses, H, Wd, N, g = problem(355 + mode, det=(5, 7), N=23, tf=True)
     bits = W.round_to_bf16_bits(vol)
     vol_r = (bits.astype(np.uint32) << 16).view(np.float32)
     transfer = knots(2)
@@ -174,6 +178,38 @@ def test_render_bf16_transfer_mapped_linear(dev, mode):
     got = gp.cpu().double().numpy()
     errs = [np.abs(got[i] - ref_p[i]).max() / np.abs(ref_p[i]).max() for i in range(len(ref_p))]
     say(f"bf16 mapped linear m{mode}: pose gradient per-view normwise err max {max(errs):.3e}")
+    assert max(errs) <= GRAD
+
+
+@pytest.mark.parametrize("tf", [False, True])
+@pytest.mark.parametrize("mode", [BL, RAW, ALPHA])
+def test_render_sparse_rays_read_the_volume(dev, mode, tf):
+    """Under one sample per cell (5 x 7 detectors, N = 23) no copy pays: the
+    march reads the caller's volume, or its mapped fp32 copy, as x-pairs;
+    forward, volume gradient and pose gradient."""
+    seed = 360 + 2 * mode + tf
+    vol, spacing, K, poses, H, Wd, N, g = problem(seed, det=(5, 7), N=23, tf=tf)
+    transfer = knots(2) if tf else None
+    f = 30.0 if tf else 1.1
+    name = plan_name(vol, H, Wd, N, poses.shape[0], mode, BOX, 3 if tf else 0)
+    say(f"case: sparse rays mode={mode} tf={tf} plan={name} seed={seed}")
+    assert name == ("mapped linear" if tf else "caller's volume")
+    img, tau, grad = run_gpu(dev, vol, spacing, K, poses, H, Wd, N, mode, f, BOX, 0.0, transfer, g)
+    kw = dict(density_factor=f, clip=BOX, margin=0.0, transfer=transfer)
+    ref, ref_tau = oracle.render(vol, spacing, K, poses, H, Wd, N, mode, **kw)
+    ref_g = oracle.render_adjoint(vol, spacing, K, poses, H, Wd, N, mode, g, **kw)
+    check(img, tau, grad, ref, ref_tau, ref_g, f"sparse m{mode} tf{int(tf)}")
+    if mode == ALPHA:
+        return
+    gp = drr.drr_render_backward_pose(torch.from_numpy(vol).to(dev), spacing, K,
+                                      torch.from_numpy(poses).to(dev), H, Wd, N, mode,
+                                      torch.from_numpy(g).to(dev), f, BOX, 0.0, transfer)
+    torch.cuda.synchronize()
+    ref_p = oracle.render_pose_gradient(vol, spacing, K, poses, H, Wd, N, mode, g,
+                                        density_factor=f, transfer=transfer)
+    got = gp.cpu().double().numpy()
+    errs = [np.abs(got[i] - ref_p[i]).max() / np.abs(ref_p[i]).max() for i in range(len(ref_p))]
+    say(f"sparse m{mode} tf{int(tf)}: pose gradient per-view normwise err max {max(errs):.3e}")
     assert max(errs) <= GRAD
 
 
@@ -284,7 +320,8 @@ def test_render_edge_cases(dev):
 def test_render_pose_gradient(dev, mode, tf, N):
     """Pose gradients of batched renders (2 volumes x 2 channels, 2 views each,
     density factor, transfer function) against the oracle, per view normwise
-    over the twelve entries; N = 101 reads (mapped) corner cells."""
+    over the twelve entries; N = 37 reads (mapped) z-pairs, N = 101 (mapped)
+    corner cells."""
     seed = 400 + 4 * mode + 2 * tf + (N > 50)
     vol, spacing, K, poses, H, Wd, N, g = problem(seed, N=N, tf=tf)
     transfer = knots(2) if tf else None
