@@ -884,46 +884,63 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 const int64_t shift[3] = {REBASE ? (int64_t)lo[0] * kFixedOne : 0,
                                           REBASE ? (int64_t)lo[1] * kFixedOne : 0,
                                           REBASE ? (int64_t)lo[2] * kFixedOne : 0};
-                int64_t qx = R.q0[0] + (int64_t)k0 * R.dq[0] - shift[0];
-                int64_t qy = R.q0[1] + (int64_t)k0 * R.dq[1] - shift[1];
-                int64_t qz = R.q0[2] + (int64_t)k0 * R.dq[2] - shift[2];
+                // Without compositing the order of a chunk's samples is free:
+                // the four lanes of each 2 x 2 block of the wave's pixel lattice
+                // (neighbouring rays, often in the same cell at the same step)
+                // walk the chunk's quarters starting from different ones, so
+                // that one LDS atomic instruction rarely has several lanes on one
+                // address (those serialise).  Compositing visits samples in order.
+                constexpr int kParts = ALPHA ? 1 : 4;
+                const int lane = (int)threadIdx.x & 63;
+                const int first = ALPHA ? 0 : ((lane & 1) | ((lane >> 2) & 2));
+                const int part = (S + kParts - 1) / kParts;
                 int pbase = -1;
                 float acc[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-                for (int k = k0; k < k0 + S; ++k) {
-                    const int fx = fixed_floor(qx), fy = fixed_floor(qy), fz = fixed_floor(qz);
-                    float c = ys;
-                    int base;
-                    if constexpr (REBASE) {
-                        base = fx + __mul24(fy, wy) + __mul24(fz, wz);
-                    } else {
-                        const int ix = clampi(fx, -1, V.n[0] - 1), iy = clampi(fy, -1, V.n[1] - 1);
-                        const int iz = clampi(fz, -1, V.n[2] - 1);
-                        if constexpr (ALPHA) {
-                            Cell C;
-                            float m[6];
-                            cell_of(V, qx, qy, qz, C);
-                            if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
-                            c = coef.next(C, m) * scale;
+                for (int r = 0; r < kParts; ++r) {
+                    const int ka = k0 + ((first + r) & (kParts - 1)) * part;
+                    const int kb = min(ka + part, k0 + S);
+                    int64_t qx = R.q0[0] + (int64_t)ka * R.dq[0] - shift[0];
+                    int64_t qy = R.q0[1] + (int64_t)ka * R.dq[1] - shift[1];
+                    int64_t qz = R.q0[2] + (int64_t)ka * R.dq[2] - shift[2];
+                    for (int k = ka; k < kb; ++k) {
+                        const int fx = fixed_floor(qx), fy = fixed_floor(qy), fz = fixed_floor(qz);
+                        float c = ys;
+                        int base;
+                        if constexpr (REBASE) {
+                            base = fx + __mul24(fy, wy) + __mul24(fz, wz);
+                        } else {
+                            const int ix = clampi(fx, -1, V.n[0] - 1);
+                            const int iy = clampi(fy, -1, V.n[1] - 1);
+                            const int iz = clampi(fz, -1, V.n[2] - 1);
+                            if constexpr (ALPHA) {
+                                Cell C;
+                                float m[6];
+                                cell_of(V, qx, qy, qz, C);
+                                if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
+                                c = coef.next(C, m) * scale;
+                            }
+                            if constexpr (ZP) {
+                                // a sample with every corner outside the volume adds nothing
+                                if (fx != ix || fy != iy || fz != iz) c = 0.0f;
+                            }
+                            base = (ix - lo[0]) + __mul24(iy - lo[1], wy) +
+                                   __mul24(iz - lo[2], wz);
                         }
-                        if constexpr (ZP) {
-                            // a sample with every corner outside the volume adds nothing
-                            if (fx != ix || fy != iy || fz != iz) c = 0.0f;
-                        }
-                        base = (ix - lo[0]) + __mul24(iy - lo[1], wy) + __mul24(iz - lo[2], wz);
-                    }
-                    const float tx = fixed_frac(qx), ty = fixed_frac(qy), tz = fixed_frac(qz);
-                    serial_step_after(qx, qy, qz, tx, ty, tz);
-                    qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
-                    // consecutive samples in one cell are summed in registers;
-                    // a new cell adds the finished sum to the window
-                    const bool same = base == pbase;
-                    if (!same && pbase >= 0) window_add_at(win, pbase, wy, wz, acc);
+                        const float tx = fixed_frac(qx), ty = fixed_frac(qy);
+                        const float tz = fixed_frac(qz);
+                        serial_step_after(qx, qy, qz, tx, ty, tz);
+                        qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
+                        // consecutive samples in one cell are summed in registers;
+                        // a new cell adds the finished sum to the window
+                        const bool same = base == pbase;
+                        if (!same && pbase >= 0) window_add_at(win, pbase, wy, wz, acc);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[i] = same ? acc[i] : 0.0f;
-                    add_weights8(tx, ty, tz, c, acc);
-                    pbase = base;
+                        for (int i = 0; i < 8; ++i) acc[i] = same ? acc[i] : 0.0f;
+                        add_weights8(tx, ty, tz, c, acc);
+                        pbase = base;
+                    }
                 }
                 if (pbase >= 0) window_add_at(win, pbase, wy, wz, acc);
             }
