@@ -639,17 +639,27 @@ __device__ inline void add_weights8(float fx, float fy, float fz, float c, float
     acc[7] = fmaf(w11, fx, acc[7]);
 }
 
+// Fixed-point value of a register sum for the window, rounded to nearest.
+// TRUNC: the sum already carries +-1/2 with the sign of all its terms, so
+// truncation toward zero rounds it (half away from zero) in one conversion.
+template <bool TRUNC>
+__device__ inline int to_window(float w)
+{
+    return TRUNC ? (int)w : __float2int_rn(w);
+}
+
 // Add eight fixed-point weights at window entry `base` and its corner offsets.
+template <bool TRUNC = false>
 __device__ inline void window_add_at(int* win, int base, int wy, int wz, const float w[8])
 {
-    atomicAdd(&win[base], __float2int_rn(w[0]));
-    atomicAdd(&win[base + 1], __float2int_rn(w[1]));
-    atomicAdd(&win[base + wy], __float2int_rn(w[2]));
-    atomicAdd(&win[base + wy + 1], __float2int_rn(w[3]));
-    atomicAdd(&win[base + wz], __float2int_rn(w[4]));
-    atomicAdd(&win[base + wz + 1], __float2int_rn(w[5]));
-    atomicAdd(&win[base + wz + wy], __float2int_rn(w[6]));
-    atomicAdd(&win[base + wz + wy + 1], __float2int_rn(w[7]));
+    atomicAdd(&win[base], to_window<TRUNC>(w[0]));
+    atomicAdd(&win[base + 1], to_window<TRUNC>(w[1]));
+    atomicAdd(&win[base + wy], to_window<TRUNC>(w[2]));
+    atomicAdd(&win[base + wy + 1], to_window<TRUNC>(w[3]));
+    atomicAdd(&win[base + wz], to_window<TRUNC>(w[4]));
+    atomicAdd(&win[base + wz + 1], to_window<TRUNC>(w[5]));
+    atomicAdd(&win[base + wz + wy], to_window<TRUNC>(w[6]));
+    atomicAdd(&win[base + wz + wy + 1], to_window<TRUNC>(w[7]));
 }
 
 // Per-sample coefficient of the compositing backward (MODE = kAlpha).  For
@@ -895,9 +905,13 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 const int first = ALPHA ? 0 : ((lane & 1) | ((lane >> 2) & 2));
                 const int part = (S + kParts - 1) / kParts;
                 int pbase = -1;
+                // a cell's register sums start at 0, or, without compositing
+                // (one coefficient per ray), at +-1/2 with its sign, which lets
+                // the window conversion truncate (see to_window)
+                const float start = REBASE ? copysignf(0.5f, ys) : 0.0f;
                 float acc[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+                for (int i = 0; i < 8; ++i) acc[i] = start;
                 for (int r = 0; r < kParts; ++r) {
                     const int ka = k0 + ((first + r) & (kParts - 1)) * part;
                     const int kb = min(ka + part, k0 + S);
@@ -935,14 +949,14 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                         // consecutive samples in one cell are summed in registers;
                         // a new cell adds the finished sum to the window
                         const bool same = base == pbase;
-                        if (!same && pbase >= 0) window_add_at(win, pbase, wy, wz, acc);
+                        if (!same && pbase >= 0) window_add_at<REBASE>(win, pbase, wy, wz, acc);
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) acc[i] = same ? acc[i] : 0.0f;
+                        for (int i = 0; i < 8; ++i) acc[i] = same ? acc[i] : start;
                         add_weights8(tx, ty, tz, c, acc);
                         pbase = base;
                     }
                 }
-                if (pbase >= 0) window_add_at(win, pbase, wy, wz, acc);
+                if (pbase >= 0) window_add_at<REBASE>(win, pbase, wy, wz, acc);
             }
             __syncthreads();
             BoxWalk bw(ext);
