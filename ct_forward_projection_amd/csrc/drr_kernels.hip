@@ -461,7 +461,19 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
         if (vol_cells <= kStageCap) {
             const int n_box = (int)vol_cells;
             BoxWalk bw(ext);
-            for (int i = threadIdx.x; i < n_box; i += kBlock, bw.next())
+            int i = threadIdx.x;
+            // eight loads in flight per thread before the first LDS write
+            constexpr int kFill = 8;
+            for (; i + (kFill - 1) * kBlock < n_box; i += kFill * kBlock) {
+                float v[kFill];
+#pragma unroll
+                for (int u = 0; u < kFill; ++u, bw.next())
+                    v[u] = staged_value<T, TF>(rs, V, lo[0] + bw.x, lo[1] + bw.y, lo[2] + bw.z,
+                                               tf, ch);
+#pragma unroll
+                for (int u = 0; u < kFill; ++u) box[i + u * kBlock] = v[u];
+            }
+            for (; i < n_box; i += kBlock, bw.next())
                 box[i] = staged_value<T, TF>(rs, V, lo[0] + bw.x, lo[1] + bw.y, lo[2] + bw.z, tf,
                                              ch);
             __syncthreads();
