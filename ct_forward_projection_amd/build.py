@@ -18,7 +18,8 @@ SOURCES = [os.path.join(CSRC, "drr_kernels.hip"), os.path.join(CSRC, "drr_pose.h
            os.path.join(CSRC, "drr_siddon.hip"), os.path.join(CSRC, "drr_camera.hip"),
            os.path.join(CSRC, "drr_noise.hip"), os.path.join(CSRC, "drr_abi.hip")]
 HEADERS = [os.path.join(CSRC, "drr_device.hpp"), os.path.join(CSRC, "drr_internal.hpp"),
-           os.path.join(CSRC, "drr_sample.hpp"), os.path.join(CSRC, "drr_window.hpp"),
+           os.path.join(CSRC, "drr_sample.hpp"), os.path.join(CSRC, "drr_stage.hpp"),
+           os.path.join(CSRC, "drr_window.hpp"),
            os.path.join(os.path.dirname(HERE), "include", "drr.h")]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -340,7 +340,7 @@ size_t drr_workspace_bytes(int nz, int ny, int nx, int dtype, int n_views, int d
     if (for_backward == DRR_WORKSPACE_VOLUME_BACKWARD) return 0;
     const bool fwd = for_backward == DRR_WORKSPACE_FORWARD;
     const size_t plan = drr::plan_render(1, 1, nz, ny, nx, dtype == DRR_F32 ? 4 : 2, n_views,
-                                         det_h, det_w, n_samples, drr::kClipBox, false, fwd)
+                                         det_h, det_w, n_samples, drr::kClipBox, false, true)
                             .workspace_bytes;
     if (for_backward == DRR_WORKSPACE_POSE_BACKWARD) return drr::pose_acc_bytes(n_views) + plan;
     return fwd ? plan : 0;
@@ -421,7 +421,7 @@ size_t drr_render_workspace_bytes(int n_volumes, int n_channels, int nz, int ny,
     const bool fwd = for_backward == DRR_WORKSPACE_FORWARD;
     const size_t plan = drr::plan_render(n_volumes, n_channels, nz, ny, nx,
                                          dtype == DRR_F32 ? 4 : 2, n_views, det_h, det_w,
-                                         n_samples, clip, has_tf, fwd)
+                                         n_samples, clip, has_tf, true)
                             .workspace_bytes;
     if (for_backward == DRR_WORKSPACE_POSE_BACKWARD) return drr::pose_acc_bytes(n_views) + plan;
     return fwd ? plan : 0;
@@ -526,7 +526,7 @@ int pose_backward(drr::LaunchArgs& a, const void* volume, int dtype, const float
     const int eb = dtype == DRR_F32 ? 4 : 2;
     const drr::RenderPlan plan =
         drr::plan_render(a.n_volumes, a.C, a.V.n[2], a.V.n[1], a.V.n[0], eb, a.n_views, a.H, a.W,
-                         a.N, drr::kClipBox, a.has_tf);
+                         a.N, drr::kClipBox, a.has_tf, true);
     if (!plan.fits)
         return fail(DRR_ERR_UNSUPPORTED, "one channel-volume of the march's copy exceeds 4 GiB");
     const size_t acc_bytes = drr::pose_acc_bytes(a.n_views);

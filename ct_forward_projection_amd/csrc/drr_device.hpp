@@ -232,6 +232,14 @@ __device__ inline void serial_step(int64_t& qx, int64_t& qy, int64_t& qz)
     asm("" : "+v"(qx), "+v"(qy), "+v"(qz));
 }
 
+// The same, placed where a sample's fractions have been taken from the
+// positions: the position registers can then be updated in place.
+__device__ inline void serial_step_after(int64_t& qx, int64_t& qy, int64_t& qz, float tx,
+                                         float ty, float tz)
+{
+    asm("" : "+v"(qx), "+v"(qy), "+v"(qz) : "v"(tx), "v"(ty), "v"(tz));
+}
+
 // Clamped trilinear cell of a sample: both corner indices per axis clamped to
 // [0, n-1] (clamp to edge) and the weights of the upper corners.
 struct Cell {

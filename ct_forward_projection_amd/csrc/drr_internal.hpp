@@ -66,8 +66,8 @@ struct RenderPlan {
     bool fits;               // every channel-volume fits 32-bit byte offsets
 };
 
-// The forward (for_forward) may instead stage boxes of the caller's volumes
-// in LDS, tile by tile (box clip, one lane per ray, i.e. launches of at least
+// The forward and the pose gradient (allow_staged) may instead stage boxes of
+// the caller's volumes in LDS, tile by tile (box clip, one lane per ray, i.e. launches of at least
 // 65,536 rays): that needs neither a relayout pass nor a workspace, and the
 // transfer function is applied as the boxes are filled.  Staging pays when the
 // rays of one tile are dense against the voxels, which the samples one view
@@ -94,7 +94,7 @@ constexpr double kZPairMinReuse = 4.0;
 
 inline RenderPlan plan_render(int n_volumes, int C, int nz, int ny, int nx, int elem_bytes,
                               int n_views, int H, int W, int N, int clip, bool has_tf,
-                              bool for_forward = false)
+                              bool allow_staged = false)
 {
     RenderPlan p{};
     p.mapped = has_tf;
@@ -109,7 +109,7 @@ inline RenderPlan plan_render(int n_volumes, int C, int nz, int ny, int nx, int 
     const bool cells_fit = cell_bytes < 4294967040.0;
     const bool reuse = rays_per_volume > 0 && samples_per_cell >= min_reuse;
     const double view_reuse = (double)H * (double)W * (double)N / n_cells;
-    if (for_forward && clip == kClipBox && view_reuse >= kStagedMinViewReuse &&
+    if (allow_staged && clip == kClipBox && view_reuse >= kStagedMinViewReuse &&
         (long long)n_views * C * H * W >= kStagedMinRays) {
         p.staged = true;
         p.mapped = false;

@@ -39,29 +39,10 @@
 #include "drr_device.hpp"
 #include "drr_internal.hpp"
 #include "drr_sample.hpp"
+#include "drr_stage.hpp"
 #include "drr_window.hpp"
 
 namespace drr {
-
-// Value of one voxel as fp32 (bf16 widens exactly).
-__device__ inline float widen(float x) { return x; }
-__device__ inline float widen(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
-
-// The transfer function of channel ch at x (segment search over uniform knots,
-// so every knot is a scalar operand); slope receives the segment's slope.
-__device__ inline float transfer_eval(const TransferFn& T, int ch, float x, float& slope)
-{
-    const int b = ch * T.knots;
-    float x0 = T.xp[b], y0 = T.yp[b], m = T.m[b];
-    for (int i = 1; i < T.knots - 1; ++i) {
-        const bool up = x >= T.xp[b + i];
-        x0 = up ? T.xp[b + i] : x0;
-        y0 = up ? T.yp[b + i] : y0;
-        m = up ? T.m[b + i] : m;
-    }
-    slope = m;
-    return fmaf(m, x - x0, y0);
-}
 
 // Corner-cell relayout: cell (i, j, k), 0 <= i <= nx etc., holds the eight
 // corners (x0, x1) x (y0, y1) x (z0, z1) of the trilinear cell whose low corner
@@ -356,46 +337,6 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
 // fits, doubled while it has room); a chunk whose box does not fit even for
 // one sample gathers its corners from global memory.  No relayout pass and no
 // workspace.
-constexpr int kStageCap = 8192;              // fp32 entries of the staged box (32 KB)
-
-template <typename T, bool TF>
-__device__ inline float staged_value(__amdgpu_buffer_rsrc_t rs, const VolumeDesc& V, int x,
-                                     int y, int z, const TransferFn& tf, int ch)
-{
-    const uint32_t off = (uint32_t)clampi(z, 0, V.n[2] - 1) * (uint32_t)V.n[1] * (uint32_t)V.n[0] +
-                         (uint32_t)clampi(y, 0, V.n[1] - 1) * (uint32_t)V.n[0] +
-                         (uint32_t)clampi(x, 0, V.n[0] - 1);
-    const float v = load_one<T>(rs, off * (uint32_t)sizeof(T));
-    if constexpr (TF) {
-        float m;
-        return transfer_eval(tf, ch, v, m);
-    } else {
-        return v;
-    }
-}
-
-// The eight corners of a cell of the staged box at byte address p (row and
-// slice strides sy, sz in bytes): four pairs adjacent in x.
-__device__ inline void box_corners(const char* p, uint32_t sy, uint32_t sz, CornerVals& c)
-{
-    const float* p00 = reinterpret_cast<const float*>(p);
-    const float* p10 = reinterpret_cast<const float*>(p + sy);
-    const float* p01 = reinterpret_cast<const float*>(p + sz);
-    const float* p11 = reinterpret_cast<const float*>(p + sz + sy);
-    c.v[0] = p00[0]; c.v[1] = p00[1];
-    c.v[2] = p10[0]; c.v[3] = p10[1];
-    c.v[4] = p01[0]; c.v[5] = p01[1];
-    c.v[6] = p11[0]; c.v[7] = p11[1];
-}
-
-// The same, placed where the sample's fractions have been taken from the
-// positions: the position registers can then be updated in place.
-__device__ inline void serial_step_after(int64_t& qx, int64_t& qy, int64_t& qz, float tx,
-                                         float ty, float tz)
-{
-    asm("" : "+v"(qx), "+v"(qy), "+v"(qz) : "v"(tx), "v"(ty), "v"(tz));
-}
-
 template <typename T, int MODE, bool TF>
 __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
     const T* __restrict__ src, uint32_t src_bytes, VolumeDesc V, Intrinsics K,
@@ -432,50 +373,27 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
         S = min(S, N - k0);
         int ext[3] = {1, 1, 1}, lo[3] = {0, 0, 0};
         long long vol_cells = 1;
+        bool any;
         for (;;) {
-            // unclamped floor indices of the chunk's end samples, and one past
-            int v[6] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+            // unclamped floor indices bounding the chunk's samples (its end samples)
+            int lo_f[3] = {INT_MAX, INT_MAX, INT_MAX}, hi_f[3] = {INT_MAX, INT_MAX, INT_MAX};
             if (hit) {
 #pragma unroll
                 for (int a = 0; a < 3; ++a) {
                     const int fa = fixed_floor(R.q0[a] + (int64_t)k0 * R.dq[a]);
                     const int fb = fixed_floor(R.q0[a] + (int64_t)(k0 + S - 1) * R.dq[a]);
-                    v[a] = min(fa, fb);
-                    v[3 + a] = -(max(fa, fb) + 1);
+                    lo_f[a] = min(fa, fb);
+                    hi_f[a] = max(fa, fb);
                 }
             }
-            block_min6(v, red, bb);
-            if (bb[0] == INT_MAX) break;             // no ray of this tile hits the box
-            vol_cells = 1;
-#pragma unroll
-            for (int a = 0; a < 3; ++a) {
-                lo[a] = bb[a];
-                ext[a] = max(-bb[3 + a] - bb[a] + 1, 1);
-                vol_cells *= ext[a];
-            }
-            if (vol_cells <= kStageCap || S == 1) break;
+            any = chunk_box(lo_f, hi_f, red, bb, lo, ext, vol_cells);
+            if (!any || vol_cells <= kStageCap || S == 1) break;
             S = max(1, S >> 1);
         }
-        if (bb[0] == INT_MAX) break;
+        if (!any) break;                             // no ray of this tile hits the box
         const int ey = ext[0], ez = ext[0] * ext[1];
         if (vol_cells <= kStageCap) {
-            const int n_box = (int)vol_cells;
-            BoxWalk bw(ext);
-            int i = threadIdx.x;
-            // eight loads in flight per thread before the first LDS write
-            constexpr int kFill = 8;
-            for (; i + (kFill - 1) * kBlock < n_box; i += kFill * kBlock) {
-                float v[kFill];
-#pragma unroll
-                for (int u = 0; u < kFill; ++u, bw.next())
-                    v[u] = staged_value<T, TF>(rs, V, lo[0] + bw.x, lo[1] + bw.y, lo[2] + bw.z,
-                                               tf, ch);
-#pragma unroll
-                for (int u = 0; u < kFill; ++u) box[i + u * kBlock] = v[u];
-            }
-            for (; i < n_box; i += kBlock, bw.next())
-                box[i] = staged_value<T, TF>(rs, V, lo[0] + bw.x, lo[1] + bw.y, lo[2] + bw.z, tf,
-                                             ch);
+            stage_fill<T, TF>(box, (int)vol_cells, rs, V, lo, ext, tf, ch);
             __syncthreads();
             if (hit) {
                 // positions relative to the box corner, so that the fixed-point
@@ -494,9 +412,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
                         A[i].fx = fixed_frac(qx);
                         A[i].fy = fixed_frac(qy);
                         A[i].fz = fixed_frac(qz);
-                        A[i].o = __umul24((uint32_t)fixed_floor(qz), sz) +
-                                 __umul24((uint32_t)fixed_floor(qy), sy) +
-                                 ((uint32_t)fixed_floor(qx) << 2);
+                        A[i].o = box_offset(qx, qy, qz, sy, sz);
                         qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
                         serial_step(qx, qy, qz);
                     }
@@ -514,9 +430,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
                     A.fx = fixed_frac(qx);
                     A.fy = fixed_frac(qy);
                     A.fz = fixed_frac(qz);
-                    A.o = __umul24((uint32_t)fixed_floor(qz), sz) +
-                          __umul24((uint32_t)fixed_floor(qy), sy) +
-                          ((uint32_t)fixed_floor(qx) << 2);
+                    A.o = box_offset(qx, qy, qz, sy, sz);
                     qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
                     CornerVals c;
                     box_corners(bx + A.o, sy, sz, c);

@@ -32,6 +32,7 @@
 #include "drr_device.hpp"
 #include "drr_internal.hpp"
 #include "drr_sample.hpp"
+#include "drr_stage.hpp"
 
 namespace drr {
 
@@ -119,6 +120,69 @@ __device__ inline double block_sum12(const double v_in[12], double* red)
     return t;
 }
 
+// A ray's contribution to its view's sums P (contrib[0..2]) and Q
+// (contrib[3..11]) from its march sums s0 = sum_k mu_k, g0 = sum_k grad mu_k
+// and h1 = sum_k k grad mu_k (per voxel index), chain rule in fp64.
+template <int MODE>
+__device__ inline void pose_chain_rule(const RayFrame& F, const VolumeDesc& V, int N, float g,
+                                       float density, double s0, const double g0[3],
+                                       const double h1[3], double contrib[12])
+{
+    const double Nd = (double)N, dz = (F.t1 - F.t0) / Nd;
+    const double S0 = s0;
+    double G0[3], G1[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        G0[a] = g0[a] * V.inv_s[a];                               // per mm
+        G1[a] = (h1[a] + 0.5 * g0[a]) / Nd * V.inv_s[a];
+    }
+    const double s = dz * S0, f = (double)density;
+    const double y = (double)g * f * (MODE == kBeerLambert ? exp(-f * s) : 1.0);
+    double G0d = 0.0, G1d = 0.0;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        G0d += G0[a] * F.d[a];
+        G1d += G1[a] * F.d[a];
+    }
+    const double beta0 = -S0 / Nd + dz * (G0d - G1d);
+    const double beta1 = S0 / Nd + dz * G1d;
+    double Ac[3], Bd[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        Ac[a] = dz * G0[a];
+        Bd[a] = dz * (F.t0 * G0[a] + (F.t1 - F.t0) * G1[a]);
+    }
+    if (F.a_in >= 0) {
+        Ac[F.a_in] -= beta0 / F.d[F.a_in];
+        Bd[F.a_in] -= beta0 * F.t0 / F.d[F.a_in];
+    }
+    Ac[F.a_out] -= beta1 / F.d[F.a_out];
+    Bd[F.a_out] -= beta1 * F.t1 / F.d[F.a_out];
+    const double dBd = Bd[0] * F.d[0] + Bd[1] * F.d[1] + Bd[2] * F.d[2];
+    double Bw[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) Bw[a] = (Bd[a] - F.d[a] * dBd) / F.len;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) contrib[a] = y * Ac[a];
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int j = 0; j < 3; ++j) contrib[3 + i * 3 + j] = y * F.u[i] * Bw[j];
+}
+
+// One group of samples' value and gradient terms, summed in fp32 (at most four
+// terms), added to the ray's fp64 sums; the group starts at sample k.
+__device__ inline void pose_add_group(int k, float ps, const float pg[3], const float ph[3],
+                                      double& s0, double g0[3], double h1[3])
+{
+    s0 += (double)ps;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        g0[a] += (double)pg[a];
+        h1[a] = fma((double)k, (double)pg[a], h1[a] + (double)ph[a]);
+    }
+}
+
 // The tiles of a launch run over (view, channel) pairs (a tile lies in one
 // pair); every channel of a view adds to that view's sums, and the density
 // factor enters dI/ds (f exp(-f s) or f).  `src` holds one channel-volume of
@@ -190,12 +254,7 @@ __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
                     ph[a] = fmaf((float)i, gq[a], ph[a]);
                 }
             }
-            s0 += (double)ps;
-#pragma unroll
-            for (int a = 0; a < 3; ++a) {
-                g0[a] += (double)pg[a];
-                h1[a] = fma((double)k, (double)pg[a], h1[a] + (double)ph[a]);
-            }
+            pose_add_group(k, ps, pg, ph, s0, g0, h1);
         }
         for (; k < N; ++k) {
             const SampleAddr A = sample_addr<T, L>(V, sample_fixed(F, 0, k), sample_fixed(F, 1, k),
@@ -210,48 +269,167 @@ __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
                 h1[a] = fma((double)k, (double)gq[a], h1[a]);
             }
         }
-        // chain rule, fp64
-        const double Nd = (double)N, dz = (F.t1 - F.t0) / Nd;
-        const double S0 = s0;
-        double G0[3], G1[3];
-#pragma unroll
-        for (int a = 0; a < 3; ++a) {
-            G0[a] = g0[a] * V.inv_s[a];                               // per mm
-            G1[a] = (h1[a] + 0.5 * g0[a]) / Nd * V.inv_s[a];
-        }
-        const double s = dz * S0, f = (double)b.f;
-        const double y = (double)g * f * (MODE == kBeerLambert ? exp(-f * s) : 1.0);
-        double G0d = 0.0, G1d = 0.0;
-#pragma unroll
-        for (int a = 0; a < 3; ++a) {
-            G0d += G0[a] * F.d[a];
-            G1d += G1[a] * F.d[a];
-        }
-        const double beta0 = -S0 / Nd + dz * (G0d - G1d);
-        const double beta1 = S0 / Nd + dz * G1d;
-        double Ac[3], Bd[3];
-#pragma unroll
-        for (int a = 0; a < 3; ++a) {
-            Ac[a] = dz * G0[a];
-            Bd[a] = dz * (F.t0 * G0[a] + (F.t1 - F.t0) * G1[a]);
-        }
-        if (F.a_in >= 0) {
-            Ac[F.a_in] -= beta0 / F.d[F.a_in];
-            Bd[F.a_in] -= beta0 * F.t0 / F.d[F.a_in];
-        }
-        Ac[F.a_out] -= beta1 / F.d[F.a_out];
-        Bd[F.a_out] -= beta1 * F.t1 / F.d[F.a_out];
-        const double dBd = Bd[0] * F.d[0] + Bd[1] * F.d[1] + Bd[2] * F.d[2];
-        double Bw[3];
-#pragma unroll
-        for (int a = 0; a < 3; ++a) Bw[a] = (Bd[a] - F.d[a] * dBd) / F.len;
-#pragma unroll
-        for (int a = 0; a < 3; ++a) contrib[a] = y * Ac[a];
-#pragma unroll
-        for (int i = 0; i < 3; ++i)
-#pragma unroll
-            for (int j = 0; j < 3; ++j) contrib[3 + i * 3 + j] = y * F.u[i] * Bw[j];
+        pose_chain_rule<MODE>(F, V, N, g, b.f, s0, g0, h1, contrib);
     }
+    const double t = block_sum12(contrib, red);
+    if (threadIdx.x < 12 && t != 0.0) unsafeAtomicAdd(acc + 12 * view + threadIdx.x, t);
+}
+
+// LDS-staged pose gradient (box clip), the forward's staging applied to the
+// pose march: the workgroup loads the box of voxels a chunk of its tile's
+// samples touch (clamped, mapped by the transfer function when TF) and the
+// samples read their corners from LDS.  Positions are those of the linear
+// kernel (each group of four re-anchored on its fp64 position, then stepped
+// by the rounded increment, at most 2.5 fixed-point units from each sample's
+// own fp64 position), so the chunk box is widened by 4 units each way.
+template <typename T, int MODE, bool TF>
+__global__ __launch_bounds__(kBlock) void drr_pose_staged_kernel(
+    const T* __restrict__ src, uint32_t src_bytes, VolumeDesc V, Intrinsics K,
+    const float* __restrict__ poses, int H, int W, int N, int tiles_x, int tiles_per_view,
+    Batch b, TransferFn tf, const float* __restrict__ grad_out, double* __restrict__ acc)
+{
+    __shared__ float box[kStageCap];
+    __shared__ int ired[(kBlock / 64) * 6];
+    __shared__ int bb[6];
+    __shared__ double red[(kBlock / 64) * 12];
+    const int tile = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
+    const PixelCoord px = tile_pixel(tile, tiles_x, tiles_per_view);
+    const int view = px.view / b.C, ch = px.view - view * b.C;
+    const int cvol = (view / b.vpv) * b.C + ch;
+    double contrib[12];
+#pragma unroll
+    for (int i = 0; i < 12; ++i) contrib[i] = 0.0;
+
+    const float g = (px.r < H && px.c < W) ? grad_out[((size_t)px.view * H + px.r) * W + px.c]
+                                           : 0.0f;
+    RayFrame F;
+    bool hit = false;
+    if (g != 0.0f) {
+        ViewGeom G;
+        view_setup(poses + 12 * view, K, G);
+        double Ki[9];
+        intrinsics_inverse(K, Ki);
+        hit = ray_frame(G, Ki, V, px.r, px.c, N, F);
+    }
+    const char* base = reinterpret_cast<const char*>(src) + (uint64_t)cvol * b.src_stride;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)src_bytes, kBufferWord3);
+    int64_t dq[3] = {0, 0, 0};
+    if (hit) {
+#pragma unroll
+        for (int a = 0; a < 3; ++a) dq[a] = to_fixed(F.dq[a]);
+    }
+    double s0 = 0.0, g0[3] = {0.0, 0.0, 0.0}, h1[3] = {0.0, 0.0, 0.0};
+    constexpr int64_t kSlack = 4;          // fixed-point units, see above
+    constexpr int kGroup = 4;
+
+    int S = N;
+    int k0 = 0;
+    while (k0 < N) {
+        S = min(S, N - k0);
+        int ext[3] = {1, 1, 1}, lo[3] = {0, 0, 0};
+        long long vol_cells = 1;
+        bool any;
+        for (;;) {
+            int lo_f[3] = {INT_MAX, INT_MAX, INT_MAX}, hi_f[3] = {INT_MAX, INT_MAX, INT_MAX};
+            if (hit) {
+#pragma unroll
+                for (int a = 0; a < 3; ++a) {
+                    const int64_t qa = sample_fixed(F, a, k0), qb = sample_fixed(F, a, k0 + S - 1);
+                    lo_f[a] = fixed_floor(min(qa, qb) - kSlack);
+                    hi_f[a] = fixed_floor(max(qa, qb) + kSlack);
+                }
+            }
+            any = chunk_box(lo_f, hi_f, ired, bb, lo, ext, vol_cells);
+            if (!any || vol_cells <= kStageCap || S == 1) break;
+            S = max(1, S >> 1);
+        }
+        if (!any) break;                             // no ray of this tile contributes
+        if (vol_cells <= kStageCap) {
+            stage_fill<T, TF>(box, (int)vol_cells, rs, V, lo, ext, tf, ch);
+            __syncthreads();
+            if (hit) {
+                const uint32_t sy = 4u * (uint32_t)ext[0], sz = 4u * (uint32_t)(ext[0] * ext[1]);
+                const char* bx = reinterpret_cast<const char*>(box);
+                const int64_t shift[3] = {(int64_t)lo[0] * kFixedOne, (int64_t)lo[1] * kFixedOne,
+                                          (int64_t)lo[2] * kFixedOne};
+                int k = k0;
+                for (; k + kGroup <= k0 + S; k += kGroup) {
+                    int64_t qx = sample_fixed(F, 0, k) - shift[0];
+                    int64_t qy = sample_fixed(F, 1, k) - shift[1];
+                    int64_t qz = sample_fixed(F, 2, k) - shift[2];
+                    SampleAddr A[kGroup];
+                    CornerVals c[kGroup];
+#pragma unroll
+                    for (int i = 0; i < kGroup; ++i) {
+                        A[i].fx = fixed_frac(qx);
+                        A[i].fy = fixed_frac(qy);
+                        A[i].fz = fixed_frac(qz);
+                        A[i].gxs = A[i].gzs = 1.0f;
+                        A[i].o = box_offset(qx, qy, qz, sy, sz);
+                        qx += dq[0]; qy += dq[1]; qz += dq[2];
+                        serial_step(qx, qy, qz);
+                    }
+#pragma unroll
+                    for (int i = 0; i < kGroup; ++i) box_corners(bx + A[i].o, sy, sz, c[i]);
+                    float ps = 0.0f, pg[3] = {0.0f, 0.0f, 0.0f}, ph[3] = {0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int i = 0; i < kGroup; ++i) {
+                        float gq[3];
+                        ps += interpolate_grad(A[i], c[i], gq);
+#pragma unroll
+                        for (int a = 0; a < 3; ++a) {
+                            pg[a] += gq[a];
+                            ph[a] = fmaf((float)i, gq[a], ph[a]);
+                        }
+                    }
+                    pose_add_group(k, ps, pg, ph, s0, g0, h1);
+                }
+                for (; k < k0 + S; ++k) {
+                    const int64_t qx = sample_fixed(F, 0, k) - shift[0];
+                    const int64_t qy = sample_fixed(F, 1, k) - shift[1];
+                    const int64_t qz = sample_fixed(F, 2, k) - shift[2];
+                    SampleAddr A;
+                    A.fx = fixed_frac(qx);
+                    A.fy = fixed_frac(qy);
+                    A.fz = fixed_frac(qz);
+                    A.gxs = A.gzs = 1.0f;
+                    A.o = box_offset(qx, qy, qz, sy, sz);
+                    CornerVals c;
+                    box_corners(bx + A.o, sy, sz, c);
+                    float gq[3];
+                    const float v = interpolate_grad(A, c, gq);
+                    const float zero[3] = {0.0f, 0.0f, 0.0f};
+                    pose_add_group(k, v, gq, zero, s0, g0, h1);
+                }
+            }
+            __syncthreads();
+        } else if (hit) {
+            // the box does not fit: gather this chunk's corners from global memory
+            for (int k = k0; k < k0 + S; ++k) {
+                const int64_t qx = sample_fixed(F, 0, k), qy = sample_fixed(F, 1, k);
+                const int64_t qz = sample_fixed(F, 2, k);
+                const int ix = fixed_floor(qx), iy = fixed_floor(qy), iz = fixed_floor(qz);
+                SampleAddr A;
+                A.fx = fixed_frac(qx);
+                A.fy = fixed_frac(qy);
+                A.fz = fixed_frac(qz);
+                A.gxs = A.gzs = 1.0f;
+                CornerVals c;
+#pragma unroll
+                for (int n = 0; n < 8; ++n)
+                    c.v[n] = staged_value<T, TF>(rs, V, ix + (n & 1), iy + ((n >> 1) & 1),
+                                                 iz + (n >> 2), tf, ch);
+                float gq[3];
+                const float v = interpolate_grad(A, c, gq);
+                const float zero[3] = {0.0f, 0.0f, 0.0f};
+                pose_add_group(k, v, gq, zero, s0, g0, h1);
+            }
+        }
+        k0 += S;
+        if (vol_cells * 2 <= kStageCap) S *= 2;
+    }
+    if (hit) pose_chain_rule<MODE>(F, V, N, g, b.f, s0, g0, h1, contrib);
     const double t = block_sum12(contrib, red);
     if (threadIdx.x < 12 && t != 0.0) unsafeAtomicAdd(acc + 12 * view + threadIdx.x, t);
 }
@@ -321,6 +499,35 @@ static void pose_typed(const LaunchArgs& a, const RenderPlan& p, const T* src, c
         launch_pose<T, Layout::Single>(a, src, bytes, b, grad_out, acc, stream);
 }
 
+template <typename T>
+static void launch_pose_staged(const LaunchArgs& a, const T* vol, const Batch& b,
+                               const float* grad_out, double* acc, hipStream_t stream)
+{
+    const int tiles_x = (a.W + kTile - 1) / kTile, tiles_y = (a.H + kTile - 1) / kTile;
+    const int tiles_per_view = tiles_x * tiles_y;
+    const dim3 grid(tiles_per_view * a.n_views * a.C), block(kBlock);
+    const uint32_t bytes = (uint32_t)((size_t)a.V.n[0] * a.V.n[1] * a.V.n[2] * sizeof(T));
+    if (a.mode == kBeerLambert) {
+        if (a.has_tf)
+            hipLaunchKernelGGL((drr_pose_staged_kernel<T, kBeerLambert, true>), grid, block, 0,
+                               stream, vol, bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                               tiles_per_view, b, a.tf, grad_out, acc);
+        else
+            hipLaunchKernelGGL((drr_pose_staged_kernel<T, kBeerLambert, false>), grid, block, 0,
+                               stream, vol, bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                               tiles_per_view, b, a.tf, grad_out, acc);
+    } else {
+        if (a.has_tf)
+            hipLaunchKernelGGL((drr_pose_staged_kernel<T, kLineIntegral, true>), grid, block, 0,
+                               stream, vol, bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                               tiles_per_view, b, a.tf, grad_out, acc);
+        else
+            hipLaunchKernelGGL((drr_pose_staged_kernel<T, kLineIntegral, false>), grid, block, 0,
+                               stream, vol, bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                               tiles_per_view, b, a.tf, grad_out, acc);
+    }
+}
+
 hipError_t launch_backward_pose(const LaunchArgs& a, const RenderPlan& plan, const void* vol,
                                 int dtype, void* read_buf, double* acc, const float* grad_out,
                                 float* grad_poses, hipStream_t stream)
@@ -332,6 +539,27 @@ hipError_t launch_backward_pose(const LaunchArgs& a, const RenderPlan& plan, con
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if ((long long)a.H * a.W > 0) {
+        if (plan.staged) {
+            // boxes of the caller's volumes, staged in LDS tile by tile
+            Batch b;
+            b.src_stride = (uint64_t)plan.per_volume_bytes;
+            b.grad_stride = 0;
+            b.C = a.C;
+            b.vpv = a.n_views / a.n_volumes;
+            b.f = a.f;
+            b.margin = a.margin;
+            if (dtype == 0)
+                launch_pose_staged<float>(a, static_cast<const float*>(vol), b, grad_out, acc,
+                                          stream);
+            else
+                launch_pose_staged<uint16_t>(a, static_cast<const uint16_t*>(vol), b, grad_out,
+                                             acc, stream);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(drr_pose_finalize_kernel, dim3((n_acc + 63) / 64), dim3(64), 0,
+                               stream, acc, a.poses, a.n_views, grad_poses);
+            return hipGetLastError();
+        }
         e = launch_read_copy(a, plan, vol, dtype, read_buf, stream);
         if (e != hipSuccess) return e;
         Batch b;

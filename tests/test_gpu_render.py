@@ -404,6 +404,80 @@ def test_render_staged_bf16(dev):
     check(img, tau, grad, ref, ref_tau, ref_g, "staged bf16")
 
 
+def _pose_is_staged(vol, H, Wd, N, V, nk, bf16=False):
+    """The pose gradient stages boxes exactly when its workspace holds only the
+    fp64 view sums (12 per view, 256-byte multiple)."""
+    B, C, nz, ny, nx = vol.shape
+    ws = drr.drr_render_workspace_bytes(B, C, nz, ny, nx, 1 if bf16 else 0, V, H, Wd, N, BL,
+                                        BOX, nk, 2)
+    return ws == (V * 12 * 8 + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("tf", [False, True])
+@pytest.mark.parametrize("mode", [BL, RAW])
+def test_render_staged_pose_gradient(dev, mode, tf):
+    """The LDS-staged pose gradient (2 volumes x 2 channels, 2 views each,
+    96 x 96 detector over a 16^3 volume, as the staged forward test), with the
+    transfer function applied as the boxes are filled."""
+    seed = 530 + 2 * mode + tf
+    vol, spacing, K, poses, H, Wd, N, g = problem(seed, shape=(16, 16, 16), det=(96, 96), N=37,
+                                                   tf=tf)
+    transfer = knots(2) if tf else None
+    nk = 3 if tf else 0
+    assert _pose_is_staged(vol, H, Wd, N, poses.shape[0], nk)
+    f = 25.0 if tf else 0.8
+    say(f"case: staged pose gradient mode={mode} tf={tf}")
+    gp = drr.drr_render_backward_pose(torch.from_numpy(vol).to(dev), spacing, K,
+                                      torch.from_numpy(poses).to(dev), H, Wd, N, mode,
+                                      torch.from_numpy(g).to(dev), f, BOX, 0.0, transfer)
+    torch.cuda.synchronize()
+    ref = oracle.render_pose_gradient(vol, spacing, K, poses, H, Wd, N, mode, g,
+                                      density_factor=f, transfer=transfer)
+    got = gp.cpu().double().numpy()
+    errs = [np.abs(got[i] - ref[i]).max() / np.abs(ref[i]).max() for i in range(len(ref))]
+    say(f"staged pose m{mode} tf{int(tf)}: per-view normwise err max {max(errs):.3e}")
+    assert max(errs) <= GRAD
+
+
+def test_render_staged_pose_gradient_bf16_and_diverging_rays(dev):
+    """The staged pose gradient on a bf16 volume, and with the ~150 degree
+    camera inside a 64^3 volume whose chunks fall back to global gathers."""
+    vol, spacing, K, poses, H, Wd, N, g = problem(540, shape=(16, 16, 16), det=(96, 96), N=37)
+    bits = W.round_to_bf16_bits(vol)
+    vol_r = (bits.astype(np.uint32) << 16).view(np.float32)
+    assert _pose_is_staged(vol, H, Wd, N, poses.shape[0], 0, bf16=True)
+    say("case: staged pose gradient bf16")
+    v = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+    gp = drr.drr_render_backward_pose(v, spacing, K, torch.from_numpy(poses).to(dev), H, Wd, N,
+                                      BL, torch.from_numpy(g).to(dev), 1.0, BOX, 0.0, None)
+    torch.cuda.synchronize()
+    ref = oracle.render_pose_gradient(vol_r, spacing, K, poses, H, Wd, N, BL, g)
+    got = gp.cpu().double().numpy()
+    errs = [np.abs(got[i] - ref[i]).max() / np.abs(ref[i]).max() for i in range(len(ref))]
+    say(f"staged pose bf16: per-view normwise err max {max(errs):.3e}")
+    assert max(errs) <= GRAD
+
+    rng = np.random.default_rng(541)
+    vol = rng.uniform(0.0, 1.0, size=(1, 1, 64, 64, 64)).astype(np.float32)
+    spacing = np.ones(3, dtype=np.float32)
+    K = W.intrinsics(32.0, 128.0, 128.0)
+    pose = W.pose_from_rotation_and_centre(np.eye(3), np.array([3.0, -2.0, -20.0]))[None]
+    H = Wd = 256
+    N = 80
+    assert _pose_is_staged(vol, H, Wd, N, 1, 0)
+    g = rng.uniform(-1, 1, size=(1, 1, H, Wd)).astype(np.float32)
+    say("case: staged pose gradient, diverging rays")
+    gp = drr.drr_render_backward_pose(torch.from_numpy(vol).to(dev), spacing, K,
+                                      torch.from_numpy(pose).to(dev), H, Wd, N, RAW,
+                                      torch.from_numpy(g).to(dev), 1.0, BOX, 0.0, None)
+    torch.cuda.synchronize()
+    ref = oracle.render_pose_gradient(vol, spacing, K, pose, H, Wd, N, RAW, g)
+    got = gp.cpu().double().numpy()
+    err = np.abs(got[0] - ref[0]).max() / np.abs(ref[0]).max()
+    say(f"staged pose diverging: normwise err {err:.3e}")
+    assert err <= GRAD
+
+
 def test_render_staged_diverging_rays_fall_back_to_global_gathers(dev):
     """A camera inside a 64^3 volume with a ~150 degree field of view: a tile's
     rays spread over more voxels than a staged box holds even for one sample,
