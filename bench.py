@@ -329,6 +329,22 @@ def workload_lines(dev, reps):
     return lines
 
 
+def read_plan(ws, B, C, nz, ny, nx, elem, V, H, Wd, N, clip, nk):
+    """Name of the forward's read plan, told apart by its workspace size
+    (corner cells, z-pairs and the mapped linear copy differ in size; no
+    workspace is the LDS-staged boxes or the caller's volume)."""
+    rnd = lambda b: (b + 255) // 256 * 256
+    if ws == B * C * rnd((nx + 1) * (ny + 1) * (nz + 1) * 8 * elem):
+        return "mapped corner cells" if nk else "corner cells"
+    if nz >= 2 and ws == B * C * rnd(nx * ny * (nz - 1) * 2 * elem):
+        return "mapped z-pairs" if nk else "z-pairs"
+    if ws > 0:
+        return "mapped volume"
+    staged = clip == 0 and V * C * H * Wd >= 65536 and \
+        H * Wd * N / ((nx + 1) * (ny + 1) * (nz + 1)) >= 16
+    return "LDS-staged boxes" if staged else "volume"
+
+
 class RenderCase:
     """A drr_render configuration resident on the device, with preallocated
     outputs, workspaces and upstream gradient (so a captured graph allocates
@@ -357,8 +373,8 @@ class RenderCase:
         self.ws_f = torch.empty(wf, dtype=torch.uint8, device=dev) if wf else None
         self.ws_b = torch.empty(wb, dtype=torch.uint8, device=dev) if wb else None
         self.samples = V * C * H * Wd * N
-        self.cells = wf > 0 and wf != B * C * ((nx * ny * nz * 4 + 255) // 256 * 256)
         self.read_elem = 4 if (transfer is not None or dt == drr.F32) else 2
+        self.plan = read_plan(wf, B, C, nz, ny, nx, self.read_elem, V, H, Wd, N, clip, nk)
 
     def forward(self):
         import ct_forward_projection_amd as drr
@@ -422,7 +438,7 @@ def frontend_lines(dev):
                 "dtype": "bf16" if vol.dtype == torch.bfloat16 else "f32",
                 "mode": {0: "beer-lambert", 1: "line-integral", 2: "alpha"}[mode],
                 "clip": "near-far-30mm" if clip else "box",
-                "transfer": transfer is not None, "cells": bool(c.cells),
+                "transfer": transfer is not None, "read": c.plan,
                 "forward_ms": round(f_ms, 4), "forward_fps": round(views / f_ms * 1e3, 1),
                 "forward_gsamples_s": round(c.samples / f_ms / 1e6, 1),
                 "forward_hbm_frac": round(fwd_bytes / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -480,7 +496,7 @@ PMC_SETS = {
 # kernels whose counters each pass reports (matched as substrings of the name)
 KERNEL_KEYS = {"forward": ["drr_march_staged_kernel"],
                "backward": ["drr_fill_kernel", "drr_scatter_kernel"],
-               "pose": ["drr_cells_kernel", "drr_pose_grad_kernel"],
+               "pose": ["drr_pose_staged_kernel"],
                "copy": ["copy"]}
 PMC_KINDS = ("forward", "backward", "pose", "copy")
 
@@ -569,7 +585,7 @@ def profile_summary(root: str):
               "(factors applied below).", ""]
     for kind in ("forward", "backward", "pose"):
         for name in KERNEL_KEYS[kind]:
-            if (kind, name) not in med or (kind == "pose" and name == "drr_cells_kernel"):
+            if (kind, name) not in med:
                 continue
             _counter_table(lines, traffic, name, f"{kind} pass", med[(kind, name)],
                            fetch_factor, write_factor, durations.get(name))

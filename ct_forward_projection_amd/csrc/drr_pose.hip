@@ -152,12 +152,19 @@ __device__ inline void pose_chain_rule(const RayFrame& F, const VolumeDesc& V, i
         Ac[a] = dz * G0[a];
         Bd[a] = dz * (F.t0 * G0[a] + (F.t1 - F.t0) * G1[a]);
     }
-    if (F.a_in >= 0) {
-        Ac[F.a_in] -= beta0 / F.d[F.a_in];
-        Bd[F.a_in] -= beta0 * F.t0 / F.d[F.a_in];
+    // the planes that bound the range (unrolled selects: a run-time index into
+    // these small arrays would put them in scratch memory)
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        if (a == F.a_in) {
+            Ac[a] -= beta0 / F.d[a];
+            Bd[a] -= beta0 * F.t0 / F.d[a];
+        }
+        if (a == F.a_out) {
+            Ac[a] -= beta1 / F.d[a];
+            Bd[a] -= beta1 * F.t1 / F.d[a];
+        }
     }
-    Ac[F.a_out] -= beta1 / F.d[F.a_out];
-    Bd[F.a_out] -= beta1 * F.t1 / F.d[F.a_out];
     const double dBd = Bd[0] * F.d[0] + Bd[1] * F.d[1] + Bd[2] * F.d[2];
     double Bw[3];
 #pragma unroll
