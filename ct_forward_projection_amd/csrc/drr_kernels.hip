@@ -594,10 +594,11 @@ __device__ inline void window_add_at(int* win, int base, int wy, int wz, const f
 //   dI/dv_k = T_k (alpha_k + f dz (1 - alpha_k) v_k) - f dz sum_{j>k} T_j alpha_j v_j
 // (its emission and opacity, and the transmittance it takes from every later
 // sample); the later-sample sum is the forward's I minus the running emission
-// up to k.  Each call gathers the sample's eight corners again from the linear
-// volume (the caller's, or the fp32 mapped copy; clamped or zero-padded as the
-// cell and mask say) and advances the running state, so samples are visited in
-// order; tau and the running emission are fp64.
+// up to k.  Each call reads the sample's corners again from the linear volume
+// (the caller's, or the fp32 mapped copy): four x-pair loads with clamp to edge,
+// or eight single loads of the zero-padded cell in the near/far mode (and for
+// volumes one voxel wide); it advances the running state, so samples are
+// visited in order; tau and the running emission are fp64.
 template <typename T, bool ZP>
 struct AlphaCoef {
     __amdgpu_buffer_rsrc_t rs;
@@ -605,7 +606,8 @@ struct AlphaCoef {
     float fdz, g;
     double I, tau, run;
 
-    __device__ float next(const Cell& C, const float* m)
+    // mu at a sample from its clamped (or zero-padded) cell: eight loads
+    __device__ float value(const Cell& C, const float* m) const
     {
         float w[8];
         corner_weights<ZP>(C, 1.0f, w, m);
@@ -621,6 +623,36 @@ struct AlphaCoef {
         float v = 0.0f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) v = fmaf(w[c], val[c], v);
+        return v;
+    }
+
+    // mu at a sample, clamp to edge, from four x-pair loads (nx >= 2): the pair
+    // starts at clamp(ix, 0, nx - 2) and the x weight is pinned to 0 or 1 at the
+    // clamped edges, rows y and z are clamped
+    __device__ float value_pairs(const VolumeDesc& V, int64_t qx, int64_t qy, int64_t qz) const
+    {
+        const int ix = fixed_floor(qx), iy = fixed_floor(qy), iz = fixed_floor(qz);
+        const int xp = clampi(ix, 0, V.n[0] - 2);
+        const float fx = __builtin_amdgcn_fmed3f(fixed_frac(qx) + (float)(ix - xp), 0.0f, 1.0f);
+        const float fy = fixed_frac(qy), fz = fixed_frac(qz);
+        const uint32_t y0 = (uint32_t)clampi(iy, 0, V.n[1] - 1) * sy;
+        const uint32_t y1 = (uint32_t)clampi(iy + 1, 0, V.n[1] - 1) * sy;
+        const uint32_t z0 = (uint32_t)clampi(iz, 0, V.n[2] - 1) * sz;
+        const uint32_t z1 = (uint32_t)clampi(iz + 1, 0, V.n[2] - 1) * sz;
+        const uint32_t rows[4] = {z0 + y0, z0 + y1, z1 + y0, z1 + y1};
+        float a[4], b[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            load_pair<T>(rs, (rows[r] + (uint32_t)xp) * (uint32_t)sizeof(T), a[r], b[r]);
+        const float c00 = fmaf(fx, b[0] - a[0], a[0]), c10 = fmaf(fx, b[1] - a[1], a[1]);
+        const float c01 = fmaf(fx, b[2] - a[2], a[2]), c11 = fmaf(fx, b[3] - a[3], a[3]);
+        const float c0 = fmaf(fy, c10 - c00, c00), c1 = fmaf(fy, c11 - c01, c01);
+        return fmaf(fz, c1 - c0, c0);
+    }
+
+    // the coefficient of the next sample (in order) from its mu
+    __device__ float next_of(float v)
+    {
         const float a = fdz * v;
         const float Tk = expf(-(float)tau);
         const float alpha = -expm1f(-a);
@@ -628,6 +660,21 @@ struct AlphaCoef {
         const float later = (float)(I - run);
         tau += (double)a;
         return g * (Tk * (alpha + fdz * (1.0f - alpha) * v) - fdz * later);
+    }
+
+    __device__ float next(const Cell& C, const float* m) { return next_of(value(C, m)); }
+
+    // the coefficient of the next sample (in order) at fixed-point position q
+    __device__ float next_at(const VolumeDesc& V, int64_t qx, int64_t qy, int64_t qz)
+    {
+        if constexpr (!ZP) {
+            if (V.n[0] >= 2) return next_of(value_pairs(V, qx, qy, qz));
+        }
+        Cell C;
+        float m[6];
+        cell_of(V, qx, qy, qz, C);
+        if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
+        return next(C, m);
     }
 };
 
@@ -736,12 +783,8 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
             int64_t qx = R.q0[0], qy = R.q0[1], qz = R.q0[2];
             bool finite = true;
             for (int k = 0; k < N; ++k) {
-                Cell C;
-                float m[6];
-                cell_of(V, qx, qy, qz, C);
-                if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
+                const float ck = coef.next_at(V, qx, qy, qz);
                 qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
-                const float ck = coef.next(C, m);
                 finite = finite && isfinite(ck);
                 cmax = fmaxf(cmax, fabsf(ck));
             }
@@ -854,13 +897,7 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                             const int ix = clampi(fx, -1, V.n[0] - 1);
                             const int iy = clampi(fy, -1, V.n[1] - 1);
                             const int iz = clampi(fz, -1, V.n[2] - 1);
-                            if constexpr (ALPHA) {
-                                Cell C;
-                                float m[6];
-                                cell_of(V, qx, qy, qz, C);
-                                if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
-                                c = coef.next(C, m) * scale;
-                            }
+                            if constexpr (ALPHA) c = coef.next_at(V, qx, qy, qz) * scale;
                             if constexpr (ZP) {
                                 // a sample with every corner outside the volume adds nothing
                                 if (fx != ix || fy != iy || fz != iz) c = 0.0f;
