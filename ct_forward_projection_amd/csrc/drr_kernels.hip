@@ -799,6 +799,9 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
             Cs = (float)n;
         }
     }
+    // the window starts zeroed here; each flush zeroes the entries it read, so
+    // every chunk finds the entries it uses at zero (block_sum2 synchronises)
+    for (int i = threadIdx.x; i < win_cap; i += kBlock) win[i] = 0;
     block_sum2(B, Cs, reinterpret_cast<float*>(red));
     if (Cs == 0.0f) return;                        // no ray of this tile contributes
     const bool fixed_ok = isfinite(B) && B > 0.0f && Cs <= 1073741824.0f;
@@ -845,8 +848,6 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
         }
         if (fixed_ok && vol_cells <= win_cap) {
             const int n_win = (int)vol_cells;
-            for (int i = threadIdx.x; i < n_win; i += kBlock) win[i] = 0;
-            __syncthreads();
             if (active) {
                 // the window lives in unclamped index space: a sample's floor
                 // places its eight corners at fixed offsets; entries at -1 or n
@@ -926,6 +927,7 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
             for (int i = threadIdx.x; i < n_win; i += kBlock, bw.next()) {
                 const int val = win[i];
                 if (val == 0) continue;
+                win[i] = 0;
                 int g[3] = {lo[0] + bw.x, lo[1] + bw.y, lo[2] + bw.z};
                 bool inside = true;
 #pragma unroll

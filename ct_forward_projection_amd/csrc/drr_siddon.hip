@@ -241,6 +241,9 @@ __global__ __launch_bounds__(kBlock) void drr_siddon_scatter_kernel(
     const double diag = sqrt(V.s[0] * V.s[0] + V.s[1] * V.s[1] + V.s[2] * V.s[2]);
     float B = live ? (float)(fabs((double)y) * diag) : 0.0f;
     float Cs = live ? 1.0f : 0.0f;
+    // the window starts zeroed here; each flush zeroes the entries it read, so
+    // every chunk finds the entries it uses at zero (block_sum2 synchronises)
+    for (int i = threadIdx.x; i < win_cap; i += kBlock) win[i] = 0;
     block_sum2(B, Cs, reinterpret_cast<float*>(red));
     if (Cs == 0.0f) return;                        // no ray of this tile contributes
     const bool fixed_ok = isfinite(B) && B > 0.0f;
@@ -292,11 +295,6 @@ __global__ __launch_bounds__(kBlock) void drr_siddon_scatter_kernel(
         if (box[0] == INT_MAX) break;
         const bool windowed = fixed_ok && vol <= win_cap;
         const int wy = ext[0], wz = ext[0] * ext[1];
-        if (windowed) {
-            const int n_win = (int)vol;
-            for (int i = threadIdx.x; i < n_win; i += kBlock) win[i] = 0;
-            __syncthreads();
-        }
         // walk this ray's pieces up to tb
         while (live) {
             const NextAxis m = next_axis(S);
@@ -325,10 +323,12 @@ __global__ __launch_bounds__(kBlock) void drr_siddon_scatter_kernel(
             BoxWalk bw(ext);
             for (int i = threadIdx.x; i < (int)vol; i += kBlock, bw.next()) {
                 const int val = win[i];
-                if (val != 0)
+                if (val != 0) {
+                    win[i] = 0;
                     unsafeAtomicAdd(grad + (uint32_t)(lo[2] + bw.z) * sz +
                                         (uint32_t)(lo[1] + bw.y) * sy + (uint32_t)(lo[0] + bw.x),
                                     (float)val * inv_scale);
+                }
             }
             __syncthreads();
         }
