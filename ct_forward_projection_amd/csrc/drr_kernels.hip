@@ -924,7 +924,26 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
             }
             __syncthreads();
             BoxWalk bw(ext);
-            for (int i = threadIdx.x; i < n_win; i += kBlock, bw.next()) {
+            bool interior = true;
+#pragma unroll
+            for (int a = 0; a < 3; ++a)
+                interior = interior && lo[a] >= 0 && lo[a] + ext[a] <= V.n[a];
+            if (interior) {
+                // every entry is a voxel of the volume: no clamping, and the
+                // gradient offset steps with the walk
+                BoxAddr ba(bw, lo, sy, sz);
+                for (int i = threadIdx.x; i < n_win; i += kBlock) {
+                    const int val = win[i];
+                    if (val != 0) {
+                        win[i] = 0;
+                        unsafeAtomicAdd(grad + ba.addr, (float)val * inv_scale);
+                    }
+                    int cx, cy;
+                    bw.next(cx, cy);
+                    ba.next(cx, cy);
+                }
+            }
+            for (int i = threadIdx.x; !interior && i < n_win; i += kBlock, bw.next()) {
                 const int val = win[i];
                 if (val == 0) continue;
                 win[i] = 0;

@@ -320,15 +320,18 @@ __global__ __launch_bounds__(kBlock) void drr_siddon_scatter_kernel(
         }
         if (windowed) {
             __syncthreads();
+            // the box lies inside the volume: the gradient offset steps with the walk
             BoxWalk bw(ext);
-            for (int i = threadIdx.x; i < (int)vol; i += kBlock, bw.next()) {
+            BoxAddr ba(bw, lo, sy, sz);
+            for (int i = threadIdx.x; i < (int)vol; i += kBlock) {
                 const int val = win[i];
                 if (val != 0) {
                     win[i] = 0;
-                    unsafeAtomicAdd(grad + (uint32_t)(lo[2] + bw.z) * sz +
-                                        (uint32_t)(lo[1] + bw.y) * sy + (uint32_t)(lo[0] + bw.x),
-                                    (float)val * inv_scale);
+                    unsafeAtomicAdd(grad + ba.addr, (float)val * inv_scale);
                 }
+                int cx, cy;
+                bw.next(cx, cy);
+                ba.next(cx, cy);
             }
             __syncthreads();
         }

@@ -51,13 +51,40 @@ struct BoxWalk {
     }
     __device__ void next()
     {
+        int cx, cy;
+        next(cx, cy);
+    }
+
+    // The same, reporting the carries out of x and out of y (0 or 1).
+    __device__ void next(int& cx, int& cy)
+    {
         x += sx;                       // sx < ex: at most one carry
-        int c = x >= ex ? 1 : 0;
-        x -= c * ex;
-        y += sy + c;                   // sy + c <= ey: at most one carry
-        c = y >= ey ? 1 : 0;
-        y -= c * ey;
-        z += sz + c;
+        cx = x >= ex ? 1 : 0;
+        x -= cx * ex;
+        y += sy + cx;                  // sy + cx <= ey: at most one carry
+        cy = y >= ey ? 1 : 0;
+        y -= cy * ey;
+        z += sz + cy;
+    }
+};
+
+// Element offset in a volume (row stride vy, slice stride vz elements) of the
+// entries a BoxWalk visits, box corner lo, stepped with the walk's carries
+// instead of multiplied out; valid for a box inside the volume.
+struct BoxAddr {
+    uint32_t addr;
+    uint32_t step, carry_x, carry_y;
+
+    __device__ BoxAddr(const BoxWalk& w, const int lo[3], uint32_t vy, uint32_t vz)
+    {
+        addr = (uint32_t)(lo[2] + w.z) * vz + (uint32_t)(lo[1] + w.y) * vy + (uint32_t)(lo[0] + w.x);
+        step = (uint32_t)w.sx + (uint32_t)w.sy * vy + (uint32_t)w.sz * vz;
+        carry_x = vy - (uint32_t)w.ex;                 // next row: back ex, on vy
+        carry_y = vz - (uint32_t)w.ey * vy;            // next slice: back ey rows, on vz
+    }
+    __device__ void next(int cx, int cy)
+    {
+        addr += step + (cx ? carry_x : 0u) + (cy ? carry_y : 0u);
     }
 };
 
