@@ -67,17 +67,18 @@ struct RenderPlan {
 };
 
 // The forward and the pose gradient (allow_staged) may instead stage boxes of
-// the caller's volumes in LDS, tile by tile (box clip, one lane per ray, i.e. launches of at least
-// 65,536 rays): that needs neither a relayout pass nor a workspace, and the
-// transfer function is applied as the boxes are filled.  Staging pays when the
-// rays of one tile are dense against the voxels, which the samples one view
-// puts per cell measure: measured on MI355X, 1024^2 x 512 samples over 256^3
-// (32 per view-cell) 0.85 -> 0.57 ms and 2048^2 x 256 (64) 1.24 -> 1.15 ms,
-// while the 360-view helix (12 per view-cell; corner cells amortised over the
-// views) went 11.0 -> 12.1 ms and the 16-view 200^2 bf16 batch (0.6) 0.74 ->
-// 2.24 ms.
+// the caller's volumes in LDS, tile by tile (box clip, one lane per ray, i.e.
+// launches of at least 65,536 rays): that needs neither a relayout pass nor a
+// workspace, and the transfer function is applied as the boxes are filled.
+// Staging pays when the rays of one tile are dense against the voxels, which
+// the samples one view puts per cell measure.  Measured on MI355X, staged
+// against the best copy: 1024^2 x 512 samples over 256^3 (32 per view-cell)
+// 0.45 against 0.85 ms; the 360-view 256 x 384 helix over 128^3 at 256 samples
+// (11.7) 10.0 against 11.0 ms, at 128 (5.9) 6.4 against 5.6 ms and at 64 (2.9)
+// 6.8 against 3.4 ms; 16 views of 512^2 x 256 over 256^3 (3.9) 2.7 against
+// 1.7 ms.  The crossover lies between 6 and 12 per view-cell.
 constexpr long long kStagedMinRays = 65536;
-constexpr double kStagedMinViewReuse = 16.0;
+constexpr double kStagedMinViewReuse = 8.0;
 
 // Read plans of the other launches, by the samples the launch puts per cell of
 // each volume: at 16 or more the corner-cell copy (eight values per cell, one
