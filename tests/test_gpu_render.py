@@ -213,6 +213,49 @@ def test_render_sparse_rays_read_the_volume(dev, mode, tf):
     assert max(errs) <= GRAD
 
 
+@pytest.mark.parametrize("shape,det,N,plan", [
+    ((2, 9, 11), (19, 23), 5, "z-pairs"),          # one z-pair slice
+    ((7, 9, 2), (19, 23), 3, "z-pairs"),           # one x-pair per row
+    ((2, 2, 2), (8, 8), 2, "z-pairs"),             # both at once
+    ((1, 9, 11), (19, 23), 3, "caller's volume"),  # no z-pairs in a one-voxel-deep volume
+])
+@pytest.mark.parametrize("tf", [False, True])
+def test_render_thin_volumes(dev, shape, det, N, plan, tf):
+    """Volumes two (or one) voxels thick at the reuse that picks z-pairs: every
+    x and z weight is pinned or edge-clamped somewhere; forward, volume and pose
+    gradients against the oracle, both modes, with and without the transfer
+    function."""
+    seed = 370 + shape[0] + 3 * shape[2] + tf
+    vol, spacing, K, poses, H, Wd, N, g = problem(seed, shape=shape, det=det, N=N, tf=tf)
+    transfer = knots(2) if tf else None
+    name = plan_name(vol, H, Wd, N, poses.shape[0], BL, BOX, 3 if tf else 0)
+    say(f"case: thin volume {shape} det={det} N={N} tf={tf} plan={name}")
+    expected = plan
+    if tf:
+        expected = "mapped linear" if plan == "caller's volume" else "mapped " + plan
+    assert name == expected
+    f = 30.0 if tf else 1.3
+    for mode in (BL, RAW):
+        img, tau, grad = run_gpu(dev, vol, spacing, K, poses, H, Wd, N, mode, f, BOX, 0.0,
+                                 transfer, g)
+        kw = dict(density_factor=f, clip=BOX, margin=0.0, transfer=transfer)
+        ref, ref_tau = oracle.render(vol, spacing, K, poses, H, Wd, N, mode, **kw)
+        ref_g = oracle.render_adjoint(vol, spacing, K, poses, H, Wd, N, mode, g, **kw)
+        check(img, tau, grad, ref, ref_tau, ref_g, f"thin {shape} m{mode} tf{int(tf)}")
+        gp = drr.drr_render_backward_pose(torch.from_numpy(vol).to(dev), spacing, K,
+                                          torch.from_numpy(poses).to(dev), H, Wd, N, mode,
+                                          torch.from_numpy(g).to(dev), f, BOX, 0.0, transfer)
+        torch.cuda.synchronize()
+        ref_p = oracle.render_pose_gradient(vol, spacing, K, poses, H, Wd, N, mode, g,
+                                            density_factor=f, transfer=transfer)
+        got = gp.cpu().double().numpy()
+        errs = [np.abs(got[i] - ref_p[i]).max() / max(np.abs(ref_p[i]).max(), 1e-30)
+                for i in range(len(ref_p))]
+        say(f"thin {shape} m{mode} tf{int(tf)}: pose gradient per-view normwise err max "
+            f"{max(errs):.3e}")
+        assert max(errs) <= GRAD
+
+
 def test_render_bf16_density_without_transfer(dev):
     """bf16 densities read directly (cells keep bf16), near/far and box."""
     vol, spacing, K, poses, H, Wd, N, g = problem(352, N=101)
