@@ -215,6 +215,36 @@ __device__ inline bool ray_setup_range(const ViewGeom& G, const VolumeDesc& V, i
     return true;
 }
 
+// Samples [k_lo, k_hi) of a near/far march whose continuous index lies in
+// [-1, n) on every axis: the zero-padded trilinear support.  Every other sample
+// reads only padding and adds exactly 0 (to the sum, the composite and the
+// gradient), so the march can skip it.  The bounds come from the fixed-point
+// start and step in fp64 and are widened by one sample each way.
+__device__ inline void padded_support(const MarchRay& R, const VolumeDesc& V, int N, int& k_lo,
+                                      int& k_hi)
+{
+    double lo = 0.0, hi = (double)N;
+    bool none = false;             // an axis the ray does not move along, outside the support
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        const double q0 = (double)R.q0[a] * 2.3283064365386963e-10;
+        const double dq = (double)R.dq[a] * 2.3283064365386963e-10;
+        const double b0 = -1.0, b1 = (double)V.n[a];
+        if (dq == 0.0) {
+            none = none || !(q0 >= b0 && q0 < b1);
+        } else {
+            const double k0 = (b0 - q0) / dq, k1 = (b1 - q0) / dq;
+            lo = fmax(lo, fmin(k0, k1));
+            hi = fmin(hi, fmax(k0, k1));
+        }
+    }
+    lo = fmin(fmax(lo, 0.0), (double)N);
+    hi = fmin(fmax(hi, 0.0), (double)N);
+    k_lo = max((int)floor(lo) - 1, 0);
+    k_hi = min((int)ceil(hi) + 1, N);
+    if (none || k_hi < k_lo) k_hi = k_lo;
+}
+
 __device__ inline int fixed_floor(int64_t q) { return (int)(q >> 32); }
 
 __device__ inline float fixed_frac(int64_t q)

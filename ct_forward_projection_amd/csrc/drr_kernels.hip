@@ -260,12 +260,17 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
         const char* base = reinterpret_cast<const char*>(src) + (uint64_t)cvol * b.src_stride;
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)src_bytes, kBufferWord3);
-        int64_t qx = R.q0[0] + (int64_t)j * R.dq[0];
-        int64_t qy = R.q0[1] + (int64_t)j * R.dq[1];
-        int64_t qz = R.q0[2] + (int64_t)j * R.dq[2];
+        // samples [k_lo, k_hi): all of them, or in the near/far mode those
+        // that can reach the volume (the rest read zero padding and add 0)
+        int k_lo = 0, k_hi = N;
+        if constexpr (ZP) padded_support(R, V, N, k_lo, k_hi);
+        const int k_first = k_lo + j;
+        int64_t qx = R.q0[0] + (int64_t)k_first * R.dq[0];
+        int64_t qy = R.q0[1] + (int64_t)k_first * R.dq[1];
+        int64_t qz = R.q0[2] + (int64_t)k_first * R.dq[2];
         const int64_t dqx = (int64_t)SPLIT * R.dq[0], dqy = (int64_t)SPLIT * R.dq[1];
         const int64_t dqz = (int64_t)SPLIT * R.dq[2];
-        const int n_mine = j < N ? (N - j + SPLIT - 1) / SPLIT : 0;
+        const int n_mine = k_first < k_hi ? (k_hi - k_first + SPLIT - 1) / SPLIT : 0;
         const float fdz = b.f * R.dz;
         // independent partial sums, one per in-flight sample: a shorter fp32
         // summation chain as well
@@ -770,6 +775,15 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
         }
     }
 
+    // samples [k_lo, k_hi) of this ray: all of them, or in the near/far mode
+    // those that can reach the volume (the rest read zero padding: they add
+    // nothing to the gradient and leave the compositing state unchanged)
+    int k_lo = 0, k_hi = N;
+    if constexpr (ZP) {
+        if (active) padded_support(R, V, N, k_lo, k_hi);
+        active = active && k_hi > k_lo;
+    }
+
     // fixed-point scale of this tile
     float B = 0.0f, Cs = 0.0f;
     if (active) {
@@ -780,9 +794,11 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
         if constexpr (ALPHA) {
             // first pass: the largest coefficient of the ray (NaN if any is not finite)
             coef.tau = coef.run = 0.0;
-            int64_t qx = R.q0[0], qy = R.q0[1], qz = R.q0[2];
+            int64_t qx = R.q0[0] + (int64_t)k_lo * R.dq[0];
+            int64_t qy = R.q0[1] + (int64_t)k_lo * R.dq[1];
+            int64_t qz = R.q0[2] + (int64_t)k_lo * R.dq[2];
             bool finite = true;
-            for (int k = 0; k < N; ++k) {
+            for (int k = k_lo; k < k_hi; ++k) {
                 const float ck = coef.next_at(V, qx, qy, qz);
                 qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
                 finite = finite && isfinite(ck);
@@ -821,11 +837,12 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
         long long vol_cells;
         for (;;) {
             int v[6] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX, INT_MAX, INT_MAX};
-            if (active) {
+            const int ka = max(k0, k_lo), kb = min(k0 + S, k_hi);   // this ray's samples
+            if (active && ka < kb) {
 #pragma unroll
                 for (int a = 0; a < 3; ++a) {
-                    const int64_t qa = R.q0[a] + (int64_t)k0 * R.dq[a];
-                    const int64_t qb = R.q0[a] + (int64_t)(k0 + S - 1) * R.dq[a];
+                    const int64_t qa = R.q0[a] + (int64_t)ka * R.dq[a];
+                    const int64_t qb = R.q0[a] + (int64_t)(kb - 1) * R.dq[a];
                     int fa = fixed_floor(qa), fb = fixed_floor(qb);
                     if constexpr (!REBASE) {
                         fa = clampi(fa, -1, V.n[a] - 1);
@@ -836,6 +853,7 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 }
             }
             block_min6(v, red, box);
+            if (box[0] == INT_MAX) break;            // no ray of the tile has samples here
             vol_cells = 1;
 #pragma unroll
             for (int a = 0; a < 3; ++a) {
@@ -845,6 +863,10 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
             }
             if (!fixed_ok || vol_cells <= win_cap || S == 1) break;
             S = max(1, S >> 1);
+        }
+        if (box[0] == INT_MAX) {                     // (near/far only) nothing to add
+            k0 += S;
+            continue;
         }
         if (fixed_ok && vol_cells <= win_cap) {
             const int n_win = (int)vol_cells;
@@ -883,8 +905,8 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] = start;
                 for (int r = 0; r < kParts; ++r) {
-                    const int ka = k0 + ((first + r) & (kParts - 1)) * part;
-                    const int kb = min(ka + part, k0 + S);
+                    const int kp = k0 + ((first + r) & (kParts - 1)) * part;
+                    const int ka = max(kp, k_lo), kb = min(min(kp + part, k0 + S), k_hi);
                     int64_t qx = R.q0[0] + (int64_t)ka * R.dq[0] - shift[0];
                     int64_t qy = R.q0[1] + (int64_t)ka * R.dq[1] - shift[1];
                     int64_t qz = R.q0[2] + (int64_t)ka * R.dq[2] - shift[2];
@@ -960,10 +982,11 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
             }
             __syncthreads();
         } else if (active) {
-            int64_t qx = R.q0[0] + (int64_t)k0 * R.dq[0];
-            int64_t qy = R.q0[1] + (int64_t)k0 * R.dq[1];
-            int64_t qz = R.q0[2] + (int64_t)k0 * R.dq[2];
-            for (int k = k0; k < k0 + S; ++k) {
+            const int ka = max(k0, k_lo), kb = min(k0 + S, k_hi);
+            int64_t qx = R.q0[0] + (int64_t)ka * R.dq[0];
+            int64_t qy = R.q0[1] + (int64_t)ka * R.dq[1];
+            int64_t qz = R.q0[2] + (int64_t)ka * R.dq[2];
+            for (int k = ka; k < kb; ++k) {
                 Cell C;
                 float m[6];
                 cell_of(V, qx, qy, qz, C);
