@@ -336,6 +336,8 @@ def read_plan(ws, B, C, nz, ny, nx, elem, V, H, Wd, N, clip, nk):
     rnd = lambda b: (b + 255) // 256 * 256
     if ws == B * C * rnd((nx + 1) * (ny + 1) * (nz + 1) * 8 * elem):
         return "mapped corner cells" if nk else "corner cells"
+    if clip == 1 and ws == B * C * rnd((nx + 2) * (ny + 2) * (nz + 1) * 2 * elem):
+        return "mapped padded z-pairs" if nk else "padded z-pairs"
     if nz >= 2 and ws == B * C * rnd(nx * ny * (nz - 1) * 2 * elem):
         return "mapped z-pairs" if nk else "z-pairs"
     if ws > 0:

@@ -112,7 +112,12 @@ void set_read_geometry(drr::VolumeDesc& V, const drr::RenderPlan& plan)
 {
     const uint32_t nx = (uint32_t)V.n[0], ny = (uint32_t)V.n[1], nz = (uint32_t)V.n[2];
     const uint32_t eb = (uint32_t)plan.read_elem;
-    if (plan.zpair) {
+    if (plan.zpair && plan.padded) {
+        // zero-padded z-pairs: nz + 1 slices of (ny + 2) rows of nx + 2 pairs
+        V.row_bytes = (nx + 2) * 2u * eb;
+        V.slice_bytes = (ny + 2) * V.row_bytes;
+        V.total_bytes = (uint32_t)((unsigned long long)(nz + 1) * V.slice_bytes);
+    } else if (plan.zpair) {
         // z-pair copy: nz - 1 slices of (x, y) elements of two values each
         V.row_bytes = nx * 2u * eb;
         V.slice_bytes = nx * ny * 2u * eb;

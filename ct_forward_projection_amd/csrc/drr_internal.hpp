@@ -59,6 +59,7 @@ struct RenderPlan {
     bool staged;             // forward: LDS-staged boxes of the caller's volumes (no workspace)
     bool cells;
     bool zpair;              // the march reads the z-pair copy (Layout::ZPair)
+    bool padded;             // ... zero-padded (near/far mode)
     bool mapped;             // the march reads fp32 mu made by the transfer function
     int read_elem;           // element bytes the march reads
     size_t per_volume_bytes;
@@ -120,11 +121,22 @@ inline RenderPlan plan_render(int n_volumes, int C, int nz, int ny, int nx, int 
         p.fits = true;
         return p;
     }
-    p.cells = clip == kClipNearFar || (reuse && cells_fit);
-    const double zpair_bytes = (double)nx * ny * (nz - 1) * 2.0 * p.read_elem;
-    p.zpair = !p.cells && nx >= 2 && nz >= 2 && rays_per_volume > 0 &&
-              samples_per_cell >= kZPairMinReuse && zpair_bytes < 4294967040.0;
-    p.fits = p.cells ? cells_fit : lin_bytes < 4294967040.0;
+    double zpair_bytes;
+    if (clip == kClipNearFar) {
+        // zero padding needs a copy: corner cells where they are reused
+        // enough, else the zero-padded z-pairs (about 2x the volume)
+        zpair_bytes = (double)(nx + 2) * (ny + 2) * (nz + 1) * 2.0 * p.read_elem;
+        const bool zpair_fit = zpair_bytes < 4294967040.0;
+        p.cells = (reuse || !zpair_fit) && cells_fit;
+        p.zpair = p.padded = !p.cells && zpair_fit;
+        if (!p.cells && !p.zpair) p.cells = true;            // reported as not fitting
+    } else {
+        zpair_bytes = (double)nx * ny * (nz - 1) * 2.0 * p.read_elem;
+        p.cells = reuse && cells_fit;
+        p.zpair = !p.cells && nx >= 2 && nz >= 2 && rays_per_volume > 0 &&
+                  samples_per_cell >= kZPairMinReuse && zpair_bytes < 4294967040.0;
+    }
+    p.fits = p.cells ? cells_fit : (p.zpair ? true : lin_bytes < 4294967040.0);
     const double nv = (double)n_volumes * (double)C;
     if (p.cells) {
         p.per_volume_bytes = ((size_t)cell_bytes + 255) & ~(size_t)255;

@@ -136,6 +136,57 @@ __global__ __launch_bounds__(256) void drr_zpair_kernel(const Tin* __restrict__ 
     }
 }
 
+// Zero-padded z-pair relayout (near/far mode): element (X, Y, Z) of the copy,
+// 0 <= X <= nx + 1, 0 <= Y <= ny + 1, 0 <= Z <= nz, holds voxels
+// (X - 1, Y - 1, Z - 1) and (X - 1, Y - 1, Z) side by side, 0 for a voxel
+// outside the volume (mapped by channel c's transfer function into fp32 with
+// TF; the padding stays 0).  One thread per element; blockIdx.y = channel-volume.
+template <typename Tin, typename Tout, bool TF>
+__global__ __launch_bounds__(256) void drr_zpair_pad_kernel(const Tin* __restrict__ vol, int nx,
+                                                            int ny, int nz, size_t in_stride,
+                                                            Tout* __restrict__ pairs,
+                                                            size_t out_stride, int C,
+                                                            TransferFn tf)
+{
+    static_assert(TF || sizeof(Tin) == sizeof(Tout), "no transfer: pairs keep the dtype");
+    const int cv = (int)blockIdx.y, ch = cv % C;
+    vol += (size_t)cv * in_stride;
+    pairs += (size_t)cv * out_stride;
+    const int px = nx + 2, py = ny + 2;
+    const size_t n = (size_t)px * py * (size_t)(nz + 1);
+    const size_t sy = (size_t)nx, sz = (size_t)nx * ny;
+    for (size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x; id < n;
+         id += (size_t)gridDim.x * blockDim.x) {
+        const int X = (int)(id % px);
+        const size_t rest = id / px;
+        const int Y = (int)(rest % py), Z = (int)(rest / py);
+        const int x = X - 1, y = Y - 1, z = Z - 1;
+        const bool xy = x >= 0 && x < nx && y >= 0 && y < ny;
+        const size_t base = (size_t)y * sy + (size_t)x;
+        float v[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int zz = z + h;
+            if (xy && zz >= 0 && zz < nz) {
+                const float w = widen(vol[(size_t)zz * sz + base]);
+                if constexpr (TF) {
+                    float m;
+                    v[h] = transfer_eval(tf, ch, w, m);
+                } else {
+                    v[h] = w;
+                }
+            }
+        }
+        if constexpr (sizeof(Tout) == 4) {
+            reinterpret_cast<float2*>(pairs)[id] = make_float2(v[0], v[1]);
+        } else {
+            // no transfer: v holds the bf16 values exactly
+            reinterpret_cast<uint32_t*>(pairs)[id] =
+                (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xffff0000u);
+        }
+    }
+}
+
 // mu = tf(x) for every voxel of every channel-volume (blockIdx.y), fp32 out.
 template <typename Tin>
 __global__ __launch_bounds__(256) void drr_transfer_kernel(const Tin* __restrict__ vol,
@@ -226,7 +277,8 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
     Batch b, float* __restrict__ out, float* __restrict__ s_out)
 {
     constexpr bool ZP = CLIP == kClipNearFar;
-    static_assert(!ZP || L == Layout::Cell, "the near/far mode reads zero-padded cells");
+    static_assert(!ZP || L == Layout::Cell || L == Layout::ZPair,
+                  "the near/far mode reads zero-padded cells or z-pairs");
     static_assert(MODE != kAlpha || SPLIT == 1, "compositing runs one lane per ray");
     const int tile = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
     PixelCoord px;
@@ -1131,6 +1183,22 @@ template <typename Tin>
 static hipError_t launch_zpair_typed(const LaunchArgs& a, const RenderPlan& p, const Tin* vol,
                                      void* pairs, hipStream_t stream)
 {
+    if (p.padded) {
+        const long long np = (long long)(a.V.n[0] + 2) * (a.V.n[1] + 2) * (a.V.n[2] + 1);
+        const dim3 grid(grid_blocks(np, 16384), a.n_volumes * a.C);
+        const size_t in_stride = (size_t)a.V.n[0] * a.V.n[1] * a.V.n[2];
+        if (p.mapped)
+            hipLaunchKernelGGL((drr_zpair_pad_kernel<Tin, float, true>), grid, dim3(256), 0,
+                               stream, vol, a.V.n[0], a.V.n[1], a.V.n[2], in_stride,
+                               static_cast<float*>(pairs), p.per_volume_bytes / sizeof(float),
+                               a.C, a.tf);
+        else
+            hipLaunchKernelGGL((drr_zpair_pad_kernel<Tin, Tin, false>), grid, dim3(256), 0,
+                               stream, vol, a.V.n[0], a.V.n[1], a.V.n[2], in_stride,
+                               static_cast<Tin*>(pairs), p.per_volume_bytes / sizeof(Tin), a.C,
+                               a.tf);
+        return hipGetLastError();
+    }
     const long long n = (long long)a.V.n[0] * a.V.n[1] * (a.V.n[2] - 1);
     const dim3 grid(grid_blocks(n, 16384), a.n_volumes * a.C);
     const size_t in_stride = (size_t)a.V.n[0] * a.V.n[1] * a.V.n[2];
@@ -1218,12 +1286,23 @@ static hipError_t forward_typed(const LaunchArgs& a, const RenderPlan& p, const 
     if (p.zpair) {
         hipError_t e = launch_zpair_typed<Tin>(a, p, vol, workspace, stream);
         if (e != hipSuccess) return e;
-        if (p.mapped)
-            launch_march_mode<float, Layout::ZPair, kClipBox>(
-                a, static_cast<const float*>(workspace), bytes, b, out, s_out, stream);
-        else
-            launch_march_mode<Tin, Layout::ZPair, kClipBox>(
-                a, static_cast<const Tin*>(workspace), bytes, b, out, s_out, stream);
+        const float* mu = static_cast<const float*>(workspace);
+        const Tin* pr = static_cast<const Tin*>(workspace);
+        if (p.padded) {
+            if (p.mapped)
+                launch_march_mode<float, Layout::ZPair, kClipNearFar>(a, mu, bytes, b, out, s_out,
+                                                                      stream);
+            else
+                launch_march_mode<Tin, Layout::ZPair, kClipNearFar>(a, pr, bytes, b, out, s_out,
+                                                                    stream);
+        } else {
+            if (p.mapped)
+                launch_march_mode<float, Layout::ZPair, kClipBox>(a, mu, bytes, b, out, s_out,
+                                                                  stream);
+            else
+                launch_march_mode<Tin, Layout::ZPair, kClipBox>(a, pr, bytes, b, out, s_out,
+                                                                stream);
+        }
         return hipGetLastError();
     }
     if (p.cells) {

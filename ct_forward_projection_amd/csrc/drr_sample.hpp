@@ -64,7 +64,9 @@ __device__ inline float load_one<uint16_t>(__amdgpu_buffer_rsrc_t rs, uint32_t o
 //          0 <= z <= nz - 2, holds the voxels (x, y, z) and (x, y, z + 1), so
 //          the x-neighbours (xp, xp + 1) of one y row are four values in one
 //          16-byte (fp32) or 8-byte (bf16) load: 2 loads per sample.  x and z
-//          are pinned at the clamped edges as in Pair.
+//          are pinned at the clamped edges as in Pair.  With zero padding the
+//          copy has a border of zeros instead (pairs for x, y in [-1, n] and z
+//          in [-1, nz - 1]) and nothing is pinned.
 enum class Layout { Single, Pair, Cell, ZPair };
 
 struct SampleAddr {
@@ -92,8 +94,8 @@ __device__ inline float fixed_comp(int64_t q)
 // 0xffffff00 bytes): buffer loads there return zeros.
 constexpr uint32_t kOutOfRange = 0xffffff00u;
 
-// ZP (zero padding, Cell layout only): a sample whose cell lies outside the
-// corner-cell grid reads 0; the cells themselves hold 0 for corners outside the
+// ZP (zero padding, Cell and ZPair layouts): a sample whose cell lies outside
+// the copy's grid reads 0; the copy itself holds 0 for corners outside the
 // volume.
 template <typename T, Layout L, bool ZP = false>
 __device__ inline SampleAddr sample_addr(const VolumeDesc& V, int64_t qx, int64_t qy, int64_t qz)
@@ -105,6 +107,24 @@ __device__ inline SampleAddr sample_addr(const VolumeDesc& V, int64_t qx, int64_
     A.fz = fixed_frac(qz);
     A.gxs = 1.0f;
     A.gzs = 1.0f;
+    if constexpr (L == Layout::ZPair && ZP) {
+        // zero-padded z-pairs: element (ix + 1, iy + 1, iz + 1) of a copy with a
+        // border of zeros (rows nx + 2 long, ny + 2 rows, nz + 1 slices); a
+        // sample whose cell lies outside it reads past the buffer's end (both
+        // rows), where loads return 0
+        A.ex = fixed_comp(qx);
+        A.ey = fixed_comp(qy);
+        A.ez = fixed_comp(qz);
+        const bool in = (uint32_t)(ix + 1) <= (uint32_t)V.n[0] &&
+                        (uint32_t)(iy + 1) <= (uint32_t)V.n[1] &&
+                        (uint32_t)(iz + 1) <= (uint32_t)V.n[2];
+        A.o = in ? (uint32_t)(iz + 1) * V.slice_bytes + __umul24((uint32_t)(iy + 1), V.row_bytes) +
+                       (uint32_t)(ix + 1) * (uint32_t)(2 * sizeof(T))
+                 : kOutOfRange;
+        A.dy = in ? V.row_bytes : 0u;
+        A.dz = A.x1 = 0;
+        return A;
+    }
     if constexpr (L == Layout::ZPair) {
         // row and slice strides of the z-pair copy (V.row_bytes, V.slice_bytes)
         const int y0 = clampi(iy, 0, V.n[1] - 1), y1 = clampi(iy + 1, 0, V.n[1] - 1);
@@ -117,7 +137,6 @@ __device__ inline SampleAddr sample_addr(const VolumeDesc& V, int64_t qx, int64_
               (uint32_t)xp * (uint32_t)(2 * sizeof(T));
         A.dy = y1 > y0 ? V.row_bytes : 0u;
         A.dz = A.x1 = 0;
-        static_assert(!ZP, "zero padding reads the corner-cell copy");
         return A;
     }
     if constexpr (L == Layout::Cell) {
@@ -137,7 +156,9 @@ __device__ inline SampleAddr sample_addr(const VolumeDesc& V, int64_t qx, int64_
         A.dy = A.dz = A.x1 = 0;
         return A;
     } else {
-        static_assert(!ZP, "zero padding reads the corner-cell copy");
+        // (the padded z-pair case returned above)
+        static_assert(!ZP || L == Layout::ZPair,
+                      "zero padding reads the corner-cell or padded z-pair copy");
     }
     const int y0 = clampi(iy, 0, V.n[1] - 1), y1 = clampi(iy + 1, 0, V.n[1] - 1);
     const int z0 = clampi(iz, 0, V.n[2] - 1), z1 = clampi(iz + 1, 0, V.n[2] - 1);

@@ -219,7 +219,7 @@ def render_bwd_call(**kw):
     (dict(xp=_f(0.0, float("nan")), yp=_f(0.0, 1.0), knots=2), 1),
     (dict(C=65, xp=_f(*range(130)), yp=_f(*range(130)), knots=2), 2),
     (dict(B=300, C=300, n_views=300), 2),
-    (dict(clip=1), 3),                      # the near/far mode always needs its cells
+    (dict(clip=1), 3),                      # the near/far mode always needs a padded copy
 ])
 def test_render_rejects_invalid_arguments(kw, status):
     assert render_call(**kw) == status
@@ -243,9 +243,13 @@ def test_render_empty_call_and_workspace_queries():
     assert render_call(det_h=0, out=None) == 0
     lib = drr.library()
     q = lib.drr_render_workspace_bytes
-    # near/far: zero-padded corner cells of every channel-volume, 256-byte multiples
+    # near/far: a zero-padded copy of every channel-volume, 256-byte multiples --
+    # z-pairs with a border of zeros ((nx + 2) x (ny + 2) x (nz + 1) pairs) ...
+    zpad = ((10 * 10 * 9 * 2 * 4 + 255) // 256) * 256
+    assert q(2, 3, 8, 8, 8, 0, 4, 4, 4, 8, 0, 1, 0, 0) == 6 * zpad
+    # ... or, from 16 samples per cell, zero-padded corner cells
     cells = ((9 * 9 * 9 * 8 * 4 + 255) // 256) * 256
-    assert q(2, 3, 8, 8, 8, 0, 4, 4, 4, 8, 0, 1, 0, 0) == 6 * cells
+    assert q(1, 1, 8, 8, 8, 0, 1, 32, 32, 16, 0, 1, 0, 0) == cells
     # a transfer function and few samples per cell: the mapped fp32 volumes
     assert q(1, 2, 8, 8, 8, 1, 1, 4, 4, 8, 0, 0, 3, 0) == 2 * 2048
     # about one sample per cell or more, but under 16: z-pair copies of

@@ -81,8 +81,11 @@ def plan_name(vol, H, Wd, N, V, mode, clip, nk, bf16=False):
     cells = B * C * (((nx + 1) * (ny + 1) * (nz + 1) * 8 * elem + 255) // 256 * 256)
     lin = B * C * ((nx * ny * nz * 4 + 255) // 256 * 256)
     zpair = B * C * ((nx * ny * (nz - 1) * 2 * elem + 255) // 256 * 256)
+    zpad = B * C * (((nx + 2) * (ny + 2) * (nz + 1) * 2 * elem + 255) // 256 * 256)
     if ws == cells:
         return "mapped cells" if nk else "cells"
+    if clip == NEAR_FAR and ws == zpad:
+        return "mapped padded z-pairs" if nk else "padded z-pairs"
     if ws == zpair and nz >= 2:
         return "mapped z-pairs" if nk else "z-pairs"
     if nk:
