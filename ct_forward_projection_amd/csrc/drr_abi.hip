@@ -422,7 +422,9 @@ size_t drr_render_workspace_bytes(int n_volumes, int n_channels, int nz, int ny,
         return 0;
     const bool has_tf = tf_knots > 0;
     if (for_backward == DRR_WORKSPACE_VOLUME_BACKWARD)
-        return drr::render_backward_workspace(n_volumes, n_channels, nz, ny, nx, mode, has_tf);
+        return drr::plan_backward(n_volumes, n_channels, nz, ny, nx, dtype == DRR_F32 ? 4 : 2,
+                                  n_views, det_h, det_w, n_samples, mode, clip, has_tf)
+            .workspace_bytes;
     const bool fwd = for_backward == DRR_WORKSPACE_FORWARD;
     const size_t plan = drr::plan_render(n_volumes, n_channels, nz, ny, nx,
                                          dtype == DRR_F32 ? 4 : 2, n_views, det_h, det_w,
@@ -499,7 +501,9 @@ int drr_render_backward_volume(const void* volume, int dtype, int n_volumes, int
         return fail(DRR_ERR_INVALID_ARGUMENT,
                     "volume is required for alpha compositing and for a transfer function");
     const size_t need =
-        drr::render_backward_workspace(n_volumes, n_channels, nz, ny, nx, mode, a.has_tf);
+        drr::plan_backward(n_volumes, n_channels, nz, ny, nx, dtype == DRR_F32 ? 4 : 2, n_views,
+                           det_h, det_w, n_samples, mode, clip, a.has_tf)
+            .workspace_bytes;
     if (workspace_bytes < need)
         return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
                     workspace_bytes, need);

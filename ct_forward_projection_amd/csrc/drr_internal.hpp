@@ -154,14 +154,44 @@ inline RenderPlan plan_render(int n_volumes, int C, int nz, int ny, int nx, int 
     return p;
 }
 
-// Workspace of the volume backward: the alpha-compositing backward gathers the
-// mapped volumes, so with a transfer function it needs their fp32 copy.
-inline size_t render_backward_workspace(int n_volumes, int C, int nz, int ny, int nx, int mode,
-                                        bool has_tf)
+// What the compositing backward's coefficient passes read.  Both passes read
+// every sample again, so from one sample per cell a z-pair copy in the
+// workspace pays (two loads per sample; zero-padded in the near/far mode; fp32
+// and mapped with a transfer function); below that they read the volume (the
+// mapped fp32 linear copy with a transfer function).  The other modes read
+// nothing.
+struct BackwardRead {
+    bool zpair, padded, mapped;
+    int read_elem;
+    size_t per_volume_bytes, workspace_bytes;
+};
+
+inline BackwardRead plan_backward(int n_volumes, int C, int nz, int ny, int nx, int elem_bytes,
+                                  int n_views, int H, int W, int N, int mode, int clip,
+                                  bool has_tf)
 {
-    if (mode != kAlpha || !has_tf) return 0;
-    const size_t per = ((size_t)nx * ny * nz * 4 + 255) & ~(size_t)255;
-    return per * (size_t)n_volumes * (size_t)C;
+    BackwardRead r{};
+    if (mode != kAlpha) return r;
+    r.mapped = has_tf;
+    r.read_elem = has_tf ? 4 : elem_bytes;
+    const double n_cells = (double)(nx + 1) * (double)(ny + 1) * (double)(nz + 1);
+    const double rays = n_volumes > 0 ? (double)(n_views / n_volumes) * H * W : 0.0;
+    const bool reuse = rays * N >= n_cells;
+    double bytes = 0.0;
+    if (reuse && clip == kClipNearFar) {
+        bytes = (double)(nx + 2) * (ny + 2) * (nz + 1) * 2.0 * r.read_elem;
+        r.zpair = r.padded = bytes < 4294967040.0;
+    } else if (reuse && nx >= 2 && nz >= 2) {
+        bytes = (double)nx * ny * (nz - 1) * 2.0 * r.read_elem;
+        r.zpair = bytes < 4294967040.0;
+    }
+    if (!r.zpair) {
+        r.padded = false;
+        bytes = has_tf ? (double)nx * ny * nz * 4.0 : 0.0;
+    }
+    r.per_volume_bytes = ((size_t)bytes + 255) & ~(size_t)255;
+    r.workspace_bytes = r.per_volume_bytes * (size_t)n_volumes * (size_t)C;
+    return r;
 }
 
 hipError_t launch_forward(const LaunchArgs& a, const RenderPlan& plan, const void* vol, int dtype,

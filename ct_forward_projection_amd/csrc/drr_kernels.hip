@@ -656,10 +656,10 @@ __device__ inline void window_add_at(int* win, int base, int wy, int wz, const f
 // or eight single loads of the zero-padded cell in the near/far mode (and for
 // volumes one voxel wide); it advances the running state, so samples are
 // visited in order; tau and the running emission are fp64.
-template <typename T, bool ZP>
+template <typename T, bool ZP, bool ZPAIR>
 struct AlphaCoef {
     __amdgpu_buffer_rsrc_t rs;
-    uint32_t sy, sz;               // element strides of the volume
+    uint32_t sy, sz;               // element strides of the volume (linear reads)
     float fdz, g;
     double I, tau, run;
 
@@ -721,9 +721,17 @@ struct AlphaCoef {
 
     __device__ float next(const Cell& C, const float* m) { return next_of(value(C, m)); }
 
-    // the coefficient of the next sample (in order) at fixed-point position q
-    __device__ float next_at(const VolumeDesc& V, int64_t qx, int64_t qy, int64_t qz)
+    // the coefficient of the next sample (in order) at fixed-point position q;
+    // Vc: the volume with the byte strides of the z-pair copy (ZPAIR)
+    __device__ float next_at(const VolumeDesc& V, const VolumeDesc& Vc, int64_t qx, int64_t qy,
+                             int64_t qz)
     {
+        if constexpr (ZPAIR) {
+            const SampleAddr A = sample_addr<T, Layout::ZPair, ZP>(Vc, qx, qy, qz);
+            CornerVals c;
+            gather<T, Layout::ZPair>(rs, A, c);
+            return next_of(ZP ? interpolate_exact(A, c) : interpolate(A, c));
+        }
         if constexpr (!ZP) {
             if (V.n[0] >= 2) return next_of(value_pairs(V, qx, qy, qz));
         }
@@ -767,13 +775,16 @@ struct AlphaCoef {
 // near/far range and drops corners outside the volume (zero padding); all
 // rays of a workgroup belong to one view, so they share the range.  MODE =
 // kAlpha reads the volume (`vol`, one channel-volume of `vol_bytes` every
-// bt.src_stride bytes) and the forward image `out_in`.
-template <int MODE, int CLIP, typename T>
+// bt.src_stride bytes: the caller's, its mapped fp32 copy, or with ZPAIR its
+// z-pair copy, zero-padded in the near/far mode, of row and slice strides
+// copy_row, copy_slice bytes) and the forward image `out_in`.
+template <int MODE, int CLIP, typename T, bool ZPAIR>
 __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
     VolumeDesc V, Intrinsics K, const float* __restrict__ poses, int H, int W, int N,
     int tiles_x, int tiles_per_view, Batch bt, const float* __restrict__ grad_out,
     const float* __restrict__ s_in, const float* __restrict__ out_in,
-    const T* __restrict__ vol, uint32_t vol_bytes, float* __restrict__ grad, int win_cap)
+    const T* __restrict__ vol, uint32_t vol_bytes, uint32_t copy_row, uint32_t copy_slice,
+    float* __restrict__ grad, int win_cap)
 {
     constexpr bool ZP = CLIP == kClipNearFar;
     constexpr bool ALPHA = MODE == kAlpha;
@@ -795,7 +806,10 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
     bool active = px.r < H && px.c < W;
     MarchRay R;
     float yd = 0.0f;
-    AlphaCoef<T, ZP> coef;
+    AlphaCoef<T, ZP, ZPAIR> coef;
+    VolumeDesc Vc = V;                  // byte strides of the z-pair copy (ZPAIR)
+    Vc.row_bytes = copy_row;
+    Vc.slice_bytes = copy_slice;
     if (active) {
         ViewGeom G;
         view_setup(poses + 12 * view, K, G);
@@ -851,7 +865,7 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
             int64_t qz = R.q0[2] + (int64_t)k_lo * R.dq[2];
             bool finite = true;
             for (int k = k_lo; k < k_hi; ++k) {
-                const float ck = coef.next_at(V, qx, qy, qz);
+                const float ck = coef.next_at(V, Vc, qx, qy, qz);
                 qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
                 finite = finite && isfinite(ck);
                 cmax = fmaxf(cmax, fabsf(ck));
@@ -972,7 +986,7 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                             const int ix = clampi(fx, -1, V.n[0] - 1);
                             const int iy = clampi(fy, -1, V.n[1] - 1);
                             const int iz = clampi(fz, -1, V.n[2] - 1);
-                            if constexpr (ALPHA) c = coef.next_at(V, qx, qy, qz) * scale;
+                            if constexpr (ALPHA) c = coef.next_at(V, Vc, qx, qy, qz) * scale;
                             if constexpr (ZP) {
                                 // a sample with every corner outside the volume adds nothing
                                 if (fx != ix || fy != iy || fz != iz) c = 0.0f;
@@ -1043,8 +1057,9 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 float m[6];
                 cell_of(V, qx, qy, qz, C);
                 if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
+                float c = yd;
+                if constexpr (ALPHA) c = coef.next_at(V, Vc, qx, qy, qz);
                 qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
-                const float c = ALPHA ? coef.next(C, m) : yd;
                 scatter_sample_global<ZP>(grad, sy, sz, C, c, m);
             }
         }
@@ -1359,23 +1374,26 @@ hipError_t launch_fill(float* p, size_t n, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int MODE, typename T>
+template <int MODE, typename T, bool ZPAIR = false>
 static void launch_scatter(const LaunchArgs& a, const Batch& b, const float* grad_out,
                            const float* s_in, const float* out_in, const T* vol,
                            uint32_t vol_bytes, float* grad, int tiles_x, int tiles_per_view,
-                           int n_tiles, hipStream_t stream)
+                           int n_tiles, hipStream_t stream, uint32_t copy_row = 0,
+                           uint32_t copy_slice = 0)
 {
     const double cells = (double)(a.V.n[0] + 1) * (a.V.n[1] + 1) * (a.V.n[2] + 1);
     const int cap = window_cap((double)a.H * a.W * a.N / cells);
     const size_t lds = (size_t)cap * sizeof(int);
     if (a.clip == kClipNearFar)
-        hipLaunchKernelGGL((drr_scatter_kernel<MODE, kClipNearFar, T>), dim3(n_tiles),
+        hipLaunchKernelGGL((drr_scatter_kernel<MODE, kClipNearFar, T, ZPAIR>), dim3(n_tiles),
                            dim3(kBlock), lds, stream, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
-                           tiles_per_view, b, grad_out, s_in, out_in, vol, vol_bytes, grad, cap);
+                           tiles_per_view, b, grad_out, s_in, out_in, vol, vol_bytes, copy_row,
+                           copy_slice, grad, cap);
     else
-        hipLaunchKernelGGL((drr_scatter_kernel<MODE, kClipBox, T>), dim3(n_tiles), dim3(kBlock),
-                           lds, stream, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view,
-                           b, grad_out, s_in, out_in, vol, vol_bytes, grad, cap);
+        hipLaunchKernelGGL((drr_scatter_kernel<MODE, kClipBox, T, ZPAIR>), dim3(n_tiles),
+                           dim3(kBlock), lds, stream, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                           tiles_per_view, b, grad_out, s_in, out_in, vol, vol_bytes, copy_row,
+                           copy_slice, grad, cap);
 }
 
 template <typename Tin>
@@ -1390,7 +1408,36 @@ static hipError_t backward_typed(const LaunchArgs& a, const Tin* vol, const floa
     tile_grid(a.n_views * a.C, a.H, a.W, kTile, tiles_x, tiles_per_view, n_tiles);
     if (n_tiles == 0) return hipSuccess;
     if (a.mode == kAlpha) {
-        if (a.has_tf) {
+        const BackwardRead r = plan_backward(a.n_volumes, a.C, a.V.n[2], a.V.n[1], a.V.n[0],
+                                             (int)sizeof(Tin), a.n_views, a.H, a.W, a.N, kAlpha,
+                                             a.clip, a.has_tf);
+        if (r.zpair) {
+            // gather from a z-pair copy in the workspace (zero-padded in the
+            // near/far mode, fp32 and mapped with a transfer function)
+            RenderPlan p{};
+            p.zpair = true;
+            p.padded = r.padded;
+            p.mapped = r.mapped;
+            p.per_volume_bytes = r.per_volume_bytes;
+            e = launch_zpair_typed<Tin>(a, p, vol, workspace, stream);
+            if (e != hipSuccess) return e;
+            const uint32_t eb = (uint32_t)r.read_elem, nx = (uint32_t)a.V.n[0];
+            const uint32_t ny = (uint32_t)a.V.n[1], nz = (uint32_t)a.V.n[2];
+            const uint32_t row = (r.padded ? nx + 2 : nx) * 2u * eb;
+            const uint32_t slice = (r.padded ? ny + 2 : ny) * row;
+            const uint32_t total = (r.padded ? nz + 1 : nz - 1) * slice;
+            const Batch b = make_batch(a, &p, 0);
+            if (r.mapped)
+                launch_scatter<kAlpha, float, true>(a, b, grad_out, s_in, out_in,
+                                                    static_cast<const float*>(workspace), total,
+                                                    grad, tiles_x, tiles_per_view, n_tiles, stream,
+                                                    row, slice);
+            else
+                launch_scatter<kAlpha, Tin, true>(a, b, grad_out, s_in, out_in,
+                                                  static_cast<const Tin*>(workspace), total, grad,
+                                                  tiles_x, tiles_per_view, n_tiles, stream, row,
+                                                  slice);
+        } else if (a.has_tf) {
             // gather the mapped volumes: their fp32 copy in the workspace
             RenderPlan p{};
             p.mapped = true;
