@@ -259,6 +259,27 @@ def test_render_thin_volumes(dev, shape, det, N, plan, tf):
         assert max(errs) <= GRAD
 
 
+@pytest.mark.parametrize("tf", [False, True])
+def test_render_sparse_near_far_compositing(dev, tf):
+    """Near/far compositing under one sample per cell: the forward reads padded
+    z-pairs, while the backward's coefficient passes gather the zero-padded
+    corners from the volume itself (or its mapped fp32 copy) -- no copy pays."""
+    vol, spacing, K, poses, H, Wd, N, g = problem(380 + tf, det=(5, 7), N=23, tf=tf)
+    B, C, nz, ny, nx = vol.shape
+    transfer = knots(2) if tf else None
+    ws_b = drr.drr_render_workspace_bytes(B, C, nz, ny, nx, 0, poses.shape[0], H, Wd, N, ALPHA,
+                                          NEAR_FAR, 3 if tf else 0, 1)
+    assert ws_b == (B * C * ((nx * ny * nz * 4 + 255) // 256 * 256) if tf else 0)
+    say(f"case: sparse near/far compositing tf={tf}")
+    f = 30.0 if tf else 1.1
+    img, tau, grad = run_gpu(dev, vol, spacing, K, poses, H, Wd, N, ALPHA, f, NEAR_FAR, 3.0,
+                             transfer, g)
+    kw = dict(density_factor=f, clip=NEAR_FAR, margin=3.0, transfer=transfer)
+    ref, ref_tau = oracle.render(vol, spacing, K, poses, H, Wd, N, ALPHA, **kw)
+    ref_g = oracle.render_adjoint(vol, spacing, K, poses, H, Wd, N, ALPHA, g, **kw)
+    check(img, tau, grad, ref, ref_tau, ref_g, f"sparse near/far alpha tf{int(tf)}")
+
+
 def test_render_bf16_density_without_transfer(dev):
     """bf16 densities read directly (cells keep bf16), near/far and box."""
     vol, spacing, K, poses, H, Wd, N, g = problem(352, N=101)
