@@ -90,8 +90,11 @@ typedef enum {
  * (1) or drr_backward_pose (2) needs for these sizes; 0 means no workspace is
  * needed (a NULL workspace is then accepted).  Returns 0 as well for invalid
  * sizes (the call itself then reports the error).  The forward and the pose
- * backward use the workspace for a corner-cell copy of the volume (8 clamped
- * trilinear corners per cell) when rays reuse cells enough for it to pay. */
+ * backward use the workspace for a copy of the volume the march reads when
+ * rays reuse cells enough for it to pay: corner cells (8 clamped trilinear
+ * corners per cell) or z-pairs (each voxel next to its z neighbour); dense
+ * views stage boxes of the volume in LDS and need none.  The pose backward
+ * also keeps 12 fp64 sums per view there. */
 size_t drr_workspace_bytes(int nz, int ny, int nx, int dtype, int n_views, int det_h,
                            int det_w, int n_samples, int for_backward);
 
@@ -214,11 +217,15 @@ int drr_backward_volume_siddon(int nz, int ny, int nx, const float *spacing, con
 
 /* Workspace bytes of drr_render (for_backward = DRR_WORKSPACE_FORWARD),
  * drr_render_backward_volume (DRR_WORKSPACE_VOLUME_BACKWARD) or
- * drr_render_backward_pose (DRR_WORKSPACE_POSE_BACKWARD) for these sizes; tf_knots = 0 means no transfer function.  0 for invalid sizes or when
- * none is needed.  The forward uses it for a corner-cell copy of every
- * channel-volume (when rays reuse cells enough, and always in the near/far
- * mode), or for the mapped fp32 volumes; the compositing backward with a
- * transfer function for the mapped fp32 volumes. */
+ * drr_render_backward_pose (DRR_WORKSPACE_POSE_BACKWARD) for these sizes;
+ * tf_knots = 0 means no transfer function.  0 for invalid sizes or when none
+ * is needed.  The forward (and the pose backward) use it for a copy of every
+ * channel-volume when rays reuse cells enough -- corner cells or z-pairs,
+ * zero-padded in the near/far mode, which always reads a copy -- or for the
+ * mapped fp32 volumes; the compositing backward for a z-pair copy its
+ * coefficient passes read (from about one sample per cell), or for the mapped
+ * fp32 volumes with a transfer function.  Values are mapped by the transfer
+ * function in every copy. */
 size_t drr_render_workspace_bytes(int n_volumes, int n_channels, int nz, int ny, int nx,
                                   int dtype, int n_views, int det_h, int det_w, int n_samples,
                                   int mode, int clip, int tf_knots, int for_backward);
