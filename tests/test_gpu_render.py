@@ -280,6 +280,33 @@ def test_render_sparse_near_far_compositing(dev, tf):
     check(img, tau, grad, ref, ref_tau, ref_g, f"sparse near/far alpha tf{int(tf)}")
 
 
+@pytest.mark.parametrize("N", [6, 64])
+@pytest.mark.parametrize("mode", [BL, RAW, ALPHA])
+def test_render_near_far_axis_aligned_and_boundary_rays(dev, mode, N):
+    """Near/far rays the support test must get exactly right: with cx = cy = 7.5
+    the ray through pixel (7, 7) runs along z (no step in x or y), and cameras
+    shifted by 5 mm put that ray on q_x = -1 (support boundary, included, adds
+    0) and q_x = n (outside, skipped).  N = 6 reads padded z-pairs, N = 64
+    corner cells; forward and volume gradient against the oracle."""
+    rng = np.random.default_rng(390 + mode + N)
+    vol = rng.uniform(0.05, 1.0, size=(1, 1, 9, 9, 9)).astype(np.float32)
+    spacing = np.ones(3, dtype=np.float32)
+    K = W.intrinsics(30.0, 7.5, 7.5)
+    poses = np.stack([W.pose_from_rotation_and_centre(np.eye(3), np.array([x, 0.0, -40.0]))
+                      for x in (0.0, -5.0, 5.0, 2.5)]).astype(np.float32)
+    H = Wd = 16
+    g = rng.uniform(-1, 1, size=(4, 1, H, Wd)).astype(np.float32)
+    name = plan_name(vol, H, Wd, N, 4, mode, NEAR_FAR, 0)
+    say(f"case: near/far axis-aligned rays mode={mode} N={N} plan={name}")
+    assert name == ("padded z-pairs" if N == 6 else "cells")
+    img, tau, grad = run_gpu(dev, vol, spacing, K, poses, H, Wd, N, mode, 1.2, NEAR_FAR, 2.0,
+                             None, g)
+    kw = dict(density_factor=1.2, clip=NEAR_FAR, margin=2.0)
+    ref, ref_tau = oracle.render(vol, spacing, K, poses, H, Wd, N, mode, **kw)
+    ref_g = oracle.render_adjoint(vol, spacing, K, poses, H, Wd, N, mode, g, **kw)
+    check(img, tau, grad, ref, ref_tau, ref_g, f"near/far axis m{mode} N{N}")
+
+
 def test_render_bf16_density_without_transfer(dev):
     """bf16 densities read directly (cells keep bf16), near/far and box."""
     vol, spacing, K, poses, H, Wd, N, g = problem(352, N=101)
