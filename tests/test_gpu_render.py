@@ -307,6 +307,57 @@ def test_render_near_far_axis_aligned_and_boundary_rays(dev, mode, N):
     check(img, tau, grad, ref, ref_tau, ref_g, f"near/far axis m{mode} N{N}")
 
 
+def test_render_graph_capture_replays_match_eager(dev):
+    """drr_render and its backwards captured in a HIP graph replay to the eager
+    results, four times, with eager work and synchronisations in between: near/far
+    compositing with a transfer function (zero-padded z-pair copies in the
+    forward's and the backward's workspaces, made by kernels) and a render that
+    stages boxes, with its staged pose gradient."""
+    vol, spacing, K, poses, H, Wd, N, g = problem(395, N=37, tf=True)
+    v = torch.from_numpy(vol).to(dev)
+    P = torch.from_numpy(poses).to(dev)
+    gt = torch.from_numpy(g).to(dev)
+    tf = knots(2)
+    vol2, spacing2, K2, poses2, H2, Wd2, N2, g2 = problem(396, shape=(16, 16, 16), det=(96, 96),
+                                                        N=37)
+    assert _pose_is_staged(vol2, H2, Wd2, N2, poses2.shape[0], 0)
+    v2 = torch.from_numpy(vol2).to(dev)
+    P2 = torch.from_numpy(poses2).to(dev)
+    g2t = torch.from_numpy(g2).to(dev)
+    bufs = {}
+
+    def step():
+        img, tau = drr.drr_render(v, spacing, K, P, H, Wd, N, ALPHA, 30.0, NEAR_FAR, 2.0, tf)
+        grad = drr.drr_render_backward_volume(v, tuple(vol.shape), 0, spacing, K, P, H, Wd, N,
+                                              ALPHA, gt, img, tau, 30.0, NEAR_FAR, 2.0, tf)
+        img2, _ = drr.drr_render(v2, spacing2, K2, P2, H2, Wd2, N2, BL, 0.8, BOX, 0.0, None)
+        gp = drr.drr_render_backward_pose(v2, spacing2, K2, P2, H2, Wd2, N2, BL, g2t, 0.8, BOX,
+                                          0.0, None)
+        bufs.update(img=img, grad=grad, img2=img2, gp=gp)
+
+    step()
+    torch.cuda.synchronize()
+    ref = {k: t.clone() for k, t in bufs.items()}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    outs = dict(bufs)
+    for i in range(4):
+        for t in outs.values():
+            t.fill_(-7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs["img"], ref["img"]), f"replay {i}: image"
+        assert torch.equal(outs["img2"], ref["img2"]), f"replay {i}: staged image"
+        for k in ("grad", "gp"):
+            e = normwise_err(outs[k].cpu().double().numpy(), ref[k].cpu().double().numpy())
+            assert e <= 1e-6, f"replay {i}: {k} {e}"
+        step()   # eager work between replays
+        torch.cuda.synchronize()
+    say("render graph capture: 4 replays match the eager results")
+
+
 def test_render_bf16_density_without_transfer(dev):
     """bf16 densities read directly (cells keep bf16), near/far and box."""
     vol, spacing, K, poses, H, Wd, N, g = problem(352, N=101)
