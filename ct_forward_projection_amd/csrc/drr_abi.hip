@@ -32,6 +32,9 @@ int ok()
 }
 
 constexpr long long kMaxDim = 16384;
+// The pose kernels round in-box positions to fixed point with a 1.5 * 2^52
+// add, exact only under 2^19 voxels per axis.
+static_assert(kMaxDim < 524288, "axis limit must stay under 2^19");
 constexpr long long kMaxElems = (1LL << 31) - 1;
 constexpr long long kMaxVolumeBytes = (1LL << 32) - 1;  // 32-bit buffer offsets
 constexpr int kMaxSamples = 1 << 24;

@@ -92,10 +92,16 @@ __device__ inline bool ray_frame(const ViewGeom& G, const double Ki[9], const Vo
     return true;
 }
 
-// Sample k's position, evaluated in fp64 and rounded once to 32.32 fixed point.
+// Sample k's position, evaluated in fp64 and rounded once to 32.32 fixed point
+// (to nearest, ties to even, as to_fixed).  Positions lie inside the box and
+// axes stay under 2^19 voxels (the library's 16384 limit), so the fused
+// q 2^32 + 1.5 2^52 lands in [2^52, 2^53) and holds the rounded integer in its
+// low mantissa bits.
 __device__ inline int64_t sample_fixed(const RayFrame& F, int a, int k)
 {
-    return to_fixed(fma((double)k, F.dq[a], F.q0[a]));
+    constexpr double kMagic = 6755399441055744.0;       // 1.5 * 2^52
+    const double q = fma((double)k, F.dq[a], F.q0[a]);
+    return __double_as_longlong(fma(q, 4294967296.0, kMagic)) - __double_as_longlong(kMagic);
 }
 
 // Workgroup sum of twelve doubles, returned to threads 0..11 (one each).
