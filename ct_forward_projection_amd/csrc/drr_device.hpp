@@ -247,6 +247,16 @@ __device__ inline void padded_support(const MarchRay& R, const VolumeDesc& V, in
 
 __device__ inline int fixed_floor(int64_t q) { return (int)(q >> 32); }
 
+// 4 floor(q) + off in one instruction on the high word.  Left to itself the
+// compiler folds the shift into a 64-bit funnel shift and a mask, then adds
+// (three instructions for what v_lshl_add_u32 does in one).
+__device__ inline uint32_t fixed_floor_x4_add(int64_t q, uint32_t off)
+{
+    uint32_t r;
+    asm("v_lshl_add_u32 %0, %1, 2, %2" : "=v"(r) : "v"((uint32_t)(q >> 32)), "v"(off));
+    return r;
+}
+
 __device__ inline float fixed_frac(int64_t q)
 {
     return (float)(uint32_t)q * 2.3283064365386963e-10f;  // 2^-32

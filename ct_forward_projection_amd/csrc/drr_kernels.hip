@@ -608,9 +608,9 @@ __device__ inline void scatter_sample_global(float* __restrict__ grad, uint32_t 
 // corner order x fastest: acc[i] += c w_x(i & 1) w_y((i >> 1) & 1) w_z(i >> 2).
 __device__ inline void add_weights8(float fx, float fy, float fz, float c, float acc[8])
 {
-    const float wz1 = c * fz, wz0 = c * (1.0f - fz);
-    const float w11 = wz1 * fy, w10 = wz1 * (1.0f - fy);
-    const float w01 = wz0 * fy, w00 = wz0 * (1.0f - fy);
+    const float wz1 = c * fz, wz0 = c - wz1;
+    const float w11 = wz1 * fy, w10 = wz1 - w11;
+    const float w01 = wz0 * fy, w00 = wz0 - w01;
     const float fx0 = 1.0f - fx;
     acc[0] = fmaf(w00, fx0, acc[0]);
     acc[1] = fmaf(w00, fx, acc[1]);
@@ -631,18 +631,24 @@ __device__ inline int to_window(float w)
     return TRUNC ? (int)w : __float2int_rn(w);
 }
 
-// Add eight fixed-point weights at window entry `base` and its corner offsets.
+// Add eight fixed-point weights at the window entry of LDS byte address `at`
+// and its corner offsets (row and slice strides wy, wz in bytes).
 template <bool TRUNC = false>
-__device__ inline void window_add_at(int* win, int base, int wy, int wz, const float w[8])
+__device__ inline void window_add_at(uint32_t at, int wy, int wz, const float w[8])
 {
-    atomicAdd(&win[base], to_window<TRUNC>(w[0]));
-    atomicAdd(&win[base + 1], to_window<TRUNC>(w[1]));
-    atomicAdd(&win[base + wy], to_window<TRUNC>(w[2]));
-    atomicAdd(&win[base + wy + 1], to_window<TRUNC>(w[3]));
-    atomicAdd(&win[base + wz], to_window<TRUNC>(w[4]));
-    atomicAdd(&win[base + wz + 1], to_window<TRUNC>(w[5]));
-    atomicAdd(&win[base + wz + wy], to_window<TRUNC>(w[6]));
-    atomicAdd(&win[base + wz + wy + 1], to_window<TRUNC>(w[7]));
+    char* p = (char*)(__attribute__((address_space(3))) char*)(uintptr_t)at;
+    int* r0 = reinterpret_cast<int*>(p);
+    int* r1 = reinterpret_cast<int*>(p + wy);
+    int* r2 = reinterpret_cast<int*>(p + wz);
+    int* r3 = reinterpret_cast<int*>(p + wz + wy);
+    atomicAdd(r0, to_window<TRUNC>(w[0]));
+    atomicAdd(r0 + 1, to_window<TRUNC>(w[1]));
+    atomicAdd(r1, to_window<TRUNC>(w[2]));
+    atomicAdd(r1 + 1, to_window<TRUNC>(w[3]));
+    atomicAdd(r2, to_window<TRUNC>(w[4]));
+    atomicAdd(r2 + 1, to_window<TRUNC>(w[5]));
+    atomicAdd(r3, to_window<TRUNC>(w[6]));
+    atomicAdd(r3 + 1, to_window<TRUNC>(w[7]));
 }
 
 // Per-sample coefficient of the compositing backward (MODE = kAlpha).  For
@@ -962,7 +968,21 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 const int lane = (int)threadIdx.x & 63;
                 const int first = ALPHA ? 0 : ((lane & 1) | ((lane >> 2) & 2));
                 const int part = (S + kParts - 1) / kParts;
+                // window strides in bytes and the window's LDS byte address
+                const int wy4 = 4 * wy, wz4 = 4 * wz;
+                const int w0 = (int)(uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)win;
+                // the register sums' cell as the LDS address of its window
+                // entry; without compositing it starts on a cell of one of the
+                // lane's samples (sums still zero after truncation), so a window
+                // add needs no test for a first sample
                 int pbase = -1;
+                if constexpr (REBASE) {
+                    const int ki = min(k0 + first * part, k0 + S - 1);
+                    const int ix = fixed_floor(R.q0[0] + (int64_t)ki * R.dq[0] - shift[0]);
+                    const int iy = fixed_floor(R.q0[1] + (int64_t)ki * R.dq[1] - shift[1]);
+                    const int iz = fixed_floor(R.q0[2] + (int64_t)ki * R.dq[2] - shift[2]);
+                    pbase = w0 + 4 * ix + __mul24(iy, wy4) + __mul24(iz, wz4);
+                }
                 // a cell's register sums start at 0, or, without compositing
                 // (one coefficient per ray), at +-1/2 with its sign, which lets
                 // the window conversion truncate (see to_window)
@@ -970,45 +990,60 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 float acc[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] = start;
+                auto sample = [&](int64_t& qx, int64_t& qy, int64_t& qz) {
+                    const int fx = fixed_floor(qx), fy = fixed_floor(qy), fz = fixed_floor(qz);
+                    float c = ys;
+                    int base;
+                    if constexpr (REBASE) {
+                        base = (int)fixed_floor_x4_add(qx, w0 + __mul24(fy, wy4) + __mul24(fz, wz4));
+                    } else {
+                        const int ix = clampi(fx, -1, V.n[0] - 1);
+                        const int iy = clampi(fy, -1, V.n[1] - 1);
+                        const int iz = clampi(fz, -1, V.n[2] - 1);
+                        if constexpr (ALPHA) c = coef.next_at(V, Vc, qx, qy, qz) * scale;
+                        if constexpr (ZP) {
+                            // a sample with every corner outside the volume adds nothing
+                            if (fx != ix || fy != iy || fz != iz) c = 0.0f;
+                        }
+                        base = w0 + 4 * (ix - lo[0]) + __mul24(iy - lo[1], wy4) +
+                               __mul24(iz - lo[2], wz4);
+                    }
+                    const float tx = fixed_frac(qx), ty = fixed_frac(qy);
+                    const float tz = fixed_frac(qz);
+                    serial_step_after(qx, qy, qz, tx, ty, tz);
+                    qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
+                    // consecutive samples in one cell are summed in registers;
+                    // a new cell adds the finished sum to the window
+                    const bool same = base == pbase;
+                    if (!same && (REBASE || pbase >= 0))
+                        window_add_at<REBASE>((uint32_t)pbase, wy4, wz4, acc);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] = same ? acc[i] : start;
+                    add_weights8(tx, ty, tz, c, acc);
+                    pbase = base;
+                };
+                // without compositing every lane walks all S samples; when the
+                // quarters are equal, every part has the same (uniform) length
+                const bool even = REBASE && S % kParts == 0;
                 for (int r = 0; r < kParts; ++r) {
                     const int kp = k0 + ((first + r) & (kParts - 1)) * part;
                     const int ka = max(kp, k_lo), kb = min(min(kp + part, k0 + S), k_hi);
                     int64_t qx = R.q0[0] + (int64_t)ka * R.dq[0] - shift[0];
                     int64_t qy = R.q0[1] + (int64_t)ka * R.dq[1] - shift[1];
                     int64_t qz = R.q0[2] + (int64_t)ka * R.dq[2] - shift[2];
-                    for (int k = ka; k < kb; ++k) {
-                        const int fx = fixed_floor(qx), fy = fixed_floor(qy), fz = fixed_floor(qz);
-                        float c = ys;
-                        int base;
-                        if constexpr (REBASE) {
-                            base = fx + __mul24(fy, wy) + __mul24(fz, wz);
-                        } else {
-                            const int ix = clampi(fx, -1, V.n[0] - 1);
-                            const int iy = clampi(fy, -1, V.n[1] - 1);
-                            const int iz = clampi(fz, -1, V.n[2] - 1);
-                            if constexpr (ALPHA) c = coef.next_at(V, Vc, qx, qy, qz) * scale;
-                            if constexpr (ZP) {
-                                // a sample with every corner outside the volume adds nothing
-                                if (fx != ix || fy != iy || fz != iz) c = 0.0f;
-                            }
-                            base = (ix - lo[0]) + __mul24(iy - lo[1], wy) +
-                                   __mul24(iz - lo[2], wz);
+                    if (even) {
+                        // two samples per trip: the cell register alternates
+                        // without a copy
+                        for (int j = 0; j + 1 < part; j += 2) {
+                            sample(qx, qy, qz);
+                            sample(qx, qy, qz);
                         }
-                        const float tx = fixed_frac(qx), ty = fixed_frac(qy);
-                        const float tz = fixed_frac(qz);
-                        serial_step_after(qx, qy, qz, tx, ty, tz);
-                        qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
-                        // consecutive samples in one cell are summed in registers;
-                        // a new cell adds the finished sum to the window
-                        const bool same = base == pbase;
-                        if (!same && pbase >= 0) window_add_at<REBASE>(win, pbase, wy, wz, acc);
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) acc[i] = same ? acc[i] : start;
-                        add_weights8(tx, ty, tz, c, acc);
-                        pbase = base;
+                        if (part & 1) sample(qx, qy, qz);
+                    } else {
+                        for (int k = ka; k < kb; ++k) sample(qx, qy, qz);
                     }
                 }
-                if (pbase >= 0) window_add_at<REBASE>(win, pbase, wy, wz, acc);
+                if (pbase >= 0) window_add_at<REBASE>((uint32_t)pbase, wy4, wz4, acc);
             }
             __syncthreads();
             BoxWalk bw(ext);

@@ -127,8 +127,8 @@ __device__ inline void box_corners(const char* p, uint32_t sy, uint32_t sz, Corn
 __device__ inline uint32_t box_offset(int64_t qx, int64_t qy, int64_t qz, uint32_t sy,
                                       uint32_t sz)
 {
-    return __umul24((uint32_t)fixed_floor(qz), sz) + __umul24((uint32_t)fixed_floor(qy), sy) +
-           ((uint32_t)fixed_floor(qx) << 2);
+    return fixed_floor_x4_add(qx, __umul24((uint32_t)fixed_floor(qz), sz) +
+                                      __umul24((uint32_t)fixed_floor(qy), sy));
 }
 
 }  // namespace drr
