@@ -231,23 +231,42 @@ def backward_bytes(res, hits):
     return hits * w.n_samples * 8 * 4 + w.n_rays * 8
 
 
-def roofline(name, alg_bytes, ms, traffic=None):
+def roofline(name, alg_bytes, ms, traffic=None, valu_busy=None):
+    """HBM roofline on algorithmic bytes.  Staged and cached kernels move far
+    fewer bytes than the algorithm names (frac above 1): ``traffic`` gives the
+    calibrated HBM bytes and ``valu_busy`` the share of VALU issue cycles, both
+    from the committed counters of the current kernel sources (else None)."""
     achieved = alg_bytes / (ms * 1e-3) / 1e9
     return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic}
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "valu_busy": valu_busy}
 
 
-def measured_traffic(kernels):
-    """HBM bytes per launch of a pass (the sum over its kernels) from the
-    committed rocprofv3 counter summary, if it was taken on the current kernel
-    sources and covers every kernel; otherwise None."""
+def _committed_counters():
+    """The committed counter summary, if it was taken on the current kernel
+    sources; otherwise None."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     try:
         with open(path) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("kernel_revision") != kernel_revision():
+    return d if d.get("kernel_revision") == kernel_revision() else None
+
+
+def measured_valu_busy(kernel):
+    """VALU busy of one kernel from the committed counters (None if stale)."""
+    d = _committed_counters()
+    k = None if d is None else d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("valu_busy")
+
+
+def measured_traffic(kernels):
+    """HBM bytes per launch of a pass (the sum over its kernels) from the
+    committed rocprofv3 counter summary, if it was taken on the current kernel
+    sources and covers every kernel; otherwise None."""
+    d = _committed_counters()
+    if d is None:
         return None
     total = 0.0
     for name in kernels:
@@ -616,11 +635,13 @@ def _counter_table(lines, traffic, name, where, m, fetch_factor, write_factor, d
     hit = m.get("TCC_HIT_sum"), m.get("TCC_MISS_sum")
     if all(h is not None for h in hit) and sum(hit) > 0:
         lines.append(f"| L2 hit rate | {hit[0] / (hit[0] + hit[1]):.4f} |")
+    valu_busy = None
     if dur_ns:
         cycles = dur_ns * MI355X_GHZ
         lines.append(f"| traced duration (us) | {dur_ns / 1e3:.2f} |")
         if m.get("SQ_INSTS_VALU"):
-            lines.append(f"| VALU busy | {m['SQ_INSTS_VALU'] * 4 / (MI355X_SIMDS * cycles):.3f} |")
+            valu_busy = round(m["SQ_INSTS_VALU"] * 4 / (MI355X_SIMDS * cycles), 3)
+            lines.append(f"| VALU busy | {valu_busy:.3f} |")
         if m.get("SQ_LDS_BANK_CONFLICT") is not None:
             lines.append(f"| LDS bank-conflict share | "
                          f"{m['SQ_LDS_BANK_CONFLICT'] / (MI355X_CUS * cycles):.3f} |")
@@ -628,7 +649,7 @@ def _counter_table(lines, traffic, name, where, m, fetch_factor, write_factor, d
                   f"write {wb / 1e6:.1f} MB, total {(fb + wb) / 1e6:.1f} MB", ""]
     if fb or wb:
         traffic["kernels"][name] = {"hbm_bytes_per_launch": fb + wb, "read_bytes": fb,
-                                    "write_bytes": wb}
+                                    "write_bytes": wb, "valu_busy": valu_busy}
 
 
 def main():
@@ -689,9 +710,11 @@ def main():
     # and the march, the backward the gradient fill and the scatter
     # the forward of this workload is one launch of the LDS-staged march
     rf = roofline("drr_march_staged_kernel", forward_bytes(res, hits), fwd_ms,
-                  measured_traffic(KERNEL_KEYS["forward"]))
+                  measured_traffic(KERNEL_KEYS["forward"]),
+                  measured_valu_busy("drr_march_staged_kernel"))
     rb = roofline("drr_scatter_kernel (with gradient fill)", backward_bytes(res, hits), bwd_ms,
-                  measured_traffic(KERNEL_KEYS["backward"]))
+                  measured_traffic(KERNEL_KEYS["backward"]),
+                  measured_valu_busy("drr_scatter_kernel"))
     dominant, other = (rb, rf) if bwd_ms >= fwd_ms else (rf, rb)
 
     out = {
