@@ -40,7 +40,7 @@ namespace drr {
 // of the planes that bound the range, and the sample positions in fp64.
 struct RayFrame {
     double C[3], d[3], u[3];
-    double q0[3], dq[3];     // continuous index of sample 0 and the step, fp64
+    double q0[3], dq[3];     // continuous index of sample 0 and the step, fp64, times 2^32
     double len, t0, t1;
     int a_in;      // entry plane axis, -1 when the range starts at the source
     int a_out;     // exit plane axis
@@ -86,22 +86,43 @@ __device__ inline bool ray_frame(const ViewGeom& G, const double Ki[9], const Vo
     const double ts = F.t0 + 0.5 * dz;
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
-        F.q0[a] = (G.C[a] + ts * F.d[a]) * V.inv_s[a] + V.q_off[a];
-        F.dq[a] = dz * F.d[a] * V.inv_s[a];
+        F.q0[a] = ((G.C[a] + ts * F.d[a]) * V.inv_s[a] + V.q_off[a]) * 4294967296.0;
+        F.dq[a] = (dz * F.d[a] * V.inv_s[a]) * 4294967296.0;
     }
     return true;
 }
 
 // Sample k's position, evaluated in fp64 and rounded once to 32.32 fixed point
-// (to nearest, ties to even, as to_fixed).  Positions lie inside the box and
-// axes stay under 2^19 voxels (the library's 16384 limit), so the fused
-// q 2^32 + 1.5 2^52 lands in [2^52, 2^53) and holds the rounded integer in its
-// low mantissa bits.
+// (to nearest, ties to even, as to_fixed).  The frame holds the position and
+// step times 2^32, a power of two that commutes with the rounding of the fma,
+// so q 2^32 comes out exactly.  Positions lie inside the box and axes stay
+// under 2^19 voxels (the library's 16384 limit), so q 2^32 + 1.5 2^52 lands in
+// [2^52, 2^53) and its rounding leaves the rounded integer in the low mantissa
+// bits.
 __device__ inline int64_t sample_fixed(const RayFrame& F, int a, int k)
 {
     constexpr double kMagic = 6755399441055744.0;       // 1.5 * 2^52
-    const double q = fma((double)k, F.dq[a], F.q0[a]);
-    return __double_as_longlong(fma(q, 4294967296.0, kMagic)) - __double_as_longlong(kMagic);
+    const double q32 = fma((double)k, F.dq[a], F.q0[a]);
+    return __double_as_longlong(q32 + kMagic) - __double_as_longlong(kMagic);
+}
+
+// Fixed-point step of the frame (to_fixed of the fp64 step).
+__device__ inline int64_t step_fixed(const RayFrame& F, int a)
+{
+    return __double2ll_rn(F.dq[a]);
+}
+
+// A group of four samples' terms summed in fp32: ps = sum v_i, pg = sum g_i and
+// ph = sum i g_i, formed from the terms themselves (no additions to zero).
+__device__ inline void group_sums4(const float v[4], const float g[4][3], float& ps, float pg[3],
+                                   float ph[3])
+{
+    ps = ((v[0] + v[1]) + v[2]) + v[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        pg[a] = ((g[0][a] + g[1][a]) + g[2][a]) + g[3][a];
+        ph[a] = fmaf(3.0f, g[3][a], fmaf(2.0f, g[2][a], g[1][a]));
+    }
 }
 
 // Workgroup sum of twelve doubles, returned to threads 0..11 (one each).
@@ -239,7 +260,7 @@ __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
         // drift from their fp64 values: each group of four starts from its
         // first sample evaluated in fp64 and rounded once, and steps by the
         // rounded increment from there (at most 3.5 2^-32 voxel off)
-        const int64_t dqx = to_fixed(F.dq[0]), dqy = to_fixed(F.dq[1]), dqz = to_fixed(F.dq[2]);
+        const int64_t dqx = step_fixed(F, 0), dqy = step_fixed(F, 1), dqz = step_fixed(F, 2);
         constexpr int kGroup = 4;
         int k = 0;
         for (; k + kGroup <= N; k += kGroup) {
@@ -256,17 +277,11 @@ __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
             for (int i = 0; i < kGroup; ++i) gather<T, L>(rs, A[i], c[i]);
             __builtin_amdgcn_sched_barrier(0);
             // the group's sums in fp32 (four terms), then into the ray's fp64 sums
-            float ps = 0.0f, pg[3] = {0.0f, 0.0f, 0.0f}, ph[3] = {0.0f, 0.0f, 0.0f};
+            float v[kGroup], gq[kGroup][3];
 #pragma unroll
-            for (int i = 0; i < kGroup; ++i) {
-                float gq[3];
-                ps += interpolate_grad(A[i], c[i], gq);
-#pragma unroll
-                for (int a = 0; a < 3; ++a) {
-                    pg[a] += gq[a];
-                    ph[a] = fmaf((float)i, gq[a], ph[a]);
-                }
-            }
+            for (int i = 0; i < kGroup; ++i) v[i] = interpolate_grad(A[i], c[i], gq[i]);
+            float ps, pg[3], ph[3];
+            group_sums4(v, gq, ps, pg, ph);
             pose_add_group(k, ps, pg, ph, s0, g0, h1);
         }
         for (; k < N; ++k) {
@@ -330,7 +345,7 @@ __global__ __launch_bounds__(kBlock) void drr_pose_staged_kernel(
     int64_t dq[3] = {0, 0, 0};
     if (hit) {
 #pragma unroll
-        for (int a = 0; a < 3; ++a) dq[a] = to_fixed(F.dq[a]);
+        for (int a = 0; a < 3; ++a) dq[a] = step_fixed(F, a);
     }
     double s0 = 0.0, g0[3] = {0.0, 0.0, 0.0}, h1[3] = {0.0, 0.0, 0.0};
     constexpr int64_t kSlack = 4;          // fixed-point units, see above
@@ -385,17 +400,11 @@ __global__ __launch_bounds__(kBlock) void drr_pose_staged_kernel(
                     }
 #pragma unroll
                     for (int i = 0; i < kGroup; ++i) box_corners(bx + A[i].o, sy, sz, c[i]);
-                    float ps = 0.0f, pg[3] = {0.0f, 0.0f, 0.0f}, ph[3] = {0.0f, 0.0f, 0.0f};
+                    float v[kGroup], gq[kGroup][3];
 #pragma unroll
-                    for (int i = 0; i < kGroup; ++i) {
-                        float gq[3];
-                        ps += interpolate_grad(A[i], c[i], gq);
-#pragma unroll
-                        for (int a = 0; a < 3; ++a) {
-                            pg[a] += gq[a];
-                            ph[a] = fmaf((float)i, gq[a], ph[a]);
-                        }
-                    }
+                    for (int i = 0; i < kGroup; ++i) v[i] = interpolate_grad(A[i], c[i], gq[i]);
+                    float ps, pg[3], ph[3];
+                    group_sums4(v, gq, ps, pg, ph);
                     pose_add_group(k, ps, pg, ph, s0, g0, h1);
                 }
                 for (; k < k0 + S; ++k) {
