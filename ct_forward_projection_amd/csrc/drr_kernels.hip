@@ -249,14 +249,16 @@ constexpr int march_tile_side() { return SPLIT == 1 ? kTile : (SPLIT == 4 ? 8 : 
 // One sample of front-to-back alpha compositing (flashdrr API,
 // VolumeRaycaster.__init__: use_beer_lambert = False): the sample is a slab of
 // thickness dz emitting v with opacity alpha = 1 - exp(-f v dz) behind the
-// transmittance T = exp(-tau) of the samples in front of it.  tau and I run in
-// fp64 so that neither drifts over long rays.
-__device__ inline void composite(float v, float fdz, double& tau, double& I)
+// transmittance T = exp(-tau) of the samples in front of it, carried as the
+// running product T <- T (1 - alpha) = T - T alpha (one fp64 fma, no
+// exponential per sample).  T, tau (the line integral, also returned) and I run
+// in fp64 so that none of them drifts over long rays.
+__device__ inline void composite(float v, float fdz, double& T, double& tau, double& I)
 {
     const float a = fdz * v;
-    const float T = expf(-(float)tau);
     const float alpha = -expm1f(-a);
-    I += (double)(T * alpha * v);
+    I = fma(T, (double)(alpha * v), I);
+    T = fma(-T, (double)alpha, T);
     tau += (double)a;
 }
 
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
         hit = ray_setup_range(G, V, px.r, px.c, N, t_near, t_far, R);
     }
     float s = 0.0f;
-    double tau_c = 0.0, I_c = 0.0;   // compositing
+    double T_c = 1.0, tau_c = 0.0, I_c = 0.0;   // compositing
     if (hit) {
         const char* base = reinterpret_cast<const char*>(src) + (uint64_t)cvol * b.src_stride;
         const __amdgpu_buffer_rsrc_t rs =
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
 #pragma unroll
             for (int i = 0; i < kInflight; ++i) {
                 const float v = ZP ? interpolate_exact(A[i], c[i]) : interpolate(A[i], c[i]);
-                if constexpr (MODE == kAlpha) composite(v, fdz, tau_c, I_c);
+                if constexpr (MODE == kAlpha) composite(v, fdz, T_c, tau_c, I_c);
                 else acc[i] += v;
             }
         }
@@ -357,7 +359,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
             CornerVals c;
             gather<T, L>(rs, A, c);
             const float v = ZP ? interpolate_exact(A, c) : interpolate(A, c);
-            if constexpr (MODE == kAlpha) composite(v, fdz, tau_c, I_c);
+            if constexpr (MODE == kAlpha) composite(v, fdz, T_c, tau_c, I_c);
             else acc[0] += v;
         }
 #pragma unroll
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
     float acc[kInflight];
 #pragma unroll
     for (int i = 0; i < kInflight; ++i) acc[i] = 0.0f;
-    double tau_c = 0.0, I_c = 0.0;
+    double T_c = 1.0, tau_c = 0.0, I_c = 0.0;
 
     int S = N;
     int k0 = 0;
@@ -478,7 +480,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
 #pragma unroll
                     for (int i = 0; i < kInflight; ++i) {
                         const float val = interpolate(A[i], c[i]);
-                        if constexpr (MODE == kAlpha) composite(val, fdz, tau_c, I_c);
+                        if constexpr (MODE == kAlpha) composite(val, fdz, T_c, tau_c, I_c);
                         else acc[i] += val;
                     }
                 }
@@ -492,7 +494,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
                     CornerVals c;
                     box_corners(bx + A.o, sy, sz, c);
                     const float val = interpolate(A, c);
-                    if constexpr (MODE == kAlpha) composite(val, fdz, tau_c, I_c);
+                    if constexpr (MODE == kAlpha) composite(val, fdz, T_c, tau_c, I_c);
                     else acc[0] += val;
                 }
             }
@@ -515,7 +517,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
                     c.v[n] = staged_value<T, TF>(rs, V, ix + (n & 1), iy + ((n >> 1) & 1),
                                                  iz + (n >> 2), tf, ch);
                 const float val = interpolate(A, c);
-                if constexpr (MODE == kAlpha) composite(val, fdz, tau_c, I_c);
+                if constexpr (MODE == kAlpha) composite(val, fdz, T_c, tau_c, I_c);
                 else acc[0] += val;
             }
         }
@@ -661,13 +663,14 @@ __device__ inline void window_add_at(uint32_t at, int wy, int wz, const float w[
 // (the caller's, or the fp32 mapped copy): four x-pair loads with clamp to edge,
 // or eight single loads of the zero-padded cell in the near/far mode (and for
 // volumes one voxel wide); it advances the running state, so samples are
-// visited in order; tau and the running emission are fp64.
+// visited in order; the transmittance (a running product, as in the forward)
+// and the running emission are fp64.
 template <typename T, bool ZP, bool ZPAIR>
 struct AlphaCoef {
     __amdgpu_buffer_rsrc_t rs;
     uint32_t sy, sz;               // element strides of the volume (linear reads)
     float fdz, g;
-    double I, tau, run;
+    double I, trans, run;          // forward image, transmittance, running emission
 
     // mu at a sample from its clamped (or zero-padded) cell: eight loads
     __device__ float value(const Cell& C, const float* m) const
@@ -716,12 +719,11 @@ struct AlphaCoef {
     // the coefficient of the next sample (in order) from its mu
     __device__ float next_of(float v)
     {
-        const float a = fdz * v;
-        const float Tk = expf(-(float)tau);
-        const float alpha = -expm1f(-a);
-        run += (double)(Tk * alpha * v);
+        const float alpha = -expm1f(-(fdz * v));
+        const float Tk = (float)trans;
+        run = fma(trans, (double)(alpha * v), run);
         const float later = (float)(I - run);
-        tau += (double)a;
+        trans = fma(-trans, (double)alpha, trans);
         return g * (Tk * (alpha + fdz * (1.0f - alpha) * v) - fdz * later);
     }
 
@@ -865,7 +867,8 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
         float cmax = fabsf(yd);
         if constexpr (ALPHA) {
             // first pass: the largest coefficient of the ray (NaN if any is not finite)
-            coef.tau = coef.run = 0.0;
+            coef.trans = 1.0;
+            coef.run = 0.0;
             int64_t qx = R.q0[0] + (int64_t)k_lo * R.dq[0];
             int64_t qy = R.q0[1] + (int64_t)k_lo * R.dq[1];
             int64_t qz = R.q0[2] + (int64_t)k_lo * R.dq[2];
@@ -877,7 +880,8 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 cmax = fmaxf(cmax, fabsf(ck));
             }
             if (!finite) cmax = __builtin_nanf("");
-            coef.tau = coef.run = 0.0;
+            coef.trans = 1.0;
+            coef.run = 0.0;
             // a ray whose coefficients are all 0 (through air: emission times
             // opacity is quadratic in mu) adds nothing
             active = cmax != 0.0f;
