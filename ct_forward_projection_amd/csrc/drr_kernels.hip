@@ -223,7 +223,8 @@ __global__ __launch_bounds__(256) void drr_slope_kernel(const Tin* __restrict__ 
 }
 
 // Samples a lane keeps in flight: their gathers are all issued before any is
-// consumed, so each wave has 4 samples' loads outstanding.
+// consumed, so each wave has 4 samples' loads outstanding (8 in the plain
+// z-pair march, see drr_march_kernel).
 constexpr int kInflight = 4;
 
 // Pixel of a thread when SPLIT adjacent lanes share one ray (small launches):
@@ -326,28 +327,36 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
         const int64_t dqz = (int64_t)SPLIT * R.dq[2];
         const int n_mine = k_first < k_hi ? (k_hi - k_first + SPLIT - 1) / SPLIT : 0;
         const float fdz = b.f * R.dz;
+        // samples in flight per group: eight for plain z-pair reads with one ray
+        // per lane, whose loads miss L2 about half the time (16 views of 200^2:
+        // 0.652 -> 0.562 ms fp32, 0.509 -> 0.448 ms bf16); the zero-padded
+        // compositing march (0.404 -> 0.436 ms), x-pair reads (1.64 -> 1.71 ms on
+        // 4 volumes x 2 channels) and split lanes run better with four (fewer
+        // registers, more waves), and ten measured no better than eight
+        constexpr int kGroup =
+            (SPLIT == 1 && L == Layout::ZPair && !ZP && MODE != kAlpha) ? 2 * kInflight : kInflight;
         // independent partial sums, one per in-flight sample: a shorter fp32
         // summation chain as well
-        float acc[kInflight];
+        float acc[kGroup];
 #pragma unroll
-        for (int i = 0; i < kInflight; ++i) acc[i] = 0.0f;
+        for (int i = 0; i < kGroup; ++i) acc[i] = 0.0f;
         int k = 0;
-        for (; k + kInflight <= n_mine; k += kInflight) {
-            SampleAddr A[kInflight];
-            CornerVals c[kInflight];
+        for (; k + kGroup <= n_mine; k += kGroup) {
+            SampleAddr A[kGroup];
+            CornerVals c[kGroup];
 #pragma unroll
-            for (int i = 0; i < kInflight; ++i) {
+            for (int i = 0; i < kGroup; ++i) {
                 A[i] = sample_addr<T, L, ZP>(V, qx, qy, qz);
                 qx += dqx; qy += dqy; qz += dqz;
             }
 #pragma unroll
-            for (int i = 0; i < kInflight; ++i) gather<T, L>(rs, A[i], c[i]);
+            for (int i = 0; i < kGroup; ++i) gather<T, L>(rs, A[i], c[i]);
             // keep every gather of the group ahead of the first use: otherwise
             // the scheduler sinks each sample's loads to just before their use
             // and a wave never has more than one sample's loads in flight
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int i = 0; i < kInflight; ++i) {
+            for (int i = 0; i < kGroup; ++i) {
                 const float v = ZP ? interpolate_exact(A[i], c[i]) : interpolate(A[i], c[i]);
                 if constexpr (MODE == kAlpha) composite(v, fdz, T_c, tau_c, I_c);
                 else acc[i] += v;
@@ -363,7 +372,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
             else acc[0] += v;
         }
 #pragma unroll
-        for (int i = 0; i < kInflight; ++i) s += acc[i];
+        for (int i = 0; i < kGroup; ++i) s += acc[i];
     }
     if constexpr (SPLIT > 1) {
         // all SPLIT lanes of this ray are here (hit or miss alike)
