@@ -23,10 +23,10 @@
 // -t_i e_j, dw/dR_ij = u_i e_j, dC/dt_i = -R_i. (row i), so with y = g dI/ds
 // summed over a view's rays, P = sum y Ac and Q_ij = sum y u_i Bw_j:
 //   dL/dR_ij = -t_i P_j + Q_ij,   dL/dt_i = -sum_a R_ia P_a.
-// The march steps 32.32 fixed-point positions (re-anchored on fp64 every four
-// samples), interpolates in fp32 and accumulates S0, G0 and sum_k k grad mu_k
-// per ray in fp64 (from fp32 sums of four samples); the chain rule runs in fp64
-// and the view sums in fp64 atomics.
+// The march steps 32.32 fixed-point positions (re-anchored on fp64 every eight
+// samples, every four in the LDS-staged march), interpolates in fp32 and
+// accumulates S0, G0 and sum_k k grad mu_k per ray in fp64 (from fp32 sums of
+// each group); the chain rule runs in fp64 and the view sums in fp64 atomics.
 #include <limits.h>
 
 #include "drr_device.hpp"
@@ -112,16 +112,25 @@ __device__ inline int64_t step_fixed(const RayFrame& F, int a)
     return __double2ll_rn(F.dq[a]);
 }
 
-// A group of four samples' terms summed in fp32: ps = sum v_i, pg = sum g_i and
+// A group of NG samples' terms summed in fp32: ps = sum v_i, pg = sum g_i and
 // ph = sum i g_i, formed from the terms themselves (no additions to zero).
-__device__ inline void group_sums4(const float v[4], const float g[4][3], float& ps, float pg[3],
-                                   float ph[3])
+template <int NG>
+__device__ inline void group_sums(const float v[NG], const float g[NG][3], float& ps, float pg[3],
+                                  float ph[3])
 {
-    ps = ((v[0] + v[1]) + v[2]) + v[3];
+    static_assert(NG >= 2, "a group has at least two samples");
+    ps = v[0] + v[1];
+#pragma unroll
+    for (int i = 2; i < NG; ++i) ps += v[i];
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
-        pg[a] = ((g[0][a] + g[1][a]) + g[2][a]) + g[3][a];
-        ph[a] = fmaf(3.0f, g[3][a], fmaf(2.0f, g[2][a], g[1][a]));
+        pg[a] = g[0][a] + g[1][a];
+        ph[a] = g[1][a];
+#pragma unroll
+        for (int i = 2; i < NG; ++i) {
+            pg[a] += g[i][a];
+            ph[a] = fmaf((float)i, g[i][a], ph[a]);
+        }
     }
 }
 
@@ -253,15 +262,17 @@ __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
             __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)src_bytes, kBufferWord3);
         // fp64 ray sums: sum grad mu . d telescopes to about mu(exit) - mu(entry),
         // a small difference of large edge terms that fp32 sums over a whole ray
-        // would round away (a group of four fp32 terms is summed first)
+        // would round away (a group of eight fp32 terms is summed first)
         double s0 = 0.0, g0[3] = {0.0, 0.0, 0.0}, h1[3] = {0.0, 0.0, 0.0};
         // sample positions in 32.32 fixed point.  The gradient of trilinear mu
         // jumps where a sample crosses a cell face, so positions must not
-        // drift from their fp64 values: each group of four starts from its
+        // drift from their fp64 values: each group of eight starts from its
         // first sample evaluated in fp64 and rounded once, and steps by the
-        // rounded increment from there (at most 3.5 2^-32 voxel off)
+        // rounded increment from there (at most 5.5 2^-32 voxel off).  Eight
+        // samples' gathers in flight (against four: 0.596 -> 0.516 ms on 16
+        // views of 200^2 from the z-pair copy)
         const int64_t dqx = step_fixed(F, 0), dqy = step_fixed(F, 1), dqz = step_fixed(F, 2);
-        constexpr int kGroup = 4;
+        constexpr int kGroup = 8;
         int k = 0;
         for (; k + kGroup <= N; k += kGroup) {
             SampleAddr A[kGroup];
@@ -281,7 +292,7 @@ __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) v[i] = interpolate_grad(A[i], c[i], gq[i]);
             float ps, pg[3], ph[3];
-            group_sums4(v, gq, ps, pg, ph);
+            group_sums<kGroup>(v, gq, ps, pg, ph);
             pose_add_group(k, ps, pg, ph, s0, g0, h1);
         }
         for (; k < N; ++k) {
@@ -306,10 +317,10 @@ __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
 // LDS-staged pose gradient (box clip), the forward's staging applied to the
 // pose march: the workgroup loads the box of voxels a chunk of its tile's
 // samples touch (clamped, mapped by the transfer function when TF) and the
-// samples read their corners from LDS.  Positions are those of the linear
-// kernel (each group of four re-anchored on its fp64 position, then stepped
-// by the rounded increment, at most 2.5 fixed-point units from each sample's
-// own fp64 position), so the chunk box is widened by 4 units each way.
+// samples read their corners from LDS.  Positions are stepped as in the linear
+// kernel but in groups of four (each re-anchored on its fp64 position, then
+// stepped by the rounded increment, at most 2.5 fixed-point units from each
+// sample's own fp64 position), so the chunk box is widened by 4 units each way.
 template <typename T, int MODE, bool TF>
 __global__ __launch_bounds__(kBlock) void drr_pose_staged_kernel(
     const T* __restrict__ src, uint32_t src_bytes, VolumeDesc V, Intrinsics K,
@@ -404,7 +415,7 @@ __global__ __launch_bounds__(kBlock) void drr_pose_staged_kernel(
 #pragma unroll
                     for (int i = 0; i < kGroup; ++i) v[i] = interpolate_grad(A[i], c[i], gq[i]);
                     float ps, pg[3], ph[3];
-                    group_sums4(v, gq, ps, pg, ph);
+                    group_sums<kGroup>(v, gq, ps, pg, ph);
                     pose_add_group(k, ps, pg, ph, s0, g0, h1);
                 }
                 for (; k < k0 + S; ++k) {
