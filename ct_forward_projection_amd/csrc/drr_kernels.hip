@@ -758,6 +758,29 @@ struct AlphaCoef {
         if constexpr (ZP) pad_mask(V, qx, qy, qz, m);
         return next(C, m);
     }
+
+    // ZPAIR: the coefficients of the next G samples (in order) at q, q + dq,
+    // ..., with all G samples' gathers issued before the first is used (one
+    // sample at a time leaves each load's latency exposed)
+    template <int G>
+    __device__ void next_group(const VolumeDesc& Vc, int64_t qx, int64_t qy, int64_t qz,
+                               int64_t dqx, int64_t dqy, int64_t dqz, float out[G])
+    {
+        static_assert(ZPAIR, "grouped coefficients read the z-pair copy");
+        SampleAddr A[G];
+        CornerVals c[G];
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            A[i] = sample_addr<T, Layout::ZPair, ZP>(Vc, qx, qy, qz);
+            qx += dqx; qy += dqy; qz += dqz;
+        }
+#pragma unroll
+        for (int i = 0; i < G; ++i) gather<T, Layout::ZPair>(rs, A[i], c[i]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < G; ++i)
+            out[i] = next_of(ZP ? interpolate_exact(A[i], c[i]) : interpolate(A[i], c[i]));
+    }
 };
 
 // Backward scatter with LDS pre-reduction in fixed point.
@@ -882,7 +905,22 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
             int64_t qy = R.q0[1] + (int64_t)k_lo * R.dq[1];
             int64_t qz = R.q0[2] + (int64_t)k_lo * R.dq[2];
             bool finite = true;
-            for (int k = k_lo; k < k_hi; ++k) {
+            int k = k_lo;
+            if constexpr (ZPAIR) {
+                for (; k + kInflight <= k_hi; k += kInflight) {
+                    float ck[kInflight];
+                    coef.template next_group<kInflight>(Vc, qx, qy, qz, R.dq[0], R.dq[1],
+                                                        R.dq[2], ck);
+                    qx += kInflight * R.dq[0]; qy += kInflight * R.dq[1];
+                    qz += kInflight * R.dq[2];
+#pragma unroll
+                    for (int i = 0; i < kInflight; ++i) {
+                        finite = finite && isfinite(ck[i]);
+                        cmax = fmaxf(cmax, fabsf(ck[i]));
+                    }
+                }
+            }
+            for (; k < k_hi; ++k) {
                 const float ck = coef.next_at(V, Vc, qx, qy, qz);
                 qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
                 finite = finite && isfinite(ck);
@@ -1003,7 +1041,8 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 float acc[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] = start;
-                auto sample = [&](int64_t& qx, int64_t& qy, int64_t& qz) {
+                // ca: the compositing coefficient of the sample (ALPHA)
+                auto sample = [&](int64_t& qx, int64_t& qy, int64_t& qz, float ca) {
                     const int fx = fixed_floor(qx), fy = fixed_floor(qy), fz = fixed_floor(qz);
                     float c = ys;
                     int base;
@@ -1013,7 +1052,7 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                         const int ix = clampi(fx, -1, V.n[0] - 1);
                         const int iy = clampi(fy, -1, V.n[1] - 1);
                         const int iz = clampi(fz, -1, V.n[2] - 1);
-                        if constexpr (ALPHA) c = coef.next_at(V, Vc, qx, qy, qz) * scale;
+                        if constexpr (ALPHA) c = ca * scale;
                         if constexpr (ZP) {
                             // a sample with every corner outside the volume adds nothing
                             if (fx != ix || fy != iy || fz != iz) c = 0.0f;
@@ -1048,12 +1087,26 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                         // two samples per trip: the cell register alternates
                         // without a copy
                         for (int j = 0; j + 1 < part; j += 2) {
-                            sample(qx, qy, qz);
-                            sample(qx, qy, qz);
+                            sample(qx, qy, qz, 0.0f);
+                            sample(qx, qy, qz, 0.0f);
                         }
-                        if (part & 1) sample(qx, qy, qz);
+                        if (part & 1) sample(qx, qy, qz, 0.0f);
                     } else {
-                        for (int k = ka; k < kb; ++k) sample(qx, qy, qz);
+                        int k = ka;
+                        if constexpr (ALPHA && ZPAIR) {
+                            for (; k + kInflight <= kb; k += kInflight) {
+                                float ca[kInflight];
+                                coef.template next_group<kInflight>(Vc, qx, qy, qz, R.dq[0],
+                                                                    R.dq[1], R.dq[2], ca);
+#pragma unroll
+                                for (int i = 0; i < kInflight; ++i) sample(qx, qy, qz, ca[i]);
+                            }
+                        }
+                        for (; k < kb; ++k) {
+                            float ca = 0.0f;
+                            if constexpr (ALPHA) ca = coef.next_at(V, Vc, qx, qy, qz);
+                            sample(qx, qy, qz, ca);
+                        }
                     }
                 }
                 if (pbase >= 0) window_add_at<REBASE>((uint32_t)pbase, wy4, wz4, acc);
