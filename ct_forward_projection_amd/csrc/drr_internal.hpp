@@ -165,6 +165,7 @@ struct BackwardRead {
     bool zpair, padded, mapped;
     int read_elem;
     size_t per_volume_bytes, workspace_bytes;
+    size_t bound_offset;   // with a copy: the value bounds after the copies (else 0)
 };
 
 inline BackwardRead plan_backward(int n_volumes, int C, int nz, int ny, int nx, int elem_bytes,
@@ -192,6 +193,13 @@ inline BackwardRead plan_backward(int n_volumes, int C, int nz, int ny, int nx, 
     }
     r.per_volume_bytes = ((size_t)bytes + 255) & ~(size_t)255;
     r.workspace_bytes = r.per_volume_bytes * (size_t)n_volumes * (size_t)C;
+    // with a copy, one (flag, maximum) int pair per channel-volume of the
+    // values the coefficient passes read, which bounds every coefficient in
+    // closed form (drr_value_bound_kernel)
+    if (r.workspace_bytes > 0) {
+        r.bound_offset = r.workspace_bytes;
+        r.workspace_bytes += ((size_t)8 * n_volumes * C + 255) & ~(size_t)255;
+    }
     return r;
 }
 

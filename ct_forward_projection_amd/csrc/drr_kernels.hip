@@ -22,6 +22,9 @@
 //                       when a mapped volume is marched without cells.
 //   drr_slope_kernel    the backward's last step with a transfer function:
 //                       dL/dx = dL/dmu tf'(x) per voxel.
+//   drr_value_bound_kernel  the largest value of what the compositing backward
+//                       reads, and whether any is negative or not finite: a
+//                       closed-form bound on its coefficients.
 //                       The compositing backward runs in the same kernel: each
 //                       sample is gathered again for its own coefficient.
 //
@@ -219,6 +222,35 @@ __global__ __launch_bounds__(256) void drr_slope_kernel(const Tin* __restrict__ 
         float m;
         transfer_eval(tf, ch, widen(vol[i]), m);
         grad[i] *= m;
+    }
+}
+
+// Value bounds of a compositing backward's read copy, per channel-volume
+// (blockIdx.y; n_elem values every `stride` values): out[2 cv] turns non-zero
+// if any value is negative or not finite, out[2 cv + 1] is raised to the bit
+// pattern of the largest value (non-negative floats order as their bits).
+// out starts at zero.
+template <typename T>
+__global__ __launch_bounds__(256) void drr_value_bound_kernel(const T* __restrict__ src,
+                                                              size_t n_elem, size_t stride,
+                                                              int* __restrict__ out)
+{
+    const int cv = (int)blockIdx.y;
+    src += (size_t)cv * stride;
+    float vmax = 0.0f;
+    bool bad = false;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_elem;
+         i += (size_t)gridDim.x * blockDim.x) {
+        const float v = widen(src[i]);
+        bad = bad || !(v >= 0.0f) || !isfinite(v);          // NaN fails v >= 0
+        vmax = fmaxf(vmax, v);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off, 64));
+    const bool any_bad = __ballot(bad) != 0;
+    if ((threadIdx.x & 63) == 0) {
+        if (any_bad) atomicOr(out + 2 * cv, 1);
+        atomicMax(out + 2 * cv + 1, __float_as_int(vmax));
     }
 }
 
@@ -824,7 +856,7 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
     int tiles_x, int tiles_per_view, Batch bt, const float* __restrict__ grad_out,
     const float* __restrict__ s_in, const float* __restrict__ out_in,
     const T* __restrict__ vol, uint32_t vol_bytes, uint32_t copy_row, uint32_t copy_slice,
-    float* __restrict__ grad, int win_cap)
+    const int* __restrict__ vbound, float* __restrict__ grad, int win_cap)
 {
     constexpr bool ZP = CLIP == kClipNearFar;
     constexpr bool ALPHA = MODE == kAlpha;
@@ -898,35 +930,50 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
         const double n = fmin((double)N, floor(2.0 / dq_inf) + 1.0);
         float cmax = fabsf(yd);
         if constexpr (ALPHA) {
-            // first pass: the largest coefficient of the ray (NaN if any is not finite)
-            coef.trans = 1.0;
-            coef.run = 0.0;
-            int64_t qx = R.q0[0] + (int64_t)k_lo * R.dq[0];
-            int64_t qy = R.q0[1] + (int64_t)k_lo * R.dq[1];
-            int64_t qz = R.q0[2] + (int64_t)k_lo * R.dq[2];
-            bool finite = true;
-            int k = k_lo;
-            if constexpr (ZPAIR) {
-                for (; k + kInflight <= k_hi; k += kInflight) {
-                    float ck[kInflight];
-                    coef.template next_group<kInflight>(Vc, qx, qy, qz, R.dq[0], R.dq[1],
-                                                        R.dq[2], ck);
-                    qx += kInflight * R.dq[0]; qy += kInflight * R.dq[1];
-                    qz += kInflight * R.dq[2];
+            // With values v >= 0 (so 0 <= alpha <= f v dz, T <= 1) and f >= 0,
+            // a coefficient g (T (alpha + f dz (1 - alpha) v) - f dz later) is a
+            // difference of two non-negative terms bounded by 2 f dz vmax and
+            // f dz I, so |c| <= |g| f dz max(2 vmax, I) (with a margin for
+            // rounding) without visiting the samples; otherwise (a negative or
+            // non-finite value, or no bounds) a first pass takes the largest
+            // coefficient of the ray (NaN if any is not finite).
+            const float fdz = coef.fdz;
+            if (vbound != nullptr && vbound[2 * cvol] == 0 && fdz >= 0.0f) {
+                const float vmax = __int_as_float(vbound[2 * cvol + 1]);
+                const float I = (float)coef.I;
+                cmax = (isfinite(I) && isfinite(coef.g))
+                           ? fabsf(coef.g) * fdz * fmaxf(2.0f * vmax, fabsf(I)) * 1.0625f
+                           : __builtin_nanf("");
+            } else {
+                coef.trans = 1.0;
+                coef.run = 0.0;
+                int64_t qx = R.q0[0] + (int64_t)k_lo * R.dq[0];
+                int64_t qy = R.q0[1] + (int64_t)k_lo * R.dq[1];
+                int64_t qz = R.q0[2] + (int64_t)k_lo * R.dq[2];
+                bool finite = true;
+                int k = k_lo;
+                if constexpr (ZPAIR) {
+                    for (; k + kInflight <= k_hi; k += kInflight) {
+                        float ck[kInflight];
+                        coef.template next_group<kInflight>(Vc, qx, qy, qz, R.dq[0], R.dq[1],
+                                                            R.dq[2], ck);
+                        qx += kInflight * R.dq[0]; qy += kInflight * R.dq[1];
+                        qz += kInflight * R.dq[2];
 #pragma unroll
-                    for (int i = 0; i < kInflight; ++i) {
-                        finite = finite && isfinite(ck[i]);
-                        cmax = fmaxf(cmax, fabsf(ck[i]));
+                        for (int i = 0; i < kInflight; ++i) {
+                            finite = finite && isfinite(ck[i]);
+                            cmax = fmaxf(cmax, fabsf(ck[i]));
+                        }
                     }
                 }
+                for (; k < k_hi; ++k) {
+                    const float ck = coef.next_at(V, Vc, qx, qy, qz);
+                    qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
+                    finite = finite && isfinite(ck);
+                    cmax = fmaxf(cmax, fabsf(ck));
+                }
+                if (!finite) cmax = __builtin_nanf("");
             }
-            for (; k < k_hi; ++k) {
-                const float ck = coef.next_at(V, Vc, qx, qy, qz);
-                qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
-                finite = finite && isfinite(ck);
-                cmax = fmaxf(cmax, fabsf(ck));
-            }
-            if (!finite) cmax = __builtin_nanf("");
             coef.trans = 1.0;
             coef.run = 0.0;
             // a ray whose coefficients are all 0 (through air: emission times
@@ -1524,7 +1571,7 @@ static void launch_scatter(const LaunchArgs& a, const Batch& b, const float* gra
                            const float* s_in, const float* out_in, const T* vol,
                            uint32_t vol_bytes, float* grad, int tiles_x, int tiles_per_view,
                            int n_tiles, hipStream_t stream, uint32_t copy_row = 0,
-                           uint32_t copy_slice = 0)
+                           uint32_t copy_slice = 0, const int* vbound = nullptr)
 {
     const double cells = (double)(a.V.n[0] + 1) * (a.V.n[1] + 1) * (a.V.n[2] + 1);
     const int cap = window_cap((double)a.H * a.W * a.N / cells);
@@ -1533,12 +1580,27 @@ static void launch_scatter(const LaunchArgs& a, const Batch& b, const float* gra
         hipLaunchKernelGGL((drr_scatter_kernel<MODE, kClipNearFar, T, ZPAIR>), dim3(n_tiles),
                            dim3(kBlock), lds, stream, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
                            tiles_per_view, b, grad_out, s_in, out_in, vol, vol_bytes, copy_row,
-                           copy_slice, grad, cap);
+                           copy_slice, vbound, grad, cap);
     else
         hipLaunchKernelGGL((drr_scatter_kernel<MODE, kClipBox, T, ZPAIR>), dim3(n_tiles),
                            dim3(kBlock), lds, stream, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
                            tiles_per_view, b, grad_out, s_in, out_in, vol, vol_bytes, copy_row,
-                           copy_slice, grad, cap);
+                           copy_slice, vbound, grad, cap);
+}
+
+// Value bounds of a read copy (n_elem values of type T every `stride` values per
+// channel-volume) into `vbound` (two ints per channel-volume), zeroed first.
+template <typename T>
+static hipError_t launch_value_bound(const LaunchArgs& a, const T* src, size_t n_elem,
+                                     size_t stride, int* vbound, hipStream_t stream)
+{
+    const int n_cv = a.n_volumes * a.C;
+    hipError_t e = launch_fill(reinterpret_cast<float*>(vbound), 2 * (size_t)n_cv, stream);
+    if (e != hipSuccess) return e;
+    const dim3 grid(grid_blocks((long long)n_elem, 2048), n_cv);
+    hipLaunchKernelGGL((drr_value_bound_kernel<T>), grid, dim3(256), 0, stream, src, n_elem,
+                       stride, vbound);
+    return hipGetLastError();
 }
 
 template <typename Tin>
@@ -1572,16 +1634,24 @@ static hipError_t backward_typed(const LaunchArgs& a, const Tin* vol, const floa
             const uint32_t slice = (r.padded ? ny + 2 : ny) * row;
             const uint32_t total = (r.padded ? nz + 1 : nz - 1) * slice;
             const Batch b = make_batch(a, &p, 0);
-            if (r.mapped)
-                launch_scatter<kAlpha, float, true>(a, b, grad_out, s_in, out_in,
-                                                    static_cast<const float*>(workspace), total,
-                                                    grad, tiles_x, tiles_per_view, n_tiles, stream,
-                                                    row, slice);
-            else
-                launch_scatter<kAlpha, Tin, true>(a, b, grad_out, s_in, out_in,
-                                                  static_cast<const Tin*>(workspace), total, grad,
+            int* vbound = reinterpret_cast<int*>(static_cast<char*>(workspace) + r.bound_offset);
+            if (r.mapped) {
+                const float* cp = static_cast<const float*>(workspace);
+                e = launch_value_bound<float>(a, cp, total / eb, r.per_volume_bytes / eb, vbound,
+                                              stream);
+                if (e != hipSuccess) return e;
+                launch_scatter<kAlpha, float, true>(a, b, grad_out, s_in, out_in, cp, total, grad,
+                                                    tiles_x, tiles_per_view, n_tiles, stream, row,
+                                                    slice, vbound);
+            } else {
+                const Tin* cp = static_cast<const Tin*>(workspace);
+                e = launch_value_bound<Tin>(a, cp, total / eb, r.per_volume_bytes / eb, vbound,
+                                            stream);
+                if (e != hipSuccess) return e;
+                launch_scatter<kAlpha, Tin, true>(a, b, grad_out, s_in, out_in, cp, total, grad,
                                                   tiles_x, tiles_per_view, n_tiles, stream, row,
-                                                  slice);
+                                                  slice, vbound);
+            }
         } else if (a.has_tf) {
             // gather the mapped volumes: their fp32 copy in the workspace
             RenderPlan p{};
@@ -1590,10 +1660,13 @@ static hipError_t backward_typed(const LaunchArgs& a, const Tin* vol, const floa
             float* mu = static_cast<float*>(workspace);
             e = launch_transfer_typed<Tin>(a, p, vol, mu, stream);
             if (e != hipSuccess) return e;
+            int* vbound = reinterpret_cast<int*>(static_cast<char*>(workspace) + r.bound_offset);
+            e = launch_value_bound<float>(a, mu, n_vox, p.per_volume_bytes / 4, vbound, stream);
+            if (e != hipSuccess) return e;
             const Batch b = make_batch(a, &p, 0);
             launch_scatter<kAlpha, float>(a, b, grad_out, s_in, out_in, mu,
                                           (uint32_t)(n_vox * 4), grad, tiles_x, tiles_per_view,
-                                          n_tiles, stream);
+                                          n_tiles, stream, 0, 0, vbound);
         } else {
             const Batch b = make_batch(a, nullptr, n_vox * sizeof(Tin));
             launch_scatter<kAlpha, Tin>(a, b, grad_out, s_in, out_in, vol,

@@ -224,8 +224,10 @@ int drr_backward_volume_siddon(int nz, int ny, int nx, const float *spacing, con
  * zero-padded in the near/far mode, which always reads a copy -- or for the
  * mapped fp32 volumes; the compositing backward for a z-pair copy its
  * coefficient passes read (from about one sample per cell), or for the mapped
- * fp32 volumes with a transfer function.  Values are mapped by the transfer
- * function in every copy. */
+ * fp32 volumes with a transfer function, followed by 8 bytes per channel-volume
+ * (rounded up to 256) for the largest value of that copy, which bounds the
+ * coefficients without a pass over the samples.  Values are mapped by the
+ * transfer function in every copy. */
 size_t drr_render_workspace_bytes(int n_volumes, int n_channels, int nz, int ny, int nx,
                                   int dtype, int n_views, int det_h, int det_w, int n_samples,
                                   int mode, int clip, int tf_knots, int for_backward);

@@ -261,14 +261,19 @@ def test_render_empty_call_and_workspace_queries():
     assert q(1, 1, 1, 8, 8, 0, 4, 8, 8, 4, 0, 0, 0, 0) == 0
     # compositing backward: under one sample per cell the mapped fp32 volumes with
     # a transfer function (else none); from one per cell a z-pair copy for its
-    # coefficient passes, zero-padded in the near/far mode; other modes none
-    assert q(1, 2, 8, 8, 8, 0, 1, 4, 4, 8, 2, 0, 3, 1) == 2 * 2048
+    # coefficient passes, zero-padded in the near/far mode; other modes none.
+    # After a copy, 8 bytes per channel-volume (in 256) for its largest value
+    bound = 256
+    assert q(1, 2, 8, 8, 8, 0, 1, 4, 4, 8, 2, 0, 3, 1) == 2 * 2048 + bound
     assert q(1, 2, 8, 8, 8, 0, 1, 4, 4, 8, 2, 0, 0, 1) == 0
     assert q(1, 2, 8, 8, 8, 0, 1, 4, 4, 8, 0, 0, 3, 1) == 0
-    assert q(1, 1, 8, 8, 8, 0, 4, 8, 8, 16, 2, 0, 0, 1) == 8 * 8 * 7 * 2 * 4
-    assert q(1, 1, 8, 8, 8, 1, 4, 8, 8, 16, 2, 0, 0, 1) == 8 * 8 * 7 * 2 * 2
-    assert q(1, 1, 8, 8, 8, 1, 4, 8, 8, 16, 2, 0, 3, 1) == 8 * 8 * 7 * 2 * 4
-    assert q(1, 1, 8, 8, 8, 0, 4, 8, 8, 16, 2, 1, 0, 1) == ((10 * 10 * 9 * 2 * 4 + 255) // 256) * 256
+    assert q(1, 1, 8, 8, 8, 0, 4, 8, 8, 16, 2, 0, 0, 1) == 8 * 8 * 7 * 2 * 4 + bound
+    assert q(1, 1, 8, 8, 8, 1, 4, 8, 8, 16, 2, 0, 0, 1) == 8 * 8 * 7 * 2 * 2 + bound
+    assert q(1, 1, 8, 8, 8, 1, 4, 8, 8, 16, 2, 0, 3, 1) == 8 * 8 * 7 * 2 * 4 + bound
+    assert q(1, 1, 8, 8, 8, 0, 4, 8, 8, 16, 2, 1, 0, 1) == \
+        ((10 * 10 * 9 * 2 * 4 + 255) // 256) * 256 + bound
+    # 33 channel-volumes need 264 bytes of bounds: two 256-byte blocks
+    assert q(1, 33, 8, 8, 8, 0, 4, 8, 8, 16, 2, 0, 0, 1) == 33 * 8 * 8 * 7 * 2 * 4 + 512
     assert q(1, 1, 8, 8, 8, 0, 4, 8, 8, 16, 0, 1, 0, 1) == 0
     assert q(2, 1, 8, 8, 8, 0, 3, 4, 4, 8, 0, 0, 0, 0) == 0     # views not a multiple
     # the single-volume call's plan is drr_forward's

@@ -269,7 +269,8 @@ def test_render_sparse_near_far_compositing(dev, tf):
     transfer = knots(2) if tf else None
     ws_b = drr.drr_render_workspace_bytes(B, C, nz, ny, nx, 0, poses.shape[0], H, Wd, N, ALPHA,
                                           NEAR_FAR, 3 if tf else 0, 1)
-    assert ws_b == (B * C * ((nx * ny * nz * 4 + 255) // 256 * 256) if tf else 0)
+    # with a transfer function the mapped fp32 volumes and their value bounds
+    assert ws_b == (B * C * ((nx * ny * nz * 4 + 255) // 256 * 256) + 256 if tf else 0)
     say(f"case: sparse near/far compositing tf={tf}")
     f = 30.0 if tf else 1.1
     img, tau, grad = run_gpu(dev, vol, spacing, K, poses, H, Wd, N, ALPHA, f, NEAR_FAR, 3.0,
@@ -278,6 +279,28 @@ def test_render_sparse_near_far_compositing(dev, tf):
     ref, ref_tau = oracle.render(vol, spacing, K, poses, H, Wd, N, ALPHA, **kw)
     ref_g = oracle.render_adjoint(vol, spacing, K, poses, H, Wd, N, ALPHA, g, **kw)
     check(img, tau, grad, ref, ref_tau, ref_g, f"sparse near/far alpha tf{int(tf)}")
+
+
+@pytest.mark.parametrize("clip", [BOX, NEAR_FAR])
+@pytest.mark.parametrize("shift,f", [(0.0, 1.1), (-0.3, 1.1), (0.0, -0.4)])
+def test_render_compositing_backward_bound_paths(dev, clip, shift, f):
+    """The compositing backward bounds its coefficients in closed form from the
+    largest value of its z-pair copy when every value is finite and >= 0 and the
+    density factor is >= 0; negative values (shift -0.3: values in [-0.25, 0.7))
+    or a negative density factor take the pass over the samples instead.  Each
+    against the oracle."""
+    vol, spacing, K, poses, H, Wd, N, g = problem(400 + clip, N=37)
+    vol = (vol + np.float32(shift)).astype(np.float32)
+    B, C, nz, ny, nx = vol.shape
+    ws_b = drr.drr_render_workspace_bytes(B, C, nz, ny, nx, 0, poses.shape[0], H, Wd, N, ALPHA,
+                                          clip, 0, 1)
+    assert ws_b > 0                                 # a z-pair copy and its bounds
+    say(f"case: compositing backward bound clip={clip} shift={shift} f={f}")
+    img, tau, grad = run_gpu(dev, vol, spacing, K, poses, H, Wd, N, ALPHA, f, clip, 3.0, None, g)
+    kw = dict(density_factor=f, clip=clip, margin=3.0, transfer=None)
+    ref, ref_tau = oracle.render(vol, spacing, K, poses, H, Wd, N, ALPHA, **kw)
+    ref_g = oracle.render_adjoint(vol, spacing, K, poses, H, Wd, N, ALPHA, g, **kw)
+    check(img, tau, grad, ref, ref_tau, ref_g, f"compositing bound clip{clip} {shift} {f}")
 
 
 @pytest.mark.parametrize("N", [6, 64])
