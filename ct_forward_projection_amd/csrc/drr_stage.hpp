@@ -96,6 +96,42 @@ __device__ inline void stage_fill(float* box, int n, __amdgpu_buffer_rsrc_t rs,
     BoxWalk bw(ext);
     int i = threadIdx.x;
     constexpr int kFill = 8;
+    bool interior = true;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) interior = interior && lo[a] >= 0 && lo[a] + ext[a] <= V.n[a];
+    if (interior) {
+        // every entry is a voxel: no clamping, and the element offset steps
+        // with the walk
+        BoxAddr ba(bw, lo, (uint32_t)V.n[0], (uint32_t)V.n[0] * (uint32_t)V.n[1]);
+        auto value = [&](uint32_t off) {
+            const float v = load_one<T>(rs, off * (uint32_t)sizeof(T));
+            if constexpr (TF) {
+                float m;
+                return transfer_eval(tf, ch, v, m);
+            } else {
+                return v;
+            }
+        };
+        for (; i + (kFill - 1) * kBlock < n; i += kFill * kBlock) {
+            float v[kFill];
+#pragma unroll
+            for (int u = 0; u < kFill; ++u) {
+                v[u] = value(ba.addr);
+                int cx, cy;
+                bw.next(cx, cy);
+                ba.next(cx, cy);
+            }
+#pragma unroll
+            for (int u = 0; u < kFill; ++u) box[i + u * kBlock] = v[u];
+        }
+        for (; i < n; i += kBlock) {
+            box[i] = value(ba.addr);
+            int cx, cy;
+            bw.next(cx, cy);
+            ba.next(cx, cy);
+        }
+        return;
+    }
     for (; i + (kFill - 1) * kBlock < n; i += kFill * kBlock) {
         float v[kFill];
 #pragma unroll
