@@ -831,7 +831,8 @@ struct AlphaCoef {
 // adds.  The scale 2^e is chosen per tile so that no window entry overflows:
 // one sample puts at most |c| on any voxel (c its coefficient: y dz for a
 // whole ray in the Beer-Lambert and line-integral backward, c_k per sample in
-// the compositing one, bounded by a first pass over the ray) and a ray has at
+// the compositing one, bounded in closed form from the largest value read, or
+// by a first pass over the ray when values can be negative) and a ray has at
 // most n = min(N, floor(2 / |dq|_inf) + 1) samples inside a voxel's 2 x 2 x 2
 // support, so an entry never exceeds B = sum over the tile's rays of
 // max|c| n, and 2^e B <= 2^30.  (|y dz| n is about |y| times the ray's
