@@ -105,9 +105,12 @@ __global__ __launch_bounds__(256) void drr_cells_kernel(const Tin* __restrict__ 
 
 // Z-pair relayout: element (x, y, z) of the copy, 0 <= z <= nz - 2, holds
 // voxels (x, y, z) and (x, y, z + 1) side by side (mapped by channel c's
-// transfer function into fp32 with TF).  One thread per element, consecutive
-// threads on consecutive x: both reads and the paired write are coalesced.
-// blockIdx.y = channel-volume (b * C + c).
+// transfer function into fp32 with TF).  Each thread takes a run of up to
+// kZRun pairs down one (x, y) column (blockIdx.z: the run, blockIdx.y: the
+// channel-volume), so every voxel is read and mapped once; consecutive threads
+// on consecutive x keep reads and writes coalesced.
+constexpr int kZRun = 8;
+
 template <typename Tin, typename Tout, bool TF>
 __global__ __launch_bounds__(256) void drr_zpair_kernel(const Tin* __restrict__ vol, int nx,
                                                         int ny, int nz, size_t in_stride,
@@ -116,25 +119,41 @@ __global__ __launch_bounds__(256) void drr_zpair_kernel(const Tin* __restrict__ 
 {
     static_assert(TF || sizeof(Tin) == sizeof(Tout), "no transfer: pairs keep the dtype");
     const int cv = (int)blockIdx.y, ch = cv % C;
-    vol += (size_t)cv * in_stride;
-    pairs += (size_t)cv * out_stride;
     const size_t slice = (size_t)nx * ny;
-    const size_t n = slice * (size_t)(nz - 1);
-    for (size_t id = (size_t)blockIdx.x * blockDim.x + threadIdx.x; id < n;
-         id += (size_t)gridDim.x * blockDim.x) {
-        Tout lo, hi;
+    const size_t xy = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (xy >= slice) return;
+    const int z0 = (int)blockIdx.z * kZRun, z1 = min(z0 + kZRun, nz - 1);
+    vol += (size_t)cv * in_stride + xy;
+    pairs += (size_t)cv * out_stride;                // pair (z, xy) is pair z slice + xy
+    auto value = [&](int z) -> Tout {
         if constexpr (TF) {
             float m;
-            lo = transfer_eval(tf, ch, widen(vol[id]), m);
-            hi = transfer_eval(tf, ch, widen(vol[id + slice]), m);
+            return transfer_eval(tf, ch, widen(vol[(size_t)z * slice]), m);
         } else {
-            lo = vol[id];
-            hi = vol[id + slice];
+            return vol[(size_t)z * slice];
         }
+    };
+    auto store = [&](int z, Tout lo, Tout hi) {
+        const size_t id = (size_t)z * slice + xy;
         if constexpr (sizeof(Tout) == 4) {
             reinterpret_cast<float2*>(pairs)[id] = make_float2(lo, hi);
         } else {
             reinterpret_cast<uint32_t*>(pairs)[id] = (uint32_t)lo | ((uint32_t)hi << 16);
+        }
+    };
+    if (z1 - z0 == kZRun) {
+        // a full run: all kZRun + 1 loads issued before the first store
+        Tout v[kZRun + 1];
+#pragma unroll
+        for (int i = 0; i <= kZRun; ++i) v[i] = value(z0 + i);
+#pragma unroll
+        for (int i = 0; i < kZRun; ++i) store(z0 + i, v[i], v[i + 1]);
+    } else {
+        Tout lo = value(z0);
+        for (int z = z0; z < z1; ++z) {
+            const Tout hi = value(z + 1);
+            store(z, lo, hi);
+            lo = hi;
         }
     }
 }
@@ -1407,8 +1426,9 @@ static hipError_t launch_zpair_typed(const LaunchArgs& a, const RenderPlan& p, c
                                a.tf);
         return hipGetLastError();
     }
-    const long long n = (long long)a.V.n[0] * a.V.n[1] * (a.V.n[2] - 1);
-    const dim3 grid(grid_blocks(n, 16384), a.n_volumes * a.C);
+    const long long slice = (long long)a.V.n[0] * a.V.n[1];
+    const dim3 grid((unsigned)((slice + 255) / 256), a.n_volumes * a.C,
+                    (unsigned)((a.V.n[2] - 1 + kZRun - 1) / kZRun));
     const size_t in_stride = (size_t)a.V.n[0] * a.V.n[1] * a.V.n[2];
     if (p.mapped)
         hipLaunchKernelGGL((drr_zpair_kernel<Tin, float, true>), grid, dim3(256), 0, stream, vol,
