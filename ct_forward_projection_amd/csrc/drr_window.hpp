@@ -22,13 +22,23 @@ namespace drr {
 // Measured on MI355X (1024^2 step / 360-view helix / 16-view 200^2 batch):
 // 4096 entries 1.15 / 27.9 / - ms, 6144 1.12 / 19.9 / 7.37, 8192
 // 1.19 / 21.4 / 4.96, 12288 1.28 / 23.8 / 3.08, 16384 - / - / 2.81,
-// 24576 2.68 / 56.0 / 4.89.
+// 24576 2.68 / 56.0 / 4.89.  With the later scatter (register sums started on
+// the lane's own cell, uniform trip counts, flush reads ahead) views between
+// 4 and 16 samples per cell run better on 7168 entries (five workgroups per
+// CU): the helix (11.7 per view) 15.2 -> 12.1 ms, its cell-constant backward
+// 11.9 -> 11.4 ms, the 1024^2 step (31.6) unchanged at 6144 (7168: 0.577 ->
+// 0.591 ms; 8192 and 10240 slowed the 1024^2 cell-constant backward, 9.6
+// pieces per cell: 0.60 -> 0.65 / 0.73 ms).
 constexpr int kWinCapDense = 6144;
+constexpr int kWinCapMid = 7168;
 constexpr int kWinCapSparse = 16000;
 
 // Window entries for a launch whose views each put `view_reuse` samples (or
 // ray-voxel pieces) per cell of the volume.
-inline int window_cap(double view_reuse) { return view_reuse >= 4.0 ? kWinCapDense : kWinCapSparse; }
+inline int window_cap(double view_reuse)
+{
+    return view_reuse >= 16.0 ? kWinCapDense : (view_reuse >= 4.0 ? kWinCapMid : kWinCapSparse);
+}
 
 // Position (x, y, z) of entry i = threadIdx.x + n kBlock of a box of
 // ext[0] x ext[1] x ... entries (x fastest), advanced kBlock entries per
