@@ -462,6 +462,9 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
     const float* __restrict__ poses, int H, int W, int N, int tiles_x, int tiles_per_view,
     Batch b, TransferFn tf, float* __restrict__ out, float* __restrict__ s_out)
 {
+    // samples per group of the box march: LDS reads are short, and groups of
+    // two measured best (1024^2: 4 -> 2 samples 0.438 -> 0.433 ms, 8: 0.470 ms)
+    constexpr int kStagedGroup = 2;
     __shared__ float box[kStageCap];
     __shared__ int red[(kBlock / 64) * 6];
     __shared__ int bb[6];
@@ -481,9 +484,9 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)src_bytes, kBufferWord3);
     const float fdz = hit ? b.f * R.dz : 0.0f;
-    float acc[kInflight];
+    float acc[kStagedGroup];
 #pragma unroll
-    for (int i = 0; i < kInflight; ++i) acc[i] = 0.0f;
+    for (int i = 0; i < kStagedGroup; ++i) acc[i] = 0.0f;
     double T_c = 1.0, tau_c = 0.0, I_c = 0.0;
 
     int S = N;
@@ -523,11 +526,11 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
                 const uint32_t sy = 4u * (uint32_t)ey, sz = 4u * (uint32_t)ez;
                 const char* bx = reinterpret_cast<const char*>(box);
                 int k = k0;
-                for (; k + kInflight <= k0 + S; k += kInflight) {
-                    SampleAddr A[kInflight];
-                    CornerVals c[kInflight];
+                for (; k + kStagedGroup <= k0 + S; k += kStagedGroup) {
+                    SampleAddr A[kStagedGroup];
+                    CornerVals c[kStagedGroup];
 #pragma unroll
-                    for (int i = 0; i < kInflight; ++i) {
+                    for (int i = 0; i < kStagedGroup; ++i) {
                         A[i].fx = fixed_frac(qx);
                         A[i].fy = fixed_frac(qy);
                         A[i].fz = fixed_frac(qz);
@@ -536,9 +539,9 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
                         serial_step(qx, qy, qz);
                     }
 #pragma unroll
-                    for (int i = 0; i < kInflight; ++i) box_corners(bx + A[i].o, sy, sz, c[i]);
+                    for (int i = 0; i < kStagedGroup; ++i) box_corners(bx + A[i].o, sy, sz, c[i]);
 #pragma unroll
-                    for (int i = 0; i < kInflight; ++i) {
+                    for (int i = 0; i < kStagedGroup; ++i) {
                         const float val = interpolate(A[i], c[i]);
                         if constexpr (MODE == kAlpha) composite(val, fdz, T_c, tau_c, I_c);
                         else acc[i] += val;
@@ -587,7 +590,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
     if (!mine) return;
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kInflight; ++i) s += acc[i];
+    for (int i = 0; i < kStagedGroup; ++i) s += acc[i];
     float res, tau;
     if constexpr (MODE == kAlpha) {
         res = (float)I_c;
