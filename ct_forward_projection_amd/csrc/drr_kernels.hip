@@ -303,15 +303,13 @@ constexpr int march_tile_side() { return SPLIT == 1 ? kTile : (SPLIT == 4 ? 8 : 
 // thickness dz emitting v with opacity alpha = 1 - exp(-f v dz) behind the
 // transmittance T = exp(-tau) of the samples in front of it, carried as the
 // running product T <- T (1 - alpha) = T - T alpha (one fp64 fma, no
-// exponential per sample).  T, tau (the line integral, also returned) and I run
-// in fp64 so that none of them drifts over long rays.
-__device__ inline void composite(float v, float fdz, double& T, double& tau, double& I)
+// exponential per sample).  T and I run in fp64 so that neither drifts over
+// long rays; the line integral (also returned) is summed like the other modes'.
+__device__ inline void composite(float v, float fdz, double& T, double& I)
 {
-    const float a = fdz * v;
-    const float alpha = -expm1f(-a);
+    const float alpha = -expm1f(-(fdz * v));
     I = fma(T, (double)(alpha * v), I);
     T = fma(-T, (double)alpha, T);
-    tau += (double)a;
 }
 
 // Forward DRR.  SPLIT = 1: one ray per lane (16 x 16 tiles of four 8 x 8 wave
@@ -361,7 +359,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
         hit = ray_setup_range(G, V, px.r, px.c, N, t_near, t_far, R);
     }
     float s = 0.0f;
-    double T_c = 1.0, tau_c = 0.0, I_c = 0.0;   // compositing
+    double T_c = 1.0, I_c = 0.0;   // compositing
     if (hit) {
         const char* base = reinterpret_cast<const char*>(src) + (uint64_t)cvol * b.src_stride;
         const __amdgpu_buffer_rsrc_t rs =
@@ -409,8 +407,8 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) {
                 const float v = ZP ? interpolate_exact(A[i], c[i]) : interpolate(A[i], c[i]);
-                if constexpr (MODE == kAlpha) composite(v, fdz, T_c, tau_c, I_c);
-                else acc[i] += v;
+                if constexpr (MODE == kAlpha) composite(v, fdz, T_c, I_c);
+                acc[i] += v;
             }
         }
         for (; k < n_mine; ++k) {
@@ -419,8 +417,8 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
             CornerVals c;
             gather<T, L>(rs, A, c);
             const float v = ZP ? interpolate_exact(A, c) : interpolate(A, c);
-            if constexpr (MODE == kAlpha) composite(v, fdz, T_c, tau_c, I_c);
-            else acc[0] += v;
+            if constexpr (MODE == kAlpha) composite(v, fdz, T_c, I_c);
+            acc[0] += v;
         }
 #pragma unroll
         for (int i = 0; i < kGroup; ++i) s += acc[i];
@@ -431,15 +429,10 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
         for (int off = SPLIT / 2; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
         if (j != 0) return;
     }
-    float res, tau;
-    if constexpr (MODE == kAlpha) {
-        res = (float)I_c;
-        tau = (float)tau_c;
-    } else {
-        if (hit) s *= R.dz;
-        tau = b.f * s;                     // optical depth f dz sum mu
-        res = (MODE == kBeerLambert) ? -expm1f(-tau) : tau;
-    }
+    if (hit) s *= R.dz;
+    const float tau = b.f * s;                 // optical depth f dz sum mu
+    const float res = MODE == kAlpha ? (float)I_c
+                                     : (MODE == kBeerLambert ? -expm1f(-tau) : tau);
     const size_t o = ((size_t)px.view * H + px.r) * W + px.c;
     out[o] = res;
     if (s_out) s_out[o] = tau;
@@ -487,7 +480,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
     float acc[kStagedGroup];
 #pragma unroll
     for (int i = 0; i < kStagedGroup; ++i) acc[i] = 0.0f;
-    double T_c = 1.0, tau_c = 0.0, I_c = 0.0;
+    double T_c = 1.0, I_c = 0.0;
 
     int S = N;
     int k0 = 0;
@@ -543,8 +536,8 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
 #pragma unroll
                     for (int i = 0; i < kStagedGroup; ++i) {
                         const float val = interpolate(A[i], c[i]);
-                        if constexpr (MODE == kAlpha) composite(val, fdz, T_c, tau_c, I_c);
-                        else acc[i] += val;
+                        if constexpr (MODE == kAlpha) composite(val, fdz, T_c, I_c);
+                        acc[i] += val;
                     }
                 }
                 for (; k < k0 + S; ++k) {
@@ -557,8 +550,8 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
                     CornerVals c;
                     box_corners(bx + A.o, sy, sz, c);
                     const float val = interpolate(A, c);
-                    if constexpr (MODE == kAlpha) composite(val, fdz, T_c, tau_c, I_c);
-                    else acc[0] += val;
+                    if constexpr (MODE == kAlpha) composite(val, fdz, T_c, I_c);
+                    acc[0] += val;
                 }
             }
             __syncthreads();
@@ -580,8 +573,8 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
                     c.v[n] = staged_value<T, TF>(rs, V, ix + (n & 1), iy + ((n >> 1) & 1),
                                                  iz + (n >> 2), tf, ch);
                 const float val = interpolate(A, c);
-                if constexpr (MODE == kAlpha) composite(val, fdz, T_c, tau_c, I_c);
-                else acc[0] += val;
+                if constexpr (MODE == kAlpha) composite(val, fdz, T_c, I_c);
+                acc[0] += val;
             }
         }
         k0 += S;
@@ -591,15 +584,10 @@ __global__ __launch_bounds__(kBlock) void drr_march_staged_kernel(
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < kStagedGroup; ++i) s += acc[i];
-    float res, tau;
-    if constexpr (MODE == kAlpha) {
-        res = (float)I_c;
-        tau = (float)tau_c;
-    } else {
-        if (hit) s *= R.dz;
-        tau = b.f * s;
-        res = (MODE == kBeerLambert) ? -expm1f(-tau) : tau;
-    }
+    if (hit) s *= R.dz;
+    const float tau = b.f * s;                 // optical depth f dz sum mu
+    const float res = MODE == kAlpha ? (float)I_c
+                                     : (MODE == kBeerLambert ? -expm1f(-tau) : tau);
     const size_t o = ((size_t)px.view * H + px.r) * W + px.c;
     out[o] = res;
     if (s_out) s_out[o] = tau;
