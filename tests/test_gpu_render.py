@@ -303,6 +303,26 @@ def test_render_compositing_backward_bound_paths(dev, clip, shift, f):
     check(img, tau, grad, ref, ref_tau, ref_g, f"compositing bound clip{clip} {shift} {f}")
 
 
+def test_render_compositing_backward_nan_voxel(dev):
+    """A NaN voxel sets the non-finite flag of the compositing backward's value
+    bounds, so the pass over the samples runs, finds the NaN coefficients of the
+    rays through it (their forward image is NaN as well) and their tiles fall
+    back to float atomics: exactly the voxels the oracle marks NaN are NaN on the
+    GPU, and the rest match."""
+    vol, spacing, K, poses, H, Wd, N, g = problem(430, N=37)
+    vol[0, 1, 6, 5, 8] = np.nan
+    say("case: compositing backward with a NaN voxel")
+    img, tau, grad = run_gpu(dev, vol, spacing, K, poses, H, Wd, N, ALPHA, 1.1, BOX, 3.0, None, g)
+    kw = dict(density_factor=1.1, clip=BOX, margin=3.0, transfer=None)
+    ref_g = oracle.render_adjoint(vol, spacing, K, poses, H, Wd, N, ALPHA, g, **kw)
+    assert np.isnan(ref_g).any() and not np.isnan(ref_g).all()
+    assert np.array_equal(np.isnan(grad), np.isnan(ref_g))
+    ok = ~np.isnan(ref_g)
+    err = normwise_err(grad[ok], ref_g[ok])
+    say(f"NaN voxel: {int(np.isnan(ref_g).sum())} NaN voxels, the rest normwise {err:.3e}")
+    assert err <= GRAD
+
+
 @pytest.mark.parametrize("N", [6, 64])
 @pytest.mark.parametrize("mode", [BL, RAW, ALPHA])
 def test_render_near_far_axis_aligned_and_boundary_rays(dev, mode, N):
