@@ -15,8 +15,9 @@
 // planes 0 and n_a of the same expression, so the walk ends exactly at t1.  A
 // piece's length is rounded to fp32 once.
 //
-//   drr_siddon_march_kernel    forward: s = sum mu_v l_v, eight pieces' loads
-//                              in flight per lane, fp32 accumulation
+//   drr_siddon_march_kernel    forward: s = sum mu_v l_v, eight (or twelve)
+//                              pieces' loads in flight per lane, fp32
+//                              accumulation
 //   drr_siddon_scatter_kernel  backward: y l_v into the fp32 gradient, the
 //                              rays of a tile walked chunk by chunk into an LDS
 //                              window of fixed-point integer sums
@@ -140,7 +141,7 @@ __device__ inline bool advance(SiddonRay& S, const NextAxis& m, const VolumeDesc
 // pieces past the end of the walk stay memory-safe (a raw buffer load outside
 // the buffer's range returns 0), and pieces of zero length add an explicit 0,
 // so no voxel the ray does not cross (a NaN, say) leaks into the sum.
-template <typename T, int MODE>
+template <typename T, int MODE, int NG>
 __global__ __launch_bounds__(kBlock) void drr_siddon_march_kernel(
     const T* __restrict__ src, uint32_t src_bytes, VolumeDesc V, Intrinsics K,
     const float* __restrict__ poses, int H, int W, int tiles_x, int tiles_per_view,
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(kBlock) void drr_siddon_march_kernel(
         double tc = S.t0;
         int guard = V.n[0] + V.n[1] + V.n[2] + 3;
         bool live = true;
-        constexpr int kGroup = 8;
+        constexpr int kGroup = NG;  // pieces' loads in flight per lane
         while (live) {
             uint32_t o[kGroup];
             float l[kGroup];
@@ -343,34 +344,47 @@ __global__ __launch_bounds__(kBlock) void drr_siddon_scatter_kernel(
 
 // ----------------------------------------------------------------- launchers
 
+// Pieces in flight per lane: eight, or twelve for fp32 volumes under four
+// pieces per cell per view (16 views of 200^2 at 256^3: 0.430 -> 0.399 ms;
+// twelve slowed bf16 there, 0.360 -> 0.384 ms, and the denser 1024^2 and helix
+// launches by ~10%).
+template <typename T, int G>
+static void launch_siddon_march(const LaunchArgs& a, const T* v, uint32_t bytes, int tiles_x,
+                                int tiles_per_view, int n_tiles, float* out, float* s_out,
+                                hipStream_t stream)
+{
+    const dim3 grid(n_tiles), block(kBlock);
+    if (a.mode == kBeerLambert)
+        hipLaunchKernelGGL((drr_siddon_march_kernel<T, kBeerLambert, G>), grid, block, 0, stream,
+                           v, bytes, a.V, a.K, a.poses, a.H, a.W, tiles_x, tiles_per_view, out,
+                           s_out);
+    else
+        hipLaunchKernelGGL((drr_siddon_march_kernel<T, kLineIntegral, G>), grid, block, 0, stream,
+                           v, bytes, a.V, a.K, a.poses, a.H, a.W, tiles_x, tiles_per_view, out,
+                           s_out);
+}
+
 hipError_t launch_siddon_forward(const LaunchArgs& a, const void* vol, int dtype, float* out,
                                  float* s_out, hipStream_t stream)
 {
     const int tiles_x = (a.W + kTile - 1) / kTile, tiles_y = (a.H + kTile - 1) / kTile;
     const int tiles_per_view = tiles_x * tiles_y, n_tiles = tiles_per_view * a.n_views;
     if (n_tiles == 0) return hipSuccess;
-    const dim3 grid(n_tiles), block(kBlock);
     const uint32_t bytes = a.V.total_bytes;
+    // pieces one view puts per cell, with about nx + ny + nz pieces per ray
+    const double cells = (double)a.V.n[0] * a.V.n[1] * a.V.n[2];
+    const double reuse = (double)a.H * a.W * (a.V.n[0] + a.V.n[1] + a.V.n[2]) / cells;
     if (dtype == 0) {
         const float* v = static_cast<const float*>(vol);
-        if (a.mode == kBeerLambert)
-            hipLaunchKernelGGL((drr_siddon_march_kernel<float, kBeerLambert>), grid, block, 0,
-                               stream, v, bytes, a.V, a.K, a.poses, a.H, a.W, tiles_x,
-                               tiles_per_view, out, s_out);
+        if (reuse < 4.0)
+            launch_siddon_march<float, 12>(a, v, bytes, tiles_x, tiles_per_view, n_tiles, out,
+                                           s_out, stream);
         else
-            hipLaunchKernelGGL((drr_siddon_march_kernel<float, kLineIntegral>), grid, block, 0,
-                               stream, v, bytes, a.V, a.K, a.poses, a.H, a.W, tiles_x,
-                               tiles_per_view, out, s_out);
+            launch_siddon_march<float, 8>(a, v, bytes, tiles_x, tiles_per_view, n_tiles, out,
+                                          s_out, stream);
     } else {
-        const uint16_t* v = static_cast<const uint16_t*>(vol);
-        if (a.mode == kBeerLambert)
-            hipLaunchKernelGGL((drr_siddon_march_kernel<uint16_t, kBeerLambert>), grid, block, 0,
-                               stream, v, bytes, a.V, a.K, a.poses, a.H, a.W, tiles_x,
-                               tiles_per_view, out, s_out);
-        else
-            hipLaunchKernelGGL((drr_siddon_march_kernel<uint16_t, kLineIntegral>), grid, block,
-                               0, stream, v, bytes, a.V, a.K, a.poses, a.H, a.W, tiles_x,
-                               tiles_per_view, out, s_out);
+        launch_siddon_march<uint16_t, 8>(a, static_cast<const uint16_t*>(vol), bytes, tiles_x,
+                                         tiles_per_view, n_tiles, out, s_out, stream);
     }
     return hipGetLastError();
 }
