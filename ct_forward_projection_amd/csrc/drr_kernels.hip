@@ -942,18 +942,21 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
         float cmax = fabsf(yd);
         if constexpr (ALPHA) {
             // With values v >= 0 (so 0 <= alpha <= f v dz, T <= 1) and f >= 0,
-            // a coefficient g (T (alpha + f dz (1 - alpha) v) - f dz later) is a
-            // difference of two non-negative terms bounded by 2 f dz vmax and
-            // f dz I, so |c| <= |g| f dz max(2 vmax, I) (with a margin for
-            // rounding) without visiting the samples; otherwise (a negative or
-            // non-finite value, or no bounds) a first pass takes the largest
-            // coefficient of the ray (NaN if any is not finite).
+            // a coefficient g (T (alpha + f dz (1 - alpha) v) - f dz later) is
+            // a difference of T (alpha + ...) <= 2 f dz vmax and f dz later,
+            // where later = I - run and the running emission run lies in
+            // [0, vmax] (the opacities along a ray sum to at most 1), so
+            // |c| <= |g| f dz max(2 vmax, |I| + vmax) for any finite image I
+            // the caller passes (2 vmax for the forward's own, I <= vmax), with
+            // a margin for rounding, without visiting the samples; otherwise
+            // (a negative or non-finite value, or no bounds) a first pass takes
+            // the largest coefficient of the ray (NaN if any is not finite).
             const float fdz = coef.fdz;
             if (vbound != nullptr && vbound[2 * cvol] == 0 && fdz >= 0.0f) {
                 const float vmax = __int_as_float(vbound[2 * cvol + 1]);
                 const float I = (float)coef.I;
                 cmax = (isfinite(I) && isfinite(coef.g))
-                           ? fabsf(coef.g) * fdz * fmaxf(2.0f * vmax, fabsf(I)) * 1.0625f
+                           ? fabsf(coef.g) * fdz * fmaxf(2.0f * vmax, fabsf(I) + vmax) * 1.0625f
                            : __builtin_nanf("");
             } else {
                 coef.trans = 1.0;
