@@ -6,7 +6,8 @@ HIP stream -- and every step of the path runs in the library's HIP kernels.
 There is no CPU or PyTorch fallback: if the library is not built, or a tensor
 is not on a GPU, the call raises.
 
-Functions carry the C names (``drr_forward``, ``drr_backward_volume``,
+Functions carry the C names (``drr_forward``, ``drr_forward_no_alloc``,
+``drr_backward_volume``,
 ``drr_backward_pose``, ``drr_forward_siddon``, ``drr_backward_volume_siddon``,
 ``drr_render``, ``drr_render_backward_volume``, ``drr_workspace_bytes``,
 ``drr_render_workspace_bytes``, ``drr_intrinsics_from_fov``,
@@ -33,6 +34,7 @@ from .build import LIBRARY
 F32, BF16 = 0, 1
 BEER_LAMBERT, LINE_INTEGRAL, ALPHA_COMPOSITE = 0, 1, 2
 CLIP_BOX, CLIP_NEAR_FAR = 0, 1
+NO_ALLOC_SCRATCH_BYTES = 256 << 20       # DRR_NO_ALLOC_SCRATCH_BYTES of include/drr.h
 STATUS = {0: "DRR_OK", 1: "DRR_ERR_INVALID_ARGUMENT", 2: "DRR_ERR_UNSUPPORTED",
           3: "DRR_ERR_WORKSPACE_TOO_SMALL", 4: "DRR_ERR_HIP"}
 
@@ -58,6 +60,8 @@ def library() -> ctypes.CDLL:
         lib.drr_workspace_bytes.restype = Z
         lib.drr_forward.argtypes = [P, I, I, I, I, P, P, P, I, I, I, I, I, P, P, P, Z, P]
         lib.drr_forward.restype = I
+        lib.drr_forward_no_alloc.argtypes = [P, I, I, I, I, P, P, P, I, I, I, I, I, P, P, P]
+        lib.drr_forward_no_alloc.restype = I
         lib.drr_backward_volume.argtypes = [I, I, I, P, P, P, I, I, I, I, I, P, P, P, P, Z, P]
         lib.drr_backward_volume.restype = I
         lib.drr_backward_pose.argtypes = [P, I, I, I, I, P, P, P, I, I, I, I, I, P, P, P, Z, P]
@@ -184,6 +188,42 @@ def drr_forward(volume: torch.Tensor, spacing: Sequence[float], K, poses: torch.
         _ptr(volume), dtype, nz, ny, nx, _host_floats(spacing, 3), _host_floats(K, 9),
         _ptr(poses), V, det_h, det_w, n_samples, mode, _ptr(out), _ptr(line_integral),
         _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, line_integral
+
+
+def drr_forward_no_alloc(volume: torch.Tensor, spacing: Sequence[float], K,
+                         poses: torch.Tensor, det_h: int, det_w: int, n_samples: int,
+                         mode: int = BEER_LAMBERT, out: Optional[torch.Tensor] = None,
+                         line_integral=True, stream=None):
+    """``drr_forward`` without a workspace: the library's fixed device scratch
+    (``NO_ALLOC_SCRATCH_BYTES`` per GPU) holds the volume copy the read plan
+    marches.  Passing ``out`` (and ``line_integral``, or ``False``) makes the call
+    allocate nothing, e.g. under graph capture.  Calls that overlap on one GPU
+    share the scratch and race."""
+    volume = _device_tensor(volume, "volume")
+    dtype = _volume_dtype(volume)
+    poses = _device_tensor(poses, "poses", torch.float32)
+    if volume.dim() != 3 or poses.dim() != 3 or tuple(poses.shape[1:]) != (3, 4):
+        raise ValueError("volume must be (nz, ny, nx) and poses (V, 3, 4)")
+    nz, ny, nx = (int(s) for s in volume.shape)
+    V = int(poses.shape[0])
+    if out is None:
+        out = torch.empty((V, det_h, det_w), dtype=torch.float32, device=volume.device)
+    out = _device_tensor(out, "out", torch.float32)
+    if out.numel() != V * det_h * det_w:
+        raise ValueError("out has the wrong size")
+    if line_integral is True:
+        line_integral = torch.empty_like(out)
+    elif line_integral is False:
+        line_integral = None
+    if line_integral is not None:
+        line_integral = _device_tensor(line_integral, "line_integral", torch.float32)
+        if line_integral.numel() != out.numel():
+            raise ValueError("line_integral has the wrong size")
+    _check(library().drr_forward_no_alloc(
+        _ptr(volume), dtype, nz, ny, nx, _host_floats(spacing, 3), _host_floats(K, 9),
+        _ptr(poses), V, det_h, det_w, n_samples, mode, _ptr(out), _ptr(line_integral),
+        _stream(stream)))
     return out, line_integral
 
 

@@ -8,6 +8,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/drr.h"
 #include "drr_internal.hpp"
 
@@ -227,6 +229,103 @@ int frame_from_ras(const float* ras2ijk, int nz, int ny, int nx, drr::VolumeFram
     return DRR_OK;
 }
 
+// Fixed device scratch of drr_forward_no_alloc: the copy of the volume its read
+// plan marches (corner cells or z-pairs) goes here instead of into a caller
+// workspace, for callers that cannot allocate device memory.  Every GPU the
+// library runs on holds its own copy of the array until the process ends.
+// Host code never uses the array's name as a device address: its address on
+// each device comes from hipGetSymbolAddress (scratch_on_stream_device).
+constexpr size_t kScratchBytes = DRR_NO_ALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes % 256 == 0, "scratch must hold whole 256-byte blocks");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the device `stream` runs on (the current
+// device for the null stream), looked up once per device with that device
+// current.
+int scratch_on_stream_device(hipStream_t stream, void** ptr)
+{
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return fail(DRR_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    int dev = cur;
+    if (stream != nullptr) {
+        e = hipStreamGetDevice(stream, &dev);
+        if (e != hipSuccess)
+            return fail(DRR_ERR_HIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(DRR_ERR_UNSUPPORTED, "device %d is beyond the %d the scratch table holds", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(DRR_ERR_HIP, "hipSetDevice(%d) failed: %s", dev, hipGetErrorString(e));
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t back = dev != cur ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess)
+            return fail(DRR_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                        hipGetErrorString(e));
+        if (back != hipSuccess)
+            return fail(DRR_ERR_HIP, "hipSetDevice(%d) failed: %s", cur, hipGetErrorString(back));
+        if (p == nullptr || ((uintptr_t)p & 255u))
+            return fail(DRR_ERR_HIP, "scratch on device %d is not 256-byte aligned", dev);
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return DRR_OK;
+}
+
+// drr_forward with the workspace the caller passes, or (no_alloc) with the
+// fixed scratch of the stream's device.
+int forward_into(const void* volume, int dtype, int nz, int ny, int nx, const float* spacing,
+                 const float* K, const float* poses, int n_views, int det_h, int det_w,
+                 int n_samples, int mode, float* out, float* line_integral, void* workspace,
+                 size_t workspace_bytes, bool no_alloc, void* stream)
+{
+    if (dtype != DRR_F32 && dtype != DRR_BF16)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    drr::LaunchArgs a;
+    int st = check_geometry(nz, ny, nx, dtype == DRR_F32 ? 4 : 2, spacing, K, poses, n_views,
+                            det_h, det_w, n_samples, mode, a);
+    if (st != DRR_OK) return st;
+    if (!volume) return fail(DRR_ERR_INVALID_ARGUMENT, "volume is NULL");
+    const long long n_rays = (long long)n_views * det_h * det_w;
+    if (n_rays > 0 && !out) return fail(DRR_ERR_INVALID_ARGUMENT, "out is NULL");
+    const int eb = dtype == DRR_F32 ? 4 : 2;
+    const drr::RenderPlan plan = drr::plan_render(1, 1, nz, ny, nx, eb, n_views, det_h, det_w,
+                                                  n_samples, drr::kClipBox, false, true);
+    if (no_alloc) {
+        if (plan.workspace_bytes > kScratchBytes)
+            return fail(DRR_ERR_UNSUPPORTED,
+                        "this call needs %zu bytes of scratch; the fixed scratch holds %zu",
+                        plan.workspace_bytes, kScratchBytes);
+        if (n_rays == 0) return ok();
+        if (plan.workspace_bytes > 0) {
+            st = scratch_on_stream_device(static_cast<hipStream_t>(stream), &workspace);
+            if (st != DRR_OK) return st;
+        }
+    } else {
+        if (workspace_bytes < plan.workspace_bytes)
+            return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
+                        workspace_bytes, plan.workspace_bytes);
+        if (plan.workspace_bytes > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
+            return fail(DRR_ERR_INVALID_ARGUMENT,
+                        "workspace must be non-NULL and 256-byte aligned");
+        if (n_rays == 0) return ok();
+    }
+    set_read_geometry(a.V, plan);
+    hipError_t e = drr::launch_forward(a, plan, volume, dtype, workspace, out, line_integral,
+                                       static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+        return fail(DRR_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -359,30 +458,18 @@ int drr_forward(const void* volume, int dtype, int nz, int ny, int nx, const flo
                 int n_samples, int mode, float* out, float* line_integral, void* workspace,
                 size_t workspace_bytes, void* stream)
 {
-    if (dtype != DRR_F32 && dtype != DRR_BF16)
-        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
-    drr::LaunchArgs a;
-    int st = check_geometry(nz, ny, nx, dtype == DRR_F32 ? 4 : 2, spacing, K, poses, n_views,
-                            det_h, det_w, n_samples, mode, a);
-    if (st != DRR_OK) return st;
-    if (!volume) return fail(DRR_ERR_INVALID_ARGUMENT, "volume is NULL");
-    const long long n_rays = (long long)n_views * det_h * det_w;
-    if (n_rays > 0 && !out) return fail(DRR_ERR_INVALID_ARGUMENT, "out is NULL");
-    const int eb = dtype == DRR_F32 ? 4 : 2;
-    const drr::RenderPlan plan = drr::plan_render(1, 1, nz, ny, nx, eb, n_views, det_h, det_w,
-                                                  n_samples, drr::kClipBox, false, true);
-    if (workspace_bytes < plan.workspace_bytes)
-        return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
-                    workspace_bytes, plan.workspace_bytes);
-    if (plan.workspace_bytes > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
-        return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
-    if (n_rays == 0) return ok();
-    set_read_geometry(a.V, plan);
-    hipError_t e = drr::launch_forward(a, plan, volume, dtype, workspace, out, line_integral,
-                                       static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return fail(DRR_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
-    return ok();
+    return forward_into(volume, dtype, nz, ny, nx, spacing, K, poses, n_views, det_h, det_w,
+                        n_samples, mode, out, line_integral, workspace, workspace_bytes, false,
+                        stream);
+}
+
+int drr_forward_no_alloc(const void* volume, int dtype, int nz, int ny, int nx,
+                         const float* spacing, const float* K, const float* poses, int n_views,
+                         int det_h, int det_w, int n_samples, int mode, float* out,
+                         float* line_integral, void* stream)
+{
+    return forward_into(volume, dtype, nz, ny, nx, spacing, K, poses, n_views, det_h, det_w,
+                        n_samples, mode, out, line_integral, nullptr, 0, true, stream);
 }
 
 int drr_backward_volume(int nz, int ny, int nx, const float* spacing, const float* K,

@@ -33,7 +33,8 @@
  *
  * Ownership and errors:
  *   - every buffer is owned by the caller; the library never allocates,
- *     frees or synchronises device memory, and keeps no state between calls;
+ *     frees or synchronises device memory, and keeps no state between calls
+ *     (except drr_forward_no_alloc's fixed scratch array, see there);
  *   - calls are asynchronous: work is enqueued on `stream` (a hipStream_t;
  *     NULL = the default stream) and the call returns without waiting;
  *   - arguments are validated on the host before anything is enqueued; an
@@ -115,6 +116,30 @@ int drr_forward(const void *volume, int dtype, int nz, int ny, int nx, const flo
                 const float *K, const float *poses, int n_views, int det_h, int det_w,
                 int n_samples, int mode, float *out, float *line_integral, void *workspace,
                 size_t workspace_bytes, void *stream);
+
+/* drr_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, and the same launches and results.  What
+ * drr_forward keeps in its workspace (the corner-cell or z-pair copy of the
+ * volume its read plan marches) goes into a fixed device array of
+ * DRR_NO_ALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends; the call itself allocates nothing.
+ *   A call whose plan needs more than DRR_NO_ALLOC_SCRATCH_BYTES (i.e.
+ *   drr_workspace_bytes(..., DRR_WORKSPACE_FORWARD) above it) returns
+ *   DRR_ERR_UNSUPPORTED and enqueues nothing.
+ *   Every call on one GPU shares that GPU's array (each call rewrites all of
+ *   the copy it reads before reading it): calls that overlap on one GPU --
+ *   on two streams, or from two threads -- race, and must be serialised by
+ *   the caller.
+ *   The array's device address is looked up once per device, on the first
+ *   call that needs it, with that device current (a HIP runtime call, no
+ *   allocation). */
+#define DRR_NO_ALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+int drr_forward_no_alloc(const void *volume, int dtype, int nz, int ny, int nx,
+                         const float *spacing, const float *K, const float *poses, int n_views,
+                         int det_h, int det_w, int n_samples, int mode, float *out,
+                         float *line_integral, void *stream);
 
 /* Volume gradient of the forward (flashdrr autograd backward / diffct
  * backproject): for upstream dL/dI = grad_out,

@@ -326,3 +326,44 @@ def test_poisson_surrogate_validates_on_the_host():
     assert lib.drr_poisson_surrogate(DUMMY, None, 4, 10.0, DUMMY, None) == 1
     assert lib.drr_poisson_surrogate_backward(DUMMY, DUMMY, 4, 10.0, None, DUMMY, None) == 1
     assert lib.drr_poisson_surrogate_backward(None, None, 0, 10.0, None, None, None) == 0
+
+
+def fwd_no_alloc(**kw):
+    args = dict(volume=DUMMY, dtype=0, nz=8, ny=8, nx=8, spacing=SP, K=K, poses=DUMMY,
+                n_views=1, det_h=4, det_w=4, n_samples=8, mode=0, out=DUMMY, s=None,
+                stream=None)
+    args.update(kw)
+    return drr.library().drr_forward_no_alloc(
+        args["volume"], args["dtype"], args["nz"], args["ny"], args["nx"], args["spacing"],
+        args["K"], args["poses"], args["n_views"], args["det_h"], args["det_w"],
+        args["n_samples"], args["mode"], args["out"], args["s"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nz=0), 1), (dict(n_samples=0), 1), (dict(mode=2), 1), (dict(dtype=3), 1),
+    (dict(volume=None), 1), (dict(poses=None), 1), (dict(out=None), 1),
+    (dict(spacing=_f(1.0, 0.0, 1.0)), 1), (dict(nz=2048, ny=2048, nx=1024), 2),
+])
+def test_no_alloc_forward_rejects_invalid_arguments(kw, status):
+    assert fwd_no_alloc(**kw) == status
+    assert drr.library().drr_last_error() != b""
+
+
+def test_no_alloc_forward_rejects_plans_beyond_its_scratch_on_the_host():
+    """A read plan whose copy exceeds the fixed scratch is refused before any
+    HIP call (64 views of 256^2 x 256 samples put 8 samples per cell of a 512^3
+    fp32 volume: the z-pair copy, about 1 GiB)."""
+    need = drr.drr_workspace_bytes(512, 512, 512, 0, 64, 256, 256, 256, 0)
+    assert need > drr.NO_ALLOC_SCRATCH_BYTES
+    assert fwd_no_alloc(nz=512, ny=512, nx=512, n_views=64, det_h=256, det_w=256,
+                        n_samples=256) == 2
+    assert b"scratch" in drr.library().drr_last_error()
+    # an empty call within the limit is a valid no-op without a device
+    assert fwd_no_alloc(n_views=0, poses=None, out=None) == 0
+
+
+def test_no_alloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define DRR_NO_ALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m is not None
+    assert int(m.group(1)) << int(m.group(2)) == drr.NO_ALLOC_SCRATCH_BYTES
