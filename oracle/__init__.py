@@ -102,7 +102,17 @@ def _f64(a) -> np.ndarray:
 
 
 def _threads(n: Optional[int]) -> int:
-    return int(n) if n else (os.cpu_count() or 1)
+    """Threads for a call: ``n``, else OMP_NUM_THREADS when set, else the CPUs
+    this process may run on."""
+    if n:
+        return int(n)
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return len(os.sched_getaffinity(0)) or 1
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
 
 
 def max_threads() -> int:
