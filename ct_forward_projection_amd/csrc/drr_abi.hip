@@ -444,7 +444,10 @@ size_t drr_workspace_bytes(int nz, int ny, int nx, int dtype, int n_views, int d
     if (nz < 1 || ny < 1 || nx < 1 || n_views < 0 || det_h < 0 || det_w < 0 ||
         n_samples < 1 || (dtype != DRR_F32 && dtype != DRR_BF16))
         return 0;
-    if (for_backward == DRR_WORKSPACE_VOLUME_BACKWARD) return 0;
+    if (for_backward == DRR_WORKSPACE_VOLUME_BACKWARD)
+        return drr::plan_backward(1, 1, nz, ny, nx, dtype == DRR_F32 ? 4 : 2, n_views, det_h,
+                                  det_w, n_samples, DRR_BEER_LAMBERT, drr::kClipBox, false)
+            .workspace_bytes;
     const bool fwd = for_backward == DRR_WORKSPACE_FORWARD;
     const size_t plan = drr::plan_render(1, 1, nz, ny, nx, dtype == DRR_F32 ? 4 : 2, n_views,
                                          det_h, det_w, n_samples, drr::kClipBox, false, true)
@@ -496,7 +499,7 @@ int drr_backward_volume(int nz, int ny, int nx, const float* spacing, const floa
     if (need > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
         return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
     hipError_t e = drr::launch_backward(a, nullptr, DRR_F32, grad_out, nullptr, line_integral,
-                                        grad_volume, nullptr, static_cast<hipStream_t>(stream));
+                                        grad_volume, workspace, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(DRR_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -655,26 +655,6 @@ __device__ inline void scatter_sample_global(float* __restrict__ grad, uint32_t 
     unsafeAtomicAdd(grad + r11 + x1, w[7]);
 }
 
-// Trilinear weights of one sample scaled by c: w[n] for corner n (bit 0 = x1,
-// bit 1 = y1, bit 2 = z1), the same products as corner_weights without clamps.
-// Add c times the eight trilinear weights of fractions (fx, fy, fz) to acc,
-// corner order x fastest: acc[i] += c w_x(i & 1) w_y((i >> 1) & 1) w_z(i >> 2).
-__device__ inline void add_weights8(float fx, float fy, float fz, float c, float acc[8])
-{
-    const float wz1 = c * fz, wz0 = c - wz1;
-    const float w11 = wz1 * fy, w10 = wz1 - w11;
-    const float w01 = wz0 * fy, w00 = wz0 - w01;
-    const float fx0 = 1.0f - fx;
-    acc[0] = fmaf(w00, fx0, acc[0]);
-    acc[1] = fmaf(w00, fx, acc[1]);
-    acc[2] = fmaf(w01, fx0, acc[2]);
-    acc[3] = fmaf(w01, fx, acc[3]);
-    acc[4] = fmaf(w10, fx0, acc[4]);
-    acc[5] = fmaf(w10, fx, acc[5]);
-    acc[6] = fmaf(w11, fx0, acc[6]);
-    acc[7] = fmaf(w11, fx, acc[7]);
-}
-
 // Fixed-point value of a register sum for the window, rounded to nearest.
 // TRUNC: the sum already carries +-1/2 with the sign of all its terms, so
 // truncation toward zero rounds it (half away from zero) in one conversion.
@@ -1624,7 +1604,20 @@ static hipError_t backward_typed(const LaunchArgs& a, const Tin* vol, const floa
                                  void* workspace, hipStream_t stream)
 {
     const size_t n_vox = (size_t)a.V.n[0] * a.V.n[1] * a.V.n[2];
-    hipError_t e = launch_fill(grad, n_vox * (size_t)a.n_volumes * a.C, stream);
+    hipError_t e;
+    const BackwardRead plan = plan_backward(a.n_volumes, a.C, a.V.n[2], a.V.n[1], a.V.n[0],
+                                            (int)sizeof(Tin), a.n_views, a.H, a.W, a.N, a.mode,
+                                            a.clip, a.has_tf);
+    if (plan.brick) {
+        // the brick-owned backward writes every voxel itself
+        e = launch_brick_backward(a, grad_out, s_in, grad, workspace, stream);
+        if (e != hipSuccess || !a.has_tf) return e;
+        const dim3 sgrid(grid_blocks((long long)n_vox, 4096), a.n_volumes * a.C);
+        hipLaunchKernelGGL((drr_slope_kernel<Tin>), sgrid, dim3(256), 0, stream, vol, n_vox,
+                           n_vox, grad, a.C, a.tf);
+        return hipGetLastError();
+    }
+    e = launch_fill(grad, n_vox * (size_t)a.n_volumes * a.C, stream);
     if (e != hipSuccess) return e;
     int tiles_x, tiles_per_view, n_tiles;
     tile_grid(a.n_views * a.C, a.H, a.W, kTile, tiles_x, tiles_per_view, n_tiles);

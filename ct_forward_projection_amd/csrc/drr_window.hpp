@@ -40,6 +40,26 @@ inline int window_cap(double view_reuse)
     return view_reuse >= 16.0 ? kWinCapDense : (view_reuse >= 4.0 ? kWinCapMid : kWinCapSparse);
 }
 
+// Trilinear weights of one sample scaled by c: w[n] for corner n (bit 0 = x1,
+// bit 1 = y1, bit 2 = z1), the same products as corner_weights without clamps.
+// Add c times the eight trilinear weights of fractions (fx, fy, fz) to acc,
+// corner order x fastest: acc[i] += c w_x(i & 1) w_y((i >> 1) & 1) w_z(i >> 2).
+__device__ inline void add_weights8(float fx, float fy, float fz, float c, float acc[8])
+{
+    const float wz1 = c * fz, wz0 = c - wz1;
+    const float w11 = wz1 * fy, w10 = wz1 - w11;
+    const float w01 = wz0 * fy, w00 = wz0 - w01;
+    const float fx0 = 1.0f - fx;
+    acc[0] = fmaf(w00, fx0, acc[0]);
+    acc[1] = fmaf(w00, fx, acc[1]);
+    acc[2] = fmaf(w01, fx0, acc[2]);
+    acc[3] = fmaf(w01, fx, acc[3]);
+    acc[4] = fmaf(w10, fx0, acc[4]);
+    acc[5] = fmaf(w10, fx, acc[5]);
+    acc[6] = fmaf(w11, fx0, acc[6]);
+    acc[7] = fmaf(w11, fx, acc[7]);
+}
+
 // Position (x, y, z) of entry i = threadIdx.x + n kBlock of a box of
 // ext[0] x ext[1] x ... entries (x fastest), advanced kBlock entries per
 // step with carries instead of divisions.
