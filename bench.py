@@ -10,10 +10,13 @@ Printed (one JSON line on stdout):
   value        rays x samples per second of the step (nominal: every pixel's
                ray counts N samples), in Gsamples/s
   fps          views per second of the step
-  roofline     the dominant kernel against the 8 TB/s HBM peak, on
-               algorithmic bytes (8 corners x element bytes per sample on rays
-               that hit the volume, plus per-ray reads/writes), with its
-               duration measured by HIP events on the launch stream
+  roofline     the dominant kernel's VALU roofline: the method's algorithmic
+               VALU lane-operations per sample on rays that hit the volume
+               (26 forward, 28 backward) over the pass's duration from HIP
+               events on the launch stream, against MI355X's VALU issue peak
+               without packed FP32 (1024 SIMDs x 16 lanes x 2.4 GHz); with the
+               committed counters of the current kernel sources it also carries
+               the kernel's HBM traffic, L2 hit rate, measured clock and VALU busy
   cpu_baseline the CPU oracle on the same step, timed on the host cores
   front_end    flashdrr front-end variants (transfer function from HU, near/far
                clipping, alpha compositing, volume and channel batches),
@@ -26,9 +29,11 @@ Printed (one JSON line on stdout):
                back-to-back launches (GPU time, no host launch latency)
 
 Options: --gpus N (only 1 is supported: this build runs on one GPU),
---steps K, --warmup W, --no-cpu, --no-workloads, and --pmc-pass
-{forward,backward,copy} which runs a short fixed launch sequence for
-rocprofv3 counter collection.
+--steps K, --warmup W, --no-cpu, --no-workloads; --profile-run CASE [--reps R]
+runs one workload's passes as a short fixed launch sequence for rocprofv3
+(kernel trace or counters), --profile-run CASE --meta-dir DIR records the
+case's unit counts, and --profile-summary DIR turns rocprofv3's outputs into
+profiles/*.md and profiles/pmc_traffic.json on the CPU.
 """
 from __future__ import annotations
 
@@ -228,18 +233,54 @@ def forward_bytes(res, hits):
 
 def backward_bytes(res, hits):
     w = res.w
-    return hits * w.n_samples * 8 * 4 + w.n_rays * 8
+    return hits * w.n_samples * 8 * 4 + w.n_rays * 8 + int(np.prod(w.volume.shape)) * 4
 
 
-def roofline(name, alg_bytes, ms, traffic=None, valu_busy=None):
-    """HBM roofline on algorithmic bytes.  Staged and cached kernels move far
-    fewer bytes than the algorithm names (frac above 1): ``traffic`` gives the
-    calibrated HBM bytes and ``valu_busy`` the share of VALU issue cycles, both
-    from the committed counters of the current kernel sources (else None)."""
-    achieved = alg_bytes / (ms * 1e-3) / 1e9
-    return {"kernel": name, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "valu_busy": valu_busy}
+# VALU issue peak of MI355X without packed FP32 (the build switches packed-FP32
+# instruction selection off): 256 CUs x 4 SIMDs, each issuing one wave64 VALU
+# instruction over 4 cycles (16 lanes per cycle), at the 2.4 GHz peak engine
+# clock -> 16384 lane-operations per cycle, 39.3 T lane-operations per second.
+# (The published fp32 vector peak, 157.3 TFLOP/s, counts a packed FMA as four
+# flops per lane and cycle.)
+MI355X_CUS, MI355X_SIMDS, MI355X_GHZ, MI355X_XCDS = 256, 1024, 2.4, 8
+ALU_PEAK_TOPS = MI355X_SIMDS * 16 * MI355X_GHZ * 1e9 / 1e12
+# Algorithmic VALU lane-operations of one sample, the method's own work (an FMA
+# counts once, a load or an atomic's memory-side add not at all):
+#   forward trilinear sample: position step 3, floor 3, fractions 3, corner
+#   address 2 (i + nx (j + ny k)), 7 lerps x 2 (subtract, fma), accumulate 1 = 26
+#   backward sample: position 3, floor 3, fractions 3, corner address 2,
+#   1 - f per axis 3, c (1 - fz) and c fz 2, four yz products 4, eight
+#   x products fused with their accumulation 8 = 28
+#   pose-gradient sample: the forward's 26, the trilinear gradient (three
+#   bilinear differences: 3 lerps x 2 + 1 subtract each = 21), two running
+#   vector sums (3 adds, 3 fmas) = 53
+OPS_FORWARD_SAMPLE = 26
+OPS_BACKWARD_SAMPLE = 28
+OPS_POSE_SAMPLE = 53
+
+
+def roofline_alu(name, ops, ms, counters=None):
+    """VALU roofline of one kernel: algorithmic lane-operations (``ops`` per
+    launch) over its launch duration against ALU_PEAK_TOPS.  ``counters``
+    (measured at the current kernel sources, else None) add HBM traffic, L2 hit
+    rate, measured VALU busy and issued/algorithmic operations."""
+    achieved = ops / (ms * 1e-3) / 1e12
+    r = {"kernel": name, "bound": "alu", "achieved": round(achieved, 3),
+         "peak": round(ALU_PEAK_TOPS, 3), "unit": "TOP/s",
+         "frac": round(achieved / ALU_PEAK_TOPS, 4),
+         "ops_per_launch": int(ops), "traffic": None}
+    if counters:
+        r["traffic"] = counters.get("hbm_bytes_per_launch")
+        for k in ("hbm_gbs", "hbm_frac", "l2_hit", "valu_busy", "clock_ghz",
+                  "issued_per_algorithmic", "lds_bank_conflict"):
+            if counters.get(k) is not None:
+                r[k] = counters[k]
+    return r
+
+
+def backward_kernel() -> str:
+    """The kernel that carries the train step's volume backward."""
+    return "drr_scatter_kernel"
 
 
 def _committed_counters():
@@ -254,27 +295,24 @@ def _committed_counters():
     return d if d.get("kernel_revision") == kernel_revision() else None
 
 
-def measured_valu_busy(kernel):
-    """VALU busy of one kernel from the committed counters (None if stale)."""
-    d = _committed_counters()
-    k = None if d is None else d.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("valu_busy")
-
-
-def measured_traffic(kernels):
-    """HBM bytes per launch of a pass (the sum over its kernels) from the
-    committed rocprofv3 counter summary, if it was taken on the current kernel
-    sources and covers every kernel; otherwise None."""
+def measured_counters(case, kernel):
+    """Counter-derived figures of one kernel in one profile case from the
+    committed summary (None if absent or taken on other kernel sources)."""
     d = _committed_counters()
     if d is None:
         return None
-    total = 0.0
-    for name in kernels:
-        k = d.get("kernels", {}).get(name)
-        if k is None or k.get("hbm_bytes_per_launch") is None:
-            return None
-        total += k["hbm_bytes_per_launch"]
-    return round(total)
+    return d.get("cases", {}).get(case, {}).get(kernel)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(w):
@@ -287,6 +325,7 @@ def cpu_baseline(w):
     dt = time.perf_counter() - t0
     return {"value": round(w.nominal_samples / dt / 1e9, 4), "unit": "Gsamples/s",
             "cores": int(min(threads, used) if used else threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "seconds": round(dt, 2),
             "sample": f"the whole step: {w.name} forward + volume gradient, fp64, "
                       f"{threads} threads forward / {used} threads scatter"}
@@ -312,19 +351,21 @@ def workload_lines(dev, reps):
                 "forward_fps": round(w.n_views / fwd_ms * 1e3, 1),
                 "forward_gsamples_s": round(w.nominal_samples / fwd_ms / 1e6, 1),
                 "forward_effective_gsamples_s": round(hits * w.n_samples / fwd_ms / 1e6, 1),
-                "forward_hbm_frac": round(forward_bytes(res, hits) / (fwd_ms * 1e-3) / 1e9
-                                          / HBM_PEAK_GBS, 4),
+                "forward_alu_frac": round(hits * w.n_samples * OPS_FORWARD_SAMPLE /
+                                          (fwd_ms * 1e-3) / 1e12 / ALU_PEAK_TOPS, 4),
                 "hit_rays": hits}
         if with_pose:
             pose_ms = t.pop()
             line["pose_backward_ms"] = round(pose_ms, 4)
             line["pose_backward_gsamples_s"] = round(w.nominal_samples / pose_ms / 1e6, 1)
+            line["pose_backward_alu_frac"] = round(hits * w.n_samples * OPS_POSE_SAMPLE /
+                                                   (pose_ms * 1e-3) / 1e12 / ALU_PEAK_TOPS, 4)
             line["registration_step_fps"] = round(w.n_views / (fwd_ms + pose_ms) * 1e3, 1)
         if len(t) > 1:
             line["backward_ms"] = round(t[1], 4)
             line["backward_gsamples_s"] = round(w.nominal_samples / t[1] / 1e6, 1)
-            line["backward_hbm_frac"] = round(backward_bytes(res, hits) / (t[1] * 1e-3) / 1e9
-                                              / HBM_PEAK_GBS, 4)
+            line["backward_alu_frac"] = round(hits * w.n_samples * OPS_BACKWARD_SAMPLE /
+                                              (t[1] * 1e-3) / 1e12 / ALU_PEAK_TOPS, 4)
         if i in (2, 3, 5):
             # cell-constant (Siddon) pair on the same inputs: algorithmic bytes are
             # one element read (forward) or one fp32 update (backward) per
@@ -417,8 +458,8 @@ def frontend_lines(dev):
     Beer-Lambert; near/far with a 30 mm margin and alpha compositing; fp32 and
     bf16 HU), four volumes of two channels, and the 1024^2 camera composited.
     Nominal samples count every ray's N samples (the near/far range marches
-    its N samples whether or not they fall inside the volume); the HBM
-    fraction prices 8 corner elements per nominal sample of the forward."""
+    its N samples whether or not they fall inside the volume); the ALU
+    fraction prices the forward's algorithmic operations per nominal sample."""
     import torch
 
     import ct_forward_projection_amd as drr
@@ -453,7 +494,6 @@ def frontend_lines(dev):
         torch.cuda.synchronize()
         f_ms, b_ms = time_graph([c.forward, c.backward])
         views = P.shape[0] * vol.shape[1]
-        fwd_bytes = c.samples * 8 * c.read_elem + c.out.numel() * 8
         line = {"views_x_channels": views, "detector": [w.det_h, w.det_w],
                 "n_samples": w.n_samples, "volumes": vol.shape[0], "channels": vol.shape[1],
                 "dtype": "bf16" if vol.dtype == torch.bfloat16 else "f32",
@@ -462,7 +502,8 @@ def frontend_lines(dev):
                 "transfer": transfer is not None, "read": c.plan,
                 "forward_ms": round(f_ms, 4), "forward_fps": round(views / f_ms * 1e3, 1),
                 "forward_gsamples_s": round(c.samples / f_ms / 1e6, 1),
-                "forward_hbm_frac": round(fwd_bytes / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "forward_alu_frac_nominal": round(c.samples * OPS_FORWARD_SAMPLE / (f_ms * 1e-3)
+                                                  / 1e12 / ALU_PEAK_TOPS, 4),
                 "backward_ms": round(b_ms, 4),
                 "backward_gsamples_s": round(c.samples / b_ms / 1e6, 1)}
         lines[name] = line
@@ -471,40 +512,26 @@ def frontend_lines(dev):
     return lines
 
 
-def pmc_pass(kind: str, dev):
-    """A short fixed launch sequence for rocprofv3 counter runs: 3 launches of
-    the chosen pass (forward, volume backward or pose backward) on the
-    train-step workload, or a plain 1 GiB copy (the calibration kernel for the
-    byte counters)."""
-    import torch
+# ---------------------------------------------------------------- profile runs
 
-    import workloads as W
-    if kind == "copy":
-        a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        log("pmc copy: 3 x 1 GiB")
-        return
-    res = Resident(W.make_workload(3), dev)
-    res.forward()
-    torch.cuda.synchronize()
-    run = {"forward": res.forward, "backward": res.backward, "pose": res.pose_backward}[kind]
-    for _ in range(3):
-        run()
-    torch.cuda.synchronize()
-    log(f"pmc pass: 3 x {kind}")
-
-
-# ---------------------------------------------------------------- profile summaries
-
+# Profile cases: every workload's passes, each run as a fixed short launch
+# sequence (``--profile-run CASE``) under rocprofv3 -- one kernel-trace run and
+# one run per counter set -- then summarised on the CPU (``--profile-summary``).
+#   name: (workload, bf16 volume, passes)
+PROFILE_CASES = {
+    "tiny64": (1, False, ("forward",)),
+    "batch200_f32": (2, False, ("forward", "backward", "pose")),
+    "batch200_bf16": (2, True, ("forward",)),
+    "train1024": (3, False, ("forward", "backward", "pose")),
+    "hires2048": (4, False, ("forward",)),
+    "helix360": (5, False, ("forward", "backward")),
+    "siddon1024": (3, False, ("siddon_forward", "siddon_backward")),
+}
 PROFILE_COMMANDS = {
-    "trace": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/trace -o trace "
-             "--output-format csv -- python3 bench.py --steps 20 --warmup 5 --no-cpu "
-             "--no-workloads",
-    "pmc": "rocprofv3 --pmc {counters} -d gpurun_out/prof/{kind}_{tag} -o pmc "
-           "--output-format csv -- python3 bench.py --pmc-pass {kind}",
+    "trace": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/{case}/trace -o trace "
+             "--output-format csv -- python3 bench.py --profile-run {case} --reps 10",
+    "pmc": "rocprofv3 --pmc {counters} -d gpurun_out/prof/{case}/{tag} -o pmc "
+           "--output-format csv -- python3 bench.py --profile-run {case} --reps 3",
 }
 PMC_SETS = {
     "fetch": ["FETCH_SIZE"],
@@ -514,12 +541,86 @@ PMC_SETS = {
     "ta": ["TA_TA_BUSY_sum", "TA_BUSY_avr", "TD_TD_BUSY_sum", "SQ_LDS_BANK_CONFLICT",
            "SQ_LDS_ADDR_CONFLICT"],
 }
-# kernels whose counters each pass reports (matched as substrings of the name)
-KERNEL_KEYS = {"forward": ["drr_march_staged_kernel"],
-               "backward": ["drr_fill_kernel", "drr_scatter_kernel"],
-               "pose": ["drr_pose_staged_kernel"],
-               "copy": ["copy"]}
-PMC_KINDS = ("forward", "backward", "pose", "copy")
+COPY_CASE = "copy1gib"          # the calibration run of the byte counters
+
+
+def _case_resident(case, dev):
+    import workloads as W
+    wi, bf16, passes = PROFILE_CASES[case]
+    w = W.make_workload(wi, with_bf16=bf16)
+    if w.grad_out is None and any(p in ("backward", "siddon_backward") for p in passes):
+        # upstream gradient of the batch's volume backward: U[-1, 1), seeded as
+        # the front-end lines' (2100 + views)
+        w.grad_out = np.random.default_rng(2100 + w.n_views).uniform(
+            -1.0, 1.0, size=(w.n_views, w.det_h, w.det_w)).astype(np.float32)
+    return Resident(w, dev, bf16=bf16), passes
+
+
+def profile_run(case: str, reps: int, dev, meta_dir=None):
+    """The fixed launch sequence of a profile case: every pass once (warm-up),
+    then ``reps`` launches of each pass in turn.  With ``meta_dir`` it also
+    writes the case's unit counts (hit rays, samples, voxels, ray-voxel pieces)
+    as meta.json for the summary (no profiler attached)."""
+    import torch
+    if case == COPY_CASE:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(reps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"profile run: {reps} x 1 GiB copy")
+        return
+    res, passes = _case_resident(case, dev)
+    fns = {"forward": res.forward, "backward": res.backward, "pose": res.pose_backward,
+           "siddon_forward": res.siddon_forward, "siddon_backward": res.siddon_backward}
+    res.forward()
+    if "siddon_backward" in passes:
+        res.siddon_forward()
+    for p in passes:
+        fns[p]()
+    torch.cuda.synchronize()
+    if meta_dir is not None:
+        w = res.w
+        meta = {"case": case, "workload": w.name, "views": w.n_views, "det": [w.det_h, w.det_w],
+                "n_samples": w.n_samples, "volume": list(w.volume.shape),
+                "dtype": "bf16" if res.elem_bytes == 2 else "f32", "passes": list(passes),
+                "hit_rays": res.hit_rays(), "rays": w.n_rays,
+                "voxels": int(np.prod(w.volume.shape)), "kernel_revision": kernel_revision()}
+        if any(p.startswith("siddon") for p in passes):
+            meta["siddon_pieces"] = siddon_pieces(w)
+        os.makedirs(meta_dir, exist_ok=True)
+        with open(os.path.join(meta_dir, "meta.json"), "w") as f:
+            json.dump(meta, f, indent=1)
+        log(f"profile meta: {meta}")
+        return
+    for p in passes:
+        for _ in range(reps):
+            fns[p]()
+        torch.cuda.synchronize()
+    log(f"profile run: {case}: {reps} x {', '.join(passes)}")
+
+
+# what one launch of each kernel computes, for its roofline in the summaries:
+# (unit, ops per unit or None, algorithmic bytes per unit)
+def _kernel_units(short, meta):
+    eff = meta["hit_rays"] * meta["n_samples"]
+    elem = 2 if meta["dtype"] == "bf16" else 4
+    nz, ny, nx = meta["volume"]
+    if short in ("drr_march_staged_kernel", "drr_march_kernel"):
+        return "sample on a hit ray", eff, OPS_FORWARD_SAMPLE, 8 * elem
+    if short in ("drr_scatter_kernel", "drr_brick_scatter_kernel"):
+        return "sample on a hit ray", eff, OPS_BACKWARD_SAMPLE, 32
+    if short in ("drr_pose_staged_kernel", "drr_pose_grad_kernel"):
+        return "sample on a hit ray", eff, OPS_POSE_SAMPLE, 8 * elem
+    if short == "drr_zpair_kernel":
+        return "voxel pair", nx * ny * (nz - 1), None, 4 * elem
+    if short == "drr_cells_kernel":
+        return "cell", (nx + 1) * (ny + 1) * (nz + 1), None, 16 * elem
+    if short == "drr_fill_kernel":
+        return "voxel", meta["voxels"], None, 4
+    if short in ("drr_siddon_march_kernel", "drr_siddon_scatter_kernel"):
+        return "ray-voxel piece", meta.get("siddon_pieces", 0), None, elem
+    return None
 
 
 def _csv_rows(path):
@@ -535,121 +636,145 @@ def _find(root, suffix):
     return sorted(hits)
 
 
+def _short_name(name: str) -> str:
+    """drr kernel name without namespace and template arguments."""
+    import re
+    m = re.search(r"drr::(drr_\w+?)(<|\()", name)
+    return m.group(1) if m else name.split("(")[0][:60]
+
+
+def _median_counters(root):
+    """kernel short name -> counter -> median over its dispatches."""
+    values = {}
+    for tag in PMC_SETS:
+        for path in _find(os.path.join(root, tag), "counter_collection.csv"):
+            per = {}
+            for r in _csv_rows(path):
+                key = (_short_name(r.get("Kernel_Name", "")), r["Counter_Name"], r["Dispatch_Id"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+            for (kname, cname, _), v in per.items():
+                values.setdefault(kname, {}).setdefault(cname, []).append(v)
+    return {k: {c: float(np.median(v)) for c, v in d.items()} for k, d in values.items()}
+
+
 def profile_summary(root: str):
-    """Summarise rocprofv3 outputs under ``root`` (the layout PROFILE_COMMANDS
-    writes) into profiles/*.md and profiles/pmc_traffic.json."""
+    """Summarise the rocprofv3 outputs under ``root`` (PROFILE_COMMANDS' layout:
+    root/<case>/trace, root/<case>/<counter set>, root/<case>/meta.json) into
+    profiles/<dominant kernel>__<case>.md and profiles/pmc_traffic.json."""
     prof_dir = os.path.join(ROOT, "profiles")
     os.makedirs(prof_dir, exist_ok=True)
     rev = kernel_revision()
-    # kernel trace statistics
-    stats = _find(os.path.join(root, "trace"), "kernel_stats.csv")
-    durations = {}     # kernel key -> average duration (ns) in the trace
-    if stats:
-        rows = _csv_rows(stats[0])
-        for key in {k for keys in KERNEL_KEYS.values() for k in keys}:
-            hits = [r for r in rows if key in r.get("Name", "")]
-            if hits:
-                best = max(hits, key=lambda r: int(r.get("Calls", 0)))
-                durations[key] = float(best.get("AverageNs", 0))
-        lines = ["# Kernel trace: train step on the 1024x1024 workload", "",
-                 f"Command: `{PROFILE_COMMANDS['trace']}`", "",
-                 f"Kernel sources revision: `{rev}`", "",
-                 "| kernel | calls | average (us) | min (us) | max (us) | share |",
-                 "|---|---|---|---|---|---|"]
-        for r in rows:
-            name = r.get("Name", r.get("KernelName", "?"))
-            if len(name) > 90:
-                name = name[:87] + "..."
-            lines.append(f"| `{name}` | {r.get('Calls')} | {float(r.get('AverageNs', 0)) / 1e3:.2f} "
-                         f"| {float(r.get('MinNs', 0)) / 1e3:.2f} | {float(r.get('MaxNs', 0)) / 1e3:.2f} "
-                         f"| {float(r.get('Percentage', 0)):.1f}% |")
-        path = os.path.join(prof_dir, "kernel_trace_train_step_1024.md")
-        with open(path, "w") as f:
-            f.write("\n".join(lines) + "\n")
-        log("wrote", path)
-    # counters
-    values = {}   # (pass, kernel) -> counter -> per-dispatch values
-    for kind in PMC_KINDS:
-        for tag in PMC_SETS:
-            for path in _find(os.path.join(root, f"{kind}_{tag}"), "counter_collection.csv"):
-                per = {}
-                for r in _csv_rows(path):
-                    name = r.get("Kernel_Name", "")
-                    key = next((k for k in KERNEL_KEYS[kind] if k in name), None)
-                    if key is None:
-                        continue
-                    per_key = (key, r["Counter_Name"], r["Dispatch_Id"])
-                    per[per_key] = per.get(per_key, 0.0) + float(r["Counter_Value"])
-                for (key, cname, _), v in per.items():
-                    values.setdefault((kind, key), {}).setdefault(cname, []).append(v)
-    if not values:
-        return
-    med = {k: {c: float(np.median(v)) for c, v in d.items()} for k, d in values.items()}
+    copy = _median_counters(os.path.join(root, COPY_CASE))
+    cm = next(iter(copy.values()), {})
     copy_bytes = float(1 << 30)
-    fetch_factor = write_factor = None
-    cm = med.get(("copy", "copy"), {})
-    if cm.get("FETCH_SIZE"):
-        fetch_factor = copy_bytes / (cm["FETCH_SIZE"] * 1024.0)
-    if cm.get("WRITE_SIZE"):
-        write_factor = copy_bytes / (cm["WRITE_SIZE"] * 1024.0)
+    fetch_factor = copy_bytes / (cm["FETCH_SIZE"] * 1024.0) if cm.get("FETCH_SIZE") else None
+    write_factor = copy_bytes / (cm["WRITE_SIZE"] * 1024.0) if cm.get("WRITE_SIZE") else None
     traffic = {"kernel_revision": rev, "fetch_calibration": fetch_factor,
-               "write_calibration": write_factor, "kernels": {}}
-    lines = ["# Hardware counters per dispatch (median), train-step workload 1024x1024", "",
-             "Commands (one counter set per run):", ""]
-    for tag, counters in PMC_SETS.items():
-        lines.append("- `" + PROFILE_COMMANDS["pmc"].format(counters=" ".join(counters),
-                                                            kind="<forward|backward|pose|copy>",
-                                                            tag=tag) + "`")
-    lines += ["", f"Kernel sources revision: `{rev}`", "",
-              "Calibration: a plain 1 GiB device copy (`bench.py --pmc-pass copy`) reads "
-              f"FETCH_SIZE x {fetch_factor} and WRITE_SIZE x {write_factor} of its known size "
-              "(factors applied below).", ""]
-    for kind in ("forward", "backward", "pose"):
-        for name in KERNEL_KEYS[kind]:
-            if (kind, name) not in med:
+               "write_calibration": write_factor, "alu_peak_tops": ALU_PEAK_TOPS, "cases": {}}
+    for case in PROFILE_CASES:
+        croot = os.path.join(root, case)
+        try:
+            with open(os.path.join(croot, "meta.json")) as f:
+                meta = json.load(f)
+        except OSError:
+            continue
+        stats = _find(os.path.join(croot, "trace"), "kernel_stats.csv")
+        trace = {}
+        for r in (_csv_rows(stats[0]) if stats else []):
+            short = _short_name(r.get("Name", ""))
+            if short.startswith("drr_"):
+                t = trace.setdefault(short, {"calls": 0, "total_ns": 0.0, "min": 1e30, "max": 0.0})
+                t["calls"] += int(r.get("Calls", 0))
+                t["total_ns"] += float(r.get("TotalDurationNs", 0) or 0) or \
+                    float(r.get("AverageNs", 0)) * int(r.get("Calls", 0))
+                t["min"] = min(t["min"], float(r.get("MinNs", 0)))
+                t["max"] = max(t["max"], float(r.get("MaxNs", 0)))
+        med = _median_counters(croot)
+        rows, figures = [], {}
+        for short, t in sorted(trace.items(), key=lambda kv: -kv[1]["total_ns"]):
+            avg_ns = t["total_ns"] / max(t["calls"], 1)
+            m = med.get(short, {})
+            f = {"avg_us": round(avg_ns / 1e3, 2), "calls": t["calls"]}
+            fb = m.get("FETCH_SIZE", 0.0) * 1024.0 * (fetch_factor or 1.0)
+            wb = m.get("WRITE_SIZE", 0.0) * 1024.0 * (write_factor or 1.0)
+            if "FETCH_SIZE" in m or "WRITE_SIZE" in m:
+                f["hbm_bytes_per_launch"] = round(fb + wb)
+                f["hbm_read_bytes"] = round(fb)
+                f["hbm_write_bytes"] = round(wb)
+                f["hbm_gbs"] = round((fb + wb) / (avg_ns * 1e-9) / 1e9, 1)
+                f["hbm_frac"] = round(f["hbm_gbs"] / HBM_PEAK_GBS, 4)
+            hit, miss = m.get("TCC_HIT_sum"), m.get("TCC_MISS_sum")
+            if hit is not None and miss is not None and hit + miss > 0:
+                f["l2_hit"] = round(hit / (hit + miss), 4)
+            if m.get("GRBM_GUI_ACTIVE"):
+                # GRBM_GUI_ACTIVE is summed over the XCDs
+                f["clock_ghz"] = round(m["GRBM_GUI_ACTIVE"] / MI355X_XCDS / avg_ns, 3)
+            if m.get("SQ_INSTS_VALU") and f.get("clock_ghz"):
+                cycles = avg_ns * f["clock_ghz"]
+                f["valu_busy"] = round(m["SQ_INSTS_VALU"] * 4 / (MI355X_SIMDS * cycles), 3)
+            if m.get("SQ_LDS_BANK_CONFLICT") is not None and f.get("clock_ghz"):
+                f["lds_bank_conflict"] = round(
+                    m["SQ_LDS_BANK_CONFLICT"] / (MI355X_CUS * avg_ns * f["clock_ghz"]), 3)
+            u = _kernel_units(short, meta)
+            if u is not None:
+                unit, n_units, ops, abytes = u
+                f["unit"], f["units_per_launch"] = unit, int(n_units)
+                f["alg_bytes_per_launch"] = int(n_units * abytes)
+                if ops is not None:
+                    f["alg_ops_per_launch"] = int(n_units * ops)
+                    f["alu_tops"] = round(n_units * ops / (avg_ns * 1e-9) / 1e12, 3)
+                    f["alu_frac"] = round(f["alu_tops"] / ALU_PEAK_TOPS, 4)
+                    if m.get("SQ_INSTS_VALU"):
+                        f["issued_per_algorithmic"] = round(m["SQ_INSTS_VALU"] * 64 /
+                                                            (n_units * ops), 3)
+            figures[short] = f
+            rows.append((short, t, m, f))
+        traffic["cases"][case] = figures
+        if not rows:
+            continue
+        dominant = rows[0][0]
+        lines = [f"# {dominant} and the other kernels of `{case}` ({meta['workload']})", "",
+                 f"Workload: volume {meta['volume']} {meta['dtype']}, {meta['views']} view(s) "
+                 f"{meta['det'][0]}x{meta['det'][1]}, {meta['n_samples']} samples per ray; "
+                 f"{meta['hit_rays']} of {meta['rays']} rays hit the volume; passes: "
+                 f"{', '.join(meta['passes'])}.", "",
+                 "Commands:", "",
+                 "- `" + PROFILE_COMMANDS["trace"].format(case=case) + "`"]
+        for tag, counters in PMC_SETS.items():
+            lines.append("- `" + PROFILE_COMMANDS["pmc"].format(counters=" ".join(counters),
+                                                                case=case, tag=tag) + "`")
+        lines += ["", f"Kernel sources revision: `{rev}`.  Byte counters calibrated by a plain "
+                      f"1 GiB copy: FETCH_SIZE x {fetch_factor}, WRITE_SIZE x {write_factor}.",
+                  "", f"ALU roofline: algorithmic VALU lane-operations per launch over the traced "
+                      f"average duration, against {ALU_PEAK_TOPS:.2f} TOP/s (1024 SIMDs x 16 lanes "
+                      f"x 2.4 GHz, no packed FP32).  VALU busy: SQ_INSTS_VALU x 4 cycles over 1024 "
+                      f"SIMDs x the duration at the measured clock (GRBM_GUI_ACTIVE / 8 XCDs / "
+                      f"duration).", "",
+                  "| kernel | calls | avg (us) | min | max | unit x count | ALU TOP/s | ALU frac | "
+                  "VALU busy | issued/alg | clock GHz | HBM MB/launch | HBM GB/s | L2 hit | "
+                  "LDS conflict |",
+                  "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+        for short, t, m, f in rows:
+            fmt = lambda k, d=3: "" if f.get(k) is None else f"{f[k]:.{d}f}"
+            unit = f"{f['unit']} x {f['units_per_launch']}" if "unit" in f else ""
+            mb = "" if "hbm_bytes_per_launch" not in f else f"{f['hbm_bytes_per_launch'] / 1e6:.1f}"
+            lines.append(f"| `{short}` | {t['calls']} | {f['avg_us']:.2f} | {t['min'] / 1e3:.2f} "
+                         f"| {t['max'] / 1e3:.2f} | {unit} | {fmt('alu_tops')} | "
+                         f"{fmt('alu_frac', 4)} | {fmt('valu_busy')} | "
+                         f"{fmt('issued_per_algorithmic')} | {fmt('clock_ghz')} | {mb} | "
+                         f"{fmt('hbm_gbs', 1)} | {fmt('l2_hit', 4)} | "
+                         f"{fmt('lds_bank_conflict')} |")
+        lines += ["", "Raw counters (median per dispatch):", ""]
+        for short, t, m, f in rows:
+            if not m:
                 continue
-            _counter_table(lines, traffic, name, f"{kind} pass", med[(kind, name)],
-                           fetch_factor, write_factor, durations.get(name))
-    path = os.path.join(prof_dir, "counters_train_step_1024.md")
-    with open(path, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    with open(os.path.join(prof_dir, "pmc_traffic.json"), "w") as f:
-        json.dump(traffic, f, indent=1)
-    log("wrote", path)
-
-
-MI355X_CUS, MI355X_SIMDS, MI355X_GHZ = 256, 1024, 2.4
-
-
-def _counter_table(lines, traffic, name, where, m, fetch_factor, write_factor, dur_ns=None):
-    """One kernel's median counters as a markdown table, plus its calibrated
-    HBM bytes per launch into ``traffic``.  With the kernel's traced duration,
-    VALU busy = wave instructions x 4 cycles (a wave64 instruction occupies a
-    16-lane SIMD for 4 cycles) over 1024 SIMDs x the duration's cycles, and the
-    LDS bank-conflict share = conflict cycles over 256 CUs x those cycles."""
-    lines += [f"## {name} ({where})", "", "| counter | value |", "|---|---|"]
-    for c in sorted(m):
-        lines.append(f"| {c} | {m[c]:.6g} |")
-    fb = m.get("FETCH_SIZE", 0.0) * 1024.0 * (fetch_factor or 1.0)
-    wb = m.get("WRITE_SIZE", 0.0) * 1024.0 * (write_factor or 1.0)
-    hit = m.get("TCC_HIT_sum"), m.get("TCC_MISS_sum")
-    if all(h is not None for h in hit) and sum(hit) > 0:
-        lines.append(f"| L2 hit rate | {hit[0] / (hit[0] + hit[1]):.4f} |")
-    valu_busy = None
-    if dur_ns:
-        cycles = dur_ns * MI355X_GHZ
-        lines.append(f"| traced duration (us) | {dur_ns / 1e3:.2f} |")
-        if m.get("SQ_INSTS_VALU"):
-            valu_busy = round(m["SQ_INSTS_VALU"] * 4 / (MI355X_SIMDS * cycles), 3)
-            lines.append(f"| VALU busy | {valu_busy:.3f} |")
-        if m.get("SQ_LDS_BANK_CONFLICT") is not None:
-            lines.append(f"| LDS bank-conflict share | "
-                         f"{m['SQ_LDS_BANK_CONFLICT'] / (MI355X_CUS * cycles):.3f} |")
-    lines += ["", f"HBM-side traffic per launch (calibrated): read {fb / 1e6:.1f} MB, "
-                  f"write {wb / 1e6:.1f} MB, total {(fb + wb) / 1e6:.1f} MB", ""]
-    if fb or wb:
-        traffic["kernels"][name] = {"hbm_bytes_per_launch": fb + wb, "read_bytes": fb,
-                                    "write_bytes": wb, "valu_busy": valu_busy}
+            lines.append(f"- `{short}`: " + ", ".join(f"{c} {m[c]:.6g}" for c in sorted(m)))
+        path = os.path.join(prof_dir, f"{dominant}__{case}.md")
+        with open(path, "w") as fo:
+            fo.write("\n".join(lines) + "\n")
+        log("wrote", path)
+    with open(os.path.join(prof_dir, "pmc_traffic.json"), "w") as fo:
+        json.dump(traffic, fo, indent=1)
 
 
 def main():
@@ -659,7 +784,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-workloads", action="store_true")
-    ap.add_argument("--pmc-pass", choices=list(PMC_KINDS))
+    ap.add_argument("--profile-run", metavar="CASE", choices=list(PROFILE_CASES) + [COPY_CASE],
+                    help="run one profile case's fixed launch sequence (for rocprofv3)")
+    ap.add_argument("--reps", type=int, default=3)
+    ap.add_argument("--meta-dir", metavar="DIR",
+                    help="with --profile-run: write the case's unit counts to DIR/meta.json")
     ap.add_argument("--profile-summary", metavar="DIR",
                     help="summarise rocprofv3 outputs under DIR into profiles/ (CPU only)")
     args = ap.parse_args()
@@ -681,8 +810,8 @@ def main():
         sys.exit(1)
     drr.library()   # fail loudly if the HIP library is not built
     dev = torch.device("cuda:0")
-    if args.pmc_pass:
-        pmc_pass(args.pmc_pass, dev)
+    if args.profile_run:
+        profile_run(args.profile_run, args.reps, dev, args.meta_dir)
         return
 
     w = W.make_workload(3)
@@ -704,17 +833,16 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall / max(args.steps, 1) * 1e3
 
-    # per-kernel GPU time of the same step, HIP events on the launch stream
+    # per-pass GPU time of the same step, HIP events on the launch stream; each
+    # pass is one ABI call: the forward is one launch of the LDS-staged march,
+    # the backward the gradient pass named by backward_kernel()
     fwd_ms, bwd_ms = time_events([res.forward, res.backward], max(args.steps, 1))
-    # each pass is one ABI call: the forward launches the corner-cell relayout
-    # and the march, the backward the gradient fill and the scatter
-    # the forward of this workload is one launch of the LDS-staged march
-    rf = roofline("drr_march_staged_kernel", forward_bytes(res, hits), fwd_ms,
-                  measured_traffic(KERNEL_KEYS["forward"]),
-                  measured_valu_busy("drr_march_staged_kernel"))
-    rb = roofline("drr_scatter_kernel (with gradient fill)", backward_bytes(res, hits), bwd_ms,
-                  measured_traffic(KERNEL_KEYS["backward"]),
-                  measured_valu_busy("drr_scatter_kernel"))
+    eff = hits * w.n_samples
+    fk, bk = "drr_march_staged_kernel", backward_kernel()
+    rf = roofline_alu(fk, eff * OPS_FORWARD_SAMPLE, fwd_ms, measured_counters("train1024", fk))
+    rb = roofline_alu(bk, eff * OPS_BACKWARD_SAMPLE, bwd_ms, measured_counters("train1024", bk))
+    rf["algorithmic_gbs"] = round(forward_bytes(res, hits) / (fwd_ms * 1e-3) / 1e9, 1)
+    rb["algorithmic_gbs"] = round(backward_bytes(res, hits) / (bwd_ms * 1e-3) / 1e9, 1)
     dominant, other = (rb, rf) if bwd_ms >= fwd_ms else (rf, rb)
 
     out = {
