@@ -665,7 +665,9 @@ def profile_summary(root: str):
     os.makedirs(prof_dir, exist_ok=True)
     rev = kernel_revision()
     copy = _median_counters(os.path.join(root, COPY_CASE))
-    cm = next(iter(copy.values()), {})
+    # the copy kernel: the one that fetches the most (the run also fills its source)
+    cm = max(copy.values(), key=lambda m: m.get("FETCH_SIZE", 0.0) + m.get("WRITE_SIZE", 0.0),
+             default={})
     copy_bytes = float(1 << 30)
     fetch_factor = copy_bytes / (cm["FETCH_SIZE"] * 1024.0) if cm.get("FETCH_SIZE") else None
     write_factor = copy_bytes / (cm["WRITE_SIZE"] * 1024.0) if cm.get("WRITE_SIZE") else None

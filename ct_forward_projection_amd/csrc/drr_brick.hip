@@ -91,10 +91,40 @@ __global__ __launch_bounds__(256) void drr_ray_record_kernel(
         block_max[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+// One thread per view: its fp32 projection K [R | t] and its rays in
+// continuous voxel index space (from the fp64 camera), for the brick kernel.
+__global__ __launch_bounds__(64) void drr_brick_views_kernel(VolumeDesc V, Intrinsics K,
+                                                              const float* __restrict__ poses,
+                                                              int n_views,
+                                                              BrickView* __restrict__ views)
+{
+    const int v = blockIdx.x * blockDim.x + threadIdx.x;
+    if (v >= n_views) return;
+    const float* pose = poses + 12 * v;
+    BrickView out;
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            out.P[r * 4 + c] = (float)((double)K.k[r * 3 + 0] * (double)pose[0 * 4 + c] +
+                                       (double)K.k[r * 3 + 1] * (double)pose[1 * 4 + c] +
+                                       (double)K.k[r * 3 + 2] * (double)pose[2 * 4 + c]);
+    }
+    ViewGeom G;
+    view_setup(pose, K, G);
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) out.ray.m[a * 3 + k] = (float)(G.M[a * 3 + k] * V.inv_s[a]);
+        out.ray.c[a] = (float)(G.C[a] * V.inv_s[a] + V.q_off[a]);
+    }
+    views[v] = out;
+}
+
 // ------------------------------------------------------------ brick scatter
 
 constexpr int kBrickThreads = 256;
-constexpr int kViewChunk = kBrickThreads;      // views whose pixel rectangles sit in LDS at once
+constexpr int kViewChunk = 64;      // views whose pixel rectangles and rays sit in LDS at once
 
 // Workgroup-wide exclusive prefix sum of one int per thread; returns the total.
 __device__ inline int block_exclusive_scan(int v, int* red, int& excl)
@@ -125,25 +155,42 @@ __device__ inline int block_exclusive_scan(int v, int* red, int& excl)
 // kViewChunk views at a time.  Candidate j of a chunk is pixel j - start[v]
 // (row-major in the rectangle) of the view v with start[v] <= j < start[v+1].
 struct BrickCandidates {
-    int* start;      // kViewChunk + 1 exclusive prefix sums of the rectangle areas
-    int* rect;       // kViewChunk x 3: r0, c0, width
+    int* start;          // kViewChunk + 1 exclusive prefix sums of the rectangle areas
+    int* rect;           // kViewChunk x 3: r0, c0, width
+    BrickViewRay* ray;   // kViewChunk: the view's rays in index space
 
-    __device__ int total(int n_in_chunk) const { return start[n_in_chunk]; }
-
-    // record index of candidate j (pair = view * C + channel)
-    __device__ long long record(int j, int n_in_chunk, int first_view, int C, int ch, int H,
-                                int W) const
+    // view slot and pixel of candidate j
+    __device__ void pixel(int j, int n_in_chunk, int& v, int& r, int& c) const
     {
         int lo = 0, hi = n_in_chunk - 1;               // last v with start[v] <= j
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (start[mid] <= j) lo = mid; else hi = mid - 1;
         }
+        v = lo;
         const int local = j - start[lo];
         const int w = rect[3 * lo + 2];
-        const int rr = local / w;
-        const int r = rect[3 * lo] + rr, c = rect[3 * lo + 1] + (local - rr * w);
-        const long long pair = (long long)(first_view + lo) * C + ch;
+        // local / w: below 2^22 from an fp32 reciprocal (within one of the
+        // quotient), corrected to the exact one
+        int rr;
+        if (local < (1 << 22)) {
+            rr = (int)((float)local * __builtin_amdgcn_rcpf((float)w));
+            rr -= rr * w > local ? 1 : 0;
+            rr += (rr + 1) * w <= local ? 1 : 0;
+        } else {
+            rr = local / w;
+        }
+        r = rect[3 * lo] + rr;
+        c = rect[3 * lo + 1] + (local - rr * w);
+    }
+
+    // record index of candidate j (pair = view * C + channel)
+    __device__ long long record(int j, int n_in_chunk, int first_view, int C, int ch, int H,
+                                int W) const
+    {
+        int v, r, c;
+        pixel(j, n_in_chunk, v, r, c);
+        const long long pair = (long long)(first_view + v) * C + ch;
         return (pair * H + r) * W + c;
     }
 };
@@ -159,33 +206,24 @@ __device__ inline RayRecord load_record(const RayRecord* __restrict__ rec, long 
     return r;
 }
 
-// Sets up the candidate rectangles of views [first, first + count) for brick
-// box `b` (count <= kViewChunk) in `cand`; returns the candidate total.
-__device__ inline int brick_chunk(const VolumeDesc& V, const Intrinsics& K,
-                                  const float* __restrict__ poses, int H, int W,
-                                  const BrickBox& b, int first, int count,
+// Sets up the candidate rectangles and rays of views [first, first + count)
+// for the brick region `g` (count <= kViewChunk) in `cand`; returns the
+// candidate total.
+__device__ inline int brick_chunk(const BrickView* __restrict__ views, int H, int W,
+                                  const BrickRegion& g, int first, int count,
                                   BrickCandidates& cand, int* red)
 {
     int area = 0;
     const int t = threadIdx.x;
     if (t < count) {
-        const float* pose = poses + 12 * (first + t);
-        float P[12];
-#pragma unroll
-        for (int rr = 0; rr < 3; ++rr) {
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                P[rr * 4 + cc] = K.k[rr * 3 + 0] * pose[0 * 4 + cc] +
-                                 K.k[rr * 3 + 1] * pose[1 * 4 + cc] +
-                                 K.k[rr * 3 + 2] * pose[2 * 4 + cc];
-            }
-        }
-        const PixelRect R = brick_pixel_rect(P, V.n, V.s, V.q_off, b, H, W);
+        const BrickView bv = views[first + t];
+        const PixelRect R = brick_pixel_rect(bv.P, g, H, W);
         const int w = R.c1 - R.c0 + 1, h = R.r1 - R.r0 + 1;
         area = (w > 0 && h > 0) ? w * h : 0;
         cand.rect[3 * t] = R.r0;
         cand.rect[3 * t + 1] = R.c0;
         cand.rect[3 * t + 2] = w > 0 ? w : 1;
+        cand.ray[t] = bv.ray;
     }
     int excl;
     const int total = block_exclusive_scan(area, red, excl);
@@ -259,7 +297,7 @@ struct BrickQueue {
 // to the copy.
 template <int B, int Q, bool MERGE>
 __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
-    VolumeDesc V, Intrinsics K, const float* __restrict__ poses, int H, int W, Batch bt,
+    VolumeDesc V, const BrickView* __restrict__ views, int H, int W, Batch bt,
     const RayRecord* __restrict__ rec, const float* __restrict__ block_max,
     float* __restrict__ grad, int nbx, int nby)
 {
@@ -270,17 +308,19 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
     __shared__ BrickQueue<Q> qu;
     __shared__ int start[kViewChunk + 1];
     __shared__ int rect[3 * kViewChunk];
+    __shared__ BrickViewRay vrays[kViewChunk];
     __shared__ int red[kBrickThreads / 64];
     __shared__ float fred[kBrickThreads / 64];
 
     const int brick = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
     const int bx = brick % nbx, by = (brick / nbx) % nby, bz = brick / (nbx * nby);
     const BrickBox b = brick_box(V.n, B, bx, by, bz);
+    const BrickRegion reg = brick_region(V.n, V.s, V.q_off, b);
     const int cv = (int)blockIdx.y;                     // channel-volume
     const int vol = cv / bt.C, ch = cv - vol * bt.C;
     const int first_view = vol * bt.vpv;
     grad += (size_t)cv * bt.grad_stride;
-    BrickCandidates cand{start, rect};
+    BrickCandidates cand{start, rect, vrays};
     const int t = threadIdx.x;
 
     for (int i = t; i < NE; i += kBrickThreads) acc[i] = 0ull;
@@ -292,7 +332,7 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
     float cmax = 0.0f;
     for (int v0 = 0; v0 < bt.vpv; v0 += kViewChunk) {
         const int count = min(kViewChunk, bt.vpv - v0);
-        brick_chunk(V, K, poses, H, W, b, first_view + v0, count, cand, red);
+        brick_chunk(views, H, W, reg, first_view + v0, count, cand, red);
         for (int v = 0; v < count; ++v) {
             const int w = rect[3 * v + 2];
             const int h = (start[v + 1] - start[v]) / w;
@@ -320,7 +360,7 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
         cmax = 0.0f;
         for (int v0 = 0; v0 < bt.vpv; v0 += kViewChunk) {
             const int count = min(kViewChunk, bt.vpv - v0);
-            const int total = brick_chunk(V, K, poses, H, W, b, first_view + v0, count, cand, red);
+            const int total = brick_chunk(views, H, W, reg, first_view + v0, count, cand, red);
             for (int j = t; j < total; j += kBrickThreads) {
                 const long long ri = cand.record(j, count, first_view + v0, bt.C, ch, H, W);
                 const float cb = rec[ri].cell_bound;
@@ -349,27 +389,40 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
     if (cmax > 0.0f) {
         for (int v0 = 0; v0 < bt.vpv; v0 += kViewChunk) {
             const int count = min(kViewChunk, bt.vpv - v0);
-            const int total = brick_chunk(V, K, poses, H, W, b, first_view + v0, count, cand, red);
+            const int total = brick_chunk(views, H, W, reg, first_view + v0, count, cand, red);
+            // this thread's candidate of a round: its record, loaded one round
+            // ahead so the load's latency hides behind the previous round's
+            // samples (a ray that misses the region needs no record: n = 0)
+            auto fetch = [&](int j, RayRecord& r) {
+                r.n = 0;
+                if (j >= total) return;
+                int cv_slot, cr, cc;
+                cand.pixel(j, count, cv_slot, cr, cc);
+                if (!brick_ray_may_hit(vrays[cv_slot], V.n, b, (float)cc + 0.5f,
+                                       (float)cr + 0.5f))
+                    return;
+                const long long pair = (long long)(first_view + v0 + cv_slot) * bt.C + ch;
+                r = load_record(rec, (pair * H + cr) * W + cc);
+            };
+            RayRecord next;
+            fetch(t, next);
             for (int jb = 0; jb < total; jb += kBrickThreads) {
                 // fill: this thread's candidate and its samples in the brick
-                const int j = jb + t;
+                const RayRecord r = next;
+                fetch(jb + kBrickThreads + t, next);
                 int cnt = 0;
-                if (j < total) {
-                    const long long ri = cand.record(j, count, first_view + v0, bt.C, ch, H, W);
-                    const RayRecord r = load_record(rec, ri);
-                    if (r.n != 0 && isfinite(r.cell_bound)) {
-                        int k_lo, k_hi;
-                        int64_t q[3];
-                        brick_exact_range(r, b, k_lo, k_hi, q);
-                        cnt = k_hi - k_lo;
-                        if (cnt > 0) {
+                if (r.n != 0 && isfinite(r.cell_bound)) {
+                    int k_lo, k_hi;
+                    int64_t q[3];
+                    brick_exact_range(r, b, k_lo, k_hi, q);
+                    cnt = k_hi - k_lo;
+                    if (cnt > 0) {
 #pragma unroll
-                            for (int a = 0; a < 3; ++a) {
-                                qu.q[a][t] = q[a];
-                                qu.d[a][t] = r.dq[a];
-                            }
-                            qu.c[t] = r.coef * scale;
+                        for (int a = 0; a < 3; ++a) {
+                            qu.q[a][t] = q[a];
+                            qu.d[a][t] = r.dq[a];
                         }
+                        qu.c[t] = r.coef * scale;
                     }
                 }
                 int first_sample;
@@ -477,7 +530,7 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
     __syncthreads();
     for (int v0 = 0; v0 < bt.vpv; v0 += kViewChunk) {
         const int count = min(kViewChunk, bt.vpv - v0);
-        const int total = brick_chunk(V, K, poses, H, W, b, first_view + v0, count, cand, red);
+        const int total = brick_chunk(views, H, W, reg, first_view + v0, count, cand, red);
         for (int j = threadIdx.x; j < total; j += kBrickThreads) {
             const long long ri = cand.record(j, count, first_view + v0, bt.C, ch, H, W);
             const RayRecord r = load_record(rec, ri);
@@ -534,6 +587,14 @@ hipError_t launch_brick_backward(const LaunchArgs& a, const float* grad_out, con
     RayRecord* rec = static_cast<RayRecord*>(workspace);
     float* block_max = reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                 ray_record_bytes(a.n_views, a.C, a.H, a.W));
+    BrickView* views = reinterpret_cast<BrickView*>(
+        reinterpret_cast<char*>(block_max) + ray_block_max_bytes(a.n_views, a.C, a.H, a.W));
+    if (a.n_views > 0) {
+        hipLaunchKernelGGL(drr_brick_views_kernel, dim3((a.n_views + 63) / 64), dim3(64), 0,
+                           stream, a.V, a.K, a.poses, a.n_views, views);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int rb = (int)((n_rays + 255) / 256);
     if (n_rays > 0) {
         if (a.mode == kBeerLambert)
@@ -564,11 +625,11 @@ hipError_t launch_brick_backward(const LaunchArgs& a, const float* grad_out, con
     const dim3 grid((unsigned)(nbx * nby * nbz), (unsigned)(a.n_volumes * a.C));
     if (merge)
         hipLaunchKernelGGL((drr_brick_scatter_kernel<B, kBrickThreads, true>), grid,
-                           dim3(kBrickThreads), 0, stream, a.V, a.K, a.poses, a.H, a.W, bt, rec,
+                           dim3(kBrickThreads), 0, stream, a.V, views, a.H, a.W, bt, rec,
                            block_max, grad, nbx, nby);
     else
         hipLaunchKernelGGL((drr_brick_scatter_kernel<B, kBrickThreads, false>), grid,
-                           dim3(kBrickThreads), 0, stream, a.V, a.K, a.poses, a.H, a.W, bt, rec,
+                           dim3(kBrickThreads), 0, stream, a.V, views, a.H, a.W, bt, rec,
                            block_max, grad, nbx, nby);
     return hipGetLastError();
 }

@@ -135,23 +135,36 @@ __host__ __device__ inline int brick_line_base(int B, int a, int i, int& step)
 // plus 2^-12 of the largest projected coordinate, and a region with a corner
 // at or behind the camera plane, or nearer to it than 2^-10 of the farthest
 // corner's depth, gets the whole detector.
-//   P: K [R | t] as 3 x 4; s: spacing; q_off: (n - 1) / 2 per axis.
+//   P: K [R | t] as 3 x 4 (fp32); g: the region (brick_region).
 struct PixelRect {
     int r0, r1, c0, c1;
 };
 
-__host__ __device__ inline PixelRect brick_pixel_rect(const float P[12], const int n[3],
-                                                      const double s[3], const double q_off[3],
-                                                      const BrickBox& b, int H, int W)
-{
-    PixelRect R{0, H - 1, 0, W - 1};
+// The brick region in world coordinates (mm): continuous indices
+// [lo - 1, lo + e) per axis cut to [-1/2, n - 1/2], at (q - q_off) s.
+struct BrickRegion {
     float lo[3], hi[3];
+};
+
+__host__ __device__ inline BrickRegion brick_region(const int n[3], const double s[3],
+                                                    const double q_off[3], const BrickBox& b)
+{
+    BrickRegion g;
     for (int a = 0; a < 3; ++a) {
         const double ql = fmax((double)(b.lo[a] - 1), -0.5);
         const double qh = fmin((double)(b.lo[a] + b.e[a]), (double)n[a] - 0.5);
-        lo[a] = (float)((ql - q_off[a]) * s[a]);
-        hi[a] = (float)((qh - q_off[a]) * s[a]);
+        g.lo[a] = (float)((ql - q_off[a]) * s[a]);
+        g.hi[a] = (float)((qh - q_off[a]) * s[a]);
     }
+    return g;
+}
+
+__host__ __device__ inline PixelRect brick_pixel_rect(const float P[12], const BrickRegion& g,
+                                                      int H, int W)
+{
+    PixelRect R{0, H - 1, 0, W - 1};
+    const float* lo = g.lo;
+    const float* hi = g.hi;
     float umin = 3e38f, umax = -3e38f, vmin = 3e38f, vmax = -3e38f;
     float wmin = 3e38f, wmax = -3e38f;
     for (int k = 0; k < 8; ++k) {
@@ -187,6 +200,43 @@ __host__ __device__ inline PixelRect brick_pixel_rect(const float P[12], const i
     return R;
 }
 
+// A view's rays in continuous voxel index space: image point (u, v, 1) looks
+// along m (u, v, 1) from c (fp32, rounded from the fp64 camera), i.e.
+// q(t) = c + t m (u, v, 1), t >= 0.
+struct BrickViewRay {
+    float m[9];
+    float c[3];
+};
+
+// What the brick kernel needs of a view (fp32, 96 bytes): its projection
+// K [R | t] and its rays in index space.
+struct BrickView {
+    float P[12];
+    BrickViewRay ray;
+};
+
+// Whether the ray through image point (u, v, 1) can have samples in the brick
+// region (continuous indices [lo - 1, lo + e) per axis, cut to the volume): the
+// slab test against that box widened by 1/16 voxel per side, which absorbs
+// the fp32 rounding of the view's rays.  False only when the line misses the
+// widened box; a comparison with NaN (a ray parallel to a face, starting on it)
+// keeps the ray.
+__host__ __device__ inline bool brick_ray_may_hit(const BrickViewRay& vr, const int n[3],
+                                                  const BrickBox& b, float u, float v)
+{
+    float tmin = -3e38f, tmax = 3e38f;
+    for (int a = 0; a < 3; ++a) {
+        const float d = vr.m[a * 3] * u + vr.m[a * 3 + 1] * v + vr.m[a * 3 + 2];
+        const float lo = fmaxf((float)(b.lo[a] - 1), -0.5f) - 0.0625f;
+        const float hi = fminf((float)(b.lo[a] + b.e[a]), (float)n[a] - 0.5f) + 0.0625f;
+        const float inv = 1.0f / d;
+        const float t1 = (lo - vr.c[a]) * inv, t2 = (hi - vr.c[a]) * inv;
+        tmin = fmaxf(tmin, fminf(t1, t2));
+        tmax = fminf(tmax, fmaxf(t1, t2));
+    }
+    return !(tmax < tmin);
+}
+
 // fp32 value of a 64-bit integer from its two words: the high word's
 // conversion carries the scale 2^32, the low word's is exact to 2^-24
 // relative, so the result is within 2^-23 of x relative.
@@ -198,7 +248,7 @@ __host__ __device__ inline float int64_to_float(int64_t x)
 // A range [k_lo, k_hi) of a ray's samples that contains every sample whose
 // continuous index lies in the brick region [lo - 1, lo + e) on every axis (it
 // may hold a few more).  The bounds are estimated in fp32 from the exact
-// fixed-point differences to the region's faces and widened by two samples
+// fixed-point differences to the region's faces and widened by one sample
 // plus 2^-20 of their size, which covers the fp32 rounding of the estimate
 // (relative error below 2^-21) for any n <= 2^24.
 __host__ __device__ inline void brick_sample_range(const RayRecord& r, const BrickBox& b,
@@ -224,8 +274,8 @@ __host__ __device__ inline void brick_sample_range(const RayRecord& r, const Bri
         k_lo = k_hi = 0;
         return;
     }
-    const float wl = 2.0f + fabsf(lo) * 9.5367431640625e-07f;   // 2^-20
-    const float wh = 2.0f + fabsf(hi) * 9.5367431640625e-07f;
+    const float wl = 1.0f + fabsf(lo) * 9.5367431640625e-07f;   // 2^-20
+    const float wh = 1.0f + fabsf(hi) * 9.5367431640625e-07f;
     const float fl = floorf(lo - wl), fh = ceilf(hi + wh);
     k_lo = fl <= 0.0f ? 0 : (fl >= (float)r.n ? r.n : (int)fl);
     k_hi = fh <= 0.0f ? 0 : (fh >= (float)r.n ? r.n : (int)fh);
@@ -262,21 +312,20 @@ __host__ __device__ inline void brick_exact_range(const RayRecord& r, const Bric
 {
     brick_sample_range(r, b, k_lo, k_hi);
     if (k_lo >= k_hi) return;
-    int64_t q[3], qe[3];
-    for (int a = 0; a < 3; ++a) {
-        const int64_t base = r.q0[a] - (int64_t)(b.lo[a] - 1) * ((int64_t)1 << 32);
-        q[a] = base + (int64_t)k_lo * r.dq[a];
-        qe[a] = base + (int64_t)(k_hi - 1) * r.dq[a];
-    }
+    int64_t* q = q_rel;
+    for (int a = 0; a < 3; ++a)
+        q[a] = r.q0[a] - (int64_t)(b.lo[a] - 1) * ((int64_t)1 << 32) + (int64_t)k_lo * r.dq[a];
     while (k_lo < k_hi && !brick_rel_inside(q, b)) {
         ++k_lo;
         for (int a = 0; a < 3; ++a) q[a] += r.dq[a];
     }
+    if (k_lo >= k_hi) return;
+    int64_t qe[3];
+    for (int a = 0; a < 3; ++a) qe[a] = q[a] + (int64_t)(k_hi - 1 - k_lo) * r.dq[a];
     while (k_hi > k_lo && !brick_rel_inside(qe, b)) {
         --k_hi;
         for (int a = 0; a < 3; ++a) qe[a] -= r.dq[a];
     }
-    for (int a = 0; a < 3; ++a) q_rel[a] = q[a];
 }
 
 }  // namespace drr

@@ -192,7 +192,7 @@ struct BackwardRead {
 };
 
 // The brick-owned backward's workspace: 64-byte ray records, then one float
-// per 256 records (their largest cell bound).
+// per 256 records (their largest cell bound), ...
 inline size_t ray_record_bytes(int n_views, int C, int H, int W)
 {
     return ((size_t)n_views * (size_t)C * (size_t)H * (size_t)W * 64 + 255) & ~(size_t)255;
@@ -204,6 +204,9 @@ inline size_t ray_block_max_bytes(int n_views, int C, int H, int W)
     return (((rays + 255) / 256) * 4 + 255) & ~(size_t)255;
 }
 
+// ... then 96 bytes per view (its fp32 projection and index-space rays).
+inline size_t brick_view_bytes(int n_views) { return ((size_t)n_views * 96 + 255) & ~(size_t)255; }
+
 inline BackwardRead plan_backward(int n_volumes, int C, int nz, int ny, int nx, int elem_bytes,
                                   int n_views, int H, int W, int N, int mode, int clip,
                                   bool has_tf)
@@ -214,8 +217,8 @@ inline BackwardRead plan_backward(int n_volumes, int C, int nz, int ny, int nx, 
         const double view_reuse = (double)H * (double)W * (double)N / cells;
         if (clip == kClipBox && view_reuse < kBrickMaxViewReuse) {
             r.brick = true;
-            r.workspace_bytes =
-                ray_record_bytes(n_views, C, H, W) + ray_block_max_bytes(n_views, C, H, W);
+            r.workspace_bytes = ray_record_bytes(n_views, C, H, W) +
+                                ray_block_max_bytes(n_views, C, H, W) + brick_view_bytes(n_views);
         }
         return r;
     }

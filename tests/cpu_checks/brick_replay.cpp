@@ -84,7 +84,7 @@ int run_case(const Case& cs)
     const double Ki[9] = {1 / f, 0, -K[2] / f, 0, 1 / f, -K[5] / f, 0, 0, 1};
     const size_t n_vox = (size_t)nx * ny * nz;
     std::vector<double> direct(n_vox, 0.0), bricked(n_vox, 0.0);
-    long long n_samples_total = 0, n_candidates = 0;
+    long long n_samples_total = 0, n_candidates = 0, n_rejected = 0;
 
     for (int v = 0; v < cs.views; ++v) {
         // camera-to-world rotation Rc, centre C; world-to-camera R = Rc^T, t = -R C
@@ -114,6 +114,13 @@ int run_case(const Case& cs)
         for (int a = 0; a < 3; ++a)
             for (int b = 0; b < 3; ++b)
                 M[a * 3 + b] = R[a] * Ki[b] + R[3 + a] * Ki[3 + b] + R[6 + a] * Ki[6 + b];
+
+        // the view's rays in index space, fp32 (as the kernel keeps them)
+        drr::BrickViewRay vr;
+        for (int a = 0; a < 3; ++a) {
+            for (int k = 0; k < 3; ++k) vr.m[a * 3 + k] = (float)(M[a * 3 + k] / cs.s[a]);
+            vr.c[a] = (float)(C[a] / cs.s[a] + q_off[a]);
+        }
 
         // ray records of the view
         std::vector<RayRecord> rec((size_t)cs.H * cs.W);
@@ -184,7 +191,8 @@ int run_case(const Case& cs)
                 for (int bx = 0; bx < nbx; ++bx) {
                     const BrickBox b = drr::brick_box(cs.n, B, bx, by, bz);
                     for (int a = 0; a < 3; ++a) CHECK(b.e[a] >= 1 && b.e[a] <= B, "extent %d", b.e[a]);
-                    const PixelRect pr = drr::brick_pixel_rect(Pm, cs.n, cs.s, q_off, b, cs.H, cs.W);
+                    const drr::BrickRegion reg = drr::brick_region(cs.n, cs.s, q_off, b);
+                    const PixelRect pr = drr::brick_pixel_rect(Pm, reg, cs.H, cs.W);
                     std::vector<double> acc(NE, 0.0);
                     for (int r = 0; r < cs.H; ++r)
                         for (int c = 0; c < cs.W; ++c) {
@@ -192,6 +200,9 @@ int run_case(const Case& cs)
                             if (o.n == 0) continue;
                             const bool cand = r >= pr.r0 && r <= pr.r1 && c >= pr.c0 && c <= pr.c1;
                             int k_lo = 0, k_hi = 0, x_lo = 0, x_hi = 0;
+                            if (cand && !drr::brick_ray_may_hit(vr, cs.n, b, (float)c + 0.5f,
+                                                                 (float)r + 0.5f))
+                                ++n_rejected;
                             if (cand) {
                                 ++n_candidates;
                                 drr::brick_sample_range(o, b, k_lo, k_hi);
@@ -224,6 +235,9 @@ int run_case(const Case& cs)
                                 if (!in) continue;
                                 CHECK(cand, "brick (%d,%d,%d) misses pixel (%d,%d) of view %d",
                                       bx, by, bz, r, c, v);
+                                CHECK(drr::brick_ray_may_hit(vr, cs.n, b, (float)c + 0.5f,
+                                                             (float)r + 0.5f),
+                                      "reject test drops pixel (%d,%d) of view %d", r, c, v);
                                 CHECK(k >= k_lo && k < k_hi,
                                       "sample %d outside [%d, %d) (brick %d,%d,%d)", k, k_lo,
                                       k_hi, bx, by, bz);
@@ -265,10 +279,10 @@ int run_case(const Case& cs)
         scale = fmax(scale, fabs(direct[i]));
     }
     CHECK(worst <= 1e-12 * fmax(scale, 1e-300), "bricked vs direct: %g of %g", worst, scale);
-    printf("case n=(%d,%d,%d) B=%d views=%d det=%dx%d N=%d%s: %lld samples, %lld candidates, "
-           "max |bricked - direct| %.3g (scale %.3g)\n",
+    printf("case n=(%d,%d,%d) B=%d views=%d det=%dx%d N=%d%s: %lld samples, %lld candidates "
+           "(%lld rejected), max |bricked - direct| %.3g (scale %.3g)\n",
            nx, ny, nz, cs.B, cs.views, cs.H, cs.W, cs.N, cs.inside ? " inside" : "",
-           n_samples_total, n_candidates, worst, scale);
+           n_samples_total, n_candidates, n_rejected, worst, scale);
     return g_fail;
 }
 
