@@ -87,6 +87,9 @@ class Resident:
         need = drr.drr_workspace_bytes(nz, ny, nx, drr.BF16 if bf16 else drr.F32, w.n_views,
                                        w.det_h, w.det_w, w.n_samples, 0)
         self.workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        need_b = drr.drr_workspace_bytes(nz, ny, nx, drr.F32, w.n_views, w.det_h, w.det_w,
+                                         w.n_samples, 1) if w.grad_out is not None else 0
+        self.workspace_b = torch.empty(need_b, dtype=torch.uint8, device=dev) if need_b else None
         self.pose_ws = None
 
     def forward(self):
@@ -99,7 +102,8 @@ class Resident:
         import ct_forward_projection_amd as drr
         w = self.w
         drr.drr_backward_volume(w.volume.shape, w.spacing, w.K, self.poses, w.det_h, w.det_w,
-                                w.n_samples, w.mode, self.g, self.s, grad_volume=self.grad)
+                                w.n_samples, w.mode, self.g, self.s, grad_volume=self.grad,
+                                workspace=self.workspace_b)
 
     def pose_backward(self):
         import ct_forward_projection_amd as drr
@@ -336,6 +340,11 @@ def workload_lines(dev, reps):
     lines = {}
     for i, bf16 in [(1, False), (2, False), (2, True), (3, False), (4, False), (5, False)]:
         w = W.make_workload(i, with_bf16=bf16)
+        if i == 2 and not bf16:
+            # the batch's volume backward (views sparse against the voxels), for an
+            # upstream gradient U[-1, 1) seeded as the profile case's
+            w.grad_out = np.random.default_rng(2100 + w.n_views).uniform(
+                -1.0, 1.0, size=(w.n_views, w.det_h, w.det_w)).astype(np.float32)
         res = Resident(w, dev, bf16=bf16)
         hits = res.hit_rays()
         fns = [res.forward] + ([res.backward] if w.grad_out is not None else [])
