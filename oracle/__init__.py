@@ -79,6 +79,9 @@ def _load():
     lib.oracle_render_adjoint.argtypes = [P, I, I, I, I, I, P, P, P, I, I, I, I, I, D, I, D, P,
                                           P, I, P, P, I, ctypes.c_longlong]
     lib.oracle_render_adjoint.restype = I
+    lib.oracle_render_pose_gradient.argtypes = [P, I, I, I, I, I, P, P, P, I, I, I, I, I, D, I,
+                                                D, P, P, I, P, P, I]
+    lib.oracle_render_pose_gradient.restype = I
     lib.oracle_view_range.argtypes = [P, P, D, P]
     lib.oracle_view_range.restype = None
     lib.oracle_poisson_surrogate.argtypes = [P, P, ctypes.c_long, D, P, P, P]
@@ -390,44 +393,26 @@ def poisson_surrogate(transmission, noise, i0: float, grad_out=None):
     return out if grad is None else (out, grad)
 
 
-def _transfer_numpy(x, xp, yp):
-    """The per-channel piecewise-linear map written out in numpy: linear between
-    knots, the first and last segments extended beyond them."""
-    x = np.asarray(x, dtype=np.float64)
-    xp = np.asarray(xp, dtype=np.float64)
-    yp = np.asarray(yp, dtype=np.float64)
-    seg = np.clip(np.searchsorted(xp, x, side="right") - 1, 0, len(xp) - 2)
-    m = (yp[seg + 1] - yp[seg]) / (xp[seg + 1] - xp[seg])
-    return yp[seg] + m * (x - xp[seg])
-
-
 def render_pose_gradient(volume, spacing, K, poses, det_h: int, det_w: int, n_samples: int,
                          mode: int, grad_out, density_factor: float = 1.0, transfer=None,
+                         clip: int = CLIP_BOX, margin: float = 30.0,
                          n_threads: Optional[int] = None) -> np.ndarray:
-    """dL/dP (V, 3, 4) for L = sum(grad_out * render(...)) in Beer-Lambert or
-    line-integral mode with the box clip: for each view, the sum over its
-    channels of ``pose_gradient`` on the channel-volume f * tf(x), which is the
-    same operator (in these modes render(x) with factor f and map tf equals the
-    plain forward of f * tf(x)).  The mapped volume passes the fp32 interface
-    of ``pose_gradient`` (relative rounding 6e-8)."""
-    vol = np.asarray(volume, dtype=np.float32)
-    if vol.ndim == 3:
-        vol = vol[None, None]
-    B, C = vol.shape[:2]
-    P = np.asarray(poses, dtype=np.float64).reshape(-1, 3, 4)
-    V = P.shape[0]
-    vpv = V // B
-    g = np.asarray(grad_out, dtype=np.float64).reshape(V, C, det_h, det_w)
-    out = np.zeros((V, 3, 4))
-    for b in range(B):
-        for c in range(C):
-            m = vol[b, c].astype(np.float64)
-            if transfer is not None:
-                xp = np.asarray(transfer[0], dtype=np.float32).reshape(C, -1)[c]
-                yp = np.asarray(transfer[1], dtype=np.float32).reshape(C, -1)[c]
-                m = _transfer_numpy(m, xp, yp)
-            m = (density_factor * m).astype(np.float32)
-            views = slice(b * vpv, (b + 1) * vpv)
-            out[views] += pose_gradient(m, spacing, K, P[views], det_h, det_w, n_samples, mode,
-                                        g[views, c], n_threads)
-    return out
+    """dL/dP (V, 3, 4) for L = sum(grad_out * render(...)) in any mode
+    (Beer-Lambert, line integral, alpha compositing) and either clip: forward-mode
+    differentiation of ``render`` per pose entry (``oracle_render_pose_gradient``),
+    each view's channels summed."""
+    lib = _load()
+    vol, Pd, xp, yp, nk = _render_args(volume, poses, transfer)
+    B, C, nz, ny, nx = vol.shape
+    V = Pd.shape[0]
+    g = np.ascontiguousarray(grad_out, dtype=np.float64).reshape(V, C, det_h, det_w)
+    out = np.zeros((V, 12), dtype=np.float64)
+    rc = lib.oracle_render_pose_gradient(_ptr(vol), B, C, nz, ny, nx, _ptr(_f64(spacing)),
+                                         _ptr(_f64(K)), _ptr(Pd), V, det_h, det_w, n_samples,
+                                         mode, float(density_factor), clip, float(margin),
+                                         None if xp is None else _ptr(xp),
+                                         None if yp is None else _ptr(yp), nk, _ptr(g),
+                                         _ptr(out), _threads(n_threads))
+    if rc != 0:
+        raise ValueError("oracle_render_pose_gradient: invalid arguments or out of memory")
+    return out.reshape(V, 3, 4)

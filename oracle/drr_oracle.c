@@ -1267,6 +1267,225 @@ int oracle_render_adjoint(const float *vol, int B, int C, int nz, int ny, int nx
     return failed ? -1 : T;
 }
 
+/* Value and q-gradient of the render field (clamp to edge, or zero padding in
+ * the near/far mode) at q: the corner values are those render_corners reads
+ * (0 for a corner outside the volume with zero padding), the value is their
+ * trilinear blend and each gradient component the derivative of the corner
+ * weights along that axis times the corner values. */
+static double render_value_grad(const render_params_t *P, const double *mu, const double q[3],
+                                double gq[3])
+{
+    long lo[3];
+    double f[3];
+    for (int a = 0; a < 3; ++a) {
+        double fl = floor(q[a]);
+        f[a] = q[a] - fl;
+        lo[a] = (long)fl;
+    }
+    double val = 0.0;
+    gq[0] = gq[1] = gq[2] = 0.0;
+    for (int c = 0; c < 8; ++c) {
+        long idx[3];
+        int outside = 0;
+        double w = 1.0;
+        for (int a = 0; a < 3; ++a) {
+            int up = (c >> a) & 1;
+            long i = lo[a] + up;
+            if (i < 0 || i > P->n[a] - 1) outside = 1;
+            idx[a] = clamp_index(i, P->n[a]);
+            w *= up ? f[a] : 1.0 - f[a];
+        }
+        double v = (P->zero_pad && outside) ? 0.0 : mu[(idx[2] * P->n[1] + idx[1]) * P->n[0] + idx[0]];
+        val += w * v;
+        for (int a = 0; a < 3; ++a) {
+            double dw = ((c >> a) & 1) ? 1.0 : -1.0;
+            for (int b = 0; b < 3; ++b) {
+                if (b == a) continue;
+                dw *= ((c >> b) & 1) ? f[b] : 1.0 - f[b];
+            }
+            gq[a] += dw * v;
+        }
+    }
+    return val;
+}
+
+/* Pose gradient of oracle_render in every mode and both clips: for
+ * L = sum_p g_p out_p, grad_pose[12 v + e] receives dL/dP_v[e] for view v's
+ * 3x4 row-major [R | t], summed over its channels (flashdrr API,
+ * VolumeRaycaster class text: rendering is differentiable with respect to the
+ * view matrices, in either integration mode of __init__).
+ *
+ * Plain forward-mode differentiation of oracle_render, one pose entry theta at
+ * a time, as oracle_pose_gradient does for the plain forward: the tangents of
+ * the camera centre dC = -dR^T t - R^T dt and of the unit direction
+ * dd = (dw - d (d . dw)) / |w| (w = R^T K^-1 m); of the range ends -- with the
+ * box clip the bounding planes move them, dt = -(dC_a + t dd_a) / d_a for the
+ * entry (exit) axis a (the start stays 0 at the source); in the near/far mode
+ * near = |e| - margin with e the offset of C from the box's closest point and
+ * far = |(|C_a| + E_a/2)_a| + margin move with C alone, d near = e . dC / |e|
+ * (0 while near is held at 0), d far = sum_a (|C_a| + E_a/2) sign(C_a) dC_a /
+ * (far - margin) --; of dz and of each sample position
+ * dp_k = dC + dt_k d + t_k dd, and of each sample value
+ * dv_k = grad v(q_k) . dp_k / s.  Then through the output:
+ *   Beer-Lambert and line integral: tau = f dz sum v_k,
+ *     dtau = f (ddz sum v_k + dz sum dv_k), dout = exp(-tau) dtau or dtau;
+ *   compositing, a_k = f v_k dz: da_k = f (dv_k dz + v_k ddz),
+ *     alpha_k = 1 - exp(-a_k), dalpha_k = exp(-a_k) da_k,
+ *     T_k = exp(-sum_{j<k} a_j), dT_k = -T_k sum_{j<k} da_j,
+ *     dI = sum_k (dT_k alpha_k v_k + T_k dalpha_k v_k + T_k alpha_k dv_k),
+ *   with T carried as the running product of the forward.
+ * Rays that render nothing contribute nothing.  Returns 0, or -1 on invalid
+ * arguments or no memory. */
+int oracle_render_pose_gradient(const float *vol, int B, int C, int nz, int ny, int nx,
+                                const double *spacing, const double *K, const double *poses,
+                                int n_views, int H, int W, int n_samples, int mode, double f,
+                                int clip, double margin, const double *tf_xp,
+                                const double *tf_yp, int tf_knots, const double *g,
+                                double *grad_pose, int n_threads)
+{
+    if (render_check(B, C, nz, ny, nx, spacing, n_views, H, W, n_samples, mode, f, clip, margin,
+                     tf_xp, tf_yp, tf_knots))
+        return -1;
+    render_params_t P;
+    render_init(&P, nz, ny, nx, spacing, n_samples, mode, f, clip, margin);
+    long n_vox = (long)nx * ny * nz;
+    double *mu = render_mu(vol, (long)B * C, C, n_vox, tf_xp, tf_yp, tf_knots, NULL);
+    if (!mu) return -1;
+    memset(grad_pose, 0, sizeof(double) * 12 * (size_t)n_views);
+    int views_per_vol = n_views / B;
+    set_threads(n_threads);
+    for (int v = 0; v < n_views; ++v) {
+        const double *pose = poses + 12L * v;
+        double acc[12] = {0};
+#pragma omp parallel
+        {
+            double mine[12] = {0};
+#pragma omp for schedule(dynamic, 16)
+            for (long id = 0; id < (long)C * H * W; ++id) {
+                int ch = (int)(id / ((long)H * W));
+                int r = (int)((id / W) % H);
+                int c = (int)(id % W);
+                double gp = g[(long)v * C * H * W + id];
+                if (gp == 0.0) continue;
+                const double *m = mu + ((long)(v / views_per_vol) * C + ch) * n_vox;
+                oracle_ray_t ray;
+                make_ray(K, pose, P.E, r, c, &ray);
+                double t0, t1;
+                if (!render_range(&P, &ray, &t0, &t1)) continue;
+                /* unnormalised direction w = R^T K^-1 m and its length */
+                double mp[3] = { c + 0.5, r + 0.5, 1.0 }, u[3], w[3];
+                solve3(K, mp, u);
+                for (int a = 0; a < 3; ++a)
+                    w[a] = pose[0 * 4 + a] * u[0] + pose[1 * 4 + a] * u[1] + pose[2 * 4 + a] * u[2];
+                double len = sqrt(w[0] * w[0] + w[1] * w[1] + w[2] * w[2]);
+                /* box clip: the planes that bound the range */
+                int a_in = -1, a_out = -1;
+                if (clip == ORACLE_CLIP_BOX) {
+                    double t_entry = -INFINITY, t_exit = INFINITY;
+                    for (int a = 0; a < 3; ++a) {
+                        if (ray.d[a] == 0.0) continue;
+                        double ta = (-0.5 * P.E[a] - ray.C[a]) / ray.d[a];
+                        double tb = (0.5 * P.E[a] - ray.C[a]) / ray.d[a];
+                        double tmin = ta < tb ? ta : tb, tmax = ta < tb ? tb : ta;
+                        if (tmin > t_entry) { t_entry = tmin; a_in = a; }
+                        if (tmax < t_exit) { t_exit = tmax; a_out = a; }
+                    }
+                    if (!(t_entry > 0.0)) a_in = -1;
+                }
+                /* near/far: gradients of near and far with respect to C */
+                double gnear[3] = {0.0, 0.0, 0.0}, gfar[3] = {0.0, 0.0, 0.0};
+                if (clip == ORACLE_CLIP_NEAR_FAR) {
+                    double e[3], ne = 0.0, fa2 = 0.0;
+                    for (int a = 0; a < 3; ++a) {
+                        double h = 0.5 * P.E[a];
+                        e[a] = ray.C[a] < -h ? ray.C[a] + h : (ray.C[a] > h ? ray.C[a] - h : 0.0);
+                        ne += e[a] * e[a];
+                        fa2 += (fabs(ray.C[a]) + h) * (fabs(ray.C[a]) + h);
+                    }
+                    ne = sqrt(ne);
+                    double fa = sqrt(fa2);
+                    for (int a = 0; a < 3; ++a) {
+                        double h = 0.5 * P.E[a];
+                        if (ne - margin > 0.0) gnear[a] = e[a] / ne;
+                        double sg = ray.C[a] > 0.0 ? 1.0 : (ray.C[a] < 0.0 ? -1.0 : 0.0);
+                        gfar[a] = (fabs(ray.C[a]) + h) * sg / fa;
+                    }
+                }
+                double dz = (t1 - t0) / (double)n_samples;
+                double dC[12][3], dd[12][3], dt0[12], ddz[12];
+                for (int j = 0; j < 12; ++j) {
+                    double dR[9] = {0}, dtv[3] = {0}, dw[3];
+                    if (j < 9) dR[j] = 1.0; else dtv[j - 9] = 1.0;
+                    for (int a = 0; a < 3; ++a) {
+                        dC[j][a] = -(dR[0 * 3 + a] * pose[0 * 4 + 3] + dR[1 * 3 + a] * pose[1 * 4 + 3] +
+                                     dR[2 * 3 + a] * pose[2 * 4 + 3])
+                                   - (pose[0 * 4 + a] * dtv[0] + pose[1 * 4 + a] * dtv[1] +
+                                      pose[2 * 4 + a] * dtv[2]);
+                        dw[a] = dR[0 * 3 + a] * u[0] + dR[1 * 3 + a] * u[1] + dR[2 * 3 + a] * u[2];
+                    }
+                    double ddw = ray.d[0] * dw[0] + ray.d[1] * dw[1] + ray.d[2] * dw[2];
+                    for (int a = 0; a < 3; ++a) dd[j][a] = (dw[a] - ray.d[a] * ddw) / len;
+                    double dt1;
+                    if (clip == ORACLE_CLIP_BOX) {
+                        dt0[j] = a_in >= 0 ? -(dC[j][a_in] + t0 * dd[j][a_in]) / ray.d[a_in] : 0.0;
+                        dt1 = -(dC[j][a_out] + t1 * dd[j][a_out]) / ray.d[a_out];
+                    } else {
+                        dt0[j] = gnear[0] * dC[j][0] + gnear[1] * dC[j][1] + gnear[2] * dC[j][2];
+                        dt1 = gfar[0] * dC[j][0] + gfar[1] * dC[j][1] + gfar[2] * dC[j][2];
+                    }
+                    ddz[j] = (dt1 - dt0[j]) / (double)n_samples;
+                }
+                /* march: value and tangents of each sample, then the output */
+                double sum_v = 0.0, sum_dv[12] = {0};
+                double T = 1.0, dT[12] = {0}, dI[12] = {0};
+                for (int k = 0; k < n_samples; ++k) {
+                    double tk = t0 + ((double)k + 0.5) * dz, q[3], gq[3], dv[12];
+                    for (int a = 0; a < 3; ++a)
+                        q[a] = (ray.C[a] + tk * ray.d[a] + 0.5 * P.E[a]) / P.s[a] - 0.5;
+                    double val = render_value_grad(&P, m, q, gq);
+                    for (int j = 0; j < 12; ++j) {
+                        double dtk = dt0[j] + ((double)k + 0.5) * ddz[j];
+                        dv[j] = 0.0;
+                        for (int a = 0; a < 3; ++a) {
+                            double dp = dC[j][a] + dtk * ray.d[a] + tk * dd[j][a];
+                            dv[j] += gq[a] * dp / P.s[a];
+                        }
+                    }
+                    if (mode != ORACLE_ALPHA_COMPOSITE) {
+                        sum_v += val;
+                        for (int j = 0; j < 12; ++j) sum_dv[j] += dv[j];
+                        continue;
+                    }
+                    double a_k = f * val * dz, keep = exp(-a_k);
+                    double alpha = -expm1(-a_k);
+                    for (int j = 0; j < 12; ++j) {
+                        double da = f * (dv[j] * dz + val * ddz[j]);
+                        double dalpha = keep * da;
+                        dI[j] += dT[j] * alpha * val + T * dalpha * val + T * alpha * dv[j];
+                        dT[j] = dT[j] * keep - T * keep * da;
+                    }
+                    T *= keep;
+                }
+                if (mode != ORACLE_ALPHA_COMPOSITE) {
+                    double tau = f * dz * sum_v;
+                    double dout = mode == ORACLE_BEER_LAMBERT ? exp(-tau) : 1.0;
+                    for (int j = 0; j < 12; ++j)
+                        dI[j] = dout * f * (ddz[j] * sum_v + dz * sum_dv[j]);
+                }
+                for (int j = 0; j < 12; ++j) mine[j] += gp * dI[j];
+            }
+#pragma omp critical
+            for (int j = 0; j < 12; ++j) acc[j] += mine[j];
+        }
+        for (int rr = 0; rr < 3; ++rr) {
+            for (int cc = 0; cc < 3; ++cc) grad_pose[12L * v + rr * 4 + cc] = acc[rr * 3 + cc];
+            grad_pose[12L * v + rr * 4 + 3] = acc[9 + rr];
+        }
+    }
+    free(mu);
+    return 0;
+}
+
 /* Near / far range of the near/far mode for one view, for pins: out = (near,
  * far).  extent = (Ex, Ey, Ez). */
 void oracle_view_range(const double *extent, const double *pose, double margin, double *out)

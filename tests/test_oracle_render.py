@@ -361,20 +361,24 @@ def test_invalid_arguments_are_rejected():
         oracle.render(vol, spacing, K, poses, H, Wd, N, 7)
 
 
-@pytest.mark.parametrize("mode", [BL, RAW])
+@pytest.mark.parametrize("mode", [BL, RAW, ALPHA])
+@pytest.mark.parametrize("clip", [BOX, NEAR_FAR])
 @pytest.mark.parametrize("tf", [False, True])
-def test_render_pose_gradient_matches_central_differences(mode, tf):
+def test_render_pose_gradient_matches_central_differences(mode, clip, tf):
     """The batched pose gradient (per view, summed over its channels, density
     factor and transfer function included) equals central differences of
-    oracle.render with respect to each pose entry (fp64 poses pass through)."""
-    rng, vol, spacing, K, poses, H, Wd, N = _problem(70 + mode + 2 * tf)
+    oracle.render with respect to each pose entry (fp64 poses pass through), in
+    every mode and both clips."""
+    rng, vol, spacing, K, poses, H, Wd, N = _problem(70 + mode + 3 * clip + 6 * tf)
     xp = np.array([[0.0, 0.4, 1.1], [0.1, 0.5, 0.9]], dtype=np.float32)
     yp = np.array([[0.0, 0.5, 0.6], [0.2, 0.0, 0.7]], dtype=np.float32)
     transfer = (xp, yp) if tf else None
-    f = 0.8
+    f = 0.8 if mode != ALPHA else 1.7
+    margin = 2.5
     g = rng.normal(size=(poses.shape[0], vol.shape[1], H, Wd))
     gp = oracle.render_pose_gradient(vol, spacing, K, poses, H, Wd, N, mode, g,
-                                     density_factor=f, transfer=transfer)
+                                     density_factor=f, transfer=transfer, clip=clip,
+                                     margin=margin)
     P = np.asarray(poses, dtype=np.float32).astype(np.float64)
     h = 1e-6
     for v in (0, 3):
@@ -383,9 +387,92 @@ def test_render_pose_gradient_matches_central_differences(mode, tf):
             Pp[v].reshape(-1)[e] += h
             Pm[v].reshape(-1)[e] -= h
             lp = float((oracle.render(vol, spacing, K, Pp, H, Wd, N, mode, density_factor=f,
-                                      transfer=transfer)[0] * g).sum())
+                                      clip=clip, margin=margin, transfer=transfer)[0] * g).sum())
             lm = float((oracle.render(vol, spacing, K, Pm, H, Wd, N, mode, density_factor=f,
-                                      transfer=transfer)[0] * g).sum())
+                                      clip=clip, margin=margin, transfer=transfer)[0] * g).sum())
             fd = (lp - lm) / (2 * h)
             assert fd == pytest.approx(gp[v].reshape(-1)[e], rel=1e-4,
                                        abs=1e-5 * np.abs(gp[v]).max())
+    assert np.abs(gp[[0, 3]]).max() > 1e-3
+
+
+def _transfer_numpy(x, xp, yp):
+    """The per-channel piecewise-linear map written out in numpy: linear between
+    knots, the first and last segments extended beyond them."""
+    x = np.asarray(x, dtype=np.float64)
+    xp = np.asarray(xp, dtype=np.float64)
+    yp = np.asarray(yp, dtype=np.float64)
+    seg = np.clip(np.searchsorted(xp, x, side="right") - 1, 0, len(xp) - 2)
+    m = (yp[seg + 1] - yp[seg]) / (xp[seg + 1] - xp[seg])
+    return yp[seg] + m * (x - xp[seg])
+
+
+@pytest.mark.parametrize("mode", [BL, RAW])
+def test_render_pose_gradient_is_the_plain_pose_gradient_per_channel(mode):
+    """Beer-Lambert and the line integral with the box clip: render(x) with
+    factor f and map tf is the plain forward of f * tf(x), so the render pose
+    gradient equals oracle.pose_gradient (a separately pinned routine, a
+    different code path) on each channel-volume f * tf(x) (rounded to fp32 for
+    its interface), summed over a view's channels."""
+    rng, vol, spacing, K, poses, H, Wd, N = _problem(90 + mode)
+    xp = np.array([[0.0, 0.4, 1.1], [0.1, 0.5, 0.9]], dtype=np.float32)
+    yp = np.array([[0.0, 0.5, 0.6], [0.2, 0.0, 0.7]], dtype=np.float32)
+    f = 0.8
+    B, C = vol.shape[:2]
+    P = np.asarray(poses, dtype=np.float64).reshape(-1, 3, 4)
+    V = P.shape[0]
+    vpv = V // B
+    g = rng.normal(size=(V, C, H, Wd))
+    gp = oracle.render_pose_gradient(vol, spacing, K, poses, H, Wd, N, mode, g,
+                                     density_factor=f, transfer=(xp, yp))
+    ref = np.zeros((V, 3, 4))
+    for b in range(B):
+        for c in range(C):
+            m = (f * _transfer_numpy(vol[b, c], xp[c], yp[c])).astype(np.float32)
+            views = slice(b * vpv, (b + 1) * vpv)
+            ref[views] += oracle.pose_gradient(m, spacing, K, P[views], H, Wd, N, mode,
+                                               g[views, c])
+    assert np.abs(gp - ref).max() <= 1e-6 * np.abs(ref).max()
+
+
+def test_compositing_pose_gradient_of_constant_box_is_the_chord_derivative():
+    """For a constant mu_c volume and the box clip, every sample reads mu_c and
+    the over operator sums a geometric series: I = mu_c (1 - exp(-f mu_c L))
+    with L the chord.  So dL/dP of sum g I is g f mu_c^2 exp(-f mu_c L) dL/dP,
+    the chord from face intersections and its derivative by central
+    differences of that chord (no voxels, no compositing loop)."""
+    mu_c = float(np.float32(0.07))
+    f = 1.3
+    shape = (8, 10, 12)
+    vol = np.full(shape, mu_c, dtype=np.float32)
+    spacing = np.ones(3, dtype=np.float32)
+    E = np.array([12.0, 10.0, 8.0])
+    K = W.intrinsics(12.0, 2.5, 2.5)
+    poses = W.random_poses(1, 30.0, 35.0, 1.0, seed=52).astype(np.float64)
+    g = np.random.default_rng(53).normal(size=(1, 1, 5, 5))
+    grad = oracle.render_pose_gradient(vol, spacing, K, poses, 5, 5, 17, ALPHA, g,
+                                       density_factor=f)
+
+    def chords(P):
+        Rm, t = P[:, :3], P[:, 3]
+        C = -Rm.T @ t
+        out = np.zeros((5, 5))
+        for r in range(5):
+            for c in range(5):
+                u = np.linalg.solve(K.astype(np.float64), [c + 0.5, r + 0.5, 1.0])
+                d = Rm.T @ u
+                out[r, c] = chord_by_faces(C, d / np.linalg.norm(d), E)
+        return out
+
+    L0 = chords(poses[0])
+    ref = np.zeros((3, 4))
+    h = 1e-6
+    for r in range(3):
+        for c in range(4):
+            up, dn = poses[0].copy(), poses[0].copy()
+            up[r, c] += h
+            dn[r, c] -= h
+            dL = (chords(up) - chords(dn)) / (2 * h)
+            ref[r, c] = float((g[0, 0] * f * mu_c ** 2 * np.exp(-f * mu_c * L0) * dL).sum())
+    assert (L0 > 0).sum() > 10
+    assert np.abs(grad[0] - ref).max() <= 1e-6 * np.abs(ref).max()
