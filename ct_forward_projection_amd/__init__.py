@@ -559,8 +559,8 @@ def drr_render_backward_pose(volume: torch.Tensor, spacing, K, poses: torch.Tens
                              grad_poses: Optional[torch.Tensor] = None,
                              workspace: Optional[torch.Tensor] = None,
                              stream=None) -> torch.Tensor:
-    """dL/dP (V, 3, 4) for L = sum(grad_out * image) of ``drr_render``
-    (Beer-Lambert or line integral, box clip), summed over each view's channels."""
+    """dL/dP (V, 3, 4) for L = sum(grad_out * image) of ``drr_render`` (every
+    mode, either clip), summed over each view's channels."""
     volume = _device_tensor(volume, "volume")
     dtype = _volume_dtype(volume)
     poses = _device_tensor(poses, "poses", torch.float32)
@@ -619,7 +619,7 @@ def raycast(volume: torch.Tensor, spacing, K, poses: torch.Tensor, det_h: int, d
     """Differentiable flashdrr-style render: ``volume`` (B, C, nz, ny, nx) and
     ``poses`` (V, 3, 4) with V a multiple of B -- or one pose, used for every
     volume -- give images (V, C, det_h, det_w); gradients flow to the volume
-    and (Beer-Lambert or line integral with the box clip) to the poses."""
+    and to the poses."""
     if volume.dim() == 5 and poses.shape[0] == 1 and volume.shape[0] > 1:
         poses = poses.expand(volume.shape[0], 3, 4).contiguous()
     return _Raycast.apply(volume, spacing, K, poses, det_h, det_w, n_samples, mode,

@@ -614,13 +614,10 @@ int drr_render_backward_volume(const void* volume, int dtype, int n_volumes, int
 namespace {
 
 // The pose backward of a validated render call `a` (single-volume calls come
-// here too): Beer-Lambert or line integral, box clip.
+// here too): every mode, either clip.
 int pose_backward(drr::LaunchArgs& a, const void* volume, int dtype, const float* grad_out,
                   float* grad_poses, void* workspace, size_t workspace_bytes, void* stream)
 {
-    if (a.mode == DRR_ALPHA_COMPOSITE || a.clip != DRR_CLIP_BOX)
-        return fail(DRR_ERR_UNSUPPORTED,
-                    "pose gradients cover Beer-Lambert and line integral with the box clip");
     if (!volume) return fail(DRR_ERR_INVALID_ARGUMENT, "volume is NULL");
     const long long n_out = (long long)a.n_views * a.C * a.H * a.W;
     if (n_out > 0 && !grad_out) return fail(DRR_ERR_INVALID_ARGUMENT, "grad_out is NULL");
@@ -628,7 +625,7 @@ int pose_backward(drr::LaunchArgs& a, const void* volume, int dtype, const float
     const int eb = dtype == DRR_F32 ? 4 : 2;
     const drr::RenderPlan plan =
         drr::plan_render(a.n_volumes, a.C, a.V.n[2], a.V.n[1], a.V.n[0], eb, a.n_views, a.H, a.W,
-                         a.N, drr::kClipBox, a.has_tf, true);
+                         a.N, a.clip, a.has_tf, true);
     if (!plan.fits)
         return fail(DRR_ERR_UNSUPPORTED, "one channel-volume of the march's copy exceeds 4 GiB");
     const size_t acc_bytes = drr::pose_acc_bytes(a.n_views);

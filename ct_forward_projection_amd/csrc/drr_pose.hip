@@ -23,10 +23,23 @@
 // -t_i e_j, dw/dR_ij = u_i e_j, dC/dt_i = -R_i. (row i), so with y = g dI/ds
 // summed over a view's rays, P = sum y Ac and Q_ij = sum y u_i Bw_j:
 //   dL/dR_ij = -t_i P_j + Q_ij,   dL/dt_i = -sum_a R_ia P_a.
+// In general dI = sum_k c_k dv_k + D ddz with c_k = dI/dv_k and D = dI/ddz at
+// fixed values, and the same collapse holds with G0 = sum_k c_k grad v_k,
+// G1 = sum_k c_k b_k grad v_k and beta0 = (G0 - G1) . d - D / N,
+// beta1 = G1 . d + D / N (A = G0, Bv = t0 G0 + (t1 - t0) G1).  Beer-Lambert
+// and the line integral have c_k = dz and D = S0 (times f exp(-f s) or f);
+// compositing (flashdrr API, VolumeRaycaster.__init__: use_beer_lambert =
+// False) has the over operator's per-sample coefficient and
+// D = f sum_k T_k v_k ((1 - alpha_k) v_k - alpha_k P_k), P_k = sum_{j<k} v_j.
+// In the near/far mode (flashdrr compute_clipping_distances) the range ends
+// are the view's near and far, functions of C alone: dt0 = n0 . dC and
+// dt1 = n1 . dC with n0, n1 their gradients, so A gains beta0 n0 + beta1 n1
+// and no plane terms enter.
 // The march steps 32.32 fixed-point positions (re-anchored on fp64 every eight
 // samples, every four in the LDS-staged march), interpolates in fp32 and
 // accumulates S0, G0 and sum_k k grad mu_k per ray in fp64 (from fp32 sums of
-// each group); the chain rule runs in fp64 and the view sums in fp64 atomics.
+// each group; compositing's sums per sample); the chain rule runs in fp64 and
+// the view sums in fp64 atomics.
 #include <limits.h>
 
 #include "drr_device.hpp"
@@ -42,8 +55,9 @@ struct RayFrame {
     double C[3], d[3], u[3];
     double q0[3], dq[3];     // continuous index of sample 0 and the step, fp64, times 2^32
     double len, t0, t1;
-    int a_in;      // entry plane axis, -1 when the range starts at the source
-    int a_out;     // exit plane axis
+    int a_in;      // entry plane axis, -1 when the range starts at the source (or near/far)
+    int a_out;     // exit plane axis (-1 in the near/far mode)
+    double gn[3], gf[3];     // near/far mode: gradients of t0 and t1 with respect to C, else 0
 };
 
 __device__ inline bool ray_frame(const ViewGeom& G, const double Ki[9], const VolumeDesc& V,
@@ -82,6 +96,8 @@ __device__ inline bool ray_frame(const ViewGeom& G, const double Ki[9], const Vo
     if (!(t_entry > 0.0)) a_in = -1;
     F.a_in = a_in;
     F.a_out = a_out;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) F.gn[a] = F.gf[a] = 0.0;
     const double dz = (F.t1 - F.t0) / (double)N;
     const double ts = F.t0 + 0.5 * dz;
 #pragma unroll
@@ -90,6 +106,88 @@ __device__ inline bool ray_frame(const ViewGeom& G, const double Ki[9], const Vo
         F.dq[a] = (dz * F.d[a] * V.inv_s[a]) * 4294967296.0;
     }
     return true;
+}
+
+// Near/far mode: the ray of pixel (r, c) over the view's [near, far] (the
+// forward's view_near_far), no plane axes, and the gradients of near and far
+// with respect to the camera centre C: near = |e| - margin with e the offset
+// of C from the box's closest point (gradient e / |e|, 0 while near is held at
+// 0), far = |(|C_a| + E_a / 2)_a| + margin (gradient (|C_a| + E_a / 2)
+// sign(C_a) / (far - margin)).  Returns false when the range is empty.
+__device__ inline bool ray_frame_range(const ViewGeom& G, const double Ki[9], const VolumeDesc& V,
+                                       float margin, int r, int c, int N, RayFrame& F)
+{
+    double t_near, t_far;
+    view_near_far(G, V, margin, t_near, t_far);
+    if (!(t_far > t_near)) return false;
+    const double m0 = (double)c + 0.5, m1 = (double)r + 0.5;
+    double w[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        F.u[a] = Ki[a * 3 + 0] * m0 + Ki[a * 3 + 1] * m1 + Ki[a * 3 + 2];
+        w[a] = G.M[a * 3 + 0] * m0 + G.M[a * 3 + 1] * m1 + G.M[a * 3 + 2];
+        F.C[a] = G.C[a];
+    }
+    F.len = sqrt(w[0] * w[0] + w[1] * w[1] + w[2] * w[2]);
+    const double inv_len = 1.0 / F.len;
+    F.t0 = t_near;
+    F.t1 = t_far;
+    F.a_in = F.a_out = -1;
+    double e[3], ne = 0.0, fa = 0.0;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        F.d[a] = w[a] * inv_len;
+        const double h = V.half_e[a], ca = G.C[a];
+        e[a] = ca < -h ? ca + h : (ca > h ? ca - h : 0.0);
+        ne += e[a] * e[a];
+        fa += (fabs(ca) + h) * (fabs(ca) + h);
+    }
+    ne = sqrt(ne);
+    fa = sqrt(fa);
+    const bool near_moves = ne - (double)margin > 0.0;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        const double h = V.half_e[a], ca = G.C[a];
+        F.gn[a] = near_moves ? e[a] / ne : 0.0;
+        F.gf[a] = (fabs(ca) + h) * (ca > 0.0 ? 1.0 : (ca < 0.0 ? -1.0 : 0.0)) / fa;
+    }
+    const double dz = (F.t1 - F.t0) / (double)N;
+    const double ts = F.t0 + 0.5 * dz;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        F.q0[a] = ((G.C[a] + ts * F.d[a]) * V.inv_s[a] + V.q_off[a]) * 4294967296.0;
+        F.dq[a] = (dz * F.d[a] * V.inv_s[a]) * 4294967296.0;
+    }
+    return true;
+}
+
+// Samples [k_lo, k_hi) of a near/far frame whose continuous index lies in
+// [-1, n) on every axis (the zero-padded support, as padded_support for the
+// forward's march), widened by one sample each way; the others read only
+// padding and add exactly 0.
+__device__ inline void frame_support(const RayFrame& F, const VolumeDesc& V, int N, int& k_lo,
+                                     int& k_hi)
+{
+    double lo = 0.0, hi = (double)N;
+    bool none = false;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        const double q0 = F.q0[a] * 2.3283064365386963e-10;
+        const double dq = F.dq[a] * 2.3283064365386963e-10;
+        const double b0 = -1.0, b1 = (double)V.n[a];
+        if (dq == 0.0) {
+            none = none || !(q0 >= b0 && q0 < b1);
+        } else {
+            const double k0 = (b0 - q0) / dq, k1 = (b1 - q0) / dq;
+            lo = fmax(lo, fmin(k0, k1));
+            hi = fmin(hi, fmax(k0, k1));
+        }
+    }
+    lo = fmin(fmax(lo, 0.0), (double)N);
+    hi = fmin(fmax(hi, 0.0), (double)N);
+    k_lo = max((int)floor(lo) - 1, 0);
+    k_hi = min((int)ceil(hi) + 1, N);
+    if (none || k_hi < k_lo) k_hi = k_lo;
 }
 
 // Sample k's position, evaluated in fp64 and rounded once to 32.32 fixed point
@@ -157,36 +255,26 @@ __device__ inline double block_sum12(const double v_in[12], double* red)
 }
 
 // A ray's contribution to its view's sums P (contrib[0..2]) and Q
-// (contrib[3..11]) from its march sums s0 = sum_k mu_k, g0 = sum_k grad mu_k
-// and h1 = sum_k k grad mu_k (per voxel index), chain rule in fp64.
-template <int MODE>
-__device__ inline void pose_chain_rule(const RayFrame& F, const VolumeDesc& V, int N, float g,
-                                       float density, double s0, const double g0[3],
-                                       const double h1[3], double contrib[12])
+// (contrib[3..11]) from y (g times what multiplies the ray's sums), G0 =
+// sum_k c_k grad v_k and G1 = sum_k c_k b_k grad v_k (per mm) and Dn = D / N,
+// chain rule in fp64.
+__device__ inline void pose_contrib(const RayFrame& F, double y, const double G0[3],
+                                    const double G1[3], double Dn, double contrib[12])
 {
-    const double Nd = (double)N, dz = (F.t1 - F.t0) / Nd;
-    const double S0 = s0;
-    double G0[3], G1[3];
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-        G0[a] = g0[a] * V.inv_s[a];                               // per mm
-        G1[a] = (h1[a] + 0.5 * g0[a]) / Nd * V.inv_s[a];
-    }
-    const double s = dz * S0, f = (double)density;
-    const double y = (double)g * f * (MODE == kBeerLambert ? exp(-f * s) : 1.0);
     double G0d = 0.0, G1d = 0.0;
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
         G0d += G0[a] * F.d[a];
         G1d += G1[a] * F.d[a];
     }
-    const double beta0 = -S0 / Nd + dz * (G0d - G1d);
-    const double beta1 = S0 / Nd + dz * G1d;
+    const double beta0 = G0d - G1d - Dn;
+    const double beta1 = G1d + Dn;
     double Ac[3], Bd[3];
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
-        Ac[a] = dz * G0[a];
-        Bd[a] = dz * (F.t0 * G0[a] + (F.t1 - F.t0) * G1[a]);
+        // gn, gf: the near/far range ends' gradients (0 with the box clip)
+        Ac[a] = G0[a] + beta0 * F.gn[a] + beta1 * F.gf[a];
+        Bd[a] = F.t0 * G0[a] + (F.t1 - F.t0) * G1[a];
     }
     // the planes that bound the range (unrolled selects: a run-time index into
     // these small arrays would put them in scratch memory)
@@ -213,6 +301,85 @@ __device__ inline void pose_chain_rule(const RayFrame& F, const VolumeDesc& V, i
         for (int j = 0; j < 3; ++j) contrib[3 + i * 3 + j] = y * F.u[i] * Bw[j];
 }
 
+// Beer-Lambert and line integral: c_k = dz, D = S0, y = g f exp(-f s) or g f,
+// from the march sums s0 = sum_k mu_k, g0 = sum_k grad mu_k and
+// h1 = sum_k k grad mu_k (per voxel index).
+template <int MODE>
+__device__ inline void pose_chain_rule(const RayFrame& F, const VolumeDesc& V, int N, float g,
+                                       float density, double s0, const double g0[3],
+                                       const double h1[3], double contrib[12])
+{
+    const double Nd = (double)N, dz = (F.t1 - F.t0) / Nd;
+    double G0[3], G1[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        G0[a] = dz * g0[a] * V.inv_s[a];                          // per mm
+        G1[a] = dz * (h1[a] + 0.5 * g0[a]) / Nd * V.inv_s[a];
+    }
+    const double s = dz * s0, f = (double)density;
+    const double y = (double)g * f * (MODE == kBeerLambert ? exp(-f * s) : 1.0);
+    pose_contrib(F, y, G0, G1, s0 / Nd, contrib);
+}
+
+// Compositing: running state and sums of one ray, samples added in order.
+// With e_k = T_k (alpha_k + f dz (1 - alpha_k) v_k) and the running emission
+// R_k = sum_{j<=k} T_j alpha_j v_j, sample k's coefficient is
+// c_k = e_k - f dz (I - R_k) = W_k - f dz I with W_k = e_k + f dz R_k, so
+// sum_k c_k X_k = sum_k W_k X_k - f dz I sum_k X_k: one pass gives it once
+// I = R_{N-1} is known, without the forward's image.  T, R, the prefix
+// P_k = sum_{j<k} v_j and every sum are fp64 (the difference above cancels
+// where later samples carry little of I).
+struct AlphaPoseSums {
+    double T, R, P, D;
+    double sw[3], swk[3], sx[3], sxk[3];
+    float fdz;
+
+    __device__ void init(float f_dz)
+    {
+        fdz = f_dz;
+        T = 1.0;
+        R = P = D = 0.0;
+#pragma unroll
+        for (int a = 0; a < 3; ++a) sw[a] = swk[a] = sx[a] = sxk[a] = 0.0;
+    }
+
+    // sample k: value v, gradient x (per voxel index)
+    __device__ void add(int k, float v, const float x[3])
+    {
+        const float alpha = -expm1f(-(fdz * v));
+        const float e = (float)T * (alpha + fdz * (1.0f - alpha) * v);
+        D = fma(T * (double)v, (double)((1.0f - alpha) * v) - (double)alpha * P, D);
+        R = fma(T, (double)(alpha * v), R);
+        T = fma(-T, (double)alpha, T);
+        P += (double)v;
+        const double W = fma((double)fdz, R, (double)e);
+        const double Wk = W * (double)k;
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+            sw[a] = fma(W, (double)x[a], sw[a]);
+            swk[a] = fma(Wk, (double)x[a], swk[a]);
+            sx[a] += (double)x[a];
+            sxk[a] = fma((double)k, (double)x[a], sxk[a]);
+        }
+    }
+};
+
+// Compositing: y = g, D = f sum_k T_k v_k ((1 - alpha_k) v_k - alpha_k P_k).
+__device__ inline void alpha_pose_chain(const RayFrame& F, const VolumeDesc& V, int N, float g,
+                                        float density, const AlphaPoseSums& S,
+                                        double contrib[12])
+{
+    const double Nd = (double)N, fdz = (double)S.fdz, I = S.R;
+    double G0[3], G1[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        G0[a] = (S.sw[a] - fdz * I * S.sx[a]) * V.inv_s[a];
+        G1[a] = ((S.swk[a] + 0.5 * S.sw[a]) - fdz * I * (S.sxk[a] + 0.5 * S.sx[a])) / Nd *
+                V.inv_s[a];
+    }
+    pose_contrib(F, (double)g, G0, G1, (double)density * S.D / Nd, contrib);
+}
+
 // One group of samples' value and gradient terms, summed in fp32 (at most four
 // terms), added to the ray's fp64 sums; the group starts at sample k.
 __device__ inline void pose_add_group(int k, float ps, const float pg[3], const float ph[3],
@@ -228,14 +395,20 @@ __device__ inline void pose_add_group(int k, float ps, const float pg[3], const 
 
 // The tiles of a launch run over (view, channel) pairs (a tile lies in one
 // pair); every channel of a view adds to that view's sums, and the density
-// factor enters dI/ds (f exp(-f s) or f).  `src` holds one channel-volume of
-// `src_bytes` every b.src_stride bytes.
-template <typename T, Layout L, int MODE>
+// factor enters dI/ds (f exp(-f s) or f; the coefficients when compositing).
+// `src` holds one channel-volume of `src_bytes` every b.src_stride bytes: the
+// read plan's layout L, zero-padded (Cell or ZPair) in the near/far mode
+// (CLIP = kClipNearFar), whose rays march only the samples of the padded
+// support.
+template <typename T, Layout L, int MODE, int CLIP>
 __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
     const T* __restrict__ src, uint32_t src_bytes, VolumeDesc V, Intrinsics K,
     const float* __restrict__ poses, int H, int W, int N, int tiles_x, int tiles_per_view,
     Batch b, const float* __restrict__ grad_out, double* __restrict__ acc)
 {
+    constexpr bool ZP = CLIP == kClipNearFar;
+    static_assert(!ZP || L == Layout::Cell || L == Layout::ZPair,
+                  "the near/far mode reads zero-padded cells or z-pairs");
     __shared__ double red[(kBlock / 64) * 12];
     const int tile = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
     const PixelCoord px = tile_pixel(tile, tiles_x, tiles_per_view);
@@ -254,16 +427,21 @@ __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
         view_setup(poses + 12 * view, K, G);
         double Ki[9];
         intrinsics_inverse(K, Ki);
-        hit = ray_frame(G, Ki, V, px.r, px.c, N, F);
+        hit = ZP ? ray_frame_range(G, Ki, V, b.margin, px.r, px.c, N, F)
+                 : ray_frame(G, Ki, V, px.r, px.c, N, F);
     }
     if (hit) {
         const char* base = reinterpret_cast<const char*>(src) + (uint64_t)cvol * b.src_stride;
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)src_bytes, kBufferWord3);
+        int k_lo = 0, k_hi = N;
+        if constexpr (ZP) frame_support(F, V, N, k_lo, k_hi);
         // fp64 ray sums: sum grad mu . d telescopes to about mu(exit) - mu(entry),
         // a small difference of large edge terms that fp32 sums over a whole ray
         // would round away (a group of eight fp32 terms is summed first)
         double s0 = 0.0, g0[3] = {0.0, 0.0, 0.0}, h1[3] = {0.0, 0.0, 0.0};
+        AlphaPoseSums asum;
+        if constexpr (MODE == kAlpha) asum.init(b.f * (float)((F.t1 - F.t0) / (double)N));
         // sample positions in 32.32 fixed point.  The gradient of trilinear mu
         // jumps where a sample crosses a cell face, so positions must not
         // drift from their fp64 values: each group of eight starts from its
@@ -273,42 +451,60 @@ __global__ __launch_bounds__(kBlock) void drr_pose_grad_kernel(
         // views of 200^2 from the z-pair copy)
         const int64_t dqx = step_fixed(F, 0), dqy = step_fixed(F, 1), dqz = step_fixed(F, 2);
         constexpr int kGroup = 8;
-        int k = 0;
-        for (; k + kGroup <= N; k += kGroup) {
+        int k = k_lo;
+        for (; k + kGroup <= k_hi; k += kGroup) {
             SampleAddr A[kGroup];
             CornerVals c[kGroup];
             int64_t qx = sample_fixed(F, 0, k), qy = sample_fixed(F, 1, k), qz = sample_fixed(F, 2, k);
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) {
-                A[i] = sample_addr<T, L>(V, qx, qy, qz);
+                A[i] = sample_addr<T, L, ZP>(V, qx, qy, qz);
                 qx += dqx; qy += dqy; qz += dqz;
                 serial_step(qx, qy, qz);
             }
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) gather<T, L>(rs, A[i], c[i]);
             __builtin_amdgcn_sched_barrier(0);
-            // the group's sums in fp32 (four terms), then into the ray's fp64 sums
             float v[kGroup], gq[kGroup][3];
 #pragma unroll
-            for (int i = 0; i < kGroup; ++i) v[i] = interpolate_grad(A[i], c[i], gq[i]);
-            float ps, pg[3], ph[3];
-            group_sums<kGroup>(v, gq, ps, pg, ph);
-            pose_add_group(k, ps, pg, ph, s0, g0, h1);
+            for (int i = 0; i < kGroup; ++i) {
+                v[i] = interpolate_grad(A[i], c[i], gq[i]);
+                if constexpr (ZP) v[i] = interpolate_exact(A[i], c[i]);
+            }
+            if constexpr (MODE == kAlpha) {
+#pragma unroll
+                for (int i = 0; i < kGroup; ++i) asum.add(k + i, v[i], gq[i]);
+            } else {
+                // the group's sums in fp32 (four terms), then into the ray's fp64 sums
+                float ps, pg[3], ph[3];
+                group_sums<kGroup>(v, gq, ps, pg, ph);
+                pose_add_group(k, ps, pg, ph, s0, g0, h1);
+            }
         }
-        for (; k < N; ++k) {
-            const SampleAddr A = sample_addr<T, L>(V, sample_fixed(F, 0, k), sample_fixed(F, 1, k),
-                                                   sample_fixed(F, 2, k));
+        for (; k < k_hi; ++k) {
+            const SampleAddr A = sample_addr<T, L, ZP>(V, sample_fixed(F, 0, k),
+                                                       sample_fixed(F, 1, k),
+                                                       sample_fixed(F, 2, k));
             CornerVals c;
             gather<T, L>(rs, A, c);
             float gq[3];
-            s0 += (double)interpolate_grad(A, c, gq);
+            float v = interpolate_grad(A, c, gq);
+            if constexpr (ZP) v = interpolate_exact(A, c);
+            if constexpr (MODE == kAlpha) {
+                asum.add(k, v, gq);
+            } else {
+                s0 += (double)v;
 #pragma unroll
-            for (int a = 0; a < 3; ++a) {
-                g0[a] += (double)gq[a];
-                h1[a] = fma((double)k, (double)gq[a], h1[a]);
+                for (int a = 0; a < 3; ++a) {
+                    g0[a] += (double)gq[a];
+                    h1[a] = fma((double)k, (double)gq[a], h1[a]);
+                }
             }
         }
-        pose_chain_rule<MODE>(F, V, N, g, b.f, s0, g0, h1, contrib);
+        if constexpr (MODE == kAlpha)
+            alpha_pose_chain(F, V, N, g, b.f, asum, contrib);
+        else
+            pose_chain_rule<MODE>(F, V, N, g, b.f, s0, g0, h1, contrib);
     }
     const double t = block_sum12(contrib, red);
     if (threadIdx.x < 12 && t != 0.0) unsafeAtomicAdd(acc + 12 * view + threadIdx.x, t);
@@ -359,6 +555,10 @@ __global__ __launch_bounds__(kBlock) void drr_pose_staged_kernel(
         for (int a = 0; a < 3; ++a) dq[a] = step_fixed(F, a);
     }
     double s0 = 0.0, g0[3] = {0.0, 0.0, 0.0}, h1[3] = {0.0, 0.0, 0.0};
+    AlphaPoseSums asum;
+    if constexpr (MODE == kAlpha) {
+        if (hit) asum.init(b.f * (float)((F.t1 - F.t0) / (double)N));
+    }
     constexpr int64_t kSlack = 4;          // fixed-point units, see above
     constexpr int kGroup = 4;
 
@@ -414,9 +614,14 @@ __global__ __launch_bounds__(kBlock) void drr_pose_staged_kernel(
                     float v[kGroup], gq[kGroup][3];
 #pragma unroll
                     for (int i = 0; i < kGroup; ++i) v[i] = interpolate_grad(A[i], c[i], gq[i]);
-                    float ps, pg[3], ph[3];
-                    group_sums<kGroup>(v, gq, ps, pg, ph);
-                    pose_add_group(k, ps, pg, ph, s0, g0, h1);
+                    if constexpr (MODE == kAlpha) {
+#pragma unroll
+                        for (int i = 0; i < kGroup; ++i) asum.add(k + i, v[i], gq[i]);
+                    } else {
+                        float ps, pg[3], ph[3];
+                        group_sums<kGroup>(v, gq, ps, pg, ph);
+                        pose_add_group(k, ps, pg, ph, s0, g0, h1);
+                    }
                 }
                 for (; k < k0 + S; ++k) {
                     const int64_t qx = sample_fixed(F, 0, k) - shift[0];
@@ -432,8 +637,12 @@ __global__ __launch_bounds__(kBlock) void drr_pose_staged_kernel(
                     box_corners(bx + A.o, sy, sz, c);
                     float gq[3];
                     const float v = interpolate_grad(A, c, gq);
-                    const float zero[3] = {0.0f, 0.0f, 0.0f};
-                    pose_add_group(k, v, gq, zero, s0, g0, h1);
+                    if constexpr (MODE == kAlpha) {
+                        asum.add(k, v, gq);
+                    } else {
+                        const float zero[3] = {0.0f, 0.0f, 0.0f};
+                        pose_add_group(k, v, gq, zero, s0, g0, h1);
+                    }
                 }
             }
             __syncthreads();
@@ -455,14 +664,23 @@ __global__ __launch_bounds__(kBlock) void drr_pose_staged_kernel(
                                                  iz + (n >> 2), tf, ch);
                 float gq[3];
                 const float v = interpolate_grad(A, c, gq);
-                const float zero[3] = {0.0f, 0.0f, 0.0f};
-                pose_add_group(k, v, gq, zero, s0, g0, h1);
+                if constexpr (MODE == kAlpha) {
+                    asum.add(k, v, gq);
+                } else {
+                    const float zero[3] = {0.0f, 0.0f, 0.0f};
+                    pose_add_group(k, v, gq, zero, s0, g0, h1);
+                }
             }
         }
         k0 += S;
         if (vol_cells * 2 <= kStageCap) S *= 2;
     }
-    if (hit) pose_chain_rule<MODE>(F, V, N, g, b.f, s0, g0, h1, contrib);
+    if (hit) {
+        if constexpr (MODE == kAlpha)
+            alpha_pose_chain(F, V, N, g, b.f, asum, contrib);
+        else
+            pose_chain_rule<MODE>(F, V, N, g, b.f, s0, g0, h1, contrib);
+    }
     const double t = block_sum12(contrib, red);
     if (threadIdx.x < 12 && t != 0.0) unsafeAtomicAdd(acc + 12 * view + threadIdx.x, t);
 }
@@ -495,7 +713,7 @@ __global__ __launch_bounds__(256) void drr_zero_f64_kernel(double* __restrict__ 
     if (i < n) p[i] = 0.0;
 }
 
-template <typename T, Layout L>
+template <typename T, Layout L, int CLIP>
 static void launch_pose(const LaunchArgs& a, const T* src, uint32_t src_bytes, const Batch& b,
                         const float* grad_out, double* acc, hipStream_t stream)
 {
@@ -503,11 +721,15 @@ static void launch_pose(const LaunchArgs& a, const T* src, uint32_t src_bytes, c
     const int tiles_per_view = tiles_x * tiles_y;
     const dim3 grid(tiles_per_view * a.n_views * a.C), block(kBlock);
     if (a.mode == kBeerLambert)
-        hipLaunchKernelGGL((drr_pose_grad_kernel<T, L, kBeerLambert>), grid, block, 0, stream, src,
-                           src_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view,
-                           b, grad_out, acc);
+        hipLaunchKernelGGL((drr_pose_grad_kernel<T, L, kBeerLambert, CLIP>), grid, block, 0,
+                           stream, src, src_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                           tiles_per_view, b, grad_out, acc);
+    else if (a.mode == kLineIntegral)
+        hipLaunchKernelGGL((drr_pose_grad_kernel<T, L, kLineIntegral, CLIP>), grid, block, 0,
+                           stream, src, src_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
+                           tiles_per_view, b, grad_out, acc);
     else
-        hipLaunchKernelGGL((drr_pose_grad_kernel<T, L, kLineIntegral>), grid, block, 0, stream,
+        hipLaunchKernelGGL((drr_pose_grad_kernel<T, L, kAlpha, CLIP>), grid, block, 0, stream,
                            src, src_bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
                            tiles_per_view, b, grad_out, acc);
 }
@@ -517,48 +739,61 @@ template <typename T>
 static void pose_typed(const LaunchArgs& a, const RenderPlan& p, const T* src, const Batch& b,
                        const float* grad_out, double* acc, hipStream_t stream)
 {
+    if (a.clip == kClipNearFar) {
+        // zero-padded cells or z-pairs (the near/far plan always makes one)
+        if (p.cells)
+            launch_pose<T, Layout::Cell, kClipNearFar>(a, src, a.V.cell_total_bytes, b, grad_out,
+                                                       acc, stream);
+        else
+            launch_pose<T, Layout::ZPair, kClipNearFar>(a, src, a.V.total_bytes, b, grad_out,
+                                                        acc, stream);
+        return;
+    }
     if (p.cells) {
-        launch_pose<T, Layout::Cell>(a, src, a.V.cell_total_bytes, b, grad_out, acc, stream);
+        launch_pose<T, Layout::Cell, kClipBox>(a, src, a.V.cell_total_bytes, b, grad_out, acc,
+                                               stream);
         return;
     }
     if (p.zpair) {
-        launch_pose<T, Layout::ZPair>(a, src, a.V.total_bytes, b, grad_out, acc, stream);
+        launch_pose<T, Layout::ZPair, kClipBox>(a, src, a.V.total_bytes, b, grad_out, acc,
+                                                stream);
         return;
     }
     const uint32_t bytes = (uint32_t)((size_t)a.V.n[0] * a.V.n[1] * a.V.n[2] * sizeof(T));
     if (a.V.n[0] >= 2)
-        launch_pose<T, Layout::Pair>(a, src, bytes, b, grad_out, acc, stream);
+        launch_pose<T, Layout::Pair, kClipBox>(a, src, bytes, b, grad_out, acc, stream);
     else
-        launch_pose<T, Layout::Single>(a, src, bytes, b, grad_out, acc, stream);
+        launch_pose<T, Layout::Single, kClipBox>(a, src, bytes, b, grad_out, acc, stream);
+}
+
+template <typename T, int MODE>
+static void launch_pose_staged_mode(const LaunchArgs& a, const T* vol, const Batch& b,
+                                    const float* grad_out, double* acc, hipStream_t stream)
+{
+    const int tiles_x = (a.W + kTile - 1) / kTile, tiles_y = (a.H + kTile - 1) / kTile;
+    const int tiles_per_view = tiles_x * tiles_y;
+    const dim3 grid(tiles_per_view * a.n_views * a.C), block(kBlock);
+    const uint32_t bytes = (uint32_t)((size_t)a.V.n[0] * a.V.n[1] * a.V.n[2] * sizeof(T));
+    if (a.has_tf)
+        hipLaunchKernelGGL((drr_pose_staged_kernel<T, MODE, true>), grid, block, 0, stream, vol,
+                           bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view, b,
+                           a.tf, grad_out, acc);
+    else
+        hipLaunchKernelGGL((drr_pose_staged_kernel<T, MODE, false>), grid, block, 0, stream, vol,
+                           bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x, tiles_per_view, b,
+                           a.tf, grad_out, acc);
 }
 
 template <typename T>
 static void launch_pose_staged(const LaunchArgs& a, const T* vol, const Batch& b,
                                const float* grad_out, double* acc, hipStream_t stream)
 {
-    const int tiles_x = (a.W + kTile - 1) / kTile, tiles_y = (a.H + kTile - 1) / kTile;
-    const int tiles_per_view = tiles_x * tiles_y;
-    const dim3 grid(tiles_per_view * a.n_views * a.C), block(kBlock);
-    const uint32_t bytes = (uint32_t)((size_t)a.V.n[0] * a.V.n[1] * a.V.n[2] * sizeof(T));
-    if (a.mode == kBeerLambert) {
-        if (a.has_tf)
-            hipLaunchKernelGGL((drr_pose_staged_kernel<T, kBeerLambert, true>), grid, block, 0,
-                               stream, vol, bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
-                               tiles_per_view, b, a.tf, grad_out, acc);
-        else
-            hipLaunchKernelGGL((drr_pose_staged_kernel<T, kBeerLambert, false>), grid, block, 0,
-                               stream, vol, bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
-                               tiles_per_view, b, a.tf, grad_out, acc);
-    } else {
-        if (a.has_tf)
-            hipLaunchKernelGGL((drr_pose_staged_kernel<T, kLineIntegral, true>), grid, block, 0,
-                               stream, vol, bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
-                               tiles_per_view, b, a.tf, grad_out, acc);
-        else
-            hipLaunchKernelGGL((drr_pose_staged_kernel<T, kLineIntegral, false>), grid, block, 0,
-                               stream, vol, bytes, a.V, a.K, a.poses, a.H, a.W, a.N, tiles_x,
-                               tiles_per_view, b, a.tf, grad_out, acc);
-    }
+    if (a.mode == kBeerLambert)
+        launch_pose_staged_mode<T, kBeerLambert>(a, vol, b, grad_out, acc, stream);
+    else if (a.mode == kLineIntegral)
+        launch_pose_staged_mode<T, kLineIntegral>(a, vol, b, grad_out, acc, stream);
+    else
+        launch_pose_staged_mode<T, kAlpha>(a, vol, b, grad_out, acc, stream);
 }
 
 hipError_t launch_backward_pose(const LaunchArgs& a, const RenderPlan& plan, const void* vol,

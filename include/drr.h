@@ -313,12 +313,17 @@ int drr_render_backward_volume(const void *volume, int dtype, int n_volumes, int
                                size_t workspace_bytes, void *stream);
 
 /* Pose gradient of drr_render (flashdrr API, VolumeRaycaster class text:
- * rendering is differentiable with respect to the view matrices): for
- * L = sum grad_out * out it writes dL/dP_v for every view's 3x4 [R | t] as
- * drr_backward_pose does, summed over the view's channels, with the density
- * factor and the transfer function of the call.  Beer-Lambert and line
- * integral with DRR_CLIP_BOX (compositing or the near/far range return
- * DRR_ERR_UNSUPPORTED).
+ * rendering is differentiable with respect to the view matrices, in either
+ * integration mode of VolumeRaycaster.__init__): for L = sum grad_out * out it
+ * writes dL/dP_v for every view's 3x4 [R | t] as drr_backward_pose does,
+ * summed over the view's channels, with the density factor, the transfer
+ * function and the clip of the call.  Every mode: Beer-Lambert and the line
+ * integral, and alpha compositing, whose per-sample coefficient (as in
+ * drr_render_backward_volume) and dI/ddz come from one front-to-back pass
+ * (the forward's image is not needed).  Either clip: with DRR_CLIP_BOX the
+ * range ends move with the planes that bound each ray; with
+ * DRR_CLIP_NEAR_FAR with the camera centre alone (near and far are distances
+ * from it), and samples read the zero padding.
  *   grad_out      device, n_views x n_channels x det_h x det_w floats
  *   grad_poses    device, n_views x 12 floats, OVERWRITTEN
  *   workspace     device, >= drr_render_workspace_bytes(..., DRR_WORKSPACE_POSE_BACKWARD),

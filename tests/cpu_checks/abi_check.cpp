@@ -140,9 +140,11 @@ int main()
                                       1.0f, 0, 30.0f, nullptr, nullptr, 0, Df, nullptr, Df, Df,
                                       nullptr, 0, nullptr),
            DRR_ERR_INVALID_ARGUMENT, "render backward compositing without image");
-    expect(drr_render_backward_pose(D, 0, 1, 1, 8, 8, 8, sp.data(), K.data(), Df, 1, 4, 4, 8, 0,
-                                    1.0f, 1, 30.0f, nullptr, nullptr, 0, Df, Df, D, 4096, nullptr),
-           DRR_ERR_UNSUPPORTED, "render pose backward near/far");
+    // the near/far pose backward reads a zero-padded copy: a workspace of the
+    // view sums alone is too small
+    expect(drr_render_backward_pose(D, 0, 1, 1, 8, 8, 8, sp.data(), K.data(), Df, 1, 4, 4, 8, 2,
+                                    1.0f, 1, 30.0f, nullptr, nullptr, 0, Df, Df, D, 256, nullptr),
+           DRR_ERR_WORKSPACE_TOO_SMALL, "render pose backward near/far workspace");
 
     // cameras
     std::vector<float> Kout(9);

@@ -502,52 +502,100 @@ def test_render_edge_cases(dev):
     check(img, tau, grad, ref, ref_tau, ref_g, "one voxel near/far")
 
 
-@pytest.mark.parametrize("N", [37, 101])
-@pytest.mark.parametrize("tf", [False, True])
-@pytest.mark.parametrize("mode", [BL, RAW])
-def test_render_pose_gradient(dev, mode, tf, N):
-    """Pose gradients of batched renders (2 volumes x 2 channels, 2 views each,
-    density factor, transfer function) against the oracle, per view normwise
-    over the twelve entries; N = 37 reads (mapped) z-pairs, N = 101 (mapped)
-    corner cells."""
-    seed = 400 + 4 * mode + 2 * tf + (N > 50)
-    vol, spacing, K, poses, H, Wd, N, g = problem(seed, N=N, tf=tf)
-    transfer = knots(2) if tf else None
-    f = 30.0 if tf else 0.7
-    say(f"case: render pose gradient mode={mode} tf={tf} N={N}")
-    P = torch.from_numpy(poses).to(dev)
-    gp = drr.drr_render_backward_pose(torch.from_numpy(vol).to(dev), spacing, K, P, H, Wd, N,
-                                      mode, torch.from_numpy(g).to(dev), f, BOX, 0.0, transfer)
-    torch.cuda.synchronize()
-    ref = oracle.render_pose_gradient(vol, spacing, K, poses, H, Wd, N, mode, g,
-                                      density_factor=f, transfer=transfer)
-    got = gp.cpu().double().numpy()
+def check_pose_views(got, ref, what):
     errs = [np.abs(got[v] - ref[v]).max() / np.abs(ref[v]).max() for v in range(len(ref))]
-    say(f"render pose gradient m{mode} tf{int(tf)} N{N}: per-view normwise err max {max(errs):.3e}")
+    say(f"{what}: per-view normwise err max {max(errs):.3e}")
+    assert all(np.abs(ref[v]).max() > 0 for v in range(len(ref)))
     assert max(errs) <= GRAD
 
 
-def test_raycast_pose_gradient_and_unsupported_modes(dev):
-    """Autograd reaches the poses through raycast (one pose broadcast to two
-    volumes sums both volumes' gradients); compositing and the near/far range
-    refuse pose gradients."""
+@pytest.mark.parametrize("N", [37, 101])
+@pytest.mark.parametrize("tf", [False, True])
+@pytest.mark.parametrize("clip", [BOX, NEAR_FAR])
+@pytest.mark.parametrize("mode", [BL, RAW, ALPHA])
+def test_render_pose_gradient(dev, mode, clip, tf, N):
+    """Pose gradients of batched renders (2 volumes x 2 channels, 2 views each,
+    density factor, transfer function) in every mode and both clips against
+    the oracle, per view normwise over the twelve entries; with the box clip
+    N = 37 reads (mapped) z-pairs and N = 101 (mapped) corner cells, in the
+    near/far mode zero-padded z-pairs and cells."""
+    seed = 400 + 8 * mode + 4 * clip + 2 * tf + (N > 50)
+    vol, spacing, K, poses, H, Wd, N, g = problem(seed, N=N, tf=tf)
+    transfer = knots(2) if tf else None
+    f = 30.0 if tf else 0.7
+    margin = 2.0
+    name = plan_name(vol, H, Wd, N, poses.shape[0], mode, clip, 3 if tf else 0)
+    say(f"case: render pose gradient mode={mode} clip={clip} tf={tf} N={N} ({name})")
+    P = torch.from_numpy(poses).to(dev)
+    gp = drr.drr_render_backward_pose(torch.from_numpy(vol).to(dev), spacing, K, P, H, Wd, N,
+                                      mode, torch.from_numpy(g).to(dev), f, clip, margin,
+                                      transfer)
+    torch.cuda.synchronize()
+    ref = oracle.render_pose_gradient(vol, spacing, K, poses, H, Wd, N, mode, g,
+                                      density_factor=f, transfer=transfer, clip=clip,
+                                      margin=margin)
+    check_pose_views(gp.cpu().double().numpy(), ref,
+                     f"render pose gradient m{mode} c{clip} tf{int(tf)} N{N}")
+
+
+def test_raycast_pose_gradient_every_mode(dev):
+    """Autograd reaches the poses through raycast in every mode and both clips
+    (one pose broadcast to two volumes sums both volumes' gradients)."""
     vol, spacing, K, poses, H, Wd, N, g = problem(410, B=2, C=1, vpv=1, N=33)
     v = torch.from_numpy(vol).to(dev)
-    P = torch.from_numpy(poses[:1]).to(dev).requires_grad_(True)
-    img = drr.raycast(v, spacing, K, P, H, Wd, N, BL, 1.5)
-    (img * torch.from_numpy(g).to(dev)).sum().backward()
-    torch.cuda.synchronize()
-    ref = oracle.render_pose_gradient(vol, spacing, K, np.repeat(poses[:1], 2, axis=0), H, Wd, N,
-                                      BL, g, density_factor=1.5).sum(axis=0)
-    err = np.abs(P.grad.cpu().double().numpy()[0] - ref).max() / np.abs(ref).max()
-    say(f"raycast pose gradient (broadcast pose): normwise err {err:.3e}")
-    assert err <= GRAD
     gt = torch.from_numpy(g).to(dev)
-    for mode, clip in [(ALPHA, BOX), (BL, NEAR_FAR)]:
-        with pytest.raises(drr.DRRError) as e:
-            drr.drr_render_backward_pose(v, spacing, K, P.detach().expand(2, 3, 4).contiguous(),
-                                         H, Wd, N, mode, gt, 1.0, clip)
-        assert e.value.status == 2
+    for mode, clip in [(BL, BOX), (ALPHA, BOX), (RAW, NEAR_FAR), (ALPHA, NEAR_FAR)]:
+        say(f"case: raycast pose gradient mode={mode} clip={clip}")
+        P = torch.from_numpy(poses[:1]).to(dev).requires_grad_(True)
+        img = drr.raycast(v, spacing, K, P, H, Wd, N, mode, 1.5, clip, 3.0)
+        (img * gt).sum().backward()
+        torch.cuda.synchronize()
+        ref = oracle.render_pose_gradient(vol, spacing, K, np.repeat(poses[:1], 2, axis=0), H,
+                                          Wd, N, mode, g, density_factor=1.5, clip=clip,
+                                          margin=3.0).sum(axis=0)
+        err = np.abs(P.grad.cpu().double().numpy()[0] - ref).max() / np.abs(ref).max()
+        say(f"raycast pose gradient m{mode} c{clip} (broadcast pose): normwise err {err:.3e}")
+        assert err <= GRAD
+
+
+def test_batch_workload_hu_phantom_alpha_near_far_pose_gradient(dev):
+    """The 16-view 200 x 200 batch at full size from the HU phantom (transfer
+    function, near/far with a 30 mm margin, alpha compositing): pose gradient
+    of every view against the oracle."""
+    w = W.make_workload(2)
+    hu = W.hu_phantom().astype(np.float32)
+    transfer = (np.array([[-1000.0, 0.0, 1500.0]], dtype=np.float32),
+                np.array([[0.0, 0.02, 0.05]], dtype=np.float32))
+    g = np.random.default_rng(2003).uniform(-1, 1, size=(16, 1, 200, 200)).astype(np.float32)
+    say("case: batch workload, HU phantom, transfer + near/far + alpha, pose gradient")
+    gp = drr.drr_render_backward_pose(torch.from_numpy(hu[None, None]).to(dev), w.spacing, w.K,
+                                      torch.from_numpy(w.poses).to(dev), 200, 200, w.n_samples,
+                                      ALPHA, torch.from_numpy(g).to(dev), 1.0, NEAR_FAR, 30.0,
+                                      transfer)
+    torch.cuda.synchronize()
+    ref = oracle.render_pose_gradient(hu[None, None], w.spacing, w.K, w.poses, 200, 200,
+                                      w.n_samples, ALPHA, g, transfer=transfer, clip=NEAR_FAR,
+                                      margin=30.0)
+    check_pose_views(gp.cpu().double().numpy(), ref, "batch HU alpha near/far pose")
+
+
+def test_train_camera_row_band_alpha_pose_gradient(dev):
+    """The 1024^2 x 512 train-step camera composited, restricted to a 96-row
+    band through the volume's centre (same rays; cy moved so the band is the
+    whole detector; under 8 samples per cell, so the march reads the volume's
+    x-pairs): pose gradient against the oracle."""
+    w = W.make_workload(3)
+    K = w.K.copy()
+    K[1, 2] -= 464.0                  # rows 464..559 of the full detector
+    g = np.ascontiguousarray(w.grad_out[:, None, 464:560, :])
+    vol = w.volume[None, None]
+    say("case: compositing pose gradient, 1024-wide band of the train-step camera")
+    gp = drr.drr_render_backward_pose(torch.from_numpy(vol).to(dev), w.spacing, K,
+                                      torch.from_numpy(w.poses).to(dev), 96, 1024, 512, ALPHA,
+                                      torch.from_numpy(g).to(dev), 1.0, BOX, 0.0, None)
+    torch.cuda.synchronize()
+    ref = oracle.render_pose_gradient(vol, w.spacing, K, w.poses, 96, 1024, 512, ALPHA, g)
+    check_pose_views(gp.cpu().double().numpy(), ref, "train band alpha pose")
 
 
 def _is_staged(vol, H, Wd, N, V, mode, nk, bf16=False):
@@ -602,7 +650,7 @@ def _pose_is_staged(vol, H, Wd, N, V, nk, bf16=False):
 
 
 @pytest.mark.parametrize("tf", [False, True])
-@pytest.mark.parametrize("mode", [BL, RAW])
+@pytest.mark.parametrize("mode", [BL, RAW, ALPHA])
 def test_render_staged_pose_gradient(dev, mode, tf):
     """The LDS-staged pose gradient (2 volumes x 2 channels, 2 views each,
     96 x 96 detector over a 16^3 volume, as the staged forward test), with the
