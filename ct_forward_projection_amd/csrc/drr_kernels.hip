@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kBlock) void drr_march_kernel(
     PixelCoord px;
     int j = 0;
     if constexpr (SPLIT == 1) {
-        px = tile_pixel(tile, tiles_x, tiles_per_view);
+        px = tile_pixel_rows(tile, tiles_x, tiles_per_view);
     } else {
         px = split_pixel<SPLIT>(tile, tiles_x, tiles_per_view);
         j = (int)threadIdx.x % SPLIT;
