@@ -150,6 +150,40 @@ __device__ inline int block_exclusive_scan(int v, int* red, int& excl)
     return total;
 }
 
+// The same for two ints at once (a and b, exclusive sums in ea and eb);
+// returns both totals.
+__device__ inline int2 block_exclusive_scan2(int a, int b, int* red, int& ea, int& eb)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int ia = a, ib = b;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int ta = __shfl_up(ia, off, 64), tb = __shfl_up(ib, off, 64);
+        if (lane >= off) {
+            ia += ta;
+            ib += tb;
+        }
+    }
+    if (lane == 63) {
+        red[2 * wave] = ia;
+        red[2 * wave + 1] = ib;
+    }
+    __syncthreads();
+    int base_a = 0, base_b = 0, tot_a = 0, tot_b = 0;
+#pragma unroll
+    for (int w = 0; w < kBrickThreads / 64; ++w) {
+        const int sa = red[2 * w], sb = red[2 * w + 1];
+        base_a += w < wave ? sa : 0;
+        base_b += w < wave ? sb : 0;
+        tot_a += sa;
+        tot_b += sb;
+    }
+    ea = base_a + ia - a;
+    eb = base_b + ib - b;
+    __syncthreads();
+    return make_int2(tot_a, tot_b);
+}
+
 // The candidate rays of a brick: for each view of its channel-volume the
 // detector rectangle that can reach its cells (brick_pixel_rect), taken
 // kViewChunk views at a time.  Candidate j of a chunk is pixel j - start[v]
@@ -268,17 +302,20 @@ __device__ inline void weights8(float fx, float fy, float fz, float c, float w[8
     w[7] = w11 * fx; w[6] = w11 - w[7];
 }
 
-// The work queue of one round: one slot per thread for its candidate ray (a
-// ray without samples in the brick has count 0): the position of its first
-// in-brick sample relative to the copy's origin (voxel lo - 1 at 0, fixed
-// point), its step, its scaled coefficient, and the exclusive prefix sum of
-// the sample counts in slot order.
+// The work queue of one round: the candidate rays with samples in the brick,
+// compacted: the position of each one's first in-brick sample relative to the
+// copy's origin (voxel lo - 1 at 0, fixed point), its step, its scaled
+// coefficient and the exclusive prefix sum of the sample counts in queue
+// order; and for every thread the queue entry that holds the first sample of
+// its run.
 template <int Q>
 struct BrickQueue {
+    static_assert(Q <= 256, "queue entries are indexed by bytes");
     int64_t q[3][Q];
     int64_t d[3][Q];
     float c[Q];
     int pre[Q + 1];
+    unsigned char first[Q];
 };
 
 // The brick kernel.  Grid: (bricks of one channel-volume, channel-volumes).
@@ -288,11 +325,13 @@ struct BrickQueue {
 // rows of every view's candidate rectangle.  Candidate rays (brick_pixel_rect
 // over the views) are then taken kBrickThreads at a time, one per thread: its
 // exact range of samples in the brick region (brick_exact_range) goes to the
-// LDS queue.  The queue's samples, counted in slot order, are split into
-// kBrickThreads equal runs, one per thread: a thread steps through its run by
-// fixed-point adds and moves to the next queued ray where one ends, so every
-// lane of a wave has the same number of samples whatever the lengths of the
-// rays.  MERGE (views dense against the voxels, several samples of a ray per
+// LDS queue, compacted to the rays that have some.  The queue's samples,
+// counted in queue order, are split into kBrickThreads equal runs, one per
+// thread (each queue entry marks the threads whose run starts in it): a
+// thread steps through its run by fixed-point adds and moves to the next
+// queued ray, whose entry it has read ahead, where one ends, so every lane of
+// a wave has the same number of samples whatever the lengths of the rays.
+// MERGE (views dense against the voxels, several samples of a ray per
 // cell) sums consecutive samples of one cell in registers before adding them
 // to the copy.
 template <int B, int Q, bool MERGE>
@@ -309,7 +348,7 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
     __shared__ int start[kViewChunk + 1];
     __shared__ int rect[3 * kViewChunk];
     __shared__ BrickViewRay vrays[kViewChunk];
-    __shared__ int red[kBrickThreads / 64];
+    __shared__ int red[2 * (kBrickThreads / 64)];
     __shared__ float fred[kBrickThreads / 64];
 
     const int brick = xcd_contiguous_tile((int)blockIdx.x, (int)gridDim.x);
@@ -411,43 +450,67 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
                 const RayRecord r = next;
                 fetch(jb + kBrickThreads + t, next);
                 int cnt = 0;
+                int64_t q[3], dq[3];
+                float cs = 0.0f;
                 if (r.n != 0 && isfinite(r.cell_bound)) {
                     int k_lo, k_hi;
-                    int64_t q[3];
                     brick_exact_range(r, b, k_lo, k_hi, q);
                     cnt = k_hi - k_lo;
-                    if (cnt > 0) {
 #pragma unroll
-                        for (int a = 0; a < 3; ++a) {
-                            qu.q[a][t] = q[a];
-                            qu.d[a][t] = r.dq[a];
-                        }
-                        qu.c[t] = r.coef * scale;
-                    }
+                    for (int a = 0; a < 3; ++a) dq[a] = r.dq[a];
+                    cs = r.coef * scale;
                 }
-                int first_sample;
-                const int n_samples = block_exclusive_scan(cnt, red, first_sample);
-                qu.pre[t] = first_sample;
-                if (t == 0) qu.pre[Q] = n_samples;
+                int pos, first_sample;
+                const int2 tot =
+                    block_exclusive_scan2(cnt > 0 ? 1 : 0, cnt, red, pos, first_sample);
+                const int m = tot.x, n_samples = tot.y;
+                if (cnt > 0) {
+#pragma unroll
+                    for (int a = 0; a < 3; ++a) {
+                        qu.q[a][pos] = q[a];
+                        qu.d[a][pos] = dq[a];
+                    }
+                    qu.c[pos] = cs;
+                    qu.pre[pos] = first_sample;
+                    // the threads whose run [n u / Q, n (u + 1) / Q) starts in
+                    // this entry: n u / Q in [first, first + cnt)
+                    const uint64_t nn = (uint64_t)n_samples;
+                    const int u0 = (int)(((uint64_t)first_sample * Q + nn - 1) / nn);
+                    const int u1 = (int)(((uint64_t)(first_sample + cnt) * Q + nn - 1) / nn);
+                    for (int u = u0; u < u1; ++u) qu.first[u] = (unsigned char)pos;
+                }
+                if (t == 0) qu.pre[m] = n_samples;
                 __syncthreads();
                 // this thread's run [s0, s1) of the queue's samples
                 const uint32_t s0 = (uint32_t)(((uint64_t)n_samples * t) / kBrickThreads);
                 const uint32_t s1 = (uint32_t)(((uint64_t)n_samples * (t + 1)) / kBrickThreads);
                 if (s1 > s0) {
-                    // the slot holding sample s0: the last with pre <= s0 (it
-                    // has samples: its successor's prefix is above s0)
-                    int e = 0, hi = Q - 1;
-                    while (e < hi) {
-                        const int mid = (e + hi + 1) >> 1;
-                        if ((uint32_t)qu.pre[mid] <= s0) e = mid; else hi = mid - 1;
-                    }
+                    int e = qu.first[t];
                     const int64_t off = (int64_t)(s0 - (uint32_t)qu.pre[e]);
                     int64_t qx = qu.q[0][e] + off * qu.d[0][e];
                     int64_t qy = qu.q[1][e] + off * qu.d[1][e];
                     int64_t qz = qu.q[2][e] + off * qu.d[2][e];
                     int64_t dx = qu.d[0][e], dy = qu.d[1][e], dz = qu.d[2][e];
                     float c = qu.c[e];
-                    uint32_t left = (uint32_t)qu.pre[e + 1] - s0;   // samples left in slot e
+                    uint32_t left = (uint32_t)qu.pre[e + 1] - s0;   // samples left in entry e
+                    // the next entry, read ahead (the run continues there when
+                    // entry e ends before s1; its reads are clamped in range
+                    // and unused when it does not)
+                    auto next_of = [&](int i, int64_t nq[3], int64_t nd[3], float& nc,
+                                       uint32_t& nleft) {
+                        const int k = min(i, Q - 1);
+#pragma unroll
+                        for (int a = 0; a < 3; ++a) {
+                            nq[a] = qu.q[a][k];
+                            nd[a] = qu.d[a][k];
+                        }
+                        nc = qu.c[k];
+                        nleft = (uint32_t)(qu.pre[min(i + 1, Q)] - qu.pre[min(i, Q)]);
+                    };
+                    int64_t nq[3], nd[3];
+                    float nc;
+                    uint32_t nleft;
+                    next_of(e + 1, nq, nd, nc, nleft);
                     float sum[8];
 #pragma unroll
                     for (int n = 0; n < 8; ++n) sum[n] = 0.0f;
@@ -473,15 +536,14 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
                         qx += dx;
                         qy += dy;
                         qz += dz;
-                        if (--left == 0 && s + 1 < s1) {
-                            // the next slot with samples (it exists: s + 1 < s1)
-                            do {
-                                ++e;
-                            } while (qu.pre[e + 1] == qu.pre[e]);
-                            qx = qu.q[0][e]; qy = qu.q[1][e]; qz = qu.q[2][e];
-                            dx = qu.d[0][e]; dy = qu.d[1][e]; dz = qu.d[2][e];
-                            c = qu.c[e];
-                            left = (uint32_t)(qu.pre[e + 1] - qu.pre[e]);
+                        if (--left == 0) {
+                            // entry e ends: continue with the next one
+                            ++e;
+                            qx = nq[0]; qy = nq[1]; qz = nq[2];
+                            dx = nd[0]; dy = nd[1]; dz = nd[2];
+                            c = nc;
+                            left = nleft;
+                            next_of(e + 1, nq, nd, nc, nleft);
                         }
                     }
                     if (MERGE && pcell >= 0) brick_add8<B>(acc, pcell, sum);
