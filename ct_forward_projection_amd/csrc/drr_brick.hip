@@ -329,8 +329,8 @@ struct BrickQueue {
 // counted in queue order, are split into kBrickThreads equal runs, one per
 // thread (each queue entry marks the threads whose run starts in it): a
 // thread steps through its run by fixed-point adds and moves to the next
-// queued ray, whose entry it has read ahead, where one ends, so every lane of
-// a wave has the same number of samples whatever the lengths of the rays.
+// queued ray where one ends, so every lane of a wave has the same number of
+// samples whatever the lengths of the rays.
 // MERGE (views dense against the voxels, several samples of a ray per
 // cell) sums consecutive samples of one cell in registers before adding them
 // to the copy.
@@ -493,24 +493,6 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
                     int64_t dx = qu.d[0][e], dy = qu.d[1][e], dz = qu.d[2][e];
                     float c = qu.c[e];
                     uint32_t left = (uint32_t)qu.pre[e + 1] - s0;   // samples left in entry e
-                    // the next entry, read ahead (the run continues there when
-                    // entry e ends before s1; its reads are clamped in range
-                    // and unused when it does not)
-                    auto next_of = [&](int i, int64_t nq[3], int64_t nd[3], float& nc,
-                                       uint32_t& nleft) {
-                        const int k = min(i, Q - 1);
-#pragma unroll
-                        for (int a = 0; a < 3; ++a) {
-                            nq[a] = qu.q[a][k];
-                            nd[a] = qu.d[a][k];
-                        }
-                        nc = qu.c[k];
-                        nleft = (uint32_t)(qu.pre[min(i + 1, Q)] - qu.pre[min(i, Q)]);
-                    };
-                    int64_t nq[3], nd[3];
-                    float nc;
-                    uint32_t nleft;
-                    next_of(e + 1, nq, nd, nc, nleft);
                     float sum[8];
 #pragma unroll
                     for (int n = 0; n < 8; ++n) sum[n] = 0.0f;
@@ -520,6 +502,27 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
                                                           fixed_floor(qz));
                         const float fx = fixed_frac(qx), fy = fixed_frac(qy);
                         const float fz = fixed_frac(qz);
+                        // the last sample of entry e: read the next entry now,
+                        // ahead of this sample's adds, so that taking it over
+                        // below waits for these reads only (LDS operations
+                        // complete in order) and the adds stay in flight.  The
+                        // reads are clamped in range; unused when the run ends.
+                        const bool last = left == 1;
+                        int64_t nq[3], nd[3];
+                        float nc;
+                        int np0, np1;          // (nothing computed from the reads here)
+                        if (last) {
+                            const int k = min(e + 1, Q - 1);
+#pragma unroll
+                            for (int a = 0; a < 3; ++a) {
+                                nq[a] = qu.q[a][k];
+                                nd[a] = qu.d[a][k];
+                            }
+                            nc = qu.c[k];
+                            np0 = qu.pre[min(e + 1, Q)];
+                            np1 = qu.pre[min(e + 2, Q)];
+                        }
+                        __builtin_amdgcn_sched_barrier(0);
                         if constexpr (MERGE) {
                             if (cell != pcell) {
                                 if (pcell >= 0) brick_add8<B>(acc, pcell, sum);
@@ -533,17 +536,18 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
                             weights8(fx, fy, fz, c, w);
                             brick_add8<B>(acc, cell, w);
                         }
+                        __builtin_amdgcn_sched_barrier(0);
                         qx += dx;
                         qy += dy;
                         qz += dz;
-                        if (--left == 0) {
+                        --left;
+                        if (last) {
                             // entry e ends: continue with the next one
                             ++e;
                             qx = nq[0]; qy = nq[1]; qz = nq[2];
                             dx = nd[0]; dy = nd[1]; dz = nd[2];
                             c = nc;
-                            left = nleft;
-                            next_of(e + 1, nq, nd, nc, nleft);
+                            left = (uint32_t)(np1 - np0);
                         }
                     }
                     if (MERGE && pcell >= 0) brick_add8<B>(acc, pcell, sum);
