@@ -91,9 +91,8 @@ __global__ __launch_bounds__(256) void drr_ray_record_kernel(
         block_max[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-// One thread per view: its fp32 projection K [R | t] and its rays in
-// continuous voxel index space (from the fp64 camera), for the brick kernel.
-__global__ __launch_bounds__(64) void drr_brick_views_kernel(VolumeDesc V, Intrinsics K,
+// One thread per view: its fp32 projection K [R | t] (from fp64 products).
+__global__ __launch_bounds__(64) void drr_brick_views_kernel(Intrinsics K,
                                                               const float* __restrict__ poses,
                                                               int n_views,
                                                               BrickView* __restrict__ views)
@@ -109,14 +108,6 @@ __global__ __launch_bounds__(64) void drr_brick_views_kernel(VolumeDesc V, Intri
             out.P[r * 4 + c] = (float)((double)K.k[r * 3 + 0] * (double)pose[0 * 4 + c] +
                                        (double)K.k[r * 3 + 1] * (double)pose[1 * 4 + c] +
                                        (double)K.k[r * 3 + 2] * (double)pose[2 * 4 + c]);
-    }
-    ViewGeom G;
-    view_setup(pose, K, G);
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-#pragma unroll
-        for (int k = 0; k < 3; ++k) out.ray.m[a * 3 + k] = (float)(G.M[a * 3 + k] * V.inv_s[a]);
-        out.ray.c[a] = (float)(G.C[a] * V.inv_s[a] + V.q_off[a]);
     }
     views[v] = out;
 }
@@ -184,48 +175,42 @@ __device__ inline int2 block_exclusive_scan2(int a, int b, int* red, int& ea, in
     return make_int2(tot_a, tot_b);
 }
 
-// The candidate rays of a brick: for each view of its channel-volume the
-// detector rectangle that can reach its cells (brick_pixel_rect), taken
-// kViewChunk views at a time.  Candidate j of a chunk is pixel j - start[v]
-// (row-major in the rectangle) of the view v with start[v] <= j < start[v+1].
+// The candidate rays of a brick, kViewChunk views at a time: for each view of
+// its channel-volume the detector rectangle that can reach its cells
+// (brick_pixel_rect), walked row by row in batches of kBrickThreads rows, each
+// row cut to the span of the region's projection (brick_row_span).  Row p of
+// a chunk is row p - start[v] of view slot v's rectangle (start[v] <= p <
+// start[v + 1]); candidate j of a batch is column j - rowpre[i] of the
+// batch's row i (rowpre[i] <= j < rowpre[i + 1]).
 struct BrickCandidates {
-    int* start;          // kViewChunk + 1 exclusive prefix sums of the rectangle areas
+    int* start;          // kViewChunk + 1: exclusive prefix sums of the rectangles' heights
     int* rect;           // kViewChunk x 3: r0, c0, width
-    BrickViewRay* ray;   // kViewChunk: the view's rays in index space
+    int* rowpre;         // kBrickThreads + 1: exclusive prefix sums of the batch's row spans
+    int* rowinfo;        // kBrickThreads x 2: view slot << 16 | row, first column
 
-    // view slot and pixel of candidate j
-    __device__ void pixel(int j, int n_in_chunk, int& v, int& r, int& c) const
+    // view slot of chunk row p (0 <= p < start[n_in_chunk])
+    __device__ int view_of_row(int p, int n_in_chunk) const
     {
-        int lo = 0, hi = n_in_chunk - 1;               // last v with start[v] <= j
+        int lo = 0, hi = n_in_chunk - 1;               // last v with start[v] <= p
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
-            if (start[mid] <= j) lo = mid; else hi = mid - 1;
+            if (start[mid] <= p) lo = mid; else hi = mid - 1;
         }
-        v = lo;
-        const int local = j - start[lo];
-        const int w = rect[3 * lo + 2];
-        // local / w: below 2^22 from an fp32 reciprocal (within one of the
-        // quotient), corrected to the exact one
-        int rr;
-        if (local < (1 << 22)) {
-            rr = (int)((float)local * __builtin_amdgcn_rcpf((float)w));
-            rr -= rr * w > local ? 1 : 0;
-            rr += (rr + 1) * w <= local ? 1 : 0;
-        } else {
-            rr = local / w;
-        }
-        r = rect[3 * lo] + rr;
-        c = rect[3 * lo + 1] + (local - rr * w);
+        return lo;
     }
 
-    // record index of candidate j (pair = view * C + channel)
-    __device__ long long record(int j, int n_in_chunk, int first_view, int C, int ch, int H,
-                                int W) const
+    // view slot and pixel of candidate j of the current batch
+    __device__ void pixel(int j, int& v, int& r, int& c) const
     {
-        int v, r, c;
-        pixel(j, n_in_chunk, v, r, c);
-        const long long pair = (long long)(first_view + v) * C + ch;
-        return (pair * H + r) * W + c;
+        int lo = 0, hi = kBrickThreads - 1;            // last i with rowpre[i] <= j
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (rowpre[mid] <= j) lo = mid; else hi = mid - 1;
+        }
+        const int info = rowinfo[2 * lo];
+        v = info >> 16;
+        r = info & 0xffff;
+        c = rowinfo[2 * lo + 1] + (j - rowpre[lo]);
     }
 };
 
@@ -240,29 +225,53 @@ __device__ inline RayRecord load_record(const RayRecord* __restrict__ rec, long 
     return r;
 }
 
-// Sets up the candidate rectangles and rays of views [first, first + count)
-// for the brick region `g` (count <= kViewChunk) in `cand`; returns the
-// candidate total.
+// Sets up the candidate rectangles of views [first, first + count) for the
+// brick region `g` (count <= kViewChunk) in `cand`; returns their total
+// number of rows.
 __device__ inline int brick_chunk(const BrickView* __restrict__ views, int H, int W,
                                   const BrickRegion& g, int first, int count,
                                   BrickCandidates& cand, int* red)
 {
-    int area = 0;
+    int rows = 0;
     const int t = threadIdx.x;
     if (t < count) {
-        const BrickView bv = views[first + t];
-        const PixelRect R = brick_pixel_rect(bv.P, g, H, W);
+        const PixelRect R = brick_pixel_rect(views[first + t].P, g, H, W);
         const int w = R.c1 - R.c0 + 1, h = R.r1 - R.r0 + 1;
-        area = (w > 0 && h > 0) ? w * h : 0;
+        rows = (w > 0 && h > 0) ? h : 0;
         cand.rect[3 * t] = R.r0;
         cand.rect[3 * t + 1] = R.c0;
         cand.rect[3 * t + 2] = w > 0 ? w : 1;
-        cand.ray[t] = bv.ray;
     }
     int excl;
-    const int total = block_exclusive_scan(area, red, excl);
+    const int total = block_exclusive_scan(rows, red, excl);
     if (t < count) cand.start[t] = excl;
     if (t == 0) cand.start[count] = total;
+    __syncthreads();
+    return total;
+}
+
+// Rows [p0, p0 + kBrickThreads) of a chunk's rectangles, one per thread: its
+// span (the projection's when `spans`, else the whole rectangle row) into
+// `cand`; returns the batch's candidate total.
+__device__ inline int brick_row_batch(const BrickView* __restrict__ views, const BrickRegion& g,
+                                      int first, int count, int n_rows, int p0, bool spans,
+                                      BrickCandidates& cand, int* red)
+{
+    const int t = threadIdx.x, p = p0 + t;
+    int width = 0;
+    if (p < n_rows) {
+        const int v = cand.view_of_row(p, count);
+        const int r = cand.rect[3 * v] + (p - cand.start[v]);
+        int c0 = cand.rect[3 * v + 1], c1 = c0 + cand.rect[3 * v + 2] - 1;
+        if (spans) brick_row_span(brick_hull(views[first + v].P, g), r, c0, c1, c0, c1);
+        width = c1 >= c0 ? c1 - c0 + 1 : 0;
+        cand.rowinfo[2 * t] = (v << 16) | r;
+        cand.rowinfo[2 * t + 1] = c0;
+    }
+    int excl;
+    const int total = block_exclusive_scan(width, red, excl);
+    cand.rowpre[t] = excl;
+    if (t == 0) cand.rowpre[kBrickThreads] = total;
     __syncthreads();
     return total;
 }
@@ -334,8 +343,14 @@ struct BrickQueue {
 // MERGE (views dense against the voxels, several samples of a ray per
 // cell) sums consecutive samples of one cell in registers before adding them
 // to the copy.
+//
+// Four workgroups per CU (the LDS allows four): the register budget is held
+// to 128, which spills 14 registers of the cold per-row and per-chunk code to
+// scratch (60 bytes per lane; the sample loops stay in registers).  Measured
+// on MI355X, 16 views of 200^2 x 256 over 256^3: 1.51 ms at three
+// workgroups per CU (151 registers), 1.36 ms at four.
 template <int B, int Q, bool MERGE>
-__global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
+__global__ __launch_bounds__(kBrickThreads, 4) void drr_brick_scatter_kernel(
     VolumeDesc V, const BrickView* __restrict__ views, int H, int W, Batch bt,
     const RayRecord* __restrict__ rec, const float* __restrict__ block_max,
     float* __restrict__ grad, int nbx, int nby)
@@ -347,7 +362,8 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
     __shared__ BrickQueue<Q> qu;
     __shared__ int start[kViewChunk + 1];
     __shared__ int rect[3 * kViewChunk];
-    __shared__ BrickViewRay vrays[kViewChunk];
+    __shared__ int rowpre[kBrickThreads + 1];
+    __shared__ int rowinfo[2 * kBrickThreads];
     __shared__ int red[2 * (kBrickThreads / 64)];
     __shared__ float fred[kBrickThreads / 64];
 
@@ -359,7 +375,7 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
     const int vol = cv / bt.C, ch = cv - vol * bt.C;
     const int first_view = vol * bt.vpv;
     grad += (size_t)cv * bt.grad_stride;
-    BrickCandidates cand{start, rect, vrays};
+    BrickCandidates cand{start, rect, rowpre, rowinfo};
     const int t = threadIdx.x;
 
     for (int i = t; i < NE; i += kBrickThreads) acc[i] = 0ull;
@@ -374,7 +390,7 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
         brick_chunk(views, H, W, reg, first_view + v0, count, cand, red);
         for (int v = 0; v < count; ++v) {
             const int w = rect[3 * v + 2];
-            const int h = (start[v + 1] - start[v]) / w;
+            const int h = start[v + 1] - start[v];
             const long long pair = (long long)(first_view + v0 + v) * bt.C + ch;
             for (int row = t; row < h; row += kBrickThreads) {
                 const long long lin = (pair * H + rect[3 * v] + row) * W + rect[3 * v + 1];
@@ -399,13 +415,20 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
         cmax = 0.0f;
         for (int v0 = 0; v0 < bt.vpv; v0 += kViewChunk) {
             const int count = min(kViewChunk, bt.vpv - v0);
-            const int total = brick_chunk(views, H, W, reg, first_view + v0, count, cand, red);
-            for (int j = t; j < total; j += kBrickThreads) {
-                const long long ri = cand.record(j, count, first_view + v0, bt.C, ch, H, W);
-                const float cb = rec[ri].cell_bound;
-                if (rec[ri].n != 0 && isfinite(cb)) cmax = fmaxf(cmax, cb);
+            const int n_rows = brick_chunk(views, H, W, reg, first_view + v0, count, cand, red);
+            for (int p0 = 0; p0 < n_rows; p0 += kBrickThreads) {
+                const int total = brick_row_batch(views, reg, first_view + v0, count, n_rows, p0,
+                                                  true, cand, red);
+                for (int j = t; j < total; j += kBrickThreads) {
+                    int v, r, c;
+                    cand.pixel(j, v, r, c);
+                    const long long pair = (long long)(first_view + v0 + v) * bt.C + ch;
+                    const long long ri = (pair * H + r) * W + c;
+                    const float cb = rec[ri].cell_bound;
+                    if (rec[ri].n != 0 && isfinite(cb)) cmax = fmaxf(cmax, cb);
+                }
+                __syncthreads();
             }
-            __syncthreads();
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off, 64));
@@ -427,20 +450,20 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
     // pass 2: every finite ray's samples in the brick's cells into the copy
     if (cmax > 0.0f) {
         for (int v0 = 0; v0 < bt.vpv; v0 += kViewChunk) {
-            const int count = min(kViewChunk, bt.vpv - v0);
-            const int total = brick_chunk(views, H, W, reg, first_view + v0, count, cand, red);
+          const int count = min(kViewChunk, bt.vpv - v0);
+          const int n_rows = brick_chunk(views, H, W, reg, first_view + v0, count, cand, red);
+          for (int p0 = 0; p0 < n_rows; p0 += kBrickThreads) {
+            const int total = brick_row_batch(views, reg, first_view + v0, count, n_rows, p0,
+                                              true, cand, red);
             // this thread's candidate of a round: its record, loaded one round
             // ahead so the load's latency hides behind the previous round's
-            // samples (a ray that misses the region needs no record: n = 0)
+            // samples
             auto fetch = [&](int j, RayRecord& r) {
                 r.n = 0;
                 if (j >= total) return;
-                int cv_slot, cr, cc;
-                cand.pixel(j, count, cv_slot, cr, cc);
-                if (!brick_ray_may_hit(vrays[cv_slot], V.n, b, (float)cc + 0.5f,
-                                       (float)cr + 0.5f))
-                    return;
-                const long long pair = (long long)(first_view + v0 + cv_slot) * bt.C + ch;
+                int v, cr, cc;
+                cand.pixel(j, v, cr, cc);
+                const long long pair = (long long)(first_view + v0 + v) * bt.C + ch;
                 r = load_record(rec, (pair * H + cr) * W + cc);
             };
             RayRecord next;
@@ -554,6 +577,7 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
                 }
                 __syncthreads();
             }
+          }
         }
     }
     __syncthreads();
@@ -595,11 +619,16 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
     __threadfence();
     __syncthreads();
     for (int v0 = 0; v0 < bt.vpv; v0 += kViewChunk) {
-        const int count = min(kViewChunk, bt.vpv - v0);
-        const int total = brick_chunk(views, H, W, reg, first_view + v0, count, cand, red);
+      const int count = min(kViewChunk, bt.vpv - v0);
+      const int n_rows = brick_chunk(views, H, W, reg, first_view + v0, count, cand, red);
+      for (int p0 = 0; p0 < n_rows; p0 += kBrickThreads) {
+        const int total = brick_row_batch(views, reg, first_view + v0, count, n_rows, p0, true,
+                                          cand, red);
         for (int j = threadIdx.x; j < total; j += kBrickThreads) {
-            const long long ri = cand.record(j, count, first_view + v0, bt.C, ch, H, W);
-            const RayRecord r = load_record(rec, ri);
+            int cv_slot, cr, cc;
+            cand.pixel(j, cv_slot, cr, cc);
+            const long long pair = (long long)(first_view + v0 + cv_slot) * bt.C + ch;
+            const RayRecord r = load_record(rec, (pair * H + cr) * W + cc);
             if (r.n == 0 || isfinite(r.cell_bound)) continue;
             int k_lo, k_hi;
             brick_sample_range(r, b, k_lo, k_hi);
@@ -641,6 +670,7 @@ __global__ __launch_bounds__(kBrickThreads) void drr_brick_scatter_kernel(
             }
         }
         __syncthreads();
+      }
     }
 }
 
@@ -657,7 +687,7 @@ hipError_t launch_brick_backward(const LaunchArgs& a, const float* grad_out, con
         reinterpret_cast<char*>(block_max) + ray_block_max_bytes(a.n_views, a.C, a.H, a.W));
     if (a.n_views > 0) {
         hipLaunchKernelGGL(drr_brick_views_kernel, dim3((a.n_views + 63) / 64), dim3(64), 0,
-                           stream, a.V, a.K, a.poses, a.n_views, views);
+                           stream, a.K, a.poses, a.n_views, views);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -200,41 +200,96 @@ __host__ __device__ inline PixelRect brick_pixel_rect(const float P[12], const B
     return R;
 }
 
-// A view's rays in continuous voxel index space: image point (u, v, 1) looks
-// along m (u, v, 1) from c (fp32, rounded from the fp64 camera), i.e.
-// q(t) = c + t m (u, v, 1), t >= 0.
-struct BrickViewRay {
-    float m[9];
-    float c[3];
-};
-
-// What the brick kernel needs of a view (fp32, 96 bytes): its projection
-// K [R | t] and its rays in index space.
+// What the brick kernel needs of a view: its projection K [R | t] as 3 x 4,
+// fp32 (from the fp64 camera).
 struct BrickView {
     float P[12];
-    BrickViewRay ray;
 };
 
-// Whether the ray through image point (u, v, 1) can have samples in the brick
-// region (continuous indices [lo - 1, lo + e) per axis, cut to the volume): the
-// slab test against that box widened by 1/16 voxel per side, which absorbs
-// the fp32 rounding of the view's rays.  False only when the line misses the
-// widened box; a comparison with NaN (a ray parallel to a face, starting on it)
-// keeps the ray.
-__host__ __device__ inline bool brick_ray_may_hit(const BrickViewRay& vr, const int n[3],
-                                                  const BrickBox& b, float u, float v)
+// The region's eight corners projected into the image, for the per-row spans
+// below: u, v of corner k (x, y, z bits as in brick_pixel_rect) and that
+// function's margin m.  `narrow` when every corner lies in front of the
+// camera (depth above 2^-10 of the farthest): the region's projection is then
+// the convex hull of the projected corners (a perspective projection keeps a
+// convex set in front of the camera convex).  Otherwise the caller uses whole
+// rows of the rectangle.
+struct BrickHull {
+    float u[8], v[8];
+    float m;
+    bool narrow;
+};
+
+__host__ __device__ inline BrickHull brick_hull(const float P[12], const BrickRegion& g)
 {
-    float tmin = -3e38f, tmax = 3e38f;
-    for (int a = 0; a < 3; ++a) {
-        const float d = vr.m[a * 3] * u + vr.m[a * 3 + 1] * v + vr.m[a * 3 + 2];
-        const float lo = fmaxf((float)(b.lo[a] - 1), -0.5f) - 0.0625f;
-        const float hi = fminf((float)(b.lo[a] + b.e[a]), (float)n[a] - 0.5f) + 0.0625f;
-        const float inv = 1.0f / d;
-        const float t1 = (lo - vr.c[a]) * inv, t2 = (hi - vr.c[a]) * inv;
-        tmin = fmaxf(tmin, fminf(t1, t2));
-        tmax = fminf(tmax, fmaxf(t1, t2));
+    BrickHull h;
+    float wmin = 3e38f, wmax = -3e38f, big = 0.0f;
+    for (int k = 0; k < 8; ++k) {
+        const float x = (k & 1) ? g.hi[0] : g.lo[0];
+        const float y = (k & 2) ? g.hi[1] : g.lo[1];
+        const float z = (k & 4) ? g.hi[2] : g.lo[2];
+        const float w = P[8] * x + P[9] * y + P[10] * z + P[11];
+        const float iw = 1.0f / w;
+        h.u[k] = (P[0] * x + P[1] * y + P[2] * z + P[3]) * iw;
+        h.v[k] = (P[4] * x + P[5] * y + P[6] * z + P[7]) * iw;
+        wmin = fminf(wmin, w);
+        wmax = fmaxf(wmax, w);
+        big = fmaxf(big, fmaxf(fabsf(h.u[k]), fabsf(h.v[k])));
     }
-    return !(tmax < tmin);
+    h.m = 0.0625f + big * 0.000244140625f;
+    h.narrow = wmax > 0.0f && wmin > wmax * 0.0009765625f && big < 1e9f;
+    return h;
+}
+
+// Columns [c0, c1] of detector row r whose pixel centres can lie in the
+// region's projection: the hull's extent along the row over the band
+// |v - (r + 1/2)| <= m (its corners inside the band and the crossings of the
+// band's two edges with the twelve projected box edges -- the hull's outline
+// runs along some of them), widened by m and cut to [c_lo, c_hi].  A hull
+// that does not touch the band gives c1 < c0; one that is not narrow gives
+// [c_lo, c_hi].  Crossings are clamped between their edge's end points, so a
+// nearly horizontal edge cannot throw one far off.
+__host__ __device__ inline void brick_row_span(const BrickHull& h, int r, int c_lo, int c_hi,
+                                               int& c0, int& c1)
+{
+    c0 = c_lo;
+    c1 = c_hi;
+    if (!h.narrow) return;
+    const float vc = (float)r + 0.5f, b0 = vc - h.m, b1 = vc + h.m;
+    float umin = 3e38f, umax = -3e38f;
+    for (int k = 0; k < 8; ++k) {
+        if (h.v[k] >= b0 && h.v[k] <= b1) {
+            umin = fminf(umin, h.u[k]);
+            umax = fmaxf(umax, h.u[k]);
+        }
+    }
+    for (int a = 0; a < 3; ++a) {
+        const int bit = 1 << a;
+        for (int k = 0; k < 8; ++k) {
+            if (k & bit) continue;
+            const int l = k | bit;                     // the edge (k, l) along axis a
+            const float va = h.v[k], vb = h.v[l], ua = h.u[k], ub = h.u[l];
+            for (int e = 0; e < 2; ++e) {
+                const float yb = e ? b1 : b0;
+                if ((va - yb) * (vb - yb) < 0.0f) {
+                    const float x = ua + (yb - va) * (ub - ua) / (vb - va);
+                    const float xc = fminf(fmaxf(x, fminf(ua, ub)), fmaxf(ua, ub));
+                    umin = fminf(umin, xc);
+                    umax = fmaxf(umax, xc);
+                }
+            }
+        }
+    }
+    if (!(umin <= umax)) {
+        c1 = c0 - 1;
+        return;
+    }
+    const float f0 = ceilf(umin - h.m - 0.5f), f1 = floorf(umax + h.m - 0.5f);
+    if (f1 < (float)c_lo || f0 > (float)c_hi) {
+        c1 = c0 - 1;
+        return;
+    }
+    c0 = f0 > (float)c_lo ? (int)f0 : c_lo;
+    c1 = f1 < (float)c_hi ? (int)f1 : c_hi;
 }
 
 // fp32 value of a 64-bit integer from its two words: the high word's

@@ -205,7 +205,7 @@ inline size_t ray_block_max_bytes(int n_views, int C, int H, int W)
 }
 
 // ... then 96 bytes per view (its fp32 projection and index-space rays).
-inline size_t brick_view_bytes(int n_views) { return ((size_t)n_views * 96 + 255) & ~(size_t)255; }
+inline size_t brick_view_bytes(int n_views) { return ((size_t)n_views * 48 + 255) & ~(size_t)255; }
 
 inline BackwardRead plan_backward(int n_volumes, int C, int nz, int ny, int nx, int elem_bytes,
                                   int n_views, int H, int W, int N, int mode, int clip,

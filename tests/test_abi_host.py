@@ -269,14 +269,14 @@ def test_render_empty_call_and_workspace_queries():
     # Beer-Lambert / line integral with the box clip, views sparse against the
     # voxels (under 4 samples per cell from one view): the brick-owned backward's
     # ray records (64 bytes per ray of each (view, channel) pair), one float
-    # per 256 rays and 96 bytes per view (its projection and index-space rays),
+    # per 256 rays and 48 bytes per view (its fp32 projection),
     # each rounded to 256 bytes; denser views and near/far: none
     rnd = lambda b: (b + 255) // 256 * 256
-    assert q(1, 2, 8, 8, 8, 0, 1, 4, 4, 8, 0, 0, 3, 1) == rnd(2 * 16 * 64) + rnd(4) + rnd(96)
-    assert q(2, 1, 8, 8, 8, 0, 6, 40, 40, 1, 1, 0, 0, 1) == rnd(6 * 1600 * 64) + rnd(38 * 4) + rnd(6 * 96)
+    assert q(1, 2, 8, 8, 8, 0, 1, 4, 4, 8, 0, 0, 3, 1) == rnd(2 * 16 * 64) + rnd(4) + rnd(48)
+    assert q(2, 1, 8, 8, 8, 0, 6, 40, 40, 1, 1, 0, 0, 1) == rnd(6 * 1600 * 64) + rnd(38 * 4) + rnd(6 * 48)
     assert q(1, 1, 8, 8, 8, 0, 1, 32, 32, 16, 0, 0, 0, 1) == 0      # 22 samples per view-cell
     assert q(1, 1, 8, 8, 8, 0, 1, 4, 4, 8, 0, 1, 0, 1) == 0         # near/far
-    assert drr.drr_workspace_bytes(8, 8, 8, 0, 3, 5, 7, 8, 1) == rnd(105 * 64) + rnd(4) + rnd(3 * 96)
+    assert drr.drr_workspace_bytes(8, 8, 8, 0, 3, 5, 7, 8, 1) == rnd(105 * 64) + rnd(4) + rnd(3 * 48)
     assert q(1, 1, 8, 8, 8, 0, 4, 8, 8, 16, 2, 0, 0, 1) == 8 * 8 * 7 * 2 * 4 + bound
     assert q(1, 1, 8, 8, 8, 1, 4, 8, 8, 16, 2, 0, 0, 1) == 8 * 8 * 7 * 2 * 2 + bound
     assert q(1, 1, 8, 8, 8, 1, 4, 8, 8, 16, 2, 0, 3, 1) == 8 * 8 * 7 * 2 * 4 + bound
