@@ -387,16 +387,16 @@ __global__ __launch_bounds__(kBrickThreads, 4) void drr_brick_scatter_kernel(
     float cmax = 0.0f;
     for (int v0 = 0; v0 < bt.vpv; v0 += kViewChunk) {
         const int count = min(kViewChunk, bt.vpv - v0);
-        brick_chunk(views, H, W, reg, first_view + v0, count, cand, red);
-        for (int v = 0; v < count; ++v) {
+        const int n_rows = brick_chunk(views, H, W, reg, first_view + v0, count, cand, red);
+        // one rectangle row per thread, over all views of the chunk
+        for (int p = t; p < n_rows; p += kBrickThreads) {
+            const int v = cand.view_of_row(p, count);
             const int w = rect[3 * v + 2];
-            const int h = start[v + 1] - start[v];
             const long long pair = (long long)(first_view + v0 + v) * bt.C + ch;
-            for (int row = t; row < h; row += kBrickThreads) {
-                const long long lin = (pair * H + rect[3 * v] + row) * W + rect[3 * v + 1];
-                const long long b0 = lin >> 8, b1 = (lin + w - 1) >> 8;
-                for (long long k = b0; k <= b1; ++k) cmax = fmaxf(cmax, block_max[k]);
-            }
+            const long long lin =
+                (pair * H + rect[3 * v] + (p - start[v])) * W + rect[3 * v + 1];
+            const long long b0 = lin >> 8, b1 = (lin + w - 1) >> 8;
+            for (long long k = b0; k <= b1; ++k) cmax = fmaxf(cmax, block_max[k]);
         }
         __syncthreads();
     }
