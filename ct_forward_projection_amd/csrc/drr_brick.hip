@@ -142,7 +142,8 @@ __device__ inline int block_exclusive_scan(int v, int* red, int& excl)
 }
 
 // The same for two ints at once (a and b, exclusive sums in ea and eb);
-// returns both totals.
+// returns both totals.  It ends without a barrier: `red` must not be written
+// again before the next one (the brick kernel's rounds have two in between).
 __device__ inline int2 block_exclusive_scan2(int a, int b, int* red, int& ea, int& eb)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -171,7 +172,6 @@ __device__ inline int2 block_exclusive_scan2(int a, int b, int* red, int& ea, in
     }
     ea = base_a + ia - a;
     eb = base_b + ib - b;
-    __syncthreads();
     return make_int2(tot_a, tot_b);
 }
 
