@@ -117,16 +117,26 @@ __global__ __launch_bounds__(64) void drr_brick_views_kernel(Intrinsics K,
 constexpr int kBrickThreads = 256;
 constexpr int kViewChunk = 64;      // views whose pixel rectangles and rays sit in LDS at once
 
+// Inclusive prefix sum over a wave64 by DPP lane moves (no LDS round trips):
+// shifts by 1, 2, 4 and 8 lanes within each row of 16 (Hillis-Steele), then
+// the last lane of rows 0 and 2 added to rows 1 and 3, and lane 31 added to
+// rows 2 and 3.  A lane the move has no source for adds 0.
+__device__ inline int wave_inclusive_scan(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return x;
+}
+
 // Workgroup-wide exclusive prefix sum of one int per thread; returns the total.
 __device__ inline int block_exclusive_scan(int v, int* red, int& excl)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += t;
-    }
+    const int incl = wave_inclusive_scan(v);
     if (lane == 63) red[wave] = incl;
     __syncthreads();
     int base = 0, total = 0;
@@ -147,15 +157,7 @@ __device__ inline int block_exclusive_scan(int v, int* red, int& excl)
 __device__ inline int2 block_exclusive_scan2(int a, int b, int* red, int& ea, int& eb)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int ia = a, ib = b;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int ta = __shfl_up(ia, off, 64), tb = __shfl_up(ib, off, 64);
-        if (lane >= off) {
-            ia += ta;
-            ib += tb;
-        }
-    }
+    const int ia = wave_inclusive_scan(a), ib = wave_inclusive_scan(b);
     if (lane == 63) {
         red[2 * wave] = ia;
         red[2 * wave + 1] = ib;
