@@ -117,21 +117,6 @@ __global__ __launch_bounds__(64) void drr_brick_views_kernel(Intrinsics K,
 constexpr int kBrickThreads = 256;
 constexpr int kViewChunk = 64;      // views whose pixel rectangles and rays sit in LDS at once
 
-// Inclusive prefix sum over a wave64 by DPP lane moves (no LDS round trips):
-// shifts by 1, 2, 4 and 8 lanes within each row of 16 (Hillis-Steele), then
-// the last lane of rows 0 and 2 added to rows 1 and 3, and lane 31 added to
-// rows 2 and 3.  A lane the move has no source for adds 0.
-__device__ inline int wave_inclusive_scan(int x)
-{
-    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
-    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
-    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
-    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
-    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
-    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
-    return x;
-}
-
 // Workgroup-wide exclusive prefix sum of one int per thread; returns the total.
 __device__ inline int block_exclusive_scan(int v, int* red, int& excl)
 {

@@ -304,6 +304,54 @@ __device__ inline void cell_of(const VolumeDesc& V, int64_t qx, int64_t qy, int6
 // Map a hardware workgroup id to a logical tile so that the workgroups one XCD
 // receives (ids x, x + 8, x + 16, ...) own one contiguous run of tiles: every
 // XCD's L2 then serves a compact part of the detector, and so of the volume.
+// Inclusive prefix sum over a wave64 by DPP lane moves (no LDS round trips):
+// shifts by 1, 2, 4 and 8 lanes within each row of 16 (Hillis-Steele), then
+// the last lane of rows 0 and 2 added to rows 1 and 3, and lane 31 added to
+// rows 2 and 3.  A lane the move has no source for adds 0.
+__device__ inline int wave_inclusive_scan(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+    return x;
+}
+
+// Minimum over a wave64, left in lane 63 (the same DPP moves; a lane without
+// a source takes INT_MAX), then read from that lane.
+__device__ inline int wave_min(int x)
+{
+    constexpr int kMax = 0x7fffffff;
+    x = min(x, __builtin_amdgcn_update_dpp(kMax, x, 0x111, 0xf, 0xf, false));
+    x = min(x, __builtin_amdgcn_update_dpp(kMax, x, 0x112, 0xf, 0xf, false));
+    x = min(x, __builtin_amdgcn_update_dpp(kMax, x, 0x114, 0xf, 0xf, false));
+    x = min(x, __builtin_amdgcn_update_dpp(kMax, x, 0x118, 0xf, 0xf, false));
+    x = min(x, __builtin_amdgcn_update_dpp(kMax, x, 0x142, 0xa, 0xf, false));
+    x = min(x, __builtin_amdgcn_update_dpp(kMax, x, 0x143, 0xc, 0xf, false));
+    return __builtin_amdgcn_readlane(x, 63);
+}
+
+// Sum of a float over a wave64 the same way (a lane without a source adds 0).
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_move(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf,
+                                                      false));
+}
+
+__device__ inline float wave_sum(float x)
+{
+    x += dpp_move<0x111, 0xf>(x);
+    x += dpp_move<0x112, 0xf>(x);
+    x += dpp_move<0x114, 0xf>(x);
+    x += dpp_move<0x118, 0xf>(x);
+    x += dpp_move<0x142, 0xa>(x);
+    x += dpp_move<0x143, 0xc>(x);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 __device__ inline int xcd_contiguous_tile(int bid, int nblocks)
 {
     const int xcd = bid % kNumXcd, idx = bid / kNumXcd;

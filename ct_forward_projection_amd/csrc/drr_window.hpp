@@ -122,10 +122,7 @@ struct BoxAddr {
 __device__ inline void block_min6(int v[6], int* red, int* out)
 {
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) v[i] = min(v[i], __shfl_xor(v[i], off, 64));
-    }
+    for (int i = 0; i < 6; ++i) v[i] = wave_min(v[i]);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if (lane == 0) {
 #pragma unroll
@@ -143,11 +140,8 @@ __device__ inline void block_min6(int v[6], int* red, int* out)
 // Workgroup-wide sums of two floats.
 __device__ inline void block_sum2(float& a, float& b, float* red)
 {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        a += __shfl_xor(a, off, 64);
-        b += __shfl_xor(b, off, 64);
-    }
+    a = wave_sum(a);
+    b = wave_sum(b);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     if (lane == 0) {
         red[2 * wave] = a;
