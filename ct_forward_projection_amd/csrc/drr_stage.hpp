@@ -103,6 +103,23 @@ __device__ inline void stage_fill(float* box, int n, __amdgpu_buffer_rsrc_t rs,
         // every entry is a voxel: no clamping, and the element offset steps
         // with the walk
         BoxAddr ba(bw, lo, (uint32_t)V.n[0], (uint32_t)V.n[0] * (uint32_t)V.n[1]);
+        if constexpr (sizeof(T) == 4 && !TF) {
+            // fp32 as it is: the loads write LDS themselves (buffer_load ...
+            // lds puts lane l's dword at the wave's base + 4 l, and the
+            // entries i of one wave and round are consecutive), so no value
+            // passes through registers; they complete before the caller's
+            // barrier
+            for (; i < n; i += kBlock) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rs, (__attribute__((address_space(3))) void*)(box + (i & ~63)), 4,
+                    ba.addr * 4u, 0, 0, 0);
+                int cx, cy;
+                bw.next(cx, cy);
+                ba.next(cx, cy);
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            return;
+        }
         auto value = [&](uint32_t off) {
             const float v = load_one<T>(rs, off * (uint32_t)sizeof(T));
             if constexpr (TF) {
