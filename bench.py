@@ -441,8 +441,11 @@ class RenderCase:
         self.grad = torch.empty(vol.shape, device=dev)
         wf = drr.drr_render_workspace_bytes(B, C, nz, ny, nx, dt, V, H, Wd, N, mode, clip, nk, 0)
         wb = drr.drr_render_workspace_bytes(B, C, nz, ny, nx, dt, V, H, Wd, N, mode, clip, nk, 1)
+        wp = drr.drr_render_workspace_bytes(B, C, nz, ny, nx, dt, V, H, Wd, N, mode, clip, nk, 2)
         self.ws_f = torch.empty(wf, dtype=torch.uint8, device=dev) if wf else None
         self.ws_b = torch.empty(wb, dtype=torch.uint8, device=dev) if wb else None
+        self.ws_p = torch.empty(wp, dtype=torch.uint8, device=dev)
+        self.grad_poses = torch.empty((V, 3, 4), device=dev)
         self.samples = V * C * H * Wd * N
         self.read_elem = 4 if (transfer is not None or dt == drr.F32) else 2
         self.plan = read_plan(wf, B, C, nz, ny, nx, self.read_elem, V, H, Wd, N, clip, nk)
@@ -459,6 +462,12 @@ class RenderCase:
         drr.drr_render_backward_volume(self.vol, tuple(self.vol.shape), 0, sp, K, P, H, Wd, N,
                                        mode, self.g, self.out, self.aux, f, clip, margin, tf,
                                        grad_volume=self.grad, workspace=self.ws_b)
+
+    def pose_backward(self):
+        import ct_forward_projection_amd as drr
+        sp, K, P, H, Wd, N, mode, f, clip, margin, tf = self.args
+        drr.drr_render_backward_pose(self.vol, sp, K, P, H, Wd, N, mode, self.g, f, clip, margin,
+                                     tf, grad_poses=self.grad_poses, workspace=self.ws_p)
 
 
 def frontend_lines(dev):
@@ -500,8 +509,9 @@ def frontend_lines(dev):
                        30.0, transfer)
         c.forward()
         c.backward()
+        c.pose_backward()
         torch.cuda.synchronize()
-        f_ms, b_ms = time_graph([c.forward, c.backward])
+        f_ms, b_ms, p_ms = time_graph([c.forward, c.backward, c.pose_backward])
         views = P.shape[0] * vol.shape[1]
         line = {"views_x_channels": views, "detector": [w.det_h, w.det_w],
                 "n_samples": w.n_samples, "volumes": vol.shape[0], "channels": vol.shape[1],
@@ -514,7 +524,9 @@ def frontend_lines(dev):
                 "forward_alu_frac_nominal": round(c.samples * OPS_FORWARD_SAMPLE / (f_ms * 1e-3)
                                                   / 1e12 / ALU_PEAK_TOPS, 4),
                 "backward_ms": round(b_ms, 4),
-                "backward_gsamples_s": round(c.samples / b_ms / 1e6, 1)}
+                "backward_gsamples_s": round(c.samples / b_ms / 1e6, 1),
+                "pose_backward_ms": round(p_ms, 4),
+                "pose_backward_gsamples_s": round(c.samples / p_ms / 1e6, 1)}
         lines[name] = line
         log(f"front end {name}: {line}")
         del c
