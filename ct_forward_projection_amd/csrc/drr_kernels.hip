@@ -1079,6 +1079,8 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                 // (one coefficient per ray), at +-1/2 with its sign, which lets
                 // the window conversion truncate (see to_window)
                 const float start = REBASE ? copysignf(0.5f, ys) : 0.0f;
+                const float c96 = ys * 1.2621774483536189e-29f;     // ys 2^-96
+                const float c64 = ys * 5.421010862427522e-20f;      // ys 2^-64
                 float acc[8];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[i] = start;
@@ -1101,8 +1103,11 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                         base = w0 + 4 * (ix - lo[0]) + __mul24(iy - lo[1], wy4) +
                                __mul24(iz - lo[2], wz4);
                     }
-                    const float tx = fixed_frac(qx), ty = fixed_frac(qy);
-                    const float tz = fixed_frac(qz);
+                    // fractions: as they are (REBASE: times 2^32, the scale folded
+                    // into the coefficient) or in [0, 1)
+                    const float tx = REBASE ? (float)(uint32_t)qx : fixed_frac(qx);
+                    const float ty = REBASE ? (float)(uint32_t)qy : fixed_frac(qy);
+                    const float tz = REBASE ? (float)(uint32_t)qz : fixed_frac(qz);
                     serial_step_after(qx, qy, qz, tx, ty, tz);
                     qx += R.dq[0]; qy += R.dq[1]; qz += R.dq[2];
                     // consecutive samples in one cell are summed in registers;
@@ -1112,7 +1117,10 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                         window_add_at<REBASE>((uint32_t)pbase, wy4, wz4, acc);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) acc[i] = same ? acc[i] : start;
-                    add_weights8(tx, ty, tz, c, acc);
+                    if constexpr (REBASE)
+                        add_weights8_scaled(tx, ty, tz, c96, c64, acc);
+                    else
+                        add_weights8(tx, ty, tz, c, acc);
                     pbase = base;
                 };
                 // without compositing every lane walks all S samples; when the

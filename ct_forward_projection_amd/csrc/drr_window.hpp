@@ -60,6 +60,30 @@ __device__ inline void add_weights8(float fx, float fy, float fz, float c, float
     acc[7] = fmaf(w11, fx, acc[7]);
 }
 
+// The same from fractions times 2^32 (Fx = 2^32 fx, exactly the low word of a
+// 32.32 position as a float: one conversion, no scaling per sample), with the
+// coefficient passed as c 2^-96 and c 2^-64: every product then carries the
+// scale it needs, the complements are 2^32 - F (rounded as 1 - f would be),
+// and the eight additions equal c w_corner.  A coefficient below 2^-30 (in
+// window units) may lose precision to subnormals, far below the window's unit.
+__device__ inline void add_weights8_scaled(float Fx, float Fy, float Fz, float c96, float c64,
+                                           float acc[8])
+{
+    constexpr float kTwo32 = 4294967296.0f;
+    const float gx = kTwo32 - Fx, gy = kTwo32 - Fy;
+    const float wz1 = c96 * Fz, wz0 = fmaf(-c96, Fz, c64);      // c fz 2^-64, c (1 - fz) 2^-64
+    const float w11 = wz1 * Fy, w10 = wz1 * gy;                 // times 2^32 in y
+    const float w01 = wz0 * Fy, w00 = wz0 * gy;
+    acc[0] = fmaf(w00, gx, acc[0]);
+    acc[1] = fmaf(w00, Fx, acc[1]);
+    acc[2] = fmaf(w01, gx, acc[2]);
+    acc[3] = fmaf(w01, Fx, acc[3]);
+    acc[4] = fmaf(w10, gx, acc[4]);
+    acc[5] = fmaf(w10, Fx, acc[5]);
+    acc[6] = fmaf(w11, gx, acc[6]);
+    acc[7] = fmaf(w11, Fx, acc[7]);
+}
+
 // Position (x, y, z) of entry i = threadIdx.x + n kBlock of a box of
 // ext[0] x ext[1] x ... entries (x fastest), advanced kBlock entries per
 // step with carries instead of divisions.
