@@ -170,8 +170,6 @@ def test_render_bf16_transfer_mapped_linear(dev, mode):
     ref, ref_tau = oracle.render(vol_r, spacing, K, poses, H, Wd, N, mode, **kw)
     ref_g = oracle.render_adjoint(vol_r, spacing, K, poses, H, Wd, N, mode, g, **kw)
     check(img, tau, grad, ref, ref_tau, ref_g, f"bf16 mapped linear m{mode}")
-    if mode == ALPHA:
-        return
     v = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
     gp = drr.drr_render_backward_pose(v, spacing, K, torch.from_numpy(poses).to(dev), H, Wd, N,
                                       mode, torch.from_numpy(g).to(dev), 30.0, BOX, 0.0, transfer)
@@ -202,8 +200,6 @@ def test_render_sparse_rays_read_the_volume(dev, mode, tf):
     ref, ref_tau = oracle.render(vol, spacing, K, poses, H, Wd, N, mode, **kw)
     ref_g = oracle.render_adjoint(vol, spacing, K, poses, H, Wd, N, mode, g, **kw)
     check(img, tau, grad, ref, ref_tau, ref_g, f"sparse m{mode} tf{int(tf)}")
-    if mode == ALPHA:
-        return
     gp = drr.drr_render_backward_pose(torch.from_numpy(vol).to(dev), spacing, K,
                                       torch.from_numpy(poses).to(dev), H, Wd, N, mode,
                                       torch.from_numpy(g).to(dev), f, BOX, 0.0, transfer)
@@ -226,8 +222,8 @@ def test_render_sparse_rays_read_the_volume(dev, mode, tf):
 def test_render_thin_volumes(dev, shape, det, N, plan, tf):
     """Volumes two (or one) voxels thick at the reuse that picks z-pairs: every
     x and z weight is pinned or edge-clamped somewhere; forward, volume and pose
-    gradients against the oracle, both modes, with and without the transfer
-    function."""
+    gradients against the oracle, all three modes, with and without the
+    transfer function."""
     seed = 370 + shape[0] + 3 * shape[2] + tf
     vol, spacing, K, poses, H, Wd, N, g = problem(seed, shape=shape, det=det, N=N, tf=tf)
     transfer = knots(2) if tf else None
@@ -238,7 +234,7 @@ def test_render_thin_volumes(dev, shape, det, N, plan, tf):
         expected = "mapped linear" if plan == "caller's volume" else "mapped " + plan
     assert name == expected
     f = 30.0 if tf else 1.3
-    for mode in (BL, RAW):
+    for mode in (BL, RAW, ALPHA):
         img, tau, grad = run_gpu(dev, vol, spacing, K, poses, H, Wd, N, mode, f, BOX, 0.0,
                                  transfer, g)
         kw = dict(density_factor=f, clip=BOX, margin=0.0, transfer=transfer)
