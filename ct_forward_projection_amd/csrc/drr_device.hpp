@@ -257,6 +257,17 @@ __device__ inline uint32_t fixed_floor_x4_add(int64_t q, uint32_t off)
     return r;
 }
 
+// a b + c for a, b < 2^24 in one v_mad_u32_u24, with b a wave-uniform value
+// (an SGPR operand).  Left to itself the compiler keeps a uniform c in an SGPR
+// as well, which the instruction cannot take beside b, and spends a multiply
+// and a three-way add instead.
+__device__ inline uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c)
+{
+    uint32_t r;
+    asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(b), "v"(c));
+    return r;
+}
+
 __device__ inline float fixed_frac(int64_t q)
 {
     return (float)(uint32_t)q * 2.3283064365386963e-10f;  // 2^-32

@@ -1090,7 +1090,10 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                     float c = ys;
                     int base;
                     if constexpr (REBASE) {
-                        base = (int)fixed_floor_x4_add(qx, w0 + __mul24(fy, wy4) + __mul24(fz, wz4));
+                        // fy, fz >= 0: floors relative to the window corner
+                        base = (int)fixed_floor_x4_add(
+                            qx, mad_u24((uint32_t)fz, (uint32_t)wz4,
+                                        mad_u24((uint32_t)fy, (uint32_t)wy4, (uint32_t)w0)));
                     } else {
                         const int ix = clampi(fx, -1, V.n[0] - 1);
                         const int iy = clampi(fy, -1, V.n[1] - 1);
@@ -1100,8 +1103,11 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                             // a sample with every corner outside the volume adds nothing
                             if (fx != ix || fy != iy || fz != iz) c = 0.0f;
                         }
-                        base = w0 + 4 * (ix - lo[0]) + __mul24(iy - lo[1], wy4) +
-                               __mul24(iz - lo[2], wz4);
+                        // clamped floors lie between the chunk's clamped end
+                        // floors (clamping is monotone), so each is >= lo
+                        base = (int)mad_u24((uint32_t)(iz - lo[2]), (uint32_t)wz4,
+                                            mad_u24((uint32_t)(iy - lo[1]), (uint32_t)wy4,
+                                                    (uint32_t)(w0 + 4 * (ix - lo[0]))));
                     }
                     // fractions: as they are (REBASE: times 2^32, the scale folded
                     // into the coefficient) or in [0, 1)
