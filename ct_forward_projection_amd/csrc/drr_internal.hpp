@@ -204,7 +204,7 @@ inline size_t ray_block_max_bytes(int n_views, int C, int H, int W)
     return (((rays + 255) / 256) * 4 + 255) & ~(size_t)255;
 }
 
-// ... then 96 bytes per view (its fp32 projection and index-space rays).
+// ... then 48 bytes per view (its fp32 projection).
 inline size_t brick_view_bytes(int n_views) { return ((size_t)n_views * 48 + 255) & ~(size_t)255; }
 
 inline BackwardRead plan_backward(int n_volumes, int C, int nz, int ny, int nx, int elem_bytes,
@@ -295,6 +295,10 @@ hipError_t launch_siddon_forward(const LaunchArgs& a, const void* vol, int dtype
                                  float* s_out, hipStream_t stream);
 hipError_t launch_siddon_backward(const LaunchArgs& a, const float* grad_out, const float* s_in,
                                   float* grad, hipStream_t stream);
+// Its brick-owned form (drr_brick.hip), for views sparse against the voxels:
+// writes every voxel of the gradient itself.
+hipError_t launch_siddon_brick_backward(const LaunchArgs& a, const float* grad_out,
+                                        const float* s_in, float* grad, hipStream_t stream);
 
 // Pose gradient: the march of the forward (same read plan: the caller's, mapped
 // or corner-cell volumes in `read_buf`) with gradient accumulators; `acc` holds

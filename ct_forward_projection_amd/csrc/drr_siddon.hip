@@ -26,115 +26,10 @@
 #include "drr_device.hpp"
 #include "drr_internal.hpp"
 #include "drr_sample.hpp"
+#include "drr_siddon.hpp"
 #include "drr_window.hpp"
 
 namespace drr {
-
-// Walk state of one ray.  Axis a's next plane crossing is tn[a] =
-// p[a] k[a] + b[a]; i is the current voxel.
-struct SiddonRay {
-    double C[3], d[3];
-    double k[3], b[3];
-    double t0, t1;
-    double tn[3];
-    int p[3], i[3], step[3];
-};
-
-__device__ inline double plane_crossing(const SiddonRay& S, int a, int p)
-{
-    return fma((double)p, S.k[a], S.b[a]);
-}
-
-// Ray through pixel (r, c) (unit direction as in ray_setup), clipped to the box
-// by the same plane expression the walk uses, and the walk's start: the voxel
-// holding the entry point (index clamped, so a point on a face belongs to the
-// boundary voxel) and each axis' first crossing ahead.
-__device__ inline bool siddon_setup(const ViewGeom& G, const VolumeDesc& V, int r, int c,
-                                    SiddonRay& S)
-{
-    const double u = (double)c + 0.5, v = (double)r + 0.5;
-    double w[3];
-#pragma unroll
-    for (int a = 0; a < 3; ++a) w[a] = G.M[a * 3 + 0] * u + G.M[a * 3 + 1] * v + G.M[a * 3 + 2];
-    const double inv_len = 1.0 / sqrt(w[0] * w[0] + w[1] * w[1] + w[2] * w[2]);
-    double t_entry = -__builtin_inf(), t_exit = __builtin_inf();
-    bool inside = true;
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-        S.C[a] = G.C[a];
-        S.d[a] = w[a] * inv_len;
-        if (S.d[a] == 0.0) {
-            S.k[a] = 0.0;
-            S.b[a] = __builtin_inf();
-            inside = inside && !(G.C[a] < -V.half_e[a] || G.C[a] > V.half_e[a]);
-        } else {
-            const double inv = 1.0 / S.d[a];
-            S.k[a] = V.s[a] * inv;
-            S.b[a] = (-V.half_e[a] - G.C[a]) * inv;
-            const double t_lo = S.b[a];
-            const double t_hi = plane_crossing(S, a, V.n[a]);
-            t_entry = fmax(t_entry, fmin(t_lo, t_hi));
-            t_exit = fmin(t_exit, fmax(t_lo, t_hi));
-        }
-    }
-    S.t0 = fmax(t_entry, 0.0);
-    S.t1 = t_exit;
-    if (!inside || !(S.t1 > S.t0)) return false;
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-        const double ua = (S.C[a] + S.t0 * S.d[a] + V.half_e[a]) * V.inv_s[a];
-        const double fa = fmin(fmax(floor(ua), 0.0), (double)(V.n[a] - 1));
-        S.i[a] = (int)fa;
-        if (S.d[a] > 0.0) {
-            S.step[a] = 1;
-            S.p[a] = S.i[a] + 1;
-            S.tn[a] = plane_crossing(S, a, S.p[a]);
-        } else if (S.d[a] < 0.0) {
-            S.step[a] = -1;
-            S.p[a] = S.i[a];
-            S.tn[a] = plane_crossing(S, a, S.p[a]);
-        } else {
-            S.step[a] = 0;
-            S.p[a] = 0;
-            S.tn[a] = __builtin_inf();
-        }
-    }
-    return true;
-}
-
-// The axis whose crossing comes first (x before y before z on ties).
-struct NextAxis {
-    bool x, y;          // z when neither
-    double t;
-};
-
-__device__ inline NextAxis next_axis(const SiddonRay& S)
-{
-    NextAxis m;
-    m.x = S.tn[0] <= S.tn[1] && S.tn[0] <= S.tn[2];
-    m.y = !m.x && S.tn[1] <= S.tn[2];
-    m.t = m.x ? S.tn[0] : (m.y ? S.tn[1] : S.tn[2]);
-    return m;
-}
-
-// Cross the plane of the chosen axis: the voxel index and that axis' next
-// crossing move on.  Returns false when the walk leaves the volume.
-__device__ inline bool advance(SiddonRay& S, const NextAxis& m, const VolumeDesc& V)
-{
-    const bool z = !m.x && !m.y;
-    const bool sel[3] = {m.x, m.y, z};
-    bool in = true;
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-        if (sel[a]) {
-            S.i[a] += S.step[a];
-            S.p[a] += S.step[a];
-            S.tn[a] = plane_crossing(S, a, S.p[a]);
-            in = (unsigned)S.i[a] < (unsigned)V.n[a];
-        }
-    }
-    return in;
-}
 
 // Forward.  Pieces are produced eight at a time (walk only), then their eight
 // loads are issued together, then accumulated into four partial sums.  Loads of
@@ -392,17 +287,22 @@ hipError_t launch_siddon_forward(const LaunchArgs& a, const void* vol, int dtype
 hipError_t launch_siddon_backward(const LaunchArgs& a, const float* grad_out, const float* s_in,
                                   float* grad, hipStream_t stream)
 {
+    // chunks of the ray: about one voxel along the longest axis each
+    const int M = max(a.V.n[0], max(a.V.n[1], a.V.n[2]));
+    // pieces per ray ~ M: the same density measure as the trilinear scatter
+    const double cells = (double)(a.V.n[0] + 1) * (a.V.n[1] + 1) * (a.V.n[2] + 1);
+    const double view_reuse = (double)a.H * a.W * M / cells;
+    // views sparse against the voxels: the brick-owned backward, which writes
+    // every voxel itself (no fill, no global atomics)
+    if (view_reuse < kBrickMaxViewReuse)
+        return launch_siddon_brick_backward(a, grad_out, s_in, grad, stream);
     hipError_t e = launch_fill(grad, (size_t)a.V.n[0] * a.V.n[1] * a.V.n[2], stream);
     if (e != hipSuccess) return e;
     const int tiles_x = (a.W + kTile - 1) / kTile, tiles_y = (a.H + kTile - 1) / kTile;
     const int tiles_per_view = tiles_x * tiles_y, n_tiles = tiles_per_view * a.n_views;
     if (n_tiles == 0) return hipSuccess;
-    // chunks of the ray: about one voxel along the longest axis each
-    const int M = max(a.V.n[0], max(a.V.n[1], a.V.n[2]));
     const dim3 grid(n_tiles), block(kBlock);
-    // pieces per ray ~ M: the same density measure as the trilinear scatter
-    const double cells = (double)(a.V.n[0] + 1) * (a.V.n[1] + 1) * (a.V.n[2] + 1);
-    const int cap = window_cap((double)a.H * a.W * M / cells);
+    const int cap = window_cap(view_reuse);
     const size_t lds = (size_t)cap * sizeof(int);
     if (a.mode == kBeerLambert)
         hipLaunchKernelGGL((drr_siddon_scatter_kernel<kBeerLambert>), grid, block, lds, stream,

@@ -150,8 +150,11 @@ int drr_forward_no_alloc(const void *volume, int dtype, int nz, int ny, int nx,
  *   line_integral device, same layout; required for Beer-Lambert, ignored (may be
  *                 NULL) for the line integral
  *   grad_volume   device, nz*ny*nx floats, OVERWRITTEN (zeroed, then accumulated)
- * The volume itself is not needed.  Accumulation uses fp32 atomics, so the
- * result may differ between runs in the last bits. */
+ * The volume itself is not needed.  Views sparse against the voxels (fewer
+ * than four samples per cell from one view) run brick by brick: each voxel is
+ * written once from exact fixed-point sums, the same on every run.  Denser
+ * views accumulate with fp32 atomics, so the result may differ between runs in
+ * the last bits. */
 int drr_backward_volume(int nz, int ny, int nx, const float *spacing, const float *K,
                         const float *poses, int n_views, int det_h, int det_w, int n_samples,
                         int mode, const float *grad_out, const float *line_integral,
@@ -202,8 +205,11 @@ int drr_forward_siddon(const void *volume, int dtype, int nz, int ny, int nx,
  * (line integral; this is A^T grad_out for the same A as the forward).
  *   grad_out, line_integral, grad_volume: as drr_backward_volume (grad_volume
  *                 is OVERWRITTEN)
- * The volume itself is not needed.  Accumulation uses fp32 atomics, so the
- * result may differ between runs in the last bits. */
+ * The volume itself is not needed.  Views sparse against the voxels (fewer
+ * than about four pieces per voxel from one view) run brick by brick: each
+ * voxel is written once from exact fixed-point sums, the same on every run.
+ * Denser views accumulate with fp32 atomics, so the result may differ between
+ * runs in the last bits. */
 int drr_backward_volume_siddon(int nz, int ny, int nx, const float *spacing, const float *K,
                                const float *poses, int n_views, int det_h, int det_w, int mode,
                                const float *grad_out, const float *line_integral,
