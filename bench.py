@@ -547,6 +547,7 @@ PROFILE_CASES = {
     "hires2048": (4, False, ("forward",)),
     "helix360": (5, False, ("forward", "backward")),
     "siddon1024": (3, False, ("siddon_forward", "siddon_backward")),
+    "siddon200": (2, False, ("siddon_forward", "siddon_backward")),
 }
 PROFILE_COMMANDS = {
     "trace": "rocprofv3 --kernel-trace --stats -d gpurun_out/prof/{case}/trace -o trace "
@@ -639,7 +640,8 @@ def _kernel_units(short, meta):
         return "cell", (nx + 1) * (ny + 1) * (nz + 1), None, 16 * elem
     if short == "drr_fill_kernel":
         return "voxel", meta["voxels"], None, 4
-    if short in ("drr_siddon_march_kernel", "drr_siddon_scatter_kernel"):
+    if short in ("drr_siddon_march_kernel", "drr_siddon_scatter_kernel",
+                 "drr_siddon_brick_kernel"):
         return "ray-voxel piece", meta.get("siddon_pieces", 0), None, elem
     return None
 
