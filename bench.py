@@ -57,12 +57,39 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(src: str) -> str:
+    """C/C++/HIP source without its comments, whitespace runs collapsed, so
+    that the revision below changes with the code and not with its comments."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":                                   # string or char literal
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_revision() -> str:
+    """Hash of the kernel sources' code (comments and layout excluded): the
+    counters in profiles/ apply only while it is unchanged."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "ct_forward_projection_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

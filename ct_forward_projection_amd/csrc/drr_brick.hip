@@ -3,7 +3,8 @@
 // gradient that adds every sample touching its voxels in LDS and writes them
 // once.  No global atomics, no zero fill, and the sums are exact integers in
 // a fixed-point scale chosen per brick, so the result does not depend on the
-// order of the adds.
+// order of the adds.  The same for the cell-constant (Siddon) backward, at the
+// end of the file.
 //
 // Method (source pages): flashdrr.rendering VolumeRaycaster class text --
 // rendering is differentiable with respect to the volume; diffct 2.1.0
@@ -724,6 +725,11 @@ hipError_t launch_brick_backward(const LaunchArgs& a, const float* grad_out, con
 }
 
 // ------------------------------------------------------- Siddon bricks
+//
+// Method (source pages): diffct 2.1.0, "Why diffct" feature list -- project()
+// and backproject() are an exact adjoint pair for the cell-constant Siddon
+// model, so every voxel receives sum over rays of y l_v, l_v the length of the
+// ray inside it, y = g exp(-s) (Beer-Lambert) or g (line integral).
 //
 // The brick-owned backward of the cell-constant (Siddon) pair, for views sparse
 // against the voxels: one workgroup per brick of B^3 voxels finds the rays that
