@@ -92,7 +92,9 @@ __global__ __launch_bounds__(kBlock) void drr_siddon_march_kernel(
 }
 
 // Backward (matched adjoint of the forward above): every piece adds y l_v to
-// its voxel, y = g exp(-s) (Beer-Lambert) or g (line integral).
+// its voxel, y = g exp(-s) (Beer-Lambert) or g (line integral).  This tile
+// form serves views dense against the voxels; sparse ones take the
+// brick-owned backward (drr_brick.hip).
 //
 // The tile's rays are walked in M common chunks of their own ranges (chunk k of
 // a ray covers t0 + [k, k + S) (t1 - t0) / M).  For each chunk the workgroup
