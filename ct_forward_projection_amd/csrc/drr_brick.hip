@@ -739,13 +739,7 @@ hipError_t launch_brick_backward(const LaunchArgs& a, const float* grad_out, con
 // piece lies in one voxel, so the copy needs no apron, and nothing is read
 // from a workspace: the views' projections and cameras are made per chunk of
 // views in LDS, and each candidate's ray is set up again from its pixel (the
-// forward's fp64 arithmetic).
-//
-// The walk inside a brick starts at t_in, the later of the ray's entry into the
-// volume and its entry into the brick's box, in the voxel past every plane
-// crossed at or before t_in, and ends at t_out.  All crossings come from
-// plane_crossing, so the pieces are the forward's pieces between the same
-// crossings, and every piece of positive length falls in exactly one brick.
+// forward's fp64 arithmetic).  The walk inside a brick: drr_siddon.hpp.
 
 // Brick side and views per chunk of the Siddon bricks: 16^3 int64 sums (32 KB)
 // and 16 views' projections and cameras keep a workgroup's LDS under 40 KB, so
@@ -754,18 +748,6 @@ hipError_t launch_brick_backward(const LaunchArgs& a, const float* grad_out, con
 // 0.99 ms, 16^3 with 16-view chunks 0.92 ms; the tile windows 2.69 ms.
 constexpr int kSiddonBrickSide = 16;
 constexpr int kSiddonViewChunk = 16;
-
-// The brick's voxel box as world coordinates of its bounding planes.
-__device__ inline BrickRegion siddon_brick_region(const VolumeDesc& V, const BrickBox& b)
-{
-    BrickRegion g;
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-        g.lo[a] = (float)((double)b.lo[a] * V.s[a] - V.half_e[a]);
-        g.hi[a] = (float)((double)(b.lo[a] + b.e[a]) * V.s[a] - V.half_e[a]);
-    }
-    return g;
-}
 
 // Views [v0, v0 + count) into LDS, one thread per view: the fp32 projection
 // for the candidate search and the fp64 camera for the rays.
@@ -791,97 +773,6 @@ __device__ inline float siddon_coef(const float* __restrict__ grad_out,
     float y = grad_out[i];
     if (MODE == kBeerLambert) y *= expf(-s_in[i]);
     return y;
-}
-
-// The ray's range [t_in, t_out) inside the brick's box (and the volume's);
-// false when it has none.  An axis the ray runs parallel to keeps the voxel
-// the forward's walk gives it (the one holding the entry point).
-__device__ inline bool siddon_brick_range(SiddonRay& S, const VolumeDesc& V, const BrickBox& b,
-                                          double& t_in, double& t_out)
-{
-    t_in = S.t0;
-    t_out = S.t1;
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-        if (S.step[a] == 0) {
-            S.i[a] = siddon_voxel_at(S, V, a, S.t0, 0, V.n[a] - 1);
-            if (S.i[a] < b.lo[a] || S.i[a] >= b.lo[a] + b.e[a]) return false;
-        } else {
-            const double tl = plane_crossing(S, a, b.lo[a]);
-            const double th = plane_crossing(S, a, b.lo[a] + b.e[a]);
-            t_in = fmax(t_in, fmin(tl, th));
-            t_out = fmin(t_out, fmax(tl, th));
-        }
-    }
-    return t_out > t_in;
-}
-
-// The walk's state at t_in: on each axis the voxel past every plane crossed at
-// or before t_in, and the next plane ahead.  The voxel holding the point at
-// t_in is off by at most one from that (the point and the crossings round
-// differently only within a few ulps of a plane), so one test of the planes on
-// either side settles it.
-__device__ inline void siddon_brick_start(SiddonRay& S, const VolumeDesc& V, const BrickBox& b,
-                                          double t_in)
-{
-#pragma unroll
-    for (int a = 0; a < 3; ++a) {
-        if (S.step[a] == 0) continue;
-        const int lo = b.lo[a], hi = b.lo[a] + b.e[a] - 1;
-        int i = siddon_voxel_at(S, V, a, t_in, lo, hi);
-        const bool below = plane_crossing(S, a, i) <= t_in;       // plane i crossed
-        const bool above = plane_crossing(S, a, i + 1) <= t_in;   // plane i + 1 crossed
-        if (S.step[a] > 0) {
-            i += (above && i < hi) ? 1 : ((!below && i > lo) ? -1 : 0);
-            S.p[a] = i + 1;
-        } else {
-            i += (below && i > lo) ? -1 : ((!above && i < hi) ? 1 : 0);
-            S.p[a] = i;
-        }
-        S.i[a] = i;
-        S.tn[a] = plane_crossing(S, a, S.p[a]);
-    }
-}
-
-// Walks ray S from t_in to t_out through the brick, handing each piece (its
-// voxel's entry in the brick copy, its length; zero for a tie of crossings,
-// which adds nothing) to `add`.  Every crossing before t_out is of a plane
-// inside the brick (t_out is at or before each axis' exit plane, and the
-// crossings of one axis come in plane order), so the voxel stays in the brick;
-// the walk takes no branch per piece: all three next crossings are made and
-// the nearest one's kept.
-template <int B, typename Add>
-__device__ inline void siddon_brick_walk(const SiddonRay& S, const BrickBox& b, double t_in,
-                                         double t_out, Add add)
-{
-    double tn0 = S.tn[0], tn1 = S.tn[1], tn2 = S.tn[2];
-    int p0 = S.p[0], p1 = S.p[1], p2 = S.p[2];
-    int e = (S.i[0] - b.lo[0]) + B * ((S.i[1] - b.lo[1]) + B * (S.i[2] - b.lo[2]));
-    const int ex = S.step[0], ey = B * S.step[1], ez = B * B * S.step[2];
-    double tc = t_in;
-    int guard = b.e[0] + b.e[1] + b.e[2] + 3;
-    for (;;) {
-        // the nearest crossing, x before y before z on ties (as the forward)
-        const bool sx = tn0 <= tn1 && tn0 <= tn2;
-        const bool sy = !sx && tn1 <= tn2;
-        const double mt = sx ? tn0 : (sy ? tn1 : tn2);
-        const double te = mt < t_out ? mt : t_out;
-        const double len = te - tc;
-        add(e, len > 0.0 ? len : 0.0);
-        tc = te > tc ? te : tc;
-        if (!(mt < t_out) || --guard <= 0) break;
-        const int q0 = p0 + S.step[0], q1 = p1 + S.step[1], q2 = p2 + S.step[2];
-        const double n0 = plane_crossing(S, 0, q0), n1 = plane_crossing(S, 1, q1);
-        const double n2 = plane_crossing(S, 2, q2);
-        const bool sz = !sx && !sy;
-        p0 = sx ? q0 : p0;
-        p1 = sy ? q1 : p1;
-        p2 = sz ? q2 : p2;
-        tn0 = sx ? n0 : tn0;
-        tn1 = sy ? n1 : tn1;
-        tn2 = sz ? n2 : tn2;
-        e += sx ? ex : (sy ? ey : ez);
-    }
 }
 
 // Grid: the bricks of the volume.  The fixed-point scale: a piece is at most

@@ -12,6 +12,7 @@
 // only way any kernel evaluates a crossing, so all of them see the same ones.
 #pragma once
 
+#include "drr_brick.hpp"
 #include "drr_device.hpp"
 
 namespace drr {
@@ -26,7 +27,7 @@ struct SiddonRay {
     int p[3], i[3], step[3];
 };
 
-__device__ inline double plane_crossing(const SiddonRay& S, int a, int p)
+__host__ __device__ inline double plane_crossing(const SiddonRay& S, int a, int p)
 {
     return fma((double)p, S.k[a], S.b[a]);
 }
@@ -34,8 +35,8 @@ __device__ inline double plane_crossing(const SiddonRay& S, int a, int p)
 // Ray through pixel (r, c) (unit direction as in ray_setup), clipped to the box
 // by the same plane expression the walk uses: C, d, k, b, t0, t1 and the step
 // of each axis (0 for an axis the ray runs parallel to).  False on a miss.
-__device__ inline bool siddon_clip(const ViewGeom& G, const VolumeDesc& V, int r, int c,
-                                   SiddonRay& S)
+__host__ __device__ inline bool siddon_clip(const ViewGeom& G, const VolumeDesc& V, int r,
+                                            int c, SiddonRay& S)
 {
     const double u = (double)c + 0.5, v = (double)r + 0.5;
     double w[3];
@@ -71,8 +72,8 @@ __device__ inline bool siddon_clip(const ViewGeom& G, const VolumeDesc& V, int r
 
 // Axis a's index of the voxel holding the ray's point at t, clamped to
 // [lo, hi] (so a point on a face belongs to the boundary voxel).
-__device__ inline int siddon_voxel_at(const SiddonRay& S, const VolumeDesc& V, int a, double t,
-                                      int lo, int hi)
+__host__ __device__ inline int siddon_voxel_at(const SiddonRay& S, const VolumeDesc& V, int a,
+                                               double t, int lo, int hi)
 {
     const double ua = (S.C[a] + t * S.d[a] + V.half_e[a]) * V.inv_s[a];
     return (int)fmin(fmax(floor(ua), (double)lo), (double)hi);
@@ -80,8 +81,8 @@ __device__ inline int siddon_voxel_at(const SiddonRay& S, const VolumeDesc& V, i
 
 // siddon_clip and the walk's start: the voxel holding the entry point and each
 // axis' first crossing ahead.
-__device__ inline bool siddon_setup(const ViewGeom& G, const VolumeDesc& V, int r, int c,
-                                    SiddonRay& S)
+__host__ __device__ inline bool siddon_setup(const ViewGeom& G, const VolumeDesc& V, int r,
+                                             int c, SiddonRay& S)
 {
     if (!siddon_clip(G, V, r, c, S)) return false;
 #pragma unroll
@@ -100,7 +101,7 @@ struct NextAxis {
     double t;
 };
 
-__device__ inline NextAxis next_axis(const SiddonRay& S)
+__host__ __device__ inline NextAxis next_axis(const SiddonRay& S)
 {
     NextAxis m;
     m.x = S.tn[0] <= S.tn[1] && S.tn[0] <= S.tn[2];
@@ -111,7 +112,7 @@ __device__ inline NextAxis next_axis(const SiddonRay& S)
 
 // Cross the plane of the chosen axis: the voxel index and that axis' next
 // crossing move on.  Returns false when the walk leaves the volume.
-__device__ inline bool advance(SiddonRay& S, const NextAxis& m, const VolumeDesc& V)
+__host__ __device__ inline bool advance(SiddonRay& S, const NextAxis& m, const VolumeDesc& V)
 {
     const bool z = !m.x && !m.y;
     const bool sel[3] = {m.x, m.y, z};
@@ -126,6 +127,125 @@ __device__ inline bool advance(SiddonRay& S, const NextAxis& m, const VolumeDesc
         }
     }
     return in;
+}
+
+// ------------------------------------------------ the walk inside a brick
+//
+// For the brick-owned backward (drr_brick.hip): the pieces of a ray inside one
+// brick of voxels [lo, lo + e) per axis.  The walk starts at t_in, the later of
+// the ray's entry into the volume and into the brick's box, in the voxel past
+// every plane crossed at or before t_in, and ends at t_out; all crossings come
+// from plane_crossing, so these are the forward's pieces between the same
+// crossings, and every piece of positive length falls in exactly one brick.
+// Host and device: the CPU checks replay them against the whole walk.
+
+// The brick's voxel box as world coordinates of its bounding planes.
+__host__ __device__ inline BrickRegion siddon_brick_region(const VolumeDesc& V, const BrickBox& b)
+{
+    BrickRegion g;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        g.lo[a] = (float)((double)b.lo[a] * V.s[a] - V.half_e[a]);
+        g.hi[a] = (float)((double)(b.lo[a] + b.e[a]) * V.s[a] - V.half_e[a]);
+    }
+    return g;
+}
+
+// The ray's range [t_in, t_out) inside the brick's box (and the volume's);
+// false when it has none.  An axis the ray runs parallel to keeps the voxel
+// the forward's walk gives it (the one holding the entry point).
+__host__ __device__ inline bool siddon_brick_range(SiddonRay& S, const VolumeDesc& V,
+                                                   const BrickBox& b, double& t_in,
+                                                   double& t_out)
+{
+    t_in = S.t0;
+    t_out = S.t1;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        if (S.step[a] == 0) {
+            S.i[a] = siddon_voxel_at(S, V, a, S.t0, 0, V.n[a] - 1);
+            if (S.i[a] < b.lo[a] || S.i[a] >= b.lo[a] + b.e[a]) return false;
+        } else {
+            const double tl = plane_crossing(S, a, b.lo[a]);
+            const double th = plane_crossing(S, a, b.lo[a] + b.e[a]);
+            t_in = fmax(t_in, fmin(tl, th));
+            t_out = fmin(t_out, fmax(tl, th));
+        }
+    }
+    return t_out > t_in;
+}
+
+// The walk's state at t_in: on each axis the voxel past every plane crossed at
+// or before t_in, and the next plane ahead (none, at infinity, for an axis the
+// ray runs parallel to: its voxel is siddon_brick_range's).  The voxel holding
+// the point at t_in is off by at most one from that (the point and the
+// crossings round differently only within a few ulps of a plane), so one test
+// of the planes on either side settles it.
+__host__ __device__ inline void siddon_brick_start(SiddonRay& S, const VolumeDesc& V,
+                                                   const BrickBox& b, double t_in)
+{
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+        if (S.step[a] == 0) {
+            S.p[a] = 0;
+            S.tn[a] = __builtin_inf();
+            continue;
+        }
+        const int lo = b.lo[a], hi = b.lo[a] + b.e[a] - 1;
+        int i = siddon_voxel_at(S, V, a, t_in, lo, hi);
+        const bool below = plane_crossing(S, a, i) <= t_in;       // plane i crossed
+        const bool above = plane_crossing(S, a, i + 1) <= t_in;   // plane i + 1 crossed
+        if (S.step[a] > 0) {
+            i += (above && i < hi) ? 1 : ((!below && i > lo) ? -1 : 0);
+            S.p[a] = i + 1;
+        } else {
+            i += (below && i > lo) ? -1 : ((!above && i < hi) ? 1 : 0);
+            S.p[a] = i;
+        }
+        S.i[a] = i;
+        S.tn[a] = plane_crossing(S, a, S.p[a]);
+    }
+}
+
+// Walks ray S from t_in to t_out through the brick, handing each piece (its
+// voxel's entry in the brick copy, its length; zero for a tie of crossings,
+// which adds nothing) to `add`.  Every crossing before t_out is of a plane
+// inside the brick (t_out is at or before each axis' exit plane, and the
+// crossings of one axis come in plane order), so the voxel stays in the brick;
+// the walk takes no branch per piece: all three next crossings are made and
+// the nearest one's kept.
+template <int B, typename Add>
+__host__ __device__ inline void siddon_brick_walk(const SiddonRay& S, const BrickBox& b,
+                                                  double t_in, double t_out, Add add)
+{
+    double tn0 = S.tn[0], tn1 = S.tn[1], tn2 = S.tn[2];
+    int p0 = S.p[0], p1 = S.p[1], p2 = S.p[2];
+    int e = (S.i[0] - b.lo[0]) + B * ((S.i[1] - b.lo[1]) + B * (S.i[2] - b.lo[2]));
+    const int ex = S.step[0], ey = B * S.step[1], ez = B * B * S.step[2];
+    double tc = t_in;
+    int guard = b.e[0] + b.e[1] + b.e[2] + 3;
+    for (;;) {
+        // the nearest crossing, x before y before z on ties (as the forward)
+        const bool sx = tn0 <= tn1 && tn0 <= tn2;
+        const bool sy = !sx && tn1 <= tn2;
+        const double mt = sx ? tn0 : (sy ? tn1 : tn2);
+        const double te = mt < t_out ? mt : t_out;
+        const double len = te - tc;
+        add(e, len > 0.0 ? len : 0.0);
+        tc = te > tc ? te : tc;
+        if (!(mt < t_out) || --guard <= 0) break;
+        const int q0 = p0 + S.step[0], q1 = p1 + S.step[1], q2 = p2 + S.step[2];
+        const double n0 = plane_crossing(S, 0, q0), n1 = plane_crossing(S, 1, q1);
+        const double n2 = plane_crossing(S, 2, q2);
+        const bool sz = !sx && !sy;
+        p0 = sx ? q0 : p0;
+        p1 = sy ? q1 : p1;
+        p2 = sz ? q2 : p2;
+        tn0 = sx ? n0 : tn0;
+        tn1 = sy ? n1 : tn1;
+        tn2 = sz ? n2 : tn2;
+        e += sx ? ex : (sy ? ey : ez);
+    }
 }
 
 }  // namespace drr

@@ -6,7 +6,11 @@
   scatter (tests/cpu_checks/brick_replay.cpp);
 * ABI host validation under ASan/UBSan: the whole library built with the
   sanitizers on its host code, driven by tests/cpu_checks/abi_check.cpp through
-  every entry point's invalid and empty calls.
+  every entry point's invalid and empty calls;
+* Siddon brick replay: the brick-owned Siddon backward's walk
+  (csrc/drr_siddon.hpp) compiled for the host with the sanitizers, each ray's
+  pieces from the bricks against the whole walk, bit for bit
+  (tests/cpu_checks/siddon_replay.hip).
 
 Builds go to a temporary directory named by a hash of their inputs, so a
 repeated run reuses them.
@@ -62,6 +66,29 @@ def test_brick_index_replay_under_sanitizers():
     print(out)
     assert rc == 0, out
     assert "all brick index checks passed" in out
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_siddon_brick_walk_replay_under_sanitizers():
+    """Host build of the Siddon brick walk (no device code): every ray's pieces
+    from the brick walks equal the whole walk's, every brick entry is in range,
+    and every brick with a piece of a ray finds its pixel among its candidates."""
+    src = os.path.join(CHECKS, "siddon_replay.hip")
+    d = _build_dir([src] + _sources(), "siddon")
+    exe = os.path.join(d, "siddon_replay")
+    if not os.path.exists(exe):
+        rc, out = _run([HIPCC, "-x", "hip", "--cuda-host-only", "-std=c++17", "-O1", "-g",
+                        "-Xarch_host", "-fsanitize=address",
+                        "-Xarch_host", "-fsanitize=undefined",
+                        "-Xarch_host", "-fno-sanitize-recover=undefined",
+                        "-o", exe + ".tmp", src])
+        assert rc == 0, out
+        os.replace(exe + ".tmp", exe)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0", UBSAN_OPTIONS="print_stacktrace=1")
+    rc, out = _run([exe], timeout=300, env=env)
+    print(out)
+    assert rc == 0, out
+    assert "all Siddon brick checks passed" in out
 
 
 @pytest.mark.slow
