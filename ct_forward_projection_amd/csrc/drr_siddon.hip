@@ -304,7 +304,7 @@ hipError_t launch_siddon_backward(const LaunchArgs& a, const float* grad_out, co
     const int tiles_per_view = tiles_x * tiles_y, n_tiles = tiles_per_view * a.n_views;
     if (n_tiles == 0) return hipSuccess;
     const dim3 grid(n_tiles), block(kBlock);
-    const int cap = window_cap(view_reuse);
+    const int cap = window_cap(view_reuse, true);
     const size_t lds = (size_t)cap * sizeof(int);
     if (a.mode == kBeerLambert)
         hipLaunchKernelGGL((drr_siddon_scatter_kernel<kBeerLambert>), grid, block, lds, stream,

@@ -28,16 +28,23 @@ namespace drr {
 // CU): the helix (11.7 per view) 15.2 -> 12.1 ms, its cell-constant backward
 // 11.9 -> 11.4 ms, the 1024^2 step (31.6) unchanged at 6144 (7168: 0.577 ->
 // 0.591 ms; 8192 and 10240 slowed the 1024^2 cell-constant backward, 9.6
-// pieces per cell: 0.60 -> 0.65 / 0.73 ms).
+// pieces per cell: 0.60 -> 0.65 / 0.73 ms).  The trilinear scatter now takes
+// the largest window that still lets five workgroups share a CU: 7936 entries
+// (31 KB), helix 12.2 ->
+// 11.3 ms (7424: 11.8, 7680: 11.4-11.5; 8128 and 8192, four per CU: 11.5;
+// 10240: 12.9); the cell-constant scatter keeps 7168 (7680: 1024^2 0.593 ->
+// 0.598 ms, helix 11.24 -> 11.11 ms; 8192: 0.638 / 12.1 ms).
 constexpr int kWinCapDense = 6144;
-constexpr int kWinCapMid = 7168;
+constexpr int kWinCapMid = 7936;
+constexpr int kWinCapMidSiddon = 7168;
 constexpr int kWinCapSparse = 16000;
 
-// Window entries for a launch whose views each put `view_reuse` samples (or
-// ray-voxel pieces) per cell of the volume.
-inline int window_cap(double view_reuse)
+// Window entries for a launch whose views each put `view_reuse` samples per
+// cell of the volume (trilinear), or ray-voxel pieces (cell-constant, SIDDON).
+inline int window_cap(double view_reuse, bool siddon = false)
 {
-    return view_reuse >= 16.0 ? kWinCapDense : (view_reuse >= 4.0 ? kWinCapMid : kWinCapSparse);
+    const int mid = siddon ? kWinCapMidSiddon : kWinCapMid;
+    return view_reuse >= 16.0 ? kWinCapDense : (view_reuse >= 4.0 ? mid : kWinCapSparse);
 }
 
 // Trilinear weights of one sample scaled by c: w[n] for corner n (bit 0 = x1,
