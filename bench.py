@@ -582,6 +582,11 @@ PROFILE_COMMANDS = {
     "pmc": "rocprofv3 --pmc {counters} -d gpurun_out/prof/{case}/{tag} -o pmc "
            "--output-format csv -- python3 bench.py --profile-run {case} --reps 3",
 }
+# The default bench command itself under the kernel tracer: the trace's average
+# launch durations sit beside the event-timed per-pass figures of the same run.
+BENCH_STEP_CASE = "bench_step"
+BENCH_TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats -d gpurun_out/prof/bench_step/trace "
+                       "-o trace --output-format csv -- python3 bench.py --no-workloads --no-cpu")
 PMC_SETS = {
     "fetch": ["FETCH_SIZE"],
     "write": ["WRITE_SIZE", "TCC_HIT_sum", "TCC_MISS_sum"],
@@ -707,6 +712,64 @@ def _median_counters(root):
     return {k: {c: float(np.median(v)) for c, v in d.items()} for k, d in values.items()}
 
 
+def _trace_stats(trace_dir):
+    """drr kernel short name -> calls, total, min, max (ns) from a kernel_stats.csv."""
+    stats = _find(trace_dir, "kernel_stats.csv")
+    trace = {}
+    for r in (_csv_rows(stats[0]) if stats else []):
+        short = _short_name(r.get("Name", ""))
+        if short.startswith("drr_"):
+            t = trace.setdefault(short, {"calls": 0, "total_ns": 0.0, "min": 1e30, "max": 0.0})
+            t["calls"] += int(r.get("Calls", 0))
+            t["total_ns"] += float(r.get("TotalDurationNs", 0) or 0) or \
+                float(r.get("AverageNs", 0)) * int(r.get("Calls", 0))
+            t["min"] = min(t["min"], float(r.get("MinNs", 0)))
+            t["max"] = max(t["max"], float(r.get("MaxNs", 0)))
+    return trace
+
+
+def bench_step_summary(root: str, prof_dir: str, rev: str):
+    """profiles/<backward kernel>__bench_step.md from the traced default bench
+    run (root/bench_step/trace) and the JSON line it printed
+    (root/bench_step/bench.json): the trace's average durations of the step's
+    two kernels beside the run's own event-timed passes."""
+    croot = os.path.join(root, BENCH_STEP_CASE)
+    trace = _trace_stats(os.path.join(croot, "trace"))
+    if not trace:
+        return
+    line = None
+    try:
+        with open(os.path.join(croot, "bench.json")) as f:
+            for raw in f:
+                if raw.startswith("{"):
+                    line = json.loads(raw)
+    except (OSError, ValueError):
+        line = None
+    bk = backward_kernel()
+    lines = [f"# {bk} and the other kernels of the default bench run", "",
+             "Command:", "", "- `" + BENCH_TRACE_COMMAND + "`", "",
+             f"Kernel sources revision: `{rev}`.  Every launch of the run is traced: warm-up, the "
+             "timed steps, the per-pass event timing and the hit-ray count (one "
+             "`drr_march_kernel` launch of one sample per ray).", "",
+             "| kernel | calls | avg (us) | min | max |", "|---|---|---|---|---|"]
+    for short, t in sorted(trace.items(), key=lambda kv: -kv[1]["total_ns"]):
+        lines.append(f"| `{short}` | {t['calls']} | {t['total_ns'] / max(t['calls'], 1) / 1e3:.2f} "
+                     f"| {t['min'] / 1e3:.2f} | {t['max'] / 1e3:.2f} |")
+    if line is not None:
+        km = line.get("kernels_ms", {})
+        lines += ["", "The same run's JSON line (HIP events on the launch stream, mean over the "
+                      "timed steps): "
+                      f"forward {km.get('forward')} ms (`drr_march_staged_kernel`), backward "
+                      f"{km.get('backward')} ms (`drr_fill_kernel` + `{bk}`); "
+                      f"{line.get('ms_per_step')} ms per step, {line.get('value')} "
+                      f"{line.get('unit')}; dominant-kernel roofline: "
+                      f"{json.dumps(line.get('roofline'))}."]
+    path = os.path.join(prof_dir, f"{bk}__{BENCH_STEP_CASE}.md")
+    with open(path, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    log("wrote", path)
+
+
 def profile_summary(root: str):
     """Summarise the rocprofv3 outputs under ``root`` (PROFILE_COMMANDS' layout:
     root/<case>/trace, root/<case>/<counter set>, root/<case>/meta.json) into
@@ -730,17 +793,7 @@ def profile_summary(root: str):
                 meta = json.load(f)
         except OSError:
             continue
-        stats = _find(os.path.join(croot, "trace"), "kernel_stats.csv")
-        trace = {}
-        for r in (_csv_rows(stats[0]) if stats else []):
-            short = _short_name(r.get("Name", ""))
-            if short.startswith("drr_"):
-                t = trace.setdefault(short, {"calls": 0, "total_ns": 0.0, "min": 1e30, "max": 0.0})
-                t["calls"] += int(r.get("Calls", 0))
-                t["total_ns"] += float(r.get("TotalDurationNs", 0) or 0) or \
-                    float(r.get("AverageNs", 0)) * int(r.get("Calls", 0))
-                t["min"] = min(t["min"], float(r.get("MinNs", 0)))
-                t["max"] = max(t["max"], float(r.get("MaxNs", 0)))
+        trace = _trace_stats(os.path.join(croot, "trace"))
         med = _median_counters(croot)
         rows, figures = [], {}
         for short, t in sorted(trace.items(), key=lambda kv: -kv[1]["total_ns"]):
@@ -825,8 +878,10 @@ def profile_summary(root: str):
         with open(path, "w") as fo:
             fo.write("\n".join(lines) + "\n")
         log("wrote", path)
-    with open(os.path.join(prof_dir, "pmc_traffic.json"), "w") as fo:
-        json.dump(traffic, fo, indent=1)
+    if traffic["cases"]:              # a root with the bench run only keeps the case counters
+        with open(os.path.join(prof_dir, "pmc_traffic.json"), "w") as fo:
+            json.dump(traffic, fo, indent=1)
+    bench_step_summary(root, prof_dir, rev)
 
 
 def main():
