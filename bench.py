@@ -302,8 +302,8 @@ def roofline_alu(name, ops, ms, counters=None):
          "ops_per_launch": int(ops), "traffic": None}
     if counters:
         r["traffic"] = counters.get("hbm_bytes_per_launch")
-        for k in ("hbm_gbs", "hbm_frac", "l2_hit", "valu_busy", "clock_ghz",
-                  "issued_per_algorithmic", "lds_bank_conflict"):
+        for k in ("hbm_gbs", "hbm_frac", "l2_hit", "valu_busy", "valu_busy_rocprof",
+                  "valu_lane_util", "clock_ghz", "issued_per_algorithmic", "lds_bank_conflict"):
             if counters.get(k) is not None:
                 r[k] = counters[k]
     return r
@@ -594,6 +594,10 @@ PMC_SETS = {
            "SQ_INSTS_LDS", "SQ_ACTIVE_INST_VALU", "SQ_WAIT_INST_ANY", "GRBM_GUI_ACTIVE"],
     "ta": ["TA_TA_BUSY_sum", "TA_BUSY_avr", "TD_TD_BUSY_sum", "SQ_LDS_BANK_CONFLICT",
            "SQ_LDS_ADDR_CONFLICT"],
+    # rocprofv3's own derived metrics: VALUBusy = 100 sum(SQ_ACTIVE_INST_VALU) / CU_NUM /
+    # max(GRBM_GUI_ACTIVE); VALUUtilization = 100 sum(SQ_THREAD_CYCLES_VALU) /
+    # (sum(SQ_ACTIVE_INST_VALU) x 64), the active lanes of the VALU instructions
+    "valu": ["VALUBusy", "VALUUtilization"],
 }
 COPY_CASE = "copy1gib"          # the calibration run of the byte counters
 
@@ -817,6 +821,10 @@ def profile_summary(root: str):
             if m.get("SQ_INSTS_VALU") and f.get("clock_ghz"):
                 cycles = avg_ns * f["clock_ghz"]
                 f["valu_busy"] = round(m["SQ_INSTS_VALU"] * 4 / (MI355X_SIMDS * cycles), 3)
+            if m.get("VALUBusy") is not None:
+                f["valu_busy_rocprof"] = round(m["VALUBusy"] / 100.0, 3)
+            if m.get("VALUUtilization") is not None:
+                f["valu_lane_util"] = round(m["VALUUtilization"] / 100.0, 3)
             if m.get("SQ_LDS_BANK_CONFLICT") is not None and f.get("clock_ghz"):
                 f["lds_bank_conflict"] = round(
                     m["SQ_LDS_BANK_CONFLICT"] / (MI355X_CUS * avg_ns * f["clock_ghz"]), 3)
@@ -854,11 +862,12 @@ def profile_summary(root: str):
                       f"average duration, against {ALU_PEAK_TOPS:.2f} TOP/s (1024 SIMDs x 16 lanes "
                       f"x 2.4 GHz, no packed FP32).  VALU busy: SQ_INSTS_VALU x 4 cycles over 1024 "
                       f"SIMDs x the duration at the measured clock (GRBM_GUI_ACTIVE / 8 XCDs / "
-                      f"duration).", "",
+                      f"duration).  VALUBusy and VALU lanes: rocprofv3's derived VALUBusy and "
+                      f"VALUUtilization (as fractions).", "",
                   "| kernel | calls | avg (us) | min | max | unit x count | ALU TOP/s | ALU frac | "
-                  "VALU busy | issued/alg | clock GHz | HBM MB/launch | HBM GB/s | L2 hit | "
-                  "LDS conflict |",
-                  "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+                  "VALU busy | VALUBusy | VALU lanes | issued/alg | clock GHz | HBM MB/launch | "
+                  "HBM GB/s | L2 hit | LDS conflict |",
+                  "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
         for short, t, m, f in rows:
             fmt = lambda k, d=3: "" if f.get(k) is None else f"{f[k]:.{d}f}"
             unit = f"{f['unit']} x {f['units_per_launch']}" if "unit" in f else ""
@@ -866,6 +875,7 @@ def profile_summary(root: str):
             lines.append(f"| `{short}` | {t['calls']} | {f['avg_us']:.2f} | {t['min'] / 1e3:.2f} "
                          f"| {t['max'] / 1e3:.2f} | {unit} | {fmt('alu_tops')} | "
                          f"{fmt('alu_frac', 4)} | {fmt('valu_busy')} | "
+                         f"{fmt('valu_busy_rocprof')} | {fmt('valu_lane_util')} | "
                          f"{fmt('issued_per_algorithmic')} | {fmt('clock_ghz')} | {mb} | "
                          f"{fmt('hbm_gbs', 1)} | {fmt('l2_hit', 4)} | "
                          f"{fmt('lds_bank_conflict')} |")
