@@ -336,14 +336,21 @@ def measured_counters(case, kernel):
 
 
 def cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it, with its family, model and
+    stepping numbers (a virtual machine may report only the vendor's brand)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break                        # the first processor's block is enough
+                k, _, v = line.partition(":")
+                fields.setdefault(k.strip(), v.strip())
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return name + (f" ({', '.join(ids)})" if ids else "")
 
 
 def cpu_baseline(w):
