@@ -149,8 +149,9 @@ def voxel_centres(n: int, s: float) -> np.ndarray:
 
 def piecewise_linear(x: np.ndarray, xp, yp) -> np.ndarray:
     """Piecewise-linear transfer with the first and last segments extended
-    (flashdrr ``piecewise_linear_channelwise``, one channel).  Used only to build
-    an input volume."""
+    (flashdrr ``piecewise_linear_channelwise``, one channel).  Builds input
+    volumes, and in the GPU sweep the mapped values whose absolute line integral
+    scales the forward bar where mapped values of both signs cancel."""
     xp = np.asarray(xp, dtype=np.float64)
     yp = np.asarray(yp, dtype=np.float64)
     seg = np.clip(np.searchsorted(xp, x, side="right") - 1, 0, len(xp) - 2)
