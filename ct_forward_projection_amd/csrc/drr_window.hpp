@@ -30,10 +30,9 @@ namespace drr {
 // 0.591 ms; 8192 and 10240 slowed the 1024^2 cell-constant backward, 9.6
 // pieces per cell: 0.60 -> 0.65 / 0.73 ms).  The trilinear scatter now takes
 // the largest window that still lets five workgroups share a CU: 7936 entries
-// (31 KB), helix 12.2 ->
-// 11.3 ms (7424: 11.8, 7680: 11.4-11.5; 8128 and 8192, four per CU: 11.5;
-// 10240: 12.9); the cell-constant scatter keeps 7168 (7680: 1024^2 0.593 ->
-// 0.598 ms, helix 11.24 -> 11.11 ms; 8192: 0.638 / 12.1 ms).
+// (31 KB), helix 12.2 -> 11.3 ms (7424: 11.8, 7680: 11.4-11.5; 8128 and 8192,
+// four per CU: 11.5; 10240: 12.9); the cell-constant scatter keeps 7168 (7680:
+// 1024^2 0.593 -> 0.598 ms, helix 11.24 -> 11.11 ms; 8192: 0.638 / 12.1 ms).
 constexpr int kWinCapDense = 6144;
 constexpr int kWinCapMid = 7936;
 constexpr int kWinCapMidSiddon = 7168;
