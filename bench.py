@@ -132,6 +132,24 @@ class Resident:
                                 w.n_samples, w.mode, self.g, self.s, grad_volume=self.grad,
                                 workspace=self.workspace_b)
 
+    def forward_reuse(self):
+        """The forward reading the copy the last forward left in the workspace
+        (drr_forward_reuse): a registration loop over this fixed volume."""
+        import ct_forward_projection_amd as drr
+        w = self.w
+        drr.drr_forward(self.vol, w.spacing, w.K, self.poses, w.det_h, w.det_w, w.n_samples,
+                        w.mode, out=self.out, line_integral=self.s, workspace=self.workspace,
+                        reuse_copy=True)
+
+    def pose_backward_reuse(self):
+        """The pose gradient reading the copy the last pose gradient left in its
+        workspace (drr_backward_pose_reuse)."""
+        import ct_forward_projection_amd as drr
+        w = self.w
+        drr.drr_backward_pose(self.vol, w.spacing, w.K, self.poses, w.det_h, w.det_w,
+                              w.n_samples, w.mode, self.pose_g, grad_poses=self.grad_poses,
+                              workspace=self.pose_ws, reuse_copy=True)
+
     def pose_backward(self):
         import ct_forward_projection_amd as drr
         w = self.w
@@ -404,6 +422,15 @@ def workload_lines(dev, reps):
             line["pose_backward_alu_frac"] = round(hits * w.n_samples * OPS_POSE_SAMPLE /
                                                    (pose_ms * 1e-3) / 1e12 / ALU_PEAK_TOPS, 4)
             line["registration_step_fps"] = round(w.n_views / (fwd_ms + pose_ms) * 1e3, 1)
+            if res.workspace is not None:
+                # a registration loop over the fixed volume: both calls read the
+                # copies the previous step left in their workspaces
+                res.forward()
+                tr = time_graph([res.forward_reuse, res.pose_backward_reuse])
+                line["forward_reuse_ms"] = round(tr[0], 4)
+                line["forward_reuse_fps"] = round(w.n_views / tr[0] * 1e3, 1)
+                line["pose_backward_reuse_ms"] = round(tr[1], 4)
+                line["registration_step_reuse_fps"] = round(w.n_views / (tr[0] + tr[1]) * 1e3, 1)
         if len(t) > 1:
             line["backward_ms"] = round(t[1], 4)
             line["backward_gsamples_s"] = round(w.nominal_samples / t[1] / 1e6, 1)

@@ -60,12 +60,16 @@ def library() -> ctypes.CDLL:
         lib.drr_workspace_bytes.restype = Z
         lib.drr_forward.argtypes = [P, I, I, I, I, P, P, P, I, I, I, I, I, P, P, P, Z, P]
         lib.drr_forward.restype = I
+        lib.drr_forward_reuse.argtypes = lib.drr_forward.argtypes
+        lib.drr_forward_reuse.restype = I
         lib.drr_forward_no_alloc.argtypes = [P, I, I, I, I, P, P, P, I, I, I, I, I, P, P, P]
         lib.drr_forward_no_alloc.restype = I
         lib.drr_backward_volume.argtypes = [I, I, I, P, P, P, I, I, I, I, I, P, P, P, P, Z, P]
         lib.drr_backward_volume.restype = I
         lib.drr_backward_pose.argtypes = [P, I, I, I, I, P, P, P, I, I, I, I, I, P, P, P, Z, P]
         lib.drr_backward_pose.restype = I
+        lib.drr_backward_pose_reuse.argtypes = lib.drr_backward_pose.argtypes
+        lib.drr_backward_pose_reuse.restype = I
         lib.drr_forward_siddon.argtypes = [P, I, I, I, I, P, P, P, I, I, I, I, P, P, P]
         lib.drr_forward_siddon.restype = I
         lib.drr_backward_volume_siddon.argtypes = [I, I, I, P, P, P, I, I, I, I, P, P, P, P]
@@ -156,9 +160,12 @@ def drr_forward(volume: torch.Tensor, spacing: Sequence[float], K, poses: torch.
                 det_h: int, det_w: int, n_samples: int, mode: int = BEER_LAMBERT,
                 out: Optional[torch.Tensor] = None, line_integral=True,
                 workspace: Optional[torch.Tensor] = None,
-                stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                stream=None, reuse_copy: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Forward DRR of ``volume`` (nz, ny, nx) for ``poses`` (V, 3, 4) world-to-camera.
-    Returns (image (V, det_h, det_w) fp32, line integrals or None)."""
+    Returns (image (V, det_h, det_w) fp32, line integrals or None).  With
+    ``reuse_copy`` the call skips the relayout (``drr_forward_reuse``):
+    ``workspace`` must hold the read copy an earlier call made of the same
+    volume for the same n_views, det_h, det_w and n_samples."""
     volume = _device_tensor(volume, "volume")
     dtype = _volume_dtype(volume)
     poses = _device_tensor(poses, "poses", torch.float32)
@@ -181,10 +188,13 @@ def drr_forward(volume: torch.Tensor, spacing: Sequence[float], K, poses: torch.
         if line_integral.numel() != out.numel():
             raise ValueError("line_integral has the wrong size")
     need = drr_workspace_bytes(nz, ny, nx, dtype, V, det_h, det_w, n_samples, 0)
+    if reuse_copy and need and workspace is None:
+        raise ValueError("reuse_copy needs the workspace that holds the read copy")
     if workspace is None:
         workspace = _workspace(need, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(library().drr_forward(
+    fn = library().drr_forward_reuse if reuse_copy else library().drr_forward
+    _check(fn(
         _ptr(volume), dtype, nz, ny, nx, _host_floats(spacing, 3), _host_floats(K, 9),
         _ptr(poses), V, det_h, det_w, n_samples, mode, _ptr(out), _ptr(line_integral),
         _ptr(workspace), ws_bytes, _stream(stream)))
@@ -262,8 +272,12 @@ def drr_backward_volume(shape: Sequence[int], spacing: Sequence[float], K, poses
 def drr_backward_pose(volume: torch.Tensor, spacing: Sequence[float], K, poses: torch.Tensor,
                       det_h: int, det_w: int, n_samples: int, mode: int, grad_out: torch.Tensor,
                       grad_poses: Optional[torch.Tensor] = None,
-                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """dL/dP for L = sum(grad_out * I): (V, 3, 4) fp32 over each view's [R | t]."""
+                      workspace: Optional[torch.Tensor] = None, stream=None,
+                      reuse_copy: bool = False) -> torch.Tensor:
+    """dL/dP for L = sum(grad_out * I): (V, 3, 4) fp32 over each view's [R | t].
+    With ``reuse_copy`` the call skips the relayout (``drr_backward_pose_reuse``):
+    ``workspace`` must hold the read copy an earlier pose call made of the same
+    volume for the same n_views, det_h, det_w and n_samples."""
     volume = _device_tensor(volume, "volume")
     dtype = _volume_dtype(volume)
     poses = _device_tensor(poses, "poses", torch.float32)
@@ -276,10 +290,13 @@ def drr_backward_pose(volume: torch.Tensor, spacing: Sequence[float], K, poses: 
         grad_poses = torch.empty((V, 3, 4), dtype=torch.float32, device=volume.device)
     grad_poses = _device_tensor(grad_poses, "grad_poses", torch.float32)
     need = drr_workspace_bytes(nz, ny, nx, dtype, V, det_h, det_w, n_samples, 2)
+    if reuse_copy and workspace is None:
+        raise ValueError("reuse_copy needs the workspace that holds the read copy")
     if workspace is None:
         workspace = _workspace(need, volume.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(library().drr_backward_pose(
+    fn = library().drr_backward_pose_reuse if reuse_copy else library().drr_backward_pose
+    _check(fn(
         _ptr(volume), dtype, nz, ny, nx, _host_floats(spacing, 3), _host_floats(K, 9),
         _ptr(poses), V, det_h, det_w, n_samples, mode, _ptr(grad_out), _ptr(grad_poses),
         _ptr(workspace), ws_bytes, _stream(stream)))

@@ -285,7 +285,7 @@ int scratch_on_stream_device(hipStream_t stream, void** ptr)
 int forward_into(const void* volume, int dtype, int nz, int ny, int nx, const float* spacing,
                  const float* K, const float* poses, int n_views, int det_h, int det_w,
                  int n_samples, int mode, float* out, float* line_integral, void* workspace,
-                 size_t workspace_bytes, bool no_alloc, void* stream)
+                 size_t workspace_bytes, bool no_alloc, void* stream, bool reuse_copy = false)
 {
     if (dtype != DRR_F32 && dtype != DRR_BF16)
         return fail(DRR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
@@ -320,7 +320,7 @@ int forward_into(const void* volume, int dtype, int nz, int ny, int nx, const fl
     }
     set_read_geometry(a.V, plan);
     hipError_t e = drr::launch_forward(a, plan, volume, dtype, workspace, out, line_integral,
-                                       static_cast<hipStream_t>(stream));
+                                       static_cast<hipStream_t>(stream), reuse_copy);
     if (e != hipSuccess)
         return fail(DRR_ERR_HIP, "forward launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -464,6 +464,16 @@ int drr_forward(const void* volume, int dtype, int nz, int ny, int nx, const flo
     return forward_into(volume, dtype, nz, ny, nx, spacing, K, poses, n_views, det_h, det_w,
                         n_samples, mode, out, line_integral, workspace, workspace_bytes, false,
                         stream);
+}
+
+int drr_forward_reuse(const void* volume, int dtype, int nz, int ny, int nx, const float* spacing,
+                      const float* K, const float* poses, int n_views, int det_h, int det_w,
+                      int n_samples, int mode, float* out, float* line_integral, void* workspace,
+                      size_t workspace_bytes, void* stream)
+{
+    return forward_into(volume, dtype, nz, ny, nx, spacing, K, poses, n_views, det_h, det_w,
+                        n_samples, mode, out, line_integral, workspace, workspace_bytes, false,
+                        stream, true);
 }
 
 int drr_forward_no_alloc(const void* volume, int dtype, int nz, int ny, int nx,
@@ -616,7 +626,8 @@ namespace {
 // The pose backward of a validated render call `a` (single-volume calls come
 // here too): every mode, either clip.
 int pose_backward(drr::LaunchArgs& a, const void* volume, int dtype, const float* grad_out,
-                  float* grad_poses, void* workspace, size_t workspace_bytes, void* stream)
+                  float* grad_poses, void* workspace, size_t workspace_bytes, void* stream,
+                  bool reuse_copy = false)
 {
     if (!volume) return fail(DRR_ERR_INVALID_ARGUMENT, "volume is NULL");
     const long long n_out = (long long)a.n_views * a.C * a.H * a.W;
@@ -640,7 +651,7 @@ int pose_backward(drr::LaunchArgs& a, const void* volume, int dtype, const float
     char* ws = static_cast<char*>(workspace);
     hipError_t e = drr::launch_backward_pose(a, plan, volume, dtype, ws + acc_bytes,
                                              reinterpret_cast<double*>(ws), grad_out, grad_poses,
-                                             static_cast<hipStream_t>(stream));
+                                             static_cast<hipStream_t>(stream), reuse_copy);
     if (e != hipSuccess)
         return fail(DRR_ERR_HIP, "pose backward launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -663,6 +674,22 @@ int drr_backward_pose(const void* volume, int dtype, int nz, int ny, int nx, con
     if (st != DRR_OK) return st;
     return pose_backward(a, volume, dtype, grad_out, grad_poses, workspace, workspace_bytes,
                          stream);
+}
+
+int drr_backward_pose_reuse(const void* volume, int dtype, int nz, int ny, int nx,
+                            const float* spacing, const float* K, const float* poses, int n_views,
+                            int det_h, int det_w, int n_samples, int mode, const float* grad_out,
+                            float* grad_poses, void* workspace, size_t workspace_bytes,
+                            void* stream)
+{
+    if (dtype != DRR_F32 && dtype != DRR_BF16)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    drr::LaunchArgs a;
+    int st = check_geometry(nz, ny, nx, dtype == DRR_F32 ? 4 : 2, spacing, K, poses, n_views,
+                            det_h, det_w, n_samples, mode, a);
+    if (st != DRR_OK) return st;
+    return pose_backward(a, volume, dtype, grad_out, grad_poses, workspace, workspace_bytes,
+                         stream, true);
 }
 
 int drr_render_backward_pose(const void* volume, int dtype, int n_volumes, int n_channels,

@@ -251,8 +251,11 @@ inline BackwardRead plan_backward(int n_volumes, int C, int nz, int ny, int nx, 
     return r;
 }
 
+// With reuse_copy the workspace already holds the plan's read copy of `vol`
+// (made by an earlier call with the same volume and plan) and no relayout runs.
 hipError_t launch_forward(const LaunchArgs& a, const RenderPlan& plan, const void* vol, int dtype,
-                          void* workspace, float* out, float* s_out, hipStream_t stream);
+                          void* workspace, float* out, float* s_out, hipStream_t stream,
+                          bool reuse_copy = false);
 // What the plan's march reads, made in `workspace`: the corner cells (zero-padded
 // and/or mapped as the call asks) or the mapped fp32 volumes; nothing when the
 // march reads the caller's volumes.
@@ -307,6 +310,6 @@ inline size_t pose_acc_bytes(int n_views) { return ((size_t)n_views * 12 * 8 + 2
 
 hipError_t launch_backward_pose(const LaunchArgs& a, const RenderPlan& plan, const void* vol,
                                 int dtype, void* read_buf, double* acc, const float* grad_out,
-                                float* grad_poses, hipStream_t stream);
+                                float* grad_poses, hipStream_t stream, bool reuse_copy = false);
 
 }  // namespace drr

@@ -1486,7 +1486,8 @@ static void launch_staged_mode(const LaunchArgs& a, const Tin* vol, const Batch&
 
 template <typename Tin>
 static hipError_t forward_typed(const LaunchArgs& a, const RenderPlan& p, const Tin* vol,
-                                void* workspace, float* out, float* s_out, hipStream_t stream)
+                                void* workspace, float* out, float* s_out, hipStream_t stream,
+                                bool reuse_copy)
 {
     const Batch b = make_batch(a, &p, 0);
     if (p.staged) {
@@ -1500,8 +1501,10 @@ static hipError_t forward_typed(const LaunchArgs& a, const RenderPlan& p, const 
     }
     const uint32_t bytes = p.cells ? a.V.cell_total_bytes : a.V.total_bytes;
     if (p.zpair) {
-        hipError_t e = launch_zpair_typed<Tin>(a, p, vol, workspace, stream);
-        if (e != hipSuccess) return e;
+        if (!reuse_copy) {
+            hipError_t e = launch_zpair_typed<Tin>(a, p, vol, workspace, stream);
+            if (e != hipSuccess) return e;
+        }
         const float* mu = static_cast<const float*>(workspace);
         const Tin* pr = static_cast<const Tin*>(workspace);
         if (p.padded) {
@@ -1522,8 +1525,10 @@ static hipError_t forward_typed(const LaunchArgs& a, const RenderPlan& p, const 
         return hipGetLastError();
     }
     if (p.cells) {
-        hipError_t e = launch_cells_typed<Tin>(a, p, vol, workspace, stream);
-        if (e != hipSuccess) return e;
+        if (!reuse_copy) {
+            hipError_t e = launch_cells_typed<Tin>(a, p, vol, workspace, stream);
+            if (e != hipSuccess) return e;
+        }
         if (p.mapped) {
             const float* c = static_cast<const float*>(workspace);
             if (a.clip == kClipNearFar)
@@ -1542,8 +1547,10 @@ static hipError_t forward_typed(const LaunchArgs& a, const RenderPlan& p, const 
     // linear reads: the caller's volume, or its mapped fp32 copy
     if (p.mapped) {
         float* mu = static_cast<float*>(workspace);
-        hipError_t e = launch_transfer_typed<Tin>(a, p, vol, mu, stream);
-        if (e != hipSuccess) return e;
+        if (!reuse_copy) {
+            hipError_t e = launch_transfer_typed<Tin>(a, p, vol, mu, stream);
+            if (e != hipSuccess) return e;
+        }
         if (a.V.n[0] >= 2)
             launch_march_mode<float, Layout::Pair, kClipBox>(a, mu, bytes, b, out, s_out, stream);
         else
@@ -1557,14 +1564,15 @@ static hipError_t forward_typed(const LaunchArgs& a, const RenderPlan& p, const 
 }
 
 hipError_t launch_forward(const LaunchArgs& a, const RenderPlan& plan, const void* vol, int dtype,
-                          void* workspace, float* out, float* s_out, hipStream_t stream)
+                          void* workspace, float* out, float* s_out, hipStream_t stream,
+                          bool reuse_copy)
 {
     if ((long long)a.n_views * a.C * a.H * a.W == 0) return hipSuccess;
     if (dtype == 0)
         return forward_typed<float>(a, plan, static_cast<const float*>(vol), workspace, out, s_out,
-                                    stream);
+                                    stream, reuse_copy);
     return forward_typed<uint16_t>(a, plan, static_cast<const uint16_t*>(vol), workspace, out,
-                                   s_out, stream);
+                                   s_out, stream, reuse_copy);
 }
 
 hipError_t launch_fill(float* p, size_t n, hipStream_t stream)

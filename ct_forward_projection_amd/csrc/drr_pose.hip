@@ -798,7 +798,7 @@ static void launch_pose_staged(const LaunchArgs& a, const T* vol, const Batch& b
 
 hipError_t launch_backward_pose(const LaunchArgs& a, const RenderPlan& plan, const void* vol,
                                 int dtype, void* read_buf, double* acc, const float* grad_out,
-                                float* grad_poses, hipStream_t stream)
+                                float* grad_poses, hipStream_t stream, bool reuse_copy)
 {
     if (a.n_views == 0) return hipSuccess;
     const int n_acc = 12 * a.n_views;
@@ -828,8 +828,10 @@ hipError_t launch_backward_pose(const LaunchArgs& a, const RenderPlan& plan, con
                                stream, acc, a.poses, a.n_views, grad_poses);
             return hipGetLastError();
         }
-        e = launch_read_copy(a, plan, vol, dtype, read_buf, stream);
-        if (e != hipSuccess) return e;
+        if (!reuse_copy) {
+            e = launch_read_copy(a, plan, vol, dtype, read_buf, stream);
+            if (e != hipSuccess) return e;
+        }
         Batch b;
         b.src_stride = (uint64_t)plan.per_volume_bytes;
         b.grad_stride = 0;

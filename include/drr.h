@@ -117,6 +117,25 @@ int drr_forward(const void *volume, int dtype, int nz, int ny, int nx, const flo
                 int n_samples, int mode, float *out, float *line_integral, void *workspace,
                 size_t workspace_bytes, void *stream);
 
+/* drr_forward without the relayout, for renders of one volume from changing
+ * poses (the 2D/3D registration and pose estimation that the flashdrr
+ * overview names as its workloads).  `workspace` must already hold the read
+ * copy that an earlier drr_forward call wrote into it (the volume's
+ * corner-cell or z-pair copy) for the same volume contents, dtype, nz, ny,
+ * nx, n_views, det_h, det_w and n_samples: those fix the read plan and
+ * nothing else does, so the poses, K, spacing and mode may change between
+ * the calls.  When the plan reads the
+ * caller's volume itself (LDS-staged boxes, or launches too sparse for a copy)
+ * the call is drr_forward.  Arguments, validation and errors are drr_forward's.
+ * The library cannot check the copy: after the volume's contents change, or
+ * with a workspace that holds no copy of it, the images are of whatever the
+ * workspace holds (reads stay inside it). */
+int drr_forward_reuse(const void *volume, int dtype, int nz, int ny, int nx,
+                      const float *spacing, const float *K, const float *poses, int n_views,
+                      int det_h, int det_w, int n_samples, int mode, float *out,
+                      float *line_integral, void *workspace, size_t workspace_bytes,
+                      void *stream);
+
 /* drr_forward for callers that cannot allocate device memory (code under HIP
  * graph capture, serving loops, harnesses that forbid hipMalloc): the same
  * arguments without the workspace, and the same launches and results.  What
@@ -181,6 +200,20 @@ int drr_backward_pose(const void *volume, int dtype, int nz, int ny, int nx, con
                       const float *K, const float *poses, int n_views, int det_h, int det_w,
                       int n_samples, int mode, const float *grad_out, float *grad_poses,
                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* drr_backward_pose without the relayout, as drr_forward_reuse for the
+ * forward: `workspace` must already hold the read copy that an earlier
+ * drr_backward_pose call wrote into it for the same volume contents, dtype,
+ * nz, ny, nx, n_views, det_h, det_w and n_samples (poses, K, spacing, mode and
+ * grad_out may change).  When the plan reads the caller's volume itself the
+ * call is drr_backward_pose.  Arguments, validation and errors are
+ * drr_backward_pose's; the library cannot check the copy (see
+ * drr_forward_reuse). */
+int drr_backward_pose_reuse(const void *volume, int dtype, int nz, int ny, int nx,
+                            const float *spacing, const float *K, const float *poses, int n_views,
+                            int det_h, int det_w, int n_samples, int mode, const float *grad_out,
+                            float *grad_poses, void *workspace, size_t workspace_bytes,
+                            void *stream);
 
 /* Forward DRR in the cell-constant (Siddon) model (diffct 2.1.0, "Why
  * diffct": project() and backproject() are an exact adjoint pair for the

@@ -92,6 +92,12 @@ int main()
            DRR_ERR_WORKSPACE_TOO_SMALL, "forward workspace");
     expect(drr_forward(D, 0, 8, 8, 8, sp.data(), K.data(), nullptr, 0, 4, 4, 8, 0, nullptr, nullptr, nullptr, 0, nullptr),
            DRR_OK, "forward empty");
+    expect(drr_forward_reuse(D, 0, 8, 8, 8, sp_bad.data(), K.data(), Df, 1, 4, 4, 8, 0, Df, nullptr, nullptr, 0, nullptr),
+           DRR_ERR_INVALID_ARGUMENT, "reuse forward spacing 0");
+    expect(drr_forward_reuse(D, 0, 8, 8, 8, sp.data(), K.data(), Df, 64, 16, 16, 8, 0, Df, nullptr, nullptr, 0, nullptr),
+           DRR_ERR_WORKSPACE_TOO_SMALL, "reuse forward workspace");
+    expect(drr_forward_reuse(D, 0, 8, 8, 8, sp.data(), K.data(), nullptr, 0, 4, 4, 8, 0, nullptr, nullptr, nullptr, 0, nullptr),
+           DRR_OK, "reuse forward empty");
     expect(drr_forward_no_alloc(D, 0, 512, 512, 512, sp.data(), K.data(), Df, 64, 256, 256, 256, 0, Df, nullptr, nullptr),
            DRR_ERR_UNSUPPORTED, "no-alloc forward beyond the scratch");
     expect(drr_forward_no_alloc(nullptr, 0, 8, 8, 8, sp.data(), K.data(), Df, 1, 4, 4, 8, 0, Df, nullptr, nullptr),
@@ -117,6 +123,10 @@ int main()
            DRR_ERR_WORKSPACE_TOO_SMALL, "pose backward workspace");
     expect(drr_backward_pose(D, 0, 8, 8, 8, sp.data(), K.data(), Df, 1, 4, 4, 8, 0, nullptr, Df, D, 4096, nullptr),
            DRR_ERR_INVALID_ARGUMENT, "pose backward grad_out NULL");
+    expect(drr_backward_pose_reuse(D, 0, 8, 8, 8, sp.data(), K.data(), Df, 1, 4, 4, 8, 0, Df, Df, nullptr, 0, nullptr),
+           DRR_ERR_WORKSPACE_TOO_SMALL, "reuse pose backward workspace");
+    expect(drr_backward_pose_reuse(D, 0, 8, 8, 8, sp.data(), K.data(), Df, 1, 4, 4, 8, 0, nullptr, Df, D, 4096, nullptr),
+           DRR_ERR_INVALID_ARGUMENT, "reuse pose backward grad_out NULL");
     expect(drr_forward_siddon(D, 0, 8, 8, 8, sp_bad.data(), K.data(), Df, 1, 4, 4, 0, Df, nullptr, nullptr),
            DRR_ERR_INVALID_ARGUMENT, "siddon forward spacing");
     expect(drr_backward_volume_siddon(8, 8, 8, sp.data(), K.data(), Df, 1, 4, 4, 0, Df, nullptr, Df, nullptr),

@@ -46,13 +46,14 @@ K = _f(500.0, 0.0, 32.0, 0.0, 500.0, 32.0, 0.0, 0.0, 1.0)
 DUMMY = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
 
 
-def fwd(**kw):
+def fwd(reuse=False, **kw):
     args = dict(volume=DUMMY, dtype=0, nz=8, ny=8, nx=8, spacing=SP, K=K, poses=DUMMY,
                 n_views=1, det_h=4, det_w=4, n_samples=8, mode=0, out=DUMMY, s=None,
                 ws=None, ws_bytes=0, stream=None)
     args.update(kw)
     lib = drr.library()
-    return lib.drr_forward(args["volume"], args["dtype"], args["nz"], args["ny"], args["nx"],
+    fn = lib.drr_forward_reuse if reuse else lib.drr_forward
+    return fn(args["volume"], args["dtype"], args["nz"], args["ny"], args["nx"],
                            args["spacing"], args["K"], args["poses"], args["n_views"],
                            args["det_h"], args["det_w"], args["n_samples"], args["mode"],
                            args["out"], args["s"], args["ws"], args["ws_bytes"], args["stream"])
@@ -96,6 +97,32 @@ def test_forward_rejects_invalid_arguments(kw, status):
 ])
 def test_backward_rejects_invalid_arguments(kw, status):
     assert bwd(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nz=0), 1), (dict(n_samples=0), 1), (dict(mode=2), 1), (dict(dtype=3), 1),
+    (dict(volume=None), 1), (dict(poses=None), 1), (dict(out=None), 1),
+    (dict(spacing=_f(1.0, 0.0, 1.0)), 1), (dict(nz=2048, ny=2048, nx=1024), 2),
+    (dict(n_views=64, det_h=16, det_w=16), 3),               # the copy's workspace is missing
+])
+def test_reuse_forward_validates_like_the_forward(kw, status):
+    """drr_forward_reuse checks its arguments as drr_forward does (the same
+    status for the same call) before anything is enqueued."""
+    assert fwd(reuse=True, **kw) == status == fwd(**kw)
+    assert drr.library().drr_last_error() != b""
+    assert fwd(reuse=True, n_views=0, poses=None, out=None) == 0
+
+
+def test_reuse_pose_backward_validates_like_the_pose_backward():
+    lib = drr.library()
+    for fn in (lib.drr_backward_pose, lib.drr_backward_pose_reuse):
+        # no workspace, then grad_out NULL, then an unknown dtype
+        assert fn(DUMMY, 0, 8, 8, 8, SP, K, DUMMY, 1, 4, 4, 8, 0, DUMMY, DUMMY, None, 0,
+                  None) == 3
+        assert fn(DUMMY, 0, 8, 8, 8, SP, K, DUMMY, 1, 4, 4, 8, 0, None, DUMMY, DUMMY, 4096,
+                  None) == 1
+        assert fn(DUMMY, 5, 8, 8, 8, SP, K, DUMMY, 1, 4, 4, 8, 0, DUMMY, DUMMY, DUMMY, 4096,
+                  None) == 1
 
 
 def test_empty_forward_is_a_valid_no_op():
