@@ -879,7 +879,11 @@ def profile_summary(root: str):
         traffic["cases"][case] = figures
         if not rows:
             continue
-        dominant = rows[0][0]
+        # the file is named for the slowest kernel of the case's forward and
+        # backward passes (the pose pass, when the case has others, times alike
+        # and would swap the name from run to run)
+        named = [r[0] for r in rows if not (r[0].startswith("drr_pose") and len(meta["passes"]) > 1)]
+        dominant = named[0] if named else rows[0][0]
         lines = [f"# {dominant} and the other kernels of `{case}` ({meta['workload']})", "",
                  f"Workload: volume {meta['volume']} {meta['dtype']}, {meta['views']} view(s) "
                  f"{meta['det'][0]}x{meta['det'][1]}, {meta['n_samples']} samples per ray; "
