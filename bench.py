@@ -524,11 +524,22 @@ class RenderCase:
                                        mode, self.g, self.out, self.aux, f, clip, margin, tf,
                                        grad_volume=self.grad, workspace=self.ws_b)
 
-    def pose_backward(self):
+    def pose_backward(self, reuse_copy=False):
         import ct_forward_projection_amd as drr
         sp, K, P, H, Wd, N, mode, f, clip, margin, tf = self.args
         drr.drr_render_backward_pose(self.vol, sp, K, P, H, Wd, N, mode, self.g, f, clip, margin,
-                                     tf, grad_poses=self.grad_poses, workspace=self.ws_p)
+                                     tf, grad_poses=self.grad_poses, workspace=self.ws_p,
+                                     reuse_copy=reuse_copy)
+
+    def forward_reuse(self):
+        """The render reading the copy the last render left in its workspace."""
+        import ct_forward_projection_amd as drr
+        sp, K, P, H, Wd, N, mode, f, clip, margin, tf = self.args
+        drr.drr_render(self.vol, sp, K, P, H, Wd, N, mode, f, clip, margin, tf, out=self.out,
+                       aux=self.aux, workspace=self.ws_f, reuse_copy=True)
+
+    def pose_backward_reuse(self):
+        self.pose_backward(reuse_copy=True)
 
 
 def frontend_lines(dev):
@@ -587,7 +598,18 @@ def frontend_lines(dev):
                 "backward_ms": round(b_ms, 4),
                 "backward_gsamples_s": round(c.samples / b_ms / 1e6, 1),
                 "pose_backward_ms": round(p_ms, 4),
-                "pose_backward_gsamples_s": round(c.samples / p_ms / 1e6, 1)}
+                "pose_backward_gsamples_s": round(c.samples / p_ms / 1e6, 1),
+                "registration_step_fps": round(views / (f_ms + p_ms) * 1e3, 1)}
+        if c.ws_f is not None:
+            # a registration loop over the fixed volume: both calls read the
+            # copies the previous step left in their workspaces
+            c.forward()
+            c.pose_backward()
+            fr_ms, pr_ms = time_graph([c.forward_reuse, c.pose_backward_reuse])
+            line["forward_reuse_ms"] = round(fr_ms, 4)
+            line["forward_reuse_fps"] = round(views / fr_ms * 1e3, 1)
+            line["pose_backward_reuse_ms"] = round(pr_ms, 4)
+            line["registration_step_reuse_fps"] = round(views / (fr_ms + pr_ms) * 1e3, 1)
         lines[name] = line
         log(f"front end {name}: {line}")
         del c

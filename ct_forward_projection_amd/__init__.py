@@ -80,12 +80,16 @@ def library() -> ctypes.CDLL:
         lib.drr_render.argtypes = [P, I, I, I, I, I, I, P, P, P, I, I, I, I, I, F, I, F, P, P, I,
                                    P, P, P, Z, P]
         lib.drr_render.restype = I
+        lib.drr_render_reuse.argtypes = lib.drr_render.argtypes
+        lib.drr_render_reuse.restype = I
         lib.drr_render_backward_volume.argtypes = [P, I, I, I, I, I, I, P, P, P, I, I, I, I, I, F,
                                                    I, F, P, P, I, P, P, P, P, P, Z, P]
         lib.drr_render_backward_volume.restype = I
         lib.drr_render_backward_pose.argtypes = [P, I, I, I, I, I, I, P, P, P, I, I, I, I, I, F, I,
                                                  F, P, P, I, P, P, P, Z, P]
         lib.drr_render_backward_pose.restype = I
+        lib.drr_render_backward_pose_reuse.argtypes = lib.drr_render_backward_pose.argtypes
+        lib.drr_render_backward_pose_reuse.restype = I
         lib.drr_intrinsics_from_fov.argtypes = [F, I, I, P]
         lib.drr_intrinsics_from_fov.restype = I
         lib.drr_poses_from_view_matrices.argtypes = [P, I, P, I, I, I, P, P, P]
@@ -478,10 +482,13 @@ def drr_render(volume: torch.Tensor, spacing, K, poses: torch.Tensor, det_h: int
                clip: int = CLIP_BOX, margin: float = 30.0, transfer=None,
                out: Optional[torch.Tensor] = None, aux=True,
                workspace: Optional[torch.Tensor] = None,
-               stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+               stream=None, reuse_copy: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Render ``volume`` (B, C, nz, ny, nx) (or (nz, ny, nx)) for ``poses``
     (V, 3, 4), V a multiple of B (view v renders volume v // (V // B)).
-    Returns (image (V, C, det_h, det_w) fp32, optical depth or None)."""
+    Returns (image (V, C, det_h, det_w) fp32, optical depth or None).  With
+    ``reuse_copy`` the call skips the relayout (``drr_render_reuse``):
+    ``workspace`` must hold the read copy an earlier render made of the same
+    volume, transfer function and clip for the same launch shape."""
     volume = _device_tensor(volume, "volume")
     dtype = _volume_dtype(volume)
     poses = _device_tensor(poses, "poses", torch.float32)
@@ -506,10 +513,12 @@ def drr_render(volume: torch.Tensor, spacing, K, poses: torch.Tensor, det_h: int
             raise ValueError("aux has the wrong size")
     need = drr_render_workspace_bytes(B, C, nz, ny, nx, dtype, V, det_h, det_w, n_samples, mode,
                                       clip, nk, 0)
+    if reuse_copy and need and workspace is None:
+        raise ValueError("reuse_copy needs the workspace that holds the read copy")
     if workspace is None:
         workspace = _workspace(need, dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(library().drr_render(
+    _check((library().drr_render_reuse if reuse_copy else library().drr_render)(
         _ptr(volume), dtype, B, C, nz, ny, nx, _host_floats(spacing, 3), _host_floats(K, 9),
         _ptr(poses), V, det_h, det_w, n_samples, mode, float(density_factor), clip, float(margin),
         xp, yp, nk, _ptr(out), _ptr(aux), _ptr(workspace), ws_bytes, _stream(stream)))
@@ -575,9 +584,11 @@ def drr_render_backward_pose(volume: torch.Tensor, spacing, K, poses: torch.Tens
                              margin: float = 30.0, transfer=None,
                              grad_poses: Optional[torch.Tensor] = None,
                              workspace: Optional[torch.Tensor] = None,
-                             stream=None) -> torch.Tensor:
+                             stream=None, reuse_copy: bool = False) -> torch.Tensor:
     """dL/dP (V, 3, 4) for L = sum(grad_out * image) of ``drr_render`` (every
-    mode, either clip), summed over each view's channels."""
+    mode, either clip), summed over each view's channels.  With ``reuse_copy``
+    (``drr_render_backward_pose_reuse``) ``workspace`` must hold the read copy
+    an earlier call made of the same volume for the same launch shape."""
     volume = _device_tensor(volume, "volume")
     dtype = _volume_dtype(volume)
     poses = _device_tensor(poses, "poses", torch.float32)
@@ -592,10 +603,13 @@ def drr_render_backward_pose(volume: torch.Tensor, spacing, K, poses: torch.Tens
     grad_poses = _device_tensor(grad_poses, "grad_poses", torch.float32)
     need = drr_render_workspace_bytes(B, C, nz, ny, nx, dtype, V, det_h, det_w, n_samples, mode,
                                       clip, nk, 2)
+    if reuse_copy and workspace is None:
+        raise ValueError("reuse_copy needs the workspace that holds the read copy")
     if workspace is None:
         workspace = _workspace(need, volume.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(library().drr_render_backward_pose(
+    _check((library().drr_render_backward_pose_reuse if reuse_copy
+            else library().drr_render_backward_pose)(
         _ptr(volume), dtype, B, C, nz, ny, nx, _host_floats(spacing, 3), _host_floats(K, 9),
         _ptr(poses), V, det_h, det_w, n_samples, mode, float(density_factor), clip, float(margin),
         xp, yp, nk, _ptr(grad_out), _ptr(grad_poses), _ptr(workspace), ws_bytes, _stream(stream)))

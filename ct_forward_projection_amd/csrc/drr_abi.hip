@@ -326,6 +326,45 @@ int forward_into(const void* volume, int dtype, int nz, int ny, int nx, const fl
     return ok();
 }
 
+// drr_render's body; with reuse_copy the workspace already holds the read copy.
+int render_into(const void* volume, int dtype, int n_volumes, int n_channels, int nz, int ny,
+                int nx, const float* spacing, const float* K, const float* poses, int n_views,
+                int det_h, int det_w, int n_samples, int mode, float density_factor, int clip,
+                float margin, const float* tf_xp, const float* tf_yp, int tf_knots, float* out,
+                float* aux, void* workspace, size_t workspace_bytes, void* stream,
+                bool reuse_copy)
+{
+    if (dtype != DRR_F32 && dtype != DRR_BF16)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    const int eb = dtype == DRR_F32 ? 4 : 2;
+    drr::LaunchArgs a;
+    int st = check_geometry(nz, ny, nx, eb, spacing, K, poses, n_views, det_h, det_w, n_samples,
+                            mode, a, DRR_ALPHA_COMPOSITE);
+    if (st != DRR_OK) return st;
+    st = check_render(n_volumes, n_channels, n_views, density_factor, clip, margin, tf_xp, tf_yp,
+                      tf_knots, a);
+    if (st != DRR_OK) return st;
+    if (!volume) return fail(DRR_ERR_INVALID_ARGUMENT, "volume is NULL");
+    const long long n_out = (long long)n_views * n_channels * det_h * det_w;
+    if (n_out > 0 && !out) return fail(DRR_ERR_INVALID_ARGUMENT, "out is NULL");
+    const drr::RenderPlan plan = drr::plan_render(n_volumes, n_channels, nz, ny, nx, eb, n_views,
+                                                  det_h, det_w, n_samples, clip, a.has_tf, true);
+    if (!plan.fits)
+        return fail(DRR_ERR_UNSUPPORTED, "one channel-volume of the march's copy exceeds 4 GiB");
+    if (workspace_bytes < plan.workspace_bytes)
+        return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
+                    workspace_bytes, plan.workspace_bytes);
+    if (plan.workspace_bytes > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
+        return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+    if (n_out == 0) return ok();
+    set_read_geometry(a.V, plan);
+    hipError_t e = drr::launch_forward(a, plan, volume, dtype, workspace, out, aux,
+                                       static_cast<hipStream_t>(stream), reuse_copy);
+    if (e != hipSuccess)
+        return fail(DRR_ERR_HIP, "render launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -543,35 +582,21 @@ int drr_render(const void* volume, int dtype, int n_volumes, int n_channels, int
                float margin, const float* tf_xp, const float* tf_yp, int tf_knots, float* out,
                float* aux, void* workspace, size_t workspace_bytes, void* stream)
 {
-    if (dtype != DRR_F32 && dtype != DRR_BF16)
-        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
-    const int eb = dtype == DRR_F32 ? 4 : 2;
-    drr::LaunchArgs a;
-    int st = check_geometry(nz, ny, nx, eb, spacing, K, poses, n_views, det_h, det_w, n_samples,
-                            mode, a, DRR_ALPHA_COMPOSITE);
-    if (st != DRR_OK) return st;
-    st = check_render(n_volumes, n_channels, n_views, density_factor, clip, margin, tf_xp, tf_yp,
-                      tf_knots, a);
-    if (st != DRR_OK) return st;
-    if (!volume) return fail(DRR_ERR_INVALID_ARGUMENT, "volume is NULL");
-    const long long n_out = (long long)n_views * n_channels * det_h * det_w;
-    if (n_out > 0 && !out) return fail(DRR_ERR_INVALID_ARGUMENT, "out is NULL");
-    const drr::RenderPlan plan = drr::plan_render(n_volumes, n_channels, nz, ny, nx, eb, n_views,
-                                                  det_h, det_w, n_samples, clip, a.has_tf, true);
-    if (!plan.fits)
-        return fail(DRR_ERR_UNSUPPORTED, "one channel-volume of the march's copy exceeds 4 GiB");
-    if (workspace_bytes < plan.workspace_bytes)
-        return fail(DRR_ERR_WORKSPACE_TOO_SMALL, "workspace of %zu bytes, %zu needed",
-                    workspace_bytes, plan.workspace_bytes);
-    if (plan.workspace_bytes > 0 && (!workspace || ((uintptr_t)workspace & 255u)))
-        return fail(DRR_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
-    if (n_out == 0) return ok();
-    set_read_geometry(a.V, plan);
-    hipError_t e = drr::launch_forward(a, plan, volume, dtype, workspace, out, aux,
-                                       static_cast<hipStream_t>(stream));
-    if (e != hipSuccess)
-        return fail(DRR_ERR_HIP, "render launch failed: %s", hipGetErrorString(e));
-    return ok();
+    return render_into(volume, dtype, n_volumes, n_channels, nz, ny, nx, spacing, K, poses,
+                       n_views, det_h, det_w, n_samples, mode, density_factor, clip, margin, tf_xp,
+                       tf_yp, tf_knots, out, aux, workspace, workspace_bytes, stream, false);
+}
+
+int drr_render_reuse(const void* volume, int dtype, int n_volumes, int n_channels, int nz, int ny,
+                     int nx, const float* spacing, const float* K, const float* poses,
+                     int n_views, int det_h, int det_w, int n_samples, int mode,
+                     float density_factor, int clip, float margin, const float* tf_xp,
+                     const float* tf_yp, int tf_knots, float* out, float* aux, void* workspace,
+                     size_t workspace_bytes, void* stream)
+{
+    return render_into(volume, dtype, n_volumes, n_channels, nz, ny, nx, spacing, K, poses,
+                       n_views, det_h, det_w, n_samples, mode, density_factor, clip, margin, tf_xp,
+                       tf_yp, tf_knots, out, aux, workspace, workspace_bytes, stream, true);
 }
 
 int drr_render_backward_volume(const void* volume, int dtype, int n_volumes, int n_channels,
@@ -711,6 +736,28 @@ int drr_render_backward_pose(const void* volume, int dtype, int n_volumes, int n
     if (st != DRR_OK) return st;
     return pose_backward(a, volume, dtype, grad_out, grad_poses, workspace, workspace_bytes,
                          stream);
+}
+
+int drr_render_backward_pose_reuse(const void* volume, int dtype, int n_volumes,
+                                   int n_channels, int nz, int ny, int nx, const float* spacing,
+                                   const float* K, const float* poses, int n_views, int det_h,
+                                   int det_w, int n_samples, int mode, float density_factor,
+                                   int clip, float margin, const float* tf_xp,
+                                   const float* tf_yp, int tf_knots, const float* grad_out,
+                                   float* grad_poses, void* workspace, size_t workspace_bytes,
+                                   void* stream)
+{
+    if (dtype != DRR_F32 && dtype != DRR_BF16)
+        return fail(DRR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    drr::LaunchArgs a;
+    int st = check_geometry(nz, ny, nx, dtype == DRR_F32 ? 4 : 2, spacing, K, poses, n_views,
+                            det_h, det_w, n_samples, mode, a, DRR_ALPHA_COMPOSITE);
+    if (st != DRR_OK) return st;
+    st = check_render(n_volumes, n_channels, n_views, density_factor, clip, margin, tf_xp, tf_yp,
+                      tf_knots, a);
+    if (st != DRR_OK) return st;
+    return pose_backward(a, volume, dtype, grad_out, grad_poses, workspace, workspace_bytes,
+                         stream, true);
 }
 
 int drr_forward_siddon(const void* volume, int dtype, int nz, int ny, int nx,

@@ -324,6 +324,21 @@ int drr_render(const void *volume, int dtype, int n_volumes, int n_channels, int
                float margin, const float *tf_xp, const float *tf_yp, int tf_knots, float *out,
                float *aux, void *workspace, size_t workspace_bytes, void *stream);
 
+/* drr_render without the relayout (as drr_forward_reuse for drr_forward):
+ * `workspace` must already hold the read copy that an earlier drr_render call
+ * wrote into it for the same volume contents, dtype, n_volumes, n_channels,
+ * nz, ny, nx, n_views, det_h, det_w, n_samples, clip and transfer function
+ * (the copy is of the mapped values when there is one); poses, K, spacing,
+ * mode, density_factor and margin may change.  When the plan reads the
+ * caller's volumes themselves the call is drr_render.  Arguments, validation
+ * and errors are drr_render's; the library cannot check the copy. */
+int drr_render_reuse(const void *volume, int dtype, int n_volumes, int n_channels, int nz,
+                     int ny, int nx, const float *spacing, const float *K, const float *poses,
+                     int n_views, int det_h, int det_w, int n_samples, int mode,
+                     float density_factor, int clip, float margin, const float *tf_xp,
+                     const float *tf_yp, int tf_knots, float *out, float *aux, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
 /* Gradient of L = sum grad_out * out with respect to the input volume x of
  * drr_render (same arguments).  Per sample k of a ray, dL/dmu at its trilinear
  * corners receives grad_out * c_k * w_corner with
@@ -376,6 +391,20 @@ int drr_render_backward_pose(const void *volume, int dtype, int n_volumes, int n
                              float margin, const float *tf_xp, const float *tf_yp, int tf_knots,
                              const float *grad_out, float *grad_poses, void *workspace,
                              size_t workspace_bytes, void *stream);
+
+/* drr_render_backward_pose without the relayout: `workspace` must already
+ * hold the read copy that an earlier drr_render_backward_pose call wrote into
+ * it for the same volume contents and launch shape as drr_render_reuse lists
+ * (poses, K, spacing, mode, density_factor, margin and grad_out may change).
+ * Arguments, validation and errors are drr_render_backward_pose's; the
+ * library cannot check the copy. */
+int drr_render_backward_pose_reuse(const void *volume, int dtype, int n_volumes, int n_channels,
+                                   int nz, int ny, int nx, const float *spacing, const float *K,
+                                   const float *poses, int n_views, int det_h, int det_w,
+                                   int n_samples, int mode, float density_factor, int clip,
+                                   float margin, const float *tf_xp, const float *tf_yp,
+                                   int tf_knots, const float *grad_out, float *grad_poses,
+                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
  * Camera conventions of the flashdrr front end (flashdrr.rendering API:

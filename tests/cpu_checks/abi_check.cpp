@@ -146,6 +146,16 @@ int main()
     expect(drr_render(D, 0, 1, 1, 8, 8, 8, sp.data(), K.data(), Df, 1, 4, 4, 8, 0, 1.0f, 5, 30.0f,
                       nullptr, nullptr, 0, Df, nullptr, nullptr, 0, nullptr),
            DRR_ERR_INVALID_ARGUMENT, "render clip");
+    expect(drr_render_reuse(D, 0, 2, 1, 8, 8, 8, sp.data(), K.data(), Df, 3, 4, 4, 8, 0, 1.0f, 0,
+                            30.0f, nullptr, nullptr, 0, Df, nullptr, nullptr, 0, nullptr),
+           DRR_ERR_INVALID_ARGUMENT, "reuse render views per volume");
+    expect(drr_render_reuse(D, 0, 1, 1, 8, 8, 8, sp.data(), K.data(), Df, 1, 4, 4, 8, 0, 1.0f, 5,
+                            30.0f, nullptr, nullptr, 0, Df, nullptr, nullptr, 0, nullptr),
+           DRR_ERR_INVALID_ARGUMENT, "reuse render clip");
+    expect(drr_render_backward_pose_reuse(D, 0, 1, 1, 8, 8, 8, sp.data(), K.data(), Df, 1, 4, 4,
+                                          8, 0, 1.0f, 0, 30.0f, nullptr, nullptr, 0, Df, Df,
+                                          nullptr, 0, nullptr),
+           DRR_ERR_WORKSPACE_TOO_SMALL, "reuse render pose workspace");
     expect(drr_render_backward_volume(D, 0, 1, 1, 8, 8, 8, sp.data(), K.data(), Df, 1, 4, 4, 8, 2,
                                       1.0f, 0, 30.0f, nullptr, nullptr, 0, Df, nullptr, Df, Df,
                                       nullptr, 0, nullptr),

@@ -126,3 +126,55 @@ def test_reuse_without_a_workspace_is_refused(dev):
     with pytest.raises(ValueError):
         drr.drr_backward_pose(vol, w.spacing, w.K, P, 40, 36, 80, w.mode,
                               torch.zeros((8, 40, 36), device=dev), reuse_copy=True)
+
+
+# drr_render / drr_render_backward_pose: 2 volumes x 2 channels from HU-like
+# values through the transfer function (the copy holds the mapped values), the
+# box clip (mapped z-pairs) and the near/far range (zero-padded copies)
+KNOTS = (np.array([[-1000.0, 0.0, 1500.0], [-600.0, 100.0, 1200.0]], dtype=np.float32),
+         np.array([[0.0, 0.02, 0.05], [0.005, 0.0, 0.04]], dtype=np.float32))
+
+
+@pytest.mark.parametrize("clip,mode", [(drr.CLIP_BOX, drr.BEER_LAMBERT),
+                                       (drr.CLIP_NEAR_FAR, drr.ALPHA_COMPOSITE)])
+def test_reused_render_copy(dev, clip, mode):
+    rng = np.random.default_rng(510 + clip)
+    shape, det, N, f, margin = (30, 26, 34), (40, 44), 48, 30.0, 3.0
+    vol = rng.uniform(-1100.0, 1600.0, size=(2, 2) + shape).astype(np.float32)
+    spacing = np.array([1.0, 1.25, 0.8], dtype=np.float32)
+    K = W.intrinsics(1.2 * 44 * 60.0 / 34.0, 22.3, 19.8)
+    P1 = W.random_poses(6, 60.0, 30.0, 1.5, seed=511)
+    P2 = W.random_poses(6, 60.0, 30.0, 1.5, seed=512)
+    g = rng.uniform(-1.0, 1.0, size=(6, 2) + det).astype(np.float32)
+    v = torch.from_numpy(vol).to(dev)
+    gt = torch.from_numpy(g).to(dev)
+    need = drr.drr_render_workspace_bytes(2, 2, *shape, drr.F32, 6, det[0], det[1], N, mode,
+                                          clip, 3, 0)
+    need_p = drr.drr_render_workspace_bytes(2, 2, *shape, drr.F32, 6, det[0], det[1], N, mode,
+                                            clip, 3, 2)
+    say(f"case: reuse render clip={clip} mode={mode} (copy {need} bytes, pose workspace {need_p})")
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_p = torch.empty(need_p, dtype=torch.uint8, device=dev)
+    kw = dict(density_factor=f, clip=clip, margin=margin, transfer=KNOTS)
+    args = (v, spacing, K)
+    p1, p2 = torch.from_numpy(P1).to(dev), torch.from_numpy(P2).to(dev)
+    drr.drr_render(*args, p1, det[0], det[1], N, mode, workspace=ws, **kw)
+    img_r, tau_r = drr.drr_render(*args, p2, det[0], det[1], N, mode, workspace=ws,
+                                  reuse_copy=True, **kw)
+    img_f, tau_f = drr.drr_render(*args, p2, det[0], det[1], N, mode, **kw)
+    drr.drr_render_backward_pose(*args, p1, det[0], det[1], N, mode, gt, workspace=ws_p, **kw)
+    gp_r = drr.drr_render_backward_pose(*args, p2, det[0], det[1], N, mode, gt, workspace=ws_p,
+                                        reuse_copy=True, **kw)
+    gp_f = drr.drr_render_backward_pose(*args, p2, det[0], det[1], N, mode, gt, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(img_r, img_f) and torch.equal(tau_r, tau_f), "reuse differs from a fresh call"
+    ref, _ = oracle.render(vol, spacing, K, P2, det[0], det[1], N, mode, **kw)
+    check_forward(img_r, ref, FWD, f"reuse render c{clip} m{mode}")
+    a, b = gp_r.cpu().double().numpy(), gp_f.cpu().double().numpy()
+    ref_p = oracle.render_pose_gradient(vol, spacing, K, P2, det[0], det[1], N, mode, g, **kw)
+    worst = max(normwise_err(a[i], ref_p[i]) for i in range(6))
+    say(f"reuse render pose c{clip} m{mode}: normwise err {worst:.3e} (bar {GRAD:g})")
+    for i in range(6):
+        assert normwise_err(a[i], b[i]) <= 1e-6, "reuse differs from a fresh call"
+    assert worst <= GRAD
