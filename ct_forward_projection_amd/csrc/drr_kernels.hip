@@ -915,6 +915,10 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
 
     // fixed-point scale of this tile
     float B = 0.0f, Cs = 0.0f;
+    float ray_cmax = 0.0f, ray_n = 0.0f;          // this ray's coefficient bound and n
+    // compositing with values known to be >= 0: the bound also holds per chunk
+    // from the running state (see the chunk loop)
+    const bool alpha_closed = ALPHA && vbound != nullptr && vbound[2 * cvol] == 0 && bt.f >= 0.0f;
     if (active) {
         const double dq_inf = fmax(fmax(fabs((double)R.dq[0]), fabs((double)R.dq[1])),
                                    fabs((double)R.dq[2])) * 2.3283064365386963e-10;
@@ -977,6 +981,8 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
         if (active) {
             B = (float)((double)cmax * n);
             Cs = (float)n;
+            ray_cmax = cmax;
+            ray_n = (float)n;
         }
     }
     // the window starts zeroed here; each flush zeroes the entries it read, so
@@ -1034,6 +1040,35 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
         }
         if (fixed_ok && vol_cells <= win_cap) {
             const int n_win = (int)vol_cells;
+            // this chunk's fixed-point scale.  Compositing's coefficients shrink
+            // along the ray with the transmittance T and the emission still to
+            // come, I - R: for samples k >= k0, T_k <= T_k0, the first term of
+            // c_k is at most 2 f dz vmax T_k0, and |I - R_k| <= |I - R_k0-1| +
+            // vmax T_k0 (the opacities from k0 on sum to at most T_k0), so
+            // |c_k| <= |g| f dz (3 vmax T_k0 + |I - R_k0-1|).  Bounding each
+            // chunk by the state at its start keeps the window's unit in step
+            // with the coefficients: with the tile's bound alone, late samples'
+            // contributions fall below half a unit and round to zero, a loss
+            // that builds up where the rays leave the volume.
+            float cs = scale, ci = inv_scale;
+            if constexpr (ALPHA) {
+                if (alpha_closed) {
+                    float b = 0.0f, unused = 0.0f;
+                    if (active && max(k0, k_lo) < min(k0 + S, k_hi)) {
+                        const float vmax = __int_as_float(vbound[2 * cvol + 1]);
+                        const float later = (float)fabs(coef.I - coef.run);
+                        const float cb = fabsf(coef.g) * coef.fdz *
+                                         (3.0f * vmax * (float)coef.trans + later) * 1.0625f;
+                        b = fminf(ray_cmax, cb) * ray_n;
+                    }
+                    block_sum2(b, unused, reinterpret_cast<float*>(red));
+                    if (isfinite(b) && b > 0.0f) {
+                        const int e = clampi((int)floor(log2(1073741824.0 / (double)b)), -126, 126);
+                        cs = ldexpf(1.0f, e);
+                        ci = ldexpf(1.0f, -e);
+                    }
+                }
+            }
             if (active) {
                 // the window lives in unclamped index space: a sample's floor
                 // places its eight corners at fixed offsets; entries at -1 or n
@@ -1098,7 +1133,7 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                         const int ix = clampi(fx, -1, V.n[0] - 1);
                         const int iy = clampi(fy, -1, V.n[1] - 1);
                         const int iz = clampi(fz, -1, V.n[2] - 1);
-                        if constexpr (ALPHA) c = ca * scale;
+                        if constexpr (ALPHA) c = ca * cs;
                         if constexpr (ZP) {
                             // a sample with every corner outside the volume adds nothing
                             if (fx != ix || fy != iy || fz != iz) c = 0.0f;
@@ -1193,7 +1228,7 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                     for (int u = 0; u < 4; ++u) {
                         if (val[u] != 0) {
                             win[i + u * kBlock] = 0;
-                            unsafeAtomicAdd(grad + at[u], (float)val[u] * inv_scale);
+                            unsafeAtomicAdd(grad + at[u], (float)val[u] * ci);
                         }
                     }
                 }
@@ -1201,7 +1236,7 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                     const int val = win[i];
                     if (val != 0) {
                         win[i] = 0;
-                        unsafeAtomicAdd(grad + ba.addr, (float)val * inv_scale);
+                        unsafeAtomicAdd(grad + ba.addr, (float)val * ci);
                     }
                     int cx, cy;
                     bw.next(cx, cy);
@@ -1224,7 +1259,7 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
                     if (ZP && !inside) return;
                     unsafeAtomicAdd(grad + (uint32_t)g[2] * sz + (uint32_t)g[1] * sy +
                                         (uint32_t)g[0],
-                                    (float)val * inv_scale);
+                                    (float)val * ci);
                 };
                 int i = threadIdx.x;
                 // near/far: boxes reach into the padding and take this path
