@@ -935,9 +935,14 @@ __global__ __launch_bounds__(kBlock) void drr_scatter_kernel(
             // a margin for rounding, without visiting the samples; otherwise
             // (a negative or non-finite value, or no bounds) a first pass takes
             // the largest coefficient of the ray (NaN if any is not finite).
+            // The closed form grows with a = f dz vmax, but a sample's opacity
+            // saturates at 1: in media opaque within a sample or two (a > 2)
+            // the coefficients stay near |g| while the bound keeps growing, and
+            // a unit sized from it rounds the ray's smaller contributions away,
+            // so such rays take the first pass's exact largest coefficient.
             const float fdz = coef.fdz;
-            if (vbound != nullptr && vbound[2 * cvol] == 0 && fdz >= 0.0f) {
-                const float vmax = __int_as_float(vbound[2 * cvol + 1]);
+            const float vmax = vbound != nullptr ? __int_as_float(vbound[2 * cvol + 1]) : 0.0f;
+            if (vbound != nullptr && vbound[2 * cvol] == 0 && fdz >= 0.0f && fdz * vmax <= 2.0f) {
                 const float I = (float)coef.I;
                 cmax = (isfinite(I) && isfinite(coef.g))
                            ? fabsf(coef.g) * fdz * fmaxf(2.0f * vmax, fabsf(I) + vmax) * 1.0625f
