@@ -149,6 +149,31 @@ def test_siddon_bricks_non_finite_upstream(dev):
     check_grad(grad[ok], ref_g[ok], "siddon bricks non-finite (finite voxels)")
 
 
+def test_siddon_bricks_deep_attenuation(dev):
+    """Beer-Lambert on the brick path with every ray that meets the volume at
+    optical depth 13 or more (voxels 4.85 long in x), so its coefficient
+    g exp(-s) is 1e-6 of g or less, while pixels of the bricks' candidate
+    rectangles whose rays miss the volume keep y = g.  The fixed-point unit has
+    to follow the rays that cross a brick: taken over all candidates it sat
+    near the pieces' own size here (normwise error 6e-3)."""
+    shape, det = (22, 21, 17), (22, 39)
+    spacing = (4.85, 0.6, 2.54)
+    w = W.make_random_small(72646, shape=shape, n_views=2, det=det, n_samples=656,
+                            mode=W.BEER_LAMBERT, spacing=spacing, distance=443.0, rot_deg=0.0)
+    cells = (shape[0] + 1) * (shape[1] + 1) * (shape[2] + 1)
+    assert det[0] * det[1] * max(shape) / cells < 4.0          # views sparse: bricks
+    say(f"case: siddon bricks deep attenuation {shape} det={det} spacing={spacing}")
+    _, s = siddon_forward(w, dev)
+    sv = s.cpu().double().numpy()
+    hit = sv > 0
+    say(f"siddon deep attenuation: {int(hit.sum())} rays meet the volume, optical depth "
+        f"{sv[hit].min():.1f}..{sv[hit].max():.1f}; {int((~hit).sum())} miss")
+    assert sv[hit].min() > 13.0 and (~hit).any()
+    grad = siddon_backward(w, dev, s, w.grad_out)
+    ref_g, _ = oracle.siddon_adjoint_workload(w)
+    check_grad(grad, ref_g, "siddon bricks deep attenuation")
+
+
 def test_siddon_train_size_forward_and_backward(dev):
     w = W.make_workload(3)
     say("case: siddon 256^3 1024x1024 BL fwd+bwd")
